@@ -1,0 +1,152 @@
+/*
+ * q8gemv.h -- C ABI of the MI355X (gfx950) Q8_0 decode matvec library.
+ *
+ * The operation (page "IV.4: One command buffer per token", section "Eight
+ * kernels", the q8_matvec kernel and the paragraph after it):
+ *
+ *   W is a p x n matrix in Q8_0: p rows, each of n/32 consecutive 34-byte
+ *   blocks; a block is a little-endian IEEE binary16 scale d followed by 32
+ *   two's-complement int8 quants q_0..q_31.  For every row r
+ *
+ *       y[r] = sum_b d(r,b) * sum_{j<32} q(r,b,j) * x[32b + j]
+ *
+ *   with x and y float32.  The result overwrites y (no accumulate).
+ *
+ * Conventions for every entry point:
+ *   - All data pointers (x, w, y, X, Y) are DEVICE pointers owned by the
+ *     caller; the library never frees or retains them except as stated for
+ *     chains.  `stream` is a hipStream_t passed as void* (NULL = the legacy
+ *     default stream).
+ *   - Arguments are validated before anything is enqueued; a failed
+ *     validation enqueues nothing and returns a negative q8_status.  The
+ *     calls never fall back to another implementation.
+ *   - Calls are asynchronous: they enqueue on `stream` and return.  Only
+ *     q8_0_decode_chain in Q8_MODE_SYNC_EACH and q8_0_stream_wait block.
+ *   - Alignment: w must be 16-byte aligned; x, y, X, Y 4-byte aligned.
+ *   - y (Y) must not overlap x (X) or w.
+ *   - Sizes: n is a positive multiple of 32 and at most Q8_MAX_N; p is
+ *     positive and at most Q8_MAX_P; small-batch m is in 1..Q8_MAX_M.
+ *   - q8_0_gemv and q8_0_gemm_smallm allocate no device memory.
+ *   - Results are bitwise reproducible run to run for the same inputs,
+ *     shapes and device (fixed reduction order, no atomics).
+ *   - Accuracy: |y - exact| <= 1e-5 * sum_j |w_j x_j| + 1e-6 per output for
+ *     finite inputs (float32 arithmetic with a bounded summation depth).
+ */
+#ifndef Q8GEMV_H
+#define Q8GEMV_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Status codes. */
+enum q8_status {
+    Q8_OK = 0,
+    Q8_ERR_INVALID_ARG = -1, /* null pointer, unknown mode or flag, bad handle */
+    Q8_ERR_SHAPE = -2,       /* n, p or m out of range (zero is out of range) */
+    Q8_ERR_ALIGN = -3,       /* a pointer is not aligned as required */
+    Q8_ERR_ALIAS = -4,       /* an output overlaps an input */
+    Q8_ERR_NO_DEVICE = -5,   /* no HIP device is visible */
+    Q8_ERR_HIP = -6,         /* the HIP runtime reported an error (see q8_0_last_error) */
+    Q8_ERR_TIMEOUT = -7,     /* q8_0_stream_wait ran out of time */
+    Q8_ERR_UNSUPPORTED = -8  /* the current device is not gfx950 */
+};
+
+#define Q8_BLOCK_QUANTS 32
+#define Q8_BLOCK_BYTES 34
+#define Q8_MAX_N (1 << 20)         /* columns */
+#define Q8_MAX_P 0x7fffffff        /* rows */
+#define Q8_MAX_M 16                /* small-batch rows of X */
+#define Q8_MAX_CHAIN_OPS 65535
+
+/*
+ * y = W x for one p x n Q8_0 matrix.
+ * Argument order follows the page's kernel: (x, w, out, n, p) -- section
+ * "Eight kernels", q8_matvec, buffers 0..4.
+ *   x : float32[n], device.   w : p * (n/32) * 34 bytes, device, 16-B aligned.
+ *   y : float32[p], device, written.
+ */
+int q8_0_gemv(const float *x, const void *w, float *y, int64_t n, int64_t p,
+              void *stream);
+
+/*
+ * Y = X W^T for m in 1..16 activation rows in one pass over W: the small-batch
+ * matvec of multi-sequence decode (page "Metal Backend Optimizations",
+ * section 0.3, the batched-matvec kernel family left open for 2..8 tokens;
+ * page "minfer Metal Backend Design", section 4.4, the matmul tiers).
+ *   X : float32[m][n] row-major, device.   Y : float32[m][p] row-major, device.
+ * Each Y[i] equals what q8_0_gemv gives for x = X[i] to the same accuracy.
+ */
+int q8_0_gemm_smallm(const float *X, const void *w, float *Y, int64_t m,
+                     int64_t n, int64_t p, void *stream);
+
+/*
+ * One decode step's chain of matvecs, recorded once and replayed per token
+ * (page "IV.4: One command buffer per token", section "One command buffer":
+ * all of a step's dispatches are encoded once, committed and waited on once).
+ */
+typedef struct q8_0_op {
+    const float *x;  /* float32[n] */
+    const void *w;   /* Q8_0, p rows of n/32 blocks, 16-B aligned */
+    float *y;        /* float32[p] */
+    int64_t n;
+    int64_t p;
+} q8_0_op;
+
+typedef struct q8_0_chain q8_0_chain; /* opaque */
+
+/* chain_create flags */
+#define Q8_CHAIN_FUSE 0u   /* merge runs of mutually independent ops into one launch */
+#define Q8_CHAIN_PER_OP 1u /* one kernel launch per op, in array order */
+
+/* decode_chain modes */
+#define Q8_MODE_GRAPH 0     /* replay the recorded hipGraph: one host call per token */
+#define Q8_MODE_EAGER 1     /* re-issue the chain's launches on the stream */
+#define Q8_MODE_SYNC_EACH 2 /* one launch, then wait for it, per launch */
+
+/*
+ * Validate the ops (each as q8_0_gemv would), plan the launches and record
+ * them into a hipGraph on the current device.  Ops run in array order: an op
+ * that reads (x) or writes (y) memory that an earlier op writes, or writes
+ * memory an earlier op reads, starts only after that earlier op has finished;
+ * with Q8_CHAIN_FUSE, maximal runs of ops with no such overlap share one
+ * launch.  The pointers in `ops` are baked into the recording: they must stay
+ * valid, at the same addresses, until q8_0_chain_destroy.  The handle owns a
+ * small device table (op descriptors and the tile schedule), a private
+ * capture stream and the graph; a token's replay allocates nothing.
+ * On failure *out is set to NULL and nothing is leaked.
+ */
+int q8_0_chain_create(const q8_0_op *ops, int64_t n_ops, uint32_t flags,
+                      q8_0_chain **out);
+
+/* Run one token's chain on `stream` in the given mode. */
+int q8_0_decode_chain(q8_0_chain *chain, int mode, void *stream);
+
+/* Kernel launches one token costs (1 .. n_ops); negative status on a bad handle. */
+int q8_0_chain_launches(const q8_0_chain *chain);
+
+/* Release the handle (NULL is accepted).  The caller must make sure no
+ * replay is still running. */
+int q8_0_chain_destroy(q8_0_chain *chain);
+
+/*
+ * Wait until all work on `stream` has finished, for at most timeout_ms
+ * milliseconds (timeout_ms < 0: no limit).  Returns Q8_ERR_TIMEOUT when the
+ * time runs out; the work itself is not cancelled.  A bounded wait with a
+ * status check follows page "minfer Metal Backend Design", section 4.8.
+ */
+int q8_0_stream_wait(void *stream, int64_t timeout_ms);
+
+/* Static description of a status code. */
+const char *q8_0_status_string(int status);
+
+/* Detail of the last error raised on the calling thread ("" if none). */
+const char *q8_0_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* Q8GEMV_H */

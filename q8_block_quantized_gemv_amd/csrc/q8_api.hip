@@ -1,0 +1,422 @@
+// q8_api.hip -- the C ABI of include/q8gemv.h: validation, launch planning,
+// decode chains (hipGraph record/replay) and the bounded stream wait.
+#include <algorithm>
+#include <chrono>
+#include <cstdint>
+#include <cstring>
+#include <mutex>
+#include <string>
+#include <thread>
+#include <vector>
+
+#include "q8gemv.h"
+#include "q8_internal.h"
+
+using namespace q8;
+
+namespace {
+
+thread_local std::string g_last_error;
+
+int fail(int code, const std::string &msg) {
+    g_last_error = msg;
+    return code;
+}
+
+int fail_hip(hipError_t e, const char *where) {
+    std::string m = std::string(where) + ": " + hipGetErrorName(e) + " (" + hipGetErrorString(e) + ")";
+    return fail(Q8_ERR_HIP, m);
+}
+
+bool overlaps(const void *a, int64_t na, const void *b, int64_t nb) {
+    const uintptr_t a0 = (uintptr_t)a, b0 = (uintptr_t)b;
+    return a0 < b0 + (uintptr_t)nb && b0 < a0 + (uintptr_t)na;
+}
+
+int64_t w_bytes(int64_t n, int64_t p) { return p * (n / kQuants) * kBlockBytes; }
+
+// Argument checks shared by every entry point; touches no device state.
+int validate(const float *x, const void *w, const float *y, int64_t m, int64_t n, int64_t p,
+             const char *what) {
+    std::string tag(what);
+    if (!x || !w || !y) return fail(Q8_ERR_INVALID_ARG, tag + ": null pointer");
+    if (n <= 0 || n % kQuants != 0 || n > Q8_MAX_N)
+        return fail(Q8_ERR_SHAPE, tag + ": n=" + std::to_string(n) +
+                                      " must be a positive multiple of 32 and <= 1048576");
+    if (p <= 0 || p > Q8_MAX_P)
+        return fail(Q8_ERR_SHAPE, tag + ": p=" + std::to_string(p) + " out of range");
+    if (m < 1 || m > Q8_MAX_M)
+        return fail(Q8_ERR_SHAPE, tag + ": m=" + std::to_string(m) + " must be in 1..16");
+    if ((uintptr_t)w % 16) return fail(Q8_ERR_ALIGN, tag + ": w must be 16-byte aligned");
+    if ((uintptr_t)x % 4 || (uintptr_t)y % 4)
+        return fail(Q8_ERR_ALIGN, tag + ": x and y must be 4-byte aligned");
+    const int64_t yb = 4 * m * p;
+    if (overlaps(y, yb, x, 4 * m * n)) return fail(Q8_ERR_ALIAS, tag + ": y overlaps x");
+    if (overlaps(y, yb, w, w_bytes(n, p))) return fail(Q8_ERR_ALIAS, tag + ": y overlaps w");
+    return Q8_OK;
+}
+
+// The current device must exist and be gfx950 (checked once per device).
+int check_device(int *dev_out = nullptr) {
+    int count = 0;
+    hipError_t e = hipGetDeviceCount(&count);
+    if (e != hipSuccess || count <= 0) {
+        (void)hipGetLastError();
+        return fail(Q8_ERR_NO_DEVICE, "no HIP device is visible");
+    }
+    int dev = 0;
+    if ((e = hipGetDevice(&dev)) != hipSuccess) return fail_hip(e, "hipGetDevice");
+    static std::mutex mu;
+    static std::vector<int> verdict;  // -1 unknown, 0 unsupported, 1 ok
+    std::lock_guard<std::mutex> lk(mu);
+    if ((int)verdict.size() <= dev) verdict.resize(dev + 1, -1);
+    if (verdict[dev] < 0) {
+        hipDeviceProp_t prop;
+        if ((e = hipGetDeviceProperties(&prop, dev)) != hipSuccess)
+            return fail_hip(e, "hipGetDeviceProperties");
+        verdict[dev] = std::strncmp(prop.gcnArchName, "gfx950", 6) == 0 ? 1 : 0;
+        if (!verdict[dev])
+            return fail(Q8_ERR_UNSUPPORTED,
+                        std::string("device is ") + prop.gcnArchName + ", this library is built for gfx950");
+    }
+    if (!verdict[dev]) return fail(Q8_ERR_UNSUPPORTED, "device is not gfx950");
+    if (dev_out) *dev_out = dev;
+    return Q8_OK;
+}
+
+int64_t gcd64(int64_t a, int64_t b) {
+    while (b) { int64_t t = a % b; a = b; b = t; }
+    return a;
+}
+
+// Waves that split one row tile's groups.  A standalone launch wants many
+// workgroups; inside a fused chain the other ops fill the GPU, so the choice
+// only has to keep the waves of a workgroup evenly loaded.
+int choose_ks(int64_t gsr, int64_t nsr, bool standalone) {
+    auto eff = [&](int ks) {
+        const int64_t per = (gsr + ks - 1) / ks;
+        return (double)gsr / (double)(ks * per);
+    };
+    if (standalone) {
+        for (int ks : {4, 2}) {
+            if (gsr < ks) continue;
+            if (fast_tiles_for(nsr, 1) < 512 || eff(ks) >= 0.95) return ks;
+        }
+        return 1;
+    }
+    int best = 1;
+    double be = eff(1);
+    for (int ks : {2, 4}) {
+        if (gsr < ks) continue;
+        const double e = eff(ks);
+        if (e >= 0.95 || e > be + 1e-9) { best = ks; be = e; }
+    }
+    return best;
+}
+
+OpDesc plan_op(const float *x, const void *w, float *y, int64_t m, int64_t n, int64_t p,
+               bool standalone) {
+    OpDesc d;
+    std::memset(&d, 0, sizeof d);
+    const int64_t nb = n / kQuants;
+    const int64_t rs = kGroupBlocks / gcd64(nb, kGroupBlocks);
+    d.x = x;
+    d.w = (const uint8_t *)w;
+    d.y = y;
+    d.nb = (int32_t)nb;
+    d.p = (int32_t)p;
+    d.rs = (int32_t)rs;
+    d.nsr = (int32_t)(p / rs);
+    d.gsr = (int32_t)(rs * nb / kGroupBlocks);
+    d.sr_bytes = rs * nb * kBlockBytes;
+    d.ks = choose_ks(d.gsr, d.nsr, standalone);
+    d.fast_tiles = (int32_t)fast_tiles_for(d.nsr, d.ks);
+    d.tail_row0 = (int32_t)(d.nsr * rs);
+    d.m = (int32_t)m;
+    d.x_stride = n;
+    d.y_stride = p;
+    return d;
+}
+
+int64_t tiles_of(const OpDesc &d) {
+    return (int64_t)d.fast_tiles + tail_tiles_for((int64_t)d.p - d.tail_row0);
+}
+
+int gemv_launch(const float *x, const void *w, float *y, int64_t n, int64_t p, hipStream_t s) {
+    const OpDesc d = plan_op(x, w, y, 1, n, p, true);
+    hipError_t e = launch_gemv_single(d, tiles_of(d), s);
+    if (e != hipSuccess) return fail_hip(e, "q8_0_gemv launch");
+    return Q8_OK;
+}
+
+}  // namespace
+
+// ===================================================================== ABI
+extern "C" {
+
+const char *q8_0_status_string(int status) {
+    switch (status) {
+        case Q8_OK: return "ok";
+        case Q8_ERR_INVALID_ARG: return "invalid argument";
+        case Q8_ERR_SHAPE: return "shape out of range";
+        case Q8_ERR_ALIGN: return "misaligned pointer";
+        case Q8_ERR_ALIAS: return "output overlaps an input";
+        case Q8_ERR_NO_DEVICE: return "no HIP device";
+        case Q8_ERR_HIP: return "HIP runtime error";
+        case Q8_ERR_TIMEOUT: return "timed out";
+        case Q8_ERR_UNSUPPORTED: return "unsupported device";
+        default: return "unknown status";
+    }
+}
+
+const char *q8_0_last_error(void) { return g_last_error.c_str(); }
+
+int q8_0_gemv(const float *x, const void *w, float *y, int64_t n, int64_t p, void *stream) {
+    int rc = validate(x, w, y, 1, n, p, "q8_0_gemv");
+    if (rc) return rc;
+    if ((rc = check_device())) return rc;
+    return gemv_launch(x, w, y, n, p, (hipStream_t)stream);
+}
+
+int q8_0_gemm_smallm(const float *X, const void *w, float *Y, int64_t m, int64_t n, int64_t p,
+                     void *stream) {
+    int rc = validate(X, w, Y, m, n, p, "q8_0_gemm_smallm");
+    if (rc) return rc;
+    if ((rc = check_device())) return rc;
+    hipStream_t s = (hipStream_t)stream;
+    const int64_t nb = n / kQuants;
+    const int64_t rs = kGroupBlocks / gcd64(nb, kGroupBlocks);
+    if (m == 1 || rs > 2) {
+        // one weight pass per activation row: used for m = 1 and for widths
+        // whose rows need super-rows of 4 or 8 (n not a multiple of 128)
+        for (int64_t i = 0; i < m; ++i)
+            if ((rc = gemv_launch(X + i * n, w, Y + i * p, n, p, s))) return rc;
+        return Q8_OK;
+    }
+    int mpad = 2;
+    while (mpad < m) mpad *= 2;
+    OpDesc d = plan_op(X, w, Y, m, n, p, true);
+    d.ks = 1;  // the small-batch kernel keeps each row tile in one wave
+    d.fast_tiles = (int32_t)fast_tiles_for(d.nsr, 1);
+    hipError_t e = launch_gemm_single(d, mpad, tiles_of(d), s);
+    if (e != hipSuccess) return fail_hip(e, "q8_0_gemm_smallm launch");
+    return Q8_OK;
+}
+
+int q8_0_stream_wait(void *stream, int64_t timeout_ms) {
+    const auto t0 = std::chrono::steady_clock::now();
+    for (;;) {
+        hipError_t e = hipStreamQuery((hipStream_t)stream);
+        if (e == hipSuccess) return Q8_OK;
+        if (e != hipErrorNotReady) return fail_hip(e, "hipStreamQuery");
+        if (timeout_ms >= 0) {
+            const auto el = std::chrono::duration_cast<std::chrono::milliseconds>(
+                std::chrono::steady_clock::now() - t0).count();
+            if (el >= timeout_ms)
+                return fail(Q8_ERR_TIMEOUT, "stream still busy after " + std::to_string(timeout_ms) + " ms");
+        }
+        std::this_thread::sleep_for(std::chrono::microseconds(50));
+    }
+}
+
+}  // extern "C"
+
+// ===================================================================== chains
+struct q8_0_chain {
+    int device = -1;
+    uint32_t flags = 0;
+    std::vector<q8_0_op> ops;
+    // one entry per kernel launch of a token
+    struct Launch {
+        bool fused;
+        OpDesc single;        // per-op launch
+        const OpDesc *d_ops;  // fused launch
+        const Tile *d_tiles;
+        int64_t grid;
+    };
+    std::vector<Launch> launches;
+    void *d_table = nullptr;
+    hipStream_t capture = nullptr;
+    hipGraph_t graph = nullptr;
+    hipGraphExec_t exec = nullptr;
+};
+
+namespace {
+
+hipError_t issue(const q8_0_chain::Launch &L, hipStream_t s) {
+    if (L.fused) return launch_gemv_fused(L.d_ops, L.d_tiles, L.grid, s);
+    return launch_gemv_single(L.single, L.grid, s);
+}
+
+void chain_free(q8_0_chain *c) {
+    if (!c) return;
+    if (c->exec) (void)hipGraphExecDestroy(c->exec);
+    if (c->graph) (void)hipGraphDestroy(c->graph);
+    if (c->capture) (void)hipStreamDestroy(c->capture);
+    if (c->d_table) (void)hipFree(c->d_table);
+    delete c;
+}
+
+// Does op b have to wait for op a (a earlier)?  Any write of one that
+// touches memory the other reads or writes.
+bool depends(const q8_0_op &a, const q8_0_op &b) {
+    const int64_t ya = 4 * a.p, yb = 4 * b.p;
+    return overlaps(b.y, yb, a.y, ya) || overlaps(b.y, yb, a.x, 4 * a.n) ||
+           overlaps(b.y, yb, a.w, w_bytes(a.n, a.p)) || overlaps(b.x, 4 * b.n, a.y, ya) ||
+           overlaps(b.w, w_bytes(b.n, b.p), a.y, ya);
+}
+
+}  // namespace
+
+extern "C" {
+
+int q8_0_chain_create(const q8_0_op *ops, int64_t n_ops, uint32_t flags, q8_0_chain **out) {
+    if (!out) return fail(Q8_ERR_INVALID_ARG, "q8_0_chain_create: out is null");
+    *out = nullptr;
+    if (!ops || n_ops <= 0 || n_ops > Q8_MAX_CHAIN_OPS)
+        return fail(Q8_ERR_INVALID_ARG, "q8_0_chain_create: need 1..65535 ops");
+    if (flags != Q8_CHAIN_FUSE && flags != Q8_CHAIN_PER_OP)
+        return fail(Q8_ERR_INVALID_ARG, "q8_0_chain_create: unknown flags");
+    for (int64_t i = 0; i < n_ops; ++i) {
+        const std::string what = "q8_0_chain_create op " + std::to_string(i);
+        int rc = validate(ops[i].x, ops[i].w, ops[i].y, 1, ops[i].n, ops[i].p, what.c_str());
+        if (rc) return rc;
+    }
+    int dev = 0;
+    int rc = check_device(&dev);
+    if (rc) return rc;
+
+    q8_0_chain *c = new q8_0_chain();
+    c->device = dev;
+    c->flags = flags;
+    c->ops.assign(ops, ops + n_ops);
+
+    // ---- plan: runs of mutually independent ops (or single ops)
+    std::vector<std::pair<int64_t, int64_t>> segs;  // [begin, end)
+    if (flags == Q8_CHAIN_PER_OP) {
+        for (int64_t i = 0; i < n_ops; ++i) segs.push_back({i, i + 1});
+    } else {
+        int64_t b = 0;
+        for (int64_t i = 1; i <= n_ops; ++i) {
+            bool cut = (i == n_ops);
+            for (int64_t j = b; !cut && j < i; ++j) cut = depends(ops[j], ops[i]);
+            if (cut) { segs.push_back({b, i}); b = i; }
+        }
+    }
+
+    // ---- fused segments: op table + tile schedule in one device block
+    std::vector<OpDesc> h_ops;
+    std::vector<Tile> h_tiles;
+    struct SegInfo { size_t op0, tile0; int64_t ntiles; bool fused; };
+    std::vector<SegInfo> info;
+    for (auto &sg : segs) {
+        const bool fused = (flags == Q8_CHAIN_FUSE) && (sg.second - sg.first > 1);
+        SegInfo si{h_ops.size(), h_tiles.size(), 0, fused};
+        if (fused) {
+            // tiles sorted by decreasing weight bytes so that the smallest
+            // tiles finish the launch (ties keep encode order)
+            struct Item { Tile t; int64_t bytes; };
+            std::vector<Item> items;
+            for (int64_t i = sg.first; i < sg.second; ++i) {
+                const q8_0_op &o = ops[i];
+                OpDesc d = plan_op(o.x, o.w, o.y, 1, o.n, o.p, false);
+                const uint32_t oi = (uint32_t)(h_ops.size() - si.op0);
+                h_ops.push_back(d);
+                const int64_t fb = (int64_t)(kWaves / d.ks) * kWave * d.sr_bytes;
+                for (int64_t t = 0; t < d.fast_tiles; ++t) items.push_back({{oi, (uint32_t)t}, fb});
+                const int64_t tt = tail_tiles_for((int64_t)d.p - d.tail_row0);
+                for (int64_t t = 0; t < tt; ++t)
+                    items.push_back({{oi, (uint32_t)t | kTailBit}, kTailRowsPerTile * d.nb * kBlockBytes});
+            }
+            std::stable_sort(items.begin(), items.end(),
+                             [](const Item &a, const Item &b) { return a.bytes > b.bytes; });
+            for (auto &it : items) h_tiles.push_back(it.t);
+            si.ntiles = (int64_t)items.size();
+        }
+        info.push_back(si);
+    }
+    if (!h_ops.empty()) {
+        const size_t ob = h_ops.size() * sizeof(OpDesc);
+        const size_t tb = h_tiles.size() * sizeof(Tile);
+        hipError_t e = hipMalloc(&c->d_table, ob + tb);
+        if (e != hipSuccess) { chain_free(c); return fail_hip(e, "q8_0_chain_create hipMalloc"); }
+        if ((e = hipMemcpy(c->d_table, h_ops.data(), ob, hipMemcpyHostToDevice)) != hipSuccess ||
+            (e = hipMemcpy((char *)c->d_table + ob, h_tiles.data(), tb, hipMemcpyHostToDevice)) != hipSuccess) {
+            chain_free(c);
+            return fail_hip(e, "q8_0_chain_create hipMemcpy");
+        }
+    }
+    const OpDesc *d_ops = (const OpDesc *)c->d_table;
+    const Tile *d_tiles = (const Tile *)((const char *)c->d_table + h_ops.size() * sizeof(OpDesc));
+    for (size_t k = 0; k < segs.size(); ++k) {
+        q8_0_chain::Launch L;
+        std::memset(&L, 0, sizeof L);
+        if (info[k].fused) {
+            L.fused = true;
+            L.d_ops = d_ops + info[k].op0;
+            L.d_tiles = d_tiles + info[k].tile0;
+            L.grid = info[k].ntiles;
+        } else {
+            const q8_0_op &o = ops[segs[k].first];
+            L.fused = false;
+            L.single = plan_op(o.x, o.w, o.y, 1, o.n, o.p, true);
+            L.grid = tiles_of(L.single);
+        }
+        c->launches.push_back(L);
+    }
+
+    // ---- record one token into a graph on a private stream
+    hipError_t e = hipStreamCreateWithFlags(&c->capture, hipStreamNonBlocking);
+    if (e != hipSuccess) { chain_free(c); return fail_hip(e, "hipStreamCreateWithFlags"); }
+    if ((e = hipStreamBeginCapture(c->capture, hipStreamCaptureModeThreadLocal)) != hipSuccess) {
+        chain_free(c);
+        return fail_hip(e, "hipStreamBeginCapture");
+    }
+    hipError_t le = hipSuccess;
+    for (auto &L : c->launches)
+        if (le == hipSuccess) le = issue(L, c->capture);
+    e = hipStreamEndCapture(c->capture, &c->graph);
+    if (le != hipSuccess) { chain_free(c); return fail_hip(le, "chain launch during capture"); }
+    if (e != hipSuccess) { chain_free(c); return fail_hip(e, "hipStreamEndCapture"); }
+    if ((e = hipGraphInstantiate(&c->exec, c->graph, nullptr, nullptr, 0)) != hipSuccess) {
+        chain_free(c);
+        return fail_hip(e, "hipGraphInstantiate");
+    }
+    *out = c;
+    return Q8_OK;
+}
+
+int q8_0_decode_chain(q8_0_chain *c, int mode, void *stream) {
+    if (!c) return fail(Q8_ERR_INVALID_ARG, "q8_0_decode_chain: null chain");
+    if (mode != Q8_MODE_GRAPH && mode != Q8_MODE_EAGER && mode != Q8_MODE_SYNC_EACH)
+        return fail(Q8_ERR_INVALID_ARG, "q8_0_decode_chain: unknown mode");
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return fail_hip(e, "hipGetDevice");
+    if (dev != c->device)
+        return fail(Q8_ERR_INVALID_ARG, "q8_0_decode_chain: chain was created on device " +
+                                            std::to_string(c->device) + ", current is " + std::to_string(dev));
+    hipStream_t s = (hipStream_t)stream;
+    if (mode == Q8_MODE_GRAPH) {
+        if ((e = hipGraphLaunch(c->exec, s)) != hipSuccess) return fail_hip(e, "hipGraphLaunch");
+        return Q8_OK;
+    }
+    for (auto &L : c->launches) {
+        if ((e = issue(L, s)) != hipSuccess) return fail_hip(e, "chain launch");
+        if (mode == Q8_MODE_SYNC_EACH && (e = hipStreamSynchronize(s)) != hipSuccess)
+            return fail_hip(e, "hipStreamSynchronize");
+    }
+    return Q8_OK;
+}
+
+int q8_0_chain_launches(const q8_0_chain *c) {
+    if (!c) return fail(Q8_ERR_INVALID_ARG, "q8_0_chain_launches: null chain");
+    return (int)c->launches.size();
+}
+
+int q8_0_chain_destroy(q8_0_chain *c) {
+    chain_free(c);
+    return Q8_OK;
+}
+
+}  // extern "C"

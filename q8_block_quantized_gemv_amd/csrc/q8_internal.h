@@ -1,0 +1,73 @@
+// q8_internal.h -- shared between the HIP kernels and the host side of the
+// library.  Not installed; the public interface is include/q8gemv.h.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace q8 {
+
+// Q8_0 geometry (page "IV.4: One command buffer per token", section "Eight
+// kernels": 32 quants and a 2-byte binary16 scale per block).
+constexpr int kQuants = 32;
+constexpr int kBlockBytes = 34;
+// Eight consecutive blocks are 272 bytes = 17 aligned 16-byte chunks: the
+// unit the fast path moves from HBM to LDS.
+constexpr int kGroupBlocks = 8;
+constexpr int kGroupBytes = kGroupBlocks * kBlockBytes;  // 272
+constexpr int kGroupChunks = kGroupBytes / 16;           // 17
+
+constexpr int kWave = 64;
+constexpr int kWaves = 4;                 // waves per workgroup
+constexpr int kThreads = kWave * kWaves;  // 256
+constexpr int kBufs = 2;                  // LDS stages per wave
+constexpr int kStageBytes = kWave * kGroupBytes;  // one group of 64 lanes: 17408 B
+
+// One matvec (or small-batch product) as the kernels see it.  A "super-row"
+// is `rs` consecutive rows whose bytes, taken together, are a whole number of
+// 272-byte groups: rs = 8 / gcd(n/32, 8).  Lane l of a wave owns one
+// super-row; rows that do not fill a last super-row are "tail" rows and take
+// the generic path.
+struct OpDesc {
+    const float *x;      // x, or X row 0 for small batches
+    const uint8_t *w;
+    float *y;            // y, or Y row 0
+    int64_t sr_bytes;    // bytes of one super-row = rs * nb * 34
+    int64_t x_stride;    // floats between rows of X (= n)
+    int64_t y_stride;    // floats between rows of Y (= p)
+    int32_t nb;          // blocks per row = n / 32
+    int32_t p;           // rows
+    int32_t rs;          // rows per super-row: 1, 2, 4 or 8
+    int32_t nsr;         // super-rows handled by the fast path = p / rs
+    int32_t gsr;         // groups per super-row = rs * nb / 8
+    int32_t ks;          // waves that split one super-row's groups: 1, 2 or 4
+    int32_t fast_tiles;  // workgroup tiles of the fast path
+    int32_t tail_row0;   // first tail row = nsr * rs
+    int32_t m;           // activation rows (1 for a matvec)
+    int32_t pad_;
+};
+
+// One workgroup's work in a fused launch.
+struct Tile {
+    uint32_t op;    // index into the op table
+    uint32_t tile;  // tile within the op; kTailBit set: tail tile
+};
+constexpr uint32_t kTailBit = 0x80000000u;
+constexpr int kTailRowsPerTile = kWaves;  // one wave per tail row
+
+// Fast tiles cover (kWaves / ks) * 64 super-rows each.
+inline int64_t fast_tiles_for(int64_t nsr, int ks) {
+    const int64_t per = (int64_t)(kWaves / ks) * kWave;
+    return (nsr + per - 1) / per;
+}
+inline int64_t tail_tiles_for(int64_t tail_rows) {
+    return (tail_rows + kTailRowsPerTile - 1) / kTailRowsPerTile;
+}
+
+// Kernel launchers (q8_kernels.hip).  All return the hipError_t of the launch.
+hipError_t launch_gemv_single(const OpDesc &op, int64_t grid, hipStream_t s);
+hipError_t launch_gemv_fused(const OpDesc *d_ops, const Tile *d_tiles, int64_t grid,
+                             hipStream_t s);
+hipError_t launch_gemm_single(const OpDesc &op, int mpad, int64_t grid, hipStream_t s);
+
+}  // namespace q8

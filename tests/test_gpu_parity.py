@@ -1,0 +1,252 @@
+"""GPU parity of the HIP path against the CPU oracle, through the C ABI.
+
+Sizes here are small enough for the oracle to check every output; they span
+every super-row geometry the kernels have (rows of 1, 2, 4 and 8 per lane),
+several row tiles, ragged row counts and the generic tail path.
+"""
+import numpy as np
+import pytest
+
+import oracle
+import synth
+from tests.gpu_util import down, log, parity, up, w_dev
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def q8():
+    import torch
+    if not torch.cuda.is_available():
+        pytest.fail("GPU tests need a GPU")
+    import q8_block_quantized_gemv_amd as q8mod
+    return q8mod
+
+
+def _gemv(q8, w, x, n, p):
+    import torch
+    y = torch.full((p,), float("nan"), dtype=torch.float32, device="cuda")
+    q8.gemv(up(x), w_dev(w, n, p), y)
+    return down(y)
+
+
+# (n, p): nb = n/32 decides rows per super-row: nb%8==0 -> 1, ==4 -> 2,
+# ==2/6 -> 4, odd -> 8; p % rs != 0 leaves tail rows for the generic path.
+SHAPES = [
+    (32, 1), (32, 7), (32, 9), (64, 3), (96, 50), (96, 67), (160, 9), (224, 13),
+    (256, 1), (256, 64), (256, 65), (512, 300), (896, 7), (896, 130), (1024, 3072),
+    (1088, 5), (1088, 131), (2080, 67), (3072, 257), (3584, 517), (4864, 131),
+    (18944, 70), (256, 1031),
+]
+
+
+@pytest.mark.parametrize("n,p", SHAPES, ids=lambda v: str(v))
+def test_gemv_matches_oracle(q8, n, p):
+    log("gemv n=%d p=%d" % (n, p))
+    rng = np.random.default_rng(10_000 + 7 * n + p)
+    w = synth.q8_weights(n, p, rng)
+    x = synth.activations(n, rng)
+    y = _gemv(q8, w, x, n, p)
+    _, y64, mag = oracle.gemv(w, x, n, p)
+    parity(y, y64, mag, "gemv %dx%d" % (n, p))
+
+
+def test_page_rung_one_shape(q8):
+    """The page's matvec test: 50 x 96, its LCG, weight seed 7, x seed 42;
+    it holds its kernel to 5e-4 absolute.  Both that bar and ours."""
+    log("page 50x96")
+    p, n = 50, 96
+    w = synth.page_q8_bytes(p, n, 7)
+    x = synth.page_x(n, 42)
+    y = _gemv(q8, w, x, n, p)
+    _, y64, mag = oracle.gemv(w, x, n, p)
+    assert np.max(np.abs(y - y64)) < 5e-4
+    parity(y, y64, mag, "page 50x96")
+
+
+@pytest.mark.parametrize("n,p", [(32, 5), (96, 9), (896, 130), (3584, 512), (18944, 96),
+                                 (4864, 33), (1024, 3072)], ids=lambda v: str(v))
+def test_integer_case_is_bitwise(q8, n, p):
+    """Scale 0.0625, integer x in [-4, 4]: every partial sum is exact in float32
+    in any order, so the GPU must equal the oracle bit for bit."""
+    log("integer n=%d p=%d" % (n, p))
+    w, x = synth.integer_case(n, p, np.random.default_rng(77 + n + p))
+    y = _gemv(q8, w, x, n, p)
+    yo, _, _ = oracle.gemv(w, x, n, p)
+    assert np.array_equal(y.view(np.uint32), yo.view(np.uint32))
+
+
+def test_every_binary16_scale(q8):
+    """Row r has scale bits r, one quant 1 against x = 1: y[r] is the decoded
+    scale exactly, for all 65536 patterns (NaN where the pattern is NaN)."""
+    log("f16 exhaustive")
+    n, p = 32, 65536
+    blk = np.zeros((p, 34), np.uint8)
+    bits = np.arange(p, dtype=np.uint32)
+    blk[:, 0] = bits & 0xFF
+    blk[:, 1] = bits >> 8
+    blk[:, 2] = 1
+    x = np.zeros(n, np.float32)
+    x[0] = 1.0
+    import torch
+    y = torch.empty(p, dtype=torch.float32, device="cuda")
+    q8.gemv(up(x), up(blk), y)
+    y = down(y)
+    ref = np.array([oracle.f16_to_double(int(b)) for b in bits], dtype=np.float64)
+    nan = np.isnan(ref)
+    assert np.array_equal(np.isnan(y), nan)
+    assert np.array_equal(y[~nan].astype(np.float64), ref[~nan])
+
+
+@pytest.mark.parametrize("n", [32, 256, 896])
+def test_every_quant_byte(q8, n):
+    """Row r: one block of scale 1.0 holds byte r at position r % 32; x is the
+    column index + 1, so y[r] = int8(r) * (column + 1) exactly."""
+    log("quant bytes n=%d" % n)
+    p = 256
+    nb = n // 32
+    w = np.zeros((p, nb, 34), np.uint8)
+    r = np.arange(p)
+    b = r % nb
+    j = r % 32
+    w[r, b, 0:2] = [0x00, 0x3C]
+    w[r, b, 2 + j] = r.astype(np.uint8)
+    x = (np.arange(n) + 1).astype(np.float32)
+    y = _gemv(q8, w.reshape(-1), x, n, p)
+    q = r.astype(np.uint8).view(np.int8).astype(np.float64)
+    assert np.array_equal(y.astype(np.float64), q * (32 * b + j + 1))
+
+
+def test_zero_scales_give_zero(q8):
+    log("zero scales")
+    n, p = 3584, 257
+    rng = np.random.default_rng(5)
+    w = synth.q8_weights(n, p, rng).reshape(-1, 34)
+    w[:, 0:2] = 0
+    x = synth.activations(n, rng) * np.float32(100)
+    assert np.all(_gemv(q8, w.reshape(-1), x, n, p) == 0.0)
+
+
+def test_all_ones_quants(q8):
+    log("all-ones quants")
+    n, p = 896, 66
+    rng = np.random.default_rng(6)
+    w = synth.q8_weights(n, p, rng).reshape(-1, 34)
+    w[:, 2:] = 1
+    x = synth.activations(n, rng)
+    y = _gemv(q8, w.reshape(-1), x, n, p)
+    _, y64, mag = oracle.gemv(w, x, n, p)
+    parity(y, y64, mag, "all ones")
+
+
+@pytest.mark.parametrize("n,p", [(3584, 700), (896, 131), (2080, 67)], ids=lambda v: str(v))
+def test_determinism_canaries_and_sign(q8, n, p):
+    """Bitwise repeatable; guard bands around y untouched; y(-x) = -y(x) and
+    y(4x) = 4y(x) bit for bit (negation and powers of two commute with
+    rounding)."""
+    import torch
+    log("determinism n=%d p=%d" % (n, p))
+    rng = np.random.default_rng(8 + n)
+    w = w_dev(synth.q8_weights(n, p, rng), n, p)
+    x = up(synth.activations(n, rng))
+    guard = 1024
+    buf = torch.full((p + 2 * guard,), float("nan"), dtype=torch.float32, device="cuda")
+    y = buf[guard:guard + p]
+    q8.gemv(x, w, y)
+    a = down(y).copy()
+    q8.gemv(x, w, y)
+    b = down(y).copy()
+    assert np.array_equal(a.view(np.uint32), b.view(np.uint32))
+    whole = down(buf)
+    assert np.all(np.isnan(whole[:guard])) and np.all(np.isnan(whole[guard + p:]))
+    q8.gemv(-x, w, y)
+    assert np.array_equal(down(y), -a)
+    q8.gemv(x * 4, w, y)
+    assert np.array_equal(down(y), a * 4)
+
+
+@pytest.mark.parametrize("m", [1, 2, 3, 4, 5, 8, 13, 16])
+@pytest.mark.parametrize("n,p", [(256, 130), (896, 70), (3584, 300), (160, 11)],
+                         ids=lambda v: str(v))
+def test_gemm_smallm(q8, m, n, p):
+    """Each row of Y against its own oracle matvec, and bit for bit against
+    q8_0_gemv on that row of X."""
+    import torch
+    log("gemm m=%d n=%d p=%d" % (m, n, p))
+    rng = np.random.default_rng(300 + 11 * m + n + p)
+    w = synth.q8_weights(n, p, rng)
+    X = synth.activations(n, rng, m).reshape(m, n)
+    wd = w_dev(w, n, p)
+    Xd = up(X)
+    Y = torch.full((m, p), float("nan"), dtype=torch.float32, device="cuda")
+    q8.gemm_smallm(Xd, wd, Y)
+    Yh = down(Y)
+    _, Y64, MAG = oracle.gemm(w, X, m, n, p)
+    for i in range(m):
+        parity(Yh[i], Y64[i], MAG[i], "gemm row %d" % i)
+        yi = torch.empty(p, dtype=torch.float32, device="cuda")
+        q8.gemv(Xd[i].contiguous(), wd, yi)
+        assert np.array_equal(down(yi).view(np.uint32), Yh[i].view(np.uint32))
+
+
+def test_gemm_identical_rows(q8):
+    import torch
+    log("gemm identical rows")
+    n, p, m = 3584, 129, 16
+    rng = np.random.default_rng(41)
+    wd = w_dev(synth.q8_weights(n, p, rng), n, p)
+    x = synth.activations(n, rng)
+    Y = q8.gemm_smallm(up(np.tile(x, (m, 1))), wd)
+    Yh = down(Y)
+    for i in range(1, m):
+        assert np.array_equal(Yh[i].view(np.uint32), Yh[0].view(np.uint32))
+    del torch
+
+
+def _chain_case(seed):
+    """Twelve ops of mixed shapes; op 7 reads op 6's output (a dependency)."""
+    shapes = [(1024, 2048), (1024, 1024), (896, 128), (896, 130), (2048, 1024), (3584, 512),
+              (4864, 896), (896, 4864), (160, 9), (256, 1031), (18944, 64), (3584, 1000)]
+    rng = np.random.default_rng(seed)
+    ws = [synth.q8_weights(n, p, rng) for n, p in shapes]
+    xs = [synth.activations(n, rng) for n, p in shapes]
+    return shapes, ws, xs
+
+
+@pytest.mark.parametrize("fuse", [True, False])
+def test_chain_modes_equal_standalone(q8, fuse):
+    import torch
+    log("chain fuse=%s" % fuse)
+    shapes, ws, xs = _chain_case(2024)
+    wd = [w_dev(w, n, p) for w, (n, p) in zip(ws, shapes)]
+    xd = [up(x) for x in xs]
+    ys = [torch.full((p,), float("nan"), dtype=torch.float32, device="cuda") for n, p in shapes]
+    xd[7] = ys[6]                      # 4864->896 feeds 896->4864
+    chain = q8.Chain(list(zip(xd, wd, ys)), fuse=fuse)
+    assert chain.launches == (2 if fuse else len(shapes))
+    # standalone reference, in order (op 7 reads op 6's result)
+    ref = [torch.empty(p, dtype=torch.float32, device="cuda") for n, p in shapes]
+    for i, (n, p) in enumerate(shapes):
+        q8.gemv(ref[6] if i == 7 else xd[i], wd[i], ref[i])
+    refh = [down(r).copy() for r in ref]
+    for mode in (q8.MODE_GRAPH, q8.MODE_EAGER, q8.MODE_SYNC_EACH, q8.MODE_GRAPH):
+        for y in ys:
+            y.fill_(float("nan"))
+        chain.run(mode)
+        q8.stream_wait(timeout_ms=60_000)
+        for i in range(len(shapes)):
+            assert np.array_equal(down(ys[i]).view(np.uint32), refh[i].view(np.uint32)), (mode, i)
+    # and against the oracle
+    x7 = refh[6]
+    for i, (n, p) in enumerate(shapes):
+        x = x7 if i == 7 else xs[i]
+        _, y64, mag = oracle.gemv(ws[i], x, n, p)
+        parity(refh[i], y64, mag, "chain op %d" % i)
+    chain.close()
+
+
+def test_stream_wait_timeout_and_ok(q8):
+    """A bounded wait returns OK on an idle stream."""
+    import torch
+    torch.cuda.synchronize()
+    assert q8.stream_wait(timeout_ms=1000) == 0
