@@ -1,0 +1,210 @@
+#!/usr/bin/env python3
+"""Benchmark of the Q8_0 decode matvec chain on one MI355X.
+
+One step = one token's chain of matvecs (197 for the 7B-class decode step),
+replayed from the recorded hipGraph on torch's current stream, with every
+weight and activation already resident in HBM.  Prints ONE JSON line:
+
+  metric / value / unit : achieved HBM GB/s of algorithmic bytes (weights
+                          once + x once + y once per op) over the timed steps
+  ms_per_step           : milliseconds per token
+  roofline              : the dominant (only) kernel of a step, measured with
+                          HIP events on the launch stream, against 8 TB/s
+  cpu_baseline          : the CPU oracle on a bounded sample of the same
+                          workload, on this host (single thread)
+
+Progress goes to stderr.  Usage:
+  python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+KERNEL_SOURCES = [os.path.join(ROOT, "q8_block_quantized_gemv_amd", "csrc", f)
+                  for f in ("q8_kernels.hip", "q8_internal.h")]
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_7b_chain.json")
+
+
+def say(msg):
+    print("[bench] " + msg, file=sys.stderr, flush=True)
+
+
+def kernel_digest() -> str:
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        with open(f, "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(workload: str):
+    """HBM bytes per launch from the committed rocprofv3 counter runs, if they
+    were taken on the current kernel source; else None."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            rec = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if rec.get("workload") != workload or rec.get("kernel_digest") != kernel_digest():
+        return None
+    return rec.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(data, budget_s: float):
+    """The oracle, as it is, on ops in encode order until the time budget is
+    spent (at least one op); returns the baseline record."""
+    import oracle
+    import synth
+    done_bytes, t_used, ops_done = 0, 0.0, 0
+    for op, w, x in data:
+        t0 = time.perf_counter()
+        oracle.gemv(w, x, op.n, op.p)
+        t_used += time.perf_counter() - t0
+        done_bytes += synth.workload_bytes([op])
+        ops_done += 1
+        if t_used >= budget_s:
+            break
+    return {"value": round(done_bytes / t_used / 1e9, 4), "unit": "GB/s", "cores": 1,
+            "kind": "oracle",
+            "sample": "first %d of %d ops of the workload in encode order (%.1f MB, %.1f s), "
+                      "serial float64 C oracle, one host thread" % (
+                          ops_done, len(data), done_bytes / 1e6, t_used)}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="7b_chain")
+    ap.add_argument("--cpu-budget", type=float, default=12.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-modes", action="store_true",
+                    help="skip the per-op / eager / sync-each comparison")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: the matvec chain runs on a single "
+              "MI355X (rows shard across GPUs without exchange, but no multi-GPU "
+              "path is built here); run with --gpus 1", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import q8_block_quantized_gemv_amd as q8
+    import synth
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    torch.cuda.set_device(0)
+    ops_shape = synth.WORKLOADS[args.workload]
+    nbytes = synth.workload_bytes(ops_shape)
+
+    say("generating %s (%d ops, %.3f GB per token)" % (args.workload, len(ops_shape), nbytes / 1e9))
+    t0 = time.time()
+    data = synth.generate(args.workload)
+    say("generated in %.1f s; uploading" % (time.time() - t0))
+    dev_ops = []
+    for op, w, x in data:
+        dev_ops.append((torch.from_numpy(x).to("cuda"),
+                        torch.from_numpy(w.reshape(op.p, -1)).to("cuda"),
+                        torch.empty(op.p, dtype=torch.float32, device="cuda")))
+    torch.cuda.synchronize()
+    say("resident in HBM: %.2f GB" % (torch.cuda.memory_allocated() / 1e9))
+
+    chain = q8.Chain(dev_ops, fuse=True)
+    stream = torch.cuda.current_stream()
+
+    def time_steps(run, k):
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record(stream)
+        for _ in range(k):
+            run()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / 1e3  # seconds
+
+    run_graph = lambda: chain.run(q8.MODE_GRAPH, stream)
+    cold = time_steps(run_graph, 1)
+    for _ in range(args.warmup):
+        run_graph()
+    torch.cuda.synchronize()
+    say("warm; timing %d steps" % args.steps)
+
+    # the timed region: K graph replays between a synchronize on each side
+    torch.cuda.synchronize()
+    t_wall0 = time.perf_counter()
+    sec = time_steps(run_graph, args.steps)
+    t_wall = time.perf_counter() - t_wall0
+    per_step = sec / args.steps
+    value = nbytes * args.steps / sec / 1e9
+    say("fused graph: %.1f us/token, %.1f GB/s (%.1f%% of 8 TB/s); wall %.3f s" % (
+        per_step * 1e6, value, 100 * value / HBM_PEAK_GBS, t_wall))
+
+    # per-launch view of the dominant kernel: the fused chain is one kernel,
+    # so a replay's device time is that kernel's launch duration
+    launches = chain.launches
+    reps = []
+    for _ in range(5):
+        reps.append(time_steps(run_graph, max(1, args.steps // 5)) / max(1, args.steps // 5))
+    kernel_s = float(np.median(reps)) / launches
+    achieved = nbytes / launches / kernel_s / 1e9
+    roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
+                "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                "traffic": measured_traffic(args.workload),
+                "kernel": "k_q8_gemv_fused", "launches_per_step": launches,
+                "algorithmic_bytes_per_launch": nbytes // launches}
+
+    modes = {"fused_graph_us": round(per_step * 1e6, 2), "fused_graph_cold_first_us": round(cold * 1e6, 2)}
+    if not args.no_modes:
+        k = max(3, args.steps // 10)
+        modes["fused_eager_us"] = round(time_steps(lambda: chain.run(q8.MODE_EAGER, stream), k) / k * 1e6, 2)
+        per_op = q8.Chain(dev_ops, fuse=False)
+        for m, name in ((q8.MODE_GRAPH, "per_op_graph_us"), (q8.MODE_EAGER, "per_op_eager_us"),
+                        (q8.MODE_SYNC_EACH, "per_op_sync_each_us")):
+            per_op.run(m, stream)
+            torch.cuda.synchronize()
+            modes[name] = round(time_steps(lambda: per_op.run(m, stream), k) / k * 1e6, 2)
+            say("%s: %.1f us/token" % (name, modes[name]))
+        per_op.close()
+
+    base = None
+    if not args.no_cpu_baseline:
+        say("timing the CPU oracle (budget %.0f s)" % args.cpu_budget)
+        base = cpu_baseline(data, args.cpu_budget)
+
+    out = {
+        "metric": "Q8_0 GEMV achieved HBM GB/s (% of 8 TB/s); decode-chain matvec us/token",
+        "value": round(value, 2), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(per_step * 1e3, 5),
+        "us_per_token": round(per_step * 1e6, 2),
+        "pct_of_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "f32", "data": "synthetic",
+        "config": {"workload": args.workload, "ops_per_token": len(ops_shape),
+                   "bytes_per_token": nbytes, "mode": "hipGraph replay, fused launch",
+                   "weights": "Q8_0, scale U[0.001,0.02] as f16, quants U{-127..127}",
+                   "activations": "f32 N(0,1), independent per op"},
+        "roofline": roofline,
+        "modes_us_per_token": modes,
+        "cpu_baseline": base,
+    }
+    print(json.dumps(out), flush=True)
+    chain.close()
+
+
+if __name__ == "__main__":
+    main()

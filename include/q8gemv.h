@@ -22,7 +22,9 @@
  *     calls never fall back to another implementation.
  *   - Calls are asynchronous: they enqueue on `stream` and return.  Only
  *     q8_0_decode_chain in Q8_MODE_SYNC_EACH and q8_0_stream_wait block.
- *   - Alignment: w must be 16-byte aligned; x, y, X, Y 4-byte aligned.
+ *   - Alignment: w and x (X) must be 16-byte aligned; y (Y) 4-byte aligned.
+ *     (Rows of X are n floats apart, n a multiple of 32, so every row of an
+ *     aligned X is aligned too.)
  *   - y (Y) must not overlap x (X) or w.
  *   - Sizes: n is a positive multiple of 32 and at most Q8_MAX_N; p is
  *     positive and at most Q8_MAX_P; small-batch m is in 1..Q8_MAX_M.
@@ -65,7 +67,7 @@ enum q8_status {
  * y = W x for one p x n Q8_0 matrix.
  * Argument order follows the page's kernel: (x, w, out, n, p) -- section
  * "Eight kernels", q8_matvec, buffers 0..4.
- *   x : float32[n], device.   w : p * (n/32) * 34 bytes, device, 16-B aligned.
+ *   x : float32[n], device, 16-B aligned.   w : p * (n/32) * 34 bytes, device, 16-B aligned.
  *   y : float32[p], device, written.
  */
 int q8_0_gemv(const float *x, const void *w, float *y, int64_t n, int64_t p,
@@ -88,7 +90,7 @@ int q8_0_gemm_smallm(const float *X, const void *w, float *Y, int64_t m,
  * all of a step's dispatches are encoded once, committed and waited on once).
  */
 typedef struct q8_0_op {
-    const float *x;  /* float32[n] */
+    const float *x;  /* float32[n], 16-B aligned */
     const void *w;   /* Q8_0, p rows of n/32 blocks, 16-B aligned */
     float *y;        /* float32[p] */
     int64_t n;

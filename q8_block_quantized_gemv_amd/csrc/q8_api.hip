@@ -3,6 +3,8 @@
 #include <algorithm>
 #include <chrono>
 #include <cstdint>
+#include <cstdio>
+#include <cstdlib>
 #include <cstring>
 #include <mutex>
 #include <string>
@@ -47,9 +49,9 @@ int validate(const float *x, const void *w, const float *y, int64_t m, int64_t n
         return fail(Q8_ERR_SHAPE, tag + ": p=" + std::to_string(p) + " out of range");
     if (m < 1 || m > Q8_MAX_M)
         return fail(Q8_ERR_SHAPE, tag + ": m=" + std::to_string(m) + " must be in 1..16");
-    if ((uintptr_t)w % 16) return fail(Q8_ERR_ALIGN, tag + ": w must be 16-byte aligned");
-    if ((uintptr_t)x % 4 || (uintptr_t)y % 4)
-        return fail(Q8_ERR_ALIGN, tag + ": x and y must be 4-byte aligned");
+    if ((uintptr_t)w % 16 || (uintptr_t)x % 16)
+        return fail(Q8_ERR_ALIGN, tag + ": w and x must be 16-byte aligned");
+    if ((uintptr_t)y % 4) return fail(Q8_ERR_ALIGN, tag + ": y must be 4-byte aligned");
     const int64_t yb = 4 * m * p;
     if (overlaps(y, yb, x, 4 * m * n)) return fail(Q8_ERR_ALIAS, tag + ": y overlaps x");
     if (overlaps(y, yb, w, w_bytes(n, p))) return fail(Q8_ERR_ALIAS, tag + ": y overlaps w");
@@ -89,25 +91,38 @@ int64_t gcd64(int64_t a, int64_t b) {
     return a;
 }
 
-// Waves that split one row tile's groups.  A standalone launch wants many
-// workgroups; inside a fused chain the other ops fill the GPU, so the choice
-// only has to keep the waves of a workgroup evenly loaded.
-int choose_ks(int64_t gsr, int64_t nsr, bool standalone) {
+// Kernel shape per launch kind.  Q8GEMV_VARIANT=nw<1|2|4>pf<1|2> (read at
+// each planning call) overrides it for A/B measurements.
+Variant pick_variant(bool fused) {
+    Variant v = fused ? Variant{1, 1} : Variant{4, 1};
+    if (const char *e = std::getenv("Q8GEMV_VARIANT")) {
+        int nw = 0, pf = 0;
+        if (std::sscanf(e, "nw%dpf%d", &nw, &pf) == 2 && (nw == 1 || nw == 2 || nw == 4) &&
+            (pf == 1 || pf == 2))
+            v = Variant{nw, pf};
+    }
+    return v;
+}
+
+// Waves that split one row tile's groups (ks <= nw).  A standalone launch
+// wants many workgroups; inside a fused chain the other ops fill the GPU, so
+// the choice only has to keep the waves of a workgroup evenly loaded.
+int choose_ks(int64_t gsr, int64_t nsr, bool standalone, int nw) {
     auto eff = [&](int ks) {
         const int64_t per = (gsr + ks - 1) / ks;
         return (double)gsr / (double)(ks * per);
     };
     if (standalone) {
         for (int ks : {4, 2}) {
-            if (gsr < ks) continue;
-            if (fast_tiles_for(nsr, 1) < 512 || eff(ks) >= 0.95) return ks;
+            if (ks > nw || gsr < ks) continue;
+            if (fast_tiles_for(nsr, 1, nw) < 512 || eff(ks) >= 0.95) return ks;
         }
         return 1;
     }
     int best = 1;
     double be = eff(1);
     for (int ks : {2, 4}) {
-        if (gsr < ks) continue;
+        if (ks > nw || gsr < ks) continue;
         const double e = eff(ks);
         if (e >= 0.95 || e > be + 1e-9) { best = ks; be = e; }
     }
@@ -115,7 +130,7 @@ int choose_ks(int64_t gsr, int64_t nsr, bool standalone) {
 }
 
 OpDesc plan_op(const float *x, const void *w, float *y, int64_t m, int64_t n, int64_t p,
-               bool standalone) {
+               bool standalone, int nw = kWaves) {
     OpDesc d;
     std::memset(&d, 0, sizeof d);
     const int64_t nb = n / kQuants;
@@ -129,8 +144,8 @@ OpDesc plan_op(const float *x, const void *w, float *y, int64_t m, int64_t n, in
     d.nsr = (int32_t)(p / rs);
     d.gsr = (int32_t)(rs * nb / kGroupBlocks);
     d.sr_bytes = rs * nb * kBlockBytes;
-    d.ks = choose_ks(d.gsr, d.nsr, standalone);
-    d.fast_tiles = (int32_t)fast_tiles_for(d.nsr, d.ks);
+    d.ks = choose_ks(d.gsr, d.nsr, standalone, nw);
+    d.fast_tiles = (int32_t)fast_tiles_for(d.nsr, d.ks, nw);
     d.tail_row0 = (int32_t)(d.nsr * rs);
     d.m = (int32_t)m;
     d.x_stride = n;
@@ -138,13 +153,14 @@ OpDesc plan_op(const float *x, const void *w, float *y, int64_t m, int64_t n, in
     return d;
 }
 
-int64_t tiles_of(const OpDesc &d) {
-    return (int64_t)d.fast_tiles + tail_tiles_for((int64_t)d.p - d.tail_row0);
+int64_t tiles_of(const OpDesc &d, int nw = kWaves) {
+    return (int64_t)d.fast_tiles + tail_tiles_for((int64_t)d.p - d.tail_row0, nw);
 }
 
 int gemv_launch(const float *x, const void *w, float *y, int64_t n, int64_t p, hipStream_t s) {
-    const OpDesc d = plan_op(x, w, y, 1, n, p, true);
-    hipError_t e = launch_gemv_single(d, tiles_of(d), s);
+    const Variant v = pick_variant(false);
+    const OpDesc d = plan_op(x, w, y, 1, n, p, true, v.nw);
+    hipError_t e = launch_gemv_single(d, v, tiles_of(d, v.nw), s);
     if (e != hipSuccess) return fail_hip(e, "q8_0_gemv launch");
     return Q8_OK;
 }
@@ -229,6 +245,7 @@ struct q8_0_chain {
     // one entry per kernel launch of a token
     struct Launch {
         bool fused;
+        Variant v;
         OpDesc single;        // per-op launch
         const OpDesc *d_ops;  // fused launch
         const Tile *d_tiles;
@@ -244,8 +261,8 @@ struct q8_0_chain {
 namespace {
 
 hipError_t issue(const q8_0_chain::Launch &L, hipStream_t s) {
-    if (L.fused) return launch_gemv_fused(L.d_ops, L.d_tiles, L.grid, s);
-    return launch_gemv_single(L.single, L.grid, s);
+    if (L.fused) return launch_gemv_fused(L.d_ops, L.d_tiles, L.v, L.grid, s);
+    return launch_gemv_single(L.single, L.v, L.grid, s);
 }
 
 void chain_free(q8_0_chain *c) {
@@ -305,6 +322,7 @@ int q8_0_chain_create(const q8_0_op *ops, int64_t n_ops, uint32_t flags, q8_0_ch
     }
 
     // ---- fused segments: op table + tile schedule in one device block
+    const Variant vf = pick_variant(true), vs = pick_variant(false);
     std::vector<OpDesc> h_ops;
     std::vector<Tile> h_tiles;
     struct SegInfo { size_t op0, tile0; int64_t ntiles; bool fused; };
@@ -319,14 +337,14 @@ int q8_0_chain_create(const q8_0_op *ops, int64_t n_ops, uint32_t flags, q8_0_ch
             std::vector<Item> items;
             for (int64_t i = sg.first; i < sg.second; ++i) {
                 const q8_0_op &o = ops[i];
-                OpDesc d = plan_op(o.x, o.w, o.y, 1, o.n, o.p, false);
+                OpDesc d = plan_op(o.x, o.w, o.y, 1, o.n, o.p, false, vf.nw);
                 const uint32_t oi = (uint32_t)(h_ops.size() - si.op0);
                 h_ops.push_back(d);
-                const int64_t fb = (int64_t)(kWaves / d.ks) * kWave * d.sr_bytes;
+                const int64_t fb = (int64_t)(vf.nw / d.ks) * kWave * d.sr_bytes;
                 for (int64_t t = 0; t < d.fast_tiles; ++t) items.push_back({{oi, (uint32_t)t}, fb});
-                const int64_t tt = tail_tiles_for((int64_t)d.p - d.tail_row0);
+                const int64_t tt = tail_tiles_for((int64_t)d.p - d.tail_row0, vf.nw);
                 for (int64_t t = 0; t < tt; ++t)
-                    items.push_back({{oi, (uint32_t)t | kTailBit}, kTailRowsPerTile * d.nb * kBlockBytes});
+                    items.push_back({{oi, (uint32_t)t | kTailBit}, (int64_t)vf.nw * d.nb * kBlockBytes});
             }
             std::stable_sort(items.begin(), items.end(),
                              [](const Item &a, const Item &b) { return a.bytes > b.bytes; });
@@ -353,14 +371,16 @@ int q8_0_chain_create(const q8_0_op *ops, int64_t n_ops, uint32_t flags, q8_0_ch
         std::memset(&L, 0, sizeof L);
         if (info[k].fused) {
             L.fused = true;
+            L.v = vf;
             L.d_ops = d_ops + info[k].op0;
             L.d_tiles = d_tiles + info[k].tile0;
             L.grid = info[k].ntiles;
         } else {
             const q8_0_op &o = ops[segs[k].first];
             L.fused = false;
-            L.single = plan_op(o.x, o.w, o.y, 1, o.n, o.p, true);
-            L.grid = tiles_of(L.single);
+            L.v = vs;
+            L.single = plan_op(o.x, o.w, o.y, 1, o.n, o.p, true, vs.nw);
+            L.grid = tiles_of(L.single, vs.nw);
         }
         c->launches.push_back(L);
     }

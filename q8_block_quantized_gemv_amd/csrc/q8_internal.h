@@ -21,7 +21,12 @@ constexpr int kWave = 64;
 constexpr int kWaves = 4;                 // waves per workgroup
 constexpr int kThreads = kWave * kWaves;  // 256
 constexpr int kBufs = 2;                  // LDS stages per wave
-constexpr int kStageBytes = kWave * kGroupBytes;  // one group of 64 lanes: 17408 B
+// One stage holds a group of 64 lanes (17408 B of W) and, for the matvec,
+// the group's 256 x values (1 KB), which arrive by the same direct loads.
+constexpr int kStageW = kWave * kGroupBytes;       // 17408
+constexpr int kStageX = kGroupBlocks * kQuants * 4;  // 1024
+constexpr int kStageBytes = kStageW + kStageX;     // 18432
+constexpr int kStageBytesM = kStageW;              // small batch: W only
 
 // One matvec (or small-batch product) as the kernels see it.  A "super-row"
 // is `rs` consecutive rows whose bytes, taken together, are a whole number of
@@ -53,21 +58,28 @@ struct Tile {
     uint32_t tile;  // tile within the op; kTailBit set: tail tile
 };
 constexpr uint32_t kTailBit = 0x80000000u;
-constexpr int kTailRowsPerTile = kWaves;  // one wave per tail row
 
-// Fast tiles cover (kWaves / ks) * 64 super-rows each.
-inline int64_t fast_tiles_for(int64_t nsr, int ks) {
-    const int64_t per = (int64_t)(kWaves / ks) * kWave;
+// Matvec kernel shape: waves per workgroup (1, 2 or 4) and groups each wave
+// keeps in flight ahead of the one it computes (1 or 2).
+struct Variant {
+    int nw;
+    int pf;
+};
+
+// Fast tiles cover (nw / ks) * 64 super-rows each.
+inline int64_t fast_tiles_for(int64_t nsr, int ks, int nw = kWaves) {
+    const int64_t per = (int64_t)(nw / ks) * kWave;
     return (nsr + per - 1) / per;
 }
-inline int64_t tail_tiles_for(int64_t tail_rows) {
-    return (tail_rows + kTailRowsPerTile - 1) / kTailRowsPerTile;
+// Tail tiles take one row per wave.
+inline int64_t tail_tiles_for(int64_t tail_rows, int nw = kWaves) {
+    return (tail_rows + nw - 1) / nw;
 }
 
 // Kernel launchers (q8_kernels.hip).  All return the hipError_t of the launch.
-hipError_t launch_gemv_single(const OpDesc &op, int64_t grid, hipStream_t s);
-hipError_t launch_gemv_fused(const OpDesc *d_ops, const Tile *d_tiles, int64_t grid,
-                             hipStream_t s);
+hipError_t launch_gemv_single(const OpDesc &op, const Variant &v, int64_t grid, hipStream_t s);
+hipError_t launch_gemv_fused(const OpDesc *d_ops, const Tile *d_tiles, const Variant &v,
+                             int64_t grid, hipStream_t s);
 hipError_t launch_gemm_single(const OpDesc &op, int mpad, int64_t grid, hipStream_t s);
 
 }  // namespace q8

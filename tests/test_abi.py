@@ -58,9 +58,11 @@ X, W, Y = 0x10000000, 0x20000000, 0x30000000
     ((X, W, Y, 64, -1), -2),
     ((X, W, Y, 64, 1 << 31), -2),      # p too large
     ((X, W + 8, Y, 64, 4), -3),        # w not 16-byte aligned
-    ((X + 2, W, Y, 64, 4), -3),        # x not 4-byte aligned
+    ((X + 2, W, Y, 64, 4), -3),        # x not 16-byte aligned
+    ((X + 4, W, Y, 64, 4), -3),
     ((X, W, Y + 1, 64, 4), -3),
     ((X, W, X + 16, 64, 4), -4),       # y overlaps x
+    ((X, W, X - 4, 64, 4), -4),        # y's last element is x[0]
     ((X, W, W + 68, 64, 4), -4),       # y overlaps w
 ])
 def test_gemv_validation(q8, args, code):
