@@ -90,6 +90,9 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-modes", action="store_true",
                     help="skip the per-op / eager / sync-each comparison")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="instead of the bench: copy MIB MiB device-to-device 5 times "
+                         "(the known-size kernel that scales the HBM byte counters)")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -108,6 +111,16 @@ def main():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
     torch.cuda.set_device(0)
+    if args.copy_calibration:
+        nb = args.copy_calibration << 20
+        src = torch.empty(nb, dtype=torch.uint8, device="cuda").fill_(1)
+        dst = torch.empty(nb, dtype=torch.uint8, device="cuda")
+        torch.cuda.synchronize()
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_bytes_per_launch": nb, "launches": 5}), flush=True)
+        return
     ops_shape = synth.WORKLOADS[args.workload]
     nbytes = synth.workload_bytes(ops_shape)
 
