@@ -80,6 +80,55 @@ def cpu_baseline(data, budget_s: float):
                           ops_done, len(data), done_bytes / 1e6, t_used)}
 
 
+def bench_smallm(args, q8, synth, torch, np):
+    """Small-batch products at the 7B shapes.  Each case cycles through enough
+    distinct copies of W (>= 1 GiB in all) that no copy is still cached when it
+    comes round again.  The kernel runs on bfloat16 matrix cores with x split
+    into three exact parts and the batch padded to 16 rows: 3 * 16 * n * p
+    multiply-adds.  Reported against max(HBM time, MFMA time)."""
+    MFMA_BF16_FLOPS = 2.5e15                # MI355X dense bf16
+    stream = torch.cuda.current_stream()
+    cases = []
+    for shape in synth.SMALLM_SHAPES:
+        w, _ = synth.generate_smallm(shape, 2)
+        wbytes = w.size
+        copies = max(1, -(-(1 << 30) // wbytes))
+        say("smallm %s: %d copies of %.1f MB" % (shape.name, copies, wbytes / 1e6))
+        wd = [torch.from_numpy(w.reshape(shape.p, -1)).to("cuda") for _ in range(copies)]
+        for m in synth.SMALLM_M:
+            _, X = synth.generate_smallm(shape, m)
+            Xd = torch.from_numpy(X).to("cuda")
+            Y = torch.empty((m, shape.p), dtype=torch.float32, device="cuda")
+            for i in range(copies):
+                q8.gemm_smallm(Xd, wd[i], Y, stream)
+            k = max(copies * 4, 20)
+            torch.cuda.synchronize()
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            for i in range(k):
+                q8.gemm_smallm(Xd, wd[i % copies], Y, stream)
+            e1.record(stream)
+            torch.cuda.synchronize()
+            t = e0.elapsed_time(e1) / 1e3 / k
+            nbytes = synth.workload_bytes([shape], m)
+            t_hbm = nbytes / 8e12
+            t_mfma = 2 * 3 * 16 * shape.n * shape.p / MFMA_BF16_FLOPS
+            cases.append({"shape": shape.name, "n": shape.n, "p": shape.p, "m": m,
+                          "us": round(t * 1e6, 2), "GB_s": round(nbytes / t / 1e9, 1),
+                          "bound": "hbm" if t_hbm >= t_mfma else "mfma",
+                          "frac_of_roof": round(max(t_hbm, t_mfma) / t, 4)})
+            say("smallm %s m=%d: %.1f us, %.0f GB/s, %.1f%% of the %s roof" % (
+                shape.name, m, t * 1e6, nbytes / t / 1e9, 100 * max(t_hbm, t_mfma) / t,
+                cases[-1]["bound"]))
+        del wd
+        torch.cuda.empty_cache()
+    return {"metric": "q8_0_gemm_smallm at 7B shapes", "unit": "us", "n_gpus": 1,
+            "dtype": "f32", "data": "synthetic",
+            "roof_note": "HBM 8 TB/s; bf16 MFMA 2.5 PFLOP/s dense (3 exact x parts, 16 padded rows)",
+            "cases": cases}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -90,6 +139,9 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-modes", action="store_true",
                     help="skip the per-op / eager / sync-each comparison")
+    ap.add_argument("--smallm", action="store_true",
+                    help="instead of the chain: time q8_0_gemm_smallm at the 7B shapes, "
+                         "m in {2,4,8,16}, rotating weight copies past the 256 MB cache")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="instead of the bench: copy MIB MiB device-to-device 5 times "
                          "(the known-size kernel that scales the HBM byte counters)")
@@ -120,6 +172,9 @@ def main():
             dst.copy_(src)
         torch.cuda.synchronize()
         print(json.dumps({"copy_bytes_per_launch": nb, "launches": 5}), flush=True)
+        return
+    if args.smallm:
+        print(json.dumps(bench_smallm(args, q8, synth, torch, np)), flush=True)
         return
     ops_shape = synth.WORKLOADS[args.workload]
     nbytes = synth.workload_bytes(ops_shape)

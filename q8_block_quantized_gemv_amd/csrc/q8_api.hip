@@ -6,6 +6,7 @@
 #include <cstdio>
 #include <cstdlib>
 #include <cstring>
+#include <map>
 #include <mutex>
 #include <string>
 #include <thread>
@@ -153,6 +154,62 @@ OpDesc plan_op(const float *x, const void *w, float *y, int64_t m, int64_t n, in
     return d;
 }
 
+int cu_count(int dev) {
+    static std::mutex mu;
+    static std::vector<int> cus;
+    std::lock_guard<std::mutex> lk(mu);
+    if ((int)cus.size() <= dev) cus.resize(dev + 1, 0);
+    if (cus[dev] <= 0) {
+        int v = 0;
+        if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || v <= 0)
+            v = 256;
+        cus[dev] = v;
+    }
+    return cus[dev];
+}
+
+// Split-K workspace of the small-batch product, one per (device, stream):
+// calls on one stream run in order and may share it; calls on different
+// streams get different ones.  Grown on demand (hipFree synchronizes the
+// device first), kept until the process ends.  The arrival counters are
+// zeroed once here and left at zero by every launch.
+struct Workspace {
+    float *ws = nullptr;
+    size_t ws_bytes = 0;
+    uint32_t *cnt = nullptr;
+    size_t cnt_n = 0;
+};
+
+int workspace_for(int dev, hipStream_t s, size_t ws_bytes, size_t cnt_n, float **ws_out,
+                  uint32_t **cnt_out) {
+    static std::mutex mu;
+    static std::map<std::pair<int, hipStream_t>, Workspace> pool;
+    std::lock_guard<std::mutex> lk(mu);
+    Workspace &W = pool[{dev, s}];
+    hipError_t e;
+    if (W.ws_bytes < ws_bytes) {
+        if (W.ws && (e = hipFree(W.ws)) != hipSuccess) return fail_hip(e, "hipFree");
+        W.ws = nullptr;
+        W.ws_bytes = 0;
+        if ((e = hipMalloc(&W.ws, ws_bytes)) != hipSuccess) return fail_hip(e, "workspace hipMalloc");
+        W.ws_bytes = ws_bytes;
+    }
+    if (W.cnt_n < cnt_n) {
+        if (W.cnt && (e = hipFree(W.cnt)) != hipSuccess) return fail_hip(e, "hipFree");
+        W.cnt = nullptr;
+        W.cnt_n = 0;
+        if ((e = hipMalloc(&W.cnt, cnt_n * sizeof(uint32_t))) != hipSuccess)
+            return fail_hip(e, "counter hipMalloc");
+        if ((e = hipMemset(W.cnt, 0, cnt_n * sizeof(uint32_t))) != hipSuccess ||
+            (e = hipDeviceSynchronize()) != hipSuccess)
+            return fail_hip(e, "counter hipMemset");
+        W.cnt_n = cnt_n;
+    }
+    *ws_out = W.ws;
+    *cnt_out = W.cnt;
+    return Q8_OK;
+}
+
 int64_t tiles_of(const OpDesc &d, int nw = kWaves) {
     return (int64_t)d.fast_tiles + tail_tiles_for((int64_t)d.p - d.tail_row0, nw);
 }
@@ -209,12 +266,37 @@ int q8_0_gemm_smallm(const float *X, const void *w, float *Y, int64_t m, int64_t
             if ((rc = gemv_launch(X + i * n, w, Y + i * p, n, p, s))) return rc;
         return Q8_OK;
     }
-    int mpad = 2;
-    while (mpad < m) mpad *= 2;
-    OpDesc d = plan_op(X, w, Y, m, n, p, true);
-    d.ks = 1;  // the small-batch kernel keeps each row tile in one wave
-    d.fast_tiles = (int32_t)fast_tiles_for(d.nsr, 1);
-    hipError_t e = launch_gemm_single(d, mpad, tiles_of(d), s);
+    GemmDesc d;
+    std::memset(&d, 0, sizeof d);
+    d.X = X;
+    d.w = (const uint8_t *)w;
+    d.Y = Y;
+    d.n = (int32_t)n;
+    d.nb = (int32_t)nb;
+    d.p = (int32_t)p;
+    d.m = (int32_t)m;
+    d.rs = (int32_t)rs;
+    d.nsr = (int32_t)(p / rs);
+    d.gsr = (int32_t)(rs * nb / kGroupBlocks);
+    d.sr_bytes = rs * nb * kBlockBytes;
+    d.row_tiles = (int32_t)((d.nsr + kWave - 1) / kWave);
+    d.tail_row0 = d.nsr * (int32_t)rs;
+    // Split K when there are too few row tiles to give every CU about four
+    // one-wave workgroups, keeping at least three groups per part.
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return fail_hip(e, "hipGetDevice");
+    const int64_t target = 4 * (int64_t)cu_count(dev);
+    int64_t parts = d.row_tiles > 0 ? (target + d.row_tiles - 1) / d.row_tiles : 1;
+    parts = std::max<int64_t>(1, std::min<int64_t>(parts, d.gsr / 3));
+    d.parts = (int32_t)parts;
+    d.fast_wgs = d.row_tiles * d.parts;
+    if (d.parts > 1) {
+        const size_t ws_bytes = (size_t)d.fast_wgs * 16 * kWave * rs * sizeof(float);
+        if ((rc = workspace_for(dev, s, ws_bytes, (size_t)d.row_tiles, &d.ws, &d.cnt))) return rc;
+    }
+    const int64_t grid = (int64_t)d.fast_wgs + (p - d.tail_row0);
+    e = launch_gemm_mfma(d, grid, s);
     if (e != hipSuccess) return fail_hip(e, "q8_0_gemm_smallm launch");
     return Q8_OK;
 }

@@ -52,6 +52,27 @@ struct OpDesc {
     int32_t pad_;
 };
 
+// A small-batch product (2 <= m <= 16, rows of 1 or 2 per super-row) on the
+// matrix cores.  Workgroups are one wave: row tile rt = 64 super-rows, K part
+// `part` of `parts` (groups split evenly).  With parts > 1 the partial sums
+// go through the workspace `ws` (parts * 16 * 64 * rs floats per row tile)
+// and the per-row-tile arrival counters `cnt` (all zero between launches).
+struct GemmDesc {
+    const float *X;
+    const uint8_t *w;
+    float *Y;
+    float *ws;
+    uint32_t *cnt;
+    int64_t sr_bytes;
+    int32_t n, nb, p, m;
+    int32_t rs, nsr, gsr;
+    int32_t parts;
+    int32_t row_tiles;   // ceil(nsr / 64)
+    int32_t fast_wgs;    // row_tiles * parts; the tail rows follow, one per workgroup
+    int32_t tail_row0;
+    int32_t pad_;
+};
+
 // One workgroup's work in a fused launch.
 struct Tile {
     uint32_t op;    // index into the op table
@@ -80,6 +101,6 @@ inline int64_t tail_tiles_for(int64_t tail_rows, int nw = kWaves) {
 hipError_t launch_gemv_single(const OpDesc &op, const Variant &v, int64_t grid, hipStream_t s);
 hipError_t launch_gemv_fused(const OpDesc *d_ops, const Tile *d_tiles, const Variant &v,
                              int64_t grid, hipStream_t s);
-hipError_t launch_gemm_single(const OpDesc &op, int mpad, int64_t grid, hipStream_t s);
+hipError_t launch_gemm_mfma(const GemmDesc &d, int64_t grid, hipStream_t s);
 
 }  // namespace q8

@@ -38,14 +38,7 @@
 namespace q8 {
 namespace {
 
-typedef __attribute__((address_space(3))) void LdsVoid;
-// x (X) is read-only for a kernel's lifetime (outputs never overlap inputs
-// and dependent ops never share a launch), so it is read through the
-// constant address space: wave-uniform reads then become scalar loads.
-typedef const __attribute__((address_space(4))) float CFloat;
 typedef const __attribute__((address_space(1))) uint16_t GHalf;
-
-__device__ __forceinline__ CFloat *cptr(const float *p) { return (CFloat *)p; }
 
 __device__ __forceinline__ int lane_id() { return threadIdx.x & (kWave - 1); }
 __device__ __forceinline__ int wave_id() {
@@ -83,24 +76,6 @@ __device__ __forceinline__ void block_terms(const uint32_t (&D)[68], const float
     s = (a0 + a1) + (a2 + a3);
 }
 
-// The 32 quants of block K as floats.
-template <int K>
-__device__ __forceinline__ void block_quants(const uint32_t (&D)[68], float (&qf)[kQuants],
-                                             float &d) {
-    constexpr int sb = K * kBlockBytes;
-    d = half_to_float(D[sb >> 2] >> ((sb & 3) * 8));
-#pragma unroll
-    for (int j = 0; j < kQuants; ++j) qf[j] = quant(D, sb + 2 + j);
-}
-
-// s_waitcnt vmcnt(N), leaving expcnt and lgkmcnt unconstrained (gfx9
-// encoding: vmcnt in bits 3:0 and 15:14, expcnt 6:4, lgkmcnt 11:8).
-template <int N>
-__device__ __forceinline__ void wait_vm() {
-    static_assert(N >= 0 && N < 64, "vmcnt is 6 bits");
-    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
-}
-__device__ __forceinline__ void wait_vm0() { wait_vm<0>(); }
 // direct loads per group of the matvec: 17 of W and one of x
 constexpr int kLoadsPerGroup = kGroupChunks + 1;
 
@@ -119,15 +94,6 @@ __device__ __forceinline__ void chunk_offsets(uint32_t (&off)[kGroupChunks], int
         s = s < last ? s : last;
         off[i] = (uint32_t)((int64_t)s * sr_bytes + 16 * c);
     }
-}
-
-// Issue the 17 direct HBM -> LDS loads of one group into stage `st`.
-__device__ __forceinline__ void dma_group(const uint8_t *g, const uint32_t (&off)[kGroupChunks],
-                                          uint8_t *st) {
-#pragma unroll
-    for (int i = 0; i < kGroupChunks; ++i)
-        __builtin_amdgcn_global_load_lds((const void *)(g + off[i]),
-                                         (LdsVoid *)(st + kWave * 16 * i), 16, 0, 0);
 }
 
 // Where lane `lane` finds its 16 bytes of the x slice of group kk: floats
@@ -328,92 +294,227 @@ __device__ void fast_tile(const OpDesc &op, uint32_t tile, uint8_t *stage) {
 }
 
 // ---------------------------------------------------------------- m > 1
-// Small batch: the same stream of W, M activation rows (rows of X past
-// op.m are clamped to the last one and never stored).
-template <int M, int RS>
-__device__ __forceinline__ void group_dot_m(const uint32_t (&D)[68], const OpDesc &op, int kk,
-                                            float (&acc)[M][kSlots][RS]) {
-    const int slot = kk & (kSlots - 1);
-    const int bp = kk * kGroupBlocks;
-    int r = (RS == 1) ? 0 : bp / op.nb;
-    int cb = bp - r * op.nb;
-    float sub[M];
-#pragma unroll
-    for (int i = 0; i < M; ++i) sub[i] = 0.f;
-    float qf[kQuants];
-    float d;
-#define Q8_STEPM(K)                                                              \
-    block_quants<K>(D, qf, d);                                                   \
-    _Pragma("unroll") for (int i = 0; i < M; ++i) {                              \
-        const int xi = i < op.m ? i : op.m - 1;                                  \
-        CFloat *xb = cptr(op.x) + (int64_t)xi * op.x_stride + (int64_t)cb * kQuants; \
-        float a0 = 0.f, a1 = 0.f, a2 = 0.f, a3 = 0.f;                            \
-        _Pragma("unroll") for (int j = 0; j < kQuants; j += 4) {                 \
-            a0 = fmaf(qf[j + 0], xb[j + 0], a0);                                 \
-            a1 = fmaf(qf[j + 1], xb[j + 1], a1);                                 \
-            a2 = fmaf(qf[j + 2], xb[j + 2], a2);                                 \
-            a3 = fmaf(qf[j + 3], xb[j + 3], a3);                                 \
-        }                                                                        \
-        sub[i] = fmaf(d, (a0 + a1) + (a2 + a3), sub[i]);                         \
-    }                                                                            \
-    if (++cb == op.nb) {                                                         \
-        _Pragma("unroll") for (int i = 0; i < M; ++i) {                          \
-            flush_row<RS>(acc[i], slot, r, sub[i]); sub[i] = 0.f;                \
-        }                                                                        \
-        cb = 0; ++r;                                                             \
-    }
-    Q8_STEPM(0) Q8_STEPM(1) Q8_STEPM(2) Q8_STEPM(3)
-    Q8_STEPM(4) Q8_STEPM(5) Q8_STEPM(6) Q8_STEPM(7)
-#undef Q8_STEPM
-#pragma unroll
-    for (int i = 0; i < M; ++i) flush_row<RS>(acc[i], slot, r, sub[i]);
+// Small batch, Y = X W^T for m <= 16 rows of X, on the matrix cores.
+//
+// At m = 16 the contraction needs 16 FMAs per weight: over the FP32 vector
+// units that is ~3x slower than HBM delivers weights, so it runs on
+// v_mfma_f32_16x16x32_bf16 instead, exactly:
+//   * A (16 x 32) is X: row i = activation row, k = column in the block.
+//     Each x is split into three bfloat16 parts, h + m + l == x exactly
+//     (8 + 8 + 8 significant bits; non-finite x keeps only h).
+//   * B (32 x 16) is the block's int8 quants, which bfloat16 holds exactly;
+//     column j = weight row.  Every product is exact in float32.
+//   * C (16 x 16) collects one block; the lane that holds C[i][j] also read
+//     the quants of row j, so it scales its four C values by that row's
+//     block scale and adds them to per-group subtotals.
+// Lane layout (gfx950, checked on the device): A[i][k] is element k%8 of
+// lane i + 16*(k/8), B[k][j] element k%8 of lane j + 16*(k/8), and C[i][j]
+// element i%4 of lane j + 16*(i/4).
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ float bf16_as_float(__bf16 h) {
+    return __builtin_bit_cast(float, (uint32_t)__builtin_bit_cast(uint16_t, h) << 16);
 }
 
-template <int M, int RS>
-__device__ void fast_tile_m(const OpDesc &op, uint32_t tile, uint8_t *stage) {
-    const int lane = lane_id();
-    const int wave = wave_id();
-    const int64_t sr0 = ((int64_t)tile * kWaves + wave) * kWave;  // no K split
-    const int nsr = op.nsr;
-    uint8_t *st0 = stage + (size_t)wave * (kBufs * kStageBytesM);
-    if (sr0 >= nsr) return;
-
-    float acc[M][kSlots][RS];
+// x = h + m + l exactly, each part bfloat16 (round to nearest even).
+__device__ __forceinline__ void split3(const float (&x)[8], bf16x8 &h, bf16x8 &m, bf16x8 &l) {
 #pragma unroll
-    for (int i = 0; i < M; ++i)
-#pragma unroll
-        for (int q = 0; q < kSlots; ++q)
-#pragma unroll
-            for (int k = 0; k < RS; ++k) acc[i][q][k] = 0.f;
-
-    const int G = op.gsr;
-    const int64_t srb = op.sr_bytes;
-    const uint8_t *wt = op.w + sr0 * srb;
-    const int last = (int)min((int64_t)nsr - 1 - sr0, (int64_t)kWave - 1);
-    uint32_t off[kGroupChunks];
-    chunk_offsets(off, lane, last, srb);
-    dma_group(wt, off, st0);
-    for (int t = 0; t < G; ++t) {
-        uint8_t *cur = st0 + (t & 1) * kStageBytesM;
-        uint32_t D[68];
-        wait_vm0();
-        read_group(cur, lane, D);
-        if (t + 1 < G)
-            dma_group(wt + (int64_t)(t + 1) * kGroupBytes, off, st0 + ((t + 1) & 1) * kStageBytesM);
-        group_dot_m<M, RS>(D, op, t, acc);
+    for (int e = 0; e < 8; ++e) {
+        const __bf16 hh = (__bf16)x[e];
+        float r = x[e] - bf16_as_float(hh);
+        r = __builtin_isfinite(x[e]) ? r : 0.f;
+        const __bf16 mm = (__bf16)r;
+        const float r2 = r - bf16_as_float(mm);
+        h[e] = hh;
+        m[e] = mm;
+        l[e] = (__bf16)r2;
     }
-    if (sr0 + lane < nsr) {
-        const int64_t row0 = (sr0 + lane) * RS;
+}
+
+// The 8 quants of block K of super-row s that lane group g (= lane / 16)
+// feeds to the matrix core: bytes 2 + 8g .. 9 + 8g of the block, as bf16.
+template <int K>
+__device__ __forceinline__ bf16x8 quants_bf16(const uint8_t *grp, int g) {
+    constexpr int q0 = K * kBlockBytes + 2;   // first quant byte of the block
+    uint32_t w0, w1;
+    if constexpr ((q0 & 3) == 0) {
+        const uint32_t *p = reinterpret_cast<const uint32_t *>(grp + q0 + 8 * g);
+        w0 = p[0];
+        w1 = p[1];
+    } else {   // 2 bytes past a dword boundary
+        const uint32_t *p = reinterpret_cast<const uint32_t *>(grp + q0 - 2 + 8 * g);
+        const uint32_t a0 = p[0], a1 = p[1], a2 = p[2];
+        w0 = __builtin_amdgcn_alignbyte(a1, a0, 2);
+        w1 = __builtin_amdgcn_alignbyte(a2, a1, 2);
+    }
+    bf16x8 b;
 #pragma unroll
-        for (int i = 0; i < M; ++i) {
-            if (i < op.m) {
-                float *yr = op.y + (int64_t)i * op.y_stride + row0;
+    for (int e = 0; e < 4; ++e) {
+        b[e] = (__bf16)(float)(int8_t)(w0 >> (8 * e));
+        b[4 + e] = (__bf16)(float)(int8_t)(w1 >> (8 * e));
+    }
+    return b;
+}
+
+// 16 B of X row i for the lane's 8 columns of block K of group kk.
+template <int RS>
+__device__ __forceinline__ void load_x_frag(const GemmDesc &d, int kk, int i, int g,
+                                            float (&xf)[8][8]) {
+    const bool live = i < d.m;
+    const float *row = d.X + (int64_t)(live ? i : 0) * d.n;
 #pragma unroll
-                for (int k = 0; k < RS; ++k)
-                    yr[k] = combine_slots(acc[i][0][k], acc[i][1][k], acc[i][2][k], acc[i][3][k]);
-            }
+    for (int K = 0; K < kGroupBlocks; ++K) {
+        int b = kk * kGroupBlocks + K;
+        if (RS > 1) b %= d.nb;
+        const float4 *src = reinterpret_cast<const float4 *>(row + (int64_t)b * kQuants + 8 * g);
+        float4 v0 = make_float4(0.f, 0.f, 0.f, 0.f), v1 = v0;
+        if (live) {
+            v0 = src[0];
+            v1 = src[1];
         }
+        xf[K][0] = v0.x; xf[K][1] = v0.y; xf[K][2] = v0.z; xf[K][3] = v0.w;
+        xf[K][4] = v1.x; xf[K][5] = v1.y; xf[K][6] = v1.z; xf[K][7] = v1.w;
     }
+}
+
+template <int RS>
+__device__ __forceinline__ void flush_tile(f32x4 (&acc)[4][RS], f32x4 (&sub)[4], int r) {
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+#pragma unroll
+        for (int k = 0; k < RS; ++k)
+            if (k == r) acc[t][k] += sub[t];
+        sub[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+}
+
+// One group of the wave's 64 super-rows (4 MFMA tiles of 16), all blocks.
+template <int RS>
+__device__ __forceinline__ void group_mfma(const uint8_t *stage, const float (&xf)[8][8],
+                                           const GemmDesc &d, int kk, int lane,
+                                           f32x4 (&acc)[4][RS]) {
+    const int j = lane & 15, g = lane >> 4;
+    f32x4 sub[4];
+#pragma unroll
+    for (int t = 0; t < 4; ++t) sub[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+    int r = 0, cb = kk * kGroupBlocks;
+    if (RS > 1) { r = cb / d.nb; cb -= r * d.nb; }
+#define Q8_MSTEP(K)                                                                     \
+    {                                                                                   \
+        bf16x8 ah, am, al;                                                              \
+        split3(xf[K], ah, am, al);                                                      \
+        _Pragma("unroll") for (int t = 0; t < 4; ++t) {                                 \
+            const uint8_t *grp = stage + kGroupBytes * (16 * t + j);                    \
+            const float dsc = half_to_float(                                            \
+                *reinterpret_cast<const uint16_t *>(grp + (K) * kBlockBytes));          \
+            const bf16x8 bq = quants_bf16<K>(grp, g);                                   \
+            f32x4 c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, bq, f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0); \
+            c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(am, bq, c, 0, 0, 0);            \
+            c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(al, bq, c, 0, 0, 0);            \
+            sub[t] += dsc * c;                                                          \
+        }                                                                               \
+        if (RS > 1 && ++cb == d.nb) { flush_tile<RS>(acc, sub, r); cb = 0; ++r; }      \
+    }
+    Q8_MSTEP(0) Q8_MSTEP(1) Q8_MSTEP(2) Q8_MSTEP(3)
+    Q8_MSTEP(4) Q8_MSTEP(5) Q8_MSTEP(6) Q8_MSTEP(7)
+#undef Q8_MSTEP
+    flush_tile<RS>(acc, sub, RS == 1 ? 0 : r);
+}
+
+// One workgroup (one wave): 64 super-rows x groups [g0, g1) of K part `part`.
+// With d.parts > 1 the partial sums go to the workspace and the last part of
+// the row tile to arrive adds the parts in order 0, 1, ... and stores Y.
+template <int RS>
+__device__ void gemm_tile(const GemmDesc &d, int rt, int part, uint8_t *stage) {
+    const int lane = lane_id();
+    const int j = lane & 15, g = lane >> 4, i = lane & 15;
+    const int64_t sr0 = (int64_t)rt * kWave;
+    const int nsr = d.nsr;
+    const int G = d.gsr;
+    const int g0 = (int)((int64_t)part * G / d.parts), g1 = (int)((int64_t)(part + 1) * G / d.parts);
+    const int last = (int)min((int64_t)nsr - 1 - sr0, (int64_t)kWave - 1);
+    const uint8_t *wt = d.w + sr0 * d.sr_bytes;
+    uint32_t off[kGroupChunks];
+    chunk_offsets(off, lane, last, d.sr_bytes);
+
+    f32x4 acc[4][RS];
+#pragma unroll
+    for (int t = 0; t < 4; ++t)
+#pragma unroll
+        for (int k = 0; k < RS; ++k) acc[t][k] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    auto issue_w = [&](int kk, uint8_t *st) {
+        const uint32_t l0 = __builtin_amdgcn_readfirstlane(lds_addr(st));
+        const uint8_t *gb = wt + (int64_t)kk * kGroupBytes;
+#pragma unroll
+        for (int c = 0; c < kGroupChunks; ++c) dma16_s(gb, off[c], l0 + kWave * 16 * c);
+    };
+    float xf[8][8], xn[8][8];
+    if (g0 < g1) {
+        issue_w(g0, stage);
+        load_x_frag<RS>(d, g0, i, g, xn);
+    }
+    for (int kk = g0; kk < g1; ++kk) {
+        uint8_t *cur = stage + ((kk - g0) & 1) * kStageBytesM;
+        // The group's W (asm loads) and X (compiler-visible loads, issued
+        // after them) have landed; the compiler knows this wait.
+        __builtin_amdgcn_s_waitcnt(0x0F70);
+        asm volatile("" ::: "memory");
+#pragma unroll
+        for (int K = 0; K < 8; ++K)
+#pragma unroll
+            for (int e = 0; e < 8; ++e) xf[K][e] = xn[K][e];
+        if (kk + 1 < g1) {
+            issue_w(kk + 1, stage + ((kk + 1 - g0) & 1) * kStageBytesM);
+            load_x_frag<RS>(d, kk + 1, i, g, xn);
+        }
+        group_mfma<RS>(cur, xf, d, kk, lane, acc);
+    }
+
+    // lane holds C[i = 4g + e][super-row 16t + j], row-in-super-row k
+    if (d.parts == 1) {
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+            const int64_t sr = sr0 + 16 * t + j;
+            if (sr >= nsr) continue;
+#pragma unroll
+            for (int k = 0; k < RS; ++k)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int ii = 4 * g + e;
+                    if (ii < d.m) d.Y[(int64_t)ii * d.p + sr * RS + k] = acc[t][k][e];
+                }
+        }
+        return;
+    }
+    // partial tile: ws[(rt * parts + part)][16 rows of X][64 * RS rows of W]
+    float *mine = d.ws + ((int64_t)rt * d.parts + part) * (16 * kWave * RS);
+#pragma unroll
+    for (int t = 0; t < 4; ++t)
+#pragma unroll
+        for (int k = 0; k < RS; ++k)
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                mine[(4 * g + e) * (kWave * RS) + (16 * t + j) * RS + k] = acc[t][k][e];
+    __threadfence();
+    uint32_t prev = 0;
+    if (lane == 0) prev = atomicAdd(d.cnt + rt, 1u);
+    prev = __shfl(prev, 0, kWave);
+    if (prev != (uint32_t)d.parts - 1) return;
+    __threadfence();
+    // last part of this row tile: sum the parts in a fixed order
+    const float *base = d.ws + (int64_t)rt * d.parts * (16 * kWave * RS);
+    for (int idx = lane; idx < 16 * kWave * RS; idx += kWave) {
+        const int ii = idx / (kWave * RS);
+        const int rr = idx - ii * (kWave * RS);
+        const int64_t sr = sr0 + rr / RS;
+        if (ii >= d.m || sr >= nsr) continue;
+        float v = base[idx];
+        for (int q = 1; q < d.parts; ++q) v += base[(int64_t)q * (16 * kWave * RS) + idx];
+        d.Y[(int64_t)ii * d.p + sr0 * RS + rr] = v;
+    }
+    if (lane == 0) atomicExch(d.cnt + rt, 0u);   // ready for the next launch
 }
 
 // ---------------------------------------------------------------- tail rows
@@ -489,17 +590,18 @@ __global__ __launch_bounds__(NW * kWave) void k_q8_gemv_fused(const OpDesc *__re
     run_tile<NW, PF>(op, tl.tile, stage);
 }
 
-template <int M>
-__global__ __launch_bounds__(kThreads) void k_q8_gemm(OpDesc op) {
-    __shared__ __attribute__((aligned(16))) uint8_t stage[kWaves * kBufs * kStageBytesM];
-    uint32_t t = blockIdx.x;
-    if (t >= (uint32_t)op.fast_tiles) {
-        tail_tile(op, t - op.fast_tiles, kWaves);
-        return;
+template <int RS>
+__global__ __launch_bounds__(kWave) void k_q8_gemm_mfma(GemmDesc d) {
+    __shared__ __attribute__((aligned(16))) uint8_t stage[kBufs * kStageBytesM];
+    const uint32_t bid = blockIdx.x;
+    if (bid < (uint32_t)d.fast_wgs) {
+        gemm_tile<RS>(d, (int)(bid / d.parts), (int)(bid % d.parts), stage);
+    } else {
+        OpDesc t;
+        t.x = d.X; t.w = d.w; t.y = d.Y; t.nb = d.nb; t.p = d.p; t.m = d.m;
+        t.x_stride = d.n; t.y_stride = d.p; t.tail_row0 = d.tail_row0;
+        tail_tile(t, bid - d.fast_wgs, 1);
     }
-    // the host sends widths whose super-rows exceed 2 rows to the m = 1 path
-    if (op.rs == 1) fast_tile_m<M, 1>(op, t, stage);
-    else fast_tile_m<M, 2>(op, t, stage);
 }
 
 }  // namespace
@@ -543,14 +645,13 @@ hipError_t launch_gemv_fused(const OpDesc *d_ops, const Tile *d_tiles, const Var
     }
 }
 
-hipError_t launch_gemm_single(const OpDesc &op, int mpad, int64_t grid, hipStream_t s) {
-    switch (mpad) {
-        case 2: hipLaunchKernelGGL(k_q8_gemm<2>, dim3((unsigned)grid), dim3(kThreads), 0, s, op); break;
-        case 4: hipLaunchKernelGGL(k_q8_gemm<4>, dim3((unsigned)grid), dim3(kThreads), 0, s, op); break;
-        case 8: hipLaunchKernelGGL(k_q8_gemm<8>, dim3((unsigned)grid), dim3(kThreads), 0, s, op); break;
-        case 16: hipLaunchKernelGGL(k_q8_gemm<16>, dim3((unsigned)grid), dim3(kThreads), 0, s, op); break;
-        default: return hipErrorInvalidValue;
-    }
+hipError_t launch_gemm_mfma(const GemmDesc &d, int64_t grid, hipStream_t s) {
+    if (d.rs == 1)
+        hipLaunchKernelGGL(k_q8_gemm_mfma<1>, dim3((unsigned)grid), dim3(kWave), 0, s, d);
+    else if (d.rs == 2)
+        hipLaunchKernelGGL(k_q8_gemm_mfma<2>, dim3((unsigned)grid), dim3(kWave), 0, s, d);
+    else
+        return hipErrorInvalidValue;
     return hipGetLastError();
 }
 
