@@ -296,7 +296,9 @@ int q8_0_gemm_smallm(const float *X, const void *w, float *Y, int64_t m, int64_t
         if ((rc = workspace_for(dev, s, ws_bytes, (size_t)d.row_tiles, &d.ws, &d.cnt))) return rc;
     }
     const int64_t grid = (int64_t)d.fast_wgs + (p - d.tail_row0);
-    e = launch_gemm_mfma(d, grid, s);
+    int pf = 0;
+    if (const char *ev = std::getenv("Q8GEMV_SMALLM_PF")) pf = std::atoi(ev) ? 1 : 0;
+    e = launch_gemm_mfma(d, pf, grid, s);
     if (e != hipSuccess) return fail_hip(e, "q8_0_gemm_smallm launch");
     return Q8_OK;
 }

@@ -101,6 +101,6 @@ inline int64_t tail_tiles_for(int64_t tail_rows, int nw = kWaves) {
 hipError_t launch_gemv_single(const OpDesc &op, const Variant &v, int64_t grid, hipStream_t s);
 hipError_t launch_gemv_fused(const OpDesc *d_ops, const Tile *d_tiles, const Variant &v,
                              int64_t grid, hipStream_t s);
-hipError_t launch_gemm_mfma(const GemmDesc &d, int64_t grid, hipStream_t s);
+hipError_t launch_gemm_mfma(const GemmDesc &d, int pf, int64_t grid, hipStream_t s);
 
 }  // namespace q8

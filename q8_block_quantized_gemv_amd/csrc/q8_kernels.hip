@@ -402,18 +402,23 @@ __device__ __forceinline__ void group_mfma(const uint8_t *stage, const float (&x
     if (RS > 1) { r = cb / d.nb; cb -= r * d.nb; }
 #define Q8_MSTEP(K)                                                                     \
     {                                                                                   \
-        bf16x8 ah, am, al;                                                              \
-        split3(xf[K], ah, am, al);                                                      \
+        bf16x8 ah, am, al, bq[4];                                                       \
+        float dsc[4];                                                                   \
         _Pragma("unroll") for (int t = 0; t < 4; ++t) {                                 \
             const uint8_t *grp = stage + kGroupBytes * (16 * t + j);                    \
-            const float dsc = half_to_float(                                            \
+            dsc[t] = half_to_float(                                                     \
                 *reinterpret_cast<const uint16_t *>(grp + (K) * kBlockBytes));          \
-            const bf16x8 bq = quants_bf16<K>(grp, g);                                   \
-            f32x4 c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, bq, f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0); \
-            c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(am, bq, c, 0, 0, 0);            \
-            c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(al, bq, c, 0, 0, 0);            \
-            sub[t] += dsc * c;                                                          \
+            bq[t] = quants_bf16<K>(grp, g);                                             \
         }                                                                               \
+        split3(xf[K], ah, am, al);                                                      \
+        f32x4 c[4];                                                                     \
+        _Pragma("unroll") for (int t = 0; t < 4; ++t)                                   \
+            c[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, bq[t], f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0); \
+        _Pragma("unroll") for (int t = 0; t < 4; ++t)                                   \
+            c[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(am, bq[t], c[t], 0, 0, 0);   \
+        _Pragma("unroll") for (int t = 0; t < 4; ++t)                                   \
+            c[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(al, bq[t], c[t], 0, 0, 0);   \
+        _Pragma("unroll") for (int t = 0; t < 4; ++t) sub[t] += dsc[t] * c[t];         \
         if (RS > 1 && ++cb == d.nb) { flush_tile<RS>(acc, sub, r); cb = 0; ++r; }      \
     }
     Q8_MSTEP(0) Q8_MSTEP(1) Q8_MSTEP(2) Q8_MSTEP(3)
@@ -425,7 +430,11 @@ __device__ __forceinline__ void group_mfma(const uint8_t *stage, const float (&x
 // One workgroup (one wave): 64 super-rows x groups [g0, g1) of K part `part`.
 // With d.parts > 1 the partial sums go to the workspace and the last part of
 // the row tile to arrive adds the parts in order 0, 1, ... and stores Y.
-template <int RS>
+// PF = 1: two W stages and X for the next group prefetched into registers
+// while this group computes (one wave per SIMD).  PF = 0: one stage, no
+// prefetch -- half the LDS and fewer registers, so two waves share a SIMD and
+// overlap each other's loads instead.
+template <int RS, int PF>
 __device__ void gemm_tile(const GemmDesc &d, int rt, int part, uint8_t *stage) {
     const int lane = lane_id();
     const int j = lane & 15, g = lane >> 4, i = lane & 15;
@@ -450,26 +459,41 @@ __device__ void gemm_tile(const GemmDesc &d, int rt, int part, uint8_t *stage) {
 #pragma unroll
         for (int c = 0; c < kGroupChunks; ++c) dma16_s(gb, off[c], l0 + kWave * 16 * c);
     };
-    float xf[8][8], xn[8][8];
-    if (g0 < g1) {
-        issue_w(g0, stage);
-        load_x_frag<RS>(d, g0, i, g, xn);
-    }
-    for (int kk = g0; kk < g1; ++kk) {
-        uint8_t *cur = stage + ((kk - g0) & 1) * kStageBytesM;
-        // The group's W (asm loads) and X (compiler-visible loads, issued
-        // after them) have landed; the compiler knows this wait.
-        __builtin_amdgcn_s_waitcnt(0x0F70);
-        asm volatile("" ::: "memory");
-#pragma unroll
-        for (int K = 0; K < 8; ++K)
-#pragma unroll
-            for (int e = 0; e < 8; ++e) xf[K][e] = xn[K][e];
-        if (kk + 1 < g1) {
-            issue_w(kk + 1, stage + ((kk + 1 - g0) & 1) * kStageBytesM);
-            load_x_frag<RS>(d, kk + 1, i, g, xn);
+    if constexpr (PF == 1) {
+        float xf[8][8], xn[8][8];
+        if (g0 < g1) {
+            issue_w(g0, stage);
+            load_x_frag<RS>(d, g0, i, g, xn);
         }
-        group_mfma<RS>(cur, xf, d, kk, lane, acc);
+        for (int kk = g0; kk < g1; ++kk) {
+            uint8_t *cur = stage + ((kk - g0) & 1) * kStageBytesM;
+            // The group's W (asm loads) and X (compiler-visible loads, issued
+            // after them) have landed; the compiler knows this wait.
+            __builtin_amdgcn_s_waitcnt(0x0F70);
+            asm volatile("" ::: "memory");
+#pragma unroll
+            for (int K = 0; K < 8; ++K)
+#pragma unroll
+                for (int e = 0; e < 8; ++e) xf[K][e] = xn[K][e];
+            if (kk + 1 < g1) {
+                issue_w(kk + 1, stage + ((kk + 1 - g0) & 1) * kStageBytesM);
+                load_x_frag<RS>(d, kk + 1, i, g, xn);
+            }
+            group_mfma<RS>(cur, xf, d, kk, lane, acc);
+        }
+    } else {
+        float xf[8][8];
+        for (int kk = g0; kk < g1; ++kk) {
+            issue_w(kk, stage);
+            load_x_frag<RS>(d, kk, i, g, xf);
+            __builtin_amdgcn_s_waitcnt(0x0F70);
+            asm volatile("" ::: "memory");
+            group_mfma<RS>(stage, xf, d, kk, lane, acc);
+            // every LDS read of this stage has returned before the next
+            // group's loads overwrite it
+            __builtin_amdgcn_s_waitcnt(0xC07F);
+            asm volatile("" ::: "memory");
+        }
     }
 
     // lane holds C[i = 4g + e][super-row 16t + j], row-in-super-row k
@@ -488,7 +512,11 @@ __device__ void gemm_tile(const GemmDesc &d, int rt, int part, uint8_t *stage) {
         }
         return;
     }
-    // partial tile: ws[(rt * parts + part)][16 rows of X][64 * RS rows of W]
+    // Partial tile: ws[(rt * parts + part)][16 rows of X][64 * RS rows of W].
+    // The partials are written and read with device-scope (sc1) accesses,
+    // which are coherent across the XCDs' L2s by themselves: no fence has to
+    // write back or invalidate a whole L2.  The wait before the counter makes
+    // this part's stores complete before its arrival is counted.
     float *mine = d.ws + ((int64_t)rt * d.parts + part) * (16 * kWave * RS);
 #pragma unroll
     for (int t = 0; t < 4; ++t)
@@ -496,25 +524,30 @@ __device__ void gemm_tile(const GemmDesc &d, int rt, int part, uint8_t *stage) {
         for (int k = 0; k < RS; ++k)
 #pragma unroll
             for (int e = 0; e < 4; ++e)
-                mine[(4 * g + e) * (kWave * RS) + (16 * t + j) * RS + k] = acc[t][k][e];
-    __threadfence();
+                __hip_atomic_store(mine + (4 * g + e) * (kWave * RS) + (16 * t + j) * RS + k,
+                                   acc[t][k][e], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __builtin_amdgcn_s_waitcnt(0);
+    asm volatile("" ::: "memory");
     uint32_t prev = 0;
-    if (lane == 0) prev = atomicAdd(d.cnt + rt, 1u);
+    if (lane == 0)
+        prev = __hip_atomic_fetch_add(d.cnt + rt, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     prev = __shfl(prev, 0, kWave);
     if (prev != (uint32_t)d.parts - 1) return;
-    __threadfence();
-    // last part of this row tile: sum the parts in a fixed order
+    // last part of this row tile to arrive: add the parts in a fixed order
     const float *base = d.ws + (int64_t)rt * d.parts * (16 * kWave * RS);
     for (int idx = lane; idx < 16 * kWave * RS; idx += kWave) {
         const int ii = idx / (kWave * RS);
         const int rr = idx - ii * (kWave * RS);
         const int64_t sr = sr0 + rr / RS;
         if (ii >= d.m || sr >= nsr) continue;
-        float v = base[idx];
-        for (int q = 1; q < d.parts; ++q) v += base[(int64_t)q * (16 * kWave * RS) + idx];
+        float v = __hip_atomic_load(base + idx, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        for (int q = 1; q < d.parts; ++q)
+            v += __hip_atomic_load(base + (int64_t)q * (16 * kWave * RS) + idx, __ATOMIC_RELAXED,
+                                   __HIP_MEMORY_SCOPE_AGENT);
         d.Y[(int64_t)ii * d.p + sr0 * RS + rr] = v;
     }
-    if (lane == 0) atomicExch(d.cnt + rt, 0u);   // ready for the next launch
+    if (lane == 0)   // ready for the next launch
+        __hip_atomic_store(d.cnt + rt, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 // ---------------------------------------------------------------- tail rows
@@ -590,12 +623,12 @@ __global__ __launch_bounds__(NW * kWave) void k_q8_gemv_fused(const OpDesc *__re
     run_tile<NW, PF>(op, tl.tile, stage);
 }
 
-template <int RS>
+template <int RS, int PF>
 __global__ __launch_bounds__(kWave) void k_q8_gemm_mfma(GemmDesc d) {
-    __shared__ __attribute__((aligned(16))) uint8_t stage[kBufs * kStageBytesM];
+    __shared__ __attribute__((aligned(16))) uint8_t stage[(PF + 1) * kStageBytesM];
     const uint32_t bid = blockIdx.x;
     if (bid < (uint32_t)d.fast_wgs) {
-        gemm_tile<RS>(d, (int)(bid / d.parts), (int)(bid % d.parts), stage);
+        gemm_tile<RS, PF>(d, (int)(bid / d.parts), (int)(bid % d.parts), stage);
     } else {
         OpDesc t;
         t.x = d.X; t.w = d.w; t.y = d.Y; t.nb = d.nb; t.p = d.p; t.m = d.m;
@@ -645,13 +678,15 @@ hipError_t launch_gemv_fused(const OpDesc *d_ops, const Tile *d_tiles, const Var
     }
 }
 
-hipError_t launch_gemm_mfma(const GemmDesc &d, int64_t grid, hipStream_t s) {
-    if (d.rs == 1)
-        hipLaunchKernelGGL(k_q8_gemm_mfma<1>, dim3((unsigned)grid), dim3(kWave), 0, s, d);
-    else if (d.rs == 2)
-        hipLaunchKernelGGL(k_q8_gemm_mfma<2>, dim3((unsigned)grid), dim3(kWave), 0, s, d);
-    else
-        return hipErrorInvalidValue;
+hipError_t launch_gemm_mfma(const GemmDesc &d, int pf, int64_t grid, hipStream_t s) {
+    const dim3 gr((unsigned)grid), bl(kWave);
+    switch (d.rs * 10 + pf) {
+        case 10: hipLaunchKernelGGL((k_q8_gemm_mfma<1, 0>), gr, bl, 0, s, d); break;
+        case 11: hipLaunchKernelGGL((k_q8_gemm_mfma<1, 1>), gr, bl, 0, s, d); break;
+        case 20: hipLaunchKernelGGL((k_q8_gemm_mfma<2, 0>), gr, bl, 0, s, d); break;
+        case 21: hipLaunchKernelGGL((k_q8_gemm_mfma<2, 1>), gr, bl, 0, s, d); break;
+        default: return hipErrorInvalidValue;
+    }
     return hipGetLastError();
 }
 
