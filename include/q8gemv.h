@@ -28,9 +28,15 @@
  *   - y (Y) must not overlap x (X) or w.
  *   - Sizes: n is a positive multiple of 32 and at most Q8_MAX_N; p is
  *     positive and at most Q8_MAX_P; small-batch m is in 1..Q8_MAX_M.
- *   - q8_0_gemv and q8_0_gemm_smallm allocate no device memory.
+ *   - q8_0_gemv allocates no device memory.  q8_0_gemm_smallm (m >= 2) uses
+ *     a workspace per (device, stream) that the library allocates on first
+ *     use and grows when a larger shape needs more (hipMalloc/hipFree, which
+ *     synchronize the device); it is kept until the process ends.  Calls on
+ *     one stream share it in stream order.
  *   - Results are bitwise reproducible run to run for the same inputs,
- *     shapes and device (fixed reduction order, no atomics).
+ *     shapes and device: every sum runs in a fixed order (the small-batch
+ *     product counts arrivals with an atomic counter, but adds partial sums
+ *     in a fixed order).
  *   - Accuracy: |y - exact| <= 1e-5 * sum_j |w_j x_j| + 1e-6 per output for
  *     finite inputs (float32 arithmetic with a bounded summation depth).
  */

@@ -281,23 +281,37 @@ int q8_0_gemm_smallm(const float *X, const void *w, float *Y, int64_t m, int64_t
     d.sr_bytes = rs * nb * kBlockBytes;
     d.row_tiles = (int32_t)((d.nsr + kWave - 1) / kWave);
     d.tail_row0 = d.nsr * (int32_t)rs;
-    // Split K when there are too few row tiles to give every CU about four
-    // one-wave workgroups, keeping at least three groups per part.
+    // Stream-K: up to `wpc` one-wave workgroups per CU (4 of the
+    // double-buffered kernel fill a CU's LDS; 8 of the single-stage one), each
+    // an equal contiguous range of at least `min_items` (row tile, group)
+    // items, so that short ranges do not multiply the partial sums.
     int dev = 0;
     hipError_t e = hipGetDevice(&dev);
     if (e != hipSuccess) return fail_hip(e, "hipGetDevice");
-    const int64_t target = 4 * (int64_t)cu_count(dev);
-    int64_t parts = d.row_tiles > 0 ? (target + d.row_tiles - 1) / d.row_tiles : 1;
-    parts = std::max<int64_t>(1, std::min<int64_t>(parts, d.gsr / 3));
-    d.parts = (int32_t)parts;
-    d.fast_wgs = d.row_tiles * d.parts;
-    if (d.parts > 1) {
-        const size_t ws_bytes = (size_t)d.fast_wgs * 16 * kWave * rs * sizeof(float);
-        if ((rc = workspace_for(dev, s, ws_bytes, (size_t)d.row_tiles, &d.ws, &d.cnt))) return rc;
-    }
-    const int64_t grid = (int64_t)d.fast_wgs + (p - d.tail_row0);
-    int pf = 0;
+    int pf = 1;
     if (const char *ev = std::getenv("Q8GEMV_SMALLM_PF")) pf = std::atoi(ev) ? 1 : 0;
+    int wpc = pf ? 4 : 8, min_items = 4;
+    if (const char *ev = std::getenv("Q8GEMV_SMALLM_WPC")) wpc = std::max(1, std::atoi(ev));
+    if (const char *ev = std::getenv("Q8GEMV_SMALLM_MINIT")) min_items = std::max(1, std::atoi(ev));
+    const int64_t items = (int64_t)d.row_tiles * d.gsr;
+    const int64_t slots = (int64_t)wpc * cu_count(dev);
+    const int64_t wgs = std::max<int64_t>(1, std::min({items, slots, items / min_items}));
+    d.fast_wgs = (int32_t)wgs;
+    // a row tile's contributors: at most ceil(G / per) + 1, per = items per workgroup
+    const int64_t per = std::max<int64_t>(1, items / wgs);
+    d.maxc = (int32_t)std::min<int64_t>(wgs, (d.gsr + per - 1) / per + 1);
+    // workspace: the split X (m * n * 6 bytes, 256-B aligned), then the
+    // partial slots
+    const size_t xs_bytes = ((size_t)m * n * kXPartsBytesPerCol + 255) / 256 * 256;
+    const size_t part_bytes = (size_t)d.row_tiles * d.maxc * 16 * kWave * rs * sizeof(float);
+    float *ws = nullptr;
+    if ((rc = workspace_for(dev, s, xs_bytes + part_bytes, (size_t)d.row_tiles, &ws, &d.cnt)))
+        return rc;
+    d.xs = (const XParts *)ws;
+    d.ws = (float *)((char *)ws + xs_bytes);
+    e = launch_split_x(X, ws, (int)m, (int)n, s);
+    if (e != hipSuccess) return fail_hip(e, "q8_0_gemm_smallm split launch");
+    const int64_t grid = (int64_t)d.fast_wgs + (p - d.tail_row0);
     e = launch_gemm_mfma(d, pf, grid, s);
     if (e != hipSuccess) return fail_hip(e, "q8_0_gemm_smallm launch");
     return Q8_OK;

@@ -53,12 +53,22 @@ struct OpDesc {
 };
 
 // A small-batch product (2 <= m <= 16, rows of 1 or 2 per super-row) on the
-// matrix cores.  Workgroups are one wave: row tile rt = 64 super-rows, K part
-// `part` of `parts` (groups split evenly).  With parts > 1 the partial sums
-// go through the workspace `ws` (parts * 16 * 64 * rs floats per row tile)
-// and the per-row-tile arrival counters `cnt` (all zero between launches).
+// matrix cores.  Workgroups are one wave.  The work is row_tiles (64
+// super-rows each) x gsr groups of items, split stream-K style into
+// fast_wgs equal contiguous ranges; a row tile shared by several workgroups
+// goes through `maxc` partial slots (16 * 64 * rs floats each) of the
+// workspace `ws` and the per-row-tile arrival counters `cnt` (zero between
+// launches).
+// Three bf16x8 (48 bytes): one lane's A operand of X for one block, split
+// exactly into bfloat16 parts h + m + l (see k_split_x).
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+struct XParts {
+    bf16x8 h, m, l;
+};
+
 struct GemmDesc {
     const float *X;
+    const XParts *xs;    // X split into exact bf16 parts (k_split_x)
     const uint8_t *w;
     float *Y;
     float *ws;
@@ -66,9 +76,9 @@ struct GemmDesc {
     int64_t sr_bytes;
     int32_t n, nb, p, m;
     int32_t rs, nsr, gsr;
-    int32_t parts;
+    int32_t maxc;        // partial slots per row tile (>= contributors of any tile)
     int32_t row_tiles;   // ceil(nsr / 64)
-    int32_t fast_wgs;    // row_tiles * parts; the tail rows follow, one per workgroup
+    int32_t fast_wgs;    // stream-K workgroups; the tail rows follow, one per workgroup
     int32_t tail_row0;
     int32_t pad_;
 };
@@ -102,5 +112,8 @@ hipError_t launch_gemv_single(const OpDesc &op, const Variant &v, int64_t grid, 
 hipError_t launch_gemv_fused(const OpDesc *d_ops, const Tile *d_tiles, const Variant &v,
                              int64_t grid, hipStream_t s);
 hipError_t launch_gemm_mfma(const GemmDesc &d, int pf, int64_t grid, hipStream_t s);
+// X (m x n) -> the bf16 parts the matrix-core kernel reads: 96 * n bytes per row
+hipError_t launch_split_x(const float *X, void *xs, int m, int n, hipStream_t s);
+constexpr int64_t kXPartsBytesPerCol = 6;   // 3 bf16 per element
 
 }  // namespace q8

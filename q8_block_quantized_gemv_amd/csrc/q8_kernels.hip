@@ -310,7 +310,6 @@ __device__ void fast_tile(const OpDesc &op, uint32_t tile, uint8_t *stage) {
 // Lane layout (gfx950, checked on the device): A[i][k] is element k%8 of
 // lane i + 16*(k/8), B[k][j] element k%8 of lane j + 16*(k/8), and C[i][j]
 // element i%4 of lane j + 16*(i/4).
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 __device__ __forceinline__ float bf16_as_float(__bf16 h) {
@@ -357,25 +356,42 @@ __device__ __forceinline__ bf16x8 quants_bf16(const uint8_t *grp, int g) {
     return b;
 }
 
-// 16 B of X row i for the lane's 8 columns of block K of group kk.
+// The A operands of X, split once per call by k_split_x into
+// xs[i][b][g] = {h, m, l}: three bf16x8 (48 bytes) holding columns
+// 32b + 8g .. 32b + 8g + 7 of row i.  Rows i >= m are never read.
+__global__ __launch_bounds__(256) void k_split_x(const float *__restrict__ X,
+                                                 XParts *__restrict__ xs, int m, int n) {
+    const int nb = n / kQuants;
+    const int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x;   // (i, b, g)
+    if (t >= (int64_t)m * nb * 4) return;
+    const float4 *src = reinterpret_cast<const float4 *>(X) + 2 * t;
+    const float4 v0 = src[0], v1 = src[1];
+    const float x[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
+    XParts o;
+    split3(x, o.h, o.m, o.l);
+    xs[t] = o;
+}
+
+// The A operand of block K of group kk for lane (i, g).  Rows i >= m load
+// row m - 1 again: the matrix core keeps rows of A apart, so those C rows
+// are never looked at, and no lane needs a branch or a zero fill.
 template <int RS>
-__device__ __forceinline__ void load_x_frag(const GemmDesc &d, int kk, int i, int g,
-                                            float (&xf)[8][8]) {
-    const bool live = i < d.m;
-    const float *row = d.X + (int64_t)(live ? i : 0) * d.n;
+__device__ __forceinline__ XParts load_parts(const GemmDesc &d, int kk, int K, int i, int g) {
+    int b = kk * kGroupBlocks + K;
+    if (RS > 1) b %= d.nb;
+    const int ii = i < d.m ? i : d.m - 1;
+    return d.xs[((int64_t)ii * d.nb + b) * 4 + g];
+}
+
+// All eight blocks' A operands of group kk (96 VGPRs), loaded together so
+// that their latency overlaps the group's W loads instead of stalling every
+// block.
+template <int RS>
+__device__ __forceinline__ void load_xgroup(const GemmDesc &d, int kk, int lane,
+                                            XParts (&xg)[kGroupBlocks]) {
+    const int i = lane & 15, g = lane >> 4;
 #pragma unroll
-    for (int K = 0; K < kGroupBlocks; ++K) {
-        int b = kk * kGroupBlocks + K;
-        if (RS > 1) b %= d.nb;
-        const float4 *src = reinterpret_cast<const float4 *>(row + (int64_t)b * kQuants + 8 * g);
-        float4 v0 = make_float4(0.f, 0.f, 0.f, 0.f), v1 = v0;
-        if (live) {
-            v0 = src[0];
-            v1 = src[1];
-        }
-        xf[K][0] = v0.x; xf[K][1] = v0.y; xf[K][2] = v0.z; xf[K][3] = v0.w;
-        xf[K][4] = v1.x; xf[K][5] = v1.y; xf[K][6] = v1.z; xf[K][7] = v1.w;
-    }
+    for (int K = 0; K < kGroupBlocks; ++K) xg[K] = load_parts<RS>(d, kk, K, i, g);
 }
 
 template <int RS>
@@ -389,10 +405,11 @@ __device__ __forceinline__ void flush_tile(f32x4 (&acc)[4][RS], f32x4 (&sub)[4],
     }
 }
 
-// One group of the wave's 64 super-rows (4 MFMA tiles of 16), all blocks.
+// One group of the wave's 64 super-rows (4 MFMA tiles of 16), all blocks;
+// xg holds the group's A operands.
 template <int RS>
-__device__ __forceinline__ void group_mfma(const uint8_t *stage, const float (&xf)[8][8],
-                                           const GemmDesc &d, int kk, int lane,
+__device__ __forceinline__ void group_mfma(const uint8_t *stage, const GemmDesc &d, int kk,
+                                           int lane, const XParts (&xg)[kGroupBlocks],
                                            f32x4 (&acc)[4][RS]) {
     const int j = lane & 15, g = lane >> 4;
     f32x4 sub[4];
@@ -402,7 +419,8 @@ __device__ __forceinline__ void group_mfma(const uint8_t *stage, const float (&x
     if (RS > 1) { r = cb / d.nb; cb -= r * d.nb; }
 #define Q8_MSTEP(K)                                                                     \
     {                                                                                   \
-        bf16x8 ah, am, al, bq[4];                                                       \
+        asm volatile("" ::: "memory"); /* one block's LDS reads at a time */           \
+        bf16x8 bq[4];                                                                   \
         float dsc[4];                                                                   \
         _Pragma("unroll") for (int t = 0; t < 4; ++t) {                                 \
             const uint8_t *grp = stage + kGroupBytes * (16 * t + j);                    \
@@ -410,14 +428,13 @@ __device__ __forceinline__ void group_mfma(const uint8_t *stage, const float (&x
                 *reinterpret_cast<const uint16_t *>(grp + (K) * kBlockBytes));          \
             bq[t] = quants_bf16<K>(grp, g);                                             \
         }                                                                               \
-        split3(xf[K], ah, am, al);                                                      \
         f32x4 c[4];                                                                     \
         _Pragma("unroll") for (int t = 0; t < 4; ++t)                                   \
-            c[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, bq[t], f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0); \
+            c[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xg[K].h, bq[t], f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0); \
         _Pragma("unroll") for (int t = 0; t < 4; ++t)                                   \
-            c[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(am, bq[t], c[t], 0, 0, 0);   \
+            c[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xg[K].m, bq[t], c[t], 0, 0, 0); \
         _Pragma("unroll") for (int t = 0; t < 4; ++t)                                   \
-            c[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(al, bq[t], c[t], 0, 0, 0);   \
+            c[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xg[K].l, bq[t], c[t], 0, 0, 0); \
         _Pragma("unroll") for (int t = 0; t < 4; ++t) sub[t] += dsc[t] * c[t];         \
         if (RS > 1 && ++cb == d.nb) { flush_tile<RS>(acc, sub, r); cb = 0; ++r; }      \
     }
@@ -427,127 +444,186 @@ __device__ __forceinline__ void group_mfma(const uint8_t *stage, const float (&x
     flush_tile<RS>(acc, sub, RS == 1 ? 0 : r);
 }
 
-// One workgroup (one wave): 64 super-rows x groups [g0, g1) of K part `part`.
-// With d.parts > 1 the partial sums go to the workspace and the last part of
-// the row tile to arrive adds the parts in order 0, 1, ... and stores Y.
-// PF = 1: two W stages and X for the next group prefetched into registers
-// while this group computes (one wave per SIMD).  PF = 0: one stage, no
-// prefetch -- half the LDS and fewer registers, so two waves share a SIMD and
-// overlap each other's loads instead.
+// Groups [g0, g1) of row tile rt (64 super-rows = 4 MFMA tiles), added
+// into acc.  PF = 1: two W stages, the next group's loads stream while this
+// one computes (one wave per SIMD).  PF = 0: one stage -- half the LDS and
+// fewer registers, so two waves share a SIMD and overlap each other instead.
 template <int RS, int PF>
-__device__ void gemm_tile(const GemmDesc &d, int rt, int part, uint8_t *stage) {
+__device__ void gemm_run(const GemmDesc &d, int rt, int g0, int g1, uint8_t *stage,
+                         f32x4 (&acc)[4][RS]) {
     const int lane = lane_id();
-    const int j = lane & 15, g = lane >> 4, i = lane & 15;
     const int64_t sr0 = (int64_t)rt * kWave;
-    const int nsr = d.nsr;
-    const int G = d.gsr;
-    const int g0 = (int)((int64_t)part * G / d.parts), g1 = (int)((int64_t)(part + 1) * G / d.parts);
-    const int last = (int)min((int64_t)nsr - 1 - sr0, (int64_t)kWave - 1);
+    const int last = (int)min((int64_t)d.nsr - 1 - sr0, (int64_t)kWave - 1);
     const uint8_t *wt = d.w + sr0 * d.sr_bytes;
     uint32_t off[kGroupChunks];
     chunk_offsets(off, lane, last, d.sr_bytes);
-
-    f32x4 acc[4][RS];
-#pragma unroll
-    for (int t = 0; t < 4; ++t)
-#pragma unroll
-        for (int k = 0; k < RS; ++k) acc[t][k] = f32x4{0.f, 0.f, 0.f, 0.f};
-
     auto issue_w = [&](int kk, uint8_t *st) {
         const uint32_t l0 = __builtin_amdgcn_readfirstlane(lds_addr(st));
         const uint8_t *gb = wt + (int64_t)kk * kGroupBytes;
 #pragma unroll
         for (int c = 0; c < kGroupChunks; ++c) dma16_s(gb, off[c], l0 + kWave * 16 * c);
     };
+    // Every wait is vmcnt(0) through the builtin, so the compiler knows that
+    // the A operands it loaded (ordinary loads) have landed as well.
     if constexpr (PF == 1) {
-        float xf[8][8], xn[8][8];
+        // two stages and two register sets of A, used in turn
+        XParts xa[kGroupBlocks], xb[kGroupBlocks];
+        uint8_t *st1 = stage + kStageBytesM;
         if (g0 < g1) {
             issue_w(g0, stage);
-            load_x_frag<RS>(d, g0, i, g, xn);
+            load_xgroup<RS>(d, g0, lane, xa);
         }
-        for (int kk = g0; kk < g1; ++kk) {
-            uint8_t *cur = stage + ((kk - g0) & 1) * kStageBytesM;
-            // The group's W (asm loads) and X (compiler-visible loads, issued
-            // after them) have landed; the compiler knows this wait.
+        for (int kk = g0; kk < g1; kk += 2) {
             __builtin_amdgcn_s_waitcnt(0x0F70);
             asm volatile("" ::: "memory");
-#pragma unroll
-            for (int K = 0; K < 8; ++K)
-#pragma unroll
-                for (int e = 0; e < 8; ++e) xf[K][e] = xn[K][e];
             if (kk + 1 < g1) {
-                issue_w(kk + 1, stage + ((kk + 1 - g0) & 1) * kStageBytesM);
-                load_x_frag<RS>(d, kk + 1, i, g, xn);
+                issue_w(kk + 1, st1);
+                load_xgroup<RS>(d, kk + 1, lane, xb);
             }
-            group_mfma<RS>(cur, xf, d, kk, lane, acc);
+            group_mfma<RS>(stage, d, kk, lane, xa, acc);
+            __builtin_amdgcn_s_waitcnt(0xC07F);   // stage 0 fully read
+            asm volatile("" ::: "memory");
+            if (kk + 1 >= g1) break;
+            __builtin_amdgcn_s_waitcnt(0x0F70);
+            asm volatile("" ::: "memory");
+            if (kk + 2 < g1) {
+                issue_w(kk + 2, stage);
+                load_xgroup<RS>(d, kk + 2, lane, xa);
+            }
+            group_mfma<RS>(st1, d, kk + 1, lane, xb, acc);
+            __builtin_amdgcn_s_waitcnt(0xC07F);   // stage 1 fully read
+            asm volatile("" ::: "memory");
         }
     } else {
-        float xf[8][8];
+        XParts xg[kGroupBlocks];
         for (int kk = g0; kk < g1; ++kk) {
             issue_w(kk, stage);
-            load_x_frag<RS>(d, kk, i, g, xf);
+            load_xgroup<RS>(d, kk, lane, xg);
             __builtin_amdgcn_s_waitcnt(0x0F70);
             asm volatile("" ::: "memory");
-            group_mfma<RS>(stage, xf, d, kk, lane, acc);
+            group_mfma<RS>(stage, d, kk, lane, xg, acc);
             // every LDS read of this stage has returned before the next
             // group's loads overwrite it
             __builtin_amdgcn_s_waitcnt(0xC07F);
             asm volatile("" ::: "memory");
         }
     }
+}
 
-    // lane holds C[i = 4g + e][super-row 16t + j], row-in-super-row k
-    if (d.parts == 1) {
+// Stream-K split of the small-batch product: the row_tiles * G (row tile,
+// group) items, row tile major, are cut into gridDim-many equal contiguous
+// ranges, one per workgroup.  Workgroup b owns items [b*N/W, (b+1)*N/W).
+__device__ __forceinline__ int64_t sk_first_item(int64_t b, int64_t N, int64_t W) {
+    return b * N / W;
+}
+// The workgroup whose range holds item i.
+__device__ __forceinline__ int64_t sk_owner(int64_t i, int64_t N, int64_t W) {
+    return ((i + 1) * W - 1) / N;
+}
+
+// lane holds C[i = 4g + e][super-row 16t + j], row-in-super-row k
+template <int RS>
+__device__ __forceinline__ void store_tile(const GemmDesc &d, int64_t sr0, int lane,
+                                           const f32x4 (&acc)[4][RS]) {
+    const int j = lane & 15, g = lane >> 4;
 #pragma unroll
-        for (int t = 0; t < 4; ++t) {
-            const int64_t sr = sr0 + 16 * t + j;
-            if (sr >= nsr) continue;
+    for (int t = 0; t < 4; ++t) {
+        const int64_t sr = sr0 + 16 * t + j;
+        if (sr >= d.nsr) continue;
 #pragma unroll
-            for (int k = 0; k < RS; ++k)
+        for (int k = 0; k < RS; ++k)
 #pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const int ii = 4 * g + e;
-                    if (ii < d.m) d.Y[(int64_t)ii * d.p + sr * RS + k] = acc[t][k][e];
-                }
-        }
-        return;
+            for (int e = 0; e < 4; ++e) {
+                const int ii = 4 * g + e;
+                if (ii < d.m) d.Y[(int64_t)ii * d.p + sr * RS + k] = acc[t][k][e];
+            }
     }
-    // Partial tile: ws[(rt * parts + part)][16 rows of X][64 * RS rows of W].
-    // The partials are written and read with device-scope (sc1) accesses,
-    // which are coherent across the XCDs' L2s by themselves: no fence has to
-    // write back or invalidate a whole L2.  The wait before the counter makes
-    // this part's stores complete before its arrival is counted.
-    float *mine = d.ws + ((int64_t)rt * d.parts + part) * (16 * kWave * RS);
+}
+
+// A workgroup's share of one row tile, which other workgroups share too:
+// park it in slot `rank` of the tile's partials, count the arrival, and if
+// it is the last of `contributors` to arrive, add the slots in rank order and
+// store Y.  The partials are written and read with device-scope (sc1)
+// accesses, coherent across the XCDs' L2s by themselves (no fence has to
+// write back or invalidate a whole L2); the wait before the counter makes
+// this share's stores complete before its arrival is counted.
+template <int RS>
+__device__ void partial_tile(const GemmDesc &d, int rt, int rank, int contributors, int lane,
+                             const f32x4 (&acc)[4][RS]) {
+    const int j = lane & 15, g = lane >> 4;
+    constexpr int kSlot = 16 * kWave * RS;   // floats per slot: [X row][64 * RS rows of W]
+    float *slots = d.ws + (int64_t)rt * d.maxc * kSlot;
+    float *mine = slots + (int64_t)rank * kSlot;
 #pragma unroll
     for (int t = 0; t < 4; ++t)
 #pragma unroll
         for (int k = 0; k < RS; ++k)
 #pragma unroll
             for (int e = 0; e < 4; ++e)
-                __hip_atomic_store(mine + (4 * g + e) * (kWave * RS) + (16 * t + j) * RS + k,
-                                   acc[t][k][e], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                if (4 * g + e < d.m)
+                    __hip_atomic_store(mine + (4 * g + e) * (kWave * RS) + (16 * t + j) * RS + k,
+                                       acc[t][k][e], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     __builtin_amdgcn_s_waitcnt(0);
     asm volatile("" ::: "memory");
     uint32_t prev = 0;
     if (lane == 0)
         prev = __hip_atomic_fetch_add(d.cnt + rt, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     prev = __shfl(prev, 0, kWave);
-    if (prev != (uint32_t)d.parts - 1) return;
-    // last part of this row tile to arrive: add the parts in a fixed order
-    const float *base = d.ws + (int64_t)rt * d.parts * (16 * kWave * RS);
-    for (int idx = lane; idx < 16 * kWave * RS; idx += kWave) {
+    if (prev != (uint32_t)contributors - 1) return;
+    asm volatile("" ::: "memory");
+    const int64_t sr0 = (int64_t)rt * kWave;
+    // Eight slots' loads are in flight at once; the sum still runs in rank
+    // order.  Past the last rank the index is clamped and the value dropped.
+    constexpr int kBatch = 8;
+    for (int idx = lane; idx < d.m * (kWave * RS); idx += kWave) {
         const int ii = idx / (kWave * RS);
         const int rr = idx - ii * (kWave * RS);
-        const int64_t sr = sr0 + rr / RS;
-        if (ii >= d.m || sr >= nsr) continue;
-        float v = __hip_atomic_load(base + idx, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        for (int q = 1; q < d.parts; ++q)
-            v += __hip_atomic_load(base + (int64_t)q * (16 * kWave * RS) + idx, __ATOMIC_RELAXED,
-                                   __HIP_MEMORY_SCOPE_AGENT);
+        if (sr0 + rr / RS >= d.nsr) continue;
+        float v = 0.f;
+        for (int q0 = 0; q0 < contributors; q0 += kBatch) {
+            float t[kBatch];
+#pragma unroll
+            for (int u = 0; u < kBatch; ++u) {
+                const int q = min(q0 + u, contributors - 1);
+                t[u] = __hip_atomic_load(slots + (int64_t)q * kSlot + idx, __ATOMIC_RELAXED,
+                                         __HIP_MEMORY_SCOPE_AGENT);
+            }
+#pragma unroll
+            for (int u = 0; u < kBatch; ++u)
+                if (q0 + u < contributors) v = (q0 + u == 0) ? t[u] : v + t[u];
+        }
         d.Y[(int64_t)ii * d.p + sr0 * RS + rr] = v;
     }
     if (lane == 0)   // ready for the next launch
         __hip_atomic_store(d.cnt + rt, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Workgroup b's range of (row tile, group) items.
+template <int RS, int PF>
+__device__ void gemm_streamk(const GemmDesc &d, int64_t b, uint8_t *stage) {
+    const int lane = lane_id();
+    const int64_t G = d.gsr, N = (int64_t)d.row_tiles * G, W = d.fast_wgs;
+    int64_t it = sk_first_item(b, N, W);
+    const int64_t end = sk_first_item(b + 1, N, W);
+    while (it < end) {
+        const int rt = (int)(it / G);
+        const int g0 = (int)(it - (int64_t)rt * G);
+        const int g1 = (int)min(G, (int64_t)g0 + (end - it));
+        f32x4 acc[4][RS];
+#pragma unroll
+        for (int t = 0; t < 4; ++t)
+#pragma unroll
+            for (int k = 0; k < RS; ++k) acc[t][k] = f32x4{0.f, 0.f, 0.f, 0.f};
+        gemm_run<RS, PF>(d, rt, g0, g1, stage, acc);
+        if (g0 == 0 && g1 == G) {
+            store_tile<RS>(d, (int64_t)rt * kWave, lane, acc);
+        } else {
+            const int64_t first = sk_owner((int64_t)rt * G, N, W);
+            const int64_t contributors = sk_owner((int64_t)rt * G + G - 1, N, W) - first + 1;
+            partial_tile<RS>(d, rt, (int)(b - first), (int)contributors, lane, acc);
+        }
+        it += g1 - g0;
+    }
 }
 
 // ---------------------------------------------------------------- tail rows
@@ -624,11 +700,11 @@ __global__ __launch_bounds__(NW * kWave) void k_q8_gemv_fused(const OpDesc *__re
 }
 
 template <int RS, int PF>
-__global__ __launch_bounds__(kWave) void k_q8_gemm_mfma(GemmDesc d) {
+__global__ __launch_bounds__(kWave, PF == 0 ? 2 : 1) void k_q8_gemm_mfma(GemmDesc d) {
     __shared__ __attribute__((aligned(16))) uint8_t stage[(PF + 1) * kStageBytesM];
     const uint32_t bid = blockIdx.x;
     if (bid < (uint32_t)d.fast_wgs) {
-        gemm_tile<RS, PF>(d, (int)(bid / d.parts), (int)(bid % d.parts), stage);
+        gemm_streamk<RS, PF>(d, bid, stage);
     } else {
         OpDesc t;
         t.x = d.X; t.w = d.w; t.y = d.Y; t.nb = d.nb; t.p = d.p; t.m = d.m;
@@ -676,6 +752,13 @@ hipError_t launch_gemv_fused(const OpDesc *d_ops, const Tile *d_tiles, const Var
         case 42: return launch_fused_t<4, 2>(d_ops, d_tiles, grid, s);
         default: return hipErrorInvalidValue;
     }
+}
+
+hipError_t launch_split_x(const float *X, void *xs, int m, int n, hipStream_t s) {
+    const int64_t items = (int64_t)m * (n / kQuants) * 4;
+    hipLaunchKernelGGL(k_split_x, dim3((unsigned)((items + 255) / 256)), dim3(256), 0, s, X,
+                       (XParts *)xs, m, n);
+    return hipGetLastError();
 }
 
 hipError_t launch_gemm_mfma(const GemmDesc &d, int pf, int64_t grid, hipStream_t s) {
