@@ -222,6 +222,94 @@ int gemv_launch(const float *x, const void *w, float *y, int64_t n, int64_t p, h
     return Q8_OK;
 }
 
+// Shape fields of a small-batch product (validated arguments).
+GemmDesc plan_gemm(const float *X, const void *w, float *Y, int64_t m, int64_t n, int64_t p) {
+    GemmDesc d;
+    std::memset(&d, 0, sizeof d);
+    const int64_t nb = n / kQuants;
+    const int64_t rs = kGroupBlocks / gcd64(nb, kGroupBlocks);
+    d.X = X;
+    d.w = (const uint8_t *)w;
+    d.Y = Y;
+    d.n = (int32_t)n;
+    d.nb = (int32_t)nb;
+    d.p = (int32_t)p;
+    d.m = (int32_t)m;
+    d.rs = (int32_t)rs;
+    d.nsr = (int32_t)(p / rs);
+    d.gsr = (int32_t)(rs * nb / kGroupBlocks);
+    d.sr_bytes = rs * nb * kBlockBytes;
+    d.row_tiles = (int32_t)((d.nsr + kWave - 1) / kWave);
+    d.tail_row0 = d.nsr * (int32_t)rs;
+    return d;
+}
+
+int env_int(const char *name, int dflt) {
+    const char *ev = std::getenv(name);
+    return ev ? std::atoi(ev) : dflt;
+}
+
+// Stream-K split: up to `wpc` one-wave workgroups per CU, each an equal
+// contiguous range of at least `min_items` (row tile, group) items, so that
+// short ranges do not multiply the partial sums.  Sets fast_wgs and maxc
+// and returns the bytes of partial slots the split needs.
+size_t plan_streamk(GemmDesc &d, int dev, int wpc, int min_items) {
+    wpc = std::max(1, env_int("Q8GEMV_SMALLM_WPC", wpc));
+    min_items = std::max(1, env_int("Q8GEMV_SMALLM_MINIT", min_items));
+    const int64_t items = (int64_t)d.row_tiles * d.gsr;
+    const int64_t slots = (int64_t)wpc * cu_count(dev);
+    const int64_t wgs = std::max<int64_t>(1, std::min({items, slots, items / min_items}));
+    d.fast_wgs = (int32_t)wgs;
+    // a row tile's contributors: at most ceil(G / per) + 1, per = items per workgroup
+    const int64_t per = std::max<int64_t>(1, items / wgs);
+    d.maxc = (int32_t)std::min<int64_t>(wgs, (d.gsr + per - 1) / per + 1);
+    return (size_t)d.row_tiles * d.maxc * 16 * kWave * d.rs * sizeof(float);
+}
+
+// m = 2..4 rows on the vector units.
+int smallm_valu(const float *X, const void *w, float *Y, int64_t m, int64_t n, int64_t p,
+                hipStream_t s) {
+    GemmDesc d = plan_gemm(X, w, Y, m, n, p);
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return fail_hip(e, "hipGetDevice");
+    // as many workgroups per CU as their double-buffered stages fit in 160 KiB of LDS
+    const int wpc = (160 * 1024) / gemm_valu_stage_bytes((int)m);
+    const size_t part_bytes = plan_streamk(d, dev, wpc, 4);
+    float *ws = nullptr;
+    int rc = workspace_for(dev, s, std::max<size_t>(part_bytes, 256), (size_t)d.row_tiles, &ws, &d.cnt);
+    if (rc) return rc;
+    d.ws = ws;
+    e = launch_gemm_valu(d, (int64_t)d.fast_wgs + (p - d.tail_row0), s);
+    if (e != hipSuccess) return fail_hip(e, "q8_0_gemm_smallm launch");
+    return Q8_OK;
+}
+
+// m = 2..16 rows on the matrix cores (rows of 1 or 2 per super-row).
+int smallm_mfma(const float *X, const void *w, float *Y, int64_t m, int64_t n, int64_t p,
+                hipStream_t s) {
+    GemmDesc d = plan_gemm(X, w, Y, m, n, p);
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return fail_hip(e, "hipGetDevice");
+    // 4 double-buffered workgroups fill a CU's LDS; 8 single-stage ones
+    const int pf = env_int("Q8GEMV_SMALLM_PF", 1) ? 1 : 0;
+    const size_t part_bytes = plan_streamk(d, dev, pf ? 4 : 8, 4);
+    // workspace: the split X (m * n * 6 bytes, 256-B aligned), then the
+    // partial slots
+    const size_t xs_bytes = ((size_t)m * n * kXPartsBytesPerCol + 255) / 256 * 256;
+    float *ws = nullptr;
+    int rc = workspace_for(dev, s, xs_bytes + part_bytes, (size_t)d.row_tiles, &ws, &d.cnt);
+    if (rc) return rc;
+    d.xs = (const XParts *)ws;
+    d.ws = (float *)((char *)ws + xs_bytes);
+    e = launch_split_x(X, ws, (int)m, (int)n, s);
+    if (e != hipSuccess) return fail_hip(e, "q8_0_gemm_smallm split launch");
+    e = launch_gemm_mfma(d, pf, (int64_t)d.fast_wgs + (p - d.tail_row0), s);
+    if (e != hipSuccess) return fail_hip(e, "q8_0_gemm_smallm launch");
+    return Q8_OK;
+}
+
 }  // namespace
 
 // ===================================================================== ABI
@@ -257,63 +345,27 @@ int q8_0_gemm_smallm(const float *X, const void *w, float *Y, int64_t m, int64_t
     if (rc) return rc;
     if ((rc = check_device())) return rc;
     hipStream_t s = (hipStream_t)stream;
-    const int64_t nb = n / kQuants;
-    const int64_t rs = kGroupBlocks / gcd64(nb, kGroupBlocks);
-    if (m == 1 || rs > 2) {
-        // one weight pass per activation row: used for m = 1 and for widths
-        // whose rows need super-rows of 4 or 8 (n not a multiple of 128)
-        for (int64_t i = 0; i < m; ++i)
-            if ((rc = gemv_launch(X + i * n, w, Y + i * p, n, p, s))) return rc;
-        return Q8_OK;
+    if (m == 1) return gemv_launch(X, w, Y, n, p, s);
+    const int64_t rs = kGroupBlocks / gcd64(n / kQuants, kGroupBlocks);
+    // Where rows fill super-rows of 1 or 2 (n a multiple of 128) the matrix
+    // cores take every m >= 2: on the vector units, the x values every lane
+    // needs come through LDS broadcast reads, m of them per quant and lane,
+    // and those bound that kernel below the matrix cores' even at m = 2 for
+    // the 7B lm_head.  Other widths run on the vector units, kValuMaxM rows of
+    // X per pass over W.  Q8GEMV_SMALLM_PATH=valu|mfma overrides.
+    bool mfma = rs <= 2;
+    if (const char *ev = std::getenv("Q8GEMV_SMALLM_PATH")) {
+        if (!std::strcmp(ev, "valu")) mfma = false;
+        else if (!std::strcmp(ev, "mfma") && rs <= 2) mfma = true;
     }
-    GemmDesc d;
-    std::memset(&d, 0, sizeof d);
-    d.X = X;
-    d.w = (const uint8_t *)w;
-    d.Y = Y;
-    d.n = (int32_t)n;
-    d.nb = (int32_t)nb;
-    d.p = (int32_t)p;
-    d.m = (int32_t)m;
-    d.rs = (int32_t)rs;
-    d.nsr = (int32_t)(p / rs);
-    d.gsr = (int32_t)(rs * nb / kGroupBlocks);
-    d.sr_bytes = rs * nb * kBlockBytes;
-    d.row_tiles = (int32_t)((d.nsr + kWave - 1) / kWave);
-    d.tail_row0 = d.nsr * (int32_t)rs;
-    // Stream-K: up to `wpc` one-wave workgroups per CU (4 of the
-    // double-buffered kernel fill a CU's LDS; 8 of the single-stage one), each
-    // an equal contiguous range of at least `min_items` (row tile, group)
-    // items, so that short ranges do not multiply the partial sums.
-    int dev = 0;
-    hipError_t e = hipGetDevice(&dev);
-    if (e != hipSuccess) return fail_hip(e, "hipGetDevice");
-    int pf = 1;
-    if (const char *ev = std::getenv("Q8GEMV_SMALLM_PF")) pf = std::atoi(ev) ? 1 : 0;
-    int wpc = pf ? 4 : 8, min_items = 4;
-    if (const char *ev = std::getenv("Q8GEMV_SMALLM_WPC")) wpc = std::max(1, std::atoi(ev));
-    if (const char *ev = std::getenv("Q8GEMV_SMALLM_MINIT")) min_items = std::max(1, std::atoi(ev));
-    const int64_t items = (int64_t)d.row_tiles * d.gsr;
-    const int64_t slots = (int64_t)wpc * cu_count(dev);
-    const int64_t wgs = std::max<int64_t>(1, std::min({items, slots, items / min_items}));
-    d.fast_wgs = (int32_t)wgs;
-    // a row tile's contributors: at most ceil(G / per) + 1, per = items per workgroup
-    const int64_t per = std::max<int64_t>(1, items / wgs);
-    d.maxc = (int32_t)std::min<int64_t>(wgs, (d.gsr + per - 1) / per + 1);
-    // workspace: the split X (m * n * 6 bytes, 256-B aligned), then the
-    // partial slots
-    const size_t xs_bytes = ((size_t)m * n * kXPartsBytesPerCol + 255) / 256 * 256;
-    const size_t part_bytes = (size_t)d.row_tiles * d.maxc * 16 * kWave * rs * sizeof(float);
-    float *ws = nullptr;
-    if ((rc = workspace_for(dev, s, xs_bytes + part_bytes, (size_t)d.row_tiles, &ws, &d.cnt)))
-        return rc;
-    d.xs = (const XParts *)ws;
-    d.ws = (float *)((char *)ws + xs_bytes);
-    e = launch_split_x(X, ws, (int)m, (int)n, s);
-    if (e != hipSuccess) return fail_hip(e, "q8_0_gemm_smallm split launch");
-    const int64_t grid = (int64_t)d.fast_wgs + (p - d.tail_row0);
-    e = launch_gemm_mfma(d, pf, grid, s);
-    if (e != hipSuccess) return fail_hip(e, "q8_0_gemm_smallm launch");
+    if (mfma) return smallm_mfma(X, w, Y, m, n, p, s);
+    // vector units: one pass over W per kValuMaxM rows of X
+    for (int64_t i0 = 0; i0 < m; i0 += kValuMaxM) {
+        const int64_t mi = std::min<int64_t>(kValuMaxM, m - i0);
+        rc = mi == 1 ? gemv_launch(X + i0 * n, w, Y + i0 * p, n, p, s)
+                     : smallm_valu(X + i0 * n, w, Y + i0 * p, mi, n, p, s);
+        if (rc) return rc;
+    }
     return Q8_OK;
 }
 
@@ -451,19 +503,22 @@ int q8_0_chain_create(const q8_0_op *ops, int64_t n_ops, uint32_t flags, q8_0_ch
         }
         info.push_back(si);
     }
-    if (!h_ops.empty()) {
-        const size_t ob = h_ops.size() * sizeof(OpDesc);
-        const size_t tb = h_tiles.size() * sizeof(Tile);
-        hipError_t e = hipMalloc(&c->d_table, ob + tb);
+    // device block: op descriptors, then tiles
+    const size_t ob = h_ops.size() * sizeof(OpDesc);
+    const size_t tb = h_tiles.size() * sizeof(Tile);
+    if (ob + tb) {
+        std::vector<char> host(ob + tb, 0);
+        if (ob) std::memcpy(host.data(), h_ops.data(), ob);
+        if (tb) std::memcpy(host.data() + ob, h_tiles.data(), tb);
+        hipError_t e = hipMalloc(&c->d_table, host.size());
         if (e != hipSuccess) { chain_free(c); return fail_hip(e, "q8_0_chain_create hipMalloc"); }
-        if ((e = hipMemcpy(c->d_table, h_ops.data(), ob, hipMemcpyHostToDevice)) != hipSuccess ||
-            (e = hipMemcpy((char *)c->d_table + ob, h_tiles.data(), tb, hipMemcpyHostToDevice)) != hipSuccess) {
+        if ((e = hipMemcpy(c->d_table, host.data(), host.size(), hipMemcpyHostToDevice)) != hipSuccess) {
             chain_free(c);
             return fail_hip(e, "q8_0_chain_create hipMemcpy");
         }
     }
     const OpDesc *d_ops = (const OpDesc *)c->d_table;
-    const Tile *d_tiles = (const Tile *)((const char *)c->d_table + h_ops.size() * sizeof(OpDesc));
+    const Tile *d_tiles = (const Tile *)((const char *)c->d_table + ob);
     for (size_t k = 0; k < segs.size(); ++k) {
         q8_0_chain::Launch L;
         std::memset(&L, 0, sizeof L);

@@ -52,13 +52,12 @@ struct OpDesc {
     int32_t pad_;
 };
 
-// A small-batch product (2 <= m <= 16, rows of 1 or 2 per super-row) on the
-// matrix cores.  Workgroups are one wave.  The work is row_tiles (64
-// super-rows each) x gsr groups of items, split stream-K style into
-// fast_wgs equal contiguous ranges; a row tile shared by several workgroups
-// goes through `maxc` partial slots (16 * 64 * rs floats each) of the
-// workspace `ws` and the per-row-tile arrival counters `cnt` (zero between
-// launches).
+// A small-batch product (2 <= m <= 16) as its kernels see it.  Workgroups
+// are one wave.  The work is row_tiles (64 super-rows each) x gsr groups of
+// items, split stream-K style into fast_wgs equal contiguous ranges; a row
+// tile shared by several workgroups goes through `maxc` partial slots
+// (16 * 64 * rs floats each) of the workspace `ws` and the per-row-tile
+// arrival counters `cnt` (zero between launches).
 // Three bf16x8 (48 bytes): one lane's A operand of X for one block, split
 // exactly into bfloat16 parts h + m + l (see k_split_x).
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
@@ -112,6 +111,10 @@ hipError_t launch_gemv_single(const OpDesc &op, const Variant &v, int64_t grid, 
 hipError_t launch_gemv_fused(const OpDesc *d_ops, const Tile *d_tiles, const Variant &v,
                              int64_t grid, hipStream_t s);
 hipError_t launch_gemm_mfma(const GemmDesc &d, int pf, int64_t grid, hipStream_t s);
+// the vector-unit small batch for m = 2..4 (any rs); d.xs is not used
+hipError_t launch_gemm_valu(const GemmDesc &d, int64_t grid, hipStream_t s);
+int gemm_valu_stage_bytes(int m);   // LDS bytes per workgroup (0 if m is not 2..4)
+constexpr int kValuMaxM = 4;
 // X (m x n) -> the bf16 parts the matrix-core kernel reads: 96 * n bytes per row
 hipError_t launch_split_x(const float *X, void *xs, int m, int n, hipStream_t s);
 constexpr int64_t kXPartsBytesPerCol = 6;   // 3 bf16 per element

@@ -134,6 +134,15 @@ __device__ __forceinline__ void wait_vm_asm() {
     asm volatile("s_waitcnt vmcnt(%0)" :: "n"(N) : "memory");
 }
 
+// A pointer that is the same in every lane, made visibly so for the
+// compiler (it goes into a scalar register pair).
+__device__ __forceinline__ const uint8_t *uniform_ptr(const uint8_t *p) {
+    const uint64_t v = (uint64_t)(uintptr_t)p;
+    const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
+    const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
+    return (const uint8_t *)(uintptr_t)(((uint64_t)hi << 32) | lo);
+}
+
 __device__ __forceinline__ uint32_t lds_addr(const uint8_t *p) {
     return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) uint8_t *)p;
 }
@@ -540,29 +549,27 @@ __device__ __forceinline__ void store_tile(const GemmDesc &d, int64_t sr0, int l
     }
 }
 
-// A workgroup's share of one row tile, which other workgroups share too:
-// park it in slot `rank` of the tile's partials, count the arrival, and if
-// it is the last of `contributors` to arrive, add the slots in rank order and
-// store Y.  The partials are written and read with device-scope (sc1)
-// accesses, coherent across the XCDs' L2s by themselves (no fence has to
-// write back or invalidate a whole L2); the wait before the counter makes
+// A row tile shared by several workgroups: each parks its share in slot
+// `rank` of the tile's partials (16 X rows x 64 * RS W rows of floats) and
+// counts its arrival; the last of `contributors` to arrive adds the slots in
+// rank order and stores Y.  Partials are written and read with device-scope
+// (sc1) accesses, coherent across the XCDs' L2s by themselves (no fence has
+// to write back or invalidate a whole L2); the wait before the counter makes
 // this share's stores complete before its arrival is counted.
 template <int RS>
-__device__ void partial_tile(const GemmDesc &d, int rt, int rank, int contributors, int lane,
-                             const f32x4 (&acc)[4][RS]) {
-    const int j = lane & 15, g = lane >> 4;
-    constexpr int kSlot = 16 * kWave * RS;   // floats per slot: [X row][64 * RS rows of W]
-    float *slots = d.ws + (int64_t)rt * d.maxc * kSlot;
-    float *mine = slots + (int64_t)rank * kSlot;
-#pragma unroll
-    for (int t = 0; t < 4; ++t)
-#pragma unroll
-        for (int k = 0; k < RS; ++k)
-#pragma unroll
-            for (int e = 0; e < 4; ++e)
-                if (4 * g + e < d.m)
-                    __hip_atomic_store(mine + (4 * g + e) * (kWave * RS) + (16 * t + j) * RS + k,
-                                       acc[t][k][e], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+__device__ __forceinline__ float *partial_slot(const GemmDesc &d, int rt, int rank) {
+    constexpr int kSlot = 16 * kWave * RS;
+    return d.ws + ((int64_t)rt * d.maxc + rank) * kSlot;
+}
+
+__device__ __forceinline__ void store_partial(float *p, float v) {
+    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Called by every lane once this share's partial is stored.
+template <int RS>
+__device__ void arrive_reduce(const GemmDesc &d, int rt, int contributors, int lane) {
+    constexpr int kSlot = 16 * kWave * RS;
     __builtin_amdgcn_s_waitcnt(0);
     asm volatile("" ::: "memory");
     uint32_t prev = 0;
@@ -571,6 +578,7 @@ __device__ void partial_tile(const GemmDesc &d, int rt, int rank, int contributo
     prev = __shfl(prev, 0, kWave);
     if (prev != (uint32_t)contributors - 1) return;
     asm volatile("" ::: "memory");
+    const float *slots = partial_slot<RS>(d, rt, 0);
     const int64_t sr0 = (int64_t)rt * kWave;
     // Eight slots' loads are in flight at once; the sum still runs in rank
     // order.  Past the last rank the index is clamped and the value dropped.
@@ -598,6 +606,24 @@ __device__ void partial_tile(const GemmDesc &d, int rt, int rank, int contributo
         __hip_atomic_store(d.cnt + rt, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
+// The matrix-core share: lane (j, g) holds C[4g + e][16t + j] of tile t.
+template <int RS>
+__device__ void partial_tile(const GemmDesc &d, int rt, int rank, int contributors, int lane,
+                             const f32x4 (&acc)[4][RS]) {
+    const int j = lane & 15, g = lane >> 4;
+    float *mine = partial_slot<RS>(d, rt, rank);
+#pragma unroll
+    for (int t = 0; t < 4; ++t)
+#pragma unroll
+        for (int k = 0; k < RS; ++k)
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                if (4 * g + e < d.m)
+                    store_partial(mine + (4 * g + e) * (kWave * RS) + (16 * t + j) * RS + k,
+                                  acc[t][k][e]);
+    arrive_reduce<RS>(d, rt, contributors, lane);
+}
+
 // Workgroup b's range of (row tile, group) items.
 template <int RS, int PF>
 __device__ void gemm_streamk(const GemmDesc &d, int64_t b, uint8_t *stage) {
@@ -621,6 +647,164 @@ __device__ void gemm_streamk(const GemmDesc &d, int64_t b, uint8_t *stage) {
             const int64_t first = sk_owner((int64_t)rt * G, N, W);
             const int64_t contributors = sk_owner((int64_t)rt * G + G - 1, N, W) - first + 1;
             partial_tile<RS>(d, rt, (int)(b - first), (int)contributors, lane, acc);
+        }
+        it += g1 - g0;
+    }
+}
+
+// ---------------------------------------------------------------- small m, vector units
+// Y = X W^T for m = M rows of X (2 <= M <= 4) in the matvec's layout: one
+// lane per super-row, the group's 17 chunks of W and the x slices of all M
+// rows arrive by the same direct loads, and every quant is converted once and
+// then used for each row.  Per row, the arithmetic is the matvec's (four
+// chains of eight per block, the block sum scaled once, groups into four
+// slots).  Work is split stream-K style like the matrix-core kernel's.
+// One stage: the group's W, then its x slices of all M rows.
+template <int M>
+struct VStage {
+    static constexpr int kBytes = kStageW + M * kStageX;
+};
+
+// d and S_i = sum_j q_j x_i[j] for block K and each row i of X.
+template <int K, int M>
+__device__ __forceinline__ void block_terms_m(const uint32_t (&D)[68], const uint8_t *xst,
+                                              float &d, float (&s)[M]) {
+    constexpr int sb = K * kBlockBytes;
+    d = half_to_float(D[sb >> 2] >> ((sb & 3) * 8));
+    float q[kQuants];
+#pragma unroll
+    for (int j = 0; j < kQuants; ++j) q[j] = quant(D, sb + 2 + j);
+#pragma unroll
+    for (int i = 0; i < M; ++i) {
+        const float4 *xs = reinterpret_cast<const float4 *>(xst + i * kStageX);
+        float a0 = 0.f, a1 = 0.f, a2 = 0.f, a3 = 0.f;
+#pragma unroll
+        for (int j = 0; j < kQuants; j += 4) {
+            const float4 xv = xs[(K * kQuants + j) / 4];
+            a0 = fmaf(q[j + 0], xv.x, a0);
+            a1 = fmaf(q[j + 1], xv.y, a1);
+            a2 = fmaf(q[j + 2], xv.z, a2);
+            a3 = fmaf(q[j + 3], xv.w, a3);
+        }
+        s[i] = (a0 + a1) + (a2 + a3);
+    }
+}
+
+template <int RS, int M>
+__device__ __forceinline__ void group_dot_m(const uint32_t (&D)[68], const uint8_t *xst,
+                                            const GemmDesc &gd, int kk,
+                                            float (&acc)[M][kSlots][RS]) {
+    const int slot = kk & (kSlots - 1);
+    float sub[M], s[M], d;
+#pragma unroll
+    for (int i = 0; i < M; ++i) sub[i] = 0.f;
+    int r = 0, cb = 0;
+    if (RS > 1) {
+        const int bp = kk * kGroupBlocks;
+        r = bp / gd.nb;
+        cb = bp - r * gd.nb;
+    }
+    // A block's sums are finished before the next block's x is read: the
+    // compiler would otherwise read all eight blocks' x (8 * M * 32 floats)
+    // up front and run out of registers.
+#define Q8_VSTEP(K)                                                             \
+    block_terms_m<K, M>(D, xst, d, s);                                          \
+    _Pragma("unroll") for (int i = 0; i < M; ++i) {                             \
+        sub[i] = fmaf(d, s[i], sub[i]);                                         \
+        asm volatile("" : "+v"(sub[i]) :: "memory");                            \
+    }                                                                           \
+    if (RS > 1 && ++cb == gd.nb) {                                              \
+        _Pragma("unroll") for (int i = 0; i < M; ++i) {                         \
+            flush_row<RS>(acc[i], slot, r, sub[i]);                             \
+            sub[i] = 0.f;                                                       \
+        }                                                                       \
+        cb = 0;                                                                 \
+        ++r;                                                                    \
+    }
+    Q8_VSTEP(0) Q8_VSTEP(1) Q8_VSTEP(2) Q8_VSTEP(3)
+    Q8_VSTEP(4) Q8_VSTEP(5) Q8_VSTEP(6) Q8_VSTEP(7)
+#undef Q8_VSTEP
+#pragma unroll
+    for (int i = 0; i < M; ++i) flush_row<RS>(acc[i], slot, RS == 1 ? 0 : r, sub[i]);
+}
+
+// Groups [g0, g1) of row tile rt, double-buffered: the next group's loads
+// stream while this one is computed.  (Two groups in flight, with a ring of
+// three x stages, measured no faster: the x reads, not the loads, bound it.)
+template <int RS, int M>
+__device__ void vsmall_run(const GemmDesc &d, int rt, int g0, int g1, uint8_t *stage,
+                           float (&acc)[M][kSlots][RS]) {
+    constexpr int SB = VStage<M>::kBytes;
+    const int lane = lane_id();
+    const int64_t sr0 = (int64_t)rt * kWave;
+    const int last = (int)min((int64_t)d.nsr - 1 - sr0, (int64_t)kWave - 1);
+    const uint8_t *wt = d.w + sr0 * d.sr_bytes;
+    uint32_t off[kGroupChunks];
+    chunk_offsets(off, lane, last, d.sr_bytes);
+    // lane l carries floats 4(l%8) .. +3 of block l/8 of the group
+    const int xb = lane >> 3, xo = 4 * (lane & 7);
+    auto issue = [&](int kk, uint8_t *st) {
+        const uint32_t l0 = __builtin_amdgcn_readfirstlane(lds_addr(st));
+        const uint8_t *gb = uniform_ptr(wt + (int64_t)kk * kGroupBytes);
+#pragma unroll
+        for (int c = 0; c < kGroupChunks; ++c) dma16_s(gb, off[c], l0 + kWave * 16 * c);
+        int b = kk * kGroupBlocks + xb;
+        if (RS > 1) b %= d.nb;
+#pragma unroll
+        for (int i = 0; i < M; ++i)
+            dma16_v(d.X + (int64_t)i * d.n + (int64_t)b * kQuants + xo, l0 + kStageW + i * kStageX);
+    };
+    if (g0 < g1) issue(g0, stage);
+    for (int kk = g0; kk < g1; ++kk) {
+        uint8_t *cur = stage + ((kk - g0) & 1) * SB;
+        uint32_t D[68];
+        wait_vm_asm<0>();   // this group's W and x have landed
+        read_group(cur, lane, D);
+        // the other stage was last read by the previous group, whose reads
+        // have all returned (their values are used)
+        if (kk + 1 < g1) issue(kk + 1, stage + ((kk + 1 - g0) & 1) * SB);
+        group_dot_m<RS, M>(D, cur + kStageW, d, kk, acc);
+    }
+}
+
+template <int RS, int M>
+__device__ void vsmall_streamk(const GemmDesc &d, int64_t b, uint8_t *stage) {
+    const int lane = lane_id();
+    const int64_t G = d.gsr, N = (int64_t)d.row_tiles * G, W = d.fast_wgs;
+    int64_t it = sk_first_item(b, N, W);
+    const int64_t end = sk_first_item(b + 1, N, W);
+    while (it < end) {
+        const int rt = (int)(it / G);
+        const int g0 = (int)(it - (int64_t)rt * G);
+        const int g1 = (int)min(G, (int64_t)g0 + (end - it));
+        float acc[M][kSlots][RS];
+#pragma unroll
+        for (int i = 0; i < M; ++i)
+#pragma unroll
+            for (int q = 0; q < kSlots; ++q)
+#pragma unroll
+                for (int k = 0; k < RS; ++k) acc[i][q][k] = 0.f;
+        vsmall_run<RS, M>(d, rt, g0, g1, stage, acc);
+        const int64_t sr = (int64_t)rt * kWave + lane;
+        if (g0 == 0 && g1 == G) {
+            if (sr < d.nsr)
+#pragma unroll
+                for (int i = 0; i < M; ++i)
+#pragma unroll
+                    for (int k = 0; k < RS; ++k)
+                        d.Y[(int64_t)i * d.p + sr * RS + k] =
+                            combine_slots(acc[i][0][k], acc[i][1][k], acc[i][2][k], acc[i][3][k]);
+        } else {
+            const int64_t first = sk_owner((int64_t)rt * G, N, W);
+            const int64_t contributors = sk_owner((int64_t)rt * G + G - 1, N, W) - first + 1;
+            float *mine = partial_slot<RS>(d, rt, (int)(b - first));
+#pragma unroll
+            for (int i = 0; i < M; ++i)
+#pragma unroll
+                for (int k = 0; k < RS; ++k)
+                    store_partial(mine + i * (kWave * RS) + lane * RS + k,
+                                  combine_slots(acc[i][0][k], acc[i][1][k], acc[i][2][k], acc[i][3][k]));
+            arrive_reduce<RS>(d, rt, (int)contributors, lane);
         }
         it += g1 - g0;
     }
@@ -713,6 +897,20 @@ __global__ __launch_bounds__(kWave, PF == 0 ? 2 : 1) void k_q8_gemm_mfma(GemmDes
     }
 }
 
+template <int RS, int M>
+__global__ __launch_bounds__(kWave) void k_q8_gemm_valu(GemmDesc d) {
+    __shared__ __attribute__((aligned(16))) uint8_t stage[2 * VStage<M>::kBytes];
+    const uint32_t bid = blockIdx.x;
+    if (bid < (uint32_t)d.fast_wgs) {
+        vsmall_streamk<RS, M>(d, bid, stage);
+    } else {
+        OpDesc t;
+        t.x = d.X; t.w = d.w; t.y = d.Y; t.nb = d.nb; t.p = d.p; t.m = d.m;
+        t.x_stride = d.n; t.y_stride = d.p; t.tail_row0 = d.tail_row0;
+        tail_tile(t, bid - d.fast_wgs, 1);
+    }
+}
+
 }  // namespace
 
 namespace {
@@ -771,6 +969,40 @@ hipError_t launch_gemm_mfma(const GemmDesc &d, int pf, int64_t grid, hipStream_t
         default: return hipErrorInvalidValue;
     }
     return hipGetLastError();
+}
+
+int gemm_valu_stage_bytes(int m) {
+    switch (m) {
+        case 2: return 2 * VStage<2>::kBytes;
+        case 3: return 2 * VStage<3>::kBytes;
+        case 4: return 2 * VStage<4>::kBytes;
+        default: return 0;
+    }
+}
+
+namespace {
+template <int RS>
+hipError_t launch_valu_rs(const GemmDesc &d, const dim3 &gr, hipStream_t s) {
+    const dim3 bl(kWave);
+    switch (d.m) {
+        case 2: hipLaunchKernelGGL((k_q8_gemm_valu<RS, 2>), gr, bl, 0, s, d); break;
+        case 3: hipLaunchKernelGGL((k_q8_gemm_valu<RS, 3>), gr, bl, 0, s, d); break;
+        case 4: hipLaunchKernelGGL((k_q8_gemm_valu<RS, 4>), gr, bl, 0, s, d); break;
+        default: return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+}
+}  // namespace
+
+hipError_t launch_gemm_valu(const GemmDesc &d, int64_t grid, hipStream_t s) {
+    const dim3 gr((unsigned)grid);
+    switch (d.rs) {
+        case 1: return launch_valu_rs<1>(d, gr, s);
+        case 2: return launch_valu_rs<2>(d, gr, s);
+        case 4: return launch_valu_rs<4>(d, gr, s);
+        case 8: return launch_valu_rs<8>(d, gr, s);
+        default: return hipErrorInvalidValue;
+    }
 }
 
 }  // namespace q8

@@ -165,16 +165,28 @@ def test_determinism_canaries_and_sign(q8, n, p):
     assert np.array_equal(down(y), a * 4)
 
 
-@pytest.mark.parametrize("m", [1, 2, 3, 4, 5, 8, 13, 16])
-@pytest.mark.parametrize("n,p", [(256, 130), (896, 70), (896, 71), (3584, 300), (160, 11),
-                                 (18944, 70), (1024, 3072)], ids=lambda v: str(v))
-def test_gemm_smallm(q8, m, n, p):
+GEMM_SHAPES = [(256, 130), (896, 70), (896, 71), (3584, 300), (160, 11), (192, 37),
+               (18944, 70), (1024, 3072)]
+
+# (m, path): by default m >= 2 runs on the matrix cores where n is a multiple
+# of 128 and on the vector units (four rows of X per pass) elsewhere;
+# Q8GEMV_SMALLM_PATH=valu forces the vector kernel for every width.
+GEMM_CASES = ([(m, None) for m in (1, 2, 3, 4, 5, 8, 13, 16)] +
+              [(m, "valu") for m in (2, 3, 4, 5, 8, 13, 16)])
+
+
+@pytest.mark.parametrize("m,path", GEMM_CASES, ids=lambda v: str(v))
+@pytest.mark.parametrize("n,p", GEMM_SHAPES, ids=lambda v: str(v))
+def test_gemm_smallm(q8, monkeypatch, m, path, n, p):
     """Each row of Y against its own oracle matvec; bitwise repeatable.
-    (3584, 300) and (18944, 70) have few row tiles, so K is split over
-    workgroups and the last part to arrive adds the parts; (896, 71) has a
-    tail row; (160, 11) has 4-row super-rows and runs as m matvecs."""
+    (3584, 300) and (18944, 70) have few row tiles, so a row tile's groups
+    are split over workgroups and the last to arrive adds the parts;
+    (896, 71) has a tail row; (192, 37) and (160, 11) have 4- and 8-row
+    super-rows, which only the vector kernel takes."""
     import torch
-    log("gemm m=%d n=%d p=%d" % (m, n, p))
+    if path:
+        monkeypatch.setenv("Q8GEMV_SMALLM_PATH", path)
+    log("gemm m=%d n=%d p=%d path=%s" % (m, n, p, path or "default"))
     rng = np.random.default_rng(300 + 11 * m + n + p)
     w = synth.q8_weights(n, p, rng)
     X = synth.activations(n, rng, m).reshape(m, n)
