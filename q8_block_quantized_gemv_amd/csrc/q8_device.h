@@ -1,0 +1,162 @@
+// q8_device.h -- device helpers shared by the matvec (q8_gemv.hip) and the
+// small-batch kernels (q8_gemm.hip): lane bookkeeping, the direct
+// HBM -> LDS loads, the 17-chunk group layout, the per-row summation slots
+// and the generic path for tail rows.  Included by one kernel source each,
+// inside an anonymous namespace, so each keeps its own copy.
+#pragma once
+
+#include "q8_internal.h"
+
+namespace q8 {
+namespace {
+
+typedef const __attribute__((address_space(1))) uint16_t GHalf;
+
+__device__ __forceinline__ int lane_id() { return threadIdx.x & (kWave - 1); }
+__device__ __forceinline__ int wave_id() {
+    return __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+}
+
+// binary16 bit pattern in the low half of v -> float (v_cvt_f32_f16; exact,
+// subnormals included, Inf/NaN propagate).
+__device__ __forceinline__ float half_to_float(uint32_t v) {
+    return (float)__builtin_bit_cast(_Float16, (uint16_t)(v & 0xffffu));
+}
+
+// Signed quant at byte `idx` of the group held in D (idx is a constant after
+// unrolling, so this is one v_cvt_f32_i32 with an SDWA sign-extended byte).
+__device__ __forceinline__ float quant(const uint32_t (&D)[68], int idx) {
+    return (float)(int8_t)(D[idx >> 2] >> ((idx & 3) * 8));
+}
+
+// Per-lane byte offsets (from the wave's first super-row) of the 17 chunks
+// this lane moves for each group: load i of lane l carries chunk c of local
+// super-row s where 17*s + c = 64*i + l, so that lane l later finds its own
+// super-row's 272 bytes at LDS offset 272*l.  Super-rows past `last` are
+// clamped to `last` (their results are never stored).
+__device__ __forceinline__ void chunk_offsets(uint32_t (&off)[kGroupChunks], int lane,
+                                              int last, int64_t sr_bytes) {
+#pragma unroll
+    for (int i = 0; i < kGroupChunks; ++i) {
+        const int slot = kWave * i + lane;
+        int s = slot / kGroupChunks;
+        const int c = slot - s * kGroupChunks;
+        s = s < last ? s : last;
+        off[i] = (uint32_t)((int64_t)s * sr_bytes + 16 * c);
+    }
+}
+
+// The kernels issue their direct loads from inline asm.  The compiler tracks
+// LDS-DMA it emits itself and, unable to tell the two stages apart, waits
+// for ALL outstanding loads before any LDS read -- which would stall every
+// compute phase on the next group's loads.  Issued from asm, the loads are
+// invisible to that tracking, and the kernel orders them itself: wait_vm_asm
+// (a memory barrier for the compiler) before a stage is read, and a stage is
+// refilled only after its last read.  m0 carries the LDS address; nothing
+// else in these kernels uses m0.
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+// 16 bytes per lane: global (sbase + voff) -> LDS (m0 + 16 * lane)
+__device__ __forceinline__ void dma16_s(const uint8_t *sbase, uint32_t voff, uint32_t lds) {
+    asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2"
+                 :: "s"(lds), "v"(voff), "s"(sbase) : "memory", "m0");
+}
+// 16 bytes per lane: global (per-lane address) -> LDS (m0 + 16 * lane)
+__device__ __forceinline__ void dma16_v(const void *addr, uint32_t lds) {
+    asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off"
+                 :: "s"(lds), "v"(addr) : "memory", "m0");
+}
+#pragma clang diagnostic pop
+
+template <int N>
+__device__ __forceinline__ void wait_vm_asm() {
+    static_assert(N >= 0 && N < 64, "vmcnt is 6 bits");
+    asm volatile("s_waitcnt vmcnt(%0)" :: "n"(N) : "memory");
+}
+
+// A pointer that is the same in every lane, made visibly so for the
+// compiler (it goes into a scalar register pair).
+__device__ __forceinline__ const uint8_t *uniform_ptr(const uint8_t *p) {
+    const uint64_t v = (uint64_t)(uintptr_t)p;
+    const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
+    const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
+    return (const uint8_t *)(uintptr_t)(((uint64_t)hi << 32) | lo);
+}
+
+__device__ __forceinline__ uint32_t lds_addr(const uint8_t *p) {
+    return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) uint8_t *)p;
+}
+
+// This lane's 272 bytes of a staged group -> 68 dwords.
+__device__ __forceinline__ void read_group(const uint8_t *st, int lane, uint32_t (&D)[68]) {
+    const uint4 *src = reinterpret_cast<const uint4 *>(st + kGroupBytes * lane);
+#pragma unroll
+    for (int c = 0; c < kGroupChunks; ++c) {
+        const uint4 v = src[c];
+        D[4 * c + 0] = v.x;
+        D[4 * c + 1] = v.y;
+        D[4 * c + 2] = v.z;
+        D[4 * c + 3] = v.w;
+    }
+}
+
+constexpr int kSlots = 4;
+
+// acc[slot][r] += v for a uniform slot and row index (unrolled selects).
+template <int RS>
+__device__ __forceinline__ void flush_row(float (&acc)[kSlots][RS], int slot, int r, float v) {
+#pragma unroll
+    for (int q = 0; q < kSlots; ++q)
+#pragma unroll
+        for (int k = 0; k < RS; ++k)
+            if (q == slot && k == r) acc[q][k] += v;
+}
+
+__device__ __forceinline__ float combine_slots(float s0, float s1, float s2, float s3) {
+    return (s0 + s1) + (s2 + s3);
+}
+
+// ---------------------------------------------------------------- tail rows
+// Generic path for the last p % rs rows: one wave per row, lane l takes
+// blocks l, l+64, ...; blocks are read with 2-byte loads (a block is only
+// 2-byte aligned in general).  Per-lane sums are flushed every 8 blocks and
+// the 64 lanes meet in a fixed butterfly.
+__device__ void tail_tile(const OpDesc &op, uint32_t tile, int waves) {
+    const int lane = lane_id();
+    const int wave = wave_id();
+    const int64_t row = (int64_t)op.tail_row0 + (int64_t)tile * waves + wave;
+    if (row >= op.p) return;
+    const int nb = op.nb;
+    const uint8_t *wr = op.w + row * (int64_t)nb * kBlockBytes;
+    for (int i = 0; i < op.m; ++i) {
+        const __attribute__((address_space(1))) float *x =
+            (const __attribute__((address_space(1))) float *)(op.x + (int64_t)i * op.x_stride);
+        float acc = 0.f, sub = 0.f;
+        int cnt = 0;
+        for (int b = lane; b < nb; b += kWave) {
+            GHalf *blk = (GHalf *)(wr + (int64_t)b * kBlockBytes);
+            const float d = half_to_float(blk[0]);
+            const __attribute__((address_space(1))) float *xb = x + (int64_t)b * kQuants;
+            float a0 = 0.f, a1 = 0.f;
+#pragma unroll
+            for (int j = 0; j < kQuants / 2; ++j) {
+                const uint32_t v = blk[1 + j];
+                a0 = fmaf((float)(int8_t)(v & 0xffu), xb[2 * j], a0);
+                a1 = fmaf((float)(int8_t)(v >> 8), xb[2 * j + 1], a1);
+            }
+            sub = fmaf(d, a0 + a1, sub);
+            if (++cnt == 8) { acc += sub; sub = 0.f; cnt = 0; }
+        }
+        acc += sub;
+#pragma unroll
+        for (int o = kWave / 2; o > 0; o >>= 1) acc += __shfl_xor(acc, o, kWave);
+        if (lane == 0) op.y[(int64_t)i * op.y_stride + row] = acc;
+    }
+    // Settle this path's loads and stores here: the structurizer can merge
+    // its flow into the fast path's, and the compiler's wait tracking would
+    // otherwise carry them into the fast path's streaming loop as waits.
+    __builtin_amdgcn_s_waitcnt(0);
+}
+
+}  // namespace
+}  // namespace q8

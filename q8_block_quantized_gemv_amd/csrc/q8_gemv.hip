@@ -1,0 +1,272 @@
+// q8_gemv.hip -- gfx950 kernels for the Q8_0 decode matvec (m = 1): the
+// standalone launch and the fused launch of a chain.
+//
+// What is computed (page "IV.4: One command buffer per token", section
+// "Eight kernels", q8_matvec): y[r] = sum_b d(r,b) * sum_j q(r,b,j) x[32b+j],
+// accumulated within a block, scaled once per block.
+//
+// How, on CDNA4 (the page's one-SIMD-group-per-row layout is not used):
+//
+//  * One lane owns one output row (or one "super-row" of rs rows, see
+//    OpDesc).  All lanes of a wave walk the same columns at the same time,
+//    so x is wave-uniform: one x value feeds 64 rows.
+//  * W moves HBM -> LDS with gfx950's direct global_load_lds_dwordx4: eight
+//    blocks are 272 bytes = 17 aligned 16-byte chunks, so a wave's 64 rows
+//    of one "group" are 17 fully used 16-byte loads per lane, and inside a
+//    group every scale and quant sits at a compile-time byte offset.  The
+//    group's 256 x values (1 KB, L2-resident) ride along as an 18th direct
+//    load, so x never waits on its own trip through a saturated memory
+//    system; the compute reads it back with LDS broadcast reads.  Each
+//    wave double-buffers its own groups (the next group streams in while the
+//    current one is computed), so there are no workgroup barriers on the
+//    streaming path.
+//  * Quant bytes become float with one SDWA conversion each; products go
+//    into four independent float32 chains per block; the block sum is scaled
+//    once; per-group and per-row subtotals keep every summation chain short
+//    (<= ~100 roundings at the largest shapes, so the accuracy bound of
+//    1e-5 * sum|w x| holds for all finite inputs, not only random ones).
+//  * Every row sums its groups into four slots (group kk into slot kk % 4)
+//    and finishes with (s0 + s1) + (s2 + s3).  When the waves of a workgroup
+//    split one row tile's groups (ks = 2 or 4) each slot still has exactly
+//    one owner, and the slots meet in LDS: the rounding of every output is
+//    the same whatever ks, launch or batch size, so results are bitwise
+//    reproducible and a chain's outputs equal standalone calls' bit for bit.
+//    There are no atomics.
+//  * Rows that do not fill a whole super-row take a simple generic path
+//    (one wave per row, lanes across blocks, 2-byte loads).
+#include "q8_device.h"
+
+namespace q8 {
+namespace {
+
+// Block K (0..7) of a group: d and S = sum_j q_j x_j (four chains of eight).
+// xs is the group's x slice in LDS (the same address for every lane).
+template <int K>
+__device__ __forceinline__ void block_terms(const uint32_t (&D)[68], const float4 *xs,
+                                            float &d, float &s) {
+    constexpr int sb = K * kBlockBytes;
+    d = half_to_float(D[sb >> 2] >> ((sb & 3) * 8));
+    float a0 = 0.f, a1 = 0.f, a2 = 0.f, a3 = 0.f;
+#pragma unroll
+    for (int j = 0; j < kQuants; j += 4) {
+        const float4 xv = xs[(K * kQuants + j) / 4];
+        a0 = fmaf(quant(D, sb + 2 + j + 0), xv.x, a0);
+        a1 = fmaf(quant(D, sb + 2 + j + 1), xv.y, a1);
+        a2 = fmaf(quant(D, sb + 2 + j + 2), xv.z, a2);
+        a3 = fmaf(quant(D, sb + 2 + j + 3), xv.w, a3);
+    }
+    s = (a0 + a1) + (a2 + a3);
+}
+
+// direct loads per group of the matvec: 17 of W and one of x
+constexpr int kLoadsPerGroup = kGroupChunks + 1;
+
+// Where lane `lane` finds its 16 bytes of the x slice of group kk: floats
+// 4*(lane%8) .. +3 of block lane/8 of the group, i.e. of column block
+// (8*kk + lane/8) mod nb (a group of a super-row wraps past the row end).
+template <int RS>
+__device__ __forceinline__ const float *x_slice_src(const OpDesc &op, int kk, int lane) {
+    int b = kk * kGroupBlocks + (lane >> 3);
+    if (RS > 1) b %= op.nb;
+    return op.x + (int64_t)b * kQuants + 4 * (lane & 7);
+}
+
+// One group: 17 loads of W and one load of its x slice (at st + kStageW).
+template <int RS>
+__device__ __forceinline__ void dma_group_x(const uint8_t *g, const uint32_t (&off)[kGroupChunks],
+                                            uint8_t *st, const OpDesc &op, int kk, int lane) {
+    const uint32_t l0 = __builtin_amdgcn_readfirstlane(lds_addr(st));
+#pragma unroll
+    for (int i = 0; i < kGroupChunks; ++i) dma16_s(g, off[i], l0 + kWave * 16 * i);
+    dma16_v(x_slice_src<RS>(op, kk, lane), l0 + kStageW);
+}
+
+// ---------------------------------------------------------------- m = 1
+// One group (8 blocks) of this lane's super-row, accumulated into acc.
+template <int RS>
+__device__ __forceinline__ void group_dot(const uint32_t (&D)[68], const float4 *xs,
+                                          const OpDesc &op, int kk, float (&acc)[kSlots][RS]) {
+    const int slot = kk & (kSlots - 1);
+    float sub = 0.f, d, s;
+    if constexpr (RS == 1) {
+        // rows are whole groups: group kk is blocks 8kk .. 8kk+7 of the row
+        block_terms<0>(D, xs, d, s); sub = fmaf(d, s, sub);
+        block_terms<1>(D, xs, d, s); sub = fmaf(d, s, sub);
+        block_terms<2>(D, xs, d, s); sub = fmaf(d, s, sub);
+        block_terms<3>(D, xs, d, s); sub = fmaf(d, s, sub);
+        block_terms<4>(D, xs, d, s); sub = fmaf(d, s, sub);
+        block_terms<5>(D, xs, d, s); sub = fmaf(d, s, sub);
+        block_terms<6>(D, xs, d, s); sub = fmaf(d, s, sub);
+        block_terms<7>(D, xs, d, s); sub = fmaf(d, s, sub);
+        flush_row<1>(acc, slot, 0, sub);
+    } else {
+        // a group may cross row boundaries inside the super-row; where it
+        // does is the same for every lane (uniform branches)
+        const int bp = kk * kGroupBlocks;
+        int r = bp / op.nb;
+        int cb = bp - r * op.nb;
+#define Q8_STEP(K)                                                   \
+        block_terms<K>(D, xs, d, s);                                 \
+        sub = fmaf(d, s, sub);                                       \
+        if (++cb == op.nb) { flush_row<RS>(acc, slot, r, sub); sub = 0.f; cb = 0; ++r; }
+        Q8_STEP(0) Q8_STEP(1) Q8_STEP(2) Q8_STEP(3)
+        Q8_STEP(4) Q8_STEP(5) Q8_STEP(6) Q8_STEP(7)
+#undef Q8_STEP
+        flush_row<RS>(acc, slot, r, sub);
+    }
+}
+
+// One workgroup tile of NW waves: NW/ks row tiles of 64 super-rows, each
+// row tile's groups split over ks waves.  PF is how many groups each wave
+// keeps in flight ahead of the one it computes (1 or 2; each stage holds one
+// group, and with PF = 2 the stage a group was computed from is refilled
+// right after that group's compute, so two groups stream while one waits).
+template <int RS, int NW, int PF>
+__device__ void fast_tile(const OpDesc &op, uint32_t tile, uint8_t *stage) {
+    const int lane = lane_id();
+    const int wave = wave_id();
+    const int ks = op.ks;
+    const int rt = wave / ks;                 // row tile within the workgroup
+    const int ksl = wave - rt * ks;           // this wave's share of the groups
+    const int tiles_per_wg = NW / ks;
+    const int64_t sr0 = ((int64_t)tile * tiles_per_wg + rt) * kWave;
+    const int nsr = op.nsr;
+    uint8_t *st0 = stage + (size_t)wave * (kBufs * kStageBytes);
+
+    float acc[kSlots][RS];
+#pragma unroll
+    for (int q = 0; q < kSlots; ++q)
+#pragma unroll
+        for (int k = 0; k < RS; ++k) acc[q][k] = 0.f;
+
+    if (sr0 < nsr) {
+        const int G = op.gsr;
+        const int64_t srb = op.sr_bytes;
+        const uint8_t *wt = op.w + sr0 * srb;
+        const int last = (int)min((int64_t)nsr - 1 - sr0, (int64_t)kWave - 1);
+        uint32_t off[kGroupChunks];
+        chunk_offsets(off, lane, last, srb);
+        const int ng = (G - ksl + ks - 1) / ks;  // groups kk = ksl + ks*t, t < ng
+        auto issue = [&](int t) {
+            const int kk = ksl + ks * t;
+            dma_group_x<RS>(wt + (int64_t)kk * kGroupBytes, off, st0 + (t & 1) * kStageBytes, op,
+                            kk, lane);
+        };
+        if (ng > 0) issue(0);
+        if (PF == 2 && ng > 1) issue(1);
+        for (int t = 0; t < ng; ++t) {
+            uint8_t *cur = st0 + (t & 1) * kStageBytes;
+            uint32_t D[68];
+            // this group's W and x have landed in LDS (loads complete in order)
+            if (PF == 2 && t + 1 < ng) wait_vm_asm<kLoadsPerGroup>();
+            else wait_vm_asm<0>();
+            read_group(cur, lane, D);
+            if (PF == 1 && t + 1 < ng) issue(t + 1);
+            group_dot<RS>(D, reinterpret_cast<const float4 *>(cur + kStageW), op, ksl + ks * t, acc);
+            if (PF == 2 && t + 2 < ng) issue(t + 2);   // into the stage just consumed
+        }
+    }
+
+    if (ks > 1) {
+        // Slot q belongs to wave (q % ks) of the row tile, which parks it in
+        // its own (now idle) first stage: red_w[(q / ks) * RS + k][lane].
+        // Its last direct load completed before its last group was read.
+        float *mine = reinterpret_cast<float *>(st0);
+#pragma unroll
+        for (int q = 0; q < kSlots; ++q)
+            if (q % ks == ksl)
+#pragma unroll
+                for (int k = 0; k < RS; ++k) mine[((q / ks) * RS + k) * kWave + lane] = acc[q][k];
+        __syncthreads();
+        if (ksl == 0) {
+#pragma unroll
+            for (int q = 1; q < kSlots; ++q) {
+                const int owner = rt * ks + q % ks;
+                const float *theirs = reinterpret_cast<const float *>(
+                    stage + (size_t)owner * (kBufs * kStageBytes));
+                if (owner != wave)
+#pragma unroll
+                    for (int k = 0; k < RS; ++k) acc[q][k] = theirs[((q / ks) * RS + k) * kWave + lane];
+            }
+        }
+    }
+    if (ksl == 0 && sr0 + lane < nsr) {
+        float *yr = op.y + (sr0 + lane) * RS;
+#pragma unroll
+        for (int k = 0; k < RS; ++k) yr[k] = combine_slots(acc[0][k], acc[1][k], acc[2][k], acc[3][k]);
+    }
+}
+
+template <int NW, int PF>
+__device__ __forceinline__ void run_tile(const OpDesc &op, uint32_t t, uint8_t *stage) {
+    if (t & kTailBit) {
+        tail_tile(op, t & ~kTailBit, NW);
+        return;
+    }
+    switch (op.rs) {
+        case 1: fast_tile<1, NW, PF>(op, t, stage); break;
+        case 2: fast_tile<2, NW, PF>(op, t, stage); break;
+        case 4: fast_tile<4, NW, PF>(op, t, stage); break;
+        default: fast_tile<8, NW, PF>(op, t, stage); break;
+    }
+}
+
+template <int NW, int PF>
+__global__ __launch_bounds__(NW * kWave) void k_q8_gemv(OpDesc op) {
+    __shared__ __attribute__((aligned(16))) uint8_t stage[NW * kBufs * kStageBytes];
+    uint32_t t = blockIdx.x;
+    if (t >= (uint32_t)op.fast_tiles) t = (t - op.fast_tiles) | kTailBit;
+    run_tile<NW, PF>(op, t, stage);
+}
+
+template <int NW, int PF>
+__global__ __launch_bounds__(NW * kWave) void k_q8_gemv_fused(const OpDesc *__restrict__ ops,
+                                                              const Tile *__restrict__ tiles) {
+    __shared__ __attribute__((aligned(16))) uint8_t stage[NW * kBufs * kStageBytes];
+    const Tile tl = tiles[blockIdx.x];
+    const OpDesc op = ops[tl.op];
+    run_tile<NW, PF>(op, tl.tile, stage);
+}
+
+}  // namespace
+
+namespace {
+template <int NW, int PF>
+hipError_t launch_single_t(const OpDesc &op, int64_t grid, hipStream_t s) {
+    hipLaunchKernelGGL((k_q8_gemv<NW, PF>), dim3((unsigned)grid), dim3(NW * kWave), 0, s, op);
+    return hipGetLastError();
+}
+template <int NW, int PF>
+hipError_t launch_fused_t(const OpDesc *d_ops, const Tile *d_tiles, int64_t grid, hipStream_t s) {
+    hipLaunchKernelGGL((k_q8_gemv_fused<NW, PF>), dim3((unsigned)grid), dim3(NW * kWave), 0, s,
+                       d_ops, d_tiles);
+    return hipGetLastError();
+}
+}  // namespace
+
+hipError_t launch_gemv_single(const OpDesc &op, const Variant &v, int64_t grid, hipStream_t s) {
+    switch (v.nw * 10 + v.pf) {
+        case 11: return launch_single_t<1, 1>(op, grid, s);
+        case 12: return launch_single_t<1, 2>(op, grid, s);
+        case 21: return launch_single_t<2, 1>(op, grid, s);
+        case 22: return launch_single_t<2, 2>(op, grid, s);
+        case 41: return launch_single_t<4, 1>(op, grid, s);
+        case 42: return launch_single_t<4, 2>(op, grid, s);
+        default: return hipErrorInvalidValue;
+    }
+}
+
+hipError_t launch_gemv_fused(const OpDesc *d_ops, const Tile *d_tiles, const Variant &v,
+                             int64_t grid, hipStream_t s) {
+    switch (v.nw * 10 + v.pf) {
+        case 11: return launch_fused_t<1, 1>(d_ops, d_tiles, grid, s);
+        case 12: return launch_fused_t<1, 2>(d_ops, d_tiles, grid, s);
+        case 21: return launch_fused_t<2, 1>(d_ops, d_tiles, grid, s);
+        case 22: return launch_fused_t<2, 2>(d_ops, d_tiles, grid, s);
+        case 41: return launch_fused_t<4, 1>(d_ops, d_tiles, grid, s);
+        case 42: return launch_fused_t<4, 2>(d_ops, d_tiles, grid, s);
+        default: return hipErrorInvalidValue;
+    }
+}
+
+}  // namespace q8

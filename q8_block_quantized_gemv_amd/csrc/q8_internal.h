@@ -106,7 +106,8 @@ inline int64_t tail_tiles_for(int64_t tail_rows, int nw = kWaves) {
     return (tail_rows + nw - 1) / nw;
 }
 
-// Kernel launchers (q8_kernels.hip).  All return the hipError_t of the launch.
+// Kernel launchers (q8_gemv.hip, q8_gemm.hip).  All return the hipError_t of
+// the launch.
 hipError_t launch_gemv_single(const OpDesc &op, const Variant &v, int64_t grid, hipStream_t s);
 hipError_t launch_gemv_fused(const OpDesc *d_ops, const Tile *d_tiles, const Variant &v,
                              int64_t grid, hipStream_t s);
