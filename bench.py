@@ -224,28 +224,22 @@ def main():
         per_step * 1e6, value, 100 * value / HBM_PEAK_GBS, t_wall))
 
     # per-launch view of the dominant kernel: the fused chain is one kernel.
-    # Each of K launches (the chain issued directly, no graph around it) sits
-    # between its own pair of events on the launch stream, so the median is
-    # that kernel's duration without the graph's launch gap.
+    # K launches of it issued directly (no graph around them), back to back on
+    # the launch stream between one pair of events: the average is that
+    # kernel's duration plus the dispatch gap between consecutive launches.
     launches = chain.launches
-    durations = []
-    for _ in range(args.steps):
-        e0 = torch.cuda.Event(enable_timing=True)
-        e1 = torch.cuda.Event(enable_timing=True)
-        e0.record(stream)
-        chain.run(q8.MODE_EAGER, stream)
-        e1.record(stream)
-        durations.append((e0, e1))
-    torch.cuda.synchronize()
-    kernel_s = float(np.median([a.elapsed_time(b) for a, b in durations])) / 1e3 / launches
+    kernel_s = time_steps(lambda: chain.run(q8.MODE_EAGER, stream), args.steps) / args.steps / launches
     achieved = nbytes / launches / kernel_s / 1e9
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                 "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                 "traffic": measured_traffic(args.workload),
-                "kernel": "k_q8_gemv_fused", "launches_per_step": launches,
+                # a chain of one op is that op's standalone launch (four-wave
+                # workgroups); more independent ops share one fused launch
+                "kernel": "k_q8_gemv_fused<1,1>" if len(ops_shape) > 1 else "k_q8_gemv<4,1>",
+                "launches_per_step": launches,
                 "algorithmic_bytes_per_launch": nbytes // launches,
                 "kernel_us": round(kernel_s * 1e6, 2),
-                "timing": "median of %d single launches, HIP events on the launch stream" % args.steps}
+                "timing": "%d back-to-back launches between HIP events on the launch stream" % args.steps}
 
     modes = {"fused_graph_us": round(per_step * 1e6, 2), "fused_graph_cold_first_us": round(cold * 1e6, 2)}
     if not args.no_modes:
