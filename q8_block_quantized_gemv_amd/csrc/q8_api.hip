@@ -292,9 +292,8 @@ int smallm_mfma(const float *X, const void *w, float *Y, int64_t m, int64_t n, i
     int dev = 0;
     hipError_t e = hipGetDevice(&dev);
     if (e != hipSuccess) return fail_hip(e, "hipGetDevice");
-    // 4 double-buffered workgroups fill a CU's LDS; 8 single-stage ones
-    const int pf = env_int("Q8GEMV_SMALLM_PF", 1) ? 1 : 0;
-    const size_t part_bytes = plan_streamk(d, dev, pf ? 4 : 8, 4);
+    // four double-buffered one-wave workgroups fill a CU's LDS
+    const size_t part_bytes = plan_streamk(d, dev, 4, 4);
     // workspace: the split X (m * n * 6 bytes, 256-B aligned), then the
     // partial slots
     const size_t xs_bytes = ((size_t)m * n * kXPartsBytesPerCol + 255) / 256 * 256;
@@ -305,7 +304,7 @@ int smallm_mfma(const float *X, const void *w, float *Y, int64_t m, int64_t n, i
     d.ws = (float *)((char *)ws + xs_bytes);
     e = launch_split_x(X, ws, (int)m, (int)n, s);
     if (e != hipSuccess) return fail_hip(e, "q8_0_gemm_smallm split launch");
-    e = launch_gemm_mfma(d, pf, (int64_t)d.fast_wgs + (p - d.tail_row0), s);
+    e = launch_gemm_mfma(d, (int64_t)d.fast_wgs + (p - d.tail_row0), s);
     if (e != hipSuccess) return fail_hip(e, "q8_0_gemm_smallm launch");
     return Q8_OK;
 }

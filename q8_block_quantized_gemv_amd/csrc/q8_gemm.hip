@@ -45,31 +45,6 @@ __device__ __forceinline__ void split3(const float (&x)[8], bf16x8 &h, bf16x8 &m
     }
 }
 
-// The 8 quants of block K of super-row s that lane group g (= lane / 16)
-// feeds to the matrix core: bytes 2 + 8g .. 9 + 8g of the block, as bf16.
-template <int K>
-__device__ __forceinline__ bf16x8 quants_bf16(const uint8_t *grp, int g) {
-    constexpr int q0 = K * kBlockBytes + 2;   // first quant byte of the block
-    uint32_t w0, w1;
-    if constexpr ((q0 & 3) == 0) {
-        const uint32_t *p = reinterpret_cast<const uint32_t *>(grp + q0 + 8 * g);
-        w0 = p[0];
-        w1 = p[1];
-    } else {   // 2 bytes past a dword boundary
-        const uint32_t *p = reinterpret_cast<const uint32_t *>(grp + q0 - 2 + 8 * g);
-        const uint32_t a0 = p[0], a1 = p[1], a2 = p[2];
-        w0 = __builtin_amdgcn_alignbyte(a1, a0, 2);
-        w1 = __builtin_amdgcn_alignbyte(a2, a1, 2);
-    }
-    bf16x8 b;
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-        b[e] = (__bf16)(float)(int8_t)(w0 >> (8 * e));
-        b[4 + e] = (__bf16)(float)(int8_t)(w1 >> (8 * e));
-    }
-    return b;
-}
-
 // The A operands of X, split once per call by k_split_x into
 // xs[i][b][g] = {h, m, l}: three bf16x8 (48 bytes) holding columns
 // 32b + 8g .. 32b + 8g + 7 of row i.  Rows i >= m are never read.
@@ -119,8 +94,59 @@ __device__ __forceinline__ void flush_tile(f32x4 (&acc)[4][RS], f32x4 (&sub)[4],
     }
 }
 
+// The LDS words a lane needs for block K of tile t: the 8 quants it feeds
+// (two dwords, or three when they start 2 bytes past a dword) and its row's
+// scale.
+struct BRaw {
+    uint32_t a0, a1, a2;
+    uint32_t dh;
+};
+
+template <int K>
+__device__ __forceinline__ void read_braw(const uint8_t *stage, int j, int g, BRaw (&r)[4]) {
+    constexpr int q0 = K * kBlockBytes + 2;   // first quant byte of the block
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+        const uint8_t *grp = stage + kGroupBytes * (16 * t + j);
+        if constexpr ((q0 & 3) == 0) {
+            const uint32_t *p = reinterpret_cast<const uint32_t *>(grp + q0 + 8 * g);
+            r[t].a0 = p[0];
+            r[t].a1 = p[1];
+        } else {
+            const uint32_t *p = reinterpret_cast<const uint32_t *>(grp + q0 - 2 + 8 * g);
+            r[t].a0 = p[0];
+            r[t].a1 = p[1];
+            r[t].a2 = p[2];
+        }
+        r[t].dh = *reinterpret_cast<const uint16_t *>(grp + K * kBlockBytes);
+    }
+}
+
+// Raw words -> the B operands (bf16 quants) and the scales of block K.
+template <int K>
+__device__ __forceinline__ void convert_b(const BRaw (&r)[4], bf16x8 (&bq)[4], float (&dsc)[4]) {
+    constexpr int q0 = K * kBlockBytes + 2;
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+        uint32_t w0 = r[t].a0, w1 = r[t].a1;
+        if constexpr ((q0 & 3) != 0) {
+            w0 = __builtin_amdgcn_alignbyte(r[t].a1, r[t].a0, 2);
+            w1 = __builtin_amdgcn_alignbyte(r[t].a2, r[t].a1, 2);
+        }
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            bq[t][e] = (__bf16)(float)(int8_t)(w0 >> (8 * e));
+            bq[t][4 + e] = (__bf16)(float)(int8_t)(w1 >> (8 * e));
+        }
+        dsc[t] = half_to_float(r[t].dh);
+    }
+}
+
 // One group of the wave's 64 super-rows (4 MFMA tiles of 16), all blocks;
-// xg holds the group's A operands.
+// xg holds the group's A operands.  A three-deep software pipeline over the
+// blocks: while block K's MFMAs run, block K+1's quants are converted, block
+// K+2's words are read from LDS, and block K-1's results are scaled and
+// added, so the vector and matrix units and the LDS work side by side.
 template <int RS>
 __device__ __forceinline__ void group_mfma(const uint8_t *stage, const GemmDesc &d, int kk,
                                            int lane, const XParts (&xg)[kGroupBlocks],
@@ -131,38 +157,54 @@ __device__ __forceinline__ void group_mfma(const uint8_t *stage, const GemmDesc 
     for (int t = 0; t < 4; ++t) sub[t] = f32x4{0.f, 0.f, 0.f, 0.f};
     int r = 0, cb = kk * kGroupBlocks;
     if (RS > 1) { r = cb / d.nb; cb -= r * d.nb; }
-#define Q8_MSTEP(K)                                                                     \
+    BRaw R0[4], R1[4];
+    bf16x8 B0[4], B1[4];
+    float D0[4], D1[4];
+    f32x4 C0[4], C1[4];
+    auto accumulate = [&](const float (&dd)[4], const f32x4 (&cc)[4]) {
+#pragma unroll
+        for (int t = 0; t < 4; ++t) sub[t] += dd[t] * cc[t];
+        if (RS > 1 && ++cb == d.nb) { flush_tile<RS>(acc, sub, r); cb = 0; ++r; }
+    };
+    auto mfma3 = [&](const XParts &x, const bf16x8 (&bb)[4], f32x4 (&cc)[4]) {
+#pragma unroll
+        for (int t = 0; t < 4; ++t)
+            cc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(x.h, bb[t], f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
+#pragma unroll
+        for (int t = 0; t < 4; ++t) cc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(x.m, bb[t], cc[t], 0, 0, 0);
+#pragma unroll
+        for (int t = 0; t < 4; ++t) cc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(x.l, bb[t], cc[t], 0, 0, 0);
+    };
+    read_braw<0>(stage, j, g, R0);
+    read_braw<1>(stage, j, g, R1);
+    convert_b<0>(R0, B0, D0);
+    // step K: A = block K's parity, Bp = the other one
+#define Q8_MSTEP(K, RA, RB, BA, BB, DA, DB, CA, CB)                                     \
     {                                                                                   \
-        asm volatile("" ::: "memory"); /* one block's LDS reads at a time */           \
-        bf16x8 bq[4];                                                                   \
-        float dsc[4];                                                                   \
-        _Pragma("unroll") for (int t = 0; t < 4; ++t) {                                 \
-            const uint8_t *grp = stage + kGroupBytes * (16 * t + j);                    \
-            dsc[t] = half_to_float(                                                     \
-                *reinterpret_cast<const uint16_t *>(grp + (K) * kBlockBytes));          \
-            bq[t] = quants_bf16<K>(grp, g);                                             \
-        }                                                                               \
-        f32x4 c[4];                                                                     \
-        _Pragma("unroll") for (int t = 0; t < 4; ++t)                                   \
-            c[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xg[K].h, bq[t], f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0); \
-        _Pragma("unroll") for (int t = 0; t < 4; ++t)                                   \
-            c[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xg[K].m, bq[t], c[t], 0, 0, 0); \
-        _Pragma("unroll") for (int t = 0; t < 4; ++t)                                   \
-            c[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xg[K].l, bq[t], c[t], 0, 0, 0); \
-        _Pragma("unroll") for (int t = 0; t < 4; ++t) sub[t] += dsc[t] * c[t];         \
-        if (RS > 1 && ++cb == d.nb) { flush_tile<RS>(acc, sub, r); cb = 0; ++r; }      \
+        asm volatile("" ::: "memory"); /* bounds the registers the steps hold */       \
+        if constexpr ((K) >= 1) accumulate(DB, CB);                                     \
+        if constexpr ((K) + 2 < kGroupBlocks) read_braw<((K) + 2) % kGroupBlocks>(stage, j, g, RA); \
+        if constexpr ((K) + 1 < kGroupBlocks) convert_b<((K) + 1) % kGroupBlocks>(RB, BB, DB); \
+        mfma3(xg[K], BA, CA);                                                           \
     }
-    Q8_MSTEP(0) Q8_MSTEP(1) Q8_MSTEP(2) Q8_MSTEP(3)
-    Q8_MSTEP(4) Q8_MSTEP(5) Q8_MSTEP(6) Q8_MSTEP(7)
+    Q8_MSTEP(0, R0, R1, B0, B1, D0, D1, C0, C1)
+    Q8_MSTEP(1, R1, R0, B1, B0, D1, D0, C1, C0)
+    Q8_MSTEP(2, R0, R1, B0, B1, D0, D1, C0, C1)
+    Q8_MSTEP(3, R1, R0, B1, B0, D1, D0, C1, C0)
+    Q8_MSTEP(4, R0, R1, B0, B1, D0, D1, C0, C1)
+    Q8_MSTEP(5, R1, R0, B1, B0, D1, D0, C1, C0)
+    Q8_MSTEP(6, R0, R1, B0, B1, D0, D1, C0, C1)
+    Q8_MSTEP(7, R1, R0, B1, B0, D1, D0, C1, C0)
 #undef Q8_MSTEP
+    accumulate(D1, C1);   // block 7
     flush_tile<RS>(acc, sub, RS == 1 ? 0 : r);
 }
 
 // Groups [g0, g1) of row tile rt (64 super-rows = 4 MFMA tiles), added
-// into acc.  PF = 1: two W stages, the next group's loads stream while this
-// one computes (one wave per SIMD).  PF = 0: one stage -- half the LDS and
-// fewer registers, so two waves share a SIMD and overlap each other instead.
-template <int RS, int PF>
+// into acc: two W stages and two register sets of A operands, used in turn,
+// so the next group's loads stream while this one computes (one wave per
+// SIMD; a single-stage variant with two waves per SIMD measured no faster).
+template <int RS>
 __device__ void gemm_run(const GemmDesc &d, int rt, int g0, int g1, uint8_t *stage,
                          f32x4 (&acc)[4][RS]) {
     const int lane = lane_id();
@@ -179,48 +221,32 @@ __device__ void gemm_run(const GemmDesc &d, int rt, int g0, int g1, uint8_t *sta
     };
     // Every wait is vmcnt(0) through the builtin, so the compiler knows that
     // the A operands it loaded (ordinary loads) have landed as well.
-    if constexpr (PF == 1) {
-        // two stages and two register sets of A, used in turn
-        XParts xa[kGroupBlocks], xb[kGroupBlocks];
-        uint8_t *st1 = stage + kStageBytesM;
-        if (g0 < g1) {
-            issue_w(g0, stage);
-            load_xgroup<RS>(d, g0, lane, xa);
+    XParts xa[kGroupBlocks], xb[kGroupBlocks];
+    uint8_t *st1 = stage + kStageBytesM;
+    if (g0 < g1) {
+        issue_w(g0, stage);
+        load_xgroup<RS>(d, g0, lane, xa);
+    }
+    for (int kk = g0; kk < g1; kk += 2) {
+        __builtin_amdgcn_s_waitcnt(0x0F70);
+        asm volatile("" ::: "memory");
+        if (kk + 1 < g1) {
+            issue_w(kk + 1, st1);
+            load_xgroup<RS>(d, kk + 1, lane, xb);
         }
-        for (int kk = g0; kk < g1; kk += 2) {
-            __builtin_amdgcn_s_waitcnt(0x0F70);
-            asm volatile("" ::: "memory");
-            if (kk + 1 < g1) {
-                issue_w(kk + 1, st1);
-                load_xgroup<RS>(d, kk + 1, lane, xb);
-            }
-            group_mfma<RS>(stage, d, kk, lane, xa, acc);
-            __builtin_amdgcn_s_waitcnt(0xC07F);   // stage 0 fully read
-            asm volatile("" ::: "memory");
-            if (kk + 1 >= g1) break;
-            __builtin_amdgcn_s_waitcnt(0x0F70);
-            asm volatile("" ::: "memory");
-            if (kk + 2 < g1) {
-                issue_w(kk + 2, stage);
-                load_xgroup<RS>(d, kk + 2, lane, xa);
-            }
-            group_mfma<RS>(st1, d, kk + 1, lane, xb, acc);
-            __builtin_amdgcn_s_waitcnt(0xC07F);   // stage 1 fully read
-            asm volatile("" ::: "memory");
+        group_mfma<RS>(stage, d, kk, lane, xa, acc);
+        __builtin_amdgcn_s_waitcnt(0xC07F);   // stage 0 fully read
+        asm volatile("" ::: "memory");
+        if (kk + 1 >= g1) break;
+        __builtin_amdgcn_s_waitcnt(0x0F70);
+        asm volatile("" ::: "memory");
+        if (kk + 2 < g1) {
+            issue_w(kk + 2, stage);
+            load_xgroup<RS>(d, kk + 2, lane, xa);
         }
-    } else {
-        XParts xg[kGroupBlocks];
-        for (int kk = g0; kk < g1; ++kk) {
-            issue_w(kk, stage);
-            load_xgroup<RS>(d, kk, lane, xg);
-            __builtin_amdgcn_s_waitcnt(0x0F70);
-            asm volatile("" ::: "memory");
-            group_mfma<RS>(stage, d, kk, lane, xg, acc);
-            // every LDS read of this stage has returned before the next
-            // group's loads overwrite it
-            __builtin_amdgcn_s_waitcnt(0xC07F);
-            asm volatile("" ::: "memory");
-        }
+        group_mfma<RS>(st1, d, kk + 1, lane, xb, acc);
+        __builtin_amdgcn_s_waitcnt(0xC07F);   // stage 1 fully read
+        asm volatile("" ::: "memory");
     }
 }
 
@@ -330,7 +356,7 @@ __device__ void partial_tile(const GemmDesc &d, int rt, int rank, int contributo
 }
 
 // Workgroup b's range of (row tile, group) items.
-template <int RS, int PF>
+template <int RS>
 __device__ void gemm_streamk(const GemmDesc &d, int64_t b, uint8_t *stage) {
     const int lane = lane_id();
     const int64_t G = d.gsr, N = (int64_t)d.row_tiles * G, W = d.fast_wgs;
@@ -345,7 +371,7 @@ __device__ void gemm_streamk(const GemmDesc &d, int64_t b, uint8_t *stage) {
         for (int t = 0; t < 4; ++t)
 #pragma unroll
             for (int k = 0; k < RS; ++k) acc[t][k] = f32x4{0.f, 0.f, 0.f, 0.f};
-        gemm_run<RS, PF>(d, rt, g0, g1, stage, acc);
+        gemm_run<RS>(d, rt, g0, g1, stage, acc);
         if (g0 == 0 && g1 == G) {
             store_tile<RS>(d, (int64_t)rt * kWave, lane, acc);
         } else {
@@ -515,12 +541,12 @@ __device__ void vsmall_streamk(const GemmDesc &d, int64_t b, uint8_t *stage) {
     }
 }
 
-template <int RS, int PF>
-__global__ __launch_bounds__(kWave, PF == 0 ? 2 : 1) void k_q8_gemm_mfma(GemmDesc d) {
-    __shared__ __attribute__((aligned(16))) uint8_t stage[(PF + 1) * kStageBytesM];
+template <int RS>
+__global__ __launch_bounds__(kWave, 1) void k_q8_gemm_mfma(GemmDesc d) {
+    __shared__ __attribute__((aligned(16))) uint8_t stage[2 * kStageBytesM];
     const uint32_t bid = blockIdx.x;
     if (bid < (uint32_t)d.fast_wgs) {
-        gemm_streamk<RS, PF>(d, bid, stage);
+        gemm_streamk<RS>(d, bid, stage);
     } else {
         OpDesc t;
         t.x = d.X; t.w = d.w; t.y = d.Y; t.nb = d.nb; t.p = d.p; t.m = d.m;
@@ -552,13 +578,11 @@ hipError_t launch_split_x(const float *X, void *xs, int m, int n, hipStream_t s)
     return hipGetLastError();
 }
 
-hipError_t launch_gemm_mfma(const GemmDesc &d, int pf, int64_t grid, hipStream_t s) {
+hipError_t launch_gemm_mfma(const GemmDesc &d, int64_t grid, hipStream_t s) {
     const dim3 gr((unsigned)grid), bl(kWave);
-    switch (d.rs * 10 + pf) {
-        case 10: hipLaunchKernelGGL((k_q8_gemm_mfma<1, 0>), gr, bl, 0, s, d); break;
-        case 11: hipLaunchKernelGGL((k_q8_gemm_mfma<1, 1>), gr, bl, 0, s, d); break;
-        case 20: hipLaunchKernelGGL((k_q8_gemm_mfma<2, 0>), gr, bl, 0, s, d); break;
-        case 21: hipLaunchKernelGGL((k_q8_gemm_mfma<2, 1>), gr, bl, 0, s, d); break;
+    switch (d.rs) {
+        case 1: hipLaunchKernelGGL((k_q8_gemm_mfma<1>), gr, bl, 0, s, d); break;
+        case 2: hipLaunchKernelGGL((k_q8_gemm_mfma<2>), gr, bl, 0, s, d); break;
         default: return hipErrorInvalidValue;
     }
     return hipGetLastError();

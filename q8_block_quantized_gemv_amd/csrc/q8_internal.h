@@ -111,7 +111,7 @@ inline int64_t tail_tiles_for(int64_t tail_rows, int nw = kWaves) {
 hipError_t launch_gemv_single(const OpDesc &op, const Variant &v, int64_t grid, hipStream_t s);
 hipError_t launch_gemv_fused(const OpDesc *d_ops, const Tile *d_tiles, const Variant &v,
                              int64_t grid, hipStream_t s);
-hipError_t launch_gemm_mfma(const GemmDesc &d, int pf, int64_t grid, hipStream_t s);
+hipError_t launch_gemm_mfma(const GemmDesc &d, int64_t grid, hipStream_t s);
 // the vector-unit small batch for m = 2..4 (any rs); d.xs is not used
 hipError_t launch_gemm_valu(const GemmDesc &d, int64_t grid, hipStream_t s);
 int gemm_valu_stage_bytes(int m);   // LDS bytes per workgroup (0 if m is not 2..4)
