@@ -14,6 +14,7 @@
 
 #include "q8gemv.h"
 #include "q8_internal.h"
+#include "q8_gemm.h"
 
 using namespace q8;
 

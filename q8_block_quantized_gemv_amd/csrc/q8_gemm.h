@@ -1,0 +1,48 @@
+// q8_gemm.h -- the small-batch product's descriptor and launchers, shared
+// between q8_gemm.hip and the host side of the library.
+#pragma once
+
+#include "q8_internal.h"
+
+namespace q8 {
+
+// Three bf16x8 (48 bytes): one lane's A operand of X for one block, split
+// exactly into bfloat16 parts h + m + l (see k_split_x).
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+struct XParts {
+    bf16x8 h, m, l;
+};
+
+// A small-batch product (2 <= m <= 16) as its kernels see it.  Workgroups
+// are one wave.  The work is row_tiles (64 super-rows each) x gsr groups of
+// items, split stream-K style into fast_wgs equal contiguous ranges; a row
+// tile shared by several workgroups goes through `maxc` partial slots
+// (16 * 64 * rs floats each) of the workspace `ws` and the per-row-tile
+// arrival counters `cnt` (zero between launches).
+struct GemmDesc {
+    const float *X;
+    const XParts *xs;    // X split into exact bf16 parts (k_split_x)
+    const uint8_t *w;
+    float *Y;
+    float *ws;
+    uint32_t *cnt;
+    int64_t sr_bytes;
+    int32_t n, nb, p, m;
+    int32_t rs, nsr, gsr;
+    int32_t maxc;        // partial slots per row tile (>= contributors of any tile)
+    int32_t row_tiles;   // ceil(nsr / 64)
+    int32_t fast_wgs;    // stream-K workgroups; the tail rows follow, one per workgroup
+    int32_t tail_row0;
+    int32_t pad_;
+};
+
+hipError_t launch_gemm_mfma(const GemmDesc &d, int64_t grid, hipStream_t s);
+// the vector-unit small batch for m = 2..4 (any rs); d.xs is not used
+hipError_t launch_gemm_valu(const GemmDesc &d, int64_t grid, hipStream_t s);
+int gemm_valu_stage_bytes(int m);   // LDS bytes per workgroup (0 if m is not 2..4)
+constexpr int kValuMaxM = 4;
+// X (m x n) -> the bf16 parts the matrix-core kernel reads: 96 * n bytes per row
+hipError_t launch_split_x(const float *X, void *xs, int m, int n, hipStream_t s);
+constexpr int64_t kXPartsBytesPerCol = 6;   // 3 bf16 per element
+
+}  // namespace q8

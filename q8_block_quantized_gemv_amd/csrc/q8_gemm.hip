@@ -3,6 +3,7 @@
 // split into exact bfloat16 parts, and on the vector units in the matvec's
 // layout; both split their (row tile, group) items stream-K style.
 #include "q8_device.h"
+#include "q8_gemm.h"
 
 namespace q8 {
 namespace {
