@@ -265,3 +265,53 @@ def test_stream_wait_timeout_and_ok(q8):
     import torch
     torch.cuda.synchronize()
     assert q8.stream_wait(timeout_ms=1000) == 0
+
+
+def test_widest_rows(q8, monkeypatch):
+    """n at its maximum (2**20 columns, 32768 blocks, 1.1 MB per row): the
+    matvec, the small batch on the matrix cores (m = 16) and on the vector
+    units (m = 3), every output against the oracle."""
+    import torch
+    n, p = 1 << 20, 67
+    log("widest rows n=%d p=%d" % (n, p))
+    rng = np.random.default_rng(1 << 20)
+    w = synth.q8_weights(n, p, rng)
+    wd = w_dev(w, n, p)
+    x = synth.activations(n, rng)
+    y = torch.full((p,), float("nan"), dtype=torch.float32, device="cuda")
+    q8.gemv(up(x), wd, y)
+    _, y64, mag = oracle.gemv(w, x, n, p)
+    parity(down(y), y64, mag, "gemv widest")
+    for m, path in ((16, None), (3, "valu")):
+        if path:
+            monkeypatch.setenv("Q8GEMV_SMALLM_PATH", path)
+        else:
+            monkeypatch.delenv("Q8GEMV_SMALLM_PATH", raising=False)
+        X = synth.activations(n, rng, m)
+        Y = torch.full((m, p), float("nan"), dtype=torch.float32, device="cuda")
+        q8.gemm_smallm(up(X), wd, Y)
+        _, Y64, MAG = oracle.gemm(w, X, m, n, p)
+        Yh = down(Y)
+        for i in range(m):
+            parity(Yh[i], Y64[i], MAG[i], "gemm widest m=%d row %d" % (m, i))
+
+
+def test_most_rows(q8):
+    """p = 2**22 + 3 one-block rows (143 MB of W, 16385 row tiles and a tail
+    of three rows): sampled rows, the tile boundaries and the tail, against
+    the oracle."""
+    import torch
+    n, p = 32, (1 << 22) + 3
+    log("most rows n=%d p=%d" % (n, p))
+    rng = np.random.default_rng(22)
+    w = synth.q8_weights(n, p, rng)
+    x = synth.activations(n, rng)
+    y = torch.full((p,), float("nan"), dtype=torch.float32, device="cuda")
+    q8.gemv(up(x), w_dev(w, n, p), y)
+    yh = down(y)
+    rows = np.unique(np.concatenate([
+        np.arange(0, 130), np.arange(p - 130, p),
+        rng.integers(0, p, 2000), np.arange(511, p, 1 << 16), np.arange(512, p, 1 << 16)]))
+    _, y64, mag = oracle.gemv_rows(w, x, n, rows)
+    parity(yh[rows], y64, mag, "gemv most rows")
+    assert not np.isnan(yh).any()
