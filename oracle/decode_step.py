@@ -24,10 +24,16 @@ Readings taken where the page leaves a step open:
 * argmax_row: comparisons as the page writes them -- a value wins if it is
   greater, or equal with a lower index; NaN never wins, and a row of only
   NaN gives 0xFFFFFFFF, the page's initial index.
+* decode_step: the embedding row is looked up from the token id (the page
+  does it on the host before encoding); a token id outside the vocabulary
+  (only the all-NaN argmax produces one) gives a zero row.  Every buffer
+  the method keeps in float32 is rounded to float32 between the steps.
 """
 from __future__ import annotations
 
 import numpy as np
+
+from oracle import gemv as _q8_gemv
 
 NO_INDEX = 0xFFFFFFFF
 
@@ -109,3 +115,49 @@ def argmax_row(x) -> int:
         if v > best or (v == best and i < besti):
             best, besti = v, i
     return besti
+
+
+def _r32(a) -> np.ndarray:
+    return np.asarray(a, dtype=np.float64).astype(np.float32)
+
+
+def decode_step(cfg: dict, w: dict, kc: list, vc: list, token: int, pos: int):
+    """One decode step of a Qwen3-style model in the order of section "One
+    command buffer": per layer norm, q/k/v projections, per-head q and k
+    norms, rotary embedding at pos, cache append at pos, attention over pos + 1
+    rows, output projection, residual add, norm, gate and up projections,
+    SwiGLU, down projection, residual add; then the final norm, the lm_head
+    and argmax.  The Q8_0 projections are the oracle's matvec.
+
+    kc, vc: per layer float32 (max_seq, kv_width) caches, updated in place.
+    Returns (next token, logits float32, logits float64, logits magnitude
+    sum_j |w_j x_j| per row, final residual x float32).
+    """
+    hid, hd = cfg["hidden"], cfg["head_dim"]
+    nh, nkv, inter = cfg["n_heads"], cfg["n_kv_heads"], cfg["inter"]
+    eps, theta, vocab = cfg["eps"], cfg["theta"], cfg["vocab"]
+    qw, kvw = nh * hd, nkv * hd
+
+    def mv(wt, x, n, p):
+        return _q8_gemv(wt, x, n, p)[0]
+
+    x = (np.asarray(w["embed"], np.float32).reshape(vocab, hid)[token].copy()
+         if 0 <= token < vocab else np.zeros(hid, np.float32))
+    for l, L in enumerate(w["layers"]):
+        xn = _r32(rms_norm_rows(x, L["attn_norm"], hid, eps)).reshape(-1)
+        q = mv(L["wq"], xn, hid, qw)
+        k = mv(L["wk"], xn, hid, kvw)
+        v = mv(L["wv"], xn, hid, kvw)
+        q = _r32(rms_norm_rows(q, L["q_norm"], hd, eps))
+        k = _r32(rms_norm_rows(k, L["k_norm"], hd, eps))
+        q = _r32(rope_rows(q, hd, pos, theta)).reshape(-1)
+        k = _r32(rope_rows(k, hd, pos, theta)).reshape(-1)
+        kc[l], vc[l] = append_kv(k, v, kc[l], vc[l], kvw, pos)
+        a = _r32(attention_decode(q, kc[l], vc[l], pos + 1, kvw, hd, nh, nh // nkv)[0]).reshape(-1)
+        x = _r32(add_inplace(x, mv(L["wo"], a, qw, hid)))
+        xn = _r32(rms_norm_rows(x, L["ffn_norm"], hid, eps)).reshape(-1)
+        h = _r32(silu_hadamard(mv(L["wgate"], xn, hid, inter), mv(L["wup"], xn, hid, inter)))
+        x = _r32(add_inplace(x, mv(L["wdown"], h, inter, hid)))
+    xn = _r32(rms_norm_rows(x, w["out_norm"], hid, eps)).reshape(-1)
+    y, y64, mag = _q8_gemv(w["lm_head"], xn, hid, vocab)
+    return argmax_row(y), y, y64, mag, x

@@ -10,6 +10,9 @@ The names follow the C ABI:
     gemm_smallm(X, w, Y=None, stream=None)     -> q8_0_gemm_smallm
     Chain(ops, fuse=True) .run(mode, stream)   -> q8_0_chain_create / q8_0_decode_chain
     stream_wait(stream, timeout_ms)            -> q8_0_stream_wait
+    rms_norm, rope, append_kv, attention_decode, add_inplace,
+    silu_hadamard, argmax                      -> the q8_0_* calls of include/q8step.h
+    Step(cfg, weights) .reset/.run             -> q8_0_step_create / _reset / _run
 """
 from __future__ import annotations
 
@@ -41,7 +44,14 @@ BLOCK_BYTES = 34
 
 EXPORTS = ("q8_0_gemv", "q8_0_gemm_smallm", "q8_0_chain_create", "q8_0_decode_chain",
            "q8_0_chain_launches", "q8_0_chain_destroy", "q8_0_stream_wait",
-           "q8_0_status_string", "q8_0_last_error")
+           "q8_0_status_string", "q8_0_last_error",
+           "q8_0_rms_norm", "q8_0_rope", "q8_0_append_kv", "q8_0_attention_decode",
+           "q8_0_add_inplace", "q8_0_silu_hadamard", "q8_0_argmax",
+           "q8_0_step_create", "q8_0_step_reset", "q8_0_step_run", "q8_0_step_launches",
+           "q8_0_step_buffers", "q8_0_step_destroy")
+
+NO_INDEX = 0xFFFFFFFF   # argmax of a row of NaN
+MAX_SEQ = 65536
 
 
 class Q8Error(RuntimeError):
@@ -53,6 +63,25 @@ class Q8Error(RuntimeError):
 class Q8Op(ctypes.Structure):
     _fields_ = [("x", ctypes.c_void_p), ("w", ctypes.c_void_p), ("y", ctypes.c_void_p),
                 ("n", ctypes.c_int64), ("p", ctypes.c_int64)]
+
+
+class Q8LayerW(ctypes.Structure):
+    _fields_ = [(k, ctypes.c_void_p) for k in
+                ("wq", "wk", "wv", "wo", "wgate", "wup", "wdown",
+                 "attn_norm", "ffn_norm", "q_norm", "k_norm")]
+
+
+class Q8Model(ctypes.Structure):
+    _fields_ = [(k, ctypes.c_int64) for k in
+                ("n_layers", "hidden", "n_heads", "n_kv_heads", "head_dim", "inter", "vocab",
+                 "max_seq")] + [
+               ("eps", ctypes.c_float), ("theta", ctypes.c_float),
+               ("embed", ctypes.c_void_p), ("out_norm", ctypes.c_void_p),
+               ("lm_head", ctypes.c_void_p), ("layers", ctypes.POINTER(Q8LayerW))]
+
+
+class Q8StepBufs(ctypes.Structure):
+    _fields_ = [(k, ctypes.c_void_p) for k in ("token", "pos", "x", "logits", "k_cache", "v_cache")]
 
 
 def _load():
@@ -73,9 +102,23 @@ def _load():
     lib.q8_0_status_string.restype = ctypes.c_char_p
     lib.q8_0_last_error.argtypes = []
     lib.q8_0_last_error.restype = ctypes.c_char_p
-    for name in ("q8_0_gemv", "q8_0_gemm_smallm", "q8_0_chain_create", "q8_0_decode_chain",
-                 "q8_0_chain_launches", "q8_0_chain_destroy", "q8_0_stream_wait"):
-        getattr(lib, name).restype = ctypes.c_int
+    f32, u32, i32 = ctypes.c_float, ctypes.c_uint32, ctypes.c_int
+    lib.q8_0_rms_norm.argtypes = [vp, vp, vp, i64, i64, f32, vp]
+    lib.q8_0_rope.argtypes = [vp, i64, i64, i64, f32, vp]
+    lib.q8_0_append_kv.argtypes = [vp, vp, vp, vp, i64, i64, vp]
+    lib.q8_0_attention_decode.argtypes = [vp, vp, vp, vp, i64, i64, i64, i64, i64, vp]
+    lib.q8_0_add_inplace.argtypes = [vp, vp, i64, vp]
+    lib.q8_0_silu_hadamard.argtypes = [vp, vp, vp, i64, vp]
+    lib.q8_0_argmax.argtypes = [vp, i64, vp, vp]
+    lib.q8_0_step_create.argtypes = [ctypes.POINTER(Q8Model), ctypes.POINTER(vp)]
+    lib.q8_0_step_reset.argtypes = [vp, i64, u32, vp]
+    lib.q8_0_step_run.argtypes = [vp, i32, vp]
+    lib.q8_0_step_launches.argtypes = [vp]
+    lib.q8_0_step_buffers.argtypes = [vp, ctypes.POINTER(Q8StepBufs)]
+    lib.q8_0_step_destroy.argtypes = [vp]
+    for name in EXPORTS:
+        if name not in ("q8_0_status_string", "q8_0_last_error"):
+            getattr(lib, name).restype = ctypes.c_int
     return lib
 
 
@@ -219,6 +262,225 @@ class Chain:
     def close(self) -> None:
         if getattr(self, "_h", None) is not None:
             lib.q8_0_chain_destroy(self._h)
+            self._h = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+
+# ------------------------------------------------------------------ the rest of a decode step
+def _f32(t, what, numel=None):
+    torch = _torch()
+    _need(t, torch.float32, what)
+    if numel is not None and t.numel() != numel:
+        raise ValueError("%s has %d elements, expected %d" % (what, t.numel(), numel))
+
+
+def rms_norm(x, w, out=None, eps: float = 1e-6, stream=None):
+    """Each row of x (rows, dim) times (mean(x^2) + eps)^(-1/2) times w (dim,).
+    out may be x (in place)."""
+    torch = _torch()
+    dim = int(w.numel())
+    _f32(w, "w")
+    _f32(x, "x")
+    if x.numel() % dim:
+        raise ValueError("x is not a whole number of rows of %d" % dim)
+    if out is None:
+        out = torch.empty_like(x)
+    _f32(out, "out", x.numel())
+    check(lib.q8_0_rms_norm(x.data_ptr(), w.data_ptr(), out.data_ptr(), dim, x.numel() // dim,
+                            float(eps), _stream_handle(stream)))
+    return out
+
+
+def rope(x, head_dim: int, pos: int, theta: float, stream=None):
+    """Rotary embedding of every head of x (heads, head_dim), in place."""
+    _f32(x, "x")
+    if x.numel() % head_dim:
+        raise ValueError("x is not a whole number of heads of %d" % head_dim)
+    check(lib.q8_0_rope(x.data_ptr(), head_dim, x.numel() // head_dim, int(pos), float(theta),
+                        _stream_handle(stream)))
+    return x
+
+
+def append_kv(k, v, kc, vc, pos: int, stream=None):
+    """Row pos of the caches kc, vc (rows, width) becomes k, v (width,)."""
+    width = int(k.numel())
+    _f32(k, "k")
+    _f32(v, "v", width)
+    _f32(kc, "kc")
+    _f32(vc, "vc", kc.numel())
+    if kc.numel() < (int(pos) + 1) * width:
+        raise ValueError("the caches hold fewer than pos + 1 rows")
+    check(lib.q8_0_append_kv(k.data_ptr(), v.data_ptr(), kc.data_ptr(), vc.data_ptr(), width,
+                             int(pos), _stream_handle(stream)))
+
+
+def attention_decode(q, kc, vc, seq: int, head_dim: int, kv_group: int, out=None, stream=None):
+    """Decode attention of q (n_heads, head_dim) over the first seq rows of
+    the caches kc, vc (rows, kv_width); returns out (n_heads, head_dim)."""
+    torch = _torch()
+    _f32(q, "q")
+    _f32(kc, "kc")
+    _f32(vc, "vc", kc.numel())
+    if q.numel() % head_dim:
+        raise ValueError("q is not a whole number of heads")
+    n_heads = q.numel() // head_dim
+    if kc.dim() != 2:
+        raise ValueError("kc must be (rows, kv_width)")
+    kv_width = int(kc.shape[1])
+    if kc.shape[0] < seq:
+        raise ValueError("the caches hold fewer than seq rows")
+    if out is None:
+        out = torch.empty((n_heads, head_dim), dtype=torch.float32, device=q.device)
+    _f32(out, "out", n_heads * head_dim)
+    check(lib.q8_0_attention_decode(q.data_ptr(), kc.data_ptr(), vc.data_ptr(), out.data_ptr(),
+                                    int(seq), kv_width, head_dim, n_heads, int(kv_group),
+                                    _stream_handle(stream)))
+    return out
+
+
+def add_inplace(x, y, stream=None):
+    _f32(x, "x")
+    _f32(y, "y", x.numel())
+    check(lib.q8_0_add_inplace(x.data_ptr(), y.data_ptr(), x.numel(), _stream_handle(stream)))
+    return x
+
+
+def silu_hadamard(gate, up, out=None, stream=None):
+    torch = _torch()
+    _f32(gate, "gate")
+    _f32(up, "up", gate.numel())
+    if out is None:
+        out = torch.empty_like(gate)
+    _f32(out, "out", gate.numel())
+    check(lib.q8_0_silu_hadamard(gate.data_ptr(), up.data_ptr(), out.data_ptr(), gate.numel(),
+                                 _stream_handle(stream)))
+    return out
+
+
+def argmax(x, out=None, stream=None):
+    """Index of the largest value of x (ties to the lowest index, NaN never
+    wins) into out, a one-element int32 device tensor holding the uint32
+    index (NO_INDEX, read as -1, when every value is NaN)."""
+    torch = _torch()
+    _f32(x, "x")
+    if out is None:
+        out = torch.empty(1, dtype=torch.int32, device=x.device)
+    _need(out, torch.int32, "out")
+    check(lib.q8_0_argmax(x.data_ptr(), x.numel(), out.data_ptr(), _stream_handle(stream)))
+    return out
+
+
+class _DeviceView:
+    """A borrowed device buffer, shown to torch through __cuda_array_interface__."""
+
+    def __init__(self, ptr: int, shape, typestr: str):
+        self.__cuda_array_interface__ = {"shape": tuple(shape), "typestr": typestr,
+                                         "data": (int(ptr), False), "version": 2,
+                                         "strides": None}
+
+
+LAYER_KEYS = ("wq", "wk", "wv", "wo", "wgate", "wup", "wdown",
+              "attn_norm", "ffn_norm", "q_norm", "k_norm")
+CONFIG_KEYS = ("n_layers", "hidden", "n_heads", "n_kv_heads", "head_dim", "inter", "vocab",
+               "max_seq", "eps", "theta")
+
+
+class Step:
+    """A whole decode step of a Qwen3-style model, recorded once into a
+    hipGraph and replayed per token (q8_0_step_*).
+
+    cfg: dict with CONFIG_KEYS.  weights: dict with "embed" (vocab, hidden)
+    float32, "out_norm" (hidden,) float32, "lm_head" uint8 Q8_0 (vocab rows
+    of hidden) and "layers", a list of n_layers dicts with LAYER_KEYS (the
+    seven Q8_0 projections, uint8 (p, n/32*34), and the four float32 norm
+    weights).  The step keeps references to every tensor: their addresses
+    are recorded.
+    """
+
+    def __init__(self, cfg: dict, weights: dict):
+        torch = _torch()
+        c = {k: cfg[k] for k in CONFIG_KEYS}
+        hid, inter, hd = int(c["hidden"]), int(c["inter"]), int(c["head_dim"])
+        qw, kvw = int(c["n_heads"]) * hd, int(c["n_kv_heads"]) * hd
+        vocab = int(c["vocab"])
+        layers = weights["layers"]
+        if len(layers) != int(c["n_layers"]):
+            raise ValueError("weights hold %d layers, cfg says %d" % (len(layers), c["n_layers"]))
+        shapes = {"wq": (qw, hid), "wk": (kvw, hid), "wv": (kvw, hid), "wo": (hid, qw),
+                  "wgate": (inter, hid), "wup": (inter, hid), "wdown": (hid, inter)}
+        lens = {"attn_norm": hid, "ffn_norm": hid, "q_norm": hd, "k_norm": hd}
+        arr = (Q8LayerW * len(layers))()
+        self._keep = []
+        for i, L in enumerate(layers):
+            ptrs = []
+            for k in LAYER_KEYS:
+                t = L[k]
+                if k in shapes:
+                    _need(t, torch.uint8, "layers[%d].%s" % (i, k))
+                    if weight_shape(t) != shapes[k]:
+                        raise ValueError("layers[%d].%s is %s, expected %s"
+                                         % (i, k, weight_shape(t), shapes[k]))
+                else:
+                    _f32(t, "layers[%d].%s" % (i, k), lens[k])
+                ptrs.append(t.data_ptr())
+                self._keep.append(t)
+            arr[i] = Q8LayerW(*ptrs)
+        _f32(weights["embed"], "embed", vocab * hid)
+        _f32(weights["out_norm"], "out_norm", hid)
+        _need(weights["lm_head"], torch.uint8, "lm_head")
+        if weight_shape(weights["lm_head"]) != (vocab, hid):
+            raise ValueError("lm_head must be vocab rows of hidden columns")
+        for k in ("embed", "out_norm", "lm_head"):
+            self._keep.append(weights[k])
+        self._layers = arr
+        model = Q8Model(c["n_layers"], hid, c["n_heads"], c["n_kv_heads"], hd, inter, vocab,
+                        c["max_seq"], float(c["eps"]), float(c["theta"]),
+                        weights["embed"].data_ptr(), weights["out_norm"].data_ptr(),
+                        weights["lm_head"].data_ptr(), arr)
+        h = ctypes.c_void_p()
+        check(lib.q8_0_step_create(ctypes.byref(model), ctypes.byref(h)))
+        self._h = h
+        self.cfg = c
+        b = Q8StepBufs()
+        check(lib.q8_0_step_buffers(self._h, ctypes.byref(b)))
+        self._views = {
+            "token": (b.token, (1,), "<i4"), "pos": (b.pos, (1,), "<i4"),
+            "x": (b.x, (hid,), "<f4"), "logits": (b.logits, (vocab,), "<f4"),
+            "k_cache": (b.k_cache, (int(c["n_layers"]), int(c["max_seq"]), kvw), "<f4"),
+            "v_cache": (b.v_cache, (int(c["n_layers"]), int(c["max_seq"]), kvw), "<f4")}
+
+    def _handle(self):
+        if self._h is None:
+            raise RuntimeError("step is closed")
+        return self._h
+
+    @property
+    def launches(self) -> int:
+        return check(lib.q8_0_step_launches(self._handle()))
+
+    def reset(self, pos: int, token: int, stream=None) -> None:
+        check(lib.q8_0_step_reset(self._handle(), int(pos), int(token) & 0xFFFFFFFF,
+                                  _stream_handle(stream)))
+
+    def run(self, mode: int = MODE_GRAPH, stream=None) -> None:
+        check(lib.q8_0_step_run(self._handle(), int(mode), _stream_handle(stream)))
+
+    def buffer(self, name: str):
+        """A device tensor viewing one of the step's buffers (token, pos, x,
+        logits, k_cache, v_cache); valid while the step is open."""
+        torch = _torch()
+        self._handle()
+        ptr, shape, ts = self._views[name]
+        return torch.as_tensor(_DeviceView(ptr, shape, ts), device="cuda")
+
+    def close(self) -> None:
+        if getattr(self, "_h", None) is not None:
+            lib.q8_0_step_destroy(self._h)
             self._h = None
 
     def __del__(self):

@@ -12,7 +12,8 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libq8gemv.so")
-SOURCES = [os.path.join(CSRC, f) for f in ("q8_gemv.hip", "q8_gemm.hip", "q8_api.hip")]
+SOURCES = [os.path.join(CSRC, f)
+           for f in ("q8_gemv.hip", "q8_gemm.hip", "q8_step.hip", "q8_api.hip", "q8_step_api.hip")]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 

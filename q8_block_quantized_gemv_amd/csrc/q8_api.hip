@@ -15,10 +15,11 @@
 #include "q8gemv.h"
 #include "q8_internal.h"
 #include "q8_gemm.h"
+#include "q8_host.h"
 
 using namespace q8;
 
-namespace {
+namespace q8 {
 
 thread_local std::string g_last_error;
 
@@ -37,31 +38,8 @@ bool overlaps(const void *a, int64_t na, const void *b, int64_t nb) {
     return a0 < b0 + (uintptr_t)nb && b0 < a0 + (uintptr_t)na;
 }
 
-int64_t w_bytes(int64_t n, int64_t p) { return p * (n / kQuants) * kBlockBytes; }
-
-// Argument checks shared by every entry point; touches no device state.
-int validate(const float *x, const void *w, const float *y, int64_t m, int64_t n, int64_t p,
-             const char *what) {
-    std::string tag(what);
-    if (!x || !w || !y) return fail(Q8_ERR_INVALID_ARG, tag + ": null pointer");
-    if (n <= 0 || n % kQuants != 0 || n > Q8_MAX_N)
-        return fail(Q8_ERR_SHAPE, tag + ": n=" + std::to_string(n) +
-                                      " must be a positive multiple of 32 and <= 1048576");
-    if (p <= 0 || p > Q8_MAX_P)
-        return fail(Q8_ERR_SHAPE, tag + ": p=" + std::to_string(p) + " out of range");
-    if (m < 1 || m > Q8_MAX_M)
-        return fail(Q8_ERR_SHAPE, tag + ": m=" + std::to_string(m) + " must be in 1..16");
-    if ((uintptr_t)w % 16 || (uintptr_t)x % 16)
-        return fail(Q8_ERR_ALIGN, tag + ": w and x must be 16-byte aligned");
-    if ((uintptr_t)y % 4) return fail(Q8_ERR_ALIGN, tag + ": y must be 4-byte aligned");
-    const int64_t yb = 4 * m * p;
-    if (overlaps(y, yb, x, 4 * m * n)) return fail(Q8_ERR_ALIAS, tag + ": y overlaps x");
-    if (overlaps(y, yb, w, w_bytes(n, p))) return fail(Q8_ERR_ALIAS, tag + ": y overlaps w");
-    return Q8_OK;
-}
-
 // The current device must exist and be gfx950 (checked once per device).
-int check_device(int *dev_out = nullptr) {
+int check_device(int *dev_out) {
     int count = 0;
     hipError_t e = hipGetDeviceCount(&count);
     if (e != hipSuccess || count <= 0) {
@@ -85,6 +63,89 @@ int check_device(int *dev_out = nullptr) {
     }
     if (!verdict[dev]) return fail(Q8_ERR_UNSUPPORTED, "device is not gfx950");
     if (dev_out) *dev_out = dev;
+    return Q8_OK;
+}
+
+int cu_count(int dev) {
+    static std::mutex mu;
+    static std::vector<int> cus;
+    std::lock_guard<std::mutex> lk(mu);
+    if ((int)cus.size() <= dev) cus.resize(dev + 1, 0);
+    if (cus[dev] <= 0) {
+        int v = 0;
+        if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || v <= 0)
+            v = 256;
+        cus[dev] = v;
+    }
+    return cus[dev];
+}
+
+// Split-K workspace of the small-batch product, one per (device, stream):
+// calls on one stream run in order and may share it; calls on different
+// streams get different ones.  Grown on demand (hipFree synchronizes the
+// device first), kept until the process ends.  The arrival counters are
+// zeroed once here and left at zero by every launch.
+struct Workspace {
+    float *ws = nullptr;
+    size_t ws_bytes = 0;
+    uint32_t *cnt = nullptr;
+    size_t cnt_n = 0;
+};
+
+int workspace_for(int dev, hipStream_t s, size_t ws_bytes, size_t cnt_n, float **ws_out,
+                  uint32_t **cnt_out) {
+    static std::mutex mu;
+    static std::map<std::pair<int, hipStream_t>, Workspace> pool;
+    std::lock_guard<std::mutex> lk(mu);
+    Workspace &W = pool[{dev, s}];
+    hipError_t e;
+    if (W.ws_bytes < ws_bytes) {
+        if (W.ws && (e = hipFree(W.ws)) != hipSuccess) return fail_hip(e, "hipFree");
+        W.ws = nullptr;
+        W.ws_bytes = 0;
+        if ((e = hipMalloc(&W.ws, ws_bytes)) != hipSuccess) return fail_hip(e, "workspace hipMalloc");
+        W.ws_bytes = ws_bytes;
+    }
+    if (W.cnt_n < cnt_n) {
+        if (W.cnt && (e = hipFree(W.cnt)) != hipSuccess) return fail_hip(e, "hipFree");
+        W.cnt = nullptr;
+        W.cnt_n = 0;
+        if ((e = hipMalloc(&W.cnt, cnt_n * sizeof(uint32_t))) != hipSuccess)
+            return fail_hip(e, "counter hipMalloc");
+        if ((e = hipMemset(W.cnt, 0, cnt_n * sizeof(uint32_t))) != hipSuccess ||
+            (e = hipDeviceSynchronize()) != hipSuccess)
+            return fail_hip(e, "counter hipMemset");
+        W.cnt_n = cnt_n;
+    }
+    *ws_out = W.ws;
+    *cnt_out = W.cnt;
+    return Q8_OK;
+}
+
+}  // namespace q8
+
+namespace {
+
+int64_t w_bytes(int64_t n, int64_t p) { return p * (n / kQuants) * kBlockBytes; }
+
+// Argument checks shared by every entry point; touches no device state.
+int validate(const float *x, const void *w, const float *y, int64_t m, int64_t n, int64_t p,
+             const char *what) {
+    std::string tag(what);
+    if (!x || !w || !y) return fail(Q8_ERR_INVALID_ARG, tag + ": null pointer");
+    if (n <= 0 || n % kQuants != 0 || n > Q8_MAX_N)
+        return fail(Q8_ERR_SHAPE, tag + ": n=" + std::to_string(n) +
+                                      " must be a positive multiple of 32 and <= 1048576");
+    if (p <= 0 || p > Q8_MAX_P)
+        return fail(Q8_ERR_SHAPE, tag + ": p=" + std::to_string(p) + " out of range");
+    if (m < 1 || m > Q8_MAX_M)
+        return fail(Q8_ERR_SHAPE, tag + ": m=" + std::to_string(m) + " must be in 1..16");
+    if ((uintptr_t)w % 16 || (uintptr_t)x % 16)
+        return fail(Q8_ERR_ALIGN, tag + ": w and x must be 16-byte aligned");
+    if ((uintptr_t)y % 4) return fail(Q8_ERR_ALIGN, tag + ": y must be 4-byte aligned");
+    const int64_t yb = 4 * m * p;
+    if (overlaps(y, yb, x, 4 * m * n)) return fail(Q8_ERR_ALIAS, tag + ": y overlaps x");
+    if (overlaps(y, yb, w, w_bytes(n, p))) return fail(Q8_ERR_ALIAS, tag + ": y overlaps w");
     return Q8_OK;
 }
 
@@ -153,62 +214,6 @@ OpDesc plan_op(const float *x, const void *w, float *y, int64_t m, int64_t n, in
     d.x_stride = n;
     d.y_stride = p;
     return d;
-}
-
-int cu_count(int dev) {
-    static std::mutex mu;
-    static std::vector<int> cus;
-    std::lock_guard<std::mutex> lk(mu);
-    if ((int)cus.size() <= dev) cus.resize(dev + 1, 0);
-    if (cus[dev] <= 0) {
-        int v = 0;
-        if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || v <= 0)
-            v = 256;
-        cus[dev] = v;
-    }
-    return cus[dev];
-}
-
-// Split-K workspace of the small-batch product, one per (device, stream):
-// calls on one stream run in order and may share it; calls on different
-// streams get different ones.  Grown on demand (hipFree synchronizes the
-// device first), kept until the process ends.  The arrival counters are
-// zeroed once here and left at zero by every launch.
-struct Workspace {
-    float *ws = nullptr;
-    size_t ws_bytes = 0;
-    uint32_t *cnt = nullptr;
-    size_t cnt_n = 0;
-};
-
-int workspace_for(int dev, hipStream_t s, size_t ws_bytes, size_t cnt_n, float **ws_out,
-                  uint32_t **cnt_out) {
-    static std::mutex mu;
-    static std::map<std::pair<int, hipStream_t>, Workspace> pool;
-    std::lock_guard<std::mutex> lk(mu);
-    Workspace &W = pool[{dev, s}];
-    hipError_t e;
-    if (W.ws_bytes < ws_bytes) {
-        if (W.ws && (e = hipFree(W.ws)) != hipSuccess) return fail_hip(e, "hipFree");
-        W.ws = nullptr;
-        W.ws_bytes = 0;
-        if ((e = hipMalloc(&W.ws, ws_bytes)) != hipSuccess) return fail_hip(e, "workspace hipMalloc");
-        W.ws_bytes = ws_bytes;
-    }
-    if (W.cnt_n < cnt_n) {
-        if (W.cnt && (e = hipFree(W.cnt)) != hipSuccess) return fail_hip(e, "hipFree");
-        W.cnt = nullptr;
-        W.cnt_n = 0;
-        if ((e = hipMalloc(&W.cnt, cnt_n * sizeof(uint32_t))) != hipSuccess)
-            return fail_hip(e, "counter hipMalloc");
-        if ((e = hipMemset(W.cnt, 0, cnt_n * sizeof(uint32_t))) != hipSuccess ||
-            (e = hipDeviceSynchronize()) != hipSuccess)
-            return fail_hip(e, "counter hipMemset");
-        W.cnt_n = cnt_n;
-    }
-    *ws_out = W.ws;
-    *cnt_out = W.cnt;
-    return Q8_OK;
 }
 
 int64_t tiles_of(const OpDesc &d, int nw = kWaves) {
@@ -434,6 +439,14 @@ bool depends(const q8_0_op &a, const q8_0_op &b) {
 }
 
 }  // namespace
+
+int q8::chain_issue(const q8_0_chain *c, hipStream_t s) {
+    for (const auto &L : c->launches) {
+        hipError_t e = issue(L, s);
+        if (e != hipSuccess) return fail_hip(e, "chain launch");
+    }
+    return Q8_OK;
+}
 
 extern "C" {
 

@@ -1,0 +1,30 @@
+// q8_host.h -- host-side helpers shared by the library's entry points
+// (q8_api.hip, q8_step_api.hip).  Not installed.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include <string>
+
+#include "q8gemv.h"
+
+#define Q8_HIDDEN __attribute__((visibility("hidden")))
+
+namespace q8 {
+
+// Record `msg` as this thread's last error and return `code`.
+Q8_HIDDEN int fail(int code, const std::string &msg);
+Q8_HIDDEN int fail_hip(hipError_t e, const char *where);
+Q8_HIDDEN bool overlaps(const void *a, int64_t na, const void *b, int64_t nb);
+// The current device exists and is gfx950 (Q8_OK), else a status.
+Q8_HIDDEN int check_device(int *dev_out = nullptr);
+Q8_HIDDEN int cu_count(int dev);
+// A scratch buffer of at least ws_bytes and cnt_n zeroed counters for
+// stream s on device dev, kept across calls (grown when too small).
+Q8_HIDDEN int workspace_for(int dev, hipStream_t s, size_t ws_bytes, size_t cnt_n, float **ws_out,
+                            uint32_t **cnt_out);
+// Issue a chain's launches on s, without its graph.
+Q8_HIDDEN int chain_issue(const q8_0_chain *c, hipStream_t s);
+
+}  // namespace q8

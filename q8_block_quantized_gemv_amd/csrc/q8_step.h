@@ -1,0 +1,51 @@
+// q8_step.h -- the decode-step kernels' descriptors and launchers (q8_step.hip),
+// shared with the host side of the library.
+#pragma once
+
+#include "q8_internal.h"
+
+namespace q8 {
+
+// Cached rows per attention workgroup; a head's rows [0, seq) are split into
+// ceil(seq / kAttnChunk) chunks whose partial softmaxes are merged in order.
+constexpr int kAttnChunk = 128;
+
+struct AttnDesc {
+    const float *q;      // n_heads x head_dim
+    const float *kc;     // cache rows of kv_width floats
+    const float *vc;
+    float *out;          // n_heads x head_dim
+    const int *pos_dev;  // if set, seq = min(*pos_dev + 1, seq) (a recorded step); else seq
+    float *ws;           // n_heads * max_chunks * (head_dim + 2) floats
+    uint32_t *cnt;       // n_heads arrival counters, zero between launches
+    int seq, kv_width, head_dim, n_heads, kv_group, max_chunks;
+};
+
+struct ArgmaxDesc {
+    const float *x;
+    int64_t n;
+    uint32_t *out;       // the winning index (0xFFFFFFFF if every value is NaN)
+    float *ws_val;       // one (value, index) per workgroup
+    uint32_t *ws_idx;
+    uint32_t *cnt;       // arrival counter, zero between launches
+};
+
+// pos_dev, when not null, overrides pos (a recorded step reads it per replay)
+hipError_t launch_rms_norm(const float *x, const float *w, float *out, int dim, int rows, float eps,
+                           hipStream_t s);
+hipError_t launch_rope(float *x, int head_dim, int heads, const int *pos_dev, int pos, float theta,
+                       hipStream_t s);
+// rows: the caches' length; a position at or past it writes nothing.
+hipError_t launch_append_kv(const float *k, const float *v, float *kc, float *vc, int width,
+                            const int *pos_dev, int pos, int rows, hipStream_t s);
+hipError_t launch_attention(const AttnDesc &d, hipStream_t s);
+hipError_t launch_add(float *x, const float *y, int n, hipStream_t s);
+hipError_t launch_silu(const float *g, const float *u, float *out, int n, hipStream_t s);
+hipError_t launch_argmax(const ArgmaxDesc &d, int wgs, hipStream_t s);
+hipError_t launch_embed(const float *table, const uint32_t *token, uint32_t vocab, float *x, int dim,
+                        hipStream_t s);
+hipError_t launch_advance(int *pos_dev, hipStream_t s);
+// *pos_dev = pos, *token_dev = token, ordered on s (a kernel, so it may be recorded).
+hipError_t launch_set_state(int *pos_dev, uint32_t *token_dev, int pos, uint32_t token, hipStream_t s);
+
+}  // namespace q8

@@ -29,6 +29,8 @@ SEED_BASE = 0x51385F30
 
 ROLE_W = 0
 ROLE_X = 1
+ROLE_NORM = 2
+ROLE_EMBED = 3
 
 
 def row_bytes(n: int) -> int:
@@ -154,7 +156,8 @@ WORKLOADS: Dict[str, List[OpShape]] = {
 
 # workload number used in the seeds, in the order the workloads are listed
 WORKLOAD_ID = {"single_1024x3072": 0, "qwen3_0.6b_chain": 1,
-               "qwen2.5_0.5b_chain": 2, "7b_chain": 3, "smallm_7b": 4}
+               "qwen2.5_0.5b_chain": 2, "7b_chain": 3, "smallm_7b": 4,
+               "step_tiny": 5, "step_gqa4": 6}
 
 # small-batch products: X is m x n, m in {2, 4, 8, 16}, at three 7B shapes
 SMALLM_SHAPES = [OpShape("down", 18944, 3584), OpShape("gate", 3584, 18944),
@@ -195,3 +198,64 @@ def generate_smallm(shape: OpShape, m: int):
     w = q8_weights(shape.n, shape.p, rng_for(WORKLOAD_ID["smallm_7b"], k, ROLE_W))
     x = activations(shape.n, rng_for(WORKLOAD_ID["smallm_7b"], 16 * k + m, ROLE_X), m)
     return w, x
+
+
+# ------------------------------------------------------------------ whole decode-step models
+# Qwen3-style decoders (the step of page "IV.4: One command buffer per token",
+# section "One command buffer").  "qwen3_0.6b" has Qwen3-0.6B's shape and the
+# very projection bytes of the qwen3_0.6b_chain workload; the two small ones
+# are test models: "step_tiny" (2 layers, head_dim 64, two query heads per
+# KV head) and "step_gqa4" (head_dim 128, four query heads per KV head, an
+# intermediate width and a vocabulary that are not powers of two).
+STEP_MODELS = {
+    "qwen3_0.6b": dict(n_layers=28, hidden=1024, n_heads=16, n_kv_heads=8, head_dim=128,
+                       inter=3072, vocab=151936, eps=1e-6, theta=1e6),
+    "step_tiny": dict(n_layers=2, hidden=256, n_heads=4, n_kv_heads=2, head_dim=64,
+                      inter=512, vocab=1000, eps=1e-6, theta=1e6),
+    "step_gqa4": dict(n_layers=1, hidden=512, n_heads=8, n_kv_heads=2, head_dim=128,
+                      inter=1376, vocab=4099, eps=1e-6, theta=1e4),
+}
+STEP_SEED = {"qwen3_0.6b": WORKLOAD_ID["qwen3_0.6b_chain"], "step_tiny": WORKLOAD_ID["step_tiny"],
+             "step_gqa4": WORKLOAD_ID["step_gqa4"]}
+PROJ = ("wq", "wk", "wv", "wo", "wgate", "wup", "wdown")
+NORMS = ("attn_norm", "ffn_norm", "q_norm", "k_norm")
+
+
+def step_proj_shapes(cfg: dict):
+    """(name, n, p) of the seven projections of one layer, in encode order."""
+    hid, inter = cfg["hidden"], cfg["inter"]
+    qw, kvw = cfg["n_heads"] * cfg["head_dim"], cfg["n_kv_heads"] * cfg["head_dim"]
+    return [("wq", hid, qw), ("wk", hid, kvw), ("wv", hid, kvw), ("wo", qw, hid),
+            ("wgate", hid, inter), ("wup", hid, inter), ("wdown", inter, hid)]
+
+
+def step_model(name: str, threads: int | None = None):
+    """(cfg, weights) of a step model.  weights: "embed" float32 (vocab,
+    hidden) N(0, 1); "out_norm" and per layer the four norm gains, float32
+    uniform in [0.5, 1.5]; "lm_head" and the seven projections per layer as
+    flat uint8 Q8_0 (drawn like every other weight here: op index i of the
+    encode order -- layer l's projections are 7 l .. 7 l + 6, the lm_head
+    7 n_layers -- on the model's seed); "layers" a list of dicts."""
+    cfg = dict(STEP_MODELS[name])
+    seed = STEP_SEED[name]
+    L = cfg["n_layers"]
+    shapes = step_proj_shapes(cfg)
+    jobs = [(7 * l + j, n, p) for l in range(L) for j, (_, n, p) in enumerate(shapes)]
+    jobs.append((7 * L, cfg["hidden"], cfg["vocab"]))
+    threads = threads or min(16, os.cpu_count() or 1)
+    with _cf.ThreadPoolExecutor(max_workers=threads) as ex:
+        ws = list(ex.map(lambda j: q8_weights(j[1], j[2], rng_for(seed, j[0], ROLE_W)), jobs))
+    layers = []
+    for l in range(L):
+        d = {nm: ws[7 * l + j] for j, (nm, _, _) in enumerate(shapes)}
+        r = rng_for(seed, l, ROLE_NORM)
+        for nm in NORMS:
+            dim = cfg["head_dim"] if nm in ("q_norm", "k_norm") else cfg["hidden"]
+            d[nm] = r.uniform(0.5, 1.5, size=dim).astype(np.float32)
+        layers.append(d)
+    r = rng_for(seed, L, ROLE_NORM)
+    weights = {"embed": rng_for(seed, 0, ROLE_EMBED).standard_normal(
+                   cfg["vocab"] * cfg["hidden"], dtype=np.float32).reshape(cfg["vocab"], cfg["hidden"]),
+               "out_norm": r.uniform(0.5, 1.5, size=cfg["hidden"]).astype(np.float32),
+               "lm_head": ws[7 * L], "layers": layers}
+    return cfg, weights

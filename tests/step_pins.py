@@ -179,10 +179,114 @@ def pin_argmax(o):
     assert o.argmax_row(x) == int(np.argmax(x))
 
 
+# ---------------------------------------------------------------- the composed step
+# A one-layer model whose projections are 0/1 (or 0/2) selection matrices
+# with unit scales, so each stage's result is a plain function of the
+# previous one: the step must reduce to the pinned pieces above, in the
+# order and with the weights the step's wiring prescribes.
+_S = dict(n_layers=1, hidden=256, n_heads=8, n_kv_heads=2, head_dim=32, inter=512, vocab=8,
+          eps=1e-6, theta=1e4)
+
+
+def _q8(dense):
+    """Q8_0 bytes of an integer matrix (|entries| <= 127) with scale 1."""
+    import synth
+    dense = np.asarray(dense)
+    p, n = dense.shape
+    nb = p * n // 32
+    return synth.pack_blocks(np.ones(nb, np.float16), dense.astype(np.int8).reshape(nb, 32))
+
+
+def _sel(p, n, k=1):
+    m = np.zeros((p, n), np.int64)
+    r = min(p, n)
+    m[np.arange(r), np.arange(r)] = k
+    return m
+
+
+def _structured(attention: bool):
+    c = _S
+    hid, qw, kvw, inter = c["hidden"], c["n_heads"] * c["head_dim"], c["n_kv_heads"] * c["head_dim"], c["inter"]
+    rng = np.random.default_rng(11)
+    z = lambda p, n: np.zeros((p, n), np.int64)
+    L = {"wq": _sel(qw, hid) if attention else z(qw, hid),
+         "wk": _sel(kvw, hid) if attention else z(kvw, hid),
+         "wv": _sel(kvw, hid) if attention else z(kvw, hid),
+         "wo": _sel(hid, qw) if attention else z(hid, qw),
+         "wgate": z(inter, hid) if attention else _sel(inter, hid),
+         "wup": z(inter, hid) if attention else _sel(inter, hid, 2),
+         "wdown": z(hid, inter) if attention else _sel(hid, inter)}
+    L = {k: _q8(v) for k, v in L.items()}
+    for k, lo in (("attn_norm", 0.5), ("ffn_norm", 1.5), ("q_norm", 0.7), ("k_norm", 1.2)):
+        dim = c["head_dim"] if k in ("q_norm", "k_norm") else hid
+        L[k] = rng.uniform(lo, lo + 0.3, dim).astype(np.float32)
+    lm = np.zeros((c["vocab"], hid), np.int64)
+    lm[np.arange(c["vocab"]), 3 * np.arange(c["vocab"])] = 1     # logit r = x_final[3 r]
+    w = {"embed": rng.standard_normal((c["vocab"], hid)).astype(np.float32),
+         "out_norm": rng.uniform(0.9, 1.1, hid).astype(np.float32),
+         "lm_head": _q8(lm), "layers": [L]}
+    caches = ([np.zeros((4, kvw), np.float32)], [np.zeros((4, kvw), np.float32)])
+    return c, w, caches
+
+
+def _f32(a):
+    return np.asarray(a, np.float64).astype(np.float32)
+
+
+def pin_step_attention_wiring(o):
+    """Selection projections, zero FFN: after two tokens the residual is
+    embed + attention output (query head h reading KV head h // group),
+    the caches hold the normed, rotated keys and the values at rows 0, 1,
+    and the logits are the final norm of the residual at the lm_head's
+    selected columns."""
+    c, w, (kc, vc) = _structured(True)
+    L, hd, nh, kvw = w["layers"][0], c["head_dim"], c["n_heads"], c["n_kv_heads"] * c["head_dim"]
+    for pos, tok in enumerate((3, 6)):
+        tok_out, y, _, _, x = o.decode_step(c, w, kc, vc, tok, pos)
+        e = w["embed"][tok]
+        xn = _f32(o.rms_norm_rows(e, L["attn_norm"], c["hidden"], c["eps"])).reshape(-1)
+        q = _f32(o.rope_rows(_f32(o.rms_norm_rows(xn, L["q_norm"], hd, c["eps"])), hd, pos, c["theta"]))
+        k = _f32(o.rope_rows(_f32(o.rms_norm_rows(xn[:kvw], L["k_norm"], hd, c["eps"])), hd, pos,
+                             c["theta"])).reshape(-1)
+        _close(kc[0][pos], k, 1e-7)
+        _close(vc[0][pos], xn[:kvw], 0)
+        assert not np.any(kc[0][pos + 1:]) and not np.any(vc[0][pos + 1:])
+        keys = kc[0][:pos + 1].astype(np.float64)
+        vals = vc[0][:pos + 1].astype(np.float64)
+        a = np.empty((nh, hd))
+        for h in range(nh):
+            g = h // (nh // c["n_kv_heads"])
+            sc = keys[:, g * hd:(g + 1) * hd] @ q.reshape(nh, hd)[h].astype(np.float64) / math.sqrt(hd)
+            p = np.exp(sc - sc.max())
+            a[h] = (p / p.sum()) @ vals[:, g * hd:(g + 1) * hd]
+        if pos == 0:   # one cached row: the output is that row's values
+            _close(a.reshape(-1), np.repeat(xn[:kvw].reshape(2, 1, hd), 4, axis=1).reshape(-1), 1e-12)
+        x_ref = _f32(e.astype(np.float64) + _f32(a).reshape(-1))
+        _close(x, x_ref, 1e-6)
+        fin = _f32(o.rms_norm_rows(x_ref, w["out_norm"], c["hidden"], c["eps"])).reshape(-1)
+        _close(y, fin[3 * np.arange(c["vocab"])], 1e-6)
+        assert tok_out == int(np.argmax(fin[3 * np.arange(c["vocab"])]))
+
+
+def pin_step_ffn_wiring(o):
+    """Zero attention, gate = selection, up = 2 x selection, down =
+    selection: the residual gains silu(g) * 2 g for g the ffn-normed
+    embedding (SiLU on the gate, not on the up projection)."""
+    c, w, (kc, vc) = _structured(False)
+    L = w["layers"][0]
+    _, y, _, _, x = o.decode_step(c, w, kc, vc, 5, 0)
+    e = w["embed"][5].astype(np.float64)
+    g = _f32(o.rms_norm_rows(e, L["ffn_norm"], c["hidden"], c["eps"])).reshape(-1).astype(np.float64)
+    x_ref = _f32(e + _f32(g / (1.0 + np.exp(-g)) * (2.0 * g)))
+    _close(x, x_ref, 1e-6)
+    assert not np.any(vc[0])    # zero projections leave zero values
+
+
 ALL_PINS = [
     pin_rms_hand_worked, pin_rms_unit_mean_square, pin_rms_eps,
     pin_rope_hand_worked, pin_rope_invariants,
     pin_attention_hand_worked, pin_attention_special_cases, pin_attention_gqa,
     pin_attention_permutation,
     pin_silu_identities, pin_add_exact, pin_append, pin_argmax,
+    pin_step_attention_wiring, pin_step_ffn_wiring,
 ]

@@ -7,13 +7,15 @@ import re
 import pytest
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
-HEADER = os.path.join(ROOT, "include", "q8gemv.h")
+HEADERS = [os.path.join(ROOT, "include", h) for h in ("q8gemv.h", "q8step.h")]
 
 
 def declared_functions():
-    text = open(HEADER).read()
-    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(q8_0_\w+)\s*\(", text)))
+    names = set()
+    for h in HEADERS:
+        text = re.sub(r"/\*.*?\*/", "", open(h).read(), flags=re.S)
+        names.update(re.findall(r"\b(q8_0_\w+)\s*\(", text))
+    return sorted(names)
 
 
 @pytest.fixture(scope="module")
@@ -25,7 +27,9 @@ def q8():
 def test_header_declares_the_boundary():
     names = declared_functions()
     for required in ("q8_0_gemv", "q8_0_gemm_smallm", "q8_0_decode_chain",
-                     "q8_0_chain_create", "q8_0_chain_destroy"):
+                     "q8_0_chain_create", "q8_0_chain_destroy", "q8_0_rms_norm",
+                     "q8_0_attention_decode", "q8_0_argmax", "q8_0_step_create",
+                     "q8_0_step_run"):
         assert required in names
 
 
@@ -101,3 +105,91 @@ def test_no_device_path(q8):
         pytest.skip("a device is visible")
     assert q8.gemv_raw(X, W, Y, 64, 4) == -5
     assert q8.gemm_smallm_raw(X, W, Y, 2, 64, 4) == -5
+    assert q8.lib.q8_0_rms_norm(X, W, Y, 64, 1, 1e-6, None) == -5
+    assert q8.lib.q8_0_argmax(X, 8, Y, None) == -5
+    layers = (q8.Q8LayerW * 1)(_layer(q8))
+    h = ctypes.c_void_p()
+    assert q8.lib.q8_0_step_create(ctypes.byref(_model(q8, layers)), ctypes.byref(h)) == -5
+
+
+# ------------------------------------------------------------------ the decode-step calls
+F = 0x40000000   # another fake, 256-B aligned address
+
+
+@pytest.mark.parametrize("call,code", [
+    (lambda L: L.q8_0_rms_norm(0, W, Y, 64, 1, 1e-6, None), -1),
+    (lambda L: L.q8_0_rms_norm(X, W, Y, 0, 1, 1e-6, None), -2),
+    (lambda L: L.q8_0_rms_norm(X, W, Y, 64, 0, 1e-6, None), -2),
+    (lambda L: L.q8_0_rms_norm(X, W, Y, 65537, 1, 1e-6, None), -2),
+    (lambda L: L.q8_0_rms_norm(X + 2, W, Y, 64, 1, 1e-6, None), -3),
+    (lambda L: L.q8_0_rms_norm(X, W, X + 8, 64, 1, 1e-6, None), -4),   # partial overlap
+    (lambda L: L.q8_0_rms_norm(X, W, W + 4, 64, 1, 1e-6, None), -4),
+    (lambda L: L.q8_0_rms_norm(X, W, Y, 64, 1, -1.0, None), -1),
+    (lambda L: L.q8_0_rope(0, 64, 1, 0, 1e4, None), -1),
+    (lambda L: L.q8_0_rope(X, 63, 1, 0, 1e4, None), -2),
+    (lambda L: L.q8_0_rope(X, 64, 0, 0, 1e4, None), -2),
+    (lambda L: L.q8_0_rope(X, 64, 1, -1, 1e4, None), -2),
+    (lambda L: L.q8_0_rope(X, 64, 1, 0, 0.0, None), -1),
+    (lambda L: L.q8_0_append_kv(X, 0, Y, F, 64, 0, None), -1),
+    (lambda L: L.q8_0_append_kv(X, W, Y, F, 64, 65536, None), -2),
+    (lambda L: L.q8_0_append_kv(X, W, Y + 2, F, 64, 0, None), -3),
+    (lambda L: L.q8_0_attention_decode(X, W, F, 0, 8, 128, 64, 2, 1, None), -1),
+    (lambda L: L.q8_0_attention_decode(X, W, F, Y, 8, 128, 96, 2, 1, None), -2),   # head_dim
+    (lambda L: L.q8_0_attention_decode(X, W, F, Y, 8, 128, 64, 3, 2, None), -2),   # n_heads % group
+    (lambda L: L.q8_0_attention_decode(X, W, F, Y, 8, 64, 64, 2, 1, None), -2),    # kv_width
+    (lambda L: L.q8_0_attention_decode(X, W, F, Y, 0, 128, 64, 2, 1, None), -2),
+    (lambda L: L.q8_0_attention_decode(X, W, F, Y, 65537, 128, 64, 2, 1, None), -2),
+    (lambda L: L.q8_0_attention_decode(X, W, F, X + 4, 8, 128, 64, 2, 1, None), -4),
+    (lambda L: L.q8_0_add_inplace(X, 0, 8, None), -1),
+    (lambda L: L.q8_0_add_inplace(X, X + 4, 8, None), -4),
+    (lambda L: L.q8_0_add_inplace(X, Y, 0, None), -2),
+    (lambda L: L.q8_0_silu_hadamard(X, W, X + 4, 8, None), -4),
+    (lambda L: L.q8_0_silu_hadamard(X, W, Y, -3, None), -2),
+    (lambda L: L.q8_0_argmax(X, 0, Y, None), -2),
+    (lambda L: L.q8_0_argmax(X, 8, X + 4, None), -4),
+    (lambda L: L.q8_0_argmax(X, 8, Y + 1, None), -3),
+])
+def test_step_op_validation(q8, call, code):
+    assert call(q8.lib) == code
+    assert q8.last_error() != ""
+
+
+def _layer(q8):
+    return q8.Q8LayerW(*([W] * 7 + [X] * 4))
+
+
+def _model(q8, layers, **kw):
+    base = dict(n_layers=1, hidden=256, n_heads=4, n_kv_heads=2, head_dim=64, inter=512,
+                vocab=1000, max_seq=64, eps=1e-6, theta=1e6)
+    base.update(kw)
+    return q8.Q8Model(base["n_layers"], base["hidden"], base["n_heads"], base["n_kv_heads"],
+                      base["head_dim"], base["inter"], base["vocab"], base["max_seq"],
+                      base["eps"], base["theta"], F, F, W, layers)
+
+
+@pytest.mark.parametrize("kw", [
+    dict(n_layers=0), dict(head_dim=96), dict(n_heads=3), dict(n_kv_heads=0),
+    dict(hidden=250), dict(inter=0), dict(vocab=0), dict(max_seq=0), dict(max_seq=65537),
+    dict(eps=-1.0), dict(theta=0.0),
+])
+def test_step_create_validation(q8, kw):
+    layers = (q8.Q8LayerW * 1)(_layer(q8))
+    m = _model(q8, layers, **kw)
+    h = ctypes.c_void_p()
+    assert q8.lib.q8_0_step_create(ctypes.byref(m), ctypes.byref(h)) in (-1, -2)
+    assert h.value is None
+
+
+def test_step_create_null_weight(q8):
+    L = _layer(q8)
+    L.wdown = None
+    layers = (q8.Q8LayerW * 1)(L)
+    m = _model(q8, layers)
+    h = ctypes.c_void_p()
+    assert q8.lib.q8_0_step_create(ctypes.byref(m), ctypes.byref(h)) == -1
+    assert "layer 0" in q8.last_error()
+    assert q8.lib.q8_0_step_create(None, ctypes.byref(h)) == -1
+    assert q8.lib.q8_0_step_run(None, 0, None) == -1
+    assert q8.lib.q8_0_step_reset(None, 0, 0, None) == -1
+    assert q8.lib.q8_0_step_launches(None) == -1
+    assert q8.lib.q8_0_step_destroy(None) == 0

@@ -29,6 +29,18 @@ MUTANTS = {
     "append_wrong_row": ("kc[pos] = ", "kc[pos - 1] = "),
     "argmax_ties_high": ("(v == best and i < besti)", "(v == best and i > besti)"),
     "argmax_ties_last": ("if v > best or", "if v >= best or"),
+    "step_silu_on_up": ('silu_hadamard(mv(L["wgate"], xn, hid, inter), mv(L["wup"], xn, hid, inter))',
+                        'silu_hadamard(mv(L["wup"], xn, hid, inter), mv(L["wgate"], xn, hid, inter))'),
+    "step_ffn_residual_dropped": ('x = _r32(add_inplace(x, mv(L["wdown"], h, inter, hid)))',
+                                  'x = _r32(mv(L["wdown"], h, inter, hid))'),
+    "step_attn_residual_dropped": ('x = _r32(add_inplace(x, mv(L["wo"], a, qw, hid)))',
+                                   'x = _r32(mv(L["wo"], a, qw, hid))'),
+    "step_kv_group": ("pos + 1, kvw, hd, nh, nh // nkv)", "pos + 1, kvw, hd, nh, nkv)"),
+    "step_rope_next_position": ("k = _r32(rope_rows(k, hd, pos, theta))", "k = _r32(rope_rows(k, hd, pos + 1, theta))"),
+    "step_attention_skips_current": ("kc[l], vc[l], pos + 1,", "kc[l], vc[l], max(pos, 1),"),
+    "step_k_normed_with_q_gain": ('k = _r32(rms_norm_rows(k, L["k_norm"]', 'k = _r32(rms_norm_rows(k, L["q_norm"]'),
+    "step_ffn_uses_attn_norm": ('rms_norm_rows(x, L["ffn_norm"]', 'rms_norm_rows(x, L["attn_norm"]'),
+    "step_final_norm_gain": ('rms_norm_rows(x, w["out_norm"]', 'rms_norm_rows(x, L["ffn_norm"]'),
 }
 
 
