@@ -130,6 +130,66 @@ def bench_smallm(args, q8, synth, torch, np):
             "cases": cases}
 
 
+def bench_step(args, q8, synth, torch, np):
+    """A whole Qwen3-0.6B-shaped decode token (embedding, 28 layers of norms,
+    projections, rotary embedding, cache append, attention, SwiGLU, residual
+    adds, then the final norm, the lm_head and argmax) replayed from its
+    recorded hipGraph, greedy: each token feeds the next on the device.
+    Timed from two starting positions (a short and a 511-token context)."""
+    cfg, w = synth.step_model("qwen3_0.6b")
+    cfg["max_seq"] = args.step_max_seq
+    shapes = dict((nm, (p, n)) for nm, n, p in synth.step_proj_shapes(cfg))
+    dev = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to("cuda")
+    layers = [{k: (dev(a.reshape(shapes[k][0], -1)) if k in shapes else dev(a)) for k, a in L.items()}
+              for L in w["layers"]]
+    wd = {"embed": dev(w["embed"]), "out_norm": dev(w["out_norm"]),
+          "lm_head": dev(w["lm_head"].reshape(cfg["vocab"], -1)), "layers": layers}
+    del w
+    torch.cuda.synchronize()
+    st = q8.Step(cfg, wd)
+    stream = torch.cuda.current_stream()
+    launches = st.launches
+    say("step: %d launches per token, %.2f GB resident" % (launches, torch.cuda.memory_allocated() / 1e9))
+
+    def timed(mode, k):
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record(stream)
+        for _ in range(k):
+            st.run(mode, stream)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / 1e3 / k
+
+    cases = []
+    for pos0 in (0, 511):
+        rec = {"start_pos": pos0, "tokens": args.steps}
+        for mode, name in ((q8.MODE_GRAPH, "graph"), (q8.MODE_EAGER, "eager")):
+            st.reset(pos0, 1, stream)
+            for _ in range(args.warmup):
+                st.run(mode, stream)
+            st.reset(pos0, 1, stream)
+            t = timed(mode, args.steps)
+            rec[name + "_us_per_token"] = round(t * 1e6, 2)
+            rec[name + "_tokens_per_s"] = round(1.0 / t, 1)
+            say("step from pos %d, %s: %.1f us/token, %.0f tokens/s" % (pos0, name, t * 1e6, 1.0 / t))
+        cases.append(rec)
+    st.close()
+    short = cases[0]
+    return {"metric": "Qwen3-0.6B-shaped greedy decode step (whole token, one hipGraph)",
+            "value": short["graph_tokens_per_s"], "unit": "tokens/s", "n_gpus": 1,
+            "steps": args.steps, "warmup": args.warmup,
+            "ms_per_step": round(short["graph_us_per_token"] / 1e3, 5),
+            "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+            "dtype": "f32", "data": "synthetic",
+            "config": {"workload": "qwen3_0.6b decode step", "launches_per_token": launches,
+                       "max_seq": cfg["max_seq"],
+                       "weights": "the qwen3_0.6b_chain projection bytes; f32 embedding N(0,1), "
+                                  "norm gains U[0.5,1.5]"},
+            "cases": cases}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -143,6 +203,10 @@ def main():
     ap.add_argument("--smallm", action="store_true",
                     help="instead of the chain: time q8_0_gemm_smallm at the 7B shapes, "
                          "m in {2,4,8,16}, rotating weight copies past the 256 MB cache")
+    ap.add_argument("--step", action="store_true",
+                    help="instead of the chain: time a whole Qwen3-0.6B-shaped decode token "
+                         "(every kernel of the step, one hipGraph) from positions 0 and 511")
+    ap.add_argument("--step-max-seq", type=int, default=2048)
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="instead of the bench: copy MIB MiB device-to-device 5 times "
                          "(the known-size kernel that scales the HBM byte counters)")
@@ -176,6 +240,9 @@ def main():
         return
     if args.smallm:
         print(json.dumps(bench_smallm(args, q8, synth, torch, np)), flush=True)
+        return
+    if args.step:
+        print(json.dumps(bench_step(args, q8, synth, torch, np)), flush=True)
         return
     ops_shape = synth.WORKLOADS[args.workload]
     nbytes = synth.workload_bytes(ops_shape)

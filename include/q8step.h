@@ -58,8 +58,9 @@ int q8_0_append_kv(const float *k, const float *v, float *kc, float *vc, int64_t
  * h / kv_group (row t of the caches holds all KV heads, kv_width floats):
  *   out[h] = sum_{t < seq} softmax_t(q_h . k_t / sqrt(head_dim)) v_t
  * n_heads a multiple of kv_group; kv_width >= (n_heads / kv_group) *
- * head_dim; 1 <= seq <= Q8_MAX_SEQ.  Uses a library workspace per (device,
- * stream), allocated on first use and grown when needed, like
+ * head_dim and a multiple of 4; q, kc and vc 16-byte aligned (Q8_ERR_ALIGN
+ * otherwise); 1 <= seq <= Q8_MAX_SEQ.  Uses a library workspace per
+ * (device, stream), allocated on first use and grown when needed, like
  * q8_0_gemm_smallm.  Bitwise reproducible for the same inputs and shape.
  */
 int q8_0_attention_decode(const float *q, const float *kc, const float *vc, float *out,
@@ -88,20 +89,24 @@ int q8_0_argmax(const float *x, int64_t n, uint32_t *out, void *stream);
  *     x += Wo a; xn = rms_norm(x, ffn_norm); h = silu(Wgate xn) * (Wup xn);
  *     x += Wdown h
  *   logits = lm_head rms_norm(x, out_norm); token = argmax(logits); pos += 1
- * Independent matvecs (q, k, v; gate, up) share one fused launch.
+ * Independent matvecs (q, k, v; gate, up) share one fused launch, and the
+ * small kernels are fused where one feeds the next: the embedding row with
+ * the first norm, each residual add with the norm after it, the per-head
+ * q/k norms with the rotary embedding and the cache append, and argmax with
+ * the position advance.
  */
 typedef struct q8_0_layer_w {
     const void *wq, *wk, *wv, *wo;   /* Q8_0, 16-B aligned, as q8_0_gemv's w */
     const void *wgate, *wup, *wdown;
-    const float *attn_norm, *ffn_norm;   /* hidden floats */
+    const float *attn_norm, *ffn_norm;   /* hidden floats, 16-B aligned */
     const float *q_norm, *k_norm;        /* head_dim floats */
 } q8_0_layer_w;
 
 typedef struct q8_0_model {
     int64_t n_layers, hidden, n_heads, n_kv_heads, head_dim, inter, vocab, max_seq;
     float eps, theta;
-    const float *embed;       /* vocab x hidden */
-    const float *out_norm;    /* hidden */
+    const float *embed;       /* vocab x hidden, 16-B aligned */
+    const float *out_norm;    /* hidden, 16-B aligned */
     const void *lm_head;      /* Q8_0, vocab rows of hidden */
     const q8_0_layer_w *layers;   /* n_layers entries, copied at create */
 } q8_0_model;

@@ -28,6 +28,21 @@ struct ArgmaxDesc {
     float *ws_val;       // one (value, index) per workgroup
     uint32_t *ws_idx;
     uint32_t *cnt;       // arrival counter, zero between launches
+    int *pos_dev;        // if set, incremented once the index is written
+};
+
+// The per-head work between the q/k/v projections and attention in a
+// recorded token: q heads normed (q_norm) and rotated in place; k heads
+// normed (k_norm), rotated and stored at cache row *pos_dev; v heads stored
+// there.  Rows past `rows` (the caches' length) are not written.
+struct QkPostDesc {
+    float *q;
+    const float *k, *v;
+    const float *q_norm, *k_norm;
+    float *kc, *vc;
+    const int *pos_dev;
+    int n_heads, n_kv, kv_width, rows;
+    float eps, theta;
 };
 
 // pos_dev, when not null, overrides pos (a recorded step reads it per replay)
@@ -38,13 +53,19 @@ hipError_t launch_rope(float *x, int head_dim, int heads, const int *pos_dev, in
 // rows: the caches' length; a position at or past it writes nothing.
 hipError_t launch_append_kv(const float *k, const float *v, float *kc, float *vc, int width,
                             const int *pos_dev, int pos, int rows, hipStream_t s);
+// head_dim 64, 128, 192 or 256; q, kc, vc 16-byte aligned, kv_width % 4 == 0
 hipError_t launch_attention(const AttnDesc &d, hipStream_t s);
 hipError_t launch_add(float *x, const float *y, int n, hipStream_t s);
 hipError_t launch_silu(const float *g, const float *u, float *out, int n, hipStream_t s);
 hipError_t launch_argmax(const ArgmaxDesc &d, int wgs, hipStream_t s);
-hipError_t launch_embed(const float *table, const uint32_t *token, uint32_t vocab, float *x, int dim,
-                        hipStream_t s);
-hipError_t launch_advance(int *pos_dev, hipStream_t s);
+// head_dim 64, 128, 192 or 256; q, k, v, kc, vc 16-byte aligned, kv_width % 4 == 0
+hipError_t launch_qk_post(const QkPostDesc &d, int head_dim, hipStream_t s);
+// x += y, then xn = rms_norm(x) * w (one wave; dim % 4 == 0, 16-byte aligned)
+hipError_t launch_add_rms(float *x, const float *y, const float *w, float *xn, int dim, float eps,
+                          hipStream_t s);
+// x = row *token of table (zeros if *token >= vocab), then xn = rms_norm(x) * w
+hipError_t launch_embed_rms(const float *table, const uint32_t *token, uint32_t vocab, float *x,
+                            const float *w, float *xn, int dim, float eps, hipStream_t s);
 // *pos_dev = pos, *token_dev = token, ordered on s (a kernel, so it may be recorded).
 hipError_t launch_set_state(int *pos_dev, uint32_t *token_dev, int pos, uint32_t token, hipStream_t s);
 

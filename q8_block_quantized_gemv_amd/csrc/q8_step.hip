@@ -1,20 +1,31 @@
 // q8_step.hip -- gfx950 kernels for the rest of a decode step: the seven
 // kernels the page "IV.4: One command buffer per token" (section "Eight
 // kernels") puts around q8_matvec -- rms_norm_row, rope_row, append_kv,
-// attention_decode, add_inplace, silu_hadamard, argmax_row -- plus the two
-// a device-resident token loop needs (the embedding row of the previous
-// token, and advancing the position).
+// attention_decode, add_inplace, silu_hadamard, argmax_row -- and the fused
+// forms a recorded token uses.
 //
-// Designed for CDNA4 rather than taken over from the page's threadgroups:
-//  * rows are reduced by one 64-lane wave with a fixed butterfly (no LDS);
+// Designed for CDNA4 rather than taken over from the page's threadgroups.
+// These kernels move kilobytes, so their time is memory latency, not
+// bandwidth: every kernel issues all of a lane's loads before it uses any
+// (float4 loads into register arrays), so a kernel costs about one trip to
+// HBM instead of one trip per loop iteration.
+//  * a row (a norm, a head) belongs to one 64-lane wave and is reduced with
+//    a fixed butterfly (no LDS, no atomics);
 //  * attention splits each head's cached rows into chunks of kAttnChunk
-//    handled by separate workgroups (so a 16-head step uses hundreds of CUs,
-//    not 16) and the last chunk to arrive merges the partial softmaxes in
-//    chunk order -- deterministic, like every other reduction here;
+//    handled by separate workgroups (a 16-head step uses many CUs, not 16);
+//    the last chunk to arrive merges the partial softmaxes in chunk order --
+//    deterministic, like every reduction here;
 //  * argmax scans with many workgroups and merges their winners the same
 //    way, with the page's comparison (greater, or equal at a lower index).
-// Kernels that a recorded token replays read the position from device
-// memory (pos_dev), so one recording serves every token.
+// The fused kernels of a recorded token (the page encodes each of its
+// kernels separately; fewer, larger launches suit a hipGraph better):
+//  * embed_rms: x = embedding row of the token, xn = rms_norm(x);
+//  * add_rms: x += y, xn = rms_norm(x) (the residual add and the next norm);
+//  * qk_post: per-head q and k norms, rotary embedding of q and k, and the
+//    K/V cache append, one wave per head;
+//  * argmax also advances the position.
+// Kernels a recorded token replays read the position from device memory
+// (pos_dev), so one recording serves every token.
 #include "q8_step.h"
 
 namespace q8 {
@@ -38,37 +49,214 @@ __device__ __forceinline__ int position(const int *pos_dev, int pos) {
     return pos_dev ? *pos_dev : pos;
 }
 
+__device__ __forceinline__ float sq4(float4 v, float acc) {
+    acc = fmaf(v.x, v.x, acc);
+    acc = fmaf(v.y, v.y, acc);
+    acc = fmaf(v.z, v.z, acc);
+    return fmaf(v.w, v.w, acc);
+}
+
+__device__ __forceinline__ float4 scale4(float4 x, float inv, float4 w) {
+    return make_float4(x.x * inv * w.x, x.y * inv * w.y, x.z * inv * w.z, x.w * inv * w.w);
+}
+
 // ---------------------------------------------------------------- rms_norm_row
-// One wave per row: out = x * (sum(x^2)/dim + eps)^(-1/2) * w.  out may be x.
-__global__ __launch_bounds__(kWave) void k_rms_norm(const float *x, const float *w, float *out,
-                                                    int dim, float eps) {
+// out = x * (sum(x^2)/dim + eps)^(-1/2) * w, one wave per row.
+constexpr int kNormRegs = 16;                           // float4 a lane holds
+constexpr int kNormMaxInRegs = kWave * kNormRegs * 4;   // 4096 floats
+
+__device__ __forceinline__ float rms_inv(float ss, int dim, float eps) {
+    return 1.0f / sqrtf(ss / (float)dim + eps);
+}
+
+// A row of nv float4 (dim = 4 nv <= kNormMaxInRegs) into registers; returns
+// its sum of squares through the butterfly.
+__device__ __forceinline__ float load_row4(const float4 *xr, int nv, float4 (&xv)[kNormRegs]) {
     const int lane = lane_id();
-    const float *xr = x + (int64_t)blockIdx.x * dim;
-    float *orow = out + (int64_t)blockIdx.x * dim;
+#pragma unroll
+    for (int e = 0; e < kNormRegs; ++e) {
+        const int i = lane + kWave * e;
+        xv[e] = i < nv ? xr[i] : make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+    float ss = 0.f;
+#pragma unroll
+    for (int e = 0; e < kNormRegs; ++e) ss = sq4(xv[e], ss);
+    return wave_sum(ss);
+}
+
+__device__ __forceinline__ void store_row4(float4 *orow, const float4 *w4, int nv, float inv,
+                                           const float4 (&xv)[kNormRegs]) {
+    const int lane = lane_id();
+    float4 wv[kNormRegs];
+#pragma unroll
+    for (int e = 0; e < kNormRegs; ++e) {
+        const int i = lane + kWave * e;
+        wv[e] = i < nv ? w4[i] : make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+#pragma unroll
+    for (int e = 0; e < kNormRegs; ++e) {
+        const int i = lane + kWave * e;
+        if (i < nv) orow[i] = scale4(xv[e], inv, wv[e]);
+    }
+}
+
+// One row by one wave, any dim (float4 path when V).
+template <bool V>
+__device__ __forceinline__ void rms_row(const float *xr, const float *w, float *orow, int dim,
+                                        float eps) {
+    const int lane = lane_id();
+    if (V && dim <= kNormMaxInRegs) {
+        float4 xv[kNormRegs];
+        const int nv = dim / 4;
+        const float ss = load_row4((const float4 *)xr, nv, xv);
+        store_row4((float4 *)orow, (const float4 *)w, nv, rms_inv(ss, dim, eps), xv);
+        return;
+    }
+    if (V) {   // long rows: batches of kNormRegs float4 per lane, then a second pass
+        const int nv = dim / 4;
+        const float4 *x4 = (const float4 *)xr;
+        float ss = 0.f;
+        for (int b = 0; b < nv; b += kWave * kNormRegs) {
+            float4 xv[kNormRegs];
+#pragma unroll
+            for (int e = 0; e < kNormRegs; ++e) {
+                const int i = b + lane + kWave * e;
+                xv[e] = i < nv ? x4[i] : make_float4(0.f, 0.f, 0.f, 0.f);
+            }
+#pragma unroll
+            for (int e = 0; e < kNormRegs; ++e) ss = sq4(xv[e], ss);
+        }
+        const float inv = rms_inv(wave_sum(ss), dim, eps);
+        for (int b = 0; b < nv; b += kWave * kNormRegs) {
+            float4 xv[kNormRegs], wv[kNormRegs];
+#pragma unroll
+            for (int e = 0; e < kNormRegs; ++e) {
+                const int i = b + lane + kWave * e;
+                xv[e] = i < nv ? x4[i] : make_float4(0.f, 0.f, 0.f, 0.f);
+                wv[e] = i < nv ? ((const float4 *)w)[i] : make_float4(0.f, 0.f, 0.f, 0.f);
+            }
+#pragma unroll
+            for (int e = 0; e < kNormRegs; ++e) {
+                const int i = b + lane + kWave * e;
+                if (i < nv) ((float4 *)orow)[i] = scale4(xv[e], inv, wv[e]);
+            }
+        }
+        return;
+    }
     float ss = 0.f;
     for (int i = lane; i < dim; i += kWave) ss = fmaf(xr[i], xr[i], ss);
-    ss = wave_sum(ss);
-    const float inv = 1.0f / sqrtf(ss / (float)dim + eps);
+    const float inv = rms_inv(wave_sum(ss), dim, eps);
     for (int i = lane; i < dim; i += kWave) orow[i] = xr[i] * inv * w[i];
+}
+
+template <bool V>
+__global__ __launch_bounds__(kThreads) void k_rms_norm(const float *x, const float *w, float *out,
+                                                       int dim, int rows, float eps) {
+    const int row = blockIdx.x * kWaves + (int)(threadIdx.x / kWave);
+    if (row >= rows) return;
+    rms_row<V>(x + (int64_t)row * dim, w, out + (int64_t)row * dim, dim, eps);
+}
+
+// ---------------------------------------------------------------- fused residual + norm
+// EMBED: x = row `token` of the table y (zeros past the table: a row of only
+// NaN logits has no argmax); else x += y.  Then xn = rms_norm(x) * w.
+// One wave; dim % 4 == 0 and x, y, w, xn 16-byte aligned.
+template <bool EMBED>
+__device__ __forceinline__ float4 residual4(const float4 *x4, const float4 *src, bool zero, int i) {
+    if (EMBED) return zero ? make_float4(0.f, 0.f, 0.f, 0.f) : src[i];
+    const float4 a = x4[i], b = src[i];
+    return make_float4(a.x + b.x, a.y + b.y, a.z + b.z, a.w + b.w);
+}
+
+template <bool EMBED>
+__global__ __launch_bounds__(kWave) void k_add_rms(float *x, const float *y, const uint32_t *token,
+                                                   uint32_t vocab, const float *w, float *xn,
+                                                   int dim, float eps) {
+    const int lane = lane_id(), nv = dim / 4;
+    float4 *x4 = (float4 *)x;
+    const float4 *src = (const float4 *)y;
+    bool zero = false;
+    if (EMBED) {
+        const uint32_t t = *token;
+        zero = t >= vocab;
+        src = (const float4 *)(y + (int64_t)(zero ? 0u : t) * dim);
+    }
+    if (nv <= kWave * kNormRegs) {   // the row stays in registers
+        float4 xv[kNormRegs];
+#pragma unroll
+        for (int e = 0; e < kNormRegs; ++e) {
+            const int i = lane + kWave * e;
+            xv[e] = i < nv ? residual4<EMBED>(x4, src, zero, i) : make_float4(0.f, 0.f, 0.f, 0.f);
+        }
+#pragma unroll
+        for (int e = 0; e < kNormRegs; ++e) {
+            const int i = lane + kWave * e;
+            if (i < nv) x4[i] = xv[e];
+        }
+        float ss = 0.f;
+#pragma unroll
+        for (int e = 0; e < kNormRegs; ++e) ss = sq4(xv[e], ss);
+        store_row4((float4 *)xn, (const float4 *)w, nv, rms_inv(wave_sum(ss), dim, eps), xv);
+        return;
+    }
+    // long rows: write x batch by batch, then normalise it (each lane re-reads
+    // only what it wrote itself)
+    float ss = 0.f;
+    for (int b = 0; b < nv; b += kWave * kNormRegs) {
+        float4 xv[kNormRegs];
+#pragma unroll
+        for (int e = 0; e < kNormRegs; ++e) {
+            const int i = b + lane + kWave * e;
+            xv[e] = i < nv ? residual4<EMBED>(x4, src, zero, i) : make_float4(0.f, 0.f, 0.f, 0.f);
+        }
+#pragma unroll
+        for (int e = 0; e < kNormRegs; ++e) {
+            const int i = b + lane + kWave * e;
+            if (i < nv) x4[i] = xv[e];
+            ss = sq4(xv[e], ss);
+        }
+    }
+    const float inv = rms_inv(wave_sum(ss), dim, eps);
+    for (int b = 0; b < nv; b += kWave * kNormRegs) {
+        float4 xv[kNormRegs], wv[kNormRegs];
+#pragma unroll
+        for (int e = 0; e < kNormRegs; ++e) {
+            const int i = b + lane + kWave * e;
+            xv[e] = i < nv ? x4[i] : make_float4(0.f, 0.f, 0.f, 0.f);
+            wv[e] = i < nv ? ((const float4 *)w)[i] : make_float4(0.f, 0.f, 0.f, 0.f);
+        }
+#pragma unroll
+        for (int e = 0; e < kNormRegs; ++e) {
+            const int i = b + lane + kWave * e;
+            if (i < nv) ((float4 *)xn)[i] = scale4(xv[e], inv, wv[e]);
+        }
+    }
 }
 
 // ---------------------------------------------------------------- rope_row
 // Pair (i, i + half) of each head turns by pos * theta^(-i / half); the angle
 // and its sine and cosine are taken in double precision (the page's float32
 // angle loses ~pos * 2^-24 rad), the rotation rounds once to float.
+__device__ __forceinline__ void rotate(double a, double b, int i, int half, int pos, float theta,
+                                       float &ra, float &rb) {
+    const double ang = (double)pos * pow((double)theta, -(double)i / half);
+    double s, c;
+    sincos(ang, &s, &c);
+    ra = (float)(a * c - b * s);
+    rb = (float)(a * s + b * c);
+}
+
 __global__ __launch_bounds__(256) void k_rope(float *x, int head_dim, int heads, const int *pos_dev,
                                               int pos0, float theta) {
     const int half = head_dim / 2;
     const int t = blockIdx.x * 256 + threadIdx.x;
     if (t >= heads * half) return;
     const int h = t / half, i = t - h * half;
-    const double ang = (double)position(pos_dev, pos0) * pow((double)theta, -(double)i / half);
-    double s, c;
-    sincos(ang, &s, &c);
     float *xh = x + (int64_t)h * head_dim;
-    const double a = xh[i], b = xh[i + half];
-    xh[i] = (float)(a * c - b * s);
-    xh[i + half] = (float)(a * s + b * c);
+    float ra, rb;
+    rotate(xh[i], xh[i + half], i, half, position(pos_dev, pos0), theta, ra, rb);
+    xh[i] = ra;
+    xh[i + half] = rb;
 }
 
 // ---------------------------------------------------------------- append_kv
@@ -84,45 +272,131 @@ __global__ __launch_bounds__(256) void k_append_kv(const float *k, const float *
     vc[row + i] = v[i];
 }
 
+// ---------------------------------------------------------------- fused q/k post-processing
+// Workgroup (one wave) b: b < n_heads: query head b -- rms_norm with q_norm,
+// then rope, in place in q.  b < n_heads + n_kv: key head -- rms_norm with
+// k_norm, rope, stored into cache row pos.  Else value head: copied into
+// cache row pos.  A lane holds elements lane + 64 e of the head; the rope
+// pairs meet through LDS.
+template <int HD>
+__global__ __launch_bounds__(kWave) void k_qk_post(QkPostDesc d) {
+    constexpr int PER = HD / kWave;   // 1..4
+    constexpr int HALF = HD / 2;
+    __shared__ float buf[HD];
+    const int lane = lane_id();
+    const int b = blockIdx.x;
+    const int pos = *d.pos_dev;
+    const bool in_cache = pos >= 0 && pos < d.rows;
+    if (b >= d.n_heads + d.n_kv) {   // value head
+        const int h = b - d.n_heads - d.n_kv;
+        if (!in_cache) return;
+        float *dst = d.vc + (int64_t)pos * d.kv_width + (int64_t)h * HD;
+        const float *src = d.v + (int64_t)h * HD;
+        float vv[PER];
+#pragma unroll
+        for (int e = 0; e < PER; ++e) vv[e] = src[lane + kWave * e];
+#pragma unroll
+        for (int e = 0; e < PER; ++e) dst[lane + kWave * e] = vv[e];
+        return;
+    }
+    const bool is_q = b < d.n_heads;
+    const int h = is_q ? b : b - d.n_heads;
+    const float *src = (is_q ? d.q : d.k) + (int64_t)h * HD;
+    const float *w = is_q ? d.q_norm : d.k_norm;
+    float xv[PER], wv[PER];
+#pragma unroll
+    for (int e = 0; e < PER; ++e) {
+        xv[e] = src[lane + kWave * e];
+        wv[e] = w[lane + kWave * e];
+    }
+    float ss = 0.f;
+#pragma unroll
+    for (int e = 0; e < PER; ++e) ss = fmaf(xv[e], xv[e], ss);
+    const float inv = rms_inv(wave_sum(ss), HD, d.eps);
+#pragma unroll
+    for (int e = 0; e < PER; ++e) buf[lane + kWave * e] = xv[e] * inv * wv[e];
+    __syncthreads();
+    if (!is_q && !in_cache) return;
+    float *dst = is_q ? d.q + (int64_t)h * HD : d.kc + (int64_t)pos * d.kv_width + (int64_t)h * HD;
+#pragma unroll
+    for (int e = 0; e < (HALF + kWave - 1) / kWave; ++e) {
+        const int i = lane + kWave * e;
+        if (i < HALF) {
+            float ra, rb;
+            rotate(buf[i], buf[i + HALF], i, HALF, pos, d.theta, ra, rb);
+            dst[i] = ra;
+            dst[i + HALF] = rb;
+        }
+    }
+}
+
 // ---------------------------------------------------------------- attention_decode
 // Workgroup (chunk c, head h) of 256 threads: the scores of cached rows
 // [c*kAttnChunk, min(seq, (c+1)*kAttnChunk)) on KV head h / kv_group, their
 // local softmax (max m, sum s of e^(score - m)) and acc[j] = sum e * v[j];
 // the last chunk of a head to arrive merges the parts in chunk order.
-// Rows are scored one per wave: 64 lanes read a key row together (coalesced)
-// and reduce the dot product with a butterfly.
+// Scores: a row is read by L lanes with float4 loads (L = HD/4 rounded up
+// to a power of two), 64/L rows per wave at a time, every row of a lane's
+// share loaded before any is reduced.  Values: thread (column float4,
+// row group) accumulates its rows, the row groups meet in LDS.
 constexpr int kAttnThreads = 256;
 constexpr int kAttnWaves = kAttnThreads / kWave;
+constexpr int kMergeBatch = 8;
 
+template <int HD>
 __global__ __launch_bounds__(kAttnThreads) void k_attention(AttnDesc d) {
+    constexpr int NV = HD / 4;                                   // float4 per row
+    constexpr int L = NV <= 16 ? 16 : NV <= 32 ? 32 : 64;        // lanes per row
+    constexpr int RPW = kWave / L;                               // rows per wave per pass
+    constexpr int RPP = kAttnWaves * RPW;                        // rows per pass
+    constexpr int PASSES = kAttnChunk / RPP;
+    constexpr int SB = PASSES < 16 ? PASSES : 16;                // score loads in flight
+    constexpr int RG = kAttnThreads / NV;                        // value row groups
+    constexpr int RPT = (kAttnChunk + RG - 1) / RG;              // rows per thread
+    constexpr int VB = RPT < 16 ? RPT : 16;                      // value loads in flight
     __shared__ float sc[kAttnChunk];
     __shared__ float red[kAttnWaves];
-    __shared__ float accp[kAttnThreads];
+    __shared__ float4 accp[kAttnThreads];
+    __shared__ uint32_t prev;
     const int head = blockIdx.x % d.n_heads;
     const int c = blockIdx.x / d.n_heads;
     const int seq = d.pos_dev ? min(*d.pos_dev + 1, d.seq) : d.seq;
     const int n_chunks = (seq + kAttnChunk - 1) / kAttnChunk;
     if (c >= n_chunks) return;   // the whole workgroup: no part, no arrival
     const int tid = threadIdx.x, lane = tid & (kWave - 1), wv = tid / kWave;
-    const int hd = d.head_dim, per = hd / kWave;   // elements per lane (1..4)
     const int t0 = c * kAttnChunk, rows = min(kAttnChunk, seq - t0);
-    const int64_t kv_off = (int64_t)(head / d.kv_group) * hd;
-    const float *qh = d.q + (int64_t)head * hd;
-    float qv[4];
+    const int64_t kv_off = (int64_t)(head / d.kv_group) * HD;
+    // ---- scores
+    {
+        const int g = lane / L, col = lane % L;
+        const bool colv = col < NV;
+        float4 q4 = make_float4(0.f, 0.f, 0.f, 0.f);
+        if (colv) q4 = ((const float4 *)(d.q + (int64_t)head * HD))[col];
+        const float scale = 1.0f / sqrtf((float)HD);
+        const float *kbase = d.kc + (int64_t)t0 * d.kv_width + kv_off + 4 * col;
+        for (int p0 = 0; p0 < PASSES; p0 += SB) {
+            float4 kv[SB];
 #pragma unroll
-    for (int e = 0; e < 4; ++e) qv[e] = e < per ? qh[e * kWave + lane] : 0.f;
-    const float scale = 1.0f / sqrtf((float)hd);
-    for (int r = wv; r < rows; r += kAttnWaves) {
-        const float *kr = d.kc + (int64_t)(t0 + r) * d.kv_width + kv_off;
-        float dot = 0.f;
+            for (int b = 0; b < SB; ++b) {
+                const int r = (p0 + b) * RPP + wv * RPW + g;
+                kv[b] = make_float4(0.f, 0.f, 0.f, 0.f);
+                if (colv && r < rows) kv[b] = *(const float4 *)(kbase + (int64_t)r * d.kv_width);
+            }
 #pragma unroll
-        for (int e = 0; e < 4; ++e)
-            if (e < per) dot = fmaf(qv[e], kr[e * kWave + lane], dot);
-        dot = wave_sum(dot);
-        if (lane == 0) sc[r] = dot * scale;
+            for (int b = 0; b < SB; ++b) {
+                float dot = q4.x * kv[b].x;
+                dot = fmaf(q4.y, kv[b].y, dot);
+                dot = fmaf(q4.z, kv[b].z, dot);
+                dot = fmaf(q4.w, kv[b].w, dot);
+#pragma unroll
+                for (int o = L / 2; o > 0; o >>= 1) dot += __shfl_xor(dot, o, kWave);
+                const int r = (p0 + b) * RPP + wv * RPW + g;
+                if (col == 0 && r < rows) sc[r] = dot * scale;
+            }
+        }
     }
     __syncthreads();
-    // local max and sum over the chunk
+    // ---- local max and sum over the chunk
     float m = -INFINITY;
     for (int r = tid; r < rows; r += kAttnThreads) m = fmaxf(m, sc[r]);
     m = wave_max(m);
@@ -140,21 +414,49 @@ __global__ __launch_bounds__(kAttnThreads) void k_attention(AttnDesc d) {
     if (lane == 0) red[wv] = s;
     __syncthreads();
     s = (red[0] + red[1]) + (red[2] + red[3]);
-    // acc[j]: thread (j, part) sums rows part, part + parts, ... of the chunk
-    const int parts = kAttnThreads / hd;
-    const int j = tid % hd, part = tid / hd;
-    float a = 0.f;
-    if (part < parts)
-        for (int r = part; r < rows; r += parts)
-            a = fmaf(sc[r], d.vc[(int64_t)(t0 + r) * d.kv_width + kv_off + j], a);
-    accp[tid] = a;
+    // ---- acc over the chunk's values
+    {
+        const int col = tid % NV, rg = tid / NV;
+        float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+        if (rg < RG) {
+            const float *vbase = d.vc + (int64_t)t0 * d.kv_width + kv_off + 4 * col;
+            for (int r0 = 0; r0 < RPT; r0 += VB) {
+                float4 vv[VB];
+                float ee[VB];
+#pragma unroll
+                for (int b = 0; b < VB; ++b) {
+                    const int r = rg + (r0 + b) * RG;
+                    vv[b] = make_float4(0.f, 0.f, 0.f, 0.f);
+                    ee[b] = 0.f;
+                    if (r < rows) {
+                        vv[b] = *(const float4 *)(vbase + (int64_t)r * d.kv_width);
+                        ee[b] = sc[r];
+                    }
+                }
+#pragma unroll
+                for (int b = 0; b < VB; ++b) {
+                    acc.x = fmaf(ee[b], vv[b].x, acc.x);
+                    acc.y = fmaf(ee[b], vv[b].y, acc.y);
+                    acc.z = fmaf(ee[b], vv[b].z, acc.z);
+                    acc.w = fmaf(ee[b], vv[b].w, acc.w);
+                }
+            }
+        }
+        accp[tid] = acc;
+    }
     __syncthreads();
-    // park (m, s, acc[0..hd)) of this chunk, device-scope, then count in
-    float *mine = d.ws + ((int64_t)head * d.max_chunks + c) * (hd + 2);
-    if (tid < hd) {
-        float t = accp[tid];
-        for (int q = 1; q < parts; ++q) t += accp[q * hd + tid];
-        __hip_atomic_store(mine + 2 + tid, t, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    // ---- park (m, s, acc[0..HD)) of this chunk, device-scope, then count in
+    float *mine = d.ws + ((int64_t)head * d.max_chunks + c) * (HD + 2);
+    if (tid < NV) {
+        float4 t = accp[tid];
+        for (int q = 1; q < RG; ++q) {
+            const float4 u = accp[q * NV + tid];
+            t = make_float4(t.x + u.x, t.y + u.y, t.z + u.z, t.w + u.w);
+        }
+        __hip_atomic_store(mine + 2 + 4 * tid, t.x, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __hip_atomic_store(mine + 3 + 4 * tid, t.y, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __hip_atomic_store(mine + 4 + 4 * tid, t.z, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __hip_atomic_store(mine + 5 + 4 * tid, t.w, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
     if (tid == 0) {
         __hip_atomic_store(mine, m, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -162,27 +464,47 @@ __global__ __launch_bounds__(kAttnThreads) void k_attention(AttnDesc d) {
     }
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
-    __shared__ uint32_t prev;
     if (tid == 0)
         prev = __hip_atomic_fetch_add(d.cnt + head, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     __syncthreads();
     if (prev != (uint32_t)n_chunks - 1) return;
     asm volatile("" ::: "memory");
-    // merge: M = max m_c, S = sum s_c e^(m_c - M), out = sum acc_c e^(m_c - M) / S
-    const float *parts0 = d.ws + (int64_t)head * d.max_chunks * (hd + 2);
+    // ---- merge: M = max m_c, S = sum s_c e^(m_c - M), out = sum acc_c e^(m_c - M) / S
+    const float *parts0 = d.ws + (int64_t)head * d.max_chunks * (HD + 2);
     float M = -INFINITY;
-    for (int q = 0; q < n_chunks; ++q)
-        M = fmaxf(M, __hip_atomic_load(parts0 + (int64_t)q * (hd + 2), __ATOMIC_RELAXED,
-                                       __HIP_MEMORY_SCOPE_AGENT));
-    if (tid < hd) {
+    for (int q0 = 0; q0 < n_chunks; q0 += kMergeBatch) {
+        float mv[kMergeBatch];
+#pragma unroll
+        for (int b = 0; b < kMergeBatch; ++b)
+            mv[b] = q0 + b < n_chunks
+                        ? __hip_atomic_load(parts0 + (int64_t)(q0 + b) * (HD + 2), __ATOMIC_RELAXED,
+                                            __HIP_MEMORY_SCOPE_AGENT)
+                        : -INFINITY;
+#pragma unroll
+        for (int b = 0; b < kMergeBatch; ++b) M = fmaxf(M, mv[b]);
+    }
+    if (tid < HD) {
         float S = 0.f, A = 0.f;
-        for (int q = 0; q < n_chunks; ++q) {
-            const float *pq = parts0 + (int64_t)q * (hd + 2);
-            const float f = expf(__hip_atomic_load(pq, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) - M);
-            S = fmaf(__hip_atomic_load(pq + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT), f, S);
-            A = fmaf(__hip_atomic_load(pq + 2 + tid, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT), f, A);
+        for (int q0 = 0; q0 < n_chunks; q0 += kMergeBatch) {
+            float mv[kMergeBatch], sv[kMergeBatch], av[kMergeBatch];
+#pragma unroll
+            for (int b = 0; b < kMergeBatch; ++b) {
+                const bool ok = q0 + b < n_chunks;
+                const float *pq = parts0 + (int64_t)(ok ? q0 + b : 0) * (HD + 2);
+                mv[b] = __hip_atomic_load(pq, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                sv[b] = __hip_atomic_load(pq + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                av[b] = __hip_atomic_load(pq + 2 + tid, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            }
+#pragma unroll
+            for (int b = 0; b < kMergeBatch; ++b) {
+                if (q0 + b < n_chunks) {
+                    const float f = expf(mv[b] - M);
+                    S = fmaf(sv[b], f, S);
+                    A = fmaf(av[b], f, A);
+                }
+            }
         }
-        d.out[(int64_t)head * hd + tid] = A / S;
+        d.out[(int64_t)head * HD + tid] = A / S;
     }
     if (tid == 0)   // ready for the next launch
         __hip_atomic_store(d.cnt + head, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -221,6 +543,8 @@ __device__ __forceinline__ void wave_best(float &best, uint32_t &besti) {
     }
 }
 
+constexpr int kArgmaxLoads = 8;   // values a thread has in flight
+
 __global__ __launch_bounds__(256) void k_argmax(ArgmaxDesc d) {
     __shared__ float bv[4];
     __shared__ uint32_t bi[4];
@@ -228,8 +552,17 @@ __global__ __launch_bounds__(256) void k_argmax(ArgmaxDesc d) {
     const int tid = threadIdx.x, lane = tid & (kWave - 1), wv = tid / kWave;
     float best = -INFINITY;
     uint32_t besti = 0xFFFFFFFFu;
-    for (int64_t i = (int64_t)blockIdx.x * 256 + tid; i < d.n; i += (int64_t)gridDim.x * 256)
-        better(d.x[i], (uint32_t)i, best, besti);
+    const int64_t stride = (int64_t)gridDim.x * 256;
+    for (int64_t i0 = (int64_t)blockIdx.x * 256 + tid; i0 < d.n; i0 += stride * kArgmaxLoads) {
+        float v[kArgmaxLoads];
+#pragma unroll
+        for (int b = 0; b < kArgmaxLoads; ++b) {
+            const int64_t i = i0 + b * stride;
+            v[b] = i < d.n ? d.x[i] : __builtin_nanf("");
+        }
+#pragma unroll
+        for (int b = 0; b < kArgmaxLoads; ++b) better(v[b], (uint32_t)(i0 + b * stride), best, besti);
+    }
     wave_best(best, besti);
     if (lane == 0) { bv[wv] = best; bi[wv] = besti; }
     __syncthreads();
@@ -253,26 +586,13 @@ __global__ __launch_bounds__(256) void k_argmax(ArgmaxDesc d) {
         wave_best(best, besti);
         if (tid == 0) {
             d.out[0] = besti;
+            if (d.pos_dev) d.pos_dev[0] += 1;   // the token loop's next position
             __hip_atomic_store(d.cnt, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         }
     }
 }
 
 // ---------------------------------------------------------------- token loop
-// x = row `token` of the embedding table (zeros for a token past the table:
-// a row of only NaN logits has no argmax).
-__global__ __launch_bounds__(256) void k_embed(const float *table, const uint32_t *token,
-                                               uint32_t vocab, float *x, int dim) {
-    const int i = blockIdx.x * 256 + threadIdx.x;
-    if (i >= dim) return;
-    const uint32_t t = *token;
-    x[i] = t < vocab ? table[(int64_t)t * dim + i] : 0.f;
-}
-
-__global__ void k_advance(int *pos_dev) {
-    if (threadIdx.x == 0) pos_dev[0] += 1;
-}
-
 __global__ void k_set_state(int *pos_dev, uint32_t *token_dev, int pos, uint32_t token) {
     if (threadIdx.x == 0) {
         pos_dev[0] = pos;
@@ -282,11 +602,31 @@ __global__ void k_set_state(int *pos_dev, uint32_t *token_dev, int pos, uint32_t
 
 unsigned blocks_for(int64_t n) { return (unsigned)((n + 255) / 256); }
 
+bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
+
 }  // namespace
 
 hipError_t launch_rms_norm(const float *x, const float *w, float *out, int dim, int rows, float eps,
                            hipStream_t s) {
-    hipLaunchKernelGGL(k_rms_norm, dim3((unsigned)rows), dim3(kWave), 0, s, x, w, out, dim, eps);
+    const dim3 grid((unsigned)((rows + kWaves - 1) / kWaves));
+    if (dim % 4 == 0 && aligned16(x) && aligned16(w) && aligned16(out))
+        hipLaunchKernelGGL(k_rms_norm<true>, grid, dim3(kThreads), 0, s, x, w, out, dim, rows, eps);
+    else
+        hipLaunchKernelGGL(k_rms_norm<false>, grid, dim3(kThreads), 0, s, x, w, out, dim, rows, eps);
+    return hipGetLastError();
+}
+
+hipError_t launch_add_rms(float *x, const float *y, const float *w, float *xn, int dim, float eps,
+                          hipStream_t s) {
+    hipLaunchKernelGGL(k_add_rms<false>, dim3(1), dim3(kWave), 0, s, x, y, nullptr, 0u, w, xn, dim,
+                       eps);
+    return hipGetLastError();
+}
+
+hipError_t launch_embed_rms(const float *table, const uint32_t *token, uint32_t vocab, float *x,
+                            const float *w, float *xn, int dim, float eps, hipStream_t s) {
+    hipLaunchKernelGGL(k_add_rms<true>, dim3(1), dim3(kWave), 0, s, x, table, token, vocab, w, xn,
+                       dim, eps);
     return hipGetLastError();
 }
 
@@ -304,9 +644,27 @@ hipError_t launch_append_kv(const float *k, const float *v, float *kc, float *vc
     return hipGetLastError();
 }
 
+hipError_t launch_qk_post(const QkPostDesc &d, int head_dim, hipStream_t s) {
+    const dim3 grid((unsigned)(d.n_heads + 2 * d.n_kv));
+    switch (head_dim) {
+        case 64: hipLaunchKernelGGL(k_qk_post<64>, grid, dim3(kWave), 0, s, d); break;
+        case 128: hipLaunchKernelGGL(k_qk_post<128>, grid, dim3(kWave), 0, s, d); break;
+        case 192: hipLaunchKernelGGL(k_qk_post<192>, grid, dim3(kWave), 0, s, d); break;
+        case 256: hipLaunchKernelGGL(k_qk_post<256>, grid, dim3(kWave), 0, s, d); break;
+        default: return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+}
+
 hipError_t launch_attention(const AttnDesc &d, hipStream_t s) {
-    hipLaunchKernelGGL(k_attention, dim3((unsigned)(d.n_heads * d.max_chunks)), dim3(kAttnThreads),
-                       0, s, d);
+    const dim3 grid((unsigned)(d.n_heads * d.max_chunks));
+    switch (d.head_dim) {
+        case 64: hipLaunchKernelGGL(k_attention<64>, grid, dim3(kAttnThreads), 0, s, d); break;
+        case 128: hipLaunchKernelGGL(k_attention<128>, grid, dim3(kAttnThreads), 0, s, d); break;
+        case 192: hipLaunchKernelGGL(k_attention<192>, grid, dim3(kAttnThreads), 0, s, d); break;
+        case 256: hipLaunchKernelGGL(k_attention<256>, grid, dim3(kAttnThreads), 0, s, d); break;
+        default: return hipErrorInvalidValue;
+    }
     return hipGetLastError();
 }
 
@@ -322,17 +680,6 @@ hipError_t launch_silu(const float *g, const float *u, float *out, int n, hipStr
 
 hipError_t launch_argmax(const ArgmaxDesc &d, int wgs, hipStream_t s) {
     hipLaunchKernelGGL(k_argmax, dim3((unsigned)wgs), dim3(256), 0, s, d);
-    return hipGetLastError();
-}
-
-hipError_t launch_embed(const float *table, const uint32_t *token, uint32_t vocab, float *x, int dim,
-                        hipStream_t s) {
-    hipLaunchKernelGGL(k_embed, dim3(blocks_for(dim)), dim3(256), 0, s, table, token, vocab, x, dim);
-    return hipGetLastError();
-}
-
-hipError_t launch_advance(int *pos_dev, hipStream_t s) {
-    hipLaunchKernelGGL(k_advance, dim3(1), dim3(kWave), 0, s, pos_dev);
     return hipGetLastError();
 }
 

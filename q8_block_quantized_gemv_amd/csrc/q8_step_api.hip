@@ -21,6 +21,7 @@ constexpr int kArgmaxPerWg = 4096;   // values per argmax workgroup before more 
 constexpr int kArgmaxMaxWgs = 256;
 
 bool aligned4(const void *p) { return ((uintptr_t)p & 3u) == 0; }
+bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
 
 int argmax_wgs(int64_t n) {
     return (int)std::max<int64_t>(1, std::min<int64_t>(kArgmaxMaxWgs, (n + kArgmaxPerWg - 1) / kArgmaxPerWg));
@@ -35,8 +36,9 @@ int check_attention(const float *q, const float *kc, const float *vc, const floa
                     const char *what) {
     const std::string tag(what);
     if (!q || !kc || !vc || !out) return fail(Q8_ERR_INVALID_ARG, tag + ": null pointer");
-    if (!aligned4(q) || !aligned4(kc) || !aligned4(vc) || !aligned4(out))
-        return fail(Q8_ERR_ALIGN, tag + ": buffers must be 4-byte aligned");
+    if (!aligned16(q) || !aligned16(kc) || !aligned16(vc) || !aligned4(out) || kv_width % 4)
+        return fail(Q8_ERR_ALIGN, tag + ": q, kc, vc must be 16-byte aligned, kv_width a multiple of 4, "
+                                        "out 4-byte aligned");
     if (!head_dim_ok(head_dim))
         return fail(Q8_ERR_SHAPE, tag + ": head_dim must be 64, 128, 192 or 256");
     if (n_heads < 1 || n_heads > 4096 || kv_group < 1 || n_heads % kv_group)
@@ -156,7 +158,7 @@ int q8_0_argmax(const float *x, int64_t n, uint32_t *out, void *stream) {
     hipStream_t s = (hipStream_t)stream;
     const int wgs = argmax_wgs(n);
     ArgmaxDesc d;
-    d.x = x; d.n = n; d.out = out;
+    d.x = x; d.n = n; d.out = out; d.pos_dev = nullptr;
     float *ws = nullptr;
     if ((rc = workspace_for(dev, s, (size_t)wgs * 8, 1, &ws, &d.cnt))) return rc;
     d.ws_val = ws;
@@ -203,47 +205,47 @@ void step_free(q8_0_step *s) {
 // Every launch of one token, in order, on stream st.
 int issue_step(const q8_0_step *s, hipStream_t st) {
     const q8_0_model &m = s->m;
-    const int hid = (int)m.hidden, hd = (int)m.head_dim, nh = (int)m.n_heads, nkv = (int)m.n_kv_heads;
+    const int hid = (int)m.hidden, nh = (int)m.n_heads;
     const int64_t cache_stride = m.max_seq * s->kv_width;
-    hipError_t e = launch_embed(m.embed, s->token, (uint32_t)m.vocab, s->x, hid, st);
-    int rc = Q8_OK;
+    hipError_t e = hipSuccess;
     auto ok = [&](hipError_t err) {
         if (err != hipSuccess && e == hipSuccess) e = err;
-        return e == hipSuccess;
     };
-    for (int64_t l = 0; l < m.n_layers && ok(hipSuccess) && !rc; ++l) {
+    int rc = Q8_OK;
+    ok(launch_embed_rms(m.embed, s->token, (uint32_t)m.vocab, s->x, s->layers[0].attn_norm, s->xn, hid,
+                        m.eps, st));
+    for (int64_t l = 0; l < m.n_layers && e == hipSuccess; ++l) {
         const q8_0_layer_w &L = s->layers[l];
         float *kc = s->kcache + l * cache_stride, *vc = s->vcache + l * cache_stride;
         q8_0_chain *const *ch = &s->chains[4 * l];
-        ok(launch_rms_norm(s->x, L.attn_norm, s->xn, hid, 1, m.eps, st));
-        if ((rc = chain_issue(ch[0], st))) break;
-        ok(launch_rms_norm(s->q, L.q_norm, s->q, hd, nh, m.eps, st));
-        ok(launch_rms_norm(s->k, L.k_norm, s->k, hd, nkv, m.eps, st));
-        ok(launch_rope(s->q, hd, nh, s->pos, 0, m.theta, st));
-        ok(launch_rope(s->k, hd, nkv, s->pos, 0, m.theta, st));
-        ok(launch_append_kv(s->k, s->v, kc, vc, (int)s->kv_width, s->pos, 0, (int)m.max_seq, st));
+        if ((rc = chain_issue(ch[0], st))) return rc;
+        QkPostDesc p;
+        p.q = s->q; p.k = s->k; p.v = s->v; p.q_norm = L.q_norm; p.k_norm = L.k_norm;
+        p.kc = kc; p.vc = vc; p.pos_dev = s->pos; p.n_heads = nh; p.n_kv = (int)m.n_kv_heads;
+        p.kv_width = (int)s->kv_width; p.rows = (int)m.max_seq; p.eps = m.eps; p.theta = m.theta;
+        ok(launch_qk_post(p, (int)m.head_dim, st));
         AttnDesc d;
         std::memset(&d, 0, sizeof d);
         d.q = s->q; d.kc = kc; d.vc = vc; d.out = s->attn; d.pos_dev = s->pos;
         d.ws = s->attn_ws; d.cnt = s->cnt; d.seq = (int)m.max_seq; d.kv_width = (int)s->kv_width;
-        d.head_dim = hd; d.n_heads = nh; d.kv_group = (int)s->kv_group; d.max_chunks = s->max_chunks;
+        d.head_dim = (int)m.head_dim; d.n_heads = nh; d.kv_group = (int)s->kv_group;
+        d.max_chunks = s->max_chunks;
         ok(launch_attention(d, st));
-        if ((rc = chain_issue(ch[1], st))) break;
-        ok(launch_add(s->x, s->resid, hid, st));
-        ok(launch_rms_norm(s->x, L.ffn_norm, s->xn, hid, 1, m.eps, st));
-        if ((rc = chain_issue(ch[2], st))) break;
+        if ((rc = chain_issue(ch[1], st))) return rc;
+        ok(launch_add_rms(s->x, s->resid, L.ffn_norm, s->xn, hid, m.eps, st));
+        if ((rc = chain_issue(ch[2], st))) return rc;
         ok(launch_silu(s->gate, s->up, s->h, (int)m.inter, st));
-        if ((rc = chain_issue(ch[3], st))) break;
-        ok(launch_add(s->x, s->resid, hid, st));
+        if ((rc = chain_issue(ch[3], st))) return rc;
+        const float *next = l + 1 < m.n_layers ? s->layers[l + 1].attn_norm : m.out_norm;
+        ok(launch_add_rms(s->x, s->resid, next, s->xn, hid, m.eps, st));
     }
-    if (rc) return rc;
-    ok(launch_rms_norm(s->x, m.out_norm, s->xn, hid, 1, m.eps, st));
+    if (e != hipSuccess) return fail_hip(e, "decode step launch");
     if ((rc = chain_issue(s->chains.back(), st))) return rc;
     ArgmaxDesc a;
     a.x = s->logits; a.n = m.vocab; a.out = s->token; a.ws_val = s->amax_ws;
     a.ws_idx = (uint32_t *)(s->amax_ws + s->amax_wgs); a.cnt = s->cnt + m.n_heads;
+    a.pos_dev = s->pos;
     ok(launch_argmax(a, s->amax_wgs, st));
-    ok(launch_advance(s->pos, st));
     return e == hipSuccess ? Q8_OK : fail_hip(e, "decode step launch");
 }
 
@@ -263,11 +265,17 @@ int check_model(const q8_0_model *m) {
         return fail(Q8_ERR_SHAPE, "q8_0_step_create: vocab or max_seq out of range");
     if (!(m->eps >= 0.f) || !std::isfinite(m->eps) || !(m->theta > 0.f) || !std::isfinite(m->theta))
         return fail(Q8_ERR_INVALID_ARG, "q8_0_step_create: eps or theta");
+    if (!aligned16(m->embed) || !aligned16(m->out_norm))
+        return fail(Q8_ERR_ALIGN, "q8_0_step_create: embed and out_norm must be 16-byte aligned");
     for (int64_t l = 0; l < m->n_layers; ++l) {
         const q8_0_layer_w &L = m->layers[l];
         if (!L.wq || !L.wk || !L.wv || !L.wo || !L.wgate || !L.wup || !L.wdown || !L.attn_norm ||
             !L.ffn_norm || !L.q_norm || !L.k_norm)
             return fail(Q8_ERR_INVALID_ARG, "q8_0_step_create: null weight in layer " + std::to_string(l));
+        if (!aligned16(L.attn_norm) || !aligned16(L.ffn_norm) || !aligned4(L.q_norm) ||
+            !aligned4(L.k_norm))
+            return fail(Q8_ERR_ALIGN, "q8_0_step_create: norm weights of layer " + std::to_string(l) +
+                                          " misaligned (attn/ffn 16 bytes, q/k 4 bytes)");
     }
     return Q8_OK;
 }
@@ -341,7 +349,7 @@ int q8_0_step_create(const q8_0_model *m, q8_0_step **out) {
     if (rc) { std::string why = "q8_0_step_create: " + std::string(q8_0_last_error()); step_free(s); return fail(rc, why); }
     s->launches = 0;
     for (q8_0_chain *c : s->chains) s->launches += q8_0_chain_launches(c);
-    s->launches += (int)(m->n_layers * 11 + 4);   // the step kernels around the matvecs
+    s->launches += (int)(m->n_layers * 5 + 2);   // the step kernels around the matvecs
     // record one token
     if ((e = hipStreamCreateWithFlags(&s->capture, hipStreamNonBlocking)) != hipSuccess) {
         step_free(s);

@@ -140,6 +140,8 @@ F = 0x40000000   # another fake, 256-B aligned address
     (lambda L: L.q8_0_attention_decode(X, W, F, Y, 0, 128, 64, 2, 1, None), -2),
     (lambda L: L.q8_0_attention_decode(X, W, F, Y, 65537, 128, 64, 2, 1, None), -2),
     (lambda L: L.q8_0_attention_decode(X, W, F, X + 4, 8, 128, 64, 2, 1, None), -4),
+    (lambda L: L.q8_0_attention_decode(X + 4, W, F, Y, 8, 128, 64, 2, 1, None), -3),  # q not 16-B
+    (lambda L: L.q8_0_attention_decode(X, W, F, Y, 8, 130, 64, 2, 1, None), -3),      # kv_width % 4
     (lambda L: L.q8_0_add_inplace(X, 0, 8, None), -1),
     (lambda L: L.q8_0_add_inplace(X, X + 4, 8, None), -4),
     (lambda L: L.q8_0_add_inplace(X, Y, 0, None), -2),
