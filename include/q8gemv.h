@@ -105,9 +105,13 @@ typedef struct q8_0_op {
 
 typedef struct q8_0_chain q8_0_chain; /* opaque */
 
-/* chain_create flags */
-#define Q8_CHAIN_FUSE 0u   /* merge runs of mutually independent ops into one launch */
-#define Q8_CHAIN_PER_OP 1u /* one kernel launch per op, in array order */
+/* chain_create flags (PER_OP and SPLIT_K may be combined) */
+#define Q8_CHAIN_FUSE 0u    /* merge runs of mutually independent ops into one launch */
+#define Q8_CHAIN_PER_OP 1u  /* one kernel launch per op, in array order */
+#define Q8_CHAIN_SPLIT_K 2u /* for ops that wait on each other (a real decode step): plan
+                               every op for latency -- its K split over more waves, across
+                               workgroups when it has few rows; results stay bitwise
+                               reproducible but round differently from q8_0_gemv */
 
 /* decode_chain modes */
 #define Q8_MODE_GRAPH 0     /* replay the recorded hipGraph: one host call per token */
@@ -122,8 +126,10 @@ typedef struct q8_0_chain q8_0_chain; /* opaque */
  * with Q8_CHAIN_FUSE, maximal runs of ops with no such overlap share one
  * launch.  The pointers in `ops` are baked into the recording: they must stay
  * valid, at the same addresses, until q8_0_chain_destroy.  The handle owns a
- * small device table (op descriptors and the tile schedule), a private
- * capture stream and the graph; a token's replay allocates nothing.
+ * small device table (op descriptors, the tile schedule and, with
+ * Q8_CHAIN_SPLIT_K, the partial sums of split ops), a private capture stream
+ * and the graph; a token's replay allocates nothing.  Replays of one chain
+ * must not overlap in time (they share that table and their outputs).
  * On failure *out is set to NULL and nothing is leaked.
  */
 int q8_0_chain_create(const q8_0_op *ops, int64_t n_ops, uint32_t flags,

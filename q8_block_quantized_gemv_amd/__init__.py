@@ -8,7 +8,7 @@ implementation: if the library is missing, importing this package raises.
 The names follow the C ABI:
     gemv(x, w, y=None, stream=None)            -> q8_0_gemv
     gemm_smallm(X, w, Y=None, stream=None)     -> q8_0_gemm_smallm
-    Chain(ops, fuse=True) .run(mode, stream)   -> q8_0_chain_create / q8_0_decode_chain
+    Chain(ops, fuse=True, split_k=False) .run  -> q8_0_chain_create / q8_0_decode_chain
     stream_wait(stream, timeout_ms)            -> q8_0_stream_wait
     rms_norm, rope, append_kv, attention_decode, add_inplace,
     silu_hadamard, argmax                      -> the q8_0_* calls of include/q8step.h
@@ -35,6 +35,7 @@ Q8_ERR_UNSUPPORTED = -8
 
 Q8_CHAIN_FUSE = 0
 Q8_CHAIN_PER_OP = 1
+Q8_CHAIN_SPLIT_K = 2
 MODE_GRAPH = 0
 MODE_EAGER = 1
 MODE_SYNC_EACH = 2
@@ -231,7 +232,7 @@ class Chain:
     keeps references to them.
     """
 
-    def __init__(self, ops: Sequence, fuse: bool = True):
+    def __init__(self, ops: Sequence, fuse: bool = True, split_k: bool = False):
         torch = _torch()
         arr = (Q8Op * len(ops))()
         self._keep = []
@@ -245,8 +246,8 @@ class Chain:
             arr[i] = Q8Op(x.data_ptr(), w.data_ptr(), y.data_ptr(), n, p)
             self._keep.append((x, w, y))
         h = ctypes.c_void_p()
-        check(lib.q8_0_chain_create(arr, len(ops), Q8_CHAIN_FUSE if fuse else Q8_CHAIN_PER_OP,
-                                    ctypes.byref(h)))
+        flags = (Q8_CHAIN_FUSE if fuse else Q8_CHAIN_PER_OP) | (Q8_CHAIN_SPLIT_K if split_k else 0)
+        check(lib.q8_0_chain_create(arr, len(ops), flags, ctypes.byref(h)))
         self._h = h
         self.n_ops = len(ops)
 

@@ -192,8 +192,27 @@ int choose_ks(int64_t gsr, int64_t nsr, bool standalone, int nw) {
     return best;
 }
 
+// K slices across workgroups for an op whose row tiles alone give fewer than
+// kSplitTargetWaves waves: as many slices as that takes, at least one group
+// per wave (a slice holds a multiple of kSlots groups), at most kMaxSlices.
+constexpr int64_t kSplitTargetWaves = 1024;
+
+void plan_slices(OpDesc &d, int nw) {
+    const int64_t waves = fast_tiles_for(d.nsr, d.ks, nw) * nw;
+    if (waves == 0 || d.gsr <= kSlots) return;
+    const int64_t want = (kSplitTargetWaves + waves - 1) / waves;
+    int64_t S = std::min<int64_t>(want, std::min<int64_t>(kMaxSlices, (d.gsr + kSlots - 1) / kSlots));
+    if (S <= 1) return;
+    int64_t per = (d.gsr + S - 1) / S;
+    per = (per + kSlots - 1) / kSlots * kSlots;
+    S = (d.gsr + per - 1) / per;
+    if (S <= 1) return;
+    d.slices = (int32_t)S;
+    d.slice_groups = (int32_t)per;
+}
+
 OpDesc plan_op(const float *x, const void *w, float *y, int64_t m, int64_t n, int64_t p,
-               bool standalone, int nw = kWaves) {
+               bool standalone, int nw = kWaves, bool split_k = false) {
     OpDesc d;
     std::memset(&d, 0, sizeof d);
     const int64_t nb = n / kQuants;
@@ -208,7 +227,10 @@ OpDesc plan_op(const float *x, const void *w, float *y, int64_t m, int64_t n, in
     d.gsr = (int32_t)(rs * nb / kGroupBlocks);
     d.sr_bytes = rs * nb * kBlockBytes;
     d.ks = choose_ks(d.gsr, d.nsr, standalone, nw);
-    d.fast_tiles = (int32_t)fast_tiles_for(d.nsr, d.ks, nw);
+    d.slices = 1;
+    d.slice_groups = d.gsr;
+    if (split_k) plan_slices(d, nw);
+    d.fast_tiles = (int32_t)fast_tiles_for(d.nsr, d.ks, nw, d.slices);
     d.tail_row0 = (int32_t)(d.nsr * rs);
     d.m = (int32_t)m;
     d.x_stride = n;
@@ -455,7 +477,7 @@ int q8_0_chain_create(const q8_0_op *ops, int64_t n_ops, uint32_t flags, q8_0_ch
     *out = nullptr;
     if (!ops || n_ops <= 0 || n_ops > Q8_MAX_CHAIN_OPS)
         return fail(Q8_ERR_INVALID_ARG, "q8_0_chain_create: need 1..65535 ops");
-    if (flags != Q8_CHAIN_FUSE && flags != Q8_CHAIN_PER_OP)
+    if (flags & ~(uint32_t)(Q8_CHAIN_PER_OP | Q8_CHAIN_SPLIT_K))
         return fail(Q8_ERR_INVALID_ARG, "q8_0_chain_create: unknown flags");
     for (int64_t i = 0; i < n_ops; ++i) {
         const std::string what = "q8_0_chain_create op " + std::to_string(i);
@@ -472,8 +494,10 @@ int q8_0_chain_create(const q8_0_op *ops, int64_t n_ops, uint32_t flags, q8_0_ch
     c->ops.assign(ops, ops + n_ops);
 
     // ---- plan: runs of mutually independent ops (or single ops)
+    const bool per_op = (flags & Q8_CHAIN_PER_OP) != 0;
+    const bool split = (flags & Q8_CHAIN_SPLIT_K) != 0;
     std::vector<std::pair<int64_t, int64_t>> segs;  // [begin, end)
-    if (flags == Q8_CHAIN_PER_OP) {
+    if (per_op) {
         for (int64_t i = 0; i < n_ops; ++i) segs.push_back({i, i + 1});
     } else {
         int64_t b = 0;
@@ -484,15 +508,18 @@ int q8_0_chain_create(const q8_0_op *ops, int64_t n_ops, uint32_t flags, q8_0_ch
         }
     }
 
-    // ---- fused segments: op table + tile schedule in one device block
-    const Variant vf = pick_variant(true), vs = pick_variant(false);
+    // ---- fused segments: op table + tile schedule in one device block;
+    // with SPLIT_K every op is planned like a standalone launch (four-wave
+    // workgroups, groups split over the waves) and row-poor ops are split
+    // across workgroups too, their partial sums in the same device block
+    const Variant vs = pick_variant(false), vf = split ? vs : pick_variant(true);
     std::vector<OpDesc> h_ops;
     std::vector<Tile> h_tiles;
-    struct SegInfo { size_t op0, tile0; int64_t ntiles; bool fused; };
+    struct SegInfo { size_t op0, tile0; int64_t ntiles; bool fused; OpDesc single; };
     std::vector<SegInfo> info;
     for (auto &sg : segs) {
-        const bool fused = (flags == Q8_CHAIN_FUSE) && (sg.second - sg.first > 1);
-        SegInfo si{h_ops.size(), h_tiles.size(), 0, fused};
+        const bool fused = !per_op && (sg.second - sg.first > 1);
+        SegInfo si{h_ops.size(), h_tiles.size(), 0, fused, OpDesc{}};
         if (fused) {
             // tiles sorted by decreasing weight bytes so that the smallest
             // tiles finish the launch (ties keep encode order)
@@ -500,10 +527,11 @@ int q8_0_chain_create(const q8_0_op *ops, int64_t n_ops, uint32_t flags, q8_0_ch
             std::vector<Item> items;
             for (int64_t i = sg.first; i < sg.second; ++i) {
                 const q8_0_op &o = ops[i];
-                OpDesc d = plan_op(o.x, o.w, o.y, 1, o.n, o.p, false, vf.nw);
+                OpDesc d = plan_op(o.x, o.w, o.y, 1, o.n, o.p, split, vf.nw, split);
                 const uint32_t oi = (uint32_t)(h_ops.size() - si.op0);
                 h_ops.push_back(d);
-                const int64_t fb = (int64_t)(vf.nw / d.ks) * kWave * d.sr_bytes;
+                const int64_t fb = (int64_t)(vf.nw / d.ks) * kWave *
+                                   (d.slices > 1 ? (int64_t)d.slice_groups * kGroupBytes : d.sr_bytes);
                 for (int64_t t = 0; t < d.fast_tiles; ++t) items.push_back({{oi, (uint32_t)t}, fb});
                 const int64_t tt = tail_tiles_for((int64_t)d.p - d.tail_row0, vf.nw);
                 for (int64_t t = 0; t < tt; ++t)
@@ -513,18 +541,41 @@ int q8_0_chain_create(const q8_0_op *ops, int64_t n_ops, uint32_t flags, q8_0_ch
                              [](const Item &a, const Item &b) { return a.bytes > b.bytes; });
             for (auto &it : items) h_tiles.push_back(it.t);
             si.ntiles = (int64_t)items.size();
+        } else {
+            const q8_0_op &o = ops[sg.first];
+            si.single = plan_op(o.x, o.w, o.y, 1, o.n, o.p, true, vs.nw, split);
         }
         info.push_back(si);
     }
-    // device block: op descriptors, then tiles
+    // device block: op descriptors, tiles, then the K-split partials and counters
     const size_t ob = h_ops.size() * sizeof(OpDesc);
     const size_t tb = h_tiles.size() * sizeof(Tile);
-    if (ob + tb) {
-        std::vector<char> host(ob + tb, 0);
+    size_t wb = (ob + tb + 255) / 256 * 256;   // running end of the block
+    std::vector<std::pair<OpDesc *, size_t>> ws;  // (op, offset of its partials)
+    auto reserve = [&](OpDesc &d) {
+        if (d.slices <= 1) return;
+        ws.push_back({&d, wb});
+        const size_t part = (size_t)d.slices * d.nsr * d.rs * sizeof(float);
+        const size_t cnt = (size_t)((d.nsr + kWave - 1) / kWave) * sizeof(uint32_t);
+        wb += (part + 255) / 256 * 256 + (cnt + 255) / 256 * 256;
+    };
+    for (auto &d : h_ops) reserve(d);
+    for (auto &si : info)
+        if (!si.fused) reserve(si.single);
+    const size_t total = ws.empty() ? ob + tb : wb;
+    if (total) {
+        hipError_t e = hipMalloc(&c->d_table, total);
+        if (e != hipSuccess) { chain_free(c); return fail_hip(e, "q8_0_chain_create hipMalloc"); }
+        char *base = (char *)c->d_table;
+        for (auto &pw : ws) {
+            OpDesc &d = *pw.first;
+            const size_t part = (size_t)d.slices * d.nsr * d.rs * sizeof(float);
+            d.part = (float *)(base + pw.second);
+            d.cnt = (uint32_t *)(base + pw.second + (part + 255) / 256 * 256);
+        }
+        std::vector<char> host(total, 0);   // counters start at zero
         if (ob) std::memcpy(host.data(), h_ops.data(), ob);
         if (tb) std::memcpy(host.data() + ob, h_tiles.data(), tb);
-        hipError_t e = hipMalloc(&c->d_table, host.size());
-        if (e != hipSuccess) { chain_free(c); return fail_hip(e, "q8_0_chain_create hipMalloc"); }
         if ((e = hipMemcpy(c->d_table, host.data(), host.size(), hipMemcpyHostToDevice)) != hipSuccess) {
             chain_free(c);
             return fail_hip(e, "q8_0_chain_create hipMemcpy");
@@ -542,10 +593,9 @@ int q8_0_chain_create(const q8_0_op *ops, int64_t n_ops, uint32_t flags, q8_0_ch
             L.d_tiles = d_tiles + info[k].tile0;
             L.grid = info[k].ntiles;
         } else {
-            const q8_0_op &o = ops[segs[k].first];
             L.fused = false;
             L.v = vs;
-            L.single = plan_op(o.x, o.w, o.y, 1, o.n, o.p, true, vs.nw);
+            L.single = info[k].single;
             L.grid = tiles_of(L.single, vs.nw);
         }
         c->launches.push_back(L);

@@ -100,8 +100,6 @@ __device__ __forceinline__ void read_group(const uint8_t *st, int lane, uint32_t
     }
 }
 
-constexpr int kSlots = 4;
-
 // acc[slot][r] += v for a uniform slot and row index (unrolled selects).
 template <int RS>
 __device__ __forceinline__ void flush_row(float (&acc)[kSlots][RS], int slot, int r, float v) {

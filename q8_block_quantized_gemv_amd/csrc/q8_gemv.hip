@@ -121,6 +121,49 @@ __device__ __forceinline__ void group_dot(const uint32_t (&D)[68], const float4 
 // keeps in flight ahead of the one it computes (1 or 2; each stage holds one
 // group, and with PF = 2 the stage a group was computed from is refilled
 // right after that group's compute, so two groups stream while one waits).
+// With K slices (op.slices > 1) the ksl == 0 wave of each row tile parks
+// its rows' partial sums and counts in; the last slice to arrive adds the
+// slices in order.  The partials travel through device-scope stores and
+// loads (they come from other workgroups, possibly on other XCDs).
+template <int RS>
+__device__ __forceinline__ void slice_arrive(const OpDesc &op, int64_t row_tile, int slice, int64_t sr0,
+                                          const float (&acc)[kSlots][RS], int lane) {
+    const int64_t P = (int64_t)op.nsr * RS;
+    const bool live = sr0 + lane < op.nsr;
+    const int64_t r0 = (sr0 + lane) * RS;
+    if (live)
+#pragma unroll
+        for (int k = 0; k < RS; ++k)
+            __hip_atomic_store(op.part + slice * P + r0 + k,
+                               combine_slots(acc[0][k], acc[1][k], acc[2][k], acc[3][k]),
+                               __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __builtin_amdgcn_s_waitcnt(0);
+    uint32_t prev = 0;
+    if (lane == 0)
+        prev = __hip_atomic_fetch_add(op.cnt + row_tile, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    prev = __builtin_amdgcn_readfirstlane(prev);
+    if (prev != (uint32_t)op.slices - 1) return;
+    asm volatile("" ::: "memory");
+    if (live) {
+#pragma unroll
+        for (int k = 0; k < RS; ++k) {
+            float v[kMaxSlices];
+#pragma unroll
+            for (int q = 0; q < kMaxSlices; ++q)
+                v[q] = q < op.slices ? __hip_atomic_load(op.part + q * P + r0 + k, __ATOMIC_RELAXED,
+                                                         __HIP_MEMORY_SCOPE_AGENT)
+                                     : 0.f;
+            float sum = v[0];
+#pragma unroll
+            for (int q = 1; q < kMaxSlices; ++q)
+                if (q < op.slices) sum += v[q];
+            op.y[r0 + k] = sum;
+        }
+    }
+    if (lane == 0)   // ready for the next launch
+        __hip_atomic_store(op.cnt + row_tile, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
 template <int RS, int NW, int PF>
 __device__ void fast_tile(const OpDesc &op, uint32_t tile, uint8_t *stage) {
     const int lane = lane_id();
@@ -129,7 +172,11 @@ __device__ void fast_tile(const OpDesc &op, uint32_t tile, uint8_t *stage) {
     const int rt = wave / ks;                 // row tile within the workgroup
     const int ksl = wave - rt * ks;           // this wave's share of the groups
     const int tiles_per_wg = NW / ks;
-    const int64_t sr0 = ((int64_t)tile * tiles_per_wg + rt) * kWave;
+    const int S = op.slices;
+    const uint32_t wtile = S > 1 ? tile / (uint32_t)S : tile;   // workgroup's row tiles
+    const int slice = (int)(tile - wtile * (uint32_t)S);
+    const int64_t row_tile = (int64_t)wtile * tiles_per_wg + rt;
+    const int64_t sr0 = row_tile * kWave;
     const int nsr = op.nsr;
     uint8_t *st0 = stage + (size_t)wave * (kBufs * kStageBytes);
 
@@ -146,9 +193,13 @@ __device__ void fast_tile(const OpDesc &op, uint32_t tile, uint8_t *stage) {
         const int last = (int)min((int64_t)nsr - 1 - sr0, (int64_t)kWave - 1);
         uint32_t off[kGroupChunks];
         chunk_offsets(off, lane, last, srb);
-        const int ng = (G - ksl + ks - 1) / ks;  // groups kk = ksl + ks*t, t < ng
+        // this slice's groups [g0, g1); g0 is a multiple of kSlots, so group
+        // kk = g0 + ksl + ks*t still falls in slot kk % 4 owned by wave ksl
+        const int g0 = S > 1 ? slice * op.slice_groups : 0;
+        const int g1 = S > 1 ? min(G, g0 + op.slice_groups) : G;
+        const int ng = g1 - g0 > ksl ? (g1 - g0 - ksl + ks - 1) / ks : 0;
         auto issue = [&](int t) {
-            const int kk = ksl + ks * t;
+            const int kk = g0 + ksl + ks * t;
             dma_group_x<RS>(wt + (int64_t)kk * kGroupBytes, off, st0 + (t & 1) * kStageBytes, op,
                             kk, lane);
         };
@@ -162,7 +213,7 @@ __device__ void fast_tile(const OpDesc &op, uint32_t tile, uint8_t *stage) {
             else wait_vm_asm<0>();
             read_group(cur, lane, D);
             if (PF == 1 && t + 1 < ng) issue(t + 1);
-            group_dot<RS>(D, reinterpret_cast<const float4 *>(cur + kStageW), op, ksl + ks * t, acc);
+            group_dot<RS>(D, reinterpret_cast<const float4 *>(cur + kStageW), op, g0 + ksl + ks * t, acc);
             if (PF == 2 && t + 2 < ng) issue(t + 2);   // into the stage just consumed
         }
     }
@@ -189,6 +240,10 @@ __device__ void fast_tile(const OpDesc &op, uint32_t tile, uint8_t *stage) {
                     for (int k = 0; k < RS; ++k) acc[q][k] = theirs[((q / ks) * RS + k) * kWave + lane];
             }
         }
+    }
+    if (S > 1) {
+        if (ksl == 0 && sr0 < nsr) slice_arrive<RS>(op, row_tile, slice, sr0, acc, lane);
+        return;
     }
     if (ksl == 0 && sr0 + lane < nsr) {
         float *yr = op.y + (sr0 + lane) * RS;

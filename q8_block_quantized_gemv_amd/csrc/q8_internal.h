@@ -51,8 +51,21 @@ struct OpDesc {
     int32_t fast_tiles;  // workgroup tiles of the fast path
     int32_t tail_row0;   // first tail row = nsr * rs
     int32_t m;           // activation rows (1 for a matvec)
+    // K split across workgroups (matvec only): `slices` workgroups share a
+    // row tile, slice s taking groups [s * slice_groups, (s+1) * slice_groups).
+    // Each parks its per-row partial sums in part[s][row]; the last of them
+    // to arrive (counted in cnt[row tile]) adds the slices in order into y
+    // and clears the counter.  slices == 1: no split, part and cnt unused.
+    int32_t slices;
+    int32_t slice_groups;  // a multiple of kSlots
     int32_t pad_;
+    float *part;         // slices * nsr * rs floats
+    uint32_t *cnt;       // one per row tile of 64 super-rows, zero between launches
 };
+constexpr int kMaxSlices = 16;
+// Every row sums its groups into kSlots partial sums (group kk into slot
+// kk % kSlots) and combines them in a fixed tree at the end.
+constexpr int kSlots = 4;
 
 // One workgroup's work in a fused launch.
 struct Tile {
@@ -68,10 +81,10 @@ struct Variant {
     int pf;
 };
 
-// Fast tiles cover (nw / ks) * 64 super-rows each.
-inline int64_t fast_tiles_for(int64_t nsr, int ks, int nw = kWaves) {
+// Fast tiles cover (nw / ks) * 64 super-rows each (times the K slices).
+inline int64_t fast_tiles_for(int64_t nsr, int ks, int nw = kWaves, int slices = 1) {
     const int64_t per = (int64_t)(nw / ks) * kWave;
-    return (nsr + per - 1) / per;
+    return (nsr + per - 1) / per * slices;
 }
 // Tail tiles take one row per wave.
 inline int64_t tail_tiles_for(int64_t tail_rows, int nw = kWaves) {

@@ -332,7 +332,7 @@ int q8_0_step_create(const q8_0_model *m, q8_0_step **out) {
     // the matvecs: fused where independent
     auto mk = [&](std::vector<q8_0_op> ops) {
         q8_0_chain *c = nullptr;
-        int r = q8_0_chain_create(ops.data(), (int64_t)ops.size(), Q8_CHAIN_FUSE, &c);
+        int r = q8_0_chain_create(ops.data(), (int64_t)ops.size(), Q8_CHAIN_FUSE | Q8_CHAIN_SPLIT_K, &c);
         if (!r) s->chains.push_back(c);
         return r;
     };

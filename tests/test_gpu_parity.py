@@ -260,6 +260,51 @@ def test_chain_modes_equal_standalone(q8, fuse):
     chain.close()
 
 
+# (n, p) for K split across workgroups: row-poor shapes with many groups per
+# row (split into 2..5 slices), super-rows of 2 and 4 rows, a tail row, a
+# shape too short to split, and a 7B down projection
+SPLIT_SHAPES = [(2048, 1024), (3072, 1024), (896, 130), (896, 131), (4864, 131), (1088, 5),
+                (3584, 512), (96, 67), (18944, 3584)]
+
+
+@pytest.mark.parametrize("per_op", [False, True], ids=["fused", "per_op"])
+def test_split_k_chain(q8, per_op):
+    """Q8_CHAIN_SPLIT_K on independent ops and on a dependent pair: every
+    output within the bar against the oracle on the inputs the op actually
+    read, the same bits on every replay and in every mode (the split's
+    arrival counters reset themselves)."""
+    import torch
+    log("split-K chain per_op=%s" % per_op)
+    rng = np.random.default_rng(77)
+    ws = [synth.q8_weights(n, p, rng) for n, p in SPLIT_SHAPES]
+    xs = [synth.activations(n, rng) for n, p in SPLIT_SHAPES]
+    wd = [w_dev(w, n, p) for w, (n, p) in zip(ws, SPLIT_SHAPES)]
+    xd = [up(x) for x in xs]
+    ys = [torch.full((p,), float("nan"), dtype=torch.float32, device="cuda") for n, p in SPLIT_SHAPES]
+    # a dependent op: 3072 -> 1024 feeds 1024 -> 3072 (split too: 4 groups per row is not split)
+    w_dep = synth.q8_weights(1024, 3072, rng)
+    y_dep = torch.full((3072,), float("nan"), dtype=torch.float32, device="cuda")
+    ops = list(zip(xd, wd, ys)) + [(ys[1], w_dev(w_dep, 1024, 3072), y_dep)]
+    chain = q8.Chain(ops, fuse=not per_op, split_k=True)
+    first = None
+    for mode in (q8.MODE_GRAPH, q8.MODE_EAGER, q8.MODE_GRAPH, q8.MODE_SYNC_EACH):
+        for y in ys + [y_dep]:
+            y.fill_(float("nan"))
+        chain.run(mode)
+        q8.stream_wait(timeout_ms=60_000)
+        got = [down(y).copy() for y in ys + [y_dep]]
+        if first is None:
+            first = got
+        for a, b in zip(first, got):
+            assert np.array_equal(a.view(np.uint32), b.view(np.uint32)), mode
+    for i, (n, p) in enumerate(SPLIT_SHAPES):
+        _, y64, mag = oracle.gemv(ws[i], xs[i], n, p)
+        parity(first[i], y64, mag, "split-K op %d (%d x %d)" % (i, n, p))
+    _, y64, mag = oracle.gemv(w_dep, first[1], 1024, 3072)
+    parity(first[-1], y64, mag, "split-K dependent op")
+    chain.close()
+
+
 def test_stream_wait_timeout_and_ok(q8):
     """A bounded wait returns OK on an idle stream."""
     import torch
