@@ -512,14 +512,24 @@ int q8_0_chain_create(const q8_0_op *ops, int64_t n_ops, uint32_t flags, q8_0_ch
     // with SPLIT_K every op is planned like a standalone launch (four-wave
     // workgroups, groups split over the waves) and row-poor ops are split
     // across workgroups too, their partial sums in the same device block
-    const Variant vs = pick_variant(false), vf = split ? vs : pick_variant(true);
+    // (a SPLIT_K launch with rows enough for kSplitTargetWaves one-wave row
+    // tiles, such as an lm_head, keeps the one-wave fused variant unsplit:
+    // its waves stream several groups each and many workgroups share a CU)
+    const Variant v_single = pick_variant(false), v_fused = pick_variant(true);
     std::vector<OpDesc> h_ops;
     std::vector<Tile> h_tiles;
-    struct SegInfo { size_t op0, tile0; int64_t ntiles; bool fused; OpDesc single; };
+    struct SegInfo { size_t op0, tile0; int64_t ntiles; bool fused; OpDesc single; Variant v; };
     std::vector<SegInfo> info;
     for (auto &sg : segs) {
         const bool fused = !per_op && (sg.second - sg.first > 1);
-        SegInfo si{h_ops.size(), h_tiles.size(), 0, fused, OpDesc{}};
+        int64_t row_tiles = 0;
+        for (int64_t i = sg.first; i < sg.second; ++i)
+            row_tiles += (ops[i].p / (kGroupBlocks / gcd64(ops[i].n / kQuants, kGroupBlocks)) + kWave - 1) / kWave;
+        const bool seg_split = split && row_tiles < kSplitTargetWaves;
+        const bool big = split && !seg_split;
+        const Variant vf = seg_split ? v_single : v_fused;
+        const Variant vs = big ? v_fused : v_single;
+        SegInfo si{h_ops.size(), h_tiles.size(), 0, fused, OpDesc{}, fused ? vf : vs};
         if (fused) {
             // tiles sorted by decreasing weight bytes so that the smallest
             // tiles finish the launch (ties keep encode order)
@@ -527,7 +537,7 @@ int q8_0_chain_create(const q8_0_op *ops, int64_t n_ops, uint32_t flags, q8_0_ch
             std::vector<Item> items;
             for (int64_t i = sg.first; i < sg.second; ++i) {
                 const q8_0_op &o = ops[i];
-                OpDesc d = plan_op(o.x, o.w, o.y, 1, o.n, o.p, split, vf.nw, split);
+                OpDesc d = plan_op(o.x, o.w, o.y, 1, o.n, o.p, seg_split, vf.nw, seg_split);
                 const uint32_t oi = (uint32_t)(h_ops.size() - si.op0);
                 h_ops.push_back(d);
                 const int64_t fb = (int64_t)(vf.nw / d.ks) * kWave *
@@ -543,7 +553,7 @@ int q8_0_chain_create(const q8_0_op *ops, int64_t n_ops, uint32_t flags, q8_0_ch
             si.ntiles = (int64_t)items.size();
         } else {
             const q8_0_op &o = ops[sg.first];
-            si.single = plan_op(o.x, o.w, o.y, 1, o.n, o.p, true, vs.nw, split);
+            si.single = plan_op(o.x, o.w, o.y, 1, o.n, o.p, !big, vs.nw, seg_split);
         }
         info.push_back(si);
     }
@@ -588,15 +598,15 @@ int q8_0_chain_create(const q8_0_op *ops, int64_t n_ops, uint32_t flags, q8_0_ch
         std::memset(&L, 0, sizeof L);
         if (info[k].fused) {
             L.fused = true;
-            L.v = vf;
+            L.v = info[k].v;
             L.d_ops = d_ops + info[k].op0;
             L.d_tiles = d_tiles + info[k].tile0;
             L.grid = info[k].ntiles;
         } else {
             L.fused = false;
-            L.v = vs;
+            L.v = info[k].v;
             L.single = info[k].single;
-            L.grid = tiles_of(L.single, vs.nw);
+            L.grid = tiles_of(L.single, L.v.nw);
         }
         c->launches.push_back(L);
     }

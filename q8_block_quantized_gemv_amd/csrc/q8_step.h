@@ -21,6 +21,16 @@ struct AttnDesc {
     int seq, kv_width, head_dim, n_heads, kv_group, max_chunks;
 };
 
+// The step's per-head q/k work folded into attention (see k_attention):
+// raw q (n_heads heads), k and v (KV heads) of this token, the norm gains,
+// and the caches to store the token's row into (the same as AttnDesc's).
+struct AttnFuse {
+    const float *q, *k, *v;
+    const float *q_norm, *k_norm;
+    float *kc_w, *vc_w;
+    float eps, theta;
+};
+
 struct ArgmaxDesc {
     const float *x;
     int64_t n;
@@ -29,20 +39,6 @@ struct ArgmaxDesc {
     uint32_t *ws_idx;
     uint32_t *cnt;       // arrival counter, zero between launches
     int *pos_dev;        // if set, incremented once the index is written
-};
-
-// The per-head work between the q/k/v projections and attention in a
-// recorded token: q heads normed (q_norm) and rotated in place; k heads
-// normed (k_norm), rotated and stored at cache row *pos_dev; v heads stored
-// there.  Rows past `rows` (the caches' length) are not written.
-struct QkPostDesc {
-    float *q;
-    const float *k, *v;
-    const float *q_norm, *k_norm;
-    float *kc, *vc;
-    const int *pos_dev;
-    int n_heads, n_kv, kv_width, rows;
-    float eps, theta;
 };
 
 // pos_dev, when not null, overrides pos (a recorded step reads it per replay)
@@ -55,11 +51,12 @@ hipError_t launch_append_kv(const float *k, const float *v, float *kc, float *vc
                             const int *pos_dev, int pos, int rows, hipStream_t s);
 // head_dim 64, 128, 192 or 256; q, kc, vc 16-byte aligned, kv_width % 4 == 0
 hipError_t launch_attention(const AttnDesc &d, hipStream_t s);
+// The recorded token's attention: d.q is unused (the query comes raw from
+// f.q); needs d.pos_dev.  Also stores the token's K/V row into the caches.
+hipError_t launch_attention_fused(const AttnDesc &d, const AttnFuse &f, hipStream_t s);
 hipError_t launch_add(float *x, const float *y, int n, hipStream_t s);
 hipError_t launch_silu(const float *g, const float *u, float *out, int n, hipStream_t s);
 hipError_t launch_argmax(const ArgmaxDesc &d, int wgs, hipStream_t s);
-// head_dim 64, 128, 192 or 256; q, k, v, kc, vc 16-byte aligned, kv_width % 4 == 0
-hipError_t launch_qk_post(const QkPostDesc &d, int head_dim, hipStream_t s);
 // x += y, then xn = rms_norm(x) * w (one wave; dim % 4 == 0, 16-byte aligned)
 hipError_t launch_add_rms(float *x, const float *y, const float *w, float *xn, int dim, float eps,
                           hipStream_t s);

@@ -21,11 +21,13 @@
 // kernels separately; fewer, larger launches suit a hipGraph better):
 //  * embed_rms: x = embedding row of the token, xn = rms_norm(x);
 //  * add_rms: x += y, xn = rms_norm(x) (the residual add and the next norm);
-//  * qk_post: per-head q and k norms, rotary embedding of q and k, and the
-//    K/V cache append, one wave per head;
+//  * attention takes the per-head q and k norms, the rotary embedding of q
+//    and k and the K/V cache append into its own prologue;
 //  * argmax also advances the position.
 // Kernels a recorded token replays read the position from device memory
 // (pos_dev), so one recording serves every token.
+#include <cstring>
+
 #include "q8_step.h"
 
 namespace q8 {
@@ -272,80 +274,29 @@ __global__ __launch_bounds__(256) void k_append_kv(const float *k, const float *
     vc[row + i] = v[i];
 }
 
-// ---------------------------------------------------------------- fused q/k post-processing
-// Workgroup (one wave) b: b < n_heads: query head b -- rms_norm with q_norm,
-// then rope, in place in q.  b < n_heads + n_kv: key head -- rms_norm with
-// k_norm, rope, stored into cache row pos.  Else value head: copied into
-// cache row pos.  A lane holds elements lane + 64 e of the head; the rope
-// pairs meet through LDS.
-template <int HD>
-__global__ __launch_bounds__(kWave) void k_qk_post(QkPostDesc d) {
-    constexpr int PER = HD / kWave;   // 1..4
-    constexpr int HALF = HD / 2;
-    __shared__ float buf[HD];
-    const int lane = lane_id();
-    const int b = blockIdx.x;
-    const int pos = *d.pos_dev;
-    const bool in_cache = pos >= 0 && pos < d.rows;
-    if (b >= d.n_heads + d.n_kv) {   // value head
-        const int h = b - d.n_heads - d.n_kv;
-        if (!in_cache) return;
-        float *dst = d.vc + (int64_t)pos * d.kv_width + (int64_t)h * HD;
-        const float *src = d.v + (int64_t)h * HD;
-        float vv[PER];
-#pragma unroll
-        for (int e = 0; e < PER; ++e) vv[e] = src[lane + kWave * e];
-#pragma unroll
-        for (int e = 0; e < PER; ++e) dst[lane + kWave * e] = vv[e];
-        return;
-    }
-    const bool is_q = b < d.n_heads;
-    const int h = is_q ? b : b - d.n_heads;
-    const float *src = (is_q ? d.q : d.k) + (int64_t)h * HD;
-    const float *w = is_q ? d.q_norm : d.k_norm;
-    float xv[PER], wv[PER];
-#pragma unroll
-    for (int e = 0; e < PER; ++e) {
-        xv[e] = src[lane + kWave * e];
-        wv[e] = w[lane + kWave * e];
-    }
-    float ss = 0.f;
-#pragma unroll
-    for (int e = 0; e < PER; ++e) ss = fmaf(xv[e], xv[e], ss);
-    const float inv = rms_inv(wave_sum(ss), HD, d.eps);
-#pragma unroll
-    for (int e = 0; e < PER; ++e) buf[lane + kWave * e] = xv[e] * inv * wv[e];
-    __syncthreads();
-    if (!is_q && !in_cache) return;
-    float *dst = is_q ? d.q + (int64_t)h * HD : d.kc + (int64_t)pos * d.kv_width + (int64_t)h * HD;
-#pragma unroll
-    for (int e = 0; e < (HALF + kWave - 1) / kWave; ++e) {
-        const int i = lane + kWave * e;
-        if (i < HALF) {
-            float ra, rb;
-            rotate(buf[i], buf[i + HALF], i, HALF, pos, d.theta, ra, rb);
-            dst[i] = ra;
-            dst[i + HALF] = rb;
-        }
-    }
-}
-
 // ---------------------------------------------------------------- attention_decode
 // Workgroup (chunk c, head h) of 256 threads: the scores of cached rows
 // [c*kAttnChunk, min(seq, (c+1)*kAttnChunk)) on KV head h / kv_group, their
-// local softmax (max m, sum s of e^(score - m)) and acc[j] = sum e * v[j];
-// the last chunk of a head to arrive merges the parts in chunk order.
+// local softmax (max m, sum s of e^(score - m)) and acc[j] = sum e * v[j].
+// A head of one chunk writes acc / s; otherwise the last chunk of a head to
+// arrive merges the parts in chunk order.
 // Scores: a row is read by L lanes with float4 loads (L = HD/4 rounded up
 // to a power of two), 64/L rows per wave at a time, every row of a lane's
 // share loaded before any is reduced.  Values: thread (column float4,
 // row group) accumulates its rows, the row groups meet in LDS.
+// FUSED (a recorded token): the q head arrives raw and is normed (q_norm)
+// and rotated here; the chunk holding the token's own row (pos = seq - 1)
+// norms and rotates that row's key from the raw k and takes its value from
+// the raw v instead of reading them from the caches, and the first query
+// head of each KV group stores them into cache row pos for later tokens.
 constexpr int kAttnThreads = 256;
 constexpr int kAttnWaves = kAttnThreads / kWave;
 constexpr int kMergeBatch = 8;
 
-template <int HD>
-__global__ __launch_bounds__(kAttnThreads) void k_attention(AttnDesc d) {
+template <int HD, bool FUSED>
+__global__ __launch_bounds__(kAttnThreads) void k_attention(AttnDesc d, AttnFuse f) {
     constexpr int NV = HD / 4;                                   // float4 per row
+    constexpr int HALF = HD / 2;
     constexpr int L = NV <= 16 ? 16 : NV <= 32 ? 32 : 64;        // lanes per row
     constexpr int RPW = kWave / L;                               // rows per wave per pass
     constexpr int RPP = kAttnWaves * RPW;                        // rows per pass
@@ -355,9 +306,12 @@ __global__ __launch_bounds__(kAttnThreads) void k_attention(AttnDesc d) {
     constexpr int RPT = (kAttnChunk + RG - 1) / RG;              // rows per thread
     constexpr int VB = RPT < 16 ? RPT : 16;                      // value loads in flight
     __shared__ float sc[kAttnChunk];
-    __shared__ float red[kAttnWaves];
+    __shared__ float red[2 * kAttnWaves];
     __shared__ float4 accp[kAttnThreads];
     __shared__ uint32_t prev;
+    __shared__ __attribute__((aligned(16))) float qs[FUSED ? HD : 4];
+    __shared__ __attribute__((aligned(16))) float kn[FUSED ? HD : 4];
+    __shared__ __attribute__((aligned(16))) float vn[FUSED ? HD : 4];
     const int head = blockIdx.x % d.n_heads;
     const int c = blockIdx.x / d.n_heads;
     const int seq = d.pos_dev ? min(*d.pos_dev + 1, d.seq) : d.seq;
@@ -365,32 +319,94 @@ __global__ __launch_bounds__(kAttnThreads) void k_attention(AttnDesc d) {
     if (c >= n_chunks) return;   // the whole workgroup: no part, no arrival
     const int tid = threadIdx.x, lane = tid & (kWave - 1), wv = tid / kWave;
     const int t0 = c * kAttnChunk, rows = min(kAttnChunk, seq - t0);
-    const int64_t kv_off = (int64_t)(head / d.kv_group) * HD;
+    const int kvh = head / d.kv_group;
+    const int64_t kv_off = (int64_t)kvh * HD;
+    const int pos = seq - 1;
+    const bool cur = FUSED && pos >= t0 && pos < t0 + rows;   // this chunk holds the token's row
+    const int rcur = pos - t0;
     // ---- scores
     {
         const int g = lane / L, col = lane % L;
         const bool colv = col < NV;
-        float4 q4 = make_float4(0.f, 0.f, 0.f, 0.f);
-        if (colv) q4 = ((const float4 *)(d.q + (int64_t)head * HD))[col];
-        const float scale = 1.0f / sqrtf((float)HD);
         const float *kbase = d.kc + (int64_t)t0 * d.kv_width + kv_off + 4 * col;
-        for (int p0 = 0; p0 < PASSES; p0 += SB) {
-            float4 kv[SB];
+        float4 kv[SB];
+        auto load_keys = [&](int p0) {
 #pragma unroll
             for (int b = 0; b < SB; ++b) {
                 const int r = (p0 + b) * RPP + wv * RPW + g;
                 kv[b] = make_float4(0.f, 0.f, 0.f, 0.f);
-                if (colv && r < rows) kv[b] = *(const float4 *)(kbase + (int64_t)r * d.kv_width);
+                if (colv && r < rows && !(cur && r == rcur))
+                    kv[b] = *(const float4 *)(kbase + (int64_t)r * d.kv_width);
             }
+        };
+        load_keys(0);   // in flight while the query is prepared
+        float4 q4 = make_float4(0.f, 0.f, 0.f, 0.f);
+        if (FUSED) {
+            float qv = 0.f, kr = 0.f, vr = 0.f;
+            if (tid < HD) {
+                qv = f.q[(int64_t)head * HD + tid];
+                if (cur) {
+                    kr = f.k[kv_off + tid];
+                    vr = f.v[kv_off + tid];
+                }
+            }
+            const float sq = wave_sum(qv * qv), sk = wave_sum(kr * kr);
+            if (lane == 0) {
+                red[wv] = sq;
+                red[kAttnWaves + wv] = sk;
+            }
+            __syncthreads();
+            float SQ = red[0], SK = red[kAttnWaves];
+#pragma unroll
+            for (int w = 1; w < HD / kWave; ++w) {
+                SQ += red[w];
+                SK += red[kAttnWaves + w];
+            }
+            if (tid < HD) {
+                qs[tid] = qv * rms_inv(SQ, HD, f.eps) * f.q_norm[tid];
+                if (cur) {
+                    kn[tid] = kr * rms_inv(SK, HD, f.eps) * f.k_norm[tid];
+                    vn[tid] = vr;
+                }
+            }
+            __syncthreads();
+            const bool writer = cur && head % d.kv_group == 0;
+            const int64_t crow = (int64_t)pos * d.kv_width + kv_off;
+            if (tid < HALF) {
+                float ra, rb;
+                rotate(qs[tid], qs[tid + HALF], tid, HALF, pos, f.theta, ra, rb);
+                qs[tid] = ra;
+                qs[tid + HALF] = rb;
+            } else if (cur && tid >= 128 && tid < 128 + HALF) {
+                const int i = tid - 128;
+                float ra, rb;
+                rotate(kn[i], kn[i + HALF], i, HALF, pos, f.theta, ra, rb);
+                kn[i] = ra;
+                kn[i + HALF] = rb;
+                if (writer) {
+                    f.kc_w[crow + i] = ra;
+                    f.kc_w[crow + i + HALF] = rb;
+                }
+            }
+            if (writer && tid < HD) f.vc_w[crow + tid] = vn[tid];
+            __syncthreads();
+            if (colv) q4 = ((const float4 *)qs)[col];
+        } else if (colv) {
+            q4 = ((const float4 *)(d.q + (int64_t)head * HD))[col];
+        }
+        const float scale = 1.0f / sqrtf((float)HD);
+        for (int p0 = 0; p0 < PASSES; p0 += SB) {
+            if (p0 > 0) load_keys(p0);
 #pragma unroll
             for (int b = 0; b < SB; ++b) {
+                const int r = (p0 + b) * RPP + wv * RPW + g;
+                if (cur && r == rcur && colv) kv[b] = ((const float4 *)kn)[col];
                 float dot = q4.x * kv[b].x;
                 dot = fmaf(q4.y, kv[b].y, dot);
                 dot = fmaf(q4.z, kv[b].z, dot);
                 dot = fmaf(q4.w, kv[b].w, dot);
 #pragma unroll
                 for (int o = L / 2; o > 0; o >>= 1) dot += __shfl_xor(dot, o, kWave);
-                const int r = (p0 + b) * RPP + wv * RPW + g;
                 if (col == 0 && r < rows) sc[r] = dot * scale;
             }
         }
@@ -429,7 +445,8 @@ __global__ __launch_bounds__(kAttnThreads) void k_attention(AttnDesc d) {
                     vv[b] = make_float4(0.f, 0.f, 0.f, 0.f);
                     ee[b] = 0.f;
                     if (r < rows) {
-                        vv[b] = *(const float4 *)(vbase + (int64_t)r * d.kv_width);
+                        if (cur && r == rcur) vv[b] = ((const float4 *)vn)[col];
+                        else vv[b] = *(const float4 *)(vbase + (int64_t)r * d.kv_width);
                         ee[b] = sc[r];
                     }
                 }
@@ -445,14 +462,23 @@ __global__ __launch_bounds__(kAttnThreads) void k_attention(AttnDesc d) {
         accp[tid] = acc;
     }
     __syncthreads();
-    // ---- park (m, s, acc[0..HD)) of this chunk, device-scope, then count in
-    float *mine = d.ws + ((int64_t)head * d.max_chunks + c) * (HD + 2);
+    float4 t = make_float4(0.f, 0.f, 0.f, 0.f);
     if (tid < NV) {
-        float4 t = accp[tid];
+        t = accp[tid];
         for (int q = 1; q < RG; ++q) {
             const float4 u = accp[q * NV + tid];
             t = make_float4(t.x + u.x, t.y + u.y, t.z + u.z, t.w + u.w);
         }
+    }
+    if (n_chunks == 1) {   // the whole head in this chunk: no merge
+        if (tid < NV)
+            ((float4 *)(d.out + (int64_t)head * HD))[tid] =
+                make_float4(t.x / s, t.y / s, t.z / s, t.w / s);
+        return;
+    }
+    // ---- park (m, s, acc[0..HD)) of this chunk, device-scope, then count in
+    float *mine = d.ws + ((int64_t)head * d.max_chunks + c) * (HD + 2);
+    if (tid < NV) {
         __hip_atomic_store(mine + 2 + 4 * tid, t.x, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         __hip_atomic_store(mine + 3 + 4 * tid, t.y, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         __hip_atomic_store(mine + 4 + 4 * tid, t.z, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -475,11 +501,12 @@ __global__ __launch_bounds__(kAttnThreads) void k_attention(AttnDesc d) {
     for (int q0 = 0; q0 < n_chunks; q0 += kMergeBatch) {
         float mv[kMergeBatch];
 #pragma unroll
-        for (int b = 0; b < kMergeBatch; ++b)
-            mv[b] = q0 + b < n_chunks
-                        ? __hip_atomic_load(parts0 + (int64_t)(q0 + b) * (HD + 2), __ATOMIC_RELAXED,
-                                            __HIP_MEMORY_SCOPE_AGENT)
-                        : -INFINITY;
+        for (int b = 0; b < kMergeBatch; ++b) {
+            mv[b] = -INFINITY;
+            if (q0 + b < n_chunks)
+                mv[b] = __hip_atomic_load(parts0 + (int64_t)(q0 + b) * (HD + 2), __ATOMIC_RELAXED,
+                                          __HIP_MEMORY_SCOPE_AGENT);
+        }
 #pragma unroll
         for (int b = 0; b < kMergeBatch; ++b) M = fmaxf(M, mv[b]);
     }
@@ -498,9 +525,9 @@ __global__ __launch_bounds__(kAttnThreads) void k_attention(AttnDesc d) {
 #pragma unroll
             for (int b = 0; b < kMergeBatch; ++b) {
                 if (q0 + b < n_chunks) {
-                    const float f = expf(mv[b] - M);
-                    S = fmaf(sv[b], f, S);
-                    A = fmaf(av[b], f, A);
+                    const float fct = expf(mv[b] - M);
+                    S = fmaf(sv[b], fct, S);
+                    A = fmaf(av[b], fct, A);
                 }
             }
         }
@@ -644,28 +671,27 @@ hipError_t launch_append_kv(const float *k, const float *v, float *kc, float *vc
     return hipGetLastError();
 }
 
-hipError_t launch_qk_post(const QkPostDesc &d, int head_dim, hipStream_t s) {
-    const dim3 grid((unsigned)(d.n_heads + 2 * d.n_kv));
-    switch (head_dim) {
-        case 64: hipLaunchKernelGGL(k_qk_post<64>, grid, dim3(kWave), 0, s, d); break;
-        case 128: hipLaunchKernelGGL(k_qk_post<128>, grid, dim3(kWave), 0, s, d); break;
-        case 192: hipLaunchKernelGGL(k_qk_post<192>, grid, dim3(kWave), 0, s, d); break;
-        case 256: hipLaunchKernelGGL(k_qk_post<256>, grid, dim3(kWave), 0, s, d); break;
+template <bool FUSED>
+hipError_t launch_attention_t(const AttnDesc &d, const AttnFuse &f, hipStream_t s) {
+    const dim3 grid((unsigned)(d.n_heads * d.max_chunks));
+    switch (d.head_dim) {
+        case 64: hipLaunchKernelGGL((k_attention<64, FUSED>), grid, dim3(kAttnThreads), 0, s, d, f); break;
+        case 128: hipLaunchKernelGGL((k_attention<128, FUSED>), grid, dim3(kAttnThreads), 0, s, d, f); break;
+        case 192: hipLaunchKernelGGL((k_attention<192, FUSED>), grid, dim3(kAttnThreads), 0, s, d, f); break;
+        case 256: hipLaunchKernelGGL((k_attention<256, FUSED>), grid, dim3(kAttnThreads), 0, s, d, f); break;
         default: return hipErrorInvalidValue;
     }
     return hipGetLastError();
 }
 
 hipError_t launch_attention(const AttnDesc &d, hipStream_t s) {
-    const dim3 grid((unsigned)(d.n_heads * d.max_chunks));
-    switch (d.head_dim) {
-        case 64: hipLaunchKernelGGL(k_attention<64>, grid, dim3(kAttnThreads), 0, s, d); break;
-        case 128: hipLaunchKernelGGL(k_attention<128>, grid, dim3(kAttnThreads), 0, s, d); break;
-        case 192: hipLaunchKernelGGL(k_attention<192>, grid, dim3(kAttnThreads), 0, s, d); break;
-        case 256: hipLaunchKernelGGL(k_attention<256>, grid, dim3(kAttnThreads), 0, s, d); break;
-        default: return hipErrorInvalidValue;
-    }
-    return hipGetLastError();
+    AttnFuse f;
+    std::memset(&f, 0, sizeof f);
+    return launch_attention_t<false>(d, f, s);
+}
+
+hipError_t launch_attention_fused(const AttnDesc &d, const AttnFuse &f, hipStream_t s) {
+    return launch_attention_t<true>(d, f, s);
 }
 
 hipError_t launch_add(float *x, const float *y, int n, hipStream_t s) {

@@ -219,18 +219,16 @@ int issue_step(const q8_0_step *s, hipStream_t st) {
         float *kc = s->kcache + l * cache_stride, *vc = s->vcache + l * cache_stride;
         q8_0_chain *const *ch = &s->chains[4 * l];
         if ((rc = chain_issue(ch[0], st))) return rc;
-        QkPostDesc p;
-        p.q = s->q; p.k = s->k; p.v = s->v; p.q_norm = L.q_norm; p.k_norm = L.k_norm;
-        p.kc = kc; p.vc = vc; p.pos_dev = s->pos; p.n_heads = nh; p.n_kv = (int)m.n_kv_heads;
-        p.kv_width = (int)s->kv_width; p.rows = (int)m.max_seq; p.eps = m.eps; p.theta = m.theta;
-        ok(launch_qk_post(p, (int)m.head_dim, st));
         AttnDesc d;
         std::memset(&d, 0, sizeof d);
-        d.q = s->q; d.kc = kc; d.vc = vc; d.out = s->attn; d.pos_dev = s->pos;
+        d.q = nullptr; d.kc = kc; d.vc = vc; d.out = s->attn; d.pos_dev = s->pos;
         d.ws = s->attn_ws; d.cnt = s->cnt; d.seq = (int)m.max_seq; d.kv_width = (int)s->kv_width;
         d.head_dim = (int)m.head_dim; d.n_heads = nh; d.kv_group = (int)s->kv_group;
         d.max_chunks = s->max_chunks;
-        ok(launch_attention(d, st));
+        AttnFuse f;
+        f.q = s->q; f.k = s->k; f.v = s->v; f.q_norm = L.q_norm; f.k_norm = L.k_norm;
+        f.kc_w = kc; f.vc_w = vc; f.eps = m.eps; f.theta = m.theta;
+        ok(launch_attention_fused(d, f, st));
         if ((rc = chain_issue(ch[1], st))) return rc;
         ok(launch_add_rms(s->x, s->resid, L.ffn_norm, s->xn, hid, m.eps, st));
         if ((rc = chain_issue(ch[2], st))) return rc;
@@ -349,7 +347,7 @@ int q8_0_step_create(const q8_0_model *m, q8_0_step **out) {
     if (rc) { std::string why = "q8_0_step_create: " + std::string(q8_0_last_error()); step_free(s); return fail(rc, why); }
     s->launches = 0;
     for (q8_0_chain *c : s->chains) s->launches += q8_0_chain_launches(c);
-    s->launches += (int)(m->n_layers * 5 + 2);   // the step kernels around the matvecs
+    s->launches += (int)(m->n_layers * 4 + 2);   // the step kernels around the matvecs
     // record one token
     if ((e = hipStreamCreateWithFlags(&s->capture, hipStreamNonBlocking)) != hipSuccess) {
         step_free(s);

@@ -157,7 +157,7 @@ WORKLOADS: Dict[str, List[OpShape]] = {
 # workload number used in the seeds, in the order the workloads are listed
 WORKLOAD_ID = {"single_1024x3072": 0, "qwen3_0.6b_chain": 1,
                "qwen2.5_0.5b_chain": 2, "7b_chain": 3, "smallm_7b": 4,
-               "step_tiny": 5, "step_gqa4": 6}
+               "step_tiny": 5, "step_gqa4": 6, "step_hd192": 7, "step_hd256": 8}
 
 # small-batch products: X is m x n, m in {2, 4, 8, 16}, at three 7B shapes
 SMALLM_SHAPES = [OpShape("down", 18944, 3584), OpShape("gate", 3584, 18944),
@@ -203,10 +203,11 @@ def generate_smallm(shape: OpShape, m: int):
 # ------------------------------------------------------------------ whole decode-step models
 # Qwen3-style decoders (the step of page "IV.4: One command buffer per token",
 # section "One command buffer").  "qwen3_0.6b" has Qwen3-0.6B's shape and the
-# very projection bytes of the qwen3_0.6b_chain workload; the two small ones
+# very projection bytes of the qwen3_0.6b_chain workload; the small ones
 # are test models: "step_tiny" (2 layers, head_dim 64, two query heads per
-# KV head) and "step_gqa4" (head_dim 128, four query heads per KV head, an
-# intermediate width and a vocabulary that are not powers of two).
+# KV head), "step_gqa4" (head_dim 128, four query heads per KV head, an
+# intermediate width and a vocabulary that are not powers of two),
+# "step_hd192" (three query heads on one KV head) and "step_hd256".
 STEP_MODELS = {
     "qwen3_0.6b": dict(n_layers=28, hidden=1024, n_heads=16, n_kv_heads=8, head_dim=128,
                        inter=3072, vocab=151936, eps=1e-6, theta=1e6),
@@ -214,9 +215,14 @@ STEP_MODELS = {
                       inter=512, vocab=1000, eps=1e-6, theta=1e6),
     "step_gqa4": dict(n_layers=1, hidden=512, n_heads=8, n_kv_heads=2, head_dim=128,
                       inter=1376, vocab=4099, eps=1e-6, theta=1e4),
+    "step_hd192": dict(n_layers=1, hidden=384, n_heads=3, n_kv_heads=1, head_dim=192,
+                       inter=640, vocab=500, eps=1e-5, theta=1e6),
+    "step_hd256": dict(n_layers=2, hidden=512, n_heads=4, n_kv_heads=2, head_dim=256,
+                       inter=768, vocab=700, eps=1e-6, theta=1e6),
 }
 STEP_SEED = {"qwen3_0.6b": WORKLOAD_ID["qwen3_0.6b_chain"], "step_tiny": WORKLOAD_ID["step_tiny"],
-             "step_gqa4": WORKLOAD_ID["step_gqa4"]}
+             "step_gqa4": WORKLOAD_ID["step_gqa4"], "step_hd192": WORKLOAD_ID["step_hd192"],
+             "step_hd256": WORKLOAD_ID["step_hd256"]}
 PROJ = ("wq", "wk", "wv", "wo", "wgate", "wup", "wdown")
 NORMS = ("attn_norm", "ffn_norm", "q_norm", "k_norm")
 

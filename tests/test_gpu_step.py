@@ -278,9 +278,10 @@ def _run_tokens(q8, st, mode, pos, token, count):
 def test_step_launch_count(q8):
     log("step launches step_tiny")
     cfg, _, st = _step(q8, "step_tiny", 64)
-    # per layer: qkv fused, o, gate|up fused, down; q/k post, attention, two
-    # add+norm, silu; then embed+norm, lm_head, argmax
-    assert st.launches == cfg["n_layers"] * (4 + 5) + 1 + 2
+    # per layer: qkv fused, o, gate|up fused, down; attention (with the q/k
+    # norms, rotary embedding and cache append), two add+norm, silu; then
+    # embed+norm, lm_head, argmax
+    assert st.launches == cfg["n_layers"] * (4 + 4) + 1 + 2
     st.close()
 
 
@@ -322,6 +323,7 @@ def _compare_step(cfg, w, kc, vc, tok_in, pos, logits, x, tok_gpu, label):
 
 @pytest.mark.parametrize("name,max_seq,pos0,count", [
     ("step_tiny", 64, 0, 5), ("step_gqa4", 64, 0, 4), ("step_gqa4", 1100, 1000, 3),
+    ("step_hd192", 300, 126, 4), ("step_hd256", 200, 0, 3), ("step_hd256", 200, 127, 3),
 ], ids=str)
 def test_step_matches_oracle(q8, name, max_seq, pos0, count):
     log("step vs oracle %s max_seq=%d pos0=%d" % (name, max_seq, pos0))
