@@ -72,6 +72,12 @@ class Oracle:
         lib.q8o_gemv.restype = ctypes.c_int
         lib.q8o_gemm.argtypes = [p, p, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, p, p, p]
         lib.q8o_gemm.restype = ctypes.c_int
+        lib.q8o_f32_to_f16.argtypes = [ctypes.c_float]
+        lib.q8o_f32_to_f16.restype = ctypes.c_uint16
+        lib.q8o_quantize_x.argtypes = [p, ctypes.c_int64, p]
+        lib.q8o_quantize_x.restype = ctypes.c_int
+        lib.q8o_gemv_q8q8.argtypes = [p, p, ctypes.c_int64, ctypes.c_int64, p, p, p]
+        lib.q8o_gemv_q8q8.restype = ctypes.c_int
         self.lib = lib
         self.path = lib_path
 
@@ -127,6 +133,35 @@ class Oracle:
         return Y, Y64, MAG
 
 
+    def f32_to_f16(self, v: float) -> int:
+        """binary16 bits of a float32 value, nearest with ties to even."""
+        return int(self.lib.q8o_f32_to_f16(float(np.float32(v))))
+
+    def quantize_x(self, x) -> np.ndarray:
+        """x (n floats) as n/32 Q8_0 blocks: uint8[n/32*34] (the reading of
+        the pages' activation quantization, see the C source)."""
+        x = np.ascontiguousarray(x, dtype=np.float32).reshape(-1)
+        out = np.empty(row_bytes(x.size), np.uint8)
+        if self.lib.q8o_quantize_x(_ptr(x), x.size, _ptr(out)) != 0:
+            raise ValueError("n must be a positive multiple of 32")
+        return out
+
+    def gemv_q8q8(self, w, x, n: int, p: int) -> Tuple[np.ndarray, np.ndarray, np.ndarray]:
+        """The integer matvec (x quantized to Q8_0): (y, y64, mag) as gemv()."""
+        w = _as_w(w)
+        x = np.ascontiguousarray(x, dtype=np.float32).reshape(-1)
+        if n <= 0 or n % BLOCK_QUANTS:
+            raise ValueError("n must be a positive multiple of 32")
+        if w.size < p * row_bytes(n) or x.size < n:
+            raise ValueError("buffer too small for the stated shape")
+        y = np.empty(p, np.float32)
+        y64 = np.empty(p, np.float64)
+        mag = np.empty(p, np.float64)
+        if self.lib.q8o_gemv_q8q8(_ptr(w), _ptr(x), n, p, _ptr(y), _ptr(y64), _ptr(mag)) != 0:
+            raise ValueError("oracle rejected the shape")
+        return y, y64, mag
+
+
 _default: Optional[Oracle] = None
 
 
@@ -153,3 +188,15 @@ def gemv_rows(w, x, n: int, rows: Iterable[int]):
 
 def gemm(w, X, m: int, n: int, p: int):
     return default().gemm(w, X, m, n, p)
+
+
+def f32_to_f16(v: float) -> int:
+    return default().f32_to_f16(v)
+
+
+def quantize_x(x):
+    return default().quantize_x(x)
+
+
+def gemv_q8q8(w, x, n: int, p: int):
+    return default().gemv_q8q8(w, x, n, p)

@@ -32,9 +32,20 @@
  * scale bytes 0x00 0x2c (= 0.0625), zero-scale and all-ones invariants, an
  * integer-exact case checked against exact rational arithmetic, and the
  * exhaustive binary16 table against numpy.
+ *
+ * The integer path (q8o_quantize_x, q8o_gemv_q8q8) follows the CPU kernel the
+ * same page sets beside q8_matvec (section "Eight kernels", the note after the
+ * kernel; and page "minfer Metal Backend Design", ADR-0013): the activations
+ * are quantized to Q8_0 blocks too and each block's dot product is an integer
+ * sum of quant products.  The pages do not print the quantization rule; the
+ * reading taken is written at q8o_quantize_x.  Its pins: closed-form blocks
+ * (scales that are powers of two, ties at .5, the all-zero block), the
+ * dequantization error bound, numpy's binary16 cast for the scale encoding,
+ * brute force for the integer dot, and the distance to the float matvec.
  */
 #include <stdint.h>
 #include <stddef.h>
+#include <stdlib.h>
 #include <math.h>
 
 #define Q8O_BLOCK_QUANTS 32
@@ -129,5 +140,126 @@ int q8o_gemm(const uint8_t *w, const float *X, int64_t m, int64_t n, int64_t p,
         if (rc != 0)
             return rc;
     }
+    return 0;
+}
+
+/*
+ * float -> IEEE binary16, rounding to nearest with ties to even, from the
+ * format definition: a value a in [2^e, 2^(e+1)) with e >= -14 has the
+ * spacing 2^(e-10); below 2^-14 the spacing is 2^-24 (subnormals).  Values at
+ * or above 65520 (the midpoint between 65504 and 2^16) become infinity.
+ */
+uint16_t q8o_f32_to_f16(float vf)
+{
+    double v = (double)vf;
+    uint16_t sign = signbit(v) ? 0x8000 : 0;
+    double a = fabs(v);
+    if (isnan(a))
+        return (uint16_t)(sign | 0x7e00);
+    if (a >= 65520.0)
+        return (uint16_t)(sign | 0x7c00);
+    if (a == 0.0)
+        return sign;
+    int ex;
+    frexp(a, &ex);
+    int e = ex - 1;
+    if (e < -14)
+        e = -14;
+    double ulp = ldexp(1.0, e - 10);
+    double r = nearbyint(a / ulp) * ulp;   /* a / ulp is exact; ties go to even */
+    if (r == 0.0)
+        return sign;
+    frexp(r, &ex);
+    e = ex - 1;
+    if (e < -14)
+        return (uint16_t)(sign | (uint16_t)(r / ldexp(1.0, -24)));
+    return (uint16_t)(sign | (uint16_t)((e + 15) << 10) | (uint16_t)(r / ldexp(1.0, e - 10) - 1024.0));
+}
+
+/*
+ * x (n floats, n a positive multiple of 32) -> n/32 Q8_0 blocks of 34 bytes,
+ * the layout of a weight row.  Reading of the pages' "quantize activations
+ * to Q8_0" (the rule itself is not printed): per block of 32,
+ *   amax = max_j |x_j|                                  (float32, exact)
+ *   d    = amax / 127                                   (float32 division)
+ *   q_j  = x_j / d rounded to the nearest integer, halves away from zero
+ *          (float32 division; every q_j is 0 when d == 0)
+ *   the stored scale is d rounded to binary16 (nearest, ties to even).
+ * Every decision is a float32 operation, so an implementation doing the same
+ * IEEE operations produces the same bytes.  x must be finite.
+ * Returns 0, or -1 for a bad n.
+ */
+int q8o_quantize_x(const float *x, int64_t n, uint8_t *out)
+{
+    if (n <= 0 || n % Q8O_BLOCK_QUANTS != 0)
+        return -1;
+    for (int64_t b = 0; b < n / Q8O_BLOCK_QUANTS; ++b) {
+        const float *xb = x + b * Q8O_BLOCK_QUANTS;
+        uint8_t *o = out + b * Q8O_BLOCK_BYTES;
+        float amax = 0.0f;
+        for (int j = 0; j < Q8O_BLOCK_QUANTS; ++j) {
+            float a = fabsf(xb[j]);
+            if (a > amax)
+                amax = a;
+        }
+        float d = amax / 127.0f;
+        uint16_t db = q8o_f32_to_f16(d);
+        o[0] = (uint8_t)(db & 0xff);
+        o[1] = (uint8_t)(db >> 8);
+        for (int j = 0; j < Q8O_BLOCK_QUANTS; ++j) {
+            int q = 0;
+            if (d != 0.0f) {
+                float t = xb[j] / d;
+                q = (int)roundf(t);
+            }
+            o[2 + j] = (uint8_t)(int8_t)q;
+        }
+    }
+    return 0;
+}
+
+/*
+ * The integer matvec: x quantized as q8o_quantize_x does, then per row
+ *   y[r] = sum_b d_w(r,b) * d_x(b) * sum_j q_w(r,b,j) * q_x(b,j)
+ * with the inner sum in integers (exact) and the blocks added in double, in
+ * column order (each block's share is exact in double: 11 + 11 + 20 bits).
+ * mag[r] = sum_b |d_w d_x| * sum_j |q_w q_x|.  Outputs as in q8o_gemv.
+ * Returns 0, -1 for a bad shape, -2 if out of memory.
+ */
+int q8o_gemv_q8q8(const uint8_t *w, const float *x, int64_t n, int64_t p,
+                  float *y, double *y64, double *mag)
+{
+    if (n <= 0 || n % Q8O_BLOCK_QUANTS != 0 || p < 0)
+        return -1;
+    int64_t nblocks = n / Q8O_BLOCK_QUANTS;
+    int64_t row_bytes = nblocks * Q8O_BLOCK_BYTES;
+    uint8_t *xq = (uint8_t *)malloc((size_t)row_bytes);
+    if (!xq)
+        return -2;
+    q8o_quantize_x(x, n, xq);
+    for (int64_t r = 0; r < p; ++r) {
+        const uint8_t *row = w + r * row_bytes;
+        double acc = 0.0;
+        double m = 0.0;
+        for (int64_t b = 0; b < nblocks; ++b) {
+            const uint8_t *wb = row + b * Q8O_BLOCK_BYTES;
+            const uint8_t *xb = xq + b * Q8O_BLOCK_BYTES;
+            double dw = q8o_f16_to_double((uint16_t)(wb[0] | ((uint16_t)wb[1] << 8)));
+            double dx = q8o_f16_to_double((uint16_t)(xb[0] | ((uint16_t)xb[1] << 8)));
+            int64_t isum = 0;
+            int64_t iabs = 0;
+            for (int j = 0; j < Q8O_BLOCK_QUANTS; ++j) {
+                int64_t prod = (int64_t)(int8_t)wb[2 + j] * (int64_t)(int8_t)xb[2 + j];
+                isum += prod;
+                iabs += prod < 0 ? -prod : prod;
+            }
+            acc += (dw * dx) * (double)isum;
+            m += fabs(dw * dx) * (double)iabs;
+        }
+        if (y) y[r] = (float)acc;
+        if (y64) y64[r] = acc;
+        if (mag) mag[r] = m;
+    }
+    free(xq);
     return 0;
 }

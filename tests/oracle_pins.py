@@ -232,6 +232,137 @@ def pin_gemm_rows(o):
         assert np.all(np.abs(Y64[i] - ry) <= 1e-12 * rmag + 1e-300)
 
 
+# ---------------------------------------------------------------- activations as Q8_0
+def _f16_bits(v):
+    return int(np.asarray(v, np.float32).astype(np.float16).view(np.uint16))
+
+
+def _blocks(xq):
+    """(scale as float64, quants as int64) of Q8_0 bytes, decoded with numpy."""
+    blk = np.asarray(xq, np.uint8).reshape(-1, 34)
+    d = blk[:, 0:2].copy().view("<f2").astype(np.float64)[:, 0]
+    q = blk[:, 2:].copy().view(np.int8).astype(np.int64)
+    return d, q
+
+
+def pin_f16_encode(o):
+    """float32 -> binary16 against numpy's cast (nearest, ties to even): every
+    midpoint between consecutive finite binary16 values (the ties), the
+    values themselves, and random magnitudes from below the subnormals to
+    past the largest finite value."""
+    h = np.arange(0, 0x7c00, dtype=np.uint32).astype(np.uint16).view(np.float16).astype(np.float64)
+    mids = (h[:-1] + h[1:]) / 2.0                  # exact in float32 (12 bits)
+    rng = np.random.default_rng(31)
+    rand = np.exp(rng.uniform(np.log(1e-9), np.log(7e4), 4000))
+    vals = np.concatenate([h[::7], mids[::3], mids[-50:], mids[:50], rand, [65504.0, 65519.0, 65520.0, 1e6]])
+    vals = np.concatenate([vals, -vals]).astype(np.float32)
+    ref = vals.astype(np.float16).view(np.uint16)
+    got = np.array([o.f32_to_f16(float(v)) for v in vals], np.uint16)
+    bad = np.nonzero(got != ref)[0]
+    assert bad.size == 0, "f32 %r -> 0x%04x, numpy 0x%04x" % (float(vals[bad[0]]), got[bad[0]], ref[bad[0]])
+
+
+def pin_quantize_closed_forms(o):
+    """Blocks whose scale is a power of two times 127 quantize to the exact
+    integers; halves round away from zero; an all-zero block is all zero
+    bytes; each block has its own scale."""
+    k = np.arange(-16, 16, dtype=np.float64)
+    k[0] = -127.0                                  # the block's largest magnitude
+    blk0 = (k * 2.0 ** -3).astype(np.float32)       # d = 2^-3 exactly
+    ties = np.zeros(32)
+    ties[:7] = [127.0, 2.5, -2.5, 0.5, -0.5, 1.5, -126.5]   # d = 1
+    blk1 = ties.astype(np.float32)
+    blk2 = np.zeros(32, np.float32)
+    k3 = np.arange(32, dtype=np.float64) * 4.0 - 3.0
+    k3[31] = 127.0
+    blk3 = (k3 * 2.0 ** 4).astype(np.float32)       # d = 16
+    xq = o.quantize_x(np.concatenate([blk0, blk1, blk2, blk3]))
+    b = np.asarray(xq).reshape(4, 34)
+    assert int(b[0, 0]) | (int(b[0, 1]) << 8) == _f16_bits(2.0 ** -3)
+    assert np.array_equal(b[0, 2:].view(np.int8), k.astype(np.int8))
+    assert int(b[1, 0]) | (int(b[1, 1]) << 8) == 0x3C00
+    assert list(b[1, 2:9].view(np.int8)) == [127, 3, -3, 1, -1, 2, -127]
+    assert not b[2].any()
+    assert int(b[3, 0]) | (int(b[3, 1]) << 8) == _f16_bits(16.0)
+    assert np.array_equal(b[3, 2:].view(np.int8), k3.astype(np.int8))
+
+
+def pin_quantize_error_bound(o):
+    """On random blocks: the largest magnitude maps to +-127, every quant
+    lies in [-127, 127], and dequantizing with the unrounded float32 scale
+    d = amax/127 misses x by at most d/2 (plus the scale division's own
+    rounding); the stored scale is that d in binary16."""
+    rng = np.random.default_rng(32)
+    x = (rng.standard_normal(32 * 200) * np.repeat(np.exp(rng.uniform(-6, 6, 200)), 32)).astype(np.float32)
+    d16, q = _blocks(o.quantize_x(x))
+    xb = x.reshape(200, 32).astype(np.float64)
+    amax = np.abs(xb).max(axis=1)
+    d = amax / 127.0
+    assert np.all(np.abs(q) <= 127) and np.all(np.abs(q).max(axis=1) == 127)
+    err = np.abs(xb - d[:, None] * q)
+    assert np.all(err <= d[:, None] * (0.5 + 1e-6)), float((err / d[:, None]).max())
+    assert np.all(np.abs(d16 - d) <= d * 2.0 ** -11 + 2.0 ** -25)
+    # the sign of every non-zero quant is the sign of x
+    nz = q != 0
+    assert np.all(np.sign(q[nz]) == np.sign(xb[nz]))
+
+
+def pin_q8q8_brute_force(o):
+    """The integer matvec against a dense float64 product of the weights and
+    the quantized x, both decoded with numpy; the quantized x is the
+    oracle's own (pinned above)."""
+    rng = np.random.default_rng(33)
+    for n, p in [(32, 5), (96, 17), (256, 9)]:
+        w = synth.q8_weights(n, p, rng)
+        x = synth.activations(n, rng)
+        d, q = _blocks(o.quantize_x(x))
+        xhat = (d[:, None] * q).reshape(-1)
+        ry, rmag = dense_reference(w, xhat.astype(np.float64), n, p)
+        y, y64, mag = o.gemv_q8q8(w, x, n, p)
+        assert np.all(np.abs(y64 - ry) <= 1e-12 * rmag + 1e-300)
+        assert np.allclose(mag, rmag, rtol=1e-12, atol=0)
+        assert np.array_equal(y, y64.astype(np.float32))
+
+
+def pin_q8q8_near_float(o):
+    """The integer matvec differs from the float matvec only by x's
+    quantization error: |y_q8q8 - y_f32| <= sum_j |w_j| |x_j - xhat_j|."""
+    rng = np.random.default_rng(34)
+    n, p = 512, 40
+    w = synth.q8_weights(n, p, rng)
+    x = synth.activations(n, rng)
+    d, q = _blocks(o.quantize_x(x))
+    xhat = (d[:, None] * q).reshape(-1)
+    nb = n // 32
+    blk = w.reshape(p * nb, 34)
+    dw = blk[:, 0:2].copy().view("<f2").astype(np.float64).reshape(p, nb)
+    qw = blk[:, 2:].copy().view(np.int8).astype(np.float64).reshape(p, nb, 32)
+    absw = np.abs(dw[:, :, None] * qw).reshape(p, n)
+    bound = absw @ np.abs(x.astype(np.float64) - xhat)
+    _, yq, magq = o.gemv_q8q8(w, x, n, p)
+    _, yf, magf = o.gemv(w, x, n, p)
+    assert np.all(np.abs(yq - yf) <= bound + 1e-12 * (magq + magf))
+    assert np.all(bound < 0.05 * magf)     # and the error is small
+
+
+def pin_q8q8_integer_exact(o):
+    """Unit weight scales and integer activations whose blocks each reach
+    127: the quantized x is x itself and y is the exact integer sum."""
+    rng = np.random.default_rng(35)
+    n, p = 192, 11
+    nb = n // 32
+    xi = rng.integers(-127, 128, size=n)
+    xi[::32] = 127
+    qw = rng.integers(-127, 128, size=(p * nb, 32)).astype(np.int8)
+    w = synth.pack_blocks(np.full(p * nb, 1.0, np.float16), qw)
+    y, y64, mag = o.gemv_q8q8(w, xi.astype(np.float32), n, p)
+    exact = qw.astype(np.int64).reshape(p, n) @ xi.astype(np.int64)
+    assert np.array_equal(y64, exact.astype(np.float64))
+    assert np.array_equal(mag, (np.abs(qw.astype(np.int64).reshape(p, n)) @ np.abs(xi)).astype(np.float64))
+
+
 ALL_PINS = [pin_f16_exhaustive, pin_page_scale_bytes, pin_hand_worked_row,
             pin_quant_byte_range, pin_brute_force, pin_page_shape, pin_zero_scale,
-            pin_all_ones, pin_integer_exact, pin_specials, pin_symmetries, pin_gemm_rows]
+            pin_all_ones, pin_integer_exact, pin_specials, pin_symmetries, pin_gemm_rows,
+            pin_f16_encode, pin_quantize_closed_forms, pin_quantize_error_bound,
+            pin_q8q8_brute_force, pin_q8q8_near_float, pin_q8q8_integer_exact]

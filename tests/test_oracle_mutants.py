@@ -31,6 +31,17 @@ MUTANTS = {
     "float_accumulator": ("double acc = 0.0;", "float acc = 0.0f;"),
     "nan_as_inf": ("(f == 0) ? INFINITY : NAN", "INFINITY"),
     "gemm_x_stride": ("X + i * n", "X + i"),
+    "quant_half_even": ("q = (int)roundf(t);", "q = (int)nearbyintf(t);"),
+    "quant_truncate": ("q = (int)roundf(t);", "q = (int)t;"),
+    "amax_signed": ("float a = fabsf(xb[j]);", "float a = xb[j];"),
+    "quant_scale_128": ("amax / 127.0f", "amax / 128.0f"),
+    "f16_round_down": ("nearbyint(a / ulp)", "floor(a / ulp)"),
+    "f16_spacing": ("ldexp(1.0, e - 10)", "ldexp(1.0, e - 11)"),
+    "f16_no_subnormal_floor": ("    if (e < -14)\n        e = -14;\n", ""),
+    "xq_scale_bytes_swapped": ("o[0] = (uint8_t)(db & 0xff);", "o[0] = (uint8_t)(db >> 8);"),
+    "q8q8_dx_dropped": ("acc += (dw * dx) * (double)isum;", "acc += dw * (double)isum;"),
+    "q8q8_unsigned_x": ("(int64_t)(int8_t)xb[2 + j]", "(int64_t)xb[2 + j]"),
+    "q8q8_x_block_offset": ("xq + b * Q8O_BLOCK_BYTES", "xq"),
 }
 
 
