@@ -203,6 +203,9 @@ def main():
     ap.add_argument("--smallm", action="store_true",
                     help="instead of the chain: time q8_0_gemm_smallm at the 7B shapes, "
                          "m in {2,4,8,16}, rotating weight copies past the 256 MB cache")
+    ap.add_argument("--xq", action="store_true",
+                    help="the chain's ops quantize x to Q8_0 and multiply integers "
+                         "(q8_0_gemv_q8q8 semantics) instead of multiplying float x")
     ap.add_argument("--step", action="store_true",
                     help="instead of the chain: time a whole Qwen3-0.6B-shaped decode token "
                          "(every kernel of the step, one hipGraph) from positions 0 and 511")
@@ -259,7 +262,7 @@ def main():
     torch.cuda.synchronize()
     say("resident in HBM: %.2f GB" % (torch.cuda.memory_allocated() / 1e9))
 
-    chain = q8.Chain(dev_ops, fuse=True)
+    chain = q8.Chain(dev_ops, fuse=True, xq=args.xq)
     stream = torch.cuda.current_stream()
 
     def time_steps(run, k):
@@ -302,7 +305,8 @@ def main():
                 "traffic": measured_traffic(args.workload),
                 # a chain of one op is that op's standalone launch (four-wave
                 # workgroups); more independent ops share one fused launch
-                "kernel": "k_q8_gemv_fused<1,1>" if len(ops_shape) > 1 else "k_q8_gemv<4,1>",
+                "kernel": ("k_q8_gemv_fused<1,1,%s>" if len(ops_shape) > 1 else "k_q8_gemv<4,1,%s>")
+                          % ("true" if args.xq else "false"),
                 "launches_per_step": launches,
                 "algorithmic_bytes_per_launch": nbytes // launches,
                 "kernel_us": round(kernel_s * 1e6, 2),
@@ -312,7 +316,7 @@ def main():
     if not args.no_modes:
         k = max(3, args.steps // 10)
         modes["fused_eager_us"] = round(time_steps(lambda: chain.run(q8.MODE_EAGER, stream), k) / k * 1e6, 2)
-        per_op = q8.Chain(dev_ops, fuse=False)
+        per_op = q8.Chain(dev_ops, fuse=False, xq=args.xq)
         for m, name in ((q8.MODE_GRAPH, "per_op_graph_us"), (q8.MODE_EAGER, "per_op_eager_us"),
                         (q8.MODE_SYNC_EACH, "per_op_sync_each_us")):
             per_op.run(m, stream)
@@ -333,9 +337,10 @@ def main():
         "us_per_token": round(per_step * 1e6, 2),
         "pct_of_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
-        "dtype": "f32", "data": "synthetic",
+        "dtype": "i8xi8->f32" if args.xq else "f32", "data": "synthetic",
         "config": {"workload": args.workload, "ops_per_token": len(ops_shape),
                    "bytes_per_token": nbytes, "mode": "hipGraph replay, fused launch",
+                   "activations_as": "Q8_0, integer dots" if args.xq else "float32",
                    "weights": "Q8_0, scale U[0.001,0.02] as f16, quants U{-127..127}",
                    "activations": "f32 N(0,1), independent per op"},
         "roofline": roofline,

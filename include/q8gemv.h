@@ -112,6 +112,7 @@ typedef struct q8_0_chain q8_0_chain; /* opaque */
                                every op for latency -- its K split over more waves, across
                                workgroups when it has few rows; results stay bitwise
                                reproducible but round differently from q8_0_gemv */
+#define Q8_CHAIN_XQ 4u      /* every op as q8_0_gemv_q8q8: x quantized to Q8_0, integer dots */
 
 /* decode_chain modes */
 #define Q8_MODE_GRAPH 0     /* replay the recorded hipGraph: one host call per token */
@@ -134,6 +135,30 @@ typedef struct q8_0_chain q8_0_chain; /* opaque */
  */
 int q8_0_chain_create(const q8_0_op *ops, int64_t n_ops, uint32_t flags,
                       q8_0_chain **out);
+
+/*
+ * The integer path (page "IV.4: One command buffer per token", section
+ * "Eight kernels": the CPU kernel beside q8_matvec quantizes the activations
+ * and multiplies integers; page "minfer Metal Backend Design", ADR-0013).
+ * x is quantized to Q8_0 blocks -- per 32 values d = amax/127 (float32),
+ * code = x/d rounded half away from zero (0 when d == 0), d stored as
+ * binary16 (nearest, ties to even); the pages do not print this rule, it is
+ * the reading taken -- and each block's dot is an integer sum:
+ *   y[r] = sum_b d_w(r,b) * d_x(b) * sum_j q_w(r,b,j) * q_x(b,j).
+ * Arguments, validation and errors as q8_0_gemv; x must be finite.  The codes
+ * are bit-identical to q8_0_quantize's; y is held to the same bar as
+ * q8_0_gemv, against that integer definition.  Allocates nothing.
+ */
+int q8_0_gemv_q8q8(const float *x, const void *w, float *y, int64_t n, int64_t p,
+                   void *stream);
+
+/*
+ * x (n floats, n a positive multiple of 32, at most 2^31, 4-byte aligned) ->
+ * n/32 Q8_0 blocks of 34 bytes at xq (the weight layout; no alignment
+ * needed; must not overlap x), by the rule above.  Exact: the bytes are
+ * decided by float32 operations.
+ */
+int q8_0_quantize(const float *x, void *xq, int64_t n, void *stream);
 
 /* Run one token's chain on `stream` in the given mode. */
 int q8_0_decode_chain(q8_0_chain *chain, int mode, void *stream);

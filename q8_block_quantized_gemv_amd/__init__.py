@@ -8,6 +8,7 @@ implementation: if the library is missing, importing this package raises.
 The names follow the C ABI:
     gemv(x, w, y=None, stream=None)            -> q8_0_gemv
     gemm_smallm(X, w, Y=None, stream=None)     -> q8_0_gemm_smallm
+    gemv_q8q8(x, w, y=None), quantize(x)       -> q8_0_gemv_q8q8, q8_0_quantize
     Chain(ops, fuse=True, split_k=False) .run  -> q8_0_chain_create / q8_0_decode_chain
     stream_wait(stream, timeout_ms)            -> q8_0_stream_wait
     rms_norm, rope, append_kv, attention_decode, add_inplace,
@@ -36,6 +37,7 @@ Q8_ERR_UNSUPPORTED = -8
 Q8_CHAIN_FUSE = 0
 Q8_CHAIN_PER_OP = 1
 Q8_CHAIN_SPLIT_K = 2
+Q8_CHAIN_XQ = 4
 MODE_GRAPH = 0
 MODE_EAGER = 1
 MODE_SYNC_EACH = 2
@@ -45,7 +47,7 @@ BLOCK_BYTES = 34
 
 EXPORTS = ("q8_0_gemv", "q8_0_gemm_smallm", "q8_0_chain_create", "q8_0_decode_chain",
            "q8_0_chain_launches", "q8_0_chain_destroy", "q8_0_stream_wait",
-           "q8_0_status_string", "q8_0_last_error",
+           "q8_0_status_string", "q8_0_last_error", "q8_0_gemv_q8q8", "q8_0_quantize",
            "q8_0_rms_norm", "q8_0_rope", "q8_0_append_kv", "q8_0_attention_decode",
            "q8_0_add_inplace", "q8_0_silu_hadamard", "q8_0_argmax",
            "q8_0_step_create", "q8_0_step_reset", "q8_0_step_run", "q8_0_step_launches",
@@ -103,6 +105,8 @@ def _load():
     lib.q8_0_status_string.restype = ctypes.c_char_p
     lib.q8_0_last_error.argtypes = []
     lib.q8_0_last_error.restype = ctypes.c_char_p
+    lib.q8_0_gemv_q8q8.argtypes = [vp, vp, vp, i64, i64, vp]
+    lib.q8_0_quantize.argtypes = [vp, vp, i64, vp]
     f32, u32, i32 = ctypes.c_float, ctypes.c_uint32, ctypes.c_int
     lib.q8_0_rms_norm.argtypes = [vp, vp, vp, i64, i64, f32, vp]
     lib.q8_0_rope.argtypes = [vp, i64, i64, i64, f32, vp]
@@ -201,6 +205,37 @@ def gemv(x, w, y=None, stream=None):
     return y
 
 
+def gemv_q8q8(x, w, y=None, stream=None):
+    """y = W x with x quantized to Q8_0 and integer block dots (q8_0_gemv_q8q8)."""
+    torch = _torch()
+    _need(x, torch.float32, "x")
+    _need(w, torch.uint8, "w")
+    p, n = weight_shape(w)
+    if x.numel() != n:
+        raise ValueError("x has %d elements, w has %d columns" % (x.numel(), n))
+    if y is None:
+        y = torch.empty(p, dtype=torch.float32, device=x.device)
+    _need(y, torch.float32, "y")
+    if y.numel() != p:
+        raise ValueError("y has %d elements, w has %d rows" % (y.numel(), p))
+    check(lib.q8_0_gemv_q8q8(x.data_ptr(), w.data_ptr(), y.data_ptr(), n, p, _stream_handle(stream)))
+    return y
+
+
+def quantize(x, xq=None, stream=None):
+    """x float32 (n,) -> Q8_0 bytes uint8 (n/32*34,) (q8_0_quantize)."""
+    torch = _torch()
+    _need(x, torch.float32, "x")
+    n = x.numel()
+    if xq is None:
+        xq = torch.empty(n // BLOCK_QUANTS * BLOCK_BYTES, dtype=torch.uint8, device=x.device)
+    _need(xq, torch.uint8, "xq")
+    if xq.numel() != n // BLOCK_QUANTS * BLOCK_BYTES:
+        raise ValueError("xq must hold n/32 blocks of 34 bytes")
+    check(lib.q8_0_quantize(x.data_ptr(), xq.data_ptr(), n, _stream_handle(stream)))
+    return xq
+
+
 def gemm_smallm(X, w, Y=None, stream=None):
     """Y = X W^T for X float32 (m, n), m in 1..16; returns Y float32 (m, p)."""
     torch = _torch()
@@ -232,7 +267,7 @@ class Chain:
     keeps references to them.
     """
 
-    def __init__(self, ops: Sequence, fuse: bool = True, split_k: bool = False):
+    def __init__(self, ops: Sequence, fuse: bool = True, split_k: bool = False, xq: bool = False):
         torch = _torch()
         arr = (Q8Op * len(ops))()
         self._keep = []
@@ -246,7 +281,8 @@ class Chain:
             arr[i] = Q8Op(x.data_ptr(), w.data_ptr(), y.data_ptr(), n, p)
             self._keep.append((x, w, y))
         h = ctypes.c_void_p()
-        flags = (Q8_CHAIN_FUSE if fuse else Q8_CHAIN_PER_OP) | (Q8_CHAIN_SPLIT_K if split_k else 0)
+        flags = ((Q8_CHAIN_FUSE if fuse else Q8_CHAIN_PER_OP) | (Q8_CHAIN_SPLIT_K if split_k else 0) |
+                 (Q8_CHAIN_XQ if xq else 0))
         check(lib.q8_0_chain_create(arr, len(ops), flags, ctypes.byref(h)))
         self._h = h
         self.n_ops = len(ops)

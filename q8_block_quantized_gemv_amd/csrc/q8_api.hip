@@ -242,11 +242,12 @@ int64_t tiles_of(const OpDesc &d, int nw = kWaves) {
     return (int64_t)d.fast_tiles + tail_tiles_for((int64_t)d.p - d.tail_row0, nw);
 }
 
-int gemv_launch(const float *x, const void *w, float *y, int64_t n, int64_t p, hipStream_t s) {
+int gemv_launch(const float *x, const void *w, float *y, int64_t n, int64_t p, hipStream_t s,
+                bool xq = false) {
     const Variant v = pick_variant(false);
     const OpDesc d = plan_op(x, w, y, 1, n, p, true, v.nw);
-    hipError_t e = launch_gemv_single(d, v, tiles_of(d, v.nw), s);
-    if (e != hipSuccess) return fail_hip(e, "q8_0_gemv launch");
+    hipError_t e = launch_gemv_single(d, v, tiles_of(d, v.nw), s, xq);
+    if (e != hipSuccess) return fail_hip(e, xq ? "q8_0_gemv_q8q8 launch" : "q8_0_gemv launch");
     return Q8_OK;
 }
 
@@ -366,6 +367,26 @@ int q8_0_gemv(const float *x, const void *w, float *y, int64_t n, int64_t p, voi
     return gemv_launch(x, w, y, n, p, (hipStream_t)stream);
 }
 
+int q8_0_gemv_q8q8(const float *x, const void *w, float *y, int64_t n, int64_t p, void *stream) {
+    int rc = validate(x, w, y, 1, n, p, "q8_0_gemv_q8q8");
+    if (rc) return rc;
+    if ((rc = check_device())) return rc;
+    return gemv_launch(x, w, y, n, p, (hipStream_t)stream, true);
+}
+
+int q8_0_quantize(const float *x, void *xq, int64_t n, void *stream) {
+    if (!x || !xq) return fail(Q8_ERR_INVALID_ARG, "q8_0_quantize: null pointer");
+    if (n <= 0 || n % kQuants || n > ((int64_t)1 << 31))
+        return fail(Q8_ERR_SHAPE, "q8_0_quantize: n must be a positive multiple of 32, at most 2^31");
+    if ((uintptr_t)x & 3u) return fail(Q8_ERR_ALIGN, "q8_0_quantize: x must be 4-byte aligned");
+    if (overlaps(xq, n / kQuants * kBlockBytes, x, 4 * n))
+        return fail(Q8_ERR_ALIAS, "q8_0_quantize: xq overlaps x");
+    int rc = check_device();
+    if (rc) return rc;
+    hipError_t e = launch_quantize_x(x, xq, n, (hipStream_t)stream);
+    return e == hipSuccess ? Q8_OK : fail_hip(e, "q8_0_quantize launch");
+}
+
 int q8_0_gemm_smallm(const float *X, const void *w, float *Y, int64_t m, int64_t n, int64_t p,
                      void *stream) {
     int rc = validate(X, w, Y, m, n, p, "q8_0_gemm_smallm");
@@ -422,6 +443,7 @@ struct q8_0_chain {
     // one entry per kernel launch of a token
     struct Launch {
         bool fused;
+        bool xq;              // x quantized to Q8_0, integer products
         Variant v;
         OpDesc single;        // per-op launch
         const OpDesc *d_ops;  // fused launch
@@ -438,8 +460,8 @@ struct q8_0_chain {
 namespace {
 
 hipError_t issue(const q8_0_chain::Launch &L, hipStream_t s) {
-    if (L.fused) return launch_gemv_fused(L.d_ops, L.d_tiles, L.v, L.grid, s);
-    return launch_gemv_single(L.single, L.v, L.grid, s);
+    if (L.fused) return launch_gemv_fused(L.d_ops, L.d_tiles, L.v, L.grid, s, L.xq);
+    return launch_gemv_single(L.single, L.v, L.grid, s, L.xq);
 }
 
 void chain_free(q8_0_chain *c) {
@@ -477,7 +499,7 @@ int q8_0_chain_create(const q8_0_op *ops, int64_t n_ops, uint32_t flags, q8_0_ch
     *out = nullptr;
     if (!ops || n_ops <= 0 || n_ops > Q8_MAX_CHAIN_OPS)
         return fail(Q8_ERR_INVALID_ARG, "q8_0_chain_create: need 1..65535 ops");
-    if (flags & ~(uint32_t)(Q8_CHAIN_PER_OP | Q8_CHAIN_SPLIT_K))
+    if (flags & ~(uint32_t)(Q8_CHAIN_PER_OP | Q8_CHAIN_SPLIT_K | Q8_CHAIN_XQ))
         return fail(Q8_ERR_INVALID_ARG, "q8_0_chain_create: unknown flags");
     for (int64_t i = 0; i < n_ops; ++i) {
         const std::string what = "q8_0_chain_create op " + std::to_string(i);
@@ -596,6 +618,7 @@ int q8_0_chain_create(const q8_0_op *ops, int64_t n_ops, uint32_t flags, q8_0_ch
     for (size_t k = 0; k < segs.size(); ++k) {
         q8_0_chain::Launch L;
         std::memset(&L, 0, sizeof L);
+        L.xq = (flags & Q8_CHAIN_XQ) != 0;
         if (info[k].fused) {
             L.fused = true;
             L.v = info[k].v;

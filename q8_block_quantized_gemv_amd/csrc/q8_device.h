@@ -100,6 +100,29 @@ __device__ __forceinline__ void read_group(const uint8_t *st, int lane, uint32_t
     }
 }
 
+// direct loads per group of the matvec: 17 of W and one of x
+constexpr int kLoadsPerGroup = kGroupChunks + 1;
+
+// Where lane `lane` finds its 16 bytes of the x slice of group kk: floats
+// 4*(lane%8) .. +3 of block lane/8 of the group, i.e. of column block
+// (8*kk + lane/8) mod nb (a group of a super-row wraps past the row end).
+template <int RS>
+__device__ __forceinline__ const float *x_slice_src(const OpDesc &op, int kk, int lane) {
+    int b = kk * kGroupBlocks + (lane >> 3);
+    if (RS > 1) b %= op.nb;
+    return op.x + (int64_t)b * kQuants + 4 * (lane & 7);
+}
+
+// One group: 17 loads of W and one load of its x slice (at st + kStageW).
+template <int RS>
+__device__ __forceinline__ void dma_group_x(const uint8_t *g, const uint32_t (&off)[kGroupChunks],
+                                            uint8_t *st, const OpDesc &op, int kk, int lane) {
+    const uint32_t l0 = __builtin_amdgcn_readfirstlane(lds_addr(st));
+#pragma unroll
+    for (int i = 0; i < kGroupChunks; ++i) dma16_s(g, off[i], l0 + kWave * 16 * i);
+    dma16_v(x_slice_src<RS>(op, kk, lane), l0 + kStageW);
+}
+
 // acc[slot][r] += v for a uniform slot and row index (unrolled selects).
 template <int RS>
 __device__ __forceinline__ void flush_row(float (&acc)[kSlots][RS], int slot, int r, float v) {
@@ -112,6 +135,25 @@ __device__ __forceinline__ void flush_row(float (&acc)[kSlots][RS], int slot, in
 
 __device__ __forceinline__ float combine_slots(float s0, float s1, float s2, float s3) {
     return (s0 + s1) + (s2 + s3);
+}
+
+// ---------------------------------------------------------------- activations as Q8_0
+// The integer path quantizes x to Q8_0 blocks the way the pages' CPU path is
+// read here: per 32 values d = amax / 127 (float32 division), code =
+// x / d rounded half away from zero (0 when d == 0), and the scale kept as
+// binary16 (nearest, ties to even).  Every step is an IEEE float32 operation,
+// so every implementation doing the same operations gets the same codes.
+__device__ __forceinline__ float xq_scale(float amax) { return amax / 127.0f; }
+__device__ __forceinline__ int xq_code(float x, float d) {
+    return d != 0.f ? (int)roundf(x / d) : 0;
+}
+__device__ __forceinline__ uint16_t xq_f16_bits(float d) {
+    return __builtin_bit_cast(uint16_t, (_Float16)d);
+}
+__device__ __forceinline__ float xq_f16_value(float d) { return (float)(_Float16)d; }
+__device__ __forceinline__ uint32_t pack4(int a, int b, int c, int d) {
+    return (uint32_t)(a & 0xff) | ((uint32_t)(b & 0xff) << 8) | ((uint32_t)(c & 0xff) << 16) |
+           ((uint32_t)(d & 0xff) << 24);
 }
 
 // ---------------------------------------------------------------- tail rows

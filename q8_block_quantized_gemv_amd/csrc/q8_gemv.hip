@@ -58,29 +58,6 @@ __device__ __forceinline__ void block_terms(const uint32_t (&D)[68], const float
     s = (a0 + a1) + (a2 + a3);
 }
 
-// direct loads per group of the matvec: 17 of W and one of x
-constexpr int kLoadsPerGroup = kGroupChunks + 1;
-
-// Where lane `lane` finds its 16 bytes of the x slice of group kk: floats
-// 4*(lane%8) .. +3 of block lane/8 of the group, i.e. of column block
-// (8*kk + lane/8) mod nb (a group of a super-row wraps past the row end).
-template <int RS>
-__device__ __forceinline__ const float *x_slice_src(const OpDesc &op, int kk, int lane) {
-    int b = kk * kGroupBlocks + (lane >> 3);
-    if (RS > 1) b %= op.nb;
-    return op.x + (int64_t)b * kQuants + 4 * (lane & 7);
-}
-
-// One group: 17 loads of W and one load of its x slice (at st + kStageW).
-template <int RS>
-__device__ __forceinline__ void dma_group_x(const uint8_t *g, const uint32_t (&off)[kGroupChunks],
-                                            uint8_t *st, const OpDesc &op, int kk, int lane) {
-    const uint32_t l0 = __builtin_amdgcn_readfirstlane(lds_addr(st));
-#pragma unroll
-    for (int i = 0; i < kGroupChunks; ++i) dma16_s(g, off[i], l0 + kWave * 16 * i);
-    dma16_v(x_slice_src<RS>(op, kk, lane), l0 + kStageW);
-}
-
 // ---------------------------------------------------------------- m = 1
 // One group (8 blocks) of this lane's super-row, accumulated into acc.
 template <int RS>
@@ -114,6 +91,119 @@ __device__ __forceinline__ void group_dot(const uint32_t (&D)[68], const float4 
 #undef Q8_STEP
         flush_row<RS>(acc, slot, r, sub);
     }
+}
+
+// ---------------------------------------------------------------- m = 1, integer
+// The group's x slice (256 floats at xa, lane l holding floats 4l..4l+3, of
+// block l/8) becomes Q8_0 in place: 32 code bytes per block at xa + 32 b and
+// the eight binary16 scales, as floats, at xa + 256.  One wave, no barrier:
+// the wave's LDS reads and writes are performed in program order.
+__device__ __forceinline__ void quantize_slice(uint8_t *xa, int lane) {
+    const float4 v = reinterpret_cast<const float4 *>(xa)[lane];
+    float a = fmaxf(fmaxf(fabsf(v.x), fabsf(v.y)), fmaxf(fabsf(v.z), fabsf(v.w)));
+    a = fmaxf(a, __shfl_xor(a, 1, kWave));
+    a = fmaxf(a, __shfl_xor(a, 2, kWave));
+    a = fmaxf(a, __shfl_xor(a, 4, kWave));
+    const float d = xq_scale(a);
+    reinterpret_cast<uint32_t *>(xa)[lane] =
+        pack4(xq_code(v.x, d), xq_code(v.y, d), xq_code(v.z, d), xq_code(v.w, d));
+    if ((lane & 7) == 0) reinterpret_cast<float *>(xa + 256)[lane >> 3] = xq_f16_value(d);
+}
+
+// Block K (0..7) of a group with x as Q8_0: the integer dot of the 32 quant
+// pairs (eight v_dot4), times the two scales.  Quants of an even block start
+// 2 bytes into a dword and are realigned with v_alignbyte.
+template <int K>
+__device__ __forceinline__ float block_terms_xq(const uint32_t (&D)[68], const uint8_t *xa) {
+    constexpr int sb = K * kBlockBytes;
+    constexpr int qb = sb + 2;
+    const float dw = half_to_float(D[sb >> 2] >> ((sb & 3) * 8));
+    const uint4 x0 = reinterpret_cast<const uint4 *>(xa)[2 * K];
+    const uint4 x1 = reinterpret_cast<const uint4 *>(xa)[2 * K + 1];
+    const float dx = reinterpret_cast<const float *>(xa + 256)[K];
+    const uint32_t xw[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
+    int isum = 0;
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+        constexpr int w0 = qb >> 2;
+        uint32_t wq;
+        if constexpr ((qb & 3) == 0) wq = D[w0 + k];
+        else wq = __builtin_amdgcn_alignbyte(D[w0 + k + 1], D[w0 + k], qb & 3);
+        isum = __builtin_amdgcn_sdot4((int)wq, (int)xw[k], isum, false);
+    }
+    return (float)isum * (dw * dx);
+}
+
+template <int RS>
+__device__ __forceinline__ void group_dot_xq(const uint32_t (&D)[68], const uint8_t *xa,
+                                             const OpDesc &op, int kk, float (&acc)[kSlots][RS]) {
+    const int slot = kk & (kSlots - 1);
+    float sub = 0.f;
+    if constexpr (RS == 1) {
+        sub += block_terms_xq<0>(D, xa);
+        sub += block_terms_xq<1>(D, xa);
+        sub += block_terms_xq<2>(D, xa);
+        sub += block_terms_xq<3>(D, xa);
+        sub += block_terms_xq<4>(D, xa);
+        sub += block_terms_xq<5>(D, xa);
+        sub += block_terms_xq<6>(D, xa);
+        sub += block_terms_xq<7>(D, xa);
+        flush_row<1>(acc, slot, 0, sub);
+    } else {
+        const int bp = kk * kGroupBlocks;
+        int r = bp / op.nb;
+        int cb = bp - r * op.nb;
+#define Q8_STEP(K)                                                   \
+        sub += block_terms_xq<K>(D, xa);                             \
+        if (++cb == op.nb) { flush_row<RS>(acc, slot, r, sub); sub = 0.f; cb = 0; ++r; }
+        Q8_STEP(0) Q8_STEP(1) Q8_STEP(2) Q8_STEP(3)
+        Q8_STEP(4) Q8_STEP(5) Q8_STEP(6) Q8_STEP(7)
+#undef Q8_STEP
+        flush_row<RS>(acc, slot, r, sub);
+    }
+}
+
+// The same rows with x quantized to Q8_0 (the integer path, m = 1): each
+// lane quantizes the x blocks it needs itself and multiplies the codes.
+__device__ void tail_tile_xq(const OpDesc &op, uint32_t tile, int waves) {
+    const int lane = lane_id();
+    const int wave = wave_id();
+    const int64_t row = (int64_t)op.tail_row0 + (int64_t)tile * waves + wave;
+    if (row >= op.p) return;
+    const int nb = op.nb;
+    const uint8_t *wr = op.w + row * (int64_t)nb * kBlockBytes;
+    float acc = 0.f, sub = 0.f;
+    int cnt = 0;
+    for (int b = lane; b < nb; b += kWave) {
+        const float4 *xb = reinterpret_cast<const float4 *>(op.x + (int64_t)b * kQuants);
+        float4 xv[8];
+#pragma unroll
+        for (int k = 0; k < 8; ++k) xv[k] = xb[k];
+        float amax = 0.f;
+#pragma unroll
+        for (int k = 0; k < 8; ++k)
+            amax = fmaxf(amax, fmaxf(fmaxf(fabsf(xv[k].x), fabsf(xv[k].y)),
+                                     fmaxf(fabsf(xv[k].z), fabsf(xv[k].w))));
+        const float d = xq_scale(amax);
+        GHalf *blk = (GHalf *)(wr + (int64_t)b * kBlockBytes);
+        const float dw = half_to_float(blk[0]);
+        int isum = 0;
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+            const uint32_t lo = blk[1 + 2 * k], hi = blk[2 + 2 * k];
+            const int wq = (int)(lo | (hi << 16));
+            const int xq = (int)pack4(xq_code(xv[k].x, d), xq_code(xv[k].y, d), xq_code(xv[k].z, d),
+                                      xq_code(xv[k].w, d));
+            isum = __builtin_amdgcn_sdot4(wq, xq, isum, false);
+        }
+        sub = fmaf((float)isum, dw * xq_f16_value(d), sub);
+        if (++cnt == 8) { acc += sub; sub = 0.f; cnt = 0; }
+    }
+    acc += sub;
+#pragma unroll
+    for (int o = kWave / 2; o > 0; o >>= 1) acc += __shfl_xor(acc, o, kWave);
+    if (lane == 0) op.y[row] = acc;
+    __builtin_amdgcn_s_waitcnt(0);
 }
 
 // One workgroup tile of NW waves: NW/ks row tiles of 64 super-rows, each
@@ -164,7 +254,7 @@ __device__ __forceinline__ void slice_arrive(const OpDesc &op, int64_t row_tile,
         __hip_atomic_store(op.cnt + row_tile, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-template <int RS, int NW, int PF>
+template <int RS, int NW, int PF, bool XQ>
 __device__ void fast_tile(const OpDesc &op, uint32_t tile, uint8_t *stage) {
     const int lane = lane_id();
     const int wave = wave_id();
@@ -213,7 +303,13 @@ __device__ void fast_tile(const OpDesc &op, uint32_t tile, uint8_t *stage) {
             else wait_vm_asm<0>();
             read_group(cur, lane, D);
             if (PF == 1 && t + 1 < ng) issue(t + 1);
-            group_dot<RS>(D, reinterpret_cast<const float4 *>(cur + kStageW), op, g0 + ksl + ks * t, acc);
+            if constexpr (XQ) {
+                quantize_slice(cur + kStageW, lane);
+                group_dot_xq<RS>(D, cur + kStageW, op, g0 + ksl + ks * t, acc);
+            } else {
+                group_dot<RS>(D, reinterpret_cast<const float4 *>(cur + kStageW), op, g0 + ksl + ks * t,
+                              acc);
+            }
             if (PF == 2 && t + 2 < ng) issue(t + 2);   // into the stage just consumed
         }
     }
@@ -252,76 +348,116 @@ __device__ void fast_tile(const OpDesc &op, uint32_t tile, uint8_t *stage) {
     }
 }
 
-template <int NW, int PF>
+template <int NW, int PF, bool XQ>
 __device__ __forceinline__ void run_tile(const OpDesc &op, uint32_t t, uint8_t *stage) {
     if (t & kTailBit) {
-        tail_tile(op, t & ~kTailBit, NW);
+        if constexpr (XQ) tail_tile_xq(op, t & ~kTailBit, NW);
+        else tail_tile(op, t & ~kTailBit, NW);
         return;
     }
     switch (op.rs) {
-        case 1: fast_tile<1, NW, PF>(op, t, stage); break;
-        case 2: fast_tile<2, NW, PF>(op, t, stage); break;
-        case 4: fast_tile<4, NW, PF>(op, t, stage); break;
-        default: fast_tile<8, NW, PF>(op, t, stage); break;
+        case 1: fast_tile<1, NW, PF, XQ>(op, t, stage); break;
+        case 2: fast_tile<2, NW, PF, XQ>(op, t, stage); break;
+        case 4: fast_tile<4, NW, PF, XQ>(op, t, stage); break;
+        default: fast_tile<8, NW, PF, XQ>(op, t, stage); break;
     }
 }
 
-template <int NW, int PF>
+template <int NW, int PF, bool XQ>
 __global__ __launch_bounds__(NW * kWave) void k_q8_gemv(OpDesc op) {
     __shared__ __attribute__((aligned(16))) uint8_t stage[NW * kBufs * kStageBytes];
     uint32_t t = blockIdx.x;
     if (t >= (uint32_t)op.fast_tiles) t = (t - op.fast_tiles) | kTailBit;
-    run_tile<NW, PF>(op, t, stage);
+    run_tile<NW, PF, XQ>(op, t, stage);
 }
 
-template <int NW, int PF>
+template <int NW, int PF, bool XQ>
 __global__ __launch_bounds__(NW * kWave) void k_q8_gemv_fused(const OpDesc *__restrict__ ops,
                                                               const Tile *__restrict__ tiles) {
     __shared__ __attribute__((aligned(16))) uint8_t stage[NW * kBufs * kStageBytes];
     const Tile tl = tiles[blockIdx.x];
     const OpDesc op = ops[tl.op];
-    run_tile<NW, PF>(op, tl.tile, stage);
+    run_tile<NW, PF, XQ>(op, tl.tile, stage);
+}
+
+// x (n floats) -> n/32 Q8_0 blocks of 34 bytes: 32 lanes per block, eight
+// blocks per 256-thread workgroup.
+__global__ __launch_bounds__(256) void k_quantize_x(const float *x, uint8_t *xq, int64_t nb) {
+    const int64_t b = (int64_t)blockIdx.x * 8 + (threadIdx.x >> 5);
+    const int j = threadIdx.x & 31;
+    const bool live = b < nb;
+    const float v = live ? x[b * kQuants + j] : 0.f;
+    float a = fabsf(v);
+#pragma unroll
+    for (int o = 16; o > 0; o >>= 1) a = fmaxf(a, __shfl_xor(a, o, kWave));
+    if (!live) return;
+    const float d = xq_scale(a);
+    uint8_t *blk = xq + b * kBlockBytes;
+    blk[2 + j] = (uint8_t)(int8_t)xq_code(v, d);
+    if (j == 0) {
+        const uint16_t bits = xq_f16_bits(d);
+        blk[0] = (uint8_t)(bits & 0xff);
+        blk[1] = (uint8_t)(bits >> 8);
+    }
 }
 
 }  // namespace
 
 namespace {
-template <int NW, int PF>
+template <int NW, int PF, bool XQ>
 hipError_t launch_single_t(const OpDesc &op, int64_t grid, hipStream_t s) {
-    hipLaunchKernelGGL((k_q8_gemv<NW, PF>), dim3((unsigned)grid), dim3(NW * kWave), 0, s, op);
+    hipLaunchKernelGGL((k_q8_gemv<NW, PF, XQ>), dim3((unsigned)grid), dim3(NW * kWave), 0, s, op);
     return hipGetLastError();
 }
-template <int NW, int PF>
+template <int NW, int PF, bool XQ>
 hipError_t launch_fused_t(const OpDesc *d_ops, const Tile *d_tiles, int64_t grid, hipStream_t s) {
-    hipLaunchKernelGGL((k_q8_gemv_fused<NW, PF>), dim3((unsigned)grid), dim3(NW * kWave), 0, s,
+    hipLaunchKernelGGL((k_q8_gemv_fused<NW, PF, XQ>), dim3((unsigned)grid), dim3(NW * kWave), 0, s,
                        d_ops, d_tiles);
     return hipGetLastError();
 }
-}  // namespace
-
-hipError_t launch_gemv_single(const OpDesc &op, const Variant &v, int64_t grid, hipStream_t s) {
+template <bool XQ>
+hipError_t launch_single_v(const OpDesc &op, const Variant &v, int64_t grid, hipStream_t s) {
     switch (v.nw * 10 + v.pf) {
-        case 11: return launch_single_t<1, 1>(op, grid, s);
-        case 12: return launch_single_t<1, 2>(op, grid, s);
-        case 21: return launch_single_t<2, 1>(op, grid, s);
-        case 22: return launch_single_t<2, 2>(op, grid, s);
-        case 41: return launch_single_t<4, 1>(op, grid, s);
-        case 42: return launch_single_t<4, 2>(op, grid, s);
+        case 11: return launch_single_t<1, 1, XQ>(op, grid, s);
+        case 12: return launch_single_t<1, 2, XQ>(op, grid, s);
+        case 21: return launch_single_t<2, 1, XQ>(op, grid, s);
+        case 22: return launch_single_t<2, 2, XQ>(op, grid, s);
+        case 41: return launch_single_t<4, 1, XQ>(op, grid, s);
+        case 42: return launch_single_t<4, 2, XQ>(op, grid, s);
         default: return hipErrorInvalidValue;
     }
 }
-
-hipError_t launch_gemv_fused(const OpDesc *d_ops, const Tile *d_tiles, const Variant &v,
-                             int64_t grid, hipStream_t s) {
+template <bool XQ>
+hipError_t launch_fused_v(const OpDesc *d_ops, const Tile *d_tiles, const Variant &v, int64_t grid,
+                          hipStream_t s) {
     switch (v.nw * 10 + v.pf) {
-        case 11: return launch_fused_t<1, 1>(d_ops, d_tiles, grid, s);
-        case 12: return launch_fused_t<1, 2>(d_ops, d_tiles, grid, s);
-        case 21: return launch_fused_t<2, 1>(d_ops, d_tiles, grid, s);
-        case 22: return launch_fused_t<2, 2>(d_ops, d_tiles, grid, s);
-        case 41: return launch_fused_t<4, 1>(d_ops, d_tiles, grid, s);
-        case 42: return launch_fused_t<4, 2>(d_ops, d_tiles, grid, s);
+        case 11: return launch_fused_t<1, 1, XQ>(d_ops, d_tiles, grid, s);
+        case 12: return launch_fused_t<1, 2, XQ>(d_ops, d_tiles, grid, s);
+        case 21: return launch_fused_t<2, 1, XQ>(d_ops, d_tiles, grid, s);
+        case 22: return launch_fused_t<2, 2, XQ>(d_ops, d_tiles, grid, s);
+        case 41: return launch_fused_t<4, 1, XQ>(d_ops, d_tiles, grid, s);
+        case 42: return launch_fused_t<4, 2, XQ>(d_ops, d_tiles, grid, s);
         default: return hipErrorInvalidValue;
     }
+}
+}  // namespace
+
+hipError_t launch_gemv_single(const OpDesc &op, const Variant &v, int64_t grid, hipStream_t s,
+                              bool xq) {
+    return xq ? launch_single_v<true>(op, v, grid, s) : launch_single_v<false>(op, v, grid, s);
+}
+
+hipError_t launch_gemv_fused(const OpDesc *d_ops, const Tile *d_tiles, const Variant &v,
+                             int64_t grid, hipStream_t s, bool xq) {
+    return xq ? launch_fused_v<true>(d_ops, d_tiles, v, grid, s)
+              : launch_fused_v<false>(d_ops, d_tiles, v, grid, s);
+}
+
+hipError_t launch_quantize_x(const float *x, void *xq, int64_t n, hipStream_t s) {
+    const int64_t nb = n / kQuants;
+    hipLaunchKernelGGL(k_quantize_x, dim3((unsigned)((nb + 7) / 8)), dim3(256), 0, s, x,
+                       (uint8_t *)xq, nb);
+    return hipGetLastError();
 }
 
 }  // namespace q8

@@ -91,9 +91,13 @@ inline int64_t tail_tiles_for(int64_t tail_rows, int nw = kWaves) {
     return (tail_rows + nw - 1) / nw;
 }
 
-// Matvec launchers (q8_gemv.hip).  Both return the hipError_t of the launch.
-hipError_t launch_gemv_single(const OpDesc &op, const Variant &v, int64_t grid, hipStream_t s);
+// Matvec launchers (q8_gemv.hip).  All return the hipError_t of the launch.
+// xq: x is quantized to Q8_0 on the fly and the products are integer dots.
+hipError_t launch_gemv_single(const OpDesc &op, const Variant &v, int64_t grid, hipStream_t s,
+                              bool xq = false);
 hipError_t launch_gemv_fused(const OpDesc *d_ops, const Tile *d_tiles, const Variant &v,
-                             int64_t grid, hipStream_t s);
+                             int64_t grid, hipStream_t s, bool xq = false);
+// x (n floats, n % 32 == 0) -> n/32 Q8_0 blocks of 34 bytes at xq.
+hipError_t launch_quantize_x(const float *x, void *xq, int64_t n, hipStream_t s);
 
 }  // namespace q8

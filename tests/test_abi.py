@@ -74,6 +74,22 @@ def test_gemv_validation(q8, args, code):
     assert q8.last_error() != ""
 
 
+@pytest.mark.parametrize("args,code", [
+    ((0, W, Y, 64, 4), -1), ((X, W, Y, 33, 4), -2), ((X, W, Y, 64, 0), -2),
+    ((X, W + 8, Y, 64, 4), -3), ((X, W, X + 16, 64, 4), -4),
+])
+def test_gemv_q8q8_validation(q8, args, code):
+    assert q8.lib.q8_0_gemv_q8q8(*args, None) == code
+
+
+@pytest.mark.parametrize("args,code", [
+    ((0, Y, 64), -1), ((X, 0, 64), -1), ((X, Y, 0), -2), ((X, Y, 48), -2),
+    ((X, Y, (1 << 31) + 32), -2), ((X + 2, Y, 64), -3), ((X, X + 100, 64), -4),
+])
+def test_quantize_validation(q8, args, code):
+    assert q8.lib.q8_0_quantize(*args, None) == code
+
+
 @pytest.mark.parametrize("m,code", [(0, -2), (17, -2), (-1, -2)])
 def test_gemm_validation(q8, m, code):
     assert q8.gemm_smallm_raw(X, W, Y, m, 64, 4) == code
@@ -91,7 +107,7 @@ def test_chain_validation(q8):
     assert h.value is None
     assert "op 1" in q8.last_error()
     assert q8.lib.q8_0_chain_create(ops, 0, 0, ctypes.byref(h)) == -1
-    assert q8.lib.q8_0_chain_create(ops, 1, 7, ctypes.byref(h)) == -1
+    assert q8.lib.q8_0_chain_create(ops, 1, 8, ctypes.byref(h)) == -1
     assert q8.lib.q8_0_chain_create(None, 1, 0, ctypes.byref(h)) == -1
     assert q8.lib.q8_0_decode_chain(None, 0, None) == -1
     assert q8.lib.q8_0_chain_launches(None) == -1
