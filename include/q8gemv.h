@@ -45,6 +45,11 @@
 
 #include <stdint.h>
 
+/* Only the entry points below are exported from libq8gemv.so. */
+#ifndef Q8_API
+#define Q8_API __attribute__((visibility("default")))
+#endif
+
 #ifdef __cplusplus
 extern "C" {
 #endif
@@ -76,7 +81,7 @@ enum q8_status {
  *   x : float32[n], device, 16-B aligned.   w : p * (n/32) * 34 bytes, device, 16-B aligned.
  *   y : float32[p], device, written.
  */
-int q8_0_gemv(const float *x, const void *w, float *y, int64_t n, int64_t p,
+Q8_API int q8_0_gemv(const float *x, const void *w, float *y, int64_t n, int64_t p,
               void *stream);
 
 /*
@@ -87,7 +92,7 @@ int q8_0_gemv(const float *x, const void *w, float *y, int64_t n, int64_t p,
  *   X : float32[m][n] row-major, device.   Y : float32[m][p] row-major, device.
  * Each Y[i] equals what q8_0_gemv gives for x = X[i] to the same accuracy.
  */
-int q8_0_gemm_smallm(const float *X, const void *w, float *Y, int64_t m,
+Q8_API int q8_0_gemm_smallm(const float *X, const void *w, float *Y, int64_t m,
                      int64_t n, int64_t p, void *stream);
 
 /*
@@ -133,7 +138,7 @@ typedef struct q8_0_chain q8_0_chain; /* opaque */
  * must not overlap in time (they share that table and their outputs).
  * On failure *out is set to NULL and nothing is leaked.
  */
-int q8_0_chain_create(const q8_0_op *ops, int64_t n_ops, uint32_t flags,
+Q8_API int q8_0_chain_create(const q8_0_op *ops, int64_t n_ops, uint32_t flags,
                       q8_0_chain **out);
 
 /*
@@ -149,7 +154,7 @@ int q8_0_chain_create(const q8_0_op *ops, int64_t n_ops, uint32_t flags,
  * are bit-identical to q8_0_quantize's; y is held to the same bar as
  * q8_0_gemv, against that integer definition.  Allocates nothing.
  */
-int q8_0_gemv_q8q8(const float *x, const void *w, float *y, int64_t n, int64_t p,
+Q8_API int q8_0_gemv_q8q8(const float *x, const void *w, float *y, int64_t n, int64_t p,
                    void *stream);
 
 /*
@@ -158,17 +163,17 @@ int q8_0_gemv_q8q8(const float *x, const void *w, float *y, int64_t n, int64_t p
  * needed; must not overlap x), by the rule above.  Exact: the bytes are
  * decided by float32 operations.
  */
-int q8_0_quantize(const float *x, void *xq, int64_t n, void *stream);
+Q8_API int q8_0_quantize(const float *x, void *xq, int64_t n, void *stream);
 
 /* Run one token's chain on `stream` in the given mode. */
-int q8_0_decode_chain(q8_0_chain *chain, int mode, void *stream);
+Q8_API int q8_0_decode_chain(q8_0_chain *chain, int mode, void *stream);
 
 /* Kernel launches one token costs (1 .. n_ops); negative status on a bad handle. */
-int q8_0_chain_launches(const q8_0_chain *chain);
+Q8_API int q8_0_chain_launches(const q8_0_chain *chain);
 
 /* Release the handle (NULL is accepted).  The caller must make sure no
  * replay is still running. */
-int q8_0_chain_destroy(q8_0_chain *chain);
+Q8_API int q8_0_chain_destroy(q8_0_chain *chain);
 
 /*
  * Wait until all work on `stream` has finished, for at most timeout_ms
@@ -176,13 +181,13 @@ int q8_0_chain_destroy(q8_0_chain *chain);
  * time runs out; the work itself is not cancelled.  A bounded wait with a
  * status check follows page "minfer Metal Backend Design", section 4.8.
  */
-int q8_0_stream_wait(void *stream, int64_t timeout_ms);
+Q8_API int q8_0_stream_wait(void *stream, int64_t timeout_ms);
 
 /* Static description of a status code. */
-const char *q8_0_status_string(int status);
+Q8_API const char *q8_0_status_string(int status);
 
 /* Detail of the last error raised on the calling thread ("" if none). */
-const char *q8_0_last_error(void);
+Q8_API const char *q8_0_last_error(void);
 
 #ifdef __cplusplus
 }

@@ -34,7 +34,7 @@ extern "C" {
  * The layer norms use rows = 1; the per-head q/k norms rows = heads,
  * dim = head_dim.  1 <= dim <= 65536, 1 <= rows <= 65536.
  */
-int q8_0_rms_norm(const float *x, const float *w, float *out, int64_t dim, int64_t rows,
+Q8_API int q8_0_rms_norm(const float *x, const float *w, float *out, int64_t dim, int64_t rows,
                   float eps, void *stream);
 
 /*
@@ -44,13 +44,13 @@ int q8_0_rms_norm(const float *x, const float *w, float *out, int64_t dim, int64
  * precision; the result rounds once to float).  head_dim even, <= 65536;
  * 0 <= pos < 2^31; theta > 0.
  */
-int q8_0_rope(float *x, int64_t head_dim, int64_t heads, int64_t pos, float theta, void *stream);
+Q8_API int q8_0_rope(float *x, int64_t head_dim, int64_t heads, int64_t pos, float theta, void *stream);
 
 /*
  * append_kv: row `pos` of the caches (kc, vc: rows of `width` floats, at
  * least pos + 1 rows) becomes k (resp. v).
  */
-int q8_0_append_kv(const float *k, const float *v, float *kc, float *vc, int64_t width,
+Q8_API int q8_0_append_kv(const float *k, const float *v, float *kc, float *vc, int64_t width,
                    int64_t pos, void *stream);
 
 /*
@@ -63,22 +63,22 @@ int q8_0_append_kv(const float *k, const float *v, float *kc, float *vc, int64_t
  * (device, stream), allocated on first use and grown when needed, like
  * q8_0_gemm_smallm.  Bitwise reproducible for the same inputs and shape.
  */
-int q8_0_attention_decode(const float *q, const float *kc, const float *vc, float *out,
+Q8_API int q8_0_attention_decode(const float *q, const float *kc, const float *vc, float *out,
                           int64_t seq, int64_t kv_width, int64_t head_dim, int64_t n_heads,
                           int64_t kv_group, void *stream);
 
 /* add_inplace: x[i] += y[i] for i < n. */
-int q8_0_add_inplace(float *x, const float *y, int64_t n, void *stream);
+Q8_API int q8_0_add_inplace(float *x, const float *y, int64_t n, void *stream);
 
 /* silu_hadamard: out[i] = gate[i] / (1 + e^-gate[i]) * up[i] for i < n. */
-int q8_0_silu_hadamard(const float *gate, const float *up, float *out, int64_t n, void *stream);
+Q8_API int q8_0_silu_hadamard(const float *gate, const float *up, float *out, int64_t n, void *stream);
 
 /*
  * argmax_row: *out (device uint32) = the index of the largest of x[0..n):
  * ties to the lowest index, NaN never wins, 0xFFFFFFFF if every value is
  * NaN.  Exact.  Uses a library workspace per (device, stream).
  */
-int q8_0_argmax(const float *x, int64_t n, uint32_t *out, void *stream);
+Q8_API int q8_0_argmax(const float *x, int64_t n, uint32_t *out, void *stream);
 
 /*
  * A whole decode step of a Qwen3-style model (section "One command buffer"):
@@ -121,10 +121,10 @@ typedef struct q8_0_step q8_0_step; /* opaque */
  * and must stay valid until q8_0_step_destroy.  The position starts at 0
  * and the token at 0.  max_seq <= Q8_MAX_SEQ.
  */
-int q8_0_step_create(const q8_0_model *m, q8_0_step **out);
+Q8_API int q8_0_step_create(const q8_0_model *m, q8_0_step **out);
 
 /* Set the position and the input token (ordered on `stream`). */
-int q8_0_step_reset(q8_0_step *s, int64_t pos, uint32_t token, void *stream);
+Q8_API int q8_0_step_reset(q8_0_step *s, int64_t pos, uint32_t token, void *stream);
 
 /*
  * One token on `stream`: mode Q8_MODE_GRAPH (replay the recording) or
@@ -133,10 +133,10 @@ int q8_0_step_reset(q8_0_step *s, int64_t pos, uint32_t token, void *stream);
  * token there and advances the position; refuses to run past max_seq (the
  * check uses the host's count of steps since the last reset).
  */
-int q8_0_step_run(q8_0_step *s, int mode, void *stream);
+Q8_API int q8_0_step_run(q8_0_step *s, int mode, void *stream);
 
 /* Kernel launches one token costs. */
-int q8_0_step_launches(const q8_0_step *s);
+Q8_API int q8_0_step_launches(const q8_0_step *s);
 
 /* Device buffers of the step, for reading results. */
 typedef struct q8_0_step_bufs {
@@ -146,9 +146,9 @@ typedef struct q8_0_step_bufs {
     const float *logits;     /* vocab */
     const float *k_cache, *v_cache;   /* n_layers x max_seq x kv_width each */
 } q8_0_step_bufs;
-int q8_0_step_buffers(const q8_0_step *s, q8_0_step_bufs *out);
+Q8_API int q8_0_step_buffers(const q8_0_step *s, q8_0_step_bufs *out);
 
-int q8_0_step_destroy(q8_0_step *s);
+Q8_API int q8_0_step_destroy(q8_0_step *s);
 
 #ifdef __cplusplus
 }

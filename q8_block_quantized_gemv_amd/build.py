@@ -19,6 +19,7 @@ HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 def hipcc_command(out: str, extra=()):
     return [HIPCC, "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",
+            "-fvisibility=hidden",
             "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
             "-Wall", "-Werror", "-Wno-unused-command-line-argument", "-Wno-inline-asm",
             "-I", os.path.join(ROOT, "include"), "-I", CSRC, *extra, *SOURCES, "-o", out]

@@ -40,6 +40,19 @@ def test_library_exports_every_declared_symbol(q8):
     assert set(declared_functions()) == set(q8.EXPORTS)
 
 
+def test_library_exports_nothing_else(q8):
+    """The shared library's exported functions are exactly the C ABI."""
+    import shutil
+    import subprocess
+    if shutil.which("nm") is None:
+        pytest.skip("nm is not installed")
+    out = subprocess.run(["nm", "-D", "--defined-only", q8.LIBRARY], capture_output=True,
+                         text=True, check=True).stdout
+    exported = {parts[2] for parts in (l.split() for l in out.splitlines())
+                if len(parts) == 3 and parts[1] == "T"}
+    assert exported == set(declared_functions())
+
+
 def test_status_strings(q8):
     for code in range(0, -9, -1):
         assert q8.lib.q8_0_status_string(code).decode() != "unknown status"
