@@ -131,12 +131,15 @@ def bench_smallm(args, q8, synth, torch, np):
 
 
 def bench_step(args, q8, synth, torch, np):
-    """A whole Qwen3-0.6B-shaped decode token (embedding, 28 layers of norms,
-    projections, rotary embedding, cache append, attention, SwiGLU, residual
-    adds, then the final norm, the lm_head and argmax) replayed from its
-    recorded hipGraph, greedy: each token feeds the next on the device.
-    Timed from two starting positions (a short and a 511-token context)."""
-    cfg, w = synth.step_model("qwen3_0.6b")
+    """A whole decode token of a Qwen3-style model (embedding, per layer the
+    norms, projections, rotary embedding, cache append, attention, SwiGLU and
+    residual adds, then the final norm, the lm_head and argmax) replayed from
+    its recorded hipGraph, greedy: each token feeds the next on the device.
+    Timed from two starting positions (a short and a 511-token context).
+    Also reports the matvec weight bytes a token streams, per second."""
+    cfg, w = synth.step_model(args.step_model)
+    wbytes = sum(synth.row_bytes(n) * p for _, n, p in synth.step_proj_shapes(cfg)) * cfg["n_layers"]
+    wbytes += synth.row_bytes(cfg["hidden"]) * cfg["vocab"]
     cfg["max_seq"] = args.step_max_seq
     shapes = dict((nm, (p, n)) for nm, n, p in synth.step_proj_shapes(cfg))
     dev = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to("cuda")
@@ -173,20 +176,22 @@ def bench_step(args, q8, synth, torch, np):
             t = timed(mode, args.steps)
             rec[name + "_us_per_token"] = round(t * 1e6, 2)
             rec[name + "_tokens_per_s"] = round(1.0 / t, 1)
+            rec[name + "_weight_GB_per_s"] = round(wbytes / t / 1e9, 1)
             say("step from pos %d, %s: %.1f us/token, %.0f tokens/s" % (pos0, name, t * 1e6, 1.0 / t))
         cases.append(rec)
     st.close()
     short = cases[0]
-    return {"metric": "Qwen3-0.6B-shaped greedy decode step (whole token, one hipGraph)",
+    return {"metric": "%s-shaped greedy decode step (whole token, one hipGraph)" % args.step_model,
             "value": short["graph_tokens_per_s"], "unit": "tokens/s", "n_gpus": 1,
             "steps": args.steps, "warmup": args.warmup,
             "ms_per_step": round(short["graph_us_per_token"] / 1e3, 5),
             "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
             "dtype": "f32", "data": "synthetic",
-            "config": {"workload": "qwen3_0.6b decode step", "launches_per_token": launches,
+            "config": {"workload": "%s decode step" % args.step_model, "launches_per_token": launches,
+                       "weight_bytes_per_token": wbytes,
                        "max_seq": cfg["max_seq"],
-                       "weights": "the qwen3_0.6b_chain projection bytes; f32 embedding N(0,1), "
-                                  "norm gains U[0.5,1.5]"},
+                       "weights": "the %s chain's projection bytes; f32 embedding N(0,1), "
+                                  "norm gains U[0.5,1.5]" % args.step_model},
             "cases": cases}
 
 
@@ -210,6 +215,7 @@ def main():
                     help="instead of the chain: time a whole Qwen3-0.6B-shaped decode token "
                          "(every kernel of the step, one hipGraph) from positions 0 and 511")
     ap.add_argument("--step-max-seq", type=int, default=2048)
+    ap.add_argument("--step-model", default="qwen3_0.6b", choices=("qwen3_0.6b", "7b"))
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="instead of the bench: copy MIB MiB device-to-device 5 times "
                          "(the known-size kernel that scales the HBM byte counters)")

@@ -192,19 +192,18 @@ int choose_ks(int64_t gsr, int64_t nsr, bool standalone, int nw) {
     return best;
 }
 
-// K slices across workgroups for an op whose row tiles alone give fewer than
-// kSplitTargetWaves waves: as many slices as that takes, at least one group
-// per wave (a slice holds a multiple of kSlots groups), at most kMaxSlices.
-constexpr int64_t kSplitTargetWaves = 1024;
-
-void plan_slices(OpDesc &d, int nw) {
-    const int64_t waves = fast_tiles_for(d.nsr, d.ks, nw) * nw;
-    if (waves == 0 || d.gsr <= kSlots) return;
-    const int64_t want = (kSplitTargetWaves + waves - 1) / waves;
-    int64_t S = std::min<int64_t>(want, std::min<int64_t>(kMaxSlices, (d.gsr + kSlots - 1) / kSlots));
+// K slices across workgroups (SPLIT_K chains): up to `target` slices, at
+// least one group each, at most kMaxSlices.  With one wave per row tile
+// (ks == 1) the wave owns all kSlots slots and any run of groups can be a
+// slice; with ks > 1 a slice holds a multiple of kSlots groups.
+void plan_slices(OpDesc &d, int64_t target) {
+    if (target <= 1 || d.gsr <= 1) return;
+    const bool any_run = d.ks == 1;
+    int64_t S = std::min<int64_t>(std::min<int64_t>(target, kMaxSlices), d.gsr);
+    if (!any_run) S = std::min<int64_t>(S, (d.gsr + kSlots - 1) / kSlots);
     if (S <= 1) return;
     int64_t per = (d.gsr + S - 1) / S;
-    per = (per + kSlots - 1) / kSlots * kSlots;
+    if (!any_run) per = (per + kSlots - 1) / kSlots * kSlots;
     S = (d.gsr + per - 1) / per;
     if (S <= 1) return;
     d.slices = (int32_t)S;
@@ -212,7 +211,7 @@ void plan_slices(OpDesc &d, int nw) {
 }
 
 OpDesc plan_op(const float *x, const void *w, float *y, int64_t m, int64_t n, int64_t p,
-               bool standalone, int nw = kWaves, bool split_k = false) {
+               bool standalone, int nw = kWaves, int64_t slices = 1) {
     OpDesc d;
     std::memset(&d, 0, sizeof d);
     const int64_t nb = n / kQuants;
@@ -229,7 +228,7 @@ OpDesc plan_op(const float *x, const void *w, float *y, int64_t m, int64_t n, in
     d.ks = choose_ks(d.gsr, d.nsr, standalone, nw);
     d.slices = 1;
     d.slice_groups = d.gsr;
-    if (split_k) plan_slices(d, nw);
+    plan_slices(d, slices);
     d.fast_tiles = (int32_t)fast_tiles_for(d.nsr, d.ks, nw, d.slices);
     d.tail_row0 = (int32_t)(d.nsr * rs);
     d.m = (int32_t)m;
@@ -534,24 +533,41 @@ int q8_0_chain_create(const q8_0_op *ops, int64_t n_ops, uint32_t flags, q8_0_ch
     // with SPLIT_K every op is planned like a standalone launch (four-wave
     // workgroups, groups split over the waves) and row-poor ops are split
     // across workgroups too, their partial sums in the same device block
-    // (a SPLIT_K launch with rows enough for kSplitTargetWaves one-wave row
-    // tiles, such as an lm_head, keeps the one-wave fused variant unsplit:
-    // its waves stream several groups each and many workgroups share a CU)
+    // SPLIT_K (ops that wait on each other).  Measured on the decode step's
+    // shapes: while a launch's row tiles (64 super-rows) fit on the CUs, four-
+    // wave workgroups splitting a tile's groups in LDS, with K further sliced
+    // across workgroups until there is one workgroup per CU, are fastest (a
+    // workgroup's stages fill a CU's LDS); launches with more row tiles than
+    // CUs (an lm_head, a 7B gate|up) are fastest on unsplit one-wave tiles.
     const Variant v_single = pick_variant(false), v_fused = pick_variant(true);
+    const int64_t cus = cu_count(dev);
     std::vector<OpDesc> h_ops;
     std::vector<Tile> h_tiles;
     struct SegInfo { size_t op0, tile0; int64_t ntiles; bool fused; OpDesc single; Variant v; };
     std::vector<SegInfo> info;
     for (auto &sg : segs) {
         const bool fused = !per_op && (sg.second - sg.first > 1);
-        int64_t row_tiles = 0;
-        for (int64_t i = sg.first; i < sg.second; ++i)
-            row_tiles += (ops[i].p / (kGroupBlocks / gcd64(ops[i].n / kQuants, kGroupBlocks)) + kWave - 1) / kWave;
-        const bool seg_split = split && row_tiles < kSplitTargetWaves;
-        const bool big = split && !seg_split;
-        const Variant vf = seg_split ? v_single : v_fused;
-        const Variant vs = big ? v_fused : v_single;
-        SegInfo si{h_ops.size(), h_tiles.size(), 0, fused, OpDesc{}, fused ? vf : vs};
+        int64_t target = 1;
+        Variant v = fused ? v_fused : v_single;
+        if (split) {
+            int64_t row_tiles = 0;
+            for (int64_t i = sg.first; i < sg.second; ++i) {
+                const OpDesc d = plan_op(ops[i].x, ops[i].w, ops[i].y, 1, ops[i].n, ops[i].p, false, 1);
+                row_tiles += d.fast_tiles;
+            }
+            if (row_tiles > cus) {
+                v = Variant{1, 1};
+            } else {
+                v = Variant{kWaves, 1};
+                target = std::max<int64_t>(1, cus / std::max<int64_t>(1, row_tiles));
+            }
+            // A/B overrides: Q8GEMV_SPLIT_SLICES (slices per row tile), Q8GEMV_VARIANT
+            if (const int forced = env_int("Q8GEMV_SPLIT_SLICES", 0); forced > 0) target = forced;
+            if (std::getenv("Q8GEMV_VARIANT")) v = v_single;
+        }
+        // four-wave split workgroups take the standalone K split inside the workgroup
+        const bool standalone = (!split && !fused) || (split && v.nw > 1);
+        SegInfo si{h_ops.size(), h_tiles.size(), 0, fused, OpDesc{}, v};
         if (fused) {
             // tiles sorted by decreasing weight bytes so that the smallest
             // tiles finish the launch (ties keep encode order)
@@ -559,15 +575,15 @@ int q8_0_chain_create(const q8_0_op *ops, int64_t n_ops, uint32_t flags, q8_0_ch
             std::vector<Item> items;
             for (int64_t i = sg.first; i < sg.second; ++i) {
                 const q8_0_op &o = ops[i];
-                OpDesc d = plan_op(o.x, o.w, o.y, 1, o.n, o.p, seg_split, vf.nw, seg_split);
+                OpDesc d = plan_op(o.x, o.w, o.y, 1, o.n, o.p, standalone, v.nw, target);
                 const uint32_t oi = (uint32_t)(h_ops.size() - si.op0);
                 h_ops.push_back(d);
-                const int64_t fb = (int64_t)(vf.nw / d.ks) * kWave *
+                const int64_t fb = (int64_t)(v.nw / d.ks) * kWave *
                                    (d.slices > 1 ? (int64_t)d.slice_groups * kGroupBytes : d.sr_bytes);
                 for (int64_t t = 0; t < d.fast_tiles; ++t) items.push_back({{oi, (uint32_t)t}, fb});
-                const int64_t tt = tail_tiles_for((int64_t)d.p - d.tail_row0, vf.nw);
+                const int64_t tt = tail_tiles_for((int64_t)d.p - d.tail_row0, v.nw);
                 for (int64_t t = 0; t < tt; ++t)
-                    items.push_back({{oi, (uint32_t)t | kTailBit}, (int64_t)vf.nw * d.nb * kBlockBytes});
+                    items.push_back({{oi, (uint32_t)t | kTailBit}, (int64_t)v.nw * d.nb * kBlockBytes});
             }
             std::stable_sort(items.begin(), items.end(),
                              [](const Item &a, const Item &b) { return a.bytes > b.bytes; });
@@ -575,7 +591,7 @@ int q8_0_chain_create(const q8_0_op *ops, int64_t n_ops, uint32_t flags, q8_0_ch
             si.ntiles = (int64_t)items.size();
         } else {
             const q8_0_op &o = ops[sg.first];
-            si.single = plan_op(o.x, o.w, o.y, 1, o.n, o.p, !big, vs.nw, seg_split);
+            si.single = plan_op(o.x, o.w, o.y, 1, o.n, o.p, standalone, v.nw, target);
         }
         info.push_back(si);
     }

@@ -211,6 +211,8 @@ __device__ void tail_tile_xq(const OpDesc &op, uint32_t tile, int waves) {
 // keeps in flight ahead of the one it computes (1 or 2; each stage holds one
 // group, and with PF = 2 the stage a group was computed from is refilled
 // right after that group's compute, so two groups stream while one waits).
+constexpr int kGatherBatch = 8;
+
 // With K slices (op.slices > 1) the ksl == 0 wave of each row tile parks
 // its rows' partial sums and counts in; the last slice to arrive adds the
 // slices in order.  The partials travel through device-scope stores and
@@ -237,16 +239,20 @@ __device__ __forceinline__ void slice_arrive(const OpDesc &op, int64_t row_tile,
     if (live) {
 #pragma unroll
         for (int k = 0; k < RS; ++k) {
-            float v[kMaxSlices];
+            float sum = 0.f;
+            for (int q0 = 0; q0 < op.slices; q0 += kGatherBatch) {   // loads eight at a time
+                float v[kGatherBatch];
 #pragma unroll
-            for (int q = 0; q < kMaxSlices; ++q)
-                v[q] = q < op.slices ? __hip_atomic_load(op.part + q * P + r0 + k, __ATOMIC_RELAXED,
-                                                         __HIP_MEMORY_SCOPE_AGENT)
-                                     : 0.f;
-            float sum = v[0];
+                for (int b = 0; b < kGatherBatch; ++b) {
+                    v[b] = 0.f;
+                    if (q0 + b < op.slices)
+                        v[b] = __hip_atomic_load(op.part + (q0 + b) * P + r0 + k, __ATOMIC_RELAXED,
+                                                 __HIP_MEMORY_SCOPE_AGENT);
+                }
 #pragma unroll
-            for (int q = 1; q < kMaxSlices; ++q)
-                if (q < op.slices) sum += v[q];
+                for (int b = 0; b < kGatherBatch; ++b)
+                    if (q0 + b < op.slices) sum += v[b];
+            }
             op.y[r0 + k] = sum;
         }
     }
@@ -279,7 +285,7 @@ __device__ void fast_tile(const OpDesc &op, uint32_t tile, uint8_t *stage) {
     if (sr0 < nsr) {
         const int G = op.gsr;
         const int64_t srb = op.sr_bytes;
-        const uint8_t *wt = op.w + sr0 * srb;
+        const uint8_t *wt = uniform_ptr(op.w + sr0 * srb);   // the direct loads' scalar base
         const int last = (int)min((int64_t)nsr - 1 - sr0, (int64_t)kWave - 1);
         uint32_t off[kGroupChunks];
         chunk_offsets(off, lane, last, srb);

@@ -62,7 +62,7 @@ struct OpDesc {
     float *part;         // slices * nsr * rs floats
     uint32_t *cnt;       // one per row tile of 64 super-rows, zero between launches
 };
-constexpr int kMaxSlices = 16;
+constexpr int kMaxSlices = 32;
 // Every row sums its groups into kSlots partial sums (group kk into slot
 // kk % kSlots) and combines them in a fixed tree at the end.
 constexpr int kSlots = 4;

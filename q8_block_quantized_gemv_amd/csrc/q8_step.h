@@ -57,7 +57,7 @@ hipError_t launch_attention_fused(const AttnDesc &d, const AttnFuse &f, hipStrea
 hipError_t launch_add(float *x, const float *y, int n, hipStream_t s);
 hipError_t launch_silu(const float *g, const float *u, float *out, int n, hipStream_t s);
 hipError_t launch_argmax(const ArgmaxDesc &d, int wgs, hipStream_t s);
-// x += y, then xn = rms_norm(x) * w (one wave; dim % 4 == 0, 16-byte aligned)
+// x += y, then xn = rms_norm(x) * w (one workgroup; dim % 4 == 0, 16-byte aligned)
 hipError_t launch_add_rms(float *x, const float *y, const float *w, float *xn, int dim, float eps,
                           hipStream_t s);
 // x = row *token of table (zeros if *token >= vocab), then xn = rms_norm(x) * w

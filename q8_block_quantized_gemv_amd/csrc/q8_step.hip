@@ -162,7 +162,8 @@ __global__ __launch_bounds__(kThreads) void k_rms_norm(const float *x, const flo
 // ---------------------------------------------------------------- fused residual + norm
 // EMBED: x = row `token` of the table y (zeros past the table: a row of only
 // NaN logits has no argmax); else x += y.  Then xn = rms_norm(x) * w.
-// One wave; dim % 4 == 0 and x, y, w, xn 16-byte aligned.
+// One 256-thread workgroup (four float4 per thread in flight for rows up to
+// 4096); dim % 4 == 0 and x, y, w, xn 16-byte aligned.
 template <bool EMBED>
 __device__ __forceinline__ float4 residual4(const float4 *x4, const float4 *src, bool zero, int i) {
     if (EMBED) return zero ? make_float4(0.f, 0.f, 0.f, 0.f) : src[i];
@@ -171,11 +172,15 @@ __device__ __forceinline__ float4 residual4(const float4 *x4, const float4 *src,
 }
 
 template <bool EMBED>
-__global__ __launch_bounds__(kWave) void k_add_rms(float *x, const float *y, const uint32_t *token,
-                                                   uint32_t vocab, const float *w, float *xn,
-                                                   int dim, float eps) {
-    const int lane = lane_id(), nv = dim / 4;
+__global__ __launch_bounds__(kThreads) void k_add_rms(float *x, const float *y, const uint32_t *token,
+                                                      uint32_t vocab, const float *w, float *xn,
+                                                      int dim, float eps) {
+    constexpr int R = 4;   // float4 a thread holds: rows up to kThreads * R * 4 = 4096 floats
+    __shared__ float red[kWaves];
+    const int tid = threadIdx.x, lane = tid & (kWave - 1), wv = tid / kWave;
+    const int nv = dim / 4;
     float4 *x4 = (float4 *)x;
+    const float4 *w4 = (const float4 *)w;
     const float4 *src = (const float4 *)y;
     bool zero = false;
     if (EMBED) {
@@ -183,54 +188,75 @@ __global__ __launch_bounds__(kWave) void k_add_rms(float *x, const float *y, con
         zero = t >= vocab;
         src = (const float4 *)(y + (int64_t)(zero ? 0u : t) * dim);
     }
-    if (nv <= kWave * kNormRegs) {   // the row stays in registers
-        float4 xv[kNormRegs];
+    const float4 z4 = make_float4(0.f, 0.f, 0.f, 0.f);
+    if (nv <= kThreads * R) {   // the row stays in registers
+        float4 xv[R], wq[R];
 #pragma unroll
-        for (int e = 0; e < kNormRegs; ++e) {
-            const int i = lane + kWave * e;
-            xv[e] = i < nv ? residual4<EMBED>(x4, src, zero, i) : make_float4(0.f, 0.f, 0.f, 0.f);
-        }
-#pragma unroll
-        for (int e = 0; e < kNormRegs; ++e) {
-            const int i = lane + kWave * e;
-            if (i < nv) x4[i] = xv[e];
+        for (int e = 0; e < R; ++e) {
+            const int i = tid + kThreads * e;
+            xv[e] = z4;
+            wq[e] = z4;
+            if (i < nv) {
+                xv[e] = residual4<EMBED>(x4, src, zero, i);
+                wq[e] = w4[i];
+            }
         }
         float ss = 0.f;
 #pragma unroll
-        for (int e = 0; e < kNormRegs; ++e) ss = sq4(xv[e], ss);
-        store_row4((float4 *)xn, (const float4 *)w, nv, rms_inv(wave_sum(ss), dim, eps), xv);
+        for (int e = 0; e < R; ++e) {
+            const int i = tid + kThreads * e;
+            if (i < nv) x4[i] = xv[e];
+            ss = sq4(xv[e], ss);
+        }
+        ss = wave_sum(ss);
+        if (lane == 0) red[wv] = ss;
+        __syncthreads();
+        const float inv = rms_inv((red[0] + red[1]) + (red[2] + red[3]), dim, eps);
+#pragma unroll
+        for (int e = 0; e < R; ++e) {
+            const int i = tid + kThreads * e;
+            if (i < nv) ((float4 *)xn)[i] = scale4(xv[e], inv, wq[e]);
+        }
         return;
     }
-    // long rows: write x batch by batch, then normalise it (each lane re-reads
-    // only what it wrote itself)
+    // long rows: write x batch by batch, then normalise it (each thread
+    // re-reads only what it wrote itself)
     float ss = 0.f;
-    for (int b = 0; b < nv; b += kWave * kNormRegs) {
-        float4 xv[kNormRegs];
+    for (int b = 0; b < nv; b += kThreads * R) {
+        float4 xv[R];
 #pragma unroll
-        for (int e = 0; e < kNormRegs; ++e) {
-            const int i = b + lane + kWave * e;
-            xv[e] = i < nv ? residual4<EMBED>(x4, src, zero, i) : make_float4(0.f, 0.f, 0.f, 0.f);
+        for (int e = 0; e < R; ++e) {
+            const int i = b + tid + kThreads * e;
+            xv[e] = z4;
+            if (i < nv) xv[e] = residual4<EMBED>(x4, src, zero, i);
         }
 #pragma unroll
-        for (int e = 0; e < kNormRegs; ++e) {
-            const int i = b + lane + kWave * e;
+        for (int e = 0; e < R; ++e) {
+            const int i = b + tid + kThreads * e;
             if (i < nv) x4[i] = xv[e];
             ss = sq4(xv[e], ss);
         }
     }
-    const float inv = rms_inv(wave_sum(ss), dim, eps);
-    for (int b = 0; b < nv; b += kWave * kNormRegs) {
-        float4 xv[kNormRegs], wv[kNormRegs];
+    ss = wave_sum(ss);
+    if (lane == 0) red[wv] = ss;
+    __syncthreads();
+    const float inv = rms_inv((red[0] + red[1]) + (red[2] + red[3]), dim, eps);
+    for (int b = 0; b < nv; b += kThreads * R) {
+        float4 xv[R], wq[R];
 #pragma unroll
-        for (int e = 0; e < kNormRegs; ++e) {
-            const int i = b + lane + kWave * e;
-            xv[e] = i < nv ? x4[i] : make_float4(0.f, 0.f, 0.f, 0.f);
-            wv[e] = i < nv ? ((const float4 *)w)[i] : make_float4(0.f, 0.f, 0.f, 0.f);
+        for (int e = 0; e < R; ++e) {
+            const int i = b + tid + kThreads * e;
+            xv[e] = z4;
+            wq[e] = z4;
+            if (i < nv) {
+                xv[e] = x4[i];
+                wq[e] = w4[i];
+            }
         }
 #pragma unroll
-        for (int e = 0; e < kNormRegs; ++e) {
-            const int i = b + lane + kWave * e;
-            if (i < nv) ((float4 *)xn)[i] = scale4(xv[e], inv, wv[e]);
+        for (int e = 0; e < R; ++e) {
+            const int i = b + tid + kThreads * e;
+            if (i < nv) ((float4 *)xn)[i] = scale4(xv[e], inv, wq[e]);
         }
     }
 }
@@ -645,14 +671,14 @@ hipError_t launch_rms_norm(const float *x, const float *w, float *out, int dim, 
 
 hipError_t launch_add_rms(float *x, const float *y, const float *w, float *xn, int dim, float eps,
                           hipStream_t s) {
-    hipLaunchKernelGGL(k_add_rms<false>, dim3(1), dim3(kWave), 0, s, x, y, nullptr, 0u, w, xn, dim,
+    hipLaunchKernelGGL(k_add_rms<false>, dim3(1), dim3(kThreads), 0, s, x, y, nullptr, 0u, w, xn, dim,
                        eps);
     return hipGetLastError();
 }
 
 hipError_t launch_embed_rms(const float *table, const uint32_t *token, uint32_t vocab, float *x,
                             const float *w, float *xn, int dim, float eps, hipStream_t s) {
-    hipLaunchKernelGGL(k_add_rms<true>, dim3(1), dim3(kWave), 0, s, x, table, token, vocab, w, xn,
+    hipLaunchKernelGGL(k_add_rms<true>, dim3(1), dim3(kThreads), 0, s, x, table, token, vocab, w, xn,
                        dim, eps);
     return hipGetLastError();
 }

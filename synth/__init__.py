@@ -203,7 +203,8 @@ def generate_smallm(shape: OpShape, m: int):
 # ------------------------------------------------------------------ whole decode-step models
 # Qwen3-style decoders (the step of page "IV.4: One command buffer per token",
 # section "One command buffer").  "qwen3_0.6b" has Qwen3-0.6B's shape and the
-# very projection bytes of the qwen3_0.6b_chain workload; the small ones
+# very projection bytes of the qwen3_0.6b_chain workload, "7b" the 7B-class
+# shape (28 query heads on 4 KV heads of 128) and the 7b_chain bytes; the small ones
 # are test models: "step_tiny" (2 layers, head_dim 64, two query heads per
 # KV head), "step_gqa4" (head_dim 128, four query heads per KV head, an
 # intermediate width and a vocabulary that are not powers of two),
@@ -211,6 +212,8 @@ def generate_smallm(shape: OpShape, m: int):
 STEP_MODELS = {
     "qwen3_0.6b": dict(n_layers=28, hidden=1024, n_heads=16, n_kv_heads=8, head_dim=128,
                        inter=3072, vocab=151936, eps=1e-6, theta=1e6),
+    "7b": dict(n_layers=28, hidden=3584, n_heads=28, n_kv_heads=4, head_dim=128,
+               inter=18944, vocab=152064, eps=1e-6, theta=1e6),
     "step_tiny": dict(n_layers=2, hidden=256, n_heads=4, n_kv_heads=2, head_dim=64,
                       inter=512, vocab=1000, eps=1e-6, theta=1e6),
     "step_gqa4": dict(n_layers=1, hidden=512, n_heads=8, n_kv_heads=2, head_dim=128,
@@ -220,7 +223,8 @@ STEP_MODELS = {
     "step_hd256": dict(n_layers=2, hidden=512, n_heads=4, n_kv_heads=2, head_dim=256,
                        inter=768, vocab=700, eps=1e-6, theta=1e6),
 }
-STEP_SEED = {"qwen3_0.6b": WORKLOAD_ID["qwen3_0.6b_chain"], "step_tiny": WORKLOAD_ID["step_tiny"],
+STEP_SEED = {"qwen3_0.6b": WORKLOAD_ID["qwen3_0.6b_chain"], "7b": WORKLOAD_ID["7b_chain"],
+             "step_tiny": WORKLOAD_ID["step_tiny"],
              "step_gqa4": WORKLOAD_ID["step_gqa4"], "step_hd192": WORKLOAD_ID["step_hd192"],
              "step_hd256": WORKLOAD_ID["step_hd256"]}
 PROJ = ("wq", "wk", "wv", "wo", "wgate", "wup", "wdown")
