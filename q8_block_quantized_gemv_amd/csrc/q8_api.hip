@@ -245,7 +245,7 @@ int gemv_launch(const float *x, const void *w, float *y, int64_t n, int64_t p, h
                 bool xq = false) {
     const Variant v = pick_variant(false);
     const OpDesc d = plan_op(x, w, y, 1, n, p, true, v.nw);
-    hipError_t e = launch_gemv_single(d, v, tiles_of(d, v.nw), s, xq);
+    hipError_t e = launch_gemv_single(d, v, tiles_of(d, v.nw), s, xq ? kXQuant : kXFloat);
     if (e != hipSuccess) return fail_hip(e, xq ? "q8_0_gemv_q8q8 launch" : "q8_0_gemv launch");
     return Q8_OK;
 }
@@ -442,7 +442,7 @@ struct q8_0_chain {
     // one entry per kernel launch of a token
     struct Launch {
         bool fused;
-        bool xq;              // x quantized to Q8_0, integer products
+        int xmode;            // XMode: how the activations are read
         Variant v;
         OpDesc single;        // per-op launch
         const OpDesc *d_ops;  // fused launch
@@ -459,8 +459,8 @@ struct q8_0_chain {
 namespace {
 
 hipError_t issue(const q8_0_chain::Launch &L, hipStream_t s) {
-    if (L.fused) return launch_gemv_fused(L.d_ops, L.d_tiles, L.v, L.grid, s, L.xq);
-    return launch_gemv_single(L.single, L.v, L.grid, s, L.xq);
+    if (L.fused) return launch_gemv_fused(L.d_ops, L.d_tiles, L.v, L.grid, s, L.xmode);
+    return launch_gemv_single(L.single, L.v, L.grid, s, L.xmode);
 }
 
 void chain_free(q8_0_chain *c) {
@@ -474,11 +474,14 @@ void chain_free(q8_0_chain *c) {
 
 // Does op b have to wait for op a (a earlier)?  Any write of one that
 // touches memory the other reads or writes.
-bool depends(const q8_0_op &a, const q8_0_op &b) {
+// (ua, ub: the ops' second activation input in the SiLU·up mode, or null)
+bool depends(const q8_0_op &a, const q8_0_op &b, const float *ua = nullptr,
+             const float *ub = nullptr) {
     const int64_t ya = 4 * a.p, yb = 4 * b.p;
     return overlaps(b.y, yb, a.y, ya) || overlaps(b.y, yb, a.x, 4 * a.n) ||
            overlaps(b.y, yb, a.w, w_bytes(a.n, a.p)) || overlaps(b.x, 4 * b.n, a.y, ya) ||
-           overlaps(b.w, w_bytes(b.n, b.p), a.y, ya);
+           overlaps(b.w, w_bytes(b.n, b.p), a.y, ya) || (ua && overlaps(b.y, yb, ua, 4 * a.n)) ||
+           (ub && overlaps(ub, 4 * b.n, a.y, ya));
 }
 
 }  // namespace
@@ -494,16 +497,28 @@ int q8::chain_issue(const q8_0_chain *c, hipStream_t s) {
 extern "C" {
 
 int q8_0_chain_create(const q8_0_op *ops, int64_t n_ops, uint32_t flags, q8_0_chain **out) {
+    return q8::chain_create_ex(ops, n_ops, flags, nullptr, out);
+}
+
+}  // extern "C"
+
+int q8::chain_create_ex(const q8_0_op *ops, int64_t n_ops, uint32_t flags,
+                        const float *const *x_up, q8_0_chain **out) {
     if (!out) return fail(Q8_ERR_INVALID_ARG, "q8_0_chain_create: out is null");
     *out = nullptr;
     if (!ops || n_ops <= 0 || n_ops > Q8_MAX_CHAIN_OPS)
         return fail(Q8_ERR_INVALID_ARG, "q8_0_chain_create: need 1..65535 ops");
     if (flags & ~(uint32_t)(Q8_CHAIN_PER_OP | Q8_CHAIN_SPLIT_K | Q8_CHAIN_XQ))
         return fail(Q8_ERR_INVALID_ARG, "q8_0_chain_create: unknown flags");
+    if (x_up && (flags & Q8_CHAIN_XQ))
+        return fail(Q8_ERR_INVALID_ARG, "q8_0_chain_create: the SiLU·up input has no integer form");
     for (int64_t i = 0; i < n_ops; ++i) {
         const std::string what = "q8_0_chain_create op " + std::to_string(i);
         int rc = validate(ops[i].x, ops[i].w, ops[i].y, 1, ops[i].n, ops[i].p, what.c_str());
         if (rc) return rc;
+        if (x_up && (!x_up[i] || ((uintptr_t)x_up[i] & 15u) ||
+                     overlaps(ops[i].y, 4 * ops[i].p, x_up[i], 4 * ops[i].n)))
+            return fail(Q8_ERR_INVALID_ARG, what + ": up input null, not 16-byte aligned or aliased");
     }
     int dev = 0;
     int rc = check_device(&dev);
@@ -524,7 +539,8 @@ int q8_0_chain_create(const q8_0_op *ops, int64_t n_ops, uint32_t flags, q8_0_ch
         int64_t b = 0;
         for (int64_t i = 1; i <= n_ops; ++i) {
             bool cut = (i == n_ops);
-            for (int64_t j = b; !cut && j < i; ++j) cut = depends(ops[j], ops[i]);
+            for (int64_t j = b; !cut && j < i; ++j)
+                cut = depends(ops[j], ops[i], x_up ? x_up[j] : nullptr, x_up ? x_up[i] : nullptr);
             if (cut) { segs.push_back({b, i}); b = i; }
         }
     }
@@ -576,6 +592,7 @@ int q8_0_chain_create(const q8_0_op *ops, int64_t n_ops, uint32_t flags, q8_0_ch
             for (int64_t i = sg.first; i < sg.second; ++i) {
                 const q8_0_op &o = ops[i];
                 OpDesc d = plan_op(o.x, o.w, o.y, 1, o.n, o.p, standalone, v.nw, target);
+                d.x_up = x_up ? x_up[i] : nullptr;
                 const uint32_t oi = (uint32_t)(h_ops.size() - si.op0);
                 h_ops.push_back(d);
                 const int64_t fb = (int64_t)(v.nw / d.ks) * kWave *
@@ -592,6 +609,7 @@ int q8_0_chain_create(const q8_0_op *ops, int64_t n_ops, uint32_t flags, q8_0_ch
         } else {
             const q8_0_op &o = ops[sg.first];
             si.single = plan_op(o.x, o.w, o.y, 1, o.n, o.p, standalone, v.nw, target);
+            si.single.x_up = x_up ? x_up[sg.first] : nullptr;
         }
         info.push_back(si);
     }
@@ -634,7 +652,7 @@ int q8_0_chain_create(const q8_0_op *ops, int64_t n_ops, uint32_t flags, q8_0_ch
     for (size_t k = 0; k < segs.size(); ++k) {
         q8_0_chain::Launch L;
         std::memset(&L, 0, sizeof L);
-        L.xq = (flags & Q8_CHAIN_XQ) != 0;
+        L.xmode = x_up ? kXSiluUp : (flags & Q8_CHAIN_XQ) ? kXQuant : kXFloat;
         if (info[k].fused) {
             L.fused = true;
             L.v = info[k].v;
@@ -670,6 +688,8 @@ int q8_0_chain_create(const q8_0_op *ops, int64_t n_ops, uint32_t flags, q8_0_ch
     *out = c;
     return Q8_OK;
 }
+
+extern "C" {
 
 int q8_0_decode_chain(q8_0_chain *c, int mode, void *stream) {
     if (!c) return fail(Q8_ERR_INVALID_ARG, "q8_0_decode_chain: null chain");

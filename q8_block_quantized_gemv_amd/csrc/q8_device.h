@@ -107,10 +107,11 @@ constexpr int kLoadsPerGroup = kGroupChunks + 1;
 // 4*(lane%8) .. +3 of block lane/8 of the group, i.e. of column block
 // (8*kk + lane/8) mod nb (a group of a super-row wraps past the row end).
 template <int RS>
-__device__ __forceinline__ const float *x_slice_src(const OpDesc &op, int kk, int lane) {
+__device__ __forceinline__ const float *x_slice_src(const OpDesc &op, const float *base, int kk,
+                                                    int lane) {
     int b = kk * kGroupBlocks + (lane >> 3);
     if (RS > 1) b %= op.nb;
-    return op.x + (int64_t)b * kQuants + 4 * (lane & 7);
+    return base + (int64_t)b * kQuants + 4 * (lane & 7);
 }
 
 // One group: 17 loads of W and one load of its x slice (at st + kStageW).
@@ -120,8 +121,11 @@ __device__ __forceinline__ void dma_group_x(const uint8_t *g, const uint32_t (&o
     const uint32_t l0 = __builtin_amdgcn_readfirstlane(lds_addr(st));
 #pragma unroll
     for (int i = 0; i < kGroupChunks; ++i) dma16_s(g, off[i], l0 + kWave * 16 * i);
-    dma16_v(x_slice_src<RS>(op, kk, lane), l0 + kStageW);
+    dma16_v(x_slice_src<RS>(op, op.x, kk, lane), l0 + kStageW);
 }
+
+// The SwiGLU product, as the step's silu_hadamard kernel computes it.
+__device__ __forceinline__ float silu_up(float g, float u) { return (g / (1.0f + expf(-g))) * u; }
 
 // acc[slot][r] += v for a uniform slot and row index (unrolled selects).
 template <int RS>
@@ -161,6 +165,7 @@ __device__ __forceinline__ uint32_t pack4(int a, int b, int c, int d) {
 // blocks l, l+64, ...; blocks are read with 2-byte loads (a block is only
 // 2-byte aligned in general).  Per-lane sums are flushed every 8 blocks and
 // the 64 lanes meet in a fixed butterfly.
+template <bool SILU = false>
 __device__ void tail_tile(const OpDesc &op, uint32_t tile, int waves) {
     const int lane = lane_id();
     const int wave = wave_id();
@@ -181,8 +186,14 @@ __device__ void tail_tile(const OpDesc &op, uint32_t tile, int waves) {
 #pragma unroll
             for (int j = 0; j < kQuants / 2; ++j) {
                 const uint32_t v = blk[1 + j];
-                a0 = fmaf((float)(int8_t)(v & 0xffu), xb[2 * j], a0);
-                a1 = fmaf((float)(int8_t)(v >> 8), xb[2 * j + 1], a1);
+                float x0 = xb[2 * j], x1 = xb[2 * j + 1];
+                if constexpr (SILU) {
+                    const float *ub = op.x_up + (int64_t)b * kQuants;
+                    x0 = silu_up(x0, ub[2 * j]);
+                    x1 = silu_up(x1, ub[2 * j + 1]);
+                }
+                a0 = fmaf((float)(int8_t)(v & 0xffu), x0, a0);
+                a1 = fmaf((float)(int8_t)(v >> 8), x1, a1);
             }
             sub = fmaf(d, a0 + a1, sub);
             if (++cnt == 8) { acc += sub; sub = 0.f; cnt = 0; }

@@ -260,8 +260,14 @@ __device__ __forceinline__ void slice_arrive(const OpDesc &op, int64_t row_tile,
         __hip_atomic_store(op.cnt + row_tile, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-template <int RS, int NW, int PF, bool XQ>
+// Bytes of one stage: W, the x slice and, for kXSiluUp, the up slice.
+template <int XM>
+constexpr int stage_bytes() { return kStageBytes + (XM == kXSiluUp ? kStageX : 0); }
+
+template <int RS, int NW, int PF, int XM>
 __device__ void fast_tile(const OpDesc &op, uint32_t tile, uint8_t *stage) {
+    constexpr int SB = stage_bytes<XM>();
+    constexpr int LPG = kLoadsPerGroup + (XM == kXSiluUp ? 1 : 0);   // direct loads per group
     const int lane = lane_id();
     const int wave = wave_id();
     const int ks = op.ks;
@@ -274,7 +280,7 @@ __device__ void fast_tile(const OpDesc &op, uint32_t tile, uint8_t *stage) {
     const int64_t row_tile = (int64_t)wtile * tiles_per_wg + rt;
     const int64_t sr0 = row_tile * kWave;
     const int nsr = op.nsr;
-    uint8_t *st0 = stage + (size_t)wave * (kBufs * kStageBytes);
+    uint8_t *st0 = stage + (size_t)wave * (kBufs * SB);
 
     float acc[kSlots][RS];
 #pragma unroll
@@ -296,23 +302,33 @@ __device__ void fast_tile(const OpDesc &op, uint32_t tile, uint8_t *stage) {
         const int ng = g1 - g0 > ksl ? (g1 - g0 - ksl + ks - 1) / ks : 0;
         auto issue = [&](int t) {
             const int kk = g0 + ksl + ks * t;
-            dma_group_x<RS>(wt + (int64_t)kk * kGroupBytes, off, st0 + (t & 1) * kStageBytes, op,
-                            kk, lane);
+            uint8_t *st = st0 + (t & 1) * SB;
+            dma_group_x<RS>(wt + (int64_t)kk * kGroupBytes, off, st, op, kk, lane);
+            if constexpr (XM == kXSiluUp)
+                dma16_v(x_slice_src<RS>(op, op.x_up, kk, lane),
+                        __builtin_amdgcn_readfirstlane(lds_addr(st)) + kStageBytes);
         };
         if (ng > 0) issue(0);
         if (PF == 2 && ng > 1) issue(1);
         for (int t = 0; t < ng; ++t) {
-            uint8_t *cur = st0 + (t & 1) * kStageBytes;
+            uint8_t *cur = st0 + (t & 1) * SB;
             uint32_t D[68];
             // this group's W and x have landed in LDS (loads complete in order)
-            if (PF == 2 && t + 1 < ng) wait_vm_asm<kLoadsPerGroup>();
+            if (PF == 2 && t + 1 < ng) wait_vm_asm<LPG>();
             else wait_vm_asm<0>();
             read_group(cur, lane, D);
             if (PF == 1 && t + 1 < ng) issue(t + 1);
-            if constexpr (XQ) {
+            if constexpr (XM == kXQuant) {
                 quantize_slice(cur + kStageW, lane);
                 group_dot_xq<RS>(D, cur + kStageW, op, g0 + ksl + ks * t, acc);
             } else {
+                if constexpr (XM == kXSiluUp) {   // the x slice becomes silu(gate) * up in place
+                    float4 *xs = reinterpret_cast<float4 *>(cur + kStageW);
+                    const float4 g = xs[lane];
+                    const float4 u = reinterpret_cast<const float4 *>(cur + kStageBytes)[lane];
+                    xs[lane] = make_float4(silu_up(g.x, u.x), silu_up(g.y, u.y), silu_up(g.z, u.z),
+                                           silu_up(g.w, u.w));
+                }
                 group_dot<RS>(D, reinterpret_cast<const float4 *>(cur + kStageW), op, g0 + ksl + ks * t,
                               acc);
             }
@@ -336,7 +352,7 @@ __device__ void fast_tile(const OpDesc &op, uint32_t tile, uint8_t *stage) {
             for (int q = 1; q < kSlots; ++q) {
                 const int owner = rt * ks + q % ks;
                 const float *theirs = reinterpret_cast<const float *>(
-                    stage + (size_t)owner * (kBufs * kStageBytes));
+                    stage + (size_t)owner * (kBufs * SB));
                 if (owner != wave)
 #pragma unroll
                     for (int k = 0; k < RS; ++k) acc[q][k] = theirs[((q / ks) * RS + k) * kWave + lane];
@@ -354,36 +370,36 @@ __device__ void fast_tile(const OpDesc &op, uint32_t tile, uint8_t *stage) {
     }
 }
 
-template <int NW, int PF, bool XQ>
+template <int NW, int PF, int XM>
 __device__ __forceinline__ void run_tile(const OpDesc &op, uint32_t t, uint8_t *stage) {
     if (t & kTailBit) {
-        if constexpr (XQ) tail_tile_xq(op, t & ~kTailBit, NW);
-        else tail_tile(op, t & ~kTailBit, NW);
+        if constexpr (XM == kXQuant) tail_tile_xq(op, t & ~kTailBit, NW);
+        else tail_tile<XM == kXSiluUp>(op, t & ~kTailBit, NW);
         return;
     }
     switch (op.rs) {
-        case 1: fast_tile<1, NW, PF, XQ>(op, t, stage); break;
-        case 2: fast_tile<2, NW, PF, XQ>(op, t, stage); break;
-        case 4: fast_tile<4, NW, PF, XQ>(op, t, stage); break;
-        default: fast_tile<8, NW, PF, XQ>(op, t, stage); break;
+        case 1: fast_tile<1, NW, PF, XM>(op, t, stage); break;
+        case 2: fast_tile<2, NW, PF, XM>(op, t, stage); break;
+        case 4: fast_tile<4, NW, PF, XM>(op, t, stage); break;
+        default: fast_tile<8, NW, PF, XM>(op, t, stage); break;
     }
 }
 
-template <int NW, int PF, bool XQ>
+template <int NW, int PF, int XM>
 __global__ __launch_bounds__(NW * kWave) void k_q8_gemv(OpDesc op) {
-    __shared__ __attribute__((aligned(16))) uint8_t stage[NW * kBufs * kStageBytes];
+    __shared__ __attribute__((aligned(16))) uint8_t stage[NW * kBufs * stage_bytes<XM>()];
     uint32_t t = blockIdx.x;
     if (t >= (uint32_t)op.fast_tiles) t = (t - op.fast_tiles) | kTailBit;
-    run_tile<NW, PF, XQ>(op, t, stage);
+    run_tile<NW, PF, XM>(op, t, stage);
 }
 
-template <int NW, int PF, bool XQ>
+template <int NW, int PF, int XM>
 __global__ __launch_bounds__(NW * kWave) void k_q8_gemv_fused(const OpDesc *__restrict__ ops,
                                                               const Tile *__restrict__ tiles) {
-    __shared__ __attribute__((aligned(16))) uint8_t stage[NW * kBufs * kStageBytes];
+    __shared__ __attribute__((aligned(16))) uint8_t stage[NW * kBufs * stage_bytes<XM>()];
     const Tile tl = tiles[blockIdx.x];
     const OpDesc op = ops[tl.op];
-    run_tile<NW, PF, XQ>(op, tl.tile, stage);
+    run_tile<NW, PF, XM>(op, tl.tile, stage);
 }
 
 // x (n floats) -> n/32 Q8_0 blocks of 34 bytes: 32 lanes per block, eight
@@ -410,53 +426,76 @@ __global__ __launch_bounds__(256) void k_quantize_x(const float *x, uint8_t *xq,
 }  // namespace
 
 namespace {
-template <int NW, int PF, bool XQ>
+template <int NW, int PF, int XM>
 hipError_t launch_single_t(const OpDesc &op, int64_t grid, hipStream_t s) {
-    hipLaunchKernelGGL((k_q8_gemv<NW, PF, XQ>), dim3((unsigned)grid), dim3(NW * kWave), 0, s, op);
+    hipLaunchKernelGGL((k_q8_gemv<NW, PF, XM>), dim3((unsigned)grid), dim3(NW * kWave), 0, s, op);
     return hipGetLastError();
 }
-template <int NW, int PF, bool XQ>
+template <int NW, int PF, int XM>
 hipError_t launch_fused_t(const OpDesc *d_ops, const Tile *d_tiles, int64_t grid, hipStream_t s) {
-    hipLaunchKernelGGL((k_q8_gemv_fused<NW, PF, XQ>), dim3((unsigned)grid), dim3(NW * kWave), 0, s,
+    hipLaunchKernelGGL((k_q8_gemv_fused<NW, PF, XM>), dim3((unsigned)grid), dim3(NW * kWave), 0, s,
                        d_ops, d_tiles);
     return hipGetLastError();
 }
-template <bool XQ>
+// Every launch shape for the float and integer paths; the SiLU·up input
+// (used by the decode step's down projections) in the shapes its plans use.
+template <int XM>
 hipError_t launch_single_v(const OpDesc &op, const Variant &v, int64_t grid, hipStream_t s) {
     switch (v.nw * 10 + v.pf) {
-        case 11: return launch_single_t<1, 1, XQ>(op, grid, s);
-        case 12: return launch_single_t<1, 2, XQ>(op, grid, s);
-        case 21: return launch_single_t<2, 1, XQ>(op, grid, s);
-        case 22: return launch_single_t<2, 2, XQ>(op, grid, s);
-        case 41: return launch_single_t<4, 1, XQ>(op, grid, s);
-        case 42: return launch_single_t<4, 2, XQ>(op, grid, s);
-        default: return hipErrorInvalidValue;
+        case 11: return launch_single_t<1, 1, XM>(op, grid, s);
+        case 41: return launch_single_t<4, 1, XM>(op, grid, s);
+        default: break;
     }
+    if constexpr (XM != kXSiluUp) {
+        switch (v.nw * 10 + v.pf) {
+            case 12: return launch_single_t<1, 2, XM>(op, grid, s);
+            case 21: return launch_single_t<2, 1, XM>(op, grid, s);
+            case 22: return launch_single_t<2, 2, XM>(op, grid, s);
+            case 42: return launch_single_t<4, 2, XM>(op, grid, s);
+            default: break;
+        }
+    }
+    return hipErrorInvalidValue;
 }
-template <bool XQ>
+template <int XM>
 hipError_t launch_fused_v(const OpDesc *d_ops, const Tile *d_tiles, const Variant &v, int64_t grid,
                           hipStream_t s) {
     switch (v.nw * 10 + v.pf) {
-        case 11: return launch_fused_t<1, 1, XQ>(d_ops, d_tiles, grid, s);
-        case 12: return launch_fused_t<1, 2, XQ>(d_ops, d_tiles, grid, s);
-        case 21: return launch_fused_t<2, 1, XQ>(d_ops, d_tiles, grid, s);
-        case 22: return launch_fused_t<2, 2, XQ>(d_ops, d_tiles, grid, s);
-        case 41: return launch_fused_t<4, 1, XQ>(d_ops, d_tiles, grid, s);
-        case 42: return launch_fused_t<4, 2, XQ>(d_ops, d_tiles, grid, s);
-        default: return hipErrorInvalidValue;
+        case 11: return launch_fused_t<1, 1, XM>(d_ops, d_tiles, grid, s);
+        case 41: return launch_fused_t<4, 1, XM>(d_ops, d_tiles, grid, s);
+        default: break;
     }
+    if constexpr (XM != kXSiluUp) {
+        switch (v.nw * 10 + v.pf) {
+            case 12: return launch_fused_t<1, 2, XM>(d_ops, d_tiles, grid, s);
+            case 21: return launch_fused_t<2, 1, XM>(d_ops, d_tiles, grid, s);
+            case 22: return launch_fused_t<2, 2, XM>(d_ops, d_tiles, grid, s);
+            case 42: return launch_fused_t<4, 2, XM>(d_ops, d_tiles, grid, s);
+            default: break;
+        }
+    }
+    return hipErrorInvalidValue;
 }
 }  // namespace
 
 hipError_t launch_gemv_single(const OpDesc &op, const Variant &v, int64_t grid, hipStream_t s,
-                              bool xq) {
-    return xq ? launch_single_v<true>(op, v, grid, s) : launch_single_v<false>(op, v, grid, s);
+                              int xmode) {
+    switch (xmode) {
+        case kXFloat: return launch_single_v<kXFloat>(op, v, grid, s);
+        case kXQuant: return launch_single_v<kXQuant>(op, v, grid, s);
+        case kXSiluUp: return launch_single_v<kXSiluUp>(op, v, grid, s);
+        default: return hipErrorInvalidValue;
+    }
 }
 
 hipError_t launch_gemv_fused(const OpDesc *d_ops, const Tile *d_tiles, const Variant &v,
-                             int64_t grid, hipStream_t s, bool xq) {
-    return xq ? launch_fused_v<true>(d_ops, d_tiles, v, grid, s)
-              : launch_fused_v<false>(d_ops, d_tiles, v, grid, s);
+                             int64_t grid, hipStream_t s, int xmode) {
+    switch (xmode) {
+        case kXFloat: return launch_fused_v<kXFloat>(d_ops, d_tiles, v, grid, s);
+        case kXQuant: return launch_fused_v<kXQuant>(d_ops, d_tiles, v, grid, s);
+        case kXSiluUp: return launch_fused_v<kXSiluUp>(d_ops, d_tiles, v, grid, s);
+        default: return hipErrorInvalidValue;
+    }
 }
 
 hipError_t launch_quantize_x(const float *x, void *xq, int64_t n, hipStream_t s) {

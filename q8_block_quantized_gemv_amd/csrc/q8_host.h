@@ -24,6 +24,11 @@ Q8_HIDDEN int cu_count(int dev);
 // stream s on device dev, kept across calls (grown when too small).
 Q8_HIDDEN int workspace_for(int dev, hipStream_t s, size_t ws_bytes, size_t cnt_n, float **ws_out,
                             uint32_t **cnt_out);
+// q8_0_chain_create with, when x_up is not null, every op reading
+// silu(x) * x_up[i] (elementwise, x_up[i] 16-byte aligned, n floats) instead
+// of x: the decode step's down projection with its SwiGLU product folded in.
+Q8_HIDDEN int chain_create_ex(const q8_0_op *ops, int64_t n_ops, uint32_t flags,
+                              const float *const *x_up, q8_0_chain **out);
 // Issue a chain's launches on s, without its graph.
 Q8_HIDDEN int chain_issue(const q8_0_chain *c, hipStream_t s);
 

@@ -61,6 +61,14 @@ struct OpDesc {
     int32_t pad_;
     float *part;         // slices * nsr * rs floats
     uint32_t *cnt;       // one per row tile of 64 super-rows, zero between launches
+    const float *x_up;   // kXSiluUp: the input is silu(x) * x_up, elementwise
+};
+
+// How a matvec reads its activations (a compile-time mode of the kernels).
+enum XMode : int {
+    kXFloat = 0,    // x as float32
+    kXQuant = 1,    // x quantized to Q8_0 per group, integer dots
+    kXSiluUp = 2,   // silu(x) * x_up formed per group (the SwiGLU product feeding a down projection)
 };
 constexpr int kMaxSlices = 32;
 // Every row sums its groups into kSlots partial sums (group kk into slot
@@ -92,11 +100,11 @@ inline int64_t tail_tiles_for(int64_t tail_rows, int nw = kWaves) {
 }
 
 // Matvec launchers (q8_gemv.hip).  All return the hipError_t of the launch.
-// xq: x is quantized to Q8_0 on the fly and the products are integer dots.
+// xmode: how the activations are read (XMode).
 hipError_t launch_gemv_single(const OpDesc &op, const Variant &v, int64_t grid, hipStream_t s,
-                              bool xq = false);
+                              int xmode = kXFloat);
 hipError_t launch_gemv_fused(const OpDesc *d_ops, const Tile *d_tiles, const Variant &v,
-                             int64_t grid, hipStream_t s, bool xq = false);
+                             int64_t grid, hipStream_t s, int xmode = kXFloat);
 // x (n floats, n % 32 == 0) -> n/32 Q8_0 blocks of 34 bytes at xq.
 hipError_t launch_quantize_x(const float *x, void *xq, int64_t n, hipStream_t s);
 

@@ -177,7 +177,7 @@ struct q8_0_step {
     int64_t q_width = 0, kv_width = 0, kv_group = 0;
     void *mem = nullptr;      // one device allocation for everything below
     float *x = nullptr, *xn = nullptr, *q = nullptr, *k = nullptr, *v = nullptr, *attn = nullptr;
-    float *resid = nullptr, *gate = nullptr, *up = nullptr, *h = nullptr, *logits = nullptr;
+    float *resid = nullptr, *gate = nullptr, *up = nullptr, *logits = nullptr;
     float *kcache = nullptr, *vcache = nullptr, *attn_ws = nullptr, *amax_ws = nullptr;
     uint32_t *cnt = nullptr;  // n_heads attention counters, then the argmax counter
     int32_t *pos = nullptr;
@@ -232,7 +232,6 @@ int issue_step(const q8_0_step *s, hipStream_t st) {
         if ((rc = chain_issue(ch[1], st))) return rc;
         ok(launch_add_rms(s->x, s->resid, L.ffn_norm, s->xn, hid, m.eps, st));
         if ((rc = chain_issue(ch[2], st))) return rc;
-        ok(launch_silu(s->gate, s->up, s->h, (int)m.inter, st));
         if ((rc = chain_issue(ch[3], st))) return rc;
         const float *next = l + 1 < m.n_layers ? s->layers[l + 1].attn_norm : m.out_norm;
         ok(launch_add_rms(s->x, s->resid, next, s->xn, hid, m.eps, st));
@@ -304,7 +303,7 @@ int q8_0_step_create(const q8_0_model *m, q8_0_step **out) {
     std::vector<size_t> sizes = {
         (size_t)m->hidden, (size_t)m->hidden, (size_t)s->q_width, (size_t)s->kv_width,
         (size_t)s->kv_width, (size_t)s->q_width, (size_t)m->hidden, (size_t)m->inter,
-        (size_t)m->inter, (size_t)m->inter, (size_t)m->vocab,
+        (size_t)m->inter, (size_t)m->vocab,
         (size_t)(m->n_layers * m->max_seq * s->kv_width), (size_t)(m->n_layers * m->max_seq * s->kv_width),
         (size_t)(m->n_heads * s->max_chunks * (m->head_dim + 2)), (size_t)(2 * s->amax_wgs),
         (size_t)(m->n_heads + 1), 1, 1};
@@ -321,16 +320,19 @@ int q8_0_step_create(const q8_0_model *m, q8_0_step **out) {
         return fail_hip(e, "q8_0_step_create hipMemset");
     }
     char *b = (char *)s->mem;
-    float **fl[] = {&s->x, &s->xn, &s->q, &s->k, &s->v, &s->attn, &s->resid, &s->gate, &s->up, &s->h,
+    float **fl[] = {&s->x, &s->xn, &s->q, &s->k, &s->v, &s->attn, &s->resid, &s->gate, &s->up,
                     &s->logits, &s->kcache, &s->vcache, &s->attn_ws, &s->amax_ws};
-    for (size_t i = 0; i < sizeof fl / sizeof fl[0]; ++i) *fl[i] = (float *)(b + offs[i]);
-    s->cnt = (uint32_t *)(b + offs[15]);
-    s->pos = (int32_t *)(b + offs[16]);
-    s->token = (uint32_t *)(b + offs[17]);
+    const size_t nf = sizeof fl / sizeof fl[0];
+    for (size_t i = 0; i < nf; ++i) *fl[i] = (float *)(b + offs[i]);
+    s->cnt = (uint32_t *)(b + offs[nf]);
+    s->pos = (int32_t *)(b + offs[nf + 1]);
+    s->token = (uint32_t *)(b + offs[nf + 2]);
     // the matvecs: fused where independent
-    auto mk = [&](std::vector<q8_0_op> ops) {
+    auto mk = [&](std::vector<q8_0_op> ops, const float *up = nullptr) {
         q8_0_chain *c = nullptr;
-        int r = q8_0_chain_create(ops.data(), (int64_t)ops.size(), Q8_CHAIN_FUSE | Q8_CHAIN_SPLIT_K, &c);
+        const float *ups[1] = {up};
+        int r = chain_create_ex(ops.data(), (int64_t)ops.size(), Q8_CHAIN_FUSE | Q8_CHAIN_SPLIT_K,
+                                up ? ups : nullptr, &c);
         if (!r) s->chains.push_back(c);
         return r;
     };
@@ -340,14 +342,14 @@ int q8_0_step_create(const q8_0_model *m, q8_0_step **out) {
                       {s->xn, L.wv, s->v, m->hidden, s->kv_width}})) ||
             (rc = mk({{s->attn, L.wo, s->resid, s->q_width, m->hidden}})) ||
             (rc = mk({{s->xn, L.wgate, s->gate, m->hidden, m->inter}, {s->xn, L.wup, s->up, m->hidden, m->inter}})) ||
-            (rc = mk({{s->h, L.wdown, s->resid, m->inter, m->hidden}})))
+            (rc = mk({{s->gate, L.wdown, s->resid, m->inter, m->hidden}}, s->up)))
             break;
     }
     if (!rc) rc = mk({{s->xn, m->lm_head, s->logits, m->hidden, m->vocab}});
     if (rc) { std::string why = "q8_0_step_create: " + std::string(q8_0_last_error()); step_free(s); return fail(rc, why); }
     s->launches = 0;
     for (q8_0_chain *c : s->chains) s->launches += q8_0_chain_launches(c);
-    s->launches += (int)(m->n_layers * 4 + 2);   // the step kernels around the matvecs
+    s->launches += (int)(m->n_layers * 3 + 2);   // the step kernels around the matvecs
     // record one token
     if ((e = hipStreamCreateWithFlags(&s->capture, hipStreamNonBlocking)) != hipSuccess) {
         step_free(s);

@@ -278,10 +278,10 @@ def _run_tokens(q8, st, mode, pos, token, count):
 def test_step_launch_count(q8):
     log("step launches step_tiny")
     cfg, _, st = _step(q8, "step_tiny", 64)
-    # per layer: qkv fused, o, gate|up fused, down; attention (with the q/k
-    # norms, rotary embedding and cache append), two add+norm, silu; then
-    # embed+norm, lm_head, argmax
-    assert st.launches == cfg["n_layers"] * (4 + 4) + 1 + 2
+    # per layer: qkv fused, o, gate|up fused, down (reading silu(gate) * up);
+    # attention (with the q/k norms, rotary embedding and cache append), two
+    # add+norm; then embed+norm, lm_head, argmax
+    assert st.launches == cfg["n_layers"] * (4 + 3) + 1 + 2
     st.close()
 
 
