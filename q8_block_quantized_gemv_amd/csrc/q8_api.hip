@@ -472,16 +472,56 @@ void chain_free(q8_0_chain *c) {
     delete c;
 }
 
+// The memory an op reads and writes, as (pointer, bytes) ranges.
+struct Ranges {
+    const void *r[5];
+    int64_t rn[5];
+    int nr = 0;
+    const void *w[2];
+    int64_t wn[2];
+    int nw = 0;
+};
+
+Ranges ranges_of(const q8_0_op &o, const OpExtra *e) {
+    Ranges g;
+    auto rd = [&](const void *p, int64_t n) { if (p) { g.r[g.nr] = p; g.rn[g.nr++] = n; } };
+    auto wr = [&](const void *p, int64_t n) { if (p) { g.w[g.nw] = p; g.wn[g.nw++] = n; } };
+    rd(o.x, 4 * o.n);
+    rd(o.w, w_bytes(o.n, o.p));
+    wr(o.y, 4 * o.p);
+    if (e) {
+        rd(e->x_up, 4 * o.n);
+        rd(e->x_res, 4 * o.n);
+        rd(e->norm_w, 4 * o.n);
+        wr(e->x_out, 4 * o.n);
+    }
+    return g;
+}
+
 // Does op b have to wait for op a (a earlier)?  Any write of one that
 // touches memory the other reads or writes.
-// (ua, ub: the ops' second activation input in the SiLU·up mode, or null)
-bool depends(const q8_0_op &a, const q8_0_op &b, const float *ua = nullptr,
-             const float *ub = nullptr) {
-    const int64_t ya = 4 * a.p, yb = 4 * b.p;
-    return overlaps(b.y, yb, a.y, ya) || overlaps(b.y, yb, a.x, 4 * a.n) ||
-           overlaps(b.y, yb, a.w, w_bytes(a.n, a.p)) || overlaps(b.x, 4 * b.n, a.y, ya) ||
-           overlaps(b.w, w_bytes(b.n, b.p), a.y, ya) || (ua && overlaps(b.y, yb, ua, 4 * a.n)) ||
-           (ub && overlaps(ub, 4 * b.n, a.y, ya));
+bool depends(const q8_0_op &a, const q8_0_op &b, const OpExtra *ea = nullptr,
+             const OpExtra *eb = nullptr) {
+    const Ranges A = ranges_of(a, ea), B = ranges_of(b, eb);
+    for (int i = 0; i < B.nw; ++i) {
+        for (int j = 0; j < A.nr; ++j)
+            if (overlaps(B.w[i], B.wn[i], A.r[j], A.rn[j])) return true;
+        for (int j = 0; j < A.nw; ++j)
+            if (overlaps(B.w[i], B.wn[i], A.w[j], A.wn[j])) return true;
+    }
+    for (int i = 0; i < A.nw; ++i)
+        for (int j = 0; j < B.nr; ++j)
+            if (overlaps(A.w[i], A.wn[i], B.r[j], B.rn[j])) return true;
+    return false;
+}
+
+void set_extra(OpDesc &d, const OpExtra *e) {
+    if (!e) return;
+    d.x_up = e->x_up;
+    d.x_res = e->x_res;
+    d.norm_w = e->norm_w;
+    d.x_out = e->x_out;
+    d.norm_eps = e->eps;
 }
 
 }  // namespace
@@ -502,23 +542,34 @@ int q8_0_chain_create(const q8_0_op *ops, int64_t n_ops, uint32_t flags, q8_0_ch
 
 }  // extern "C"
 
-int q8::chain_create_ex(const q8_0_op *ops, int64_t n_ops, uint32_t flags,
-                        const float *const *x_up, q8_0_chain **out) {
+int q8::chain_create_ex(const q8_0_op *ops, int64_t n_ops, uint32_t flags, const OpExtra *extra,
+                        q8_0_chain **out) {
     if (!out) return fail(Q8_ERR_INVALID_ARG, "q8_0_chain_create: out is null");
     *out = nullptr;
     if (!ops || n_ops <= 0 || n_ops > Q8_MAX_CHAIN_OPS)
         return fail(Q8_ERR_INVALID_ARG, "q8_0_chain_create: need 1..65535 ops");
     if (flags & ~(uint32_t)(Q8_CHAIN_PER_OP | Q8_CHAIN_SPLIT_K | Q8_CHAIN_XQ))
         return fail(Q8_ERR_INVALID_ARG, "q8_0_chain_create: unknown flags");
-    if (x_up && (flags & Q8_CHAIN_XQ))
-        return fail(Q8_ERR_INVALID_ARG, "q8_0_chain_create: the SiLU·up input has no integer form");
+    const int emode = extra ? extra[0].mode : kXFloat;
+    if (extra && (flags & Q8_CHAIN_XQ))
+        return fail(Q8_ERR_INVALID_ARG, "q8_0_chain_create: these inputs have no integer form");
+    auto a16 = [](const void *p) { return p && ((uintptr_t)p & 15u) == 0; };
     for (int64_t i = 0; i < n_ops; ++i) {
         const std::string what = "q8_0_chain_create op " + std::to_string(i);
         int rc = validate(ops[i].x, ops[i].w, ops[i].y, 1, ops[i].n, ops[i].p, what.c_str());
         if (rc) return rc;
-        if (x_up && (!x_up[i] || ((uintptr_t)x_up[i] & 15u) ||
-                     overlaps(ops[i].y, 4 * ops[i].p, x_up[i], 4 * ops[i].n)))
-            return fail(Q8_ERR_INVALID_ARG, what + ": up input null, not 16-byte aligned or aliased");
+        if (!extra) continue;
+        const OpExtra &e = extra[i];
+        const int64_t xb = 4 * ops[i].n, yb = 4 * ops[i].p;
+        bool ok = e.mode == emode;
+        if (e.mode == kXSiluUp) ok = ok && a16(e.x_up) && !overlaps(ops[i].y, yb, e.x_up, xb);
+        else if (e.mode == kXNormAdd)   // (the writer of x_out needs a fast tile: p >= 8)
+            ok = ok && a16(e.x_res) && a16(e.norm_w) && (!e.x_out || (a16(e.x_out) && ops[i].p >= 8)) &&
+                 !overlaps(ops[i].y, yb, e.x_res, xb) &&
+                 !(e.x_out && (overlaps(e.x_out, xb, ops[i].x, xb) || overlaps(e.x_out, xb, e.x_res, xb) ||
+                               overlaps(e.x_out, xb, ops[i].y, yb)));
+        else ok = false;
+        if (!ok) return fail(Q8_ERR_INVALID_ARG, what + ": extra inputs missing, misaligned or aliased");
     }
     int dev = 0;
     int rc = check_device(&dev);
@@ -540,7 +591,7 @@ int q8::chain_create_ex(const q8_0_op *ops, int64_t n_ops, uint32_t flags,
         for (int64_t i = 1; i <= n_ops; ++i) {
             bool cut = (i == n_ops);
             for (int64_t j = b; !cut && j < i; ++j)
-                cut = depends(ops[j], ops[i], x_up ? x_up[j] : nullptr, x_up ? x_up[i] : nullptr);
+                cut = depends(ops[j], ops[i], extra ? &extra[j] : nullptr, extra ? &extra[i] : nullptr);
             if (cut) { segs.push_back({b, i}); b = i; }
         }
     }
@@ -592,7 +643,7 @@ int q8::chain_create_ex(const q8_0_op *ops, int64_t n_ops, uint32_t flags,
             for (int64_t i = sg.first; i < sg.second; ++i) {
                 const q8_0_op &o = ops[i];
                 OpDesc d = plan_op(o.x, o.w, o.y, 1, o.n, o.p, standalone, v.nw, target);
-                d.x_up = x_up ? x_up[i] : nullptr;
+                set_extra(d, extra ? &extra[i] : nullptr);
                 const uint32_t oi = (uint32_t)(h_ops.size() - si.op0);
                 h_ops.push_back(d);
                 const int64_t fb = (int64_t)(v.nw / d.ks) * kWave *
@@ -609,7 +660,7 @@ int q8::chain_create_ex(const q8_0_op *ops, int64_t n_ops, uint32_t flags,
         } else {
             const q8_0_op &o = ops[sg.first];
             si.single = plan_op(o.x, o.w, o.y, 1, o.n, o.p, standalone, v.nw, target);
-            si.single.x_up = x_up ? x_up[sg.first] : nullptr;
+            set_extra(si.single, extra ? &extra[sg.first] : nullptr);
         }
         info.push_back(si);
     }
@@ -652,7 +703,7 @@ int q8::chain_create_ex(const q8_0_op *ops, int64_t n_ops, uint32_t flags,
     for (size_t k = 0; k < segs.size(); ++k) {
         q8_0_chain::Launch L;
         std::memset(&L, 0, sizeof L);
-        L.xmode = x_up ? kXSiluUp : (flags & Q8_CHAIN_XQ) ? kXQuant : kXFloat;
+        L.xmode = extra ? emode : (flags & Q8_CHAIN_XQ) ? kXQuant : kXFloat;
         if (info[k].fused) {
             L.fused = true;
             L.v = info[k].v;

@@ -127,6 +127,46 @@ __device__ __forceinline__ void dma_group_x(const uint8_t *g, const uint32_t (&o
 // The SwiGLU product, as the step's silu_hadamard kernel computes it.
 __device__ __forceinline__ float silu_up(float g, float u) { return (g / (1.0f + expf(-g))) * u; }
 
+// kXNormAdd: 1 / rms of s = x + x_res over the op's n columns, for one wave
+// (lane l takes float4s l, l + 64, ...); with `write`, s also goes to x_out.
+__device__ __forceinline__ float norm_add_inv(const OpDesc &op, int lane, bool write) {
+    constexpr int B = 8;   // float4 pairs in flight per lane
+    const int n = op.nb * kQuants, nv = n / 4;
+    const float4 *a4 = reinterpret_cast<const float4 *>(op.x);
+    const float4 *r4 = reinterpret_cast<const float4 *>(op.x_res);
+    float4 *o4 = reinterpret_cast<float4 *>(op.x_out);
+    float ss = 0.f;
+    for (int i0 = 0; i0 < nv; i0 += kWave * B) {
+        float4 a[B], r[B];
+#pragma unroll
+        for (int e = 0; e < B; ++e) {
+            const int i = i0 + lane + kWave * e;
+            a[e] = make_float4(0.f, 0.f, 0.f, 0.f);
+            r[e] = a[e];
+            if (i < nv) {
+                a[e] = a4[i];
+                r[e] = r4[i];
+            }
+        }
+#pragma unroll
+        for (int e = 0; e < B; ++e) {
+            const int i = i0 + lane + kWave * e;
+            const float4 v = make_float4(a[e].x + r[e].x, a[e].y + r[e].y, a[e].z + r[e].z, a[e].w + r[e].w);
+            ss = fmaf(v.x, v.x, ss);
+            ss = fmaf(v.y, v.y, ss);
+            ss = fmaf(v.z, v.z, ss);
+            ss = fmaf(v.w, v.w, ss);
+            if (write && i < nv) o4[i] = v;
+        }
+    }
+#pragma unroll
+    for (int o = kWave / 2; o > 0; o >>= 1) ss += __shfl_xor(ss, o, kWave);
+    return 1.0f / sqrtf(ss / (float)n + op.norm_eps);
+}
+
+// One normalised value of the kXNormAdd input.
+__device__ __forceinline__ float norm_add(float a, float r, float inv, float w) { return (a + r) * inv * w; }
+
 // acc[slot][r] += v for a uniform slot and row index (unrolled selects).
 template <int RS>
 __device__ __forceinline__ void flush_row(float (&acc)[kSlots][RS], int slot, int r, float v) {
@@ -165,12 +205,14 @@ __device__ __forceinline__ uint32_t pack4(int a, int b, int c, int d) {
 // blocks l, l+64, ...; blocks are read with 2-byte loads (a block is only
 // 2-byte aligned in general).  Per-lane sums are flushed every 8 blocks and
 // the 64 lanes meet in a fixed butterfly.
-template <bool SILU = false>
+template <int XM = kXFloat>
 __device__ void tail_tile(const OpDesc &op, uint32_t tile, int waves) {
     const int lane = lane_id();
     const int wave = wave_id();
     const int64_t row = (int64_t)op.tail_row0 + (int64_t)tile * waves + wave;
     if (row >= op.p) return;
+    float inv = 0.f;
+    if constexpr (XM == kXNormAdd) inv = norm_add_inv(op, lane, false);
     const int nb = op.nb;
     const uint8_t *wr = op.w + row * (int64_t)nb * kBlockBytes;
     for (int i = 0; i < op.m; ++i) {
@@ -187,10 +229,15 @@ __device__ void tail_tile(const OpDesc &op, uint32_t tile, int waves) {
             for (int j = 0; j < kQuants / 2; ++j) {
                 const uint32_t v = blk[1 + j];
                 float x0 = xb[2 * j], x1 = xb[2 * j + 1];
-                if constexpr (SILU) {
+                if constexpr (XM == kXSiluUp) {
                     const float *ub = op.x_up + (int64_t)b * kQuants;
                     x0 = silu_up(x0, ub[2 * j]);
                     x1 = silu_up(x1, ub[2 * j + 1]);
+                } else if constexpr (XM == kXNormAdd) {
+                    const float *rb = op.x_res + (int64_t)b * kQuants;
+                    const float *wb = op.norm_w + (int64_t)b * kQuants;
+                    x0 = norm_add(x0, rb[2 * j], inv, wb[2 * j]);
+                    x1 = norm_add(x1, rb[2 * j + 1], inv, wb[2 * j + 1]);
                 }
                 a0 = fmaf((float)(int8_t)(v & 0xffu), x0, a0);
                 a1 = fmaf((float)(int8_t)(v >> 8), x1, a1);

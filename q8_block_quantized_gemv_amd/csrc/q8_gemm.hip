@@ -552,7 +552,7 @@ __global__ __launch_bounds__(kWave, 1) void k_q8_gemm_mfma(GemmDesc d) {
         OpDesc t;
         t.x = d.X; t.w = d.w; t.y = d.Y; t.nb = d.nb; t.p = d.p; t.m = d.m;
         t.x_stride = d.n; t.y_stride = d.p; t.tail_row0 = d.tail_row0;
-        tail_tile<false>(t, bid - d.fast_wgs, 1);
+        tail_tile<kXFloat>(t, bid - d.fast_wgs, 1);
     }
 }
 
@@ -566,7 +566,7 @@ __global__ __launch_bounds__(kWave) void k_q8_gemm_valu(GemmDesc d) {
         OpDesc t;
         t.x = d.X; t.w = d.w; t.y = d.Y; t.nb = d.nb; t.p = d.p; t.m = d.m;
         t.x_stride = d.n; t.y_stride = d.p; t.tail_row0 = d.tail_row0;
-        tail_tile<false>(t, bid - d.fast_wgs, 1);
+        tail_tile<kXFloat>(t, bid - d.fast_wgs, 1);
     }
 }
 

@@ -267,7 +267,9 @@ constexpr int stage_bytes() { return kStageBytes + (XM == kXSiluUp ? kStageX : 0
 template <int RS, int NW, int PF, int XM>
 __device__ void fast_tile(const OpDesc &op, uint32_t tile, uint8_t *stage) {
     constexpr int SB = stage_bytes<XM>();
-    constexpr int LPG = kLoadsPerGroup + (XM == kXSiluUp ? 1 : 0);   // direct loads per group
+    // memory operations per group: 17 direct loads of W, then the x slice
+    // (one more direct load; two for kXSiluUp; three vector loads for kXNormAdd)
+    constexpr int LPG = kGroupChunks + (XM == kXSiluUp ? 2 : XM == kXNormAdd ? 3 : 1);
     const int lane = lane_id();
     const int wave = wave_id();
     const int ks = op.ks;
@@ -300,15 +302,30 @@ __device__ void fast_tile(const OpDesc &op, uint32_t tile, uint8_t *stage) {
         const int g0 = S > 1 ? slice * op.slice_groups : 0;
         const int g1 = S > 1 ? min(G, g0 + op.slice_groups) : G;
         const int ng = g1 - g0 > ksl ? (g1 - g0 - ksl + ks - 1) / ks : 0;
+        float4 na = make_float4(0.f, 0.f, 0.f, 0.f), nr = na, nw = na;   // kXNormAdd prefetch
         auto issue = [&](int t) {
             const int kk = g0 + ksl + ks * t;
             uint8_t *st = st0 + (t & 1) * SB;
-            dma_group_x<RS>(wt + (int64_t)kk * kGroupBytes, off, st, op, kk, lane);
-            if constexpr (XM == kXSiluUp)
-                dma16_v(x_slice_src<RS>(op, op.x_up, kk, lane),
-                        __builtin_amdgcn_readfirstlane(lds_addr(st)) + kStageBytes);
+            if constexpr (XM == kXNormAdd) {
+                // W by direct loads; this lane's four x, x_res and gain values
+                // of the group into registers, used before the next issue
+                const uint32_t l0 = __builtin_amdgcn_readfirstlane(lds_addr(st));
+                const uint8_t *g = wt + (int64_t)kk * kGroupBytes;
+#pragma unroll
+                for (int i = 0; i < kGroupChunks; ++i) dma16_s(g, off[i], l0 + kWave * 16 * i);
+                na = *reinterpret_cast<const float4 *>(x_slice_src<RS>(op, op.x, kk, lane));
+                nr = *reinterpret_cast<const float4 *>(x_slice_src<RS>(op, op.x_res, kk, lane));
+                nw = *reinterpret_cast<const float4 *>(x_slice_src<RS>(op, op.norm_w, kk, lane));
+            } else {
+                dma_group_x<RS>(wt + (int64_t)kk * kGroupBytes, off, st, op, kk, lane);
+                if constexpr (XM == kXSiluUp)
+                    dma16_v(x_slice_src<RS>(op, op.x_up, kk, lane),
+                            __builtin_amdgcn_readfirstlane(lds_addr(st)) + kStageBytes);
+            }
         };
         if (ng > 0) issue(0);
+        float ninv = 0.f;
+        if constexpr (XM == kXNormAdd) ninv = norm_add_inv(op, lane, op.x_out && tile == 0 && wave == 0);
         if (PF == 2 && ng > 1) issue(1);
         for (int t = 0; t < ng; ++t) {
             uint8_t *cur = st0 + (t & 1) * SB;
@@ -317,6 +334,10 @@ __device__ void fast_tile(const OpDesc &op, uint32_t tile, uint8_t *stage) {
             if (PF == 2 && t + 1 < ng) wait_vm_asm<LPG>();
             else wait_vm_asm<0>();
             read_group(cur, lane, D);
+            if constexpr (XM == kXNormAdd)   // this group's normalised x slice into the stage
+                reinterpret_cast<float4 *>(cur + kStageW)[lane] =
+                    make_float4(norm_add(na.x, nr.x, ninv, nw.x), norm_add(na.y, nr.y, ninv, nw.y),
+                                norm_add(na.z, nr.z, ninv, nw.z), norm_add(na.w, nr.w, ninv, nw.w));
             if (PF == 1 && t + 1 < ng) issue(t + 1);
             if constexpr (XM == kXQuant) {
                 quantize_slice(cur + kStageW, lane);
@@ -374,7 +395,7 @@ template <int NW, int PF, int XM>
 __device__ __forceinline__ void run_tile(const OpDesc &op, uint32_t t, uint8_t *stage) {
     if (t & kTailBit) {
         if constexpr (XM == kXQuant) tail_tile_xq(op, t & ~kTailBit, NW);
-        else tail_tile<XM == kXSiluUp>(op, t & ~kTailBit, NW);
+        else tail_tile<XM>(op, t & ~kTailBit, NW);
         return;
     }
     switch (op.rs) {
@@ -437,8 +458,8 @@ hipError_t launch_fused_t(const OpDesc *d_ops, const Tile *d_tiles, int64_t grid
                        d_ops, d_tiles);
     return hipGetLastError();
 }
-// Every launch shape for the float and integer paths; the SiLU·up input
-// (used by the decode step's down projections) in the shapes its plans use.
+// Every launch shape for the float and integer paths; the decode step's
+// input modes (SiLU·up, residual add + norm) in the shapes its plans use.
 template <int XM>
 hipError_t launch_single_v(const OpDesc &op, const Variant &v, int64_t grid, hipStream_t s) {
     switch (v.nw * 10 + v.pf) {
@@ -446,7 +467,7 @@ hipError_t launch_single_v(const OpDesc &op, const Variant &v, int64_t grid, hip
         case 41: return launch_single_t<4, 1, XM>(op, grid, s);
         default: break;
     }
-    if constexpr (XM != kXSiluUp) {
+    if constexpr (XM == kXFloat || XM == kXQuant) {
         switch (v.nw * 10 + v.pf) {
             case 12: return launch_single_t<1, 2, XM>(op, grid, s);
             case 21: return launch_single_t<2, 1, XM>(op, grid, s);
@@ -465,7 +486,7 @@ hipError_t launch_fused_v(const OpDesc *d_ops, const Tile *d_tiles, const Varian
         case 41: return launch_fused_t<4, 1, XM>(d_ops, d_tiles, grid, s);
         default: break;
     }
-    if constexpr (XM != kXSiluUp) {
+    if constexpr (XM == kXFloat || XM == kXQuant) {
         switch (v.nw * 10 + v.pf) {
             case 12: return launch_fused_t<1, 2, XM>(d_ops, d_tiles, grid, s);
             case 21: return launch_fused_t<2, 1, XM>(d_ops, d_tiles, grid, s);
@@ -484,6 +505,7 @@ hipError_t launch_gemv_single(const OpDesc &op, const Variant &v, int64_t grid, 
         case kXFloat: return launch_single_v<kXFloat>(op, v, grid, s);
         case kXQuant: return launch_single_v<kXQuant>(op, v, grid, s);
         case kXSiluUp: return launch_single_v<kXSiluUp>(op, v, grid, s);
+        case kXNormAdd: return launch_single_v<kXNormAdd>(op, v, grid, s);
         default: return hipErrorInvalidValue;
     }
 }
@@ -494,6 +516,7 @@ hipError_t launch_gemv_fused(const OpDesc *d_ops, const Tile *d_tiles, const Var
         case kXFloat: return launch_fused_v<kXFloat>(d_ops, d_tiles, v, grid, s);
         case kXQuant: return launch_fused_v<kXQuant>(d_ops, d_tiles, v, grid, s);
         case kXSiluUp: return launch_fused_v<kXSiluUp>(d_ops, d_tiles, v, grid, s);
+        case kXNormAdd: return launch_fused_v<kXNormAdd>(d_ops, d_tiles, v, grid, s);
         default: return hipErrorInvalidValue;
     }
 }

@@ -24,11 +24,20 @@ Q8_HIDDEN int cu_count(int dev);
 // stream s on device dev, kept across calls (grown when too small).
 Q8_HIDDEN int workspace_for(int dev, hipStream_t s, size_t ws_bytes, size_t cnt_n, float **ws_out,
                             uint32_t **cnt_out);
-// q8_0_chain_create with, when x_up is not null, every op reading
-// silu(x) * x_up[i] (elementwise, x_up[i] 16-byte aligned, n floats) instead
-// of x: the decode step's down projection with its SwiGLU product folded in.
+// Per-op inputs of the decode step's chains (internal): how the op reads its
+// activations (XMode) and the extra vectors that takes, n floats each,
+// 16-byte aligned.
+struct OpExtra {
+    int mode = 0;                  // kXSiluUp or kXNormAdd; every op of a chain the same
+    const float *x_up = nullptr;   // kXSiluUp: input silu(x) * x_up
+    const float *x_res = nullptr;  // kXNormAdd: input rms_norm(x + x_res) * norm_w
+    const float *norm_w = nullptr;
+    float *x_out = nullptr;        // kXNormAdd: x + x_res written here (may be null)
+    float eps = 0.f;
+};
+// q8_0_chain_create with per-op extras (null: plain ops).
 Q8_HIDDEN int chain_create_ex(const q8_0_op *ops, int64_t n_ops, uint32_t flags,
-                              const float *const *x_up, q8_0_chain **out);
+                              const OpExtra *extra, q8_0_chain **out);
 // Issue a chain's launches on s, without its graph.
 Q8_HIDDEN int chain_issue(const q8_0_chain *c, hipStream_t s);
 

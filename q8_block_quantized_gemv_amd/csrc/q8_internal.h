@@ -62,6 +62,13 @@ struct OpDesc {
     float *part;         // slices * nsr * rs floats
     uint32_t *cnt;       // one per row tile of 64 super-rows, zero between launches
     const float *x_up;   // kXSiluUp: the input is silu(x) * x_up, elementwise
+    // kXNormAdd: the input is rms_norm(x + x_res) * norm_w over the op's n
+    // columns; the op-local tile 0's first wave also writes x + x_res to x_out
+    const float *x_res;
+    const float *norm_w;
+    float *x_out;        // may be null
+    float norm_eps;
+    int32_t pad2_;
 };
 
 // How a matvec reads its activations (a compile-time mode of the kernels).
@@ -69,6 +76,7 @@ enum XMode : int {
     kXFloat = 0,    // x as float32
     kXQuant = 1,    // x quantized to Q8_0 per group, integer dots
     kXSiluUp = 2,   // silu(x) * x_up formed per group (the SwiGLU product feeding a down projection)
+    kXNormAdd = 3,  // rms_norm(x + x_res) * norm_w formed per group (a residual add and the norm after it)
 };
 constexpr int kMaxSlices = 32;
 // Every row sums its groups into kSlots partial sums (group kk into slot

@@ -57,9 +57,6 @@ hipError_t launch_attention_fused(const AttnDesc &d, const AttnFuse &f, hipStrea
 hipError_t launch_add(float *x, const float *y, int n, hipStream_t s);
 hipError_t launch_silu(const float *g, const float *u, float *out, int n, hipStream_t s);
 hipError_t launch_argmax(const ArgmaxDesc &d, int wgs, hipStream_t s);
-// x += y, then xn = rms_norm(x) * w (one workgroup; dim % 4 == 0, 16-byte aligned)
-hipError_t launch_add_rms(float *x, const float *y, const float *w, float *xn, int dim, float eps,
-                          hipStream_t s);
 // x = row *token of table (zeros if *token >= vocab), then xn = rms_norm(x) * w
 hipError_t launch_embed_rms(const float *table, const uint32_t *token, uint32_t vocab, float *x,
                             const float *w, float *xn, int dim, float eps, hipStream_t s);

@@ -20,7 +20,8 @@
 // The fused kernels of a recorded token (the page encodes each of its
 // kernels separately; fewer, larger launches suit a hipGraph better):
 //  * embed_rms: x = embedding row of the token, xn = rms_norm(x);
-//  * add_rms: x += y, xn = rms_norm(x) (the residual add and the next norm);
+//  * (the residual adds and the norms after them are folded into the next
+//    matvec's activation staging, see q8_gemv.hip);
 //  * attention takes the per-head q and k norms, the rotary embedding of q
 //    and k and the K/V cache append into its own prologue;
 //  * argmax also advances the position.
@@ -162,6 +163,7 @@ __global__ __launch_bounds__(kThreads) void k_rms_norm(const float *x, const flo
 // ---------------------------------------------------------------- fused residual + norm
 // EMBED: x = row `token` of the table y (zeros past the table: a row of only
 // NaN logits has no argmax); else x += y.  Then xn = rms_norm(x) * w.
+// A recorded step uses the EMBED form for its first norm.
 // One 256-thread workgroup (four float4 per thread in flight for rows up to
 // 4096); dim % 4 == 0 and x, y, w, xn 16-byte aligned.
 template <bool EMBED>
@@ -666,13 +668,6 @@ hipError_t launch_rms_norm(const float *x, const float *w, float *out, int dim, 
         hipLaunchKernelGGL(k_rms_norm<true>, grid, dim3(kThreads), 0, s, x, w, out, dim, rows, eps);
     else
         hipLaunchKernelGGL(k_rms_norm<false>, grid, dim3(kThreads), 0, s, x, w, out, dim, rows, eps);
-    return hipGetLastError();
-}
-
-hipError_t launch_add_rms(float *x, const float *y, const float *w, float *xn, int dim, float eps,
-                          hipStream_t s) {
-    hipLaunchKernelGGL(k_add_rms<false>, dim3(1), dim3(kThreads), 0, s, x, y, nullptr, 0u, w, xn, dim,
-                       eps);
     return hipGetLastError();
 }
 

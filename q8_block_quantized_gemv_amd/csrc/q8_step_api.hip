@@ -177,6 +177,7 @@ struct q8_0_step {
     int64_t q_width = 0, kv_width = 0, kv_group = 0;
     void *mem = nullptr;      // one device allocation for everything below
     float *x = nullptr, *xn = nullptr, *q = nullptr, *k = nullptr, *v = nullptr, *attn = nullptr;
+    float *xa = nullptr, *xb = nullptr;   // the residual stream, alternating between layers
     float *resid = nullptr, *gate = nullptr, *up = nullptr, *logits = nullptr;
     float *kcache = nullptr, *vcache = nullptr, *attn_ws = nullptr, *amax_ws = nullptr;
     uint32_t *cnt = nullptr;  // n_heads attention counters, then the argmax counter
@@ -212,8 +213,8 @@ int issue_step(const q8_0_step *s, hipStream_t st) {
         if (err != hipSuccess && e == hipSuccess) e = err;
     };
     int rc = Q8_OK;
-    ok(launch_embed_rms(m.embed, s->token, (uint32_t)m.vocab, s->x, s->layers[0].attn_norm, s->xn, hid,
-                        m.eps, st));
+    ok(launch_embed_rms(m.embed, s->token, (uint32_t)m.vocab, s->xa, s->layers[0].attn_norm, s->xn,
+                        hid, m.eps, st));
     for (int64_t l = 0; l < m.n_layers && e == hipSuccess; ++l) {
         const q8_0_layer_w &L = s->layers[l];
         float *kc = s->kcache + l * cache_stride, *vc = s->vcache + l * cache_stride;
@@ -230,11 +231,8 @@ int issue_step(const q8_0_step *s, hipStream_t st) {
         f.kc_w = kc; f.vc_w = vc; f.eps = m.eps; f.theta = m.theta;
         ok(launch_attention_fused(d, f, st));
         if ((rc = chain_issue(ch[1], st))) return rc;
-        ok(launch_add_rms(s->x, s->resid, L.ffn_norm, s->xn, hid, m.eps, st));
         if ((rc = chain_issue(ch[2], st))) return rc;
         if ((rc = chain_issue(ch[3], st))) return rc;
-        const float *next = l + 1 < m.n_layers ? s->layers[l + 1].attn_norm : m.out_norm;
-        ok(launch_add_rms(s->x, s->resid, next, s->xn, hid, m.eps, st));
     }
     if (e != hipSuccess) return fail_hip(e, "decode step launch");
     if ((rc = chain_issue(s->chains.back(), st))) return rc;
@@ -301,7 +299,8 @@ int q8_0_step_create(const q8_0_model *m, q8_0_step **out) {
     if (s->q_width % 32) { step_free(s); return fail(Q8_ERR_SHAPE, "q8_0_step_create: n_heads * head_dim must be a multiple of 32"); }
     // one allocation, every piece 256-B aligned
     std::vector<size_t> sizes = {
-        (size_t)m->hidden, (size_t)m->hidden, (size_t)s->q_width, (size_t)s->kv_width,
+        (size_t)m->hidden, (size_t)m->hidden, (size_t)m->hidden, (size_t)m->hidden,
+        (size_t)s->q_width, (size_t)s->kv_width,
         (size_t)s->kv_width, (size_t)s->q_width, (size_t)m->hidden, (size_t)m->inter,
         (size_t)m->inter, (size_t)m->vocab,
         (size_t)(m->n_layers * m->max_seq * s->kv_width), (size_t)(m->n_layers * m->max_seq * s->kv_width),
@@ -320,36 +319,72 @@ int q8_0_step_create(const q8_0_model *m, q8_0_step **out) {
         return fail_hip(e, "q8_0_step_create hipMemset");
     }
     char *b = (char *)s->mem;
-    float **fl[] = {&s->x, &s->xn, &s->q, &s->k, &s->v, &s->attn, &s->resid, &s->gate, &s->up,
+    float **fl[] = {&s->x, &s->xn, &s->xa, &s->xb, &s->q, &s->k, &s->v, &s->attn, &s->resid, &s->gate, &s->up,
                     &s->logits, &s->kcache, &s->vcache, &s->attn_ws, &s->amax_ws};
     const size_t nf = sizeof fl / sizeof fl[0];
     for (size_t i = 0; i < nf; ++i) *fl[i] = (float *)(b + offs[i]);
     s->cnt = (uint32_t *)(b + offs[nf]);
     s->pos = (int32_t *)(b + offs[nf + 1]);
     s->token = (uint32_t *)(b + offs[nf + 2]);
-    // the matvecs: fused where independent
-    auto mk = [&](std::vector<q8_0_op> ops, const float *up = nullptr) {
+    // the matvecs: fused where independent.  Each residual add and the norm
+    // after it are folded into the next matvec's activation staging
+    // (kXNormAdd): it reads the residual stream and the block's output,
+    // normalises their sum, and its first workgroup writes the sum to the
+    // other stream buffer.  The down projections read silu(gate) * up
+    // (kXSiluUp).  The embedding row and the first norm come from embed+norm.
+    auto mk = [&](std::vector<q8_0_op> ops, const OpExtra *e = nullptr) {
         q8_0_chain *c = nullptr;
-        const float *ups[1] = {up};
+        std::vector<OpExtra> ex;
+        if (e) {
+            ex.assign(ops.size(), *e);
+            for (size_t i = 1; i < ex.size(); ++i) ex[i].x_out = nullptr;   // one writer per launch
+        }
         int r = chain_create_ex(ops.data(), (int64_t)ops.size(), Q8_CHAIN_FUSE | Q8_CHAIN_SPLIT_K,
-                                up ? ups : nullptr, &c);
+                                e ? ex.data() : nullptr, &c);
         if (!r) s->chains.push_back(c);
         return r;
     };
+    auto norm_add = [&](const float *gain, float *x_out) {
+        OpExtra e;
+        e.mode = kXNormAdd;
+        e.x_res = s->resid;
+        e.norm_w = gain;
+        e.x_out = x_out;
+        e.eps = m->eps;
+        return e;
+    };
+    float *cur = s->xa, *oth = s->xb;
+    OpExtra silu;
+    silu.mode = kXSiluUp;
+    silu.x_up = s->up;
     for (int64_t l = 0; l < m->n_layers && !rc; ++l) {
         const q8_0_layer_w &L = s->layers[l];
-        if ((rc = mk({{s->xn, L.wq, s->q, m->hidden, s->q_width}, {s->xn, L.wk, s->k, m->hidden, s->kv_width},
-                      {s->xn, L.wv, s->v, m->hidden, s->kv_width}})) ||
-            (rc = mk({{s->attn, L.wo, s->resid, s->q_width, m->hidden}})) ||
-            (rc = mk({{s->xn, L.wgate, s->gate, m->hidden, m->inter}, {s->xn, L.wup, s->up, m->hidden, m->inter}})) ||
-            (rc = mk({{s->gate, L.wdown, s->resid, m->inter, m->hidden}}, s->up)))
+        if (l == 0) {
+            rc = mk({{s->xn, L.wq, s->q, m->hidden, s->q_width}, {s->xn, L.wk, s->k, m->hidden, s->kv_width},
+                     {s->xn, L.wv, s->v, m->hidden, s->kv_width}});
+        } else {
+            const OpExtra e = norm_add(L.attn_norm, oth);
+            rc = mk({{cur, L.wq, s->q, m->hidden, s->q_width}, {cur, L.wk, s->k, m->hidden, s->kv_width},
+                     {cur, L.wv, s->v, m->hidden, s->kv_width}}, &e);
+            std::swap(cur, oth);
+        }
+        if (rc) break;
+        if ((rc = mk({{s->attn, L.wo, s->resid, s->q_width, m->hidden}}))) break;
+        const OpExtra e = norm_add(L.ffn_norm, oth);
+        if ((rc = mk({{cur, L.wgate, s->gate, m->hidden, m->inter}, {cur, L.wup, s->up, m->hidden, m->inter}},
+                     &e)))
             break;
+        std::swap(cur, oth);
+        if ((rc = mk({{s->gate, L.wdown, s->resid, m->inter, m->hidden}}, &silu))) break;
     }
-    if (!rc) rc = mk({{s->xn, m->lm_head, s->logits, m->hidden, m->vocab}});
+    if (!rc) {
+        const OpExtra e = norm_add(m->out_norm, s->x);
+        rc = mk({{cur, m->lm_head, s->logits, m->hidden, m->vocab}}, &e);
+    }
     if (rc) { std::string why = "q8_0_step_create: " + std::string(q8_0_last_error()); step_free(s); return fail(rc, why); }
     s->launches = 0;
     for (q8_0_chain *c : s->chains) s->launches += q8_0_chain_launches(c);
-    s->launches += (int)(m->n_layers * 3 + 2);   // the step kernels around the matvecs
+    s->launches += (int)(m->n_layers + 2);   // embed+norm, attention per layer, argmax
     // record one token
     if ((e = hipStreamCreateWithFlags(&s->capture, hipStreamNonBlocking)) != hipSuccess) {
         step_free(s);

@@ -278,10 +278,11 @@ def _run_tokens(q8, st, mode, pos, token, count):
 def test_step_launch_count(q8):
     log("step launches step_tiny")
     cfg, _, st = _step(q8, "step_tiny", 64)
-    # per layer: qkv fused, o, gate|up fused, down (reading silu(gate) * up);
-    # attention (with the q/k norms, rotary embedding and cache append), two
-    # add+norm; then embed+norm, lm_head, argmax
-    assert st.launches == cfg["n_layers"] * (4 + 3) + 1 + 2
+    # per layer: q|k|v (fused; from the second layer on it also adds the
+    # residual and norms), attention (with the q/k norms, rotary embedding and
+    # cache append), o, gate|up (fused, adds and norms), down (reads
+    # silu(gate) * up); then embed+norm, the lm_head (adds, norms), argmax
+    assert st.launches == cfg["n_layers"] * 5 + 1 + 2
     st.close()
 
 
