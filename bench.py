@@ -311,8 +311,10 @@ def main():
                 "traffic": measured_traffic(args.workload),
                 # a chain of one op is that op's standalone launch (four-wave
                 # workgroups); more independent ops share one fused launch
-                "kernel": ("k_q8_gemv_fused<1,1,%s>" if len(ops_shape) > 1 else "k_q8_gemv<4,1,%s>")
-                          % ("true" if args.xq else "false"),
+                # template arguments: waves per workgroup, groups in flight, input mode
+                # (0 float activations, 1 activations quantized to Q8_0)
+                "kernel": ("k_q8_gemv_fused<1,1,%d>" if len(ops_shape) > 1 else "k_q8_gemv<4,1,%d>")
+                          % (1 if args.xq else 0),
                 "launches_per_step": launches,
                 "algorithmic_bytes_per_launch": nbytes // launches,
                 "kernel_us": round(kernel_s * 1e6, 2),
