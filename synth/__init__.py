@@ -208,7 +208,9 @@ def generate_smallm(shape: OpShape, m: int):
 # are test models: "step_tiny" (2 layers, head_dim 64, two query heads per
 # KV head), "step_gqa4" (head_dim 128, four query heads per KV head, an
 # intermediate width and a vocabulary that are not powers of two),
-# "step_hd192" (three query heads on one KV head) and "step_hd256".
+# "step_hd192" (three query heads on one KV head; rows of 12 blocks pair into
+# two-row super-rows and the odd vocabulary leaves the lm_head a tail row)
+# and "step_hd256".
 STEP_MODELS = {
     "qwen3_0.6b": dict(n_layers=28, hidden=1024, n_heads=16, n_kv_heads=8, head_dim=128,
                        inter=3072, vocab=151936, eps=1e-6, theta=1e6),
@@ -219,7 +221,7 @@ STEP_MODELS = {
     "step_gqa4": dict(n_layers=1, hidden=512, n_heads=8, n_kv_heads=2, head_dim=128,
                       inter=1376, vocab=4099, eps=1e-6, theta=1e4),
     "step_hd192": dict(n_layers=1, hidden=384, n_heads=3, n_kv_heads=1, head_dim=192,
-                       inter=640, vocab=500, eps=1e-5, theta=1e6),
+                       inter=640, vocab=501, eps=1e-5, theta=1e6),
     "step_hd256": dict(n_layers=2, hidden=512, n_heads=4, n_kv_heads=2, head_dim=256,
                        inter=768, vocab=700, eps=1e-6, theta=1e6),
 }
