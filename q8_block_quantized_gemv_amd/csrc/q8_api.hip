@@ -442,11 +442,15 @@ struct q8_0_chain {
     // one entry per kernel launch of a token
     struct Launch {
         bool fused;
+        bool sk;              // stream-K launch (d_ops, d_pieces, d_begin; d_tiles = tail tiles)
         int xmode;            // XMode: how the activations are read
         Variant v;
         OpDesc single;        // per-op launch
         const OpDesc *d_ops;  // fused launch
         const Tile *d_tiles;
+        const Piece *d_pieces;
+        const uint32_t *d_begin;
+        int64_t n_sk;         // stream-K workgroups (the tail tiles' follow)
         int64_t grid;
     };
     std::vector<Launch> launches;
@@ -459,6 +463,9 @@ struct q8_0_chain {
 namespace {
 
 hipError_t issue(const q8_0_chain::Launch &L, hipStream_t s) {
+    if (L.sk)
+        return launch_gemv_streamk(L.d_ops, L.d_pieces, L.d_begin, L.d_tiles, L.n_sk, L.grid - L.n_sk,
+                                   L.v.pf, s, L.xmode);
     if (L.fused) return launch_gemv_fused(L.d_ops, L.d_tiles, L.v, L.grid, s, L.xmode);
     return launch_gemv_single(L.single, L.v, L.grid, s, L.xmode);
 }
@@ -513,6 +520,56 @@ bool depends(const q8_0_op &a, const q8_0_op &b, const OpExtra *ea = nullptr,
         for (int j = 0; j < B.nr; ++j)
             if (overlaps(A.w[i], A.wn[i], B.r[j], B.rn[j])) return true;
     return false;
+}
+
+// Stream-K schedule of a launch's ops on `wgs` one-wave workgroups: all
+// (op, row tile, group) items, in that order, are cut into wgs equal
+// contiguous ranges (workgroup b takes [b*N/wgs, (b+1)*N/wgs)), and each
+// range into pieces where it crosses a row tile.  The pieces of one row tile
+// are numbered in workgroup order (their partial slots); maxc[i] is op i's
+// largest number of pieces on one row tile.  begin holds wgs + 1 offsets.
+void plan_pieces(const std::vector<OpDesc> &ds, int64_t wgs, std::vector<Piece> &pieces,
+                 std::vector<uint32_t> &begin, std::vector<int32_t> &maxc) {
+    const size_t n_ops = ds.size();
+    std::vector<int64_t> off(n_ops + 1, 0);
+    std::vector<std::vector<uint32_t>> count(n_ops);
+    for (size_t i = 0; i < n_ops; ++i) {
+        const int64_t tiles = ((int64_t)ds[i].nsr + kWave - 1) / kWave;
+        off[i + 1] = off[i] + tiles * ds[i].gsr;
+        count[i].assign((size_t)tiles, 0u);
+    }
+    const int64_t N = off[n_ops];
+    pieces.clear();
+    begin.assign((size_t)wgs + 1, 0u);
+    size_t i = 0;
+    for (int64_t b = 0; b < wgs; ++b) {
+        begin[(size_t)b] = (uint32_t)pieces.size();
+        int64_t lo = b * N / wgs;
+        const int64_t hi = (b + 1) * N / wgs;
+        while (lo < hi) {
+            while (off[i + 1] <= lo) ++i;
+            const int64_t G = ds[i].gsr;
+            const int64_t local = lo - off[i];
+            const int64_t tile = local / G;
+            const int64_t g0 = local - tile * G;
+            const int64_t g1 = std::min<int64_t>(G, g0 + (hi - lo));
+            Piece pc;
+            pc.op = (uint32_t)i;
+            pc.tile = (uint32_t)tile;
+            pc.g0 = (uint32_t)g0;
+            pc.g1 = (uint32_t)g1;
+            pc.slot = count[i][(size_t)tile]++;
+            pc.nslots = 0;
+            pieces.push_back(pc);
+            lo += g1 - g0;
+        }
+    }
+    begin[(size_t)wgs] = (uint32_t)pieces.size();
+    maxc.assign(n_ops, 1);
+    for (auto &pc : pieces) {
+        pc.nslots = count[pc.op][pc.tile];
+        maxc[pc.op] = std::max<int32_t>(maxc[pc.op], (int32_t)pc.nslots);
+    }
 }
 
 void set_extra(OpDesc &d, const OpExtra *e) {
@@ -608,14 +665,31 @@ int q8::chain_create_ex(const q8_0_op *ops, int64_t n_ops, uint32_t flags, const
     // CUs (an lm_head, a 7B gate|up) are fastest on unsplit one-wave tiles.
     const Variant v_single = pick_variant(false), v_fused = pick_variant(true);
     const int64_t cus = cu_count(dev);
+    // Stream-K for split launches with more row tiles than CUs:
+    // Q8GEMV_STREAMK=0 turns it off, 2 uses it for every split launch (A/B
+    // runs); Q8GEMV_SK_PF sets its groups in flight (1 or 2).
+    const int sk_mode = env_int("Q8GEMV_STREAMK", 1);
+    const int sk_pf = env_int("Q8GEMV_SK_PF", 1) == 2 ? 2 : 1;
     std::vector<OpDesc> h_ops;
     std::vector<Tile> h_tiles;
-    struct SegInfo { size_t op0, tile0; int64_t ntiles; bool fused; OpDesc single; Variant v; };
+    std::vector<Piece> h_pieces;
+    std::vector<uint32_t> h_begin;
+    struct SegInfo {
+        size_t op0, tile0;
+        int64_t ntiles;
+        bool fused;
+        OpDesc single;
+        Variant v;
+        bool sk;
+        size_t piece0, begin0;
+        int64_t n_sk;
+    };
     std::vector<SegInfo> info;
     for (auto &sg : segs) {
         const bool fused = !per_op && (sg.second - sg.first > 1);
         int64_t target = 1;
         Variant v = fused ? v_fused : v_single;
+        bool sk = false;
         if (split) {
             int64_t row_tiles = 0;
             for (int64_t i = sg.first; i < sg.second; ++i) {
@@ -628,14 +702,44 @@ int q8::chain_create_ex(const q8_0_op *ops, int64_t n_ops, uint32_t flags, const
                 v = Variant{kWaves, 1};
                 target = std::max<int64_t>(1, cus / std::max<int64_t>(1, row_tiles));
             }
+            sk = sk_mode == 2 || (sk_mode == 1 && row_tiles > cus);
             // A/B overrides: Q8GEMV_SPLIT_SLICES (slices per row tile), Q8GEMV_VARIANT
             if (const int forced = env_int("Q8GEMV_SPLIT_SLICES", 0); forced > 0) target = forced;
             if (std::getenv("Q8GEMV_VARIANT")) v = v_single;
+            if (sk) v = Variant{1, sk_pf};
         }
         // four-wave split workgroups take the standalone K split inside the workgroup
         const bool standalone = (!split && !fused) || (split && v.nw > 1);
-        SegInfo si{h_ops.size(), h_tiles.size(), 0, fused, OpDesc{}, v};
-        if (fused) {
+        SegInfo si{h_ops.size(), h_tiles.size(), 0, fused, OpDesc{}, v, sk, h_pieces.size(), h_begin.size(), 0};
+        if (sk) {
+            // one-wave workgroups, four per CU (their two stages fill its LDS),
+            // each at least kSkMinItems (row tile, group) items
+            constexpr int64_t kSkMinItems = 2;
+            std::vector<OpDesc> ds;
+            int64_t items = 0;
+            for (int64_t i = sg.first; i < sg.second; ++i) {
+                const q8_0_op &o = ops[i];
+                OpDesc d = plan_op(o.x, o.w, o.y, 1, o.n, o.p, false, 1);
+                set_extra(d, extra ? &extra[i] : nullptr);
+                items += (int64_t)d.fast_tiles * d.gsr;
+                ds.push_back(d);
+            }
+            const int64_t wgs = std::min<int64_t>(4 * cus, std::max<int64_t>(1, items / kSkMinItems));
+            std::vector<Piece> pcs;
+            std::vector<uint32_t> bg;
+            std::vector<int32_t> maxc;
+            plan_pieces(ds, items > 0 ? wgs : 0, pcs, bg, maxc);
+            for (size_t i = 0; i < ds.size(); ++i) {
+                if (maxc[i] > 1) ds[i].sk_slots = maxc[i];
+                h_ops.push_back(ds[i]);
+                const int64_t tt = tail_tiles_for((int64_t)ds[i].p - ds[i].tail_row0, 1);
+                for (int64_t t = 0; t < tt; ++t) h_tiles.push_back({(uint32_t)i, (uint32_t)t | kTailBit});
+            }
+            h_pieces.insert(h_pieces.end(), pcs.begin(), pcs.end());
+            h_begin.insert(h_begin.end(), bg.begin(), bg.end());
+            si.n_sk = items > 0 ? wgs : 0;
+            si.ntiles = (int64_t)(h_tiles.size() - si.tile0);
+        } else if (fused) {
             // tiles sorted by decreasing weight bytes so that the smallest
             // tiles finish the launch (ties keep encode order)
             struct Item { Tile t; int64_t bytes; };
@@ -664,55 +768,72 @@ int q8::chain_create_ex(const q8_0_op *ops, int64_t n_ops, uint32_t flags, const
         }
         info.push_back(si);
     }
-    // device block: op descriptors, tiles, then the K-split partials and counters
+    // device block: op descriptors, tiles, pieces, piece offsets, then the
+    // K-split partials and counters
+    auto up256 = [](size_t x) { return (x + 255) / 256 * 256; };
     const size_t ob = h_ops.size() * sizeof(OpDesc);
     const size_t tb = h_tiles.size() * sizeof(Tile);
-    size_t wb = (ob + tb + 255) / 256 * 256;   // running end of the block
+    const size_t pb = h_pieces.size() * sizeof(Piece);
+    const size_t bb = h_begin.size() * sizeof(uint32_t);
+    const size_t t_at = ob, p_at = up256(ob + tb), b_at = up256(p_at + pb);
+    size_t wb = up256(b_at + bb);   // running end of the block
     std::vector<std::pair<OpDesc *, size_t>> ws;  // (op, offset of its partials)
+    auto part_bytes = [](const OpDesc &d) {
+        return (size_t)std::max(d.slices, d.sk_slots) * d.nsr * d.rs * sizeof(float);
+    };
     auto reserve = [&](OpDesc &d) {
-        if (d.slices <= 1) return;
+        if (d.slices <= 1 && d.sk_slots <= 1) return;
         ws.push_back({&d, wb});
-        const size_t part = (size_t)d.slices * d.nsr * d.rs * sizeof(float);
         const size_t cnt = (size_t)((d.nsr + kWave - 1) / kWave) * sizeof(uint32_t);
-        wb += (part + 255) / 256 * 256 + (cnt + 255) / 256 * 256;
+        wb += up256(part_bytes(d)) + up256(cnt);
     };
     for (auto &d : h_ops) reserve(d);
     for (auto &si : info)
-        if (!si.fused) reserve(si.single);
-    const size_t total = ws.empty() ? ob + tb : wb;
+        if (!si.fused && !si.sk) reserve(si.single);
+    const size_t total = wb;
     if (total) {
         hipError_t e = hipMalloc(&c->d_table, total);
         if (e != hipSuccess) { chain_free(c); return fail_hip(e, "q8_0_chain_create hipMalloc"); }
         char *base = (char *)c->d_table;
         for (auto &pw : ws) {
             OpDesc &d = *pw.first;
-            const size_t part = (size_t)d.slices * d.nsr * d.rs * sizeof(float);
             d.part = (float *)(base + pw.second);
-            d.cnt = (uint32_t *)(base + pw.second + (part + 255) / 256 * 256);
+            d.cnt = (uint32_t *)(base + pw.second + up256(part_bytes(d)));
         }
         std::vector<char> host(total, 0);   // counters start at zero
         if (ob) std::memcpy(host.data(), h_ops.data(), ob);
-        if (tb) std::memcpy(host.data() + ob, h_tiles.data(), tb);
+        if (tb) std::memcpy(host.data() + t_at, h_tiles.data(), tb);
+        if (pb) std::memcpy(host.data() + p_at, h_pieces.data(), pb);
+        if (bb) std::memcpy(host.data() + b_at, h_begin.data(), bb);
         if ((e = hipMemcpy(c->d_table, host.data(), host.size(), hipMemcpyHostToDevice)) != hipSuccess) {
             chain_free(c);
             return fail_hip(e, "q8_0_chain_create hipMemcpy");
         }
     }
     const OpDesc *d_ops = (const OpDesc *)c->d_table;
-    const Tile *d_tiles = (const Tile *)((const char *)c->d_table + ob);
+    const Tile *d_tiles = (const Tile *)((const char *)c->d_table + t_at);
+    const Piece *d_pieces = (const Piece *)((const char *)c->d_table + p_at);
+    const uint32_t *d_begin = (const uint32_t *)((const char *)c->d_table + b_at);
     for (size_t k = 0; k < segs.size(); ++k) {
         q8_0_chain::Launch L;
         std::memset(&L, 0, sizeof L);
         L.xmode = extra ? emode : (flags & Q8_CHAIN_XQ) ? kXQuant : kXFloat;
-        if (info[k].fused) {
+        L.v = info[k].v;
+        if (info[k].sk) {
+            L.sk = true;
+            L.d_ops = d_ops + info[k].op0;
+            L.d_tiles = d_tiles + info[k].tile0;
+            L.d_pieces = d_pieces + info[k].piece0;
+            L.d_begin = d_begin + info[k].begin0;
+            L.n_sk = info[k].n_sk;
+            L.grid = info[k].n_sk + info[k].ntiles;
+        } else if (info[k].fused) {
             L.fused = true;
-            L.v = info[k].v;
             L.d_ops = d_ops + info[k].op0;
             L.d_tiles = d_tiles + info[k].tile0;
             L.grid = info[k].ntiles;
         } else {
             L.fused = false;
-            L.v = info[k].v;
             L.single = info[k].single;
             L.grid = tiles_of(L.single, L.v.nw);
         }

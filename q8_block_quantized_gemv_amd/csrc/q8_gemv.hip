@@ -213,13 +213,14 @@ __device__ void tail_tile_xq(const OpDesc &op, uint32_t tile, int waves) {
 // right after that group's compute, so two groups stream while one waits).
 constexpr int kGatherBatch = 8;
 
-// With K slices (op.slices > 1) the ksl == 0 wave of each row tile parks
-// its rows' partial sums and counts in; the last slice to arrive adds the
-// slices in order.  The partials travel through device-scope stores and
+// With K slices (op.slices > 1), or a stream-K row tile shared by several
+// workgroups, the ksl == 0 wave of each row tile parks its rows' partial
+// sums in its slot and counts in; the last of the nslices to arrive adds the
+// slots in order.  The partials travel through device-scope stores and
 // loads (they come from other workgroups, possibly on other XCDs).
 template <int RS>
-__device__ __forceinline__ void slice_arrive(const OpDesc &op, int64_t row_tile, int slice, int64_t sr0,
-                                          const float (&acc)[kSlots][RS], int lane) {
+__device__ __forceinline__ void slice_arrive(const OpDesc &op, int64_t row_tile, int slice, int nslices,
+                                          int64_t sr0, const float (&acc)[kSlots][RS], int lane) {
     const int64_t P = (int64_t)op.nsr * RS;
     const bool live = sr0 + lane < op.nsr;
     const int64_t r0 = (sr0 + lane) * RS;
@@ -234,24 +235,24 @@ __device__ __forceinline__ void slice_arrive(const OpDesc &op, int64_t row_tile,
     if (lane == 0)
         prev = __hip_atomic_fetch_add(op.cnt + row_tile, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     prev = __builtin_amdgcn_readfirstlane(prev);
-    if (prev != (uint32_t)op.slices - 1) return;
+    if (prev != (uint32_t)nslices - 1) return;
     asm volatile("" ::: "memory");
     if (live) {
 #pragma unroll
         for (int k = 0; k < RS; ++k) {
             float sum = 0.f;
-            for (int q0 = 0; q0 < op.slices; q0 += kGatherBatch) {   // loads eight at a time
+            for (int q0 = 0; q0 < nslices; q0 += kGatherBatch) {   // loads eight at a time
                 float v[kGatherBatch];
 #pragma unroll
                 for (int b = 0; b < kGatherBatch; ++b) {
                     v[b] = 0.f;
-                    if (q0 + b < op.slices)
+                    if (q0 + b < nslices)
                         v[b] = __hip_atomic_load(op.part + (q0 + b) * P + r0 + k, __ATOMIC_RELAXED,
                                                  __HIP_MEMORY_SCOPE_AGENT);
                 }
 #pragma unroll
                 for (int b = 0; b < kGatherBatch; ++b)
-                    if (q0 + b < op.slices) sum += v[b];
+                    if (q0 + b < nslices) sum += v[b];
             }
             op.y[r0 + k] = sum;
         }
@@ -264,8 +265,18 @@ __device__ __forceinline__ void slice_arrive(const OpDesc &op, int64_t row_tile,
 template <int XM>
 constexpr int stage_bytes() { return kStageBytes + (XM == kXSiluUp ? kStageX : 0); }
 
+// What one workgroup does with an op: groups [g0, g1) of each of its row
+// tiles (wtile * (NW / ks) onward); nslots > 1: the row tiles are shared by
+// nslots workgroups and this one parks its partial sums in slot `slot`.
+struct TileJob {
+    int64_t wtile;
+    int g0, g1;
+    int slot, nslots;
+    bool writer;   // kXNormAdd: this workgroup's first wave writes x + x_res to x_out
+};
+
 template <int RS, int NW, int PF, int XM>
-__device__ void fast_tile(const OpDesc &op, uint32_t tile, uint8_t *stage) {
+__device__ void fast_job(const OpDesc &op, const TileJob &job, uint8_t *stage) {
     constexpr int SB = stage_bytes<XM>();
     // memory operations per group: 17 direct loads of W, then the x slice
     // (one more direct load; two for kXSiluUp; three vector loads for kXNormAdd)
@@ -276,10 +287,7 @@ __device__ void fast_tile(const OpDesc &op, uint32_t tile, uint8_t *stage) {
     const int rt = wave / ks;                 // row tile within the workgroup
     const int ksl = wave - rt * ks;           // this wave's share of the groups
     const int tiles_per_wg = NW / ks;
-    const int S = op.slices;
-    const uint32_t wtile = S > 1 ? tile / (uint32_t)S : tile;   // workgroup's row tiles
-    const int slice = (int)(tile - wtile * (uint32_t)S);
-    const int64_t row_tile = (int64_t)wtile * tiles_per_wg + rt;
+    const int64_t row_tile = job.wtile * tiles_per_wg + rt;
     const int64_t sr0 = row_tile * kWave;
     const int nsr = op.nsr;
     uint8_t *st0 = stage + (size_t)wave * (kBufs * SB);
@@ -297,10 +305,11 @@ __device__ void fast_tile(const OpDesc &op, uint32_t tile, uint8_t *stage) {
         const int last = (int)min((int64_t)nsr - 1 - sr0, (int64_t)kWave - 1);
         uint32_t off[kGroupChunks];
         chunk_offsets(off, lane, last, srb);
-        // this slice's groups [g0, g1); g0 is a multiple of kSlots, so group
-        // kk = g0 + ksl + ks*t still falls in slot kk % 4 owned by wave ksl
-        const int g0 = S > 1 ? slice * op.slice_groups : 0;
-        const int g1 = S > 1 ? min(G, g0 + op.slice_groups) : G;
+        // the job's groups [g0, g1); with ks > 1, g0 is a multiple of kSlots,
+        // so group kk = g0 + ksl + ks*t still falls in slot kk % 4 owned by
+        // wave ksl
+        const int g0 = job.g0;
+        const int g1 = min(G, job.g1);
         const int ng = g1 - g0 > ksl ? (g1 - g0 - ksl + ks - 1) / ks : 0;
         float4 na = make_float4(0.f, 0.f, 0.f, 0.f), nr = na, nw = na;   // kXNormAdd prefetch
         auto issue = [&](int t) {
@@ -325,7 +334,7 @@ __device__ void fast_tile(const OpDesc &op, uint32_t tile, uint8_t *stage) {
         };
         if (ng > 0) issue(0);
         float ninv = 0.f;
-        if constexpr (XM == kXNormAdd) ninv = norm_add_inv(op, lane, op.x_out && tile == 0 && wave == 0);
+        if constexpr (XM == kXNormAdd) ninv = norm_add_inv(op, lane, op.x_out && job.writer && wave == 0);
         if (PF == 2 && ng > 1) issue(1);
         for (int t = 0; t < ng; ++t) {
             uint8_t *cur = st0 + (t & 1) * SB;
@@ -380,8 +389,8 @@ __device__ void fast_tile(const OpDesc &op, uint32_t tile, uint8_t *stage) {
             }
         }
     }
-    if (S > 1) {
-        if (ksl == 0 && sr0 < nsr) slice_arrive<RS>(op, row_tile, slice, sr0, acc, lane);
+    if (job.nslots > 1) {
+        if (ksl == 0 && sr0 < nsr) slice_arrive<RS>(op, row_tile, job.slot, job.nslots, sr0, acc, lane);
         return;
     }
     if (ksl == 0 && sr0 + lane < nsr) {
@@ -389,6 +398,20 @@ __device__ void fast_tile(const OpDesc &op, uint32_t tile, uint8_t *stage) {
 #pragma unroll
         for (int k = 0; k < RS; ++k) yr[k] = combine_slots(acc[0][k], acc[1][k], acc[2][k], acc[3][k]);
     }
+}
+
+// Fast tile `tile` of a launch: with K slices, tile = row-tile group * slices + slice.
+template <int RS, int NW, int PF, int XM>
+__device__ __forceinline__ void fast_tile(const OpDesc &op, uint32_t tile, uint8_t *stage) {
+    const int S = op.slices;
+    TileJob job;
+    job.wtile = S > 1 ? tile / (uint32_t)S : tile;
+    job.slot = (int)(tile - (uint32_t)job.wtile * (uint32_t)S);
+    job.nslots = S;
+    job.g0 = S > 1 ? job.slot * op.slice_groups : 0;
+    job.g1 = S > 1 ? job.g0 + op.slice_groups : op.gsr;
+    job.writer = tile == 0;
+    fast_job<RS, NW, PF, XM>(op, job, stage);
 }
 
 template <int NW, int PF, int XM>
@@ -421,6 +444,42 @@ __global__ __launch_bounds__(NW * kWave) void k_q8_gemv_fused(const OpDesc *__re
     const Tile tl = tiles[blockIdx.x];
     const OpDesc op = ops[tl.op];
     run_tile<NW, PF, XM>(op, tl.tile, stage);
+}
+
+// Stream-K: one-wave workgroups, each walking its pieces (contiguous runs of
+// an equal share of all (row tile, group) items of the launch's ops) in
+// order; the workgroups after the first n_sk run tail tiles.
+template <int PF, int XM>
+__global__ __launch_bounds__(kWave) void k_q8_gemv_sk(const OpDesc *__restrict__ ops,
+                                                      const Piece *__restrict__ pieces,
+                                                      const uint32_t *__restrict__ begin,
+                                                      const Tile *__restrict__ tails, uint32_t n_sk) {
+    __shared__ __attribute__((aligned(16))) uint8_t stage[kBufs * stage_bytes<XM>()];
+    const uint32_t b = blockIdx.x;
+    if (b >= n_sk) {
+        const Tile tl = tails[b - n_sk];
+        if constexpr (XM == kXQuant) tail_tile_xq(ops[tl.op], tl.tile & ~kTailBit, 1);
+        else tail_tile<XM>(ops[tl.op], tl.tile & ~kTailBit, 1);
+        return;
+    }
+    const uint32_t e = begin[b + 1];
+    for (uint32_t i = begin[b]; i < e; ++i) {
+        const Piece pc = pieces[i];
+        const OpDesc op = ops[pc.op];
+        TileJob job;
+        job.wtile = pc.tile;
+        job.g0 = (int)pc.g0;
+        job.g1 = (int)pc.g1;
+        job.slot = (int)pc.slot;
+        job.nslots = (int)pc.nslots;
+        job.writer = pc.tile == 0 && pc.g0 == 0;
+        switch (op.rs) {
+            case 1: fast_job<1, 1, PF, XM>(op, job, stage); break;
+            case 2: fast_job<2, 1, PF, XM>(op, job, stage); break;
+            case 4: fast_job<4, 1, PF, XM>(op, job, stage); break;
+            default: fast_job<8, 1, PF, XM>(op, job, stage); break;
+        }
+    }
 }
 
 // x (n floats) -> n/32 Q8_0 blocks of 34 bytes: 32 lanes per block, eight
@@ -456,6 +515,13 @@ template <int NW, int PF, int XM>
 hipError_t launch_fused_t(const OpDesc *d_ops, const Tile *d_tiles, int64_t grid, hipStream_t s) {
     hipLaunchKernelGGL((k_q8_gemv_fused<NW, PF, XM>), dim3((unsigned)grid), dim3(NW * kWave), 0, s,
                        d_ops, d_tiles);
+    return hipGetLastError();
+}
+template <int PF, int XM>
+hipError_t launch_sk_t(const OpDesc *d_ops, const Piece *d_pieces, const uint32_t *d_begin,
+                       const Tile *d_tails, int64_t n_sk, int64_t n_tail, hipStream_t s) {
+    hipLaunchKernelGGL((k_q8_gemv_sk<PF, XM>), dim3((unsigned)(n_sk + n_tail)), dim3(kWave), 0, s, d_ops,
+                       d_pieces, d_begin, d_tails, (uint32_t)n_sk);
     return hipGetLastError();
 }
 // Every launch shape for the float and integer paths; the decode step's
@@ -519,6 +585,23 @@ hipError_t launch_gemv_fused(const OpDesc *d_ops, const Tile *d_tiles, const Var
         case kXNormAdd: return launch_fused_v<kXNormAdd>(d_ops, d_tiles, v, grid, s);
         default: return hipErrorInvalidValue;
     }
+}
+
+hipError_t launch_gemv_streamk(const OpDesc *d_ops, const Piece *d_pieces, const uint32_t *d_begin,
+                               const Tile *d_tails, int64_t n_sk, int64_t n_tail, int pf,
+                               hipStream_t s, int xmode) {
+    if (n_sk + n_tail <= 0) return hipErrorInvalidValue;
+#define Q8_SK(XM)                                                                                 \
+    return pf == 2 ? launch_sk_t<2, XM>(d_ops, d_pieces, d_begin, d_tails, n_sk, n_tail, s)       \
+                   : launch_sk_t<1, XM>(d_ops, d_pieces, d_begin, d_tails, n_sk, n_tail, s);
+    switch (xmode) {
+        case kXFloat: Q8_SK(kXFloat)
+        case kXQuant: Q8_SK(kXQuant)
+        case kXSiluUp: Q8_SK(kXSiluUp)
+        case kXNormAdd: Q8_SK(kXNormAdd)
+        default: return hipErrorInvalidValue;
+    }
+#undef Q8_SK
 }
 
 hipError_t launch_quantize_x(const float *x, void *xq, int64_t n, hipStream_t s) {

@@ -58,8 +58,10 @@ struct OpDesc {
     // and clears the counter.  slices == 1: no split, part and cnt unused.
     int32_t slices;
     int32_t slice_groups;  // a multiple of kSlots
-    int32_t pad_;
-    float *part;         // slices * nsr * rs floats
+    // Stream-K launches (Piece): the most workgroups sharing one row tile;
+    // part then holds sk_slots slots of nsr * rs floats.  0: not stream-K.
+    int32_t sk_slots;
+    float *part;         // max(slices, sk_slots) * nsr * rs floats
     uint32_t *cnt;       // one per row tile of 64 super-rows, zero between launches
     const float *x_up;   // kXSiluUp: the input is silu(x) * x_up, elementwise
     // kXNormAdd: the input is rms_norm(x + x_res) * norm_w over the op's n
@@ -90,6 +92,17 @@ struct Tile {
 };
 constexpr uint32_t kTailBit = 0x80000000u;
 
+// Stream-K work of a one-wave workgroup: groups [g0, g1) of row tile `tile`
+// (64 super-rows) of op `op`.  A row tile that several workgroups share
+// (nslots > 1) has each park its partial sums in slot `slot` of the op's
+// partials; the last of them to arrive adds the slots in slot order.
+struct Piece {
+    uint32_t op;
+    uint32_t tile;
+    uint32_t g0, g1;
+    uint32_t slot, nslots;
+};
+
 // Matvec kernel shape: waves per workgroup (1, 2 or 4) and groups each wave
 // keeps in flight ahead of the one it computes (1 or 2).
 struct Variant {
@@ -113,6 +126,12 @@ hipError_t launch_gemv_single(const OpDesc &op, const Variant &v, int64_t grid, 
                               int xmode = kXFloat);
 hipError_t launch_gemv_fused(const OpDesc *d_ops, const Tile *d_tiles, const Variant &v,
                              int64_t grid, hipStream_t s, int xmode = kXFloat);
+// Stream-K launch of one-wave workgroups: workgroup b < n_sk walks pieces
+// [begin[b], begin[b+1]); the n_tail workgroups after them run tails[b - n_sk]
+// (tail tiles).  pf: groups in flight per wave (1 or 2).
+hipError_t launch_gemv_streamk(const OpDesc *d_ops, const Piece *d_pieces, const uint32_t *d_begin,
+                               const Tile *d_tails, int64_t n_sk, int64_t n_tail, int pf,
+                               hipStream_t s, int xmode = kXFloat);
 // x (n floats, n % 32 == 0) -> n/32 Q8_0 blocks of 34 bytes at xq.
 hipError_t launch_quantize_x(const float *x, void *xq, int64_t n, hipStream_t s);
 

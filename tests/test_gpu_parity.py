@@ -262,19 +262,25 @@ def test_chain_modes_equal_standalone(q8, fuse):
 
 # (n, p) for K split across workgroups: row-poor shapes with many groups per
 # row (split into 2..5 slices), super-rows of 2 and 4 rows, a tail row, a
-# shape too short to split, and a 7B down projection
+# shape too short to split, a 7B down projection, and a shape with more row
+# tiles (257) than the GPU has CUs
 SPLIT_SHAPES = [(2048, 1024), (3072, 1024), (896, 130), (896, 131), (4864, 131), (1088, 5),
-                (3584, 512), (96, 67), (18944, 3584)]
+                (3584, 512), (96, 67), (18944, 3584), (1024, 16448)]
 
 
+@pytest.mark.parametrize("sk", ["0", "1", "2"], ids=["sk_off", "sk_auto", "sk_all"])
 @pytest.mark.parametrize("per_op", [False, True], ids=["fused", "per_op"])
-def test_split_k_chain(q8, per_op):
+def test_split_k_chain(q8, monkeypatch, per_op, sk):
     """Q8_CHAIN_SPLIT_K on independent ops and on a dependent pair: every
     output within the bar against the oracle on the inputs the op actually
     read, the same bits on every replay and in every mode (the split's
-    arrival counters reset themselves)."""
+    arrival counters reset themselves).  Q8GEMV_STREAMK picks the schedule:
+    K slices only, stream-K where row tiles outnumber CUs (the default), or
+    stream-K for every launch (pieces crossing row tiles and ops, row tiles
+    shared by many workgroups, tail rows)."""
     import torch
-    log("split-K chain per_op=%s" % per_op)
+    monkeypatch.setenv("Q8GEMV_STREAMK", sk)
+    log("split-K chain per_op=%s streamk=%s" % (per_op, sk))
     rng = np.random.default_rng(77)
     ws = [synth.q8_weights(n, p, rng) for n, p in SPLIT_SHAPES]
     xs = [synth.activations(n, rng) for n, p in SPLIT_SHAPES]

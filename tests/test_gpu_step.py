@@ -322,12 +322,17 @@ def _compare_step(cfg, w, kc, vc, tok_in, pos, logits, x, tok_gpu, label):
     return tok_gpu
 
 
-@pytest.mark.parametrize("name,max_seq,pos0,count", [
-    ("step_tiny", 64, 0, 5), ("step_gqa4", 64, 0, 4), ("step_gqa4", 1100, 1000, 3),
-    ("step_hd192", 300, 126, 4), ("step_hd256", 200, 0, 3), ("step_hd256", 200, 127, 3),
+@pytest.mark.parametrize("name,max_seq,pos0,count,sk", [
+    ("step_tiny", 64, 0, 5, None), ("step_gqa4", 64, 0, 4, None), ("step_gqa4", 1100, 1000, 3, None),
+    ("step_hd192", 300, 126, 4, None), ("step_hd256", 200, 0, 3, None), ("step_hd256", 200, 127, 3, None),
+    # every projection on the stream-K schedule (at these sizes the default
+    # keeps it for launches with more row tiles than CUs)
+    ("step_tiny", 64, 0, 4, "2"), ("step_hd192", 300, 126, 3, "2"),
 ], ids=str)
-def test_step_matches_oracle(q8, name, max_seq, pos0, count):
-    log("step vs oracle %s max_seq=%d pos0=%d" % (name, max_seq, pos0))
+def test_step_matches_oracle(q8, monkeypatch, name, max_seq, pos0, count, sk):
+    if sk is not None:
+        monkeypatch.setenv("Q8GEMV_STREAMK", sk)
+    log("step vs oracle %s max_seq=%d pos0=%d streamk=%s" % (name, max_seq, pos0, sk))
     cfg, w, st = _step(q8, name, max_seq)
     kc, vc = _oracle_caches(cfg)
     toks, logits, xs = _run_tokens(q8, st, q8.MODE_GRAPH, pos0, 11, count)
