@@ -63,7 +63,8 @@ enum q8_status {
     Q8_ERR_ALIAS = -4,       /* an output overlaps an input */
     Q8_ERR_NO_DEVICE = -5,   /* no HIP device is visible */
     Q8_ERR_HIP = -6,         /* the HIP runtime reported an error (see q8_0_last_error) */
-    Q8_ERR_TIMEOUT = -7,     /* q8_0_stream_wait ran out of time */
+    Q8_ERR_TIMEOUT = -7,     /* q8_0_stream_wait ran out of time, or a barrier wait of a
+                                Q8_CHAIN_ONE_LAUNCH chain gave up (q8_0_chain_check) */
     Q8_ERR_UNSUPPORTED = -8  /* the current device is not gfx950 */
 };
 
@@ -118,6 +119,12 @@ typedef struct q8_0_chain q8_0_chain; /* opaque */
                                workgroups when it has few rows; results stay bitwise
                                reproducible but round differently from q8_0_gemv */
 #define Q8_CHAIN_XQ 4u      /* every op as q8_0_gemv_q8q8: x quantized to Q8_0, integer dots */
+#define Q8_CHAIN_ONE_LAUNCH 8u /* the whole chain as ONE kernel launch: each run of mutually
+                               independent ops is a phase, split stream-K style over workgroups
+                               that all stay resident, and a phase starts once every
+                               workgroup has finished the one before (a device-wide barrier).
+                               Rounds like Q8_CHAIN_SPLIT_K; not with Q8_CHAIN_XQ or
+                               Q8_CHAIN_PER_OP */
 
 /* decode_chain modes */
 #define Q8_MODE_GRAPH 0     /* replay the recorded hipGraph: one host call per token */
@@ -170,6 +177,14 @@ Q8_API int q8_0_decode_chain(q8_0_chain *chain, int mode, void *stream);
 
 /* Kernel launches one token costs (1 .. n_ops); negative status on a bad handle. */
 Q8_API int q8_0_chain_launches(const q8_0_chain *chain);
+
+/* Q8_OK, or Q8_ERR_TIMEOUT if a barrier wait of a Q8_CHAIN_ONE_LAUNCH chain
+ * gave up (seconds without progress: the GPU was shared with work that kept
+ * the chain's workgroups from all being resident) since the chain was
+ * created; its outputs since then are not to be trusted.  Reads one word
+ * from the device and waits for nothing else: call it once the replays of
+ * interest have finished.  Chains without Q8_CHAIN_ONE_LAUNCH return Q8_OK. */
+Q8_API int q8_0_chain_check(const q8_0_chain *chain);
 
 /* Release the handle (NULL is accepted).  The caller must make sure no
  * replay is still running. */

@@ -38,6 +38,7 @@ Q8_CHAIN_FUSE = 0
 Q8_CHAIN_PER_OP = 1
 Q8_CHAIN_SPLIT_K = 2
 Q8_CHAIN_XQ = 4
+Q8_CHAIN_ONE_LAUNCH = 8
 MODE_GRAPH = 0
 MODE_EAGER = 1
 MODE_SYNC_EACH = 2
@@ -46,11 +47,11 @@ BLOCK_QUANTS = 32
 BLOCK_BYTES = 34
 
 EXPORTS = ("q8_0_gemv", "q8_0_gemm_smallm", "q8_0_chain_create", "q8_0_decode_chain",
-           "q8_0_chain_launches", "q8_0_chain_destroy", "q8_0_stream_wait",
+           "q8_0_chain_launches", "q8_0_chain_check", "q8_0_chain_destroy", "q8_0_stream_wait",
            "q8_0_status_string", "q8_0_last_error", "q8_0_gemv_q8q8", "q8_0_quantize",
            "q8_0_rms_norm", "q8_0_rope", "q8_0_append_kv", "q8_0_attention_decode",
            "q8_0_add_inplace", "q8_0_silu_hadamard", "q8_0_argmax",
-           "q8_0_step_create", "q8_0_step_reset", "q8_0_step_run", "q8_0_step_launches",
+           "q8_0_step_create", "q8_0_step_reset", "q8_0_step_run", "q8_0_step_launches", "q8_0_step_check",
            "q8_0_step_buffers", "q8_0_step_destroy")
 
 NO_INDEX = 0xFFFFFFFF   # argmax of a row of NaN
@@ -99,6 +100,7 @@ def _load():
                                       ctypes.POINTER(vp)]
     lib.q8_0_decode_chain.argtypes = [vp, ctypes.c_int, vp]
     lib.q8_0_chain_launches.argtypes = [vp]
+    lib.q8_0_chain_check.argtypes = [vp]
     lib.q8_0_chain_destroy.argtypes = [vp]
     lib.q8_0_stream_wait.argtypes = [vp, i64]
     lib.q8_0_status_string.argtypes = [ctypes.c_int]
@@ -119,6 +121,7 @@ def _load():
     lib.q8_0_step_reset.argtypes = [vp, i64, u32, vp]
     lib.q8_0_step_run.argtypes = [vp, i32, vp]
     lib.q8_0_step_launches.argtypes = [vp]
+    lib.q8_0_step_check.argtypes = [vp]
     lib.q8_0_step_buffers.argtypes = [vp, ctypes.POINTER(Q8StepBufs)]
     lib.q8_0_step_destroy.argtypes = [vp]
     for name in EXPORTS:
@@ -267,7 +270,8 @@ class Chain:
     keeps references to them.
     """
 
-    def __init__(self, ops: Sequence, fuse: bool = True, split_k: bool = False, xq: bool = False):
+    def __init__(self, ops: Sequence, fuse: bool = True, split_k: bool = False, xq: bool = False,
+                 one_launch: bool = False):
         torch = _torch()
         arr = (Q8Op * len(ops))()
         self._keep = []
@@ -282,7 +286,7 @@ class Chain:
             self._keep.append((x, w, y))
         h = ctypes.c_void_p()
         flags = ((Q8_CHAIN_FUSE if fuse else Q8_CHAIN_PER_OP) | (Q8_CHAIN_SPLIT_K if split_k else 0) |
-                 (Q8_CHAIN_XQ if xq else 0))
+                 (Q8_CHAIN_XQ if xq else 0) | (Q8_CHAIN_ONE_LAUNCH if one_launch else 0))
         check(lib.q8_0_chain_create(arr, len(ops), flags, ctypes.byref(h)))
         self._h = h
         self.n_ops = len(ops)
@@ -295,6 +299,13 @@ class Chain:
         if self._h is None:
             raise RuntimeError("chain is closed")
         check(lib.q8_0_decode_chain(self._h, mode, _stream_handle(stream)))
+
+    def check(self) -> None:
+        """Raise Q8Error (Q8_ERR_TIMEOUT) if a barrier wait of a one-launch
+        chain gave up since the chain was created."""
+        if self._h is None:
+            raise RuntimeError("chain is closed")
+        check(lib.q8_0_chain_check(self._h))
 
     def close(self) -> None:
         if getattr(self, "_h", None) is not None:
@@ -506,6 +517,11 @@ class Step:
 
     def run(self, mode: int = MODE_GRAPH, stream=None) -> None:
         check(lib.q8_0_step_run(self._handle(), int(mode), _stream_handle(stream)))
+
+    def check(self) -> None:
+        """Raise Q8Error (Q8_ERR_TIMEOUT) if a barrier wait of one of the
+        step's one-launch matvec chains gave up since the step was created."""
+        check(lib.q8_0_step_check(self._handle()))
 
     def buffer(self, name: str):
         """A device tensor viewing one of the step's buffers (token, pos, x,

@@ -443,6 +443,7 @@ struct q8_0_chain {
     struct Launch {
         bool fused;
         bool sk;              // stream-K launch (d_ops, d_pieces, d_begin; d_tiles = tail tiles)
+        bool phased;          // one launch of n_phases phases (d_phases, d_bar, d_err)
         int xmode;            // XMode: how the activations are read
         Variant v;
         OpDesc single;        // per-op launch
@@ -451,10 +452,15 @@ struct q8_0_chain {
         const Piece *d_pieces;
         const uint32_t *d_begin;
         int64_t n_sk;         // stream-K workgroups (the tail tiles' follow)
+        const PhaseDesc *d_phases;
+        int n_phases;
+        uint32_t *d_sync;     // barrier state (kPhasedSyncBytes)
+        uint32_t per, nx;     // workgroups per XCD, XCDs
         int64_t grid;
     };
     std::vector<Launch> launches;
     void *d_table = nullptr;
+    uint32_t *d_err = nullptr;   // one-launch chains: the barrier timeout flag
     hipStream_t capture = nullptr;
     hipGraph_t graph = nullptr;
     hipGraphExec_t exec = nullptr;
@@ -463,6 +469,7 @@ struct q8_0_chain {
 namespace {
 
 hipError_t issue(const q8_0_chain::Launch &L, hipStream_t s) {
+    if (L.phased) return launch_gemv_phased(L.d_phases, L.n_phases, L.d_sync, L.per, L.nx, L.grid, L.v.pf, s);
     if (L.sk)
         return launch_gemv_streamk(L.d_ops, L.d_pieces, L.d_begin, L.d_tiles, L.n_sk, L.grid - L.n_sk,
                                    L.v.pf, s, L.xmode);
@@ -522,6 +529,38 @@ bool depends(const q8_0_op &a, const q8_0_op &b, const OpExtra *ea = nullptr,
     return false;
 }
 
+// How the one-launch kernel's `wgs` workgroups spread over the XCDs of
+// device `dev`: a census launch of the same kernel and grid, once per
+// (device, wgs).  Sets *per and *nx and returns true when every XCD holds
+// the same number (the two-level barrier counts on it).
+bool phased_split(int dev, int64_t wgs, uint32_t *per, uint32_t *nx) {
+    static std::mutex mu;
+    static std::map<std::pair<int, int64_t>, std::pair<uint32_t, uint32_t>> known;
+    std::lock_guard<std::mutex> lock(mu);
+    const auto key = std::make_pair(dev, wgs);
+    auto it = known.find(key);
+    if (it == known.end()) {
+        uint32_t p = 0, n = 0;
+        uint32_t *d = nullptr;
+        if (hipMalloc(&d, (size_t)wgs * sizeof(uint32_t)) == hipSuccess) {
+            std::vector<uint32_t> h((size_t)wgs, 0xFFFFFFFFu);
+            if (launch_gemv_phased_census(d, wgs, nullptr) == hipSuccess &&
+                hipMemcpy(h.data(), d, h.size() * sizeof(uint32_t), hipMemcpyDeviceToHost) == hipSuccess) {
+                std::map<uint32_t, int64_t> count;
+                for (uint32_t x : h) count[x]++;
+                bool even = !count.empty() && count.size() <= 16 && count.rbegin()->first < 16;
+                for (auto &kv : count) even = even && kv.second * (int64_t)count.size() == wgs;
+                if (even) { n = (uint32_t)count.size(); p = (uint32_t)(wgs / n); }
+            }
+            (void)hipFree(d);
+        }
+        it = known.emplace(key, std::make_pair(p, n)).first;
+    }
+    *per = it->second.first;
+    *nx = it->second.second;
+    return *nx > 0;
+}
+
 // Stream-K schedule of a launch's ops on `wgs` one-wave workgroups: all
 // (op, row tile, group) items, in that order, are cut into wgs equal
 // contiguous ranges (workgroup b takes [b*N/wgs, (b+1)*N/wgs)), and each
@@ -572,6 +611,43 @@ void plan_pieces(const std::vector<OpDesc> &ds, int64_t wgs, std::vector<Piece> 
     }
 }
 
+// Does phase k (segment k) of a one-launch chain read memory that an earlier
+// phase j read and a phase in [j, k) wrote?  Then a CU may still hold
+// phase j's copy in its L1.  Ranges are widened to whole 128-byte lines.
+bool phase_rereads(const q8_0_op *ops, const OpExtra *extra,
+                   const std::vector<std::pair<int64_t, int64_t>> &segs, size_t k) {
+    auto line = [](const void *p, int64_t n, uintptr_t &a, uintptr_t &b) {
+        a = (uintptr_t)p & ~(uintptr_t)127;
+        b = ((uintptr_t)p + (uintptr_t)n + 127) & ~(uintptr_t)127;
+    };
+    auto meet = [&](const void *p, int64_t n, const void *q, int64_t m) {
+        uintptr_t a0, a1, b0, b1;
+        line(p, n, a0, a1);
+        line(q, m, b0, b1);
+        return a0 < b1 && b0 < a1;
+    };
+    auto ex = [&](int64_t i) { return extra ? &extra[i] : nullptr; };
+    if (segs.back().second > 512) return k > 0;   // long chains: every barrier acquires
+    for (int64_t i = segs[k].first; i < segs[k].second; ++i) {
+        const Ranges R = ranges_of(ops[i], ex(i));
+        for (int r = 0; r < R.nr; ++r)
+            for (size_t j = 0; j < k; ++j)
+                for (int64_t a = segs[j].first; a < segs[j].second; ++a) {
+                    const Ranges A = ranges_of(ops[a], ex(a));
+                    for (int ra = 0; ra < A.nr; ++ra) {
+                        if (!meet(R.r[r], R.rn[r], A.r[ra], A.rn[ra])) continue;
+                        for (size_t w = j; w < k; ++w)
+                            for (int64_t b = segs[w].first; b < segs[w].second; ++b) {
+                                const Ranges B = ranges_of(ops[b], ex(b));
+                                for (int wb = 0; wb < B.nw; ++wb)
+                                    if (meet(R.r[r], R.rn[r], B.w[wb], B.wn[wb])) return true;
+                            }
+                    }
+                }
+    }
+    return false;
+}
+
 void set_extra(OpDesc &d, const OpExtra *e) {
     if (!e) return;
     d.x_up = e->x_up;
@@ -605,8 +681,11 @@ int q8::chain_create_ex(const q8_0_op *ops, int64_t n_ops, uint32_t flags, const
     *out = nullptr;
     if (!ops || n_ops <= 0 || n_ops > Q8_MAX_CHAIN_OPS)
         return fail(Q8_ERR_INVALID_ARG, "q8_0_chain_create: need 1..65535 ops");
-    if (flags & ~(uint32_t)(Q8_CHAIN_PER_OP | Q8_CHAIN_SPLIT_K | Q8_CHAIN_XQ))
+    if (flags & ~(uint32_t)(Q8_CHAIN_PER_OP | Q8_CHAIN_SPLIT_K | Q8_CHAIN_XQ | Q8_CHAIN_ONE_LAUNCH))
         return fail(Q8_ERR_INVALID_ARG, "q8_0_chain_create: unknown flags");
+    const bool one = (flags & Q8_CHAIN_ONE_LAUNCH) != 0;
+    if (one && (flags & (Q8_CHAIN_XQ | Q8_CHAIN_PER_OP)))
+        return fail(Q8_ERR_INVALID_ARG, "q8_0_chain_create: Q8_CHAIN_ONE_LAUNCH takes neither XQ nor PER_OP");
     const int emode = extra ? extra[0].mode : kXFloat;
     if (extra && (flags & Q8_CHAIN_XQ))
         return fail(Q8_ERR_INVALID_ARG, "q8_0_chain_create: these inputs have no integer form");
@@ -618,8 +697,10 @@ int q8::chain_create_ex(const q8_0_op *ops, int64_t n_ops, uint32_t flags, const
         if (!extra) continue;
         const OpExtra &e = extra[i];
         const int64_t xb = 4 * ops[i].n, yb = 4 * ops[i].p;
-        bool ok = e.mode == emode;
-        if (e.mode == kXSiluUp) ok = ok && a16(e.x_up) && !overlaps(ops[i].y, yb, e.x_up, xb);
+        // one-launch chains take a mode per phase (kXFloat: none)
+        bool ok = one || e.mode == emode;
+        if (e.mode == kXFloat) ok = one;
+        else if (e.mode == kXSiluUp) ok = ok && a16(e.x_up) && !overlaps(ops[i].y, yb, e.x_up, xb);
         else if (e.mode == kXNormAdd)   // (the writer of x_out needs a fast tile: p >= 8)
             ok = ok && a16(e.x_res) && a16(e.norm_w) && (!e.x_out || (a16(e.x_out) && ops[i].p >= 8)) &&
                  !overlaps(ops[i].y, yb, e.x_res, xb) &&
@@ -647,6 +728,8 @@ int q8::chain_create_ex(const q8_0_op *ops, int64_t n_ops, uint32_t flags, const
         int64_t b = 0;
         for (int64_t i = 1; i <= n_ops; ++i) {
             bool cut = (i == n_ops);
+            // (a one-launch chain's phase reads its activations in one mode)
+            if (one && extra && extra[i].mode != extra[b].mode) cut = true;
             for (int64_t j = b; !cut && j < i; ++j)
                 cut = depends(ops[j], ops[i], extra ? &extra[j] : nullptr, extra ? &extra[i] : nullptr);
             if (cut) { segs.push_back({b, i}); b = i; }
@@ -670,6 +753,19 @@ int q8::chain_create_ex(const q8_0_op *ops, int64_t n_ops, uint32_t flags, const
     // runs); Q8GEMV_SK_PF sets its groups in flight (1 or 2).
     const int sk_mode = env_int("Q8GEMV_STREAMK", 1);
     const int sk_pf = env_int("Q8GEMV_SK_PF", 1) == 2 ? 2 : 1;
+    // a one-launch chain: every phase stream-K on the same workgroups, as
+    // many as the CUs hold at once (four one-wave workgroups fill a CU's LDS)
+    // (where the census finds the workgroups unevenly spread over the XCDs,
+    // the phases become launches of their own, planned like SPLIT_K)
+    int64_t one_wgs = 0;
+    uint32_t xcc_per = 0, xcc_n = 0;
+    bool phased = false;
+    if (one) {
+        const int per_cu = std::min(4, gemv_phased_blocks_per_cu(1));
+        if (per_cu < 1) { chain_free(c); return fail(Q8_ERR_HIP, "q8_0_chain_create: occupancy query failed"); }
+        one_wgs = per_cu * cus;
+        phased = phased_split(dev, one_wgs, &xcc_per, &xcc_n);
+    }
     std::vector<OpDesc> h_ops;
     std::vector<Tile> h_tiles;
     std::vector<Piece> h_pieces;
@@ -683,6 +779,7 @@ int q8::chain_create_ex(const q8_0_op *ops, int64_t n_ops, uint32_t flags, const
         bool sk;
         size_t piece0, begin0;
         int64_t n_sk;
+        int xmode;   // one-launch phases
     };
     std::vector<SegInfo> info;
     for (auto &sg : segs) {
@@ -690,7 +787,10 @@ int q8::chain_create_ex(const q8_0_op *ops, int64_t n_ops, uint32_t flags, const
         int64_t target = 1;
         Variant v = fused ? v_fused : v_single;
         bool sk = false;
-        if (split) {
+        if (phased) {
+            sk = true;
+            v = Variant{1, 1};
+        } else if (split || one) {
             int64_t row_tiles = 0;
             for (int64_t i = sg.first; i < sg.second; ++i) {
                 const OpDesc d = plan_op(ops[i].x, ops[i].w, ops[i].y, 1, ops[i].n, ops[i].p, false, 1);
@@ -709,8 +809,9 @@ int q8::chain_create_ex(const q8_0_op *ops, int64_t n_ops, uint32_t flags, const
             if (sk) v = Variant{1, sk_pf};
         }
         // four-wave split workgroups take the standalone K split inside the workgroup
-        const bool standalone = (!split && !fused) || (split && v.nw > 1);
-        SegInfo si{h_ops.size(), h_tiles.size(), 0, fused, OpDesc{}, v, sk, h_pieces.size(), h_begin.size(), 0};
+        const bool standalone = (!(split || one) && !fused) || ((split || one) && v.nw > 1);
+        SegInfo si{h_ops.size(), h_tiles.size(), 0, fused, OpDesc{}, v, sk, h_pieces.size(), h_begin.size(), 0,
+                   extra ? extra[sg.first].mode : kXFloat};
         if (sk) {
             // one-wave workgroups, four per CU (their two stages fill its LDS),
             // each at least kSkMinItems (row tile, group) items
@@ -724,7 +825,7 @@ int q8::chain_create_ex(const q8_0_op *ops, int64_t n_ops, uint32_t flags, const
                 items += (int64_t)d.fast_tiles * d.gsr;
                 ds.push_back(d);
             }
-            const int64_t wgs = std::min<int64_t>(4 * cus, std::max<int64_t>(1, items / kSkMinItems));
+            const int64_t wgs = std::min<int64_t>(phased ? one_wgs : 4 * cus, std::max<int64_t>(1, items / kSkMinItems));
             std::vector<Piece> pcs;
             std::vector<uint32_t> bg;
             std::vector<int32_t> maxc;
@@ -776,7 +877,11 @@ int q8::chain_create_ex(const q8_0_op *ops, int64_t n_ops, uint32_t flags, const
     const size_t pb = h_pieces.size() * sizeof(Piece);
     const size_t bb = h_begin.size() * sizeof(uint32_t);
     const size_t t_at = ob, p_at = up256(ob + tb), b_at = up256(p_at + pb);
-    size_t wb = up256(b_at + bb);   // running end of the block
+    // one-launch chains: the phase table, a barrier counter per phase, the
+    // timeout flag
+    const size_t nph = phased ? segs.size() : 0;
+    const size_t ph_at = up256(b_at + bb), sync_at = up256(ph_at + nph * sizeof(PhaseDesc));
+    size_t wb = phased ? up256(sync_at + kPhasedSyncBytes) : up256(b_at + bb);   // running end of the block
     std::vector<std::pair<OpDesc *, size_t>> ws;  // (op, offset of its partials)
     auto part_bytes = [](const OpDesc &d) {
         return (size_t)std::max(d.slices, d.sk_slots) * d.nsr * d.rs * sizeof(float);
@@ -805,6 +910,19 @@ int q8::chain_create_ex(const q8_0_op *ops, int64_t n_ops, uint32_t flags, const
         if (tb) std::memcpy(host.data() + t_at, h_tiles.data(), tb);
         if (pb) std::memcpy(host.data() + p_at, h_pieces.data(), pb);
         if (bb) std::memcpy(host.data() + b_at, h_begin.data(), bb);
+        for (size_t k = 0; k < nph; ++k) {
+            PhaseDesc ph;
+            std::memset(&ph, 0, sizeof ph);
+            ph.ops = (const OpDesc *)base + info[k].op0;
+            ph.pieces = (const Piece *)(base + p_at) + info[k].piece0;
+            ph.begin = (const uint32_t *)(base + b_at) + info[k].begin0;
+            ph.tails = (const Tile *)(base + t_at) + info[k].tile0;
+            ph.n_sk = (int32_t)info[k].n_sk;
+            ph.n_tail = (int32_t)info[k].ntiles;
+            ph.xmode = info[k].xmode;
+            ph.acquire = phase_rereads(ops, extra, segs, k) ? 1 : 0;
+            std::memcpy(host.data() + ph_at + k * sizeof(PhaseDesc), &ph, sizeof ph);
+        }
         if ((e = hipMemcpy(c->d_table, host.data(), host.size(), hipMemcpyHostToDevice)) != hipSuccess) {
             chain_free(c);
             return fail_hip(e, "q8_0_chain_create hipMemcpy");
@@ -814,10 +932,24 @@ int q8::chain_create_ex(const q8_0_op *ops, int64_t n_ops, uint32_t flags, const
     const Tile *d_tiles = (const Tile *)((const char *)c->d_table + t_at);
     const Piece *d_pieces = (const Piece *)((const char *)c->d_table + p_at);
     const uint32_t *d_begin = (const uint32_t *)((const char *)c->d_table + b_at);
-    for (size_t k = 0; k < segs.size(); ++k) {
+    if (phased) {
         q8_0_chain::Launch L;
         std::memset(&L, 0, sizeof L);
-        L.xmode = extra ? emode : (flags & Q8_CHAIN_XQ) ? kXQuant : kXFloat;
+        L.phased = true;
+        L.v = Variant{1, 1};
+        L.d_phases = (const PhaseDesc *)((const char *)c->d_table + ph_at);
+        L.n_phases = (int)nph;
+        L.d_sync = (uint32_t *)((char *)c->d_table + sync_at);
+        L.per = xcc_per;
+        L.nx = xcc_n;
+        L.grid = one_wgs;
+        c->d_err = L.d_sync + kPhasedSyncErr;
+        c->launches.push_back(L);
+    }
+    for (size_t k = 0; k < segs.size() && !phased; ++k) {
+        q8_0_chain::Launch L;
+        std::memset(&L, 0, sizeof L);
+        L.xmode = (flags & Q8_CHAIN_XQ) ? kXQuant : info[k].xmode;
         L.v = info[k].v;
         if (info[k].sk) {
             L.sk = true;
@@ -883,6 +1015,16 @@ int q8_0_decode_chain(q8_0_chain *c, int mode, void *stream) {
         if (mode == Q8_MODE_SYNC_EACH && (e = hipStreamSynchronize(s)) != hipSuccess)
             return fail_hip(e, "hipStreamSynchronize");
     }
+    return Q8_OK;
+}
+
+int q8_0_chain_check(const q8_0_chain *c) {
+    if (!c) return fail(Q8_ERR_INVALID_ARG, "q8_0_chain_check: null chain");
+    if (!c->d_err) return Q8_OK;
+    uint32_t err = 0;
+    const hipError_t e = hipMemcpy(&err, c->d_err, sizeof err, hipMemcpyDeviceToHost);
+    if (e != hipSuccess) return fail_hip(e, "q8_0_chain_check hipMemcpy");
+    if (err) return fail(Q8_ERR_TIMEOUT, "q8_0_chain_check: a barrier wait of the one-launch chain gave up");
     return Q8_OK;
 }
 

@@ -46,6 +46,15 @@ __device__ __forceinline__ void chunk_offsets(uint32_t (&off)[kGroupChunks], int
     }
 }
 
+// A pointer that is the same in every lane, made visibly so for the
+// compiler (it goes into a scalar register pair).
+__device__ __forceinline__ const uint8_t *uniform_ptr(const uint8_t *p) {
+    const uint64_t v = (uint64_t)(uintptr_t)p;
+    const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
+    const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
+    return (const uint8_t *)(uintptr_t)(((uint64_t)hi << 32) | lo);
+}
+
 // The kernels issue their direct loads from inline asm.  The compiler tracks
 // LDS-DMA it emits itself and, unable to tell the two stages apart, waits
 // for ALL outstanding loads before any LDS read -- which would stall every
@@ -56,10 +65,11 @@ __device__ __forceinline__ void chunk_offsets(uint32_t (&off)[kGroupChunks], int
 // else in these kernels uses m0.
 #pragma clang diagnostic push
 #pragma clang diagnostic ignored "-Winline-asm"
-// 16 bytes per lane: global (sbase + voff) -> LDS (m0 + 16 * lane)
+// 16 bytes per lane: global (sbase + voff) -> LDS (m0 + 16 * lane).  sbase
+// must be the same in every lane (it is taken from the first).
 __device__ __forceinline__ void dma16_s(const uint8_t *sbase, uint32_t voff, uint32_t lds) {
     asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2"
-                 :: "s"(lds), "v"(voff), "s"(sbase) : "memory", "m0");
+                 :: "s"(lds), "v"(voff), "s"(uniform_ptr(sbase)) : "memory", "m0");
 }
 // 16 bytes per lane: global (per-lane address) -> LDS (m0 + 16 * lane)
 __device__ __forceinline__ void dma16_v(const void *addr, uint32_t lds) {
@@ -72,15 +82,6 @@ template <int N>
 __device__ __forceinline__ void wait_vm_asm() {
     static_assert(N >= 0 && N < 64, "vmcnt is 6 bits");
     asm volatile("s_waitcnt vmcnt(%0)" :: "n"(N) : "memory");
-}
-
-// A pointer that is the same in every lane, made visibly so for the
-// compiler (it goes into a scalar register pair).
-__device__ __forceinline__ const uint8_t *uniform_ptr(const uint8_t *p) {
-    const uint64_t v = (uint64_t)(uintptr_t)p;
-    const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
-    const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
-    return (const uint8_t *)(uintptr_t)(((uint64_t)hi << 32) | lo);
 }
 
 __device__ __forceinline__ uint32_t lds_addr(const uint8_t *p) {

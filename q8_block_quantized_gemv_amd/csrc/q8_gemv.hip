@@ -276,7 +276,7 @@ struct TileJob {
 };
 
 template <int RS, int NW, int PF, int XM>
-__device__ void fast_job(const OpDesc &op, const TileJob &job, uint8_t *stage) {
+__device__ __forceinline__ void fast_job(const OpDesc &op, const TileJob &job, uint8_t *stage) {
     constexpr int SB = stage_bytes<XM>();
     // memory operations per group: 17 direct loads of W, then the x slice
     // (one more direct load; two for kXSiluUp; three vector loads for kXNormAdd)
@@ -446,22 +446,11 @@ __global__ __launch_bounds__(NW * kWave) void k_q8_gemv_fused(const OpDesc *__re
     run_tile<NW, PF, XM>(op, tl.tile, stage);
 }
 
-// Stream-K: one-wave workgroups, each walking its pieces (contiguous runs of
-// an equal share of all (row tile, group) items of the launch's ops) in
-// order; the workgroups after the first n_sk run tail tiles.
+// Stream-K: workgroup b (one wave) walks its pieces, contiguous runs of an
+// equal share of all (row tile, group) items of the launch's ops, in order.
 template <int PF, int XM>
-__global__ __launch_bounds__(kWave) void k_q8_gemv_sk(const OpDesc *__restrict__ ops,
-                                                      const Piece *__restrict__ pieces,
-                                                      const uint32_t *__restrict__ begin,
-                                                      const Tile *__restrict__ tails, uint32_t n_sk) {
-    __shared__ __attribute__((aligned(16))) uint8_t stage[kBufs * stage_bytes<XM>()];
-    const uint32_t b = blockIdx.x;
-    if (b >= n_sk) {
-        const Tile tl = tails[b - n_sk];
-        if constexpr (XM == kXQuant) tail_tile_xq(ops[tl.op], tl.tile & ~kTailBit, 1);
-        else tail_tile<XM>(ops[tl.op], tl.tile & ~kTailBit, 1);
-        return;
-    }
+__device__ __forceinline__ void run_pieces(const OpDesc *__restrict__ ops, const Piece *__restrict__ pieces,
+                                           const uint32_t *__restrict__ begin, uint32_t b, uint8_t *stage) {
     const uint32_t e = begin[b + 1];
     for (uint32_t i = begin[b]; i < e; ++i) {
         const Piece pc = pieces[i];
@@ -478,6 +467,152 @@ __global__ __launch_bounds__(kWave) void k_q8_gemv_sk(const OpDesc *__restrict__
             case 2: fast_job<2, 1, PF, XM>(op, job, stage); break;
             case 4: fast_job<4, 1, PF, XM>(op, job, stage); break;
             default: fast_job<8, 1, PF, XM>(op, job, stage); break;
+        }
+    }
+}
+
+template <int XM>
+__device__ __forceinline__ void run_tail(const OpDesc &op, uint32_t t) {
+    if constexpr (XM == kXQuant) tail_tile_xq(op, t & ~kTailBit, 1);
+    else tail_tile<XM>(op, t & ~kTailBit, 1);
+}
+
+// The workgroups after the first n_sk run tail tiles.
+template <int PF, int XM>
+__global__ __launch_bounds__(kWave) void k_q8_gemv_sk(const OpDesc *__restrict__ ops,
+                                                      const Piece *__restrict__ pieces,
+                                                      const uint32_t *__restrict__ begin,
+                                                      const Tile *__restrict__ tails, uint32_t n_sk) {
+    __shared__ __attribute__((aligned(16))) uint8_t stage[kBufs * stage_bytes<XM>()];
+    const uint32_t b = blockIdx.x;
+    if (b >= n_sk) {
+        const Tile tl = tails[b - n_sk];
+        run_tail<XM>(ops[tl.op], tl.tile);
+        return;
+    }
+    run_pieces<PF, XM>(ops, pieces, begin, b, stage);
+}
+
+// ---------------------------------------------------------------- one launch, many phases
+// A chain of dependent matvecs in one launch: every workgroup takes its
+// stream-K share of phase s, then waits until all workgroups have finished
+// phase s before it starts phase s + 1.  All workgroups are resident at
+// once (the host sizes the grid by occupancy), so every wait ends; a wait
+// still gives up after kSpinLimit polls (about a second) and flags err, and
+// once err is set the waits of the launch give up at once, so that no wave
+// can spin for long.
+//
+// The barrier is two-level, by XCD (each has its own L2): a workgroup
+// counts in on its XCD's counter once its own memory operations are done
+// (its stores are then in that L2); the last of the XCD's `per` workgroups
+// writes the L2 back (agent-scope release), counts the XCD in on the global
+// counter, waits for all `nx` XCDs, invalidates the L2 (acquire) and raises
+// the XCD's flag; the others wait for the flag and invalidate their CU's L1.
+// One release and one acquire per XCD instead of per wave, and no counter
+// that every wave hits: measured 3.6 us per barrier against 39 us for one
+// counter and per-wave fences.  Counts run on across launches (generation
+// g = the flag's value at launch start + s), compared modulo 2^32, so
+// nothing has to be cleared between launches.
+//
+// A CU's L1 is only dropped by a wave's own agent-scope acquire (9.9 us per
+// barrier when every wave does it).  The L1 holds only lines this launch
+// has read (each launch starts with it clean), so it can only be stale for
+// memory that an earlier phase read and a later one rewrote; the host marks
+// the phases that read such memory (PhaseDesc::acquire) and only their
+// barriers pay for the per-wave acquire.
+constexpr uint32_t kSpinLimit = 1u << 20;
+// sync words, one 256-B line each: global counter, per-XCD counters,
+// per-XCD flags, err
+constexpr int kSyncLine = 64;
+constexpr int kMaxXcc = 16;
+__device__ __forceinline__ uint32_t *sync_global(uint32_t *sy) { return sy; }
+__device__ __forceinline__ uint32_t *sync_local(uint32_t *sy, uint32_t x) { return sy + kSyncLine * (1 + x); }
+__device__ __forceinline__ uint32_t *sync_flag(uint32_t *sy, uint32_t x) { return sy + kSyncLine * (1 + kMaxXcc + x); }
+__device__ __forceinline__ uint32_t *sync_err(uint32_t *sy) { return sy + kSyncLine * (1 + 2 * kMaxXcc); }
+
+__device__ __forceinline__ uint32_t xcc_id() {
+    uint32_t v;
+    asm volatile("s_getreg_b32 %0, hwreg(HW_REG_XCC_ID, 0, 4)" : "=s"(v));
+    return v & (kMaxXcc - 1);
+}
+
+__device__ __forceinline__ uint32_t load_agent(uint32_t *p) {
+    return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Spin (lane 0) until *p has reached `target` (modulo 2^32).
+__device__ __forceinline__ void spin_to(uint32_t *p, uint32_t target, uint32_t *err) {
+    uint32_t polls = 0;
+    while ((int32_t)(load_agent(p) - target) < 0) {
+        __builtin_amdgcn_s_sleep(1);
+        if ((++polls & 1023u) == 0 && load_agent(err)) break;
+        if (polls == kSpinLimit) {
+            __hip_atomic_store(err, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            break;
+        }
+    }
+}
+
+// Barrier generation g among all workgroups (per on each of nx XCDs);
+// all: every wave takes an agent-scope acquire after it.
+__device__ __forceinline__ void phase_sync(uint32_t *sy, uint32_t x, uint32_t g, uint32_t per, uint32_t nx,
+                                           bool all) {
+    if (lane_id() == 0) {
+        uint32_t *err = sync_err(sy);
+        __builtin_amdgcn_s_waitcnt(0);   // this wave's loads and stores are done
+        const uint32_t prev =
+            __hip_atomic_fetch_add(sync_local(sy, x), 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        if (prev == g * per - 1u) {
+            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+            __hip_atomic_fetch_add(sync_global(sy), 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            spin_to(sync_global(sy), g * nx, err);
+            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+            // the invalidation completes before the flag lets the XCD's
+            // other waves load through this L2
+            __builtin_amdgcn_s_waitcnt(0);
+            __hip_atomic_store(sync_flag(sy, x), g, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        } else {
+            spin_to(sync_flag(sy, x), g, err);
+            if (all) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+        }
+    }
+    asm volatile("" ::: "memory");
+}
+
+template <int PF, int XM>
+__device__ __forceinline__ void phase_work(const PhaseDesc &ph, uint32_t b, uint32_t wgs, uint8_t *stage) {
+    if (b < (uint32_t)ph.n_sk) run_pieces<PF, XM>(ph.ops, ph.pieces, ph.begin, b, stage);
+    for (uint32_t t = b; t < (uint32_t)ph.n_tail; t += wgs) {
+        const Tile tl = ph.tails[t];
+        run_tail<XM>(ph.ops[tl.op], tl.tile);
+    }
+}
+
+// The largest stage of the modes a phase can have.
+constexpr int kPhasedStage = stage_bytes<kXSiluUp>();
+
+// n_phases == 0: census -- each workgroup writes its XCD to census[b].
+template <int PF>
+__global__ __launch_bounds__(kWave) void k_q8_gemv_phased(const PhaseDesc *__restrict__ phases, int n_phases,
+                                                          uint32_t *sy, uint32_t per, uint32_t nx,
+                                                          uint32_t *census) {
+    __shared__ __attribute__((aligned(16))) uint8_t stage[kBufs * kPhasedStage];
+    const uint32_t b = blockIdx.x, wgs = gridDim.x;
+    const uint32_t x = xcc_id();
+    if (n_phases == 0) {
+        if (lane_id() == 0) census[b] = x;
+        return;
+    }
+    // the generation before this launch: the XCD's flag cannot move until
+    // every workgroup of the XCD has arrived at this launch's first barrier
+    const uint32_t g0 = __builtin_amdgcn_readfirstlane(load_agent(sync_flag(sy, x)));
+    for (int s = 0; s < n_phases; ++s) {
+        const PhaseDesc ph = phases[s];
+        if (s > 0) phase_sync(sy, x, g0 + (uint32_t)s, per, nx, ph.acquire != 0);
+        switch (ph.xmode) {
+            case kXSiluUp: phase_work<PF, kXSiluUp>(ph, b, wgs, stage); break;
+            case kXNormAdd: phase_work<PF, kXNormAdd>(ph, b, wgs, stage); break;
+            default: phase_work<PF, kXFloat>(ph, b, wgs, stage); break;
         }
     }
 }
@@ -602,6 +737,29 @@ hipError_t launch_gemv_streamk(const OpDesc *d_ops, const Piece *d_pieces, const
         default: return hipErrorInvalidValue;
     }
 #undef Q8_SK
+}
+
+hipError_t launch_gemv_phased(const PhaseDesc *d_phases, int n_phases, uint32_t *d_sync, uint32_t per,
+                              uint32_t nx, int64_t wgs, int pf, hipStream_t s) {
+    if (n_phases <= 0 || wgs <= 0 || pf != 1 || nx == 0 || nx > (uint32_t)kMaxXcc || (uint64_t)per * nx != (uint64_t)wgs)
+        return hipErrorInvalidValue;
+    hipLaunchKernelGGL((k_q8_gemv_phased<1>), dim3((unsigned)wgs), dim3(kWave), 0, s, d_phases, n_phases,
+                       d_sync, per, nx, (uint32_t *)nullptr);
+    return hipGetLastError();
+}
+
+hipError_t launch_gemv_phased_census(uint32_t *d_census, int64_t wgs, hipStream_t s) {
+    if (wgs <= 0) return hipErrorInvalidValue;
+    hipLaunchKernelGGL((k_q8_gemv_phased<1>), dim3((unsigned)wgs), dim3(kWave), 0, s,
+                       (const PhaseDesc *)nullptr, 0, (uint32_t *)nullptr, 0u, 0u, d_census);
+    return hipGetLastError();
+}
+
+int gemv_phased_blocks_per_cu(int pf) {
+    int n = 0;
+    if (pf != 1) return 0;
+    const hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, k_q8_gemv_phased<1>, kWave, 0);
+    return e == hipSuccess ? n : 0;
 }
 
 hipError_t launch_quantize_x(const float *x, void *xq, int64_t n, hipStream_t s) {

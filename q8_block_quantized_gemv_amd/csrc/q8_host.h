@@ -28,7 +28,8 @@ Q8_HIDDEN int workspace_for(int dev, hipStream_t s, size_t ws_bytes, size_t cnt_
 // activations (XMode) and the extra vectors that takes, n floats each,
 // 16-byte aligned.
 struct OpExtra {
-    int mode = 0;                  // kXSiluUp or kXNormAdd; every op of a chain the same
+    int mode = 0;                  // kXSiluUp or kXNormAdd, the same for every op of a chain;
+                                   // Q8_CHAIN_ONE_LAUNCH chains: one per phase, kXFloat for none
     const float *x_up = nullptr;   // kXSiluUp: input silu(x) * x_up
     const float *x_res = nullptr;  // kXNormAdd: input rms_norm(x + x_res) * norm_w
     const float *norm_w = nullptr;

@@ -103,6 +103,24 @@ struct Piece {
     uint32_t slot, nslots;
 };
 
+// One phase of a one-launch chain: a stream-K schedule (pieces, then tail
+// tiles) of mutually independent ops that read their activations in one
+// mode.  The phases run in order, separated by device-wide barriers.
+struct PhaseDesc {
+    const OpDesc *ops;
+    const Piece *pieces;
+    const uint32_t *begin;   // n_sk + 1 piece offsets
+    const Tile *tails;
+    int32_t n_sk;            // workgroups with pieces (the first n_sk of the launch)
+    int32_t n_tail;          // tail tiles, taken round robin by all workgroups
+    int32_t xmode;           // XMode (kXFloat, kXSiluUp or kXNormAdd)
+    // 1: this phase reads memory that an earlier phase of the launch read
+    // and a later one rewrote, so every wave drops its CU's cached lines at
+    // the barrier before it (an agent-scope acquire) -- otherwise only the
+    // XCD leaders do, for the L2s
+    int32_t acquire;
+};
+
 // Matvec kernel shape: waves per workgroup (1, 2 or 4) and groups each wave
 // keeps in flight ahead of the one it computes (1 or 2).
 struct Variant {
@@ -132,6 +150,22 @@ hipError_t launch_gemv_fused(const OpDesc *d_ops, const Tile *d_tiles, const Var
 hipError_t launch_gemv_streamk(const OpDesc *d_ops, const Piece *d_pieces, const uint32_t *d_begin,
                                const Tile *d_tails, int64_t n_sk, int64_t n_tail, int pf,
                                hipStream_t s, int xmode = kXFloat);
+// One launch of a whole chain of dependent phases on `wgs` one-wave
+// workgroups, all of which must be resident at once (wgs <= the CUs times
+// gemv_phased_blocks_per_cu()), `per` of them on each of `nx` XCDs
+// (per * nx == wgs, as the census found).  d_sync: kPhasedSyncBytes of
+// barrier state, zero when first used and kept between launches; its word
+// kPhasedSyncErr is set to 1 if a barrier wait gave up.
+constexpr int kPhasedSyncBytes = 64 * 4 * 34;
+constexpr int kPhasedSyncErr = 64 * 33;
+hipError_t launch_gemv_phased(const PhaseDesc *d_phases, int n_phases, uint32_t *d_sync, uint32_t per,
+                              uint32_t nx, int64_t wgs, int pf, hipStream_t s);
+// The same kernel with no phases: workgroup b writes the XCD it runs on to
+// d_census[b] (wgs words).
+hipError_t launch_gemv_phased_census(uint32_t *d_census, int64_t wgs, hipStream_t s);
+// Workgroups of the one-launch kernel that fit on one CU at once (0 on error
+// or for a pf it is not built with; it has pf = 1 only).
+int gemv_phased_blocks_per_cu(int pf);
 // x (n floats, n % 32 == 0) -> n/32 Q8_0 blocks of 34 bytes at xq.
 hipError_t launch_quantize_x(const float *x, void *xq, int64_t n, hipStream_t s);
 

@@ -120,10 +120,16 @@ def test_chain_validation(q8):
     assert h.value is None
     assert "op 1" in q8.last_error()
     assert q8.lib.q8_0_chain_create(ops, 0, 0, ctypes.byref(h)) == -1
-    assert q8.lib.q8_0_chain_create(ops, 1, 8, ctypes.byref(h)) == -1
+    assert q8.lib.q8_0_chain_create(ops, 1, 16, ctypes.byref(h)) == -1
+    # one launch takes neither the integer path nor one launch per op
+    assert q8.lib.q8_0_chain_create(ops, 1, q8.Q8_CHAIN_ONE_LAUNCH | q8.Q8_CHAIN_XQ, ctypes.byref(h)) == -1
+    assert q8.lib.q8_0_chain_create(ops, 1, q8.Q8_CHAIN_ONE_LAUNCH | q8.Q8_CHAIN_PER_OP, ctypes.byref(h)) == -1
+    assert "ONE_LAUNCH" in q8.last_error()
     assert q8.lib.q8_0_chain_create(None, 1, 0, ctypes.byref(h)) == -1
     assert q8.lib.q8_0_decode_chain(None, 0, None) == -1
     assert q8.lib.q8_0_chain_launches(None) == -1
+    assert q8.lib.q8_0_chain_check(None) == -1
+    assert q8.lib.q8_0_step_check(None) == -1
     assert q8.lib.q8_0_chain_destroy(None) == 0
 
 

@@ -311,6 +311,92 @@ def test_split_k_chain(q8, monkeypatch, per_op, sk):
     chain.close()
 
 
+def test_one_launch_chain(q8, monkeypatch):
+    """Q8_CHAIN_ONE_LAUNCH: four phases in one launch -- the independent
+    split shapes (every super-row size, tail rows, a 7B down projection, more
+    row tiles than CUs), then three ops that each read the one before
+    (1024 -> 3072 -> 16448 -> 131, the last with 4-row super-rows and tail
+    rows).  The same bits as the split chain on the stream-K schedule (the
+    same pieces), on every replay and in every mode; within the bar against
+    the oracle on the inputs each op read; no barrier wait gave up."""
+    import torch
+    log("one-launch chain")
+    rng = np.random.default_rng(91)
+    ws = [synth.q8_weights(n, p, rng) for n, p in SPLIT_SHAPES]
+    xs = [synth.activations(n, rng) for n, p in SPLIT_SHAPES]
+    ys = [torch.full((p,), float("nan"), dtype=torch.float32, device="cuda") for n, p in SPLIT_SHAPES]
+    ops = list(zip([up(x) for x in xs], [w_dev(w, n, p) for w, (n, p) in zip(ws, SPLIT_SHAPES)], ys))
+    dep_shapes = [(1024, 3072), (3072, 16448), (16448, 131)]
+    dep_w = [synth.q8_weights(n, p, rng) for n, p in dep_shapes]
+    dep_y = [torch.full((p,), float("nan"), dtype=torch.float32, device="cuda") for n, p in dep_shapes]
+    src = ys[1]                       # (3072, 1024): its 1024 outputs feed the first dependent op
+    for (n, p), w, y in zip(dep_shapes, dep_w, dep_y):
+        ops.append((src, w_dev(w, n, p), y))
+        src = y
+    outs = ys + dep_y
+    one = q8.Chain(ops, one_launch=True)
+    assert one.launches == 1
+    monkeypatch.setenv("Q8GEMV_STREAMK", "2")
+    ref_chain = q8.Chain(ops, fuse=True, split_k=True)
+    assert ref_chain.launches == 4
+    for y in outs:
+        y.fill_(float("nan"))
+    ref_chain.run(q8.MODE_GRAPH)
+    q8.stream_wait(timeout_ms=60_000)
+    ref = [down(y).copy() for y in outs]
+    for mode in (q8.MODE_GRAPH, q8.MODE_EAGER, q8.MODE_GRAPH, q8.MODE_SYNC_EACH, q8.MODE_GRAPH):
+        for y in outs:
+            y.fill_(float("nan"))
+        one.run(mode)
+        q8.stream_wait(timeout_ms=60_000)
+        for i, y in enumerate(outs):
+            assert np.array_equal(down(y).view(np.uint32), ref[i].view(np.uint32)), (mode, i)
+    one.check()
+    for i, (n, p) in enumerate(SPLIT_SHAPES):
+        _, y64, mag = oracle.gemv(ws[i], xs[i], n, p)
+        parity(ref[i], y64, mag, "one-launch op %d (%d x %d)" % (i, n, p))
+    x_in = ref[1]
+    for k, ((n, p), w) in enumerate(zip(dep_shapes, dep_w)):
+        _, y64, mag = oracle.gemv(w, x_in, n, p)
+        got = ref[len(SPLIT_SHAPES) + k]
+        parity(got, y64, mag, "one-launch dependent op %d" % k)
+        x_in = got
+    one.close()
+    ref_chain.close()
+
+
+def test_one_launch_reread(q8):
+    """A one-launch chain whose last phase reads memory that its first phase
+    read and its second rewrote: u -> v, v -> u, u -> r (the barrier before
+    the third phase takes the per-wave acquire).  Replayed as a recurrence,
+    each replay checked against the oracle on the u it started from."""
+    import torch
+    log("one-launch reread")
+    rng = np.random.default_rng(92)
+    n = 1024
+    wp, wq, wr = (synth.q8_weights(n, 3072, rng), synth.q8_weights(3072, n, rng), synth.q8_weights(n, 512, rng))
+    u = up(synth.activations(n, rng))
+    v = torch.full((3072,), float("nan"), dtype=torch.float32, device="cuda")
+    r = torch.full((512,), float("nan"), dtype=torch.float32, device="cuda")
+    ch = q8.Chain([(u, w_dev(wp, n, 3072), v), (v, w_dev(wq, 3072, n), u), (u, w_dev(wr, n, 512), r)],
+                  one_launch=True)
+    assert ch.launches == 1
+    for mode in (q8.MODE_GRAPH, q8.MODE_EAGER, q8.MODE_GRAPH):
+        u0 = down(u).copy()
+        ch.run(mode)
+        q8.stream_wait(timeout_ms=60_000)
+        vh, uh, rh = down(v).copy(), down(u).copy(), down(r).copy()
+        _, y64, mag = oracle.gemv(wp, u0, n, 3072)
+        parity(vh, y64, mag, "reread P")
+        _, y64, mag = oracle.gemv(wq, vh, 3072, n)
+        parity(uh, y64, mag, "reread Q")
+        _, y64, mag = oracle.gemv(wr, uh, n, 512)
+        parity(rh, y64, mag, "reread R")
+        u.mul_(1.0 / max(1e-30, float(np.sqrt(np.mean(uh.astype(np.float64) ** 2)))))   # keep u O(1)
+    ch.check()
+    ch.close()
+
+
 def test_stream_wait_timeout_and_ok(q8):
     """A bounded wait returns OK on an idle stream."""
     import torch

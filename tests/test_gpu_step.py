@@ -275,19 +275,29 @@ def _run_tokens(q8, st, mode, pos, token, count):
     return toks, logits, xs
 
 
-def test_step_launch_count(q8):
-    log("step launches step_tiny")
+@pytest.mark.parametrize("one", ["0", "1"], ids=["per_run", "one_launch"])
+def test_step_launch_count(q8, monkeypatch, one):
+    log("step launches step_tiny one_launch=%s" % one)
+    monkeypatch.setenv("Q8GEMV_ONE_LAUNCH", one)
     cfg, _, st = _step(q8, "step_tiny", 64)
-    # per layer: q|k|v (fused; from the second layer on it also adds the
-    # residual and norms), attention (with the q/k norms, rotary embedding and
-    # cache append), o, gate|up (fused, adds and norms), down (reads
-    # silu(gate) * up); then embed+norm, the lm_head (adds, norms), argmax
-    assert st.launches == cfg["n_layers"] * 5 + 1 + 2
+    if one == "1":
+        # embed+norm, layer 0's q|k|v; per layer attention (with the q/k
+        # norms, rotary embedding and cache append) and one launch of o,
+        # gate|up (adds and norms), down (reads silu(gate) * up) and the next
+        # layer's q|k|v (adds and norms) or the lm_head; argmax
+        assert st.launches == cfg["n_layers"] * 2 + 3
+    else:
+        # per layer: q|k|v (fused; from the second layer on it also adds the
+        # residual and norms), attention, o, gate|up (fused, adds and norms),
+        # down; then embed+norm, the lm_head (adds, norms), argmax
+        assert st.launches == cfg["n_layers"] * 5 + 1 + 2
     st.close()
 
 
-def test_step_graph_equals_eager(q8):
-    log("step graph vs eager step_tiny")
+@pytest.mark.parametrize("one", ["0", "1"], ids=["per_run", "one_launch"])
+def test_step_graph_equals_eager(q8, monkeypatch, one):
+    log("step graph vs eager step_tiny one_launch=%s" % one)
+    monkeypatch.setenv("Q8GEMV_ONE_LAUNCH", one)
     _, _, st = _step(q8, "step_tiny", 300)
     a = _run_tokens(q8, st, q8.MODE_EAGER, 0, 7, 6)
     kc_a = down(st.buffer("k_cache")).copy()
@@ -300,6 +310,7 @@ def test_step_graph_equals_eager(q8):
         assert np.array_equal(xa, xb)
     assert np.array_equal(kc_a, kc_b)
     assert int(down(st.buffer("pos"))[0]) == 6
+    st.check()
     st.close()
 
 
@@ -322,17 +333,22 @@ def _compare_step(cfg, w, kc, vc, tok_in, pos, logits, x, tok_gpu, label):
     return tok_gpu
 
 
-@pytest.mark.parametrize("name,max_seq,pos0,count,sk", [
-    ("step_tiny", 64, 0, 5, None), ("step_gqa4", 64, 0, 4, None), ("step_gqa4", 1100, 1000, 3, None),
-    ("step_hd192", 300, 126, 4, None), ("step_hd256", 200, 0, 3, None), ("step_hd256", 200, 127, 3, None),
-    # every projection on the stream-K schedule (at these sizes the default
-    # keeps it for launches with more row tiles than CUs)
-    ("step_tiny", 64, 0, 4, "2"), ("step_hd192", 300, 126, 3, "2"),
+@pytest.mark.parametrize("name,max_seq,pos0,count,env", [
+    ("step_tiny", 64, 0, 5, ""), ("step_gqa4", 64, 0, 4, ""), ("step_gqa4", 1100, 1000, 3, ""),
+    ("step_hd192", 300, 126, 4, ""), ("step_hd256", 200, 0, 3, ""), ("step_hd256", 200, 127, 3, ""),
+    # the matvecs between two attentions as one launch (phases with 1-,
+    # 2-, 4- and 8-row super-rows, tail rows, every input mode); and every
+    # projection on the stream-K schedule (at these sizes the default keeps
+    # it for launches with more row tiles than CUs)
+    ("step_tiny", 64, 0, 5, "Q8GEMV_ONE_LAUNCH=1"), ("step_gqa4", 64, 0, 4, "Q8GEMV_ONE_LAUNCH=1"),
+    ("step_hd192", 300, 126, 4, "Q8GEMV_ONE_LAUNCH=1"), ("step_hd256", 200, 127, 3, "Q8GEMV_ONE_LAUNCH=1"),
+    ("step_tiny", 64, 0, 4, "Q8GEMV_STREAMK=2"), ("step_hd192", 300, 126, 3, "Q8GEMV_STREAMK=2"),
 ], ids=str)
-def test_step_matches_oracle(q8, monkeypatch, name, max_seq, pos0, count, sk):
-    if sk is not None:
-        monkeypatch.setenv("Q8GEMV_STREAMK", sk)
-    log("step vs oracle %s max_seq=%d pos0=%d streamk=%s" % (name, max_seq, pos0, sk))
+def test_step_matches_oracle(q8, monkeypatch, name, max_seq, pos0, count, env):
+    for kv in filter(None, env.split(",")):
+        k, v = kv.split("=")
+        monkeypatch.setenv(k, v)
+    log("step vs oracle %s max_seq=%d pos0=%d env=%s" % (name, max_seq, pos0, env))
     cfg, w, st = _step(q8, name, max_seq)
     kc, vc = _oracle_caches(cfg)
     toks, logits, xs = _run_tokens(q8, st, q8.MODE_GRAPH, pos0, 11, count)
@@ -347,6 +363,7 @@ def test_step_matches_oracle(q8, monkeypatch, name, max_seq, pos0, count, sk):
         _check(kc_gpu[l, pos0:pos0 + count], ref,
                STEP_BAR * (np.abs(ref) + float(np.sqrt(np.mean(ref ** 2)))), "k cache layer %d" % l)
         assert not np.any(kc_gpu[l, :pos0]) and not np.any(kc_gpu[l, pos0 + count:])
+    st.check()
     st.close()
 
 
