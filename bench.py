@@ -84,10 +84,13 @@ def cpu_baseline(data, budget_s: float):
 def bench_smallm(args, q8, synth, torch, np):
     """Small-batch products at the 7B shapes.  Each case cycles through enough
     distinct copies of W (>= 1 GiB in all) that no copy is still cached when it
-    comes round again.  The kernel runs on bfloat16 matrix cores with x split
-    into three exact parts and the batch padded to 16 rows: 3 * 16 * n * p
-    multiply-adds.  Reported against max(HBM time, MFMA time)."""
+    comes round again.  m <= 3 runs on the vector units (one conversion and m
+    multiply-adds per weight, one lane-instruction each); larger m on bfloat16
+    matrix cores with x split into three exact parts and the batch padded to
+    16 rows: 3 * 16 * n * p multiply-adds.  Reported against max(HBM time,
+    the path's compute time)."""
     MFMA_BF16_FLOPS = 2.5e15                # MI355X dense bf16
+    VALU_LANE_OPS = 256 * 4 * 16 * 2.4e9    # CUs x SIMDs x lanes x clock (no packed FP32)
     stream = torch.cuda.current_stream()
     cases = []
     for shape in synth.SMALLM_SHAPES:
@@ -114,19 +117,26 @@ def bench_smallm(args, q8, synth, torch, np):
             t = e0.elapsed_time(e1) / 1e3 / k
             nbytes = synth.workload_bytes([shape], m)
             t_hbm = nbytes / 8e12
-            t_mfma = 2 * 3 * 16 * shape.n * shape.p / MFMA_BF16_FLOPS
+            if m <= 3 and shape.n % 256 == 0:
+                kernel, unit = "k_q8_gemm_vrow<%d>" % m, "alu"
+                t_cmp = (1 + m) * shape.n * shape.p / VALU_LANE_OPS
+            else:
+                kernel, unit = "k_split_x + k_q8_gemm_mfma<1>", "mfma"
+                t_cmp = 2 * 3 * 16 * shape.n * shape.p / MFMA_BF16_FLOPS
             cases.append({"shape": shape.name, "n": shape.n, "p": shape.p, "m": m,
+                          "kernel": kernel,
                           "us": round(t * 1e6, 2), "GB_s": round(nbytes / t / 1e9, 1),
-                          "bound": "hbm" if t_hbm >= t_mfma else "mfma",
-                          "frac_of_roof": round(max(t_hbm, t_mfma) / t, 4)})
+                          "bound": "hbm" if t_hbm >= t_cmp else unit,
+                          "frac_of_roof": round(max(t_hbm, t_cmp) / t, 4)})
             say("smallm %s m=%d: %.1f us, %.0f GB/s, %.1f%% of the %s roof" % (
-                shape.name, m, t * 1e6, nbytes / t / 1e9, 100 * max(t_hbm, t_mfma) / t,
+                shape.name, m, t * 1e6, nbytes / t / 1e9, 100 * max(t_hbm, t_cmp) / t,
                 cases[-1]["bound"]))
         del wd
         torch.cuda.empty_cache()
     return {"metric": "q8_0_gemm_smallm at 7B shapes", "unit": "us", "n_gpus": 1,
             "dtype": "f32", "data": "synthetic",
-            "roof_note": "HBM 8 TB/s; bf16 MFMA 2.5 PFLOP/s dense (3 exact x parts, 16 padded rows)",
+            "roof_note": "HBM 8 TB/s; m <= 3: FP32 vector lanes 39.3e12 instr/s (1 + m per weight); "
+                         "m >= 4: bf16 MFMA 2.5 PFLOP/s dense (3 exact x parts, 16 padded rows)",
             "cases": cases}
 
 

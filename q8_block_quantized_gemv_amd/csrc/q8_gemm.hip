@@ -542,6 +542,174 @@ __device__ void vsmall_streamk(const GemmDesc &d, int64_t b, uint8_t *stage) {
     }
 }
 
+// ---------------------------------------------------------------- small m, lanes over rows and blocks
+// Y = X W^T for m = M (2 or 3) rows of X where every row is one super-row
+// (n a multiple of 256).  A group's W tile and its x slices arrive by direct
+// loads as in k_q8_gemm_valu, but lane (r, c) = (lane / 4, lane % 4) takes
+// blocks 2c and 2c + 1 of the tile's rows r, r + 16, r + 32 and r + 48.  So
+// it needs the x values of two blocks per row of X (64 floats), read from
+// LDS once per group into registers, where a lane per row needs every x
+// value of the group through broadcast reads.  The x slices are staged
+// transposed (LDS slot 4k + c holds floats 64c + 4k .. +3 of the slice), so
+// that the four lanes' reads of one instruction hit distinct banks.  Each
+// block's sum is the matvec's (four chains of eight, scaled once); a lane's
+// two blocks of a row go into that row's slot kk % 4, and when the row tile
+// is done the four lanes of a row meet in a butterfly.  No bf16 split of X
+// is needed, so a call is one launch.
+
+// Block `par` (0: 2c, 1: 2c + 1) of a local row, from the lane's 17 dwords
+// of that row in D and its x values xv[i][8 par ..]: d and the sums
+// S_i = sum_j q_j x_i[j].
+template <int PAR, int M>
+__device__ __forceinline__ void vrow_block(const uint32_t (&D)[68], const float4 (&xv)[M][16],
+                                           float &d, float (&s)[M]) {
+    constexpr int sb = 34 * PAR;   // the block's first byte in D
+    d = half_to_float(D[sb >> 2] >> ((sb & 3) * 8));
+    float a[M][4];
+#pragma unroll
+    for (int i = 0; i < M; ++i)
+#pragma unroll
+        for (int t = 0; t < 4; ++t) a[i][t] = 0.f;
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+        float q[4];
+#pragma unroll
+        for (int t = 0; t < 4; ++t) q[t] = quant(D, sb + 2 + 4 * u + t);
+#pragma unroll
+        for (int i = 0; i < M; ++i) {
+            const float4 x = xv[i][8 * PAR + u];
+            a[i][0] = fmaf(q[0], x.x, a[i][0]);
+            a[i][1] = fmaf(q[1], x.y, a[i][1]);
+            a[i][2] = fmaf(q[2], x.z, a[i][2]);
+            a[i][3] = fmaf(q[3], x.w, a[i][3]);
+        }
+    }
+#pragma unroll
+    for (int i = 0; i < M; ++i) s[i] = (a[i][0] + a[i][1]) + (a[i][2] + a[i][3]);
+}
+
+// Local row H of the lane (its 17 dwords in D, the rest of D unused): both
+// blocks, then slot kk % 4 of each row of X.
+template <int H, int M>
+__device__ __forceinline__ void vrow_row(const uint32_t (&D)[68], const float4 (&xv)[M][16], int slot,
+                                         float (&acc)[4][M][kSlots]) {
+    float d0, d1, s0[M], s1[M];
+    vrow_block<0, M>(D, xv, d0, s0);
+    vrow_block<1, M>(D, xv, d1, s1);
+#pragma unroll
+    for (int i = 0; i < M; ++i) {
+        const float sub = fmaf(d1, s1[i], d0 * s0[i]);
+#pragma unroll
+        for (int q = 0; q < kSlots; ++q)
+            if (q == slot) acc[H][i][q] += sub;
+    }
+}
+
+// Groups [g0, g1) of row tile rt, double-buffered like vsmall_run.
+template <int M>
+__device__ void vrow_run(const GemmDesc &d, int rt, int g0, int g1, uint8_t *stage,
+                         float (&acc)[4][M][kSlots]) {
+    constexpr int SB = VStage<M>::kBytes;
+    const int lane = lane_id();
+    const int r = lane >> 2, c = lane & 3;
+    const int64_t sr0 = (int64_t)rt * kWave;
+    const int last = (int)min((int64_t)d.nsr - 1 - sr0, (int64_t)kWave - 1);
+    const uint8_t *wt = d.w + sr0 * d.sr_bytes;
+    uint32_t off[kGroupChunks];
+    chunk_offsets(off, lane, last, d.sr_bytes);
+    // this lane's 16 bytes of a group's x slice (LDS slot `lane`): floats
+    // 64c + 4r .. +3, i.e. float4 r of the 16 that lane (., c) reads
+    const float *xsrc = d.X + 64 * c + 4 * r;
+    auto issue = [&](int kk, uint8_t *st) {
+        const uint32_t l0 = __builtin_amdgcn_readfirstlane(lds_addr(st));
+        const uint8_t *gb = uniform_ptr(wt + (int64_t)kk * kGroupBytes);
+#pragma unroll
+        for (int k = 0; k < kGroupChunks; ++k) dma16_s(gb, off[k], l0 + kWave * 16 * k);
+        const float *xk = xsrc + (int64_t)kk * (kGroupBlocks * kQuants);
+#pragma unroll
+        for (int i = 0; i < M; ++i) dma16_v(xk + (int64_t)i * d.n, l0 + kStageW + i * kStageX);
+    };
+    if (g0 < g1) issue(g0, stage);
+    for (int kk = g0; kk < g1; ++kk) {
+        uint8_t *cur = stage + ((kk - g0) & 1) * SB;
+        float4 xv[M][16];
+        wait_vm_asm<0>();   // this group's W and x have landed
+#pragma unroll
+        for (int i = 0; i < M; ++i) {
+            const float4 *xs = reinterpret_cast<const float4 *>(cur + kStageW + i * kStageX);
+#pragma unroll
+            for (int k = 0; k < 16; ++k) xv[i][k] = xs[4 * k + c];
+        }
+        // the other stage was last read by the previous group, whose reads
+        // have all returned (their values are used)
+        if (kk + 1 < g1) issue(kk + 1, stage + ((kk + 1 - g0) & 1) * SB);
+        const int slot = kk & (kSlots - 1);
+        // one local row's 17 dwords at a time, read from this stage while the
+        // next group streams into the other one
+        auto row = [&](auto hc) {
+            constexpr int H = decltype(hc)::value;
+            uint32_t D[68];
+            const uint32_t *src = reinterpret_cast<const uint32_t *>(
+                cur + kGroupBytes * (16 * H + r) + 2 * kBlockBytes * c);
+#pragma unroll
+            for (int w = 0; w < 17; ++w) D[w] = src[w];
+            vrow_row<H, M>(D, xv, slot, acc);
+        };
+        row(std::integral_constant<int, 0>{});
+        row(std::integral_constant<int, 1>{});
+        row(std::integral_constant<int, 2>{});
+        row(std::integral_constant<int, 3>{});
+    }
+}
+
+template <int M>
+__device__ void vrow_streamk(const GemmDesc &d, int64_t b, uint8_t *stage) {
+    const int lane = lane_id();
+    const int r = lane >> 2, c = lane & 3;
+    const int64_t G = d.gsr, N = (int64_t)d.row_tiles * G, W = d.fast_wgs;
+    int64_t it = sk_first_item(b, N, W);
+    const int64_t end = sk_first_item(b + 1, N, W);
+    while (it < end) {
+        const int rt = (int)(it / G);
+        const int g0 = (int)(it - (int64_t)rt * G);
+        const int g1 = (int)min(G, (int64_t)g0 + (end - it));
+        float acc[4][M][kSlots];
+#pragma unroll
+        for (int h = 0; h < 4; ++h)
+#pragma unroll
+            for (int i = 0; i < M; ++i)
+#pragma unroll
+                for (int q = 0; q < kSlots; ++q) acc[h][i][q] = 0.f;
+        vrow_run<M>(d, rt, g0, g1, stage, acc);
+        // the four lanes of a row meet; lane (r, c) then holds local row 16c + r
+        float out[M];
+#pragma unroll
+        for (int h = 0; h < 4; ++h)
+#pragma unroll
+            for (int i = 0; i < M; ++i) {
+                float v = combine_slots(acc[h][i][0], acc[h][i][1], acc[h][i][2], acc[h][i][3]);
+                v += __shfl_xor(v, 1, kWave);
+                v += __shfl_xor(v, 2, kWave);
+                if (h == 0 || c == h) out[i] = v;
+            }
+        const int row = 16 * c + r;
+        const int64_t sr = (int64_t)rt * kWave + row;
+        if (g0 == 0 && g1 == G) {
+            if (sr < d.nsr)
+#pragma unroll
+                for (int i = 0; i < M; ++i) d.Y[(int64_t)i * d.p + sr] = out[i];
+        } else {
+            const int64_t first = sk_owner((int64_t)rt * G, N, W);
+            const int64_t contributors = sk_owner((int64_t)rt * G + G - 1, N, W) - first + 1;
+            float *mine = partial_slot<1>(d, rt, (int)(b - first));
+#pragma unroll
+            for (int i = 0; i < M; ++i) store_partial(mine + i * kWave + row, out[i]);
+            arrive_reduce<1>(d, rt, (int)contributors, lane);
+        }
+        it += g1 - g0;
+    }
+}
+
 template <int RS>
 __global__ __launch_bounds__(kWave, 1) void k_q8_gemm_mfma(GemmDesc d) {
     __shared__ __attribute__((aligned(16))) uint8_t stage[2 * kStageBytesM];
@@ -568,6 +736,12 @@ __global__ __launch_bounds__(kWave) void k_q8_gemm_valu(GemmDesc d) {
         t.x_stride = d.n; t.y_stride = d.p; t.tail_row0 = d.tail_row0;
         tail_tile<kXFloat>(t, bid - d.fast_wgs, 1);
     }
+}
+
+template <int M>
+__global__ __launch_bounds__(kWave) void k_q8_gemm_vrow(GemmDesc d) {
+    __shared__ __attribute__((aligned(16))) uint8_t stage[2 * VStage<M>::kBytes];
+    vrow_streamk<M>(d, blockIdx.x, stage);
 }
 
 }  // namespace
@@ -611,6 +785,17 @@ hipError_t launch_valu_rs(const GemmDesc &d, const dim3 &gr, hipStream_t s) {
     return hipGetLastError();
 }
 }  // namespace
+
+hipError_t launch_gemm_vrow(const GemmDesc &d, hipStream_t s) {
+    if (d.rs != 1 || d.tail_row0 != d.p) return hipErrorInvalidValue;
+    const dim3 gr((unsigned)d.fast_wgs), bl(kWave);
+    switch (d.m) {
+        case 2: hipLaunchKernelGGL((k_q8_gemm_vrow<2>), gr, bl, 0, s, d); break;
+        case 3: hipLaunchKernelGGL((k_q8_gemm_vrow<3>), gr, bl, 0, s, d); break;
+        default: return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+}
 
 hipError_t launch_gemm_valu(const GemmDesc &d, int64_t grid, hipStream_t s) {
     const dim3 gr((unsigned)grid);

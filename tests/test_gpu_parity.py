@@ -168,11 +168,14 @@ def test_determinism_canaries_and_sign(q8, n, p):
 GEMM_SHAPES = [(256, 130), (896, 70), (896, 71), (3584, 300), (160, 11), (192, 37),
                (18944, 70), (1024, 3072)]
 
-# (m, path): by default m >= 2 runs on the matrix cores where n is a multiple
-# of 128 and on the vector units (four rows of X per pass) elsewhere;
-# Q8GEMV_SMALLM_PATH=valu forces the vector kernel for every width.
+# (m, path): by default m = 2..3 runs on the vector units with lanes over
+# (row, block pair) where n is a multiple of 256, other m >= 2 on the matrix
+# cores where n is a multiple of 128, and the rest on the vector units with a
+# lane per row (four rows of X per pass); Q8GEMV_SMALLM_PATH=valu forces the
+# lane-per-row kernel for every width, =mfma the matrix cores where they apply.
 GEMM_CASES = ([(m, None) for m in (1, 2, 3, 4, 5, 8, 13, 16)] +
-              [(m, "valu") for m in (2, 3, 4, 5, 8, 13, 16)])
+              [(m, "valu") for m in (2, 3, 4, 5, 8, 13, 16)] +
+              [(m, "mfma") for m in (2, 3)])
 
 
 @pytest.mark.parametrize("m,path", GEMM_CASES, ids=lambda v: str(v))
@@ -407,7 +410,8 @@ def test_stream_wait_timeout_and_ok(q8):
 def test_widest_rows(q8, monkeypatch):
     """n at its maximum (2**20 columns, 32768 blocks, 1.1 MB per row): the
     matvec, the small batch on the matrix cores (m = 16) and on the vector
-    units (m = 3), every output against the oracle."""
+    units (m = 2 over rows and block pairs, m = 3 a lane per row), every
+    output against the oracle."""
     import torch
     n, p = 1 << 20, 67
     log("widest rows n=%d p=%d" % (n, p))
@@ -419,7 +423,7 @@ def test_widest_rows(q8, monkeypatch):
     q8.gemv(up(x), wd, y)
     _, y64, mag = oracle.gemv(w, x, n, p)
     parity(down(y), y64, mag, "gemv widest")
-    for m, path in ((16, None), (3, "valu")):
+    for m, path in ((16, None), (2, None), (3, "valu")):
         if path:
             monkeypatch.setenv("Q8GEMV_SMALLM_PATH", path)
         else:
