@@ -207,10 +207,13 @@ def test_gemm_smallm(q8, monkeypatch, m, path, n, p):
         assert np.array_equal(down(Y).view(np.uint32), Yh.view(np.uint32))
 
 
-def test_gemm_identical_rows(q8):
+@pytest.mark.parametrize("m", [2, 3, 16])
+def test_gemm_identical_rows(q8, m):
+    """m equal rows of X give m bitwise-equal rows of Y (m = 2, 3 on the
+    vector units over rows and block pairs, 16 on the matrix cores)."""
     import torch
-    log("gemm identical rows")
-    n, p, m = 3584, 129, 16
+    log("gemm identical rows m=%d" % m)
+    n, p = 3584, 129
     rng = np.random.default_rng(41)
     wd = w_dev(synth.q8_weights(n, p, rng), n, p)
     x = synth.activations(n, rng)
@@ -218,6 +221,36 @@ def test_gemm_identical_rows(q8):
     Yh = down(Y)
     for i in range(1, m):
         assert np.array_equal(Yh[i].view(np.uint32), Yh[0].view(np.uint32))
+    del torch
+
+
+@pytest.mark.parametrize("m,path", [(2, None), (3, None), (5, "valu"), (5, None), (16, None)],
+                         ids=lambda v: str(v))
+def test_gemm_sign_and_scale(q8, monkeypatch, m, path):
+    """Y(4X) = 4 Y(X) bit for bit on every path, and Y(-X) = -Y(X) bit for
+    bit on the vector units, whose roundings are all to nearest even (no
+    value here is near overflow or the subnormal range).  The matrix cores
+    (m = 5, 16 by default) do not round their internal sums symmetrically
+    under negation, so there the sign is checked within the bar.  A row tile
+    split over workgroups (p = 300 at n = 3584) is included."""
+    import torch
+    if path:
+        monkeypatch.setenv("Q8GEMV_SMALLM_PATH", path)
+    log("gemm sign and scale m=%d path=%s" % (m, path or "default"))
+    n, p = 3584, 300
+    rng = np.random.default_rng(77 + m)
+    w = synth.q8_weights(n, p, rng)
+    wd = w_dev(w, n, p)
+    X = synth.activations(n, rng, m).reshape(m, n)
+    a = down(q8.gemm_smallm(up(X), wd)).copy()
+    assert np.array_equal(down(q8.gemm_smallm(up(X * 4), wd)), a * 4)
+    neg = down(q8.gemm_smallm(up(-X), wd))
+    if m <= 3 or path == "valu":
+        assert np.array_equal(neg, -a)
+    else:
+        _, _, MAG = oracle.gemm(w, X, m, n, p)
+        for i in range(m):
+            assert np.all(np.abs(neg[i].astype(np.float64) + a[i]) <= 2 * (1e-5 * MAG[i] + 1e-6))
     del torch
 
 
