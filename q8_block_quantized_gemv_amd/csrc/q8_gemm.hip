@@ -548,22 +548,24 @@ __device__ void vsmall_streamk(const GemmDesc &d, int64_t b, uint8_t *stage) {
 // loads as in k_q8_gemm_valu, but lane (r, c) = (lane / 4, lane % 4) takes
 // blocks 2c and 2c + 1 of the tile's rows r, r + 16, r + 32 and r + 48.  So
 // it needs the x values of two blocks per row of X (64 floats), read from
-// LDS once per group into registers, where a lane per row needs every x
-// value of the group through broadcast reads.  The x slices are staged
-// transposed (LDS slot 4k + c holds floats 64c + 4k .. +3 of the slice), so
-// that the four lanes' reads of one instruction hit distinct banks.  Each
+// LDS into registers once per block and used for its four rows, where a
+// lane per row needs every x value of the group through broadcast reads.
+// The x slices are staged transposed (LDS slot 4k + c holds floats 64c + 4k
+// .. +3 of the slice), so that the four lanes' reads of one instruction hit
+// distinct banks.  Each
 // block's sum is the matvec's (four chains of eight, scaled once); a lane's
 // two blocks of a row go into that row's slot kk % 4, and when the row tile
 // is done the four lanes of a row meet in a butterfly.  No bf16 split of X
 // is needed, so a call is one launch.
 
-// Block `par` (0: 2c, 1: 2c + 1) of a local row, from the lane's 17 dwords
-// of that row in D and its x values xv[i][8 par ..]: d and the sums
-// S_i = sum_j q_j x_i[j].
+// Block PAR (0: 2c, 1: 2c + 1) of a local row: D holds the 9 dwords from
+// the 4-byte boundary at or before the block's first byte (the block starts
+// 2 * PAR bytes in), xv[i] the block's 32 x values of row i of X.  Returns d
+// and the sums S_i = sum_j q_j x_i[j], each as four chains of eight.
 template <int PAR, int M>
-__device__ __forceinline__ void vrow_block(const uint32_t (&D)[68], const float4 (&xv)[M][16],
+__device__ __forceinline__ void vrow_block(const uint32_t (&D)[68], const float4 (&xv)[M][8],
                                            float &d, float (&s)[M]) {
-    constexpr int sb = 34 * PAR;   // the block's first byte in D
+    constexpr int sb = 2 * PAR;   // the block's first byte in D
     d = half_to_float(D[sb >> 2] >> ((sb & 3) * 8));
     float a[M][4];
 #pragma unroll
@@ -577,7 +579,7 @@ __device__ __forceinline__ void vrow_block(const uint32_t (&D)[68], const float4
         for (int t = 0; t < 4; ++t) q[t] = quant(D, sb + 2 + 4 * u + t);
 #pragma unroll
         for (int i = 0; i < M; ++i) {
-            const float4 x = xv[i][8 * PAR + u];
+            const float4 x = xv[i][u];
             a[i][0] = fmaf(q[0], x.x, a[i][0]);
             a[i][1] = fmaf(q[1], x.y, a[i][1]);
             a[i][2] = fmaf(q[2], x.z, a[i][2]);
@@ -586,23 +588,6 @@ __device__ __forceinline__ void vrow_block(const uint32_t (&D)[68], const float4
     }
 #pragma unroll
     for (int i = 0; i < M; ++i) s[i] = (a[i][0] + a[i][1]) + (a[i][2] + a[i][3]);
-}
-
-// Local row H of the lane (its 17 dwords in D, the rest of D unused): both
-// blocks, then slot kk % 4 of each row of X.
-template <int H, int M>
-__device__ __forceinline__ void vrow_row(const uint32_t (&D)[68], const float4 (&xv)[M][16], int slot,
-                                         float (&acc)[4][M][kSlots]) {
-    float d0, d1, s0[M], s1[M];
-    vrow_block<0, M>(D, xv, d0, s0);
-    vrow_block<1, M>(D, xv, d1, s1);
-#pragma unroll
-    for (int i = 0; i < M; ++i) {
-        const float sub = fmaf(d1, s1[i], d0 * s0[i]);
-#pragma unroll
-        for (int q = 0; q < kSlots; ++q)
-            if (q == slot) acc[H][i][q] += sub;
-    }
 }
 
 // Groups [g0, g1) of row tile rt, double-buffered like vsmall_run.
@@ -632,33 +617,53 @@ __device__ void vrow_run(const GemmDesc &d, int rt, int g0, int g1, uint8_t *sta
     if (g0 < g1) issue(g0, stage);
     for (int kk = g0; kk < g1; ++kk) {
         uint8_t *cur = stage + ((kk - g0) & 1) * SB;
-        float4 xv[M][16];
         wait_vm_asm<0>();   // this group's W and x have landed
-#pragma unroll
-        for (int i = 0; i < M; ++i) {
-            const float4 *xs = reinterpret_cast<const float4 *>(cur + kStageW + i * kStageX);
-#pragma unroll
-            for (int k = 0; k < 16; ++k) xv[i][k] = xs[4 * k + c];
-        }
         // the other stage was last read by the previous group, whose reads
         // have all returned (their values are used)
         if (kk + 1 < g1) issue(kk + 1, stage + ((kk + 1 - g0) & 1) * SB);
         const int slot = kk & (kSlots - 1);
-        // one local row's 17 dwords at a time, read from this stage while the
-        // next group streams into the other one
-        auto row = [&](auto hc) {
-            constexpr int H = decltype(hc)::value;
-            uint32_t D[68];
-            const uint32_t *src = reinterpret_cast<const uint32_t *>(
-                cur + kGroupBytes * (16 * H + r) + 2 * kBlockBytes * c);
+        // One block of the pair at a time: its x values for all M rows (8
+        // float4 per row) serve the four local rows; W is read from this
+        // stage one block (9 dwords) at a time while the next group streams
+        // into the other stage.
+        float sub[4][M];
+        auto half = [&](auto pc) {
+            constexpr int PAR = decltype(pc)::value;
+            float4 xv[M][8];
 #pragma unroll
-            for (int w = 0; w < 17; ++w) D[w] = src[w];
-            vrow_row<H, M>(D, xv, slot, acc);
+            for (int i = 0; i < M; ++i) {
+                const float4 *xs = reinterpret_cast<const float4 *>(cur + kStageW + i * kStageX);
+#pragma unroll
+                for (int u = 0; u < 8; ++u) xv[i][u] = xs[4 * (8 * PAR + u) + c];
+            }
+            auto one = [&](auto hc) {
+                constexpr int H = decltype(hc)::value;
+                // the block's 34 bytes start 2 * PAR bytes into these 9 dwords
+                uint32_t D[68];
+                const uint32_t *src = reinterpret_cast<const uint32_t *>(
+                    cur + kGroupBytes * (16 * H + r) + 2 * kBlockBytes * c + 32 * PAR);
+#pragma unroll
+                for (int w = 0; w < 9; ++w) D[w] = src[w];
+                float d, sv[M];
+                vrow_block<PAR, M>(D, xv, d, sv);
+#pragma unroll
+                for (int i = 0; i < M; ++i)
+                    sub[H][i] = PAR == 0 ? d * sv[i] : fmaf(d, sv[i], sub[H][i]);
+            };
+            one(std::integral_constant<int, 0>{});
+            one(std::integral_constant<int, 1>{});
+            one(std::integral_constant<int, 2>{});
+            one(std::integral_constant<int, 3>{});
         };
-        row(std::integral_constant<int, 0>{});
-        row(std::integral_constant<int, 1>{});
-        row(std::integral_constant<int, 2>{});
-        row(std::integral_constant<int, 3>{});
+        half(std::integral_constant<int, 0>{});
+        half(std::integral_constant<int, 1>{});
+#pragma unroll
+        for (int h = 0; h < 4; ++h)
+#pragma unroll
+            for (int i = 0; i < M; ++i)
+#pragma unroll
+                for (int q = 0; q < kSlots; ++q)
+                    if (q == slot) acc[h][i][q] += sub[h][i];
     }
 }
 
