@@ -327,7 +327,13 @@ int smallm_vrow(const float *X, const void *w, float *Y, int64_t m, int64_t n, i
     int rc = workspace_for(dev, s, std::max<size_t>(part_bytes, 256), (size_t)d.row_tiles, &ws, &d.cnt);
     if (rc) return rc;
     d.ws = ws;
-    e = launch_gemm_vrow(d, s);
+    // Two waves per workgroup share its stages, each taking half the rows of
+    // every group: two waves per SIMD where one wave's stages fill a quarter
+    // of the LDS (measured 5-10 % faster than one wave; four waves, held to
+    // two per SIMD by their registers, slower).  Q8GEMV_SMALLM_VROW_NW=1
+    // selects one wave for A/B runs.
+    const int nw = env_int("Q8GEMV_SMALLM_VROW_NW", 2) == 1 ? 1 : 2;
+    e = launch_gemm_vrow(d, nw, s);
     if (e != hipSuccess) return fail_hip(e, "q8_0_gemm_smallm launch");
     return Q8_OK;
 }

@@ -42,7 +42,7 @@ hipError_t launch_gemm_valu(const GemmDesc &d, int64_t grid, hipStream_t s);
 int gemm_valu_stage_bytes(int m);   // LDS bytes per workgroup (0 if m is not 2..4)
 // m = 2..3 on the vector units with lanes over (row, block pair); one row per
 // super-row only (rs == 1, so no tail rows); the same LDS bytes as the above
-hipError_t launch_gemm_vrow(const GemmDesc &d, hipStream_t s);
+hipError_t launch_gemm_vrow(const GemmDesc &d, int nw, hipStream_t s);   // nw: waves per workgroup, 1 or 2
 constexpr int kVrowMaxM = 3;
 constexpr int kValuMaxM = 4;
 // X (m x n) -> the bf16 parts the matrix-core kernel reads: 96 * n bytes per row

@@ -590,12 +590,18 @@ __device__ __forceinline__ void vrow_block(const uint32_t (&D)[68], const float4
     for (int i = 0; i < M; ++i) s[i] = (a[i][0] + a[i][1]) + (a[i][2] + a[i][3]);
 }
 
-// Groups [g0, g1) of row tile rt, double-buffered like vsmall_run.
-template <int M>
+// Groups [g0, g1) of row tile rt, double-buffered like vsmall_run.  NW
+// waves share the stages: wave w takes local rows HW*w .. HW*w + HW - 1
+// (HW = 4 / NW), the group's direct loads are split between the waves, and
+// with NW > 1 a barrier per group makes every wave's loads visible and
+// every wave done with the other stage before it is refilled.
+template <int M, int NW>
 __device__ void vrow_run(const GemmDesc &d, int rt, int g0, int g1, uint8_t *stage,
-                         float (&acc)[4][M][kSlots]) {
+                         float (&acc)[4 / NW][M][kSlots]) {
     constexpr int SB = VStage<M>::kBytes;
+    constexpr int HW = 4 / NW;
     const int lane = lane_id();
+    const int wave = NW > 1 ? wave_id() : 0;
     const int r = lane >> 2, c = lane & 3;
     const int64_t sr0 = (int64_t)rt * kWave;
     const int last = (int)min((int64_t)d.nsr - 1 - sr0, (int64_t)kWave - 1);
@@ -605,28 +611,36 @@ __device__ void vrow_run(const GemmDesc &d, int rt, int g0, int g1, uint8_t *sta
     // this lane's 16 bytes of a group's x slice (LDS slot `lane`): floats
     // 64c + 4r .. +3, i.e. float4 r of the 16 that lane (., c) reads
     const float *xsrc = d.X + 64 * c + 4 * r;
+    // loads [k_lo, k_hi) of the group's 17 W loads, and the x slices, are this wave's
+    const int k_lo = kGroupChunks * wave / NW;
+    const int k_hi = kGroupChunks * (wave + 1) / NW;
+    const bool does_x = NW == 1 || wave == NW - 1;
     auto issue = [&](int kk, uint8_t *st) {
         const uint32_t l0 = __builtin_amdgcn_readfirstlane(lds_addr(st));
         const uint8_t *gb = uniform_ptr(wt + (int64_t)kk * kGroupBytes);
 #pragma unroll
-        for (int k = 0; k < kGroupChunks; ++k) dma16_s(gb, off[k], l0 + kWave * 16 * k);
-        const float *xk = xsrc + (int64_t)kk * (kGroupBlocks * kQuants);
+        for (int k = 0; k < kGroupChunks; ++k)
+            if (k >= k_lo && k < k_hi) dma16_s(gb, off[k], l0 + kWave * 16 * k);
+        if (does_x) {
+            const float *xk = xsrc + (int64_t)kk * (kGroupBlocks * kQuants);
 #pragma unroll
-        for (int i = 0; i < M; ++i) dma16_v(xk + (int64_t)i * d.n, l0 + kStageW + i * kStageX);
+            for (int i = 0; i < M; ++i) dma16_v(xk + (int64_t)i * d.n, l0 + kStageW + i * kStageX);
+        }
     };
     if (g0 < g1) issue(g0, stage);
     for (int kk = g0; kk < g1; ++kk) {
         uint8_t *cur = stage + ((kk - g0) & 1) * SB;
-        wait_vm_asm<0>();   // this group's W and x have landed
+        wait_vm_asm<0>();   // this wave's loads of the group have landed
+        if constexpr (NW > 1) __syncthreads();   // and every other wave's
         // the other stage was last read by the previous group, whose reads
-        // have all returned (their values are used)
+        // have all returned (their values are used) in every wave
         if (kk + 1 < g1) issue(kk + 1, stage + ((kk + 1 - g0) & 1) * SB);
         const int slot = kk & (kSlots - 1);
         // One block of the pair at a time: its x values for all M rows (8
-        // float4 per row) serve the four local rows; W is read from this
+        // float4 per row) serve the wave's local rows; W is read from this
         // stage one block (9 dwords) at a time while the next group streams
         // into the other stage.
-        float sub[4][M];
+        float sub[HW][M];
         auto half = [&](auto pc) {
             constexpr int PAR = decltype(pc)::value;
             float4 xv[M][8];
@@ -636,29 +650,25 @@ __device__ void vrow_run(const GemmDesc &d, int rt, int g0, int g1, uint8_t *sta
 #pragma unroll
                 for (int u = 0; u < 8; ++u) xv[i][u] = xs[4 * (8 * PAR + u) + c];
             }
-            auto one = [&](auto hc) {
-                constexpr int H = decltype(hc)::value;
+#pragma unroll
+            for (int hh = 0; hh < HW; ++hh) {
                 // the block's 34 bytes start 2 * PAR bytes into these 9 dwords
                 uint32_t D[68];
                 const uint32_t *src = reinterpret_cast<const uint32_t *>(
-                    cur + kGroupBytes * (16 * H + r) + 2 * kBlockBytes * c + 32 * PAR);
+                    cur + kGroupBytes * (16 * (HW * wave + hh) + r) + 2 * kBlockBytes * c + 32 * PAR);
 #pragma unroll
                 for (int w = 0; w < 9; ++w) D[w] = src[w];
-                float d, sv[M];
-                vrow_block<PAR, M>(D, xv, d, sv);
+                float dd, sv[M];
+                vrow_block<PAR, M>(D, xv, dd, sv);
 #pragma unroll
                 for (int i = 0; i < M; ++i)
-                    sub[H][i] = PAR == 0 ? d * sv[i] : fmaf(d, sv[i], sub[H][i]);
-            };
-            one(std::integral_constant<int, 0>{});
-            one(std::integral_constant<int, 1>{});
-            one(std::integral_constant<int, 2>{});
-            one(std::integral_constant<int, 3>{});
+                    sub[hh][i] = PAR == 0 ? dd * sv[i] : fmaf(dd, sv[i], sub[hh][i]);
+            }
         };
         half(std::integral_constant<int, 0>{});
         half(std::integral_constant<int, 1>{});
 #pragma unroll
-        for (int h = 0; h < 4; ++h)
+        for (int h = 0; h < HW; ++h)
 #pragma unroll
             for (int i = 0; i < M; ++i)
 #pragma unroll
@@ -667,9 +677,11 @@ __device__ void vrow_run(const GemmDesc &d, int rt, int g0, int g1, uint8_t *sta
     }
 }
 
-template <int M>
+template <int M, int NW>
 __device__ void vrow_streamk(const GemmDesc &d, int64_t b, uint8_t *stage) {
+    constexpr int HW = 4 / NW;
     const int lane = lane_id();
+    const int wave = NW > 1 ? wave_id() : 0;
     const int r = lane >> 2, c = lane & 3;
     const int64_t G = d.gsr, N = (int64_t)d.row_tiles * G, W = d.fast_wgs;
     int64_t it = sk_first_item(b, N, W);
@@ -678,18 +690,19 @@ __device__ void vrow_streamk(const GemmDesc &d, int64_t b, uint8_t *stage) {
         const int rt = (int)(it / G);
         const int g0 = (int)(it - (int64_t)rt * G);
         const int g1 = (int)min(G, (int64_t)g0 + (end - it));
-        float acc[4][M][kSlots];
+        float acc[HW][M][kSlots];
 #pragma unroll
-        for (int h = 0; h < 4; ++h)
+        for (int h = 0; h < HW; ++h)
 #pragma unroll
             for (int i = 0; i < M; ++i)
 #pragma unroll
                 for (int q = 0; q < kSlots; ++q) acc[h][i][q] = 0.f;
-        vrow_run<M>(d, rt, g0, g1, stage, acc);
-        // the four lanes of a row meet; lane (r, c) then holds local row 16c + r
+        vrow_run<M, NW>(d, rt, g0, g1, stage, acc);
+        // the four lanes of a row meet; lane (r, c) then holds local row
+        // 16 (HW wave + c) + r, for c < HW
         float out[M];
 #pragma unroll
-        for (int h = 0; h < 4; ++h)
+        for (int h = 0; h < HW; ++h)
 #pragma unroll
             for (int i = 0; i < M; ++i) {
                 float v = combine_slots(acc[h][i][0], acc[h][i][1], acc[h][i][2], acc[h][i][3]);
@@ -697,19 +710,31 @@ __device__ void vrow_streamk(const GemmDesc &d, int64_t b, uint8_t *stage) {
                 v += __shfl_xor(v, 2, kWave);
                 if (h == 0 || c == h) out[i] = v;
             }
-        const int row = 16 * c + r;
+        const bool holder = c < HW;
+        const int row = 16 * (HW * wave + c) + r;
         const int64_t sr = (int64_t)rt * kWave + row;
         if (g0 == 0 && g1 == G) {
-            if (sr < d.nsr)
+            if (holder && sr < d.nsr)
 #pragma unroll
                 for (int i = 0; i < M; ++i) d.Y[(int64_t)i * d.p + sr] = out[i];
+            // with NW > 1 no wave refills a stage of the next item before
+            // every wave has finished reading this one's
+            if constexpr (NW > 1) __syncthreads();
         } else {
             const int64_t first = sk_owner((int64_t)rt * G, N, W);
             const int64_t contributors = sk_owner((int64_t)rt * G + G - 1, N, W) - first + 1;
             float *mine = partial_slot<1>(d, rt, (int)(b - first));
+            if (holder)
 #pragma unroll
-            for (int i = 0; i < M; ++i) store_partial(mine + i * kWave + row, out[i]);
-            arrive_reduce<1>(d, rt, (int)contributors, lane);
+                for (int i = 0; i < M; ++i) store_partial(mine + i * kWave + row, out[i]);
+            if constexpr (NW > 1) {
+                // every wave's share is stored before wave 0 counts the arrival
+                __builtin_amdgcn_s_waitcnt(0);
+                __syncthreads();
+                if (wave == 0) arrive_reduce<1>(d, rt, (int)contributors, lane);
+            } else {
+                arrive_reduce<1>(d, rt, (int)contributors, lane);
+            }
         }
         it += g1 - g0;
     }
@@ -743,10 +768,11 @@ __global__ __launch_bounds__(kWave) void k_q8_gemm_valu(GemmDesc d) {
     }
 }
 
-template <int M>
-__global__ __launch_bounds__(kWave) void k_q8_gemm_vrow(GemmDesc d) {
+
+template <int M, int NW>
+__global__ __launch_bounds__(NW * kWave) void k_q8_gemm_vrow(GemmDesc d) {
     __shared__ __attribute__((aligned(16))) uint8_t stage[2 * VStage<M>::kBytes];
-    vrow_streamk<M>(d, blockIdx.x, stage);
+    vrow_streamk<M, NW>(d, blockIdx.x, stage);
 }
 
 }  // namespace
@@ -791,14 +817,14 @@ hipError_t launch_valu_rs(const GemmDesc &d, const dim3 &gr, hipStream_t s) {
 }
 }  // namespace
 
-hipError_t launch_gemm_vrow(const GemmDesc &d, hipStream_t s) {
+hipError_t launch_gemm_vrow(const GemmDesc &d, int nw, hipStream_t s) {
     if (d.rs != 1 || d.tail_row0 != d.p) return hipErrorInvalidValue;
-    const dim3 gr((unsigned)d.fast_wgs), bl(kWave);
-    switch (d.m) {
-        case 2: hipLaunchKernelGGL((k_q8_gemm_vrow<2>), gr, bl, 0, s, d); break;
-        case 3: hipLaunchKernelGGL((k_q8_gemm_vrow<3>), gr, bl, 0, s, d); break;
-        default: return hipErrorInvalidValue;
-    }
+    const dim3 gr((unsigned)d.fast_wgs), bl(nw * kWave);
+    if (nw == 1 && d.m == 2) hipLaunchKernelGGL((k_q8_gemm_vrow<2, 1>), gr, bl, 0, s, d);
+    else if (nw == 1 && d.m == 3) hipLaunchKernelGGL((k_q8_gemm_vrow<3, 1>), gr, bl, 0, s, d);
+    else if (nw == 2 && d.m == 2) hipLaunchKernelGGL((k_q8_gemm_vrow<2, 2>), gr, bl, 0, s, d);
+    else if (nw == 2 && d.m == 3) hipLaunchKernelGGL((k_q8_gemm_vrow<3, 2>), gr, bl, 0, s, d);
+    else return hipErrorInvalidValue;
     return hipGetLastError();
 }
 

@@ -173,9 +173,11 @@ GEMM_SHAPES = [(256, 130), (896, 70), (896, 71), (3584, 300), (160, 11), (192, 3
 # cores where n is a multiple of 128, and the rest on the vector units with a
 # lane per row (four rows of X per pass); Q8GEMV_SMALLM_PATH=valu forces the
 # lane-per-row kernel for every width, =mfma the matrix cores where they apply.
+# "nw1" keeps the default path but runs the row-and-block-pair kernel with
+# one wave per workgroup instead of two sharing the stages.
 GEMM_CASES = ([(m, None) for m in (1, 2, 3, 4, 5, 8, 13, 16)] +
               [(m, "valu") for m in (2, 3, 4, 5, 8, 13, 16)] +
-              [(m, "mfma") for m in (2, 3)])
+              [(m, "mfma") for m in (2, 3)] + [(m, "nw1") for m in (2, 3)])
 
 
 @pytest.mark.parametrize("m,path", GEMM_CASES, ids=lambda v: str(v))
@@ -187,7 +189,9 @@ def test_gemm_smallm(q8, monkeypatch, m, path, n, p):
     (896, 71) has a tail row; (192, 37) and (160, 11) have 4- and 8-row
     super-rows, which only the vector kernel takes."""
     import torch
-    if path:
+    if path == "nw1":
+        monkeypatch.setenv("Q8GEMV_SMALLM_VROW_NW", "1")
+    elif path:
         monkeypatch.setenv("Q8GEMV_SMALLM_PATH", path)
     log("gemm m=%d n=%d p=%d path=%s" % (m, n, p, path or "default"))
     rng = np.random.default_rng(300 + 11 * m + n + p)
