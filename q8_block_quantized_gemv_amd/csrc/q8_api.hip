@@ -49,19 +49,19 @@ int check_device(int *dev_out) {
     int dev = 0;
     if ((e = hipGetDevice(&dev)) != hipSuccess) return fail_hip(e, "hipGetDevice");
     static std::mutex mu;
-    static std::vector<int> verdict;  // -1 unknown, 0 unsupported, 1 ok
+    static std::vector<int> arch_ok;  // -1 unknown, 0 unsupported, 1 ok
     std::lock_guard<std::mutex> lk(mu);
-    if ((int)verdict.size() <= dev) verdict.resize(dev + 1, -1);
-    if (verdict[dev] < 0) {
+    if ((int)arch_ok.size() <= dev) arch_ok.resize(dev + 1, -1);
+    if (arch_ok[dev] < 0) {
         hipDeviceProp_t prop;
         if ((e = hipGetDeviceProperties(&prop, dev)) != hipSuccess)
             return fail_hip(e, "hipGetDeviceProperties");
-        verdict[dev] = std::strncmp(prop.gcnArchName, "gfx950", 6) == 0 ? 1 : 0;
-        if (!verdict[dev])
+        arch_ok[dev] = std::strncmp(prop.gcnArchName, "gfx950", 6) == 0 ? 1 : 0;
+        if (!arch_ok[dev])
             return fail(Q8_ERR_UNSUPPORTED,
                         std::string("device is ") + prop.gcnArchName + ", this library is built for gfx950");
     }
-    if (!verdict[dev]) return fail(Q8_ERR_UNSUPPORTED, "device is not gfx950");
+    if (!arch_ok[dev]) return fail(Q8_ERR_UNSUPPORTED, "device is not gfx950");
     if (dev_out) *dev_out = dev;
     return Q8_OK;
 }
