@@ -347,13 +347,13 @@ int smallm_mfma(const float *X, const void *w, float *Y, int64_t m, int64_t n, i
     if (e != hipSuccess) return fail_hip(e, "hipGetDevice");
     // four double-buffered one-wave workgroups fill a CU's LDS
     const size_t part_bytes = plan_streamk(d, dev, 4, 4);
-    // workspace: the split X (m * n * 6 bytes, 256-B aligned), then the
+    // workspace: the split X (3 KiB per block of 32 columns, 256-B aligned), then the
     // partial slots
-    const size_t xs_bytes = ((size_t)m * n * kXPartsBytesPerCol + 255) / 256 * 256;
+    const size_t xs_bytes = ((size_t)(n / kQuants) * kXPartsBytesPerBlock + 255) / 256 * 256;
     float *ws = nullptr;
     int rc = workspace_for(dev, s, xs_bytes + part_bytes, (size_t)d.row_tiles, &ws, &d.cnt);
     if (rc) return rc;
-    d.xs = (const XParts *)ws;
+    d.xs = (const bf16x8 *)ws;
     d.ws = (float *)((char *)ws + xs_bytes);
     e = launch_split_x(X, ws, (int)m, (int)n, s);
     if (e != hipSuccess) return fail_hip(e, "q8_0_gemm_smallm split launch");

@@ -21,7 +21,7 @@ struct XParts {
 // arrival counters `cnt` (zero between launches).
 struct GemmDesc {
     const float *X;
-    const XParts *xs;    // X split into exact bf16 parts (k_split_x)
+    const bf16x8 *xs;    // X split into exact bf16 parts, 3 KiB per block (k_split_x)
     const uint8_t *w;
     float *Y;
     float *ws;
@@ -45,8 +45,9 @@ int gemm_valu_stage_bytes(int m);   // LDS bytes per workgroup (0 if m is not 2.
 hipError_t launch_gemm_vrow(const GemmDesc &d, int nw, hipStream_t s);   // nw: waves per workgroup, 1 or 2
 constexpr int kVrowMaxM = 3;
 constexpr int kValuMaxM = 4;
-// X (m x n) -> the bf16 parts the matrix-core kernel reads: 96 * n bytes per row
+// X (m x n) -> the bf16 parts the matrix-core kernel reads: kXPartsBytesPerBlock
+// bytes per block of 32 columns, for up to 16 rows
 hipError_t launch_split_x(const float *X, void *xs, int m, int n, hipStream_t s);
-constexpr int64_t kXPartsBytesPerCol = 6;   // 3 bf16 per element
+constexpr int64_t kXPartsBytesPerBlock = 3 * 16 * 4 * 16;   // parts x rows x column groups x bf16x8
 
 }  // namespace q8

@@ -47,19 +47,29 @@ __device__ __forceinline__ void split3(const float (&x)[8], bf16x8 &h, bf16x8 &m
 }
 
 // The A operands of X, split once per call by k_split_x into
-// xs[i][b][g] = {h, m, l}: three bf16x8 (48 bytes) holding columns
-// 32b + 8g .. 32b + 8g + 7 of row i.  Rows i >= m are never read.
+// xs[b][part][i][g]: for block b and part (h, m, l), the bf16x8 of columns
+// 32b + 8g .. 32b + 8g + 7 of row i, 16 rows x 4 column groups in a
+// contiguous 1 KiB, so that one load instruction of a wave (lane = i + 16 g
+// reads entry 4i + g) covers whole cache lines.  Rows i >= m are never
+// written or read.
+__device__ __forceinline__ int64_t xpart_index(int b, int part, int i, int g) {
+    return ((int64_t)b * 3 + part) * 64 + i * 4 + g;
+}
+
 __global__ __launch_bounds__(256) void k_split_x(const float *__restrict__ X,
-                                                 XParts *__restrict__ xs, int m, int n) {
+                                                 bf16x8 *__restrict__ xs, int m, int n) {
     const int nb = n / kQuants;
     const int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x;   // (i, b, g)
     if (t >= (int64_t)m * nb * 4) return;
+    const int g = (int)(t & 3), b = (int)((t >> 2) % nb), i = (int)((t >> 2) / nb);
     const float4 *src = reinterpret_cast<const float4 *>(X) + 2 * t;
     const float4 v0 = src[0], v1 = src[1];
     const float x[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
     XParts o;
     split3(x, o.h, o.m, o.l);
-    xs[t] = o;
+    xs[xpart_index(b, 0, i, g)] = o.h;
+    xs[xpart_index(b, 1, i, g)] = o.m;
+    xs[xpart_index(b, 2, i, g)] = o.l;
 }
 
 // The A operand of block K of group kk for lane (i, g).  Rows i >= m load
@@ -70,7 +80,11 @@ __device__ __forceinline__ XParts load_parts(const GemmDesc &d, int kk, int K, i
     int b = kk * kGroupBlocks + K;
     if (RS > 1) b %= d.nb;
     const int ii = i < d.m ? i : d.m - 1;
-    return d.xs[((int64_t)ii * d.nb + b) * 4 + g];
+    XParts r;
+    r.h = d.xs[xpart_index(b, 0, ii, g)];
+    r.m = d.xs[xpart_index(b, 1, ii, g)];
+    r.l = d.xs[xpart_index(b, 2, ii, g)];
+    return r;
 }
 
 // All eight blocks' A operands of group kk (96 VGPRs), loaded together so
@@ -780,7 +794,7 @@ __global__ __launch_bounds__(NW * kWave) void k_q8_gemm_vrow(GemmDesc d) {
 hipError_t launch_split_x(const float *X, void *xs, int m, int n, hipStream_t s) {
     const int64_t items = (int64_t)m * (n / kQuants) * 4;
     hipLaunchKernelGGL(k_split_x, dim3((unsigned)((items + 255) / 256)), dim3(256), 0, s, X,
-                       (XParts *)xs, m, n);
+                       (bf16x8 *)xs, m, n);
     return hipGetLastError();
 }
 
