@@ -326,27 +326,43 @@ __device__ void arrive_reduce(const GemmDesc &d, int rt, int contributors, int l
     asm volatile("" ::: "memory");
     const float *slots = partial_slot<RS>(d, rt, 0);
     const int64_t sr0 = (int64_t)rt * kWave;
-    // Eight slots' loads are in flight at once; the sum still runs in rank
-    // order.  Past the last rank the index is clamped and the value dropped.
-    constexpr int kBatch = 8;
-    for (int idx = lane; idx < d.m * (kWave * RS); idx += kWave) {
-        const int ii = idx / (kWave * RS);
-        const int rr = idx - ii * (kWave * RS);
-        if (sr0 + rr / RS >= d.nsr) continue;
-        float v = 0.f;
-        for (int q0 = 0; q0 < contributors; q0 += kBatch) {
-            float t[kBatch];
+    // A lane sums kIdx outputs at a time, kBatch slots of each in flight
+    // (32 loads per round trip); every sum still runs in rank order.  Past
+    // the last rank the slot index is clamped and the value dropped; outputs
+    // past the last row of X are not loaded, rows past the matrix's last
+    // row are loaded (in the slot) but not stored.
+    constexpr int kBatch = 8, kIdx = 4;
+    const int total = d.m * (kWave * RS);
+    for (int idx0 = lane; idx0 < total; idx0 += kIdx * kWave) {
+        float v[kIdx];
 #pragma unroll
-            for (int u = 0; u < kBatch; ++u) {
-                const int q = min(q0 + u, contributors - 1);
-                t[u] = __hip_atomic_load(slots + (int64_t)q * kSlot + idx, __ATOMIC_RELAXED,
-                                         __HIP_MEMORY_SCOPE_AGENT);
+        for (int k = 0; k < kIdx; ++k) v[k] = 0.f;
+        for (int q0 = 0; q0 < contributors; q0 += kBatch) {
+            float t[kIdx][kBatch];
+#pragma unroll
+            for (int k = 0; k < kIdx; ++k) {
+                const int idx = idx0 + k * kWave;
+#pragma unroll
+                for (int u = 0; u < kBatch; ++u) {
+                    const int q = min(q0 + u, contributors - 1);
+                    t[k][u] = idx < total ? __hip_atomic_load(slots + (int64_t)q * kSlot + idx,
+                                                              __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
+                                          : 0.f;
+                }
             }
 #pragma unroll
-            for (int u = 0; u < kBatch; ++u)
-                if (q0 + u < contributors) v = (q0 + u == 0) ? t[u] : v + t[u];
+            for (int k = 0; k < kIdx; ++k)
+#pragma unroll
+                for (int u = 0; u < kBatch; ++u)
+                    if (q0 + u < contributors) v[k] = (q0 + u == 0) ? t[k][u] : v[k] + t[k][u];
         }
-        d.Y[(int64_t)ii * d.p + sr0 * RS + rr] = v;
+#pragma unroll
+        for (int k = 0; k < kIdx; ++k) {
+            const int idx = idx0 + k * kWave;
+            const int ii = idx / (kWave * RS);
+            const int rr = idx - ii * (kWave * RS);
+            if (idx < total && sr0 + rr / RS < d.nsr) d.Y[(int64_t)ii * d.p + sr0 * RS + rr] = v[k];
+        }
     }
     if (lane == 0)   // ready for the next launch
         __hip_atomic_store(d.cnt + rt, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
