@@ -47,15 +47,17 @@ def kernel_digest() -> str:
     return h.hexdigest()[:16]
 
 
-def measured_traffic(workload: str):
+def measured_traffic(workload: str, kernel: str):
     """HBM bytes per launch from the committed rocprofv3 counter runs, if they
-    were taken on the current kernel source; else None."""
+    were taken on this workload's kernel (same template arguments) and the
+    current kernel source; else None."""
     try:
         with open(TRAFFIC_FILE) as f:
             rec = json.load(f)
     except (OSError, ValueError):
         return None
-    if rec.get("workload") != workload or rec.get("kernel_digest") != kernel_digest():
+    if (rec.get("workload") != workload or rec.get("kernel") != kernel
+            or rec.get("kernel_digest") != kernel_digest()):
         return None
     return rec.get("hbm_bytes_per_launch")
 
@@ -342,15 +344,16 @@ def main():
     launches = chain.launches
     kernel_s = time_steps(lambda: chain.run(q8.MODE_EAGER, stream), args.steps) / args.steps / launches
     achieved = nbytes / launches / kernel_s / 1e9
+    # a chain of one op is that op's standalone launch (four-wave workgroups);
+    # more independent ops share one fused launch.  Template arguments: waves
+    # per workgroup, groups in flight, input mode (0 float activations, 1
+    # activations quantized to Q8_0)
+    kernel = (("k_q8_gemv_fused<1,1,%d>" if len(ops_shape) > 1 else "k_q8_gemv<4,1,%d>")
+              % (1 if args.xq else 0))
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                 "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-                "traffic": measured_traffic(args.workload),
-                # a chain of one op is that op's standalone launch (four-wave
-                # workgroups); more independent ops share one fused launch
-                # template arguments: waves per workgroup, groups in flight, input mode
-                # (0 float activations, 1 activations quantized to Q8_0)
-                "kernel": ("k_q8_gemv_fused<1,1,%d>" if len(ops_shape) > 1 else "k_q8_gemv<4,1,%d>")
-                          % (1 if args.xq else 0),
+                "traffic": measured_traffic(args.workload, kernel),
+                "kernel": kernel,
                 "launches_per_step": launches,
                 "algorithmic_bytes_per_launch": nbytes // launches,
                 "kernel_us": round(kernel_s * 1e6, 2),
