@@ -582,11 +582,11 @@ __device__ void vsmall_streamk(const GemmDesc &d, int64_t b, uint8_t *stage) {
 // lane per row needs every x value of the group through broadcast reads.
 // The x slices are staged transposed (LDS slot 4k + c holds floats 64c + 4k
 // .. +3 of the slice), so that the four lanes' reads of one instruction hit
-// distinct banks.  Each
-// block's sum is the matvec's (four chains of eight, scaled once); a lane's
-// two blocks of a row go into that row's slot kk % 4, and when the row tile
-// is done the four lanes of a row meet in a butterfly.  No bf16 split of X
-// is needed, so a call is one launch.
+// distinct banks.  Each block's sum is the matvec's (four chains of eight,
+// scaled once); a lane's two blocks of a row go into that row's slot kk % 4,
+// and when the row tile is done the four lanes of a row meet in a butterfly.
+// No bf16 split of X is needed, so a call is one launch.  Two waves per
+// workgroup share the stages, each taking half of every group's rows.
 
 // Block PAR (0: 2c, 1: 2c + 1) of a local row: D holds the 9 dwords from
 // the 4-byte boundary at or before the block's first byte (the block starts
