@@ -391,6 +391,10 @@ def main():
                 "timing": "%d back-to-back launches between HIP events on the launch stream" % args.steps}
 
     modes = {"fused_graph_us": round(per_step * 1e6, 2), "fused_graph_cold_first_us": round(cold * 1e6, 2)}
+    # spread: R more regions of graph replays after the timed one
+    reps = sorted(time_steps(run_graph, 20) / 20 * 1e6 for _ in range(5))
+    modes["fused_graph_repeats_us"] = {"regions": 5, "steps_each": 20, "min": round(reps[0], 2),
+                                       "median": round(reps[2], 2), "max": round(reps[-1], 2)}
     if not args.no_modes:
         k = max(3, args.steps // 10)
         modes["fused_eager_us"] = round(time_steps(lambda: chain.run(q8.MODE_EAGER, stream), k) / k * 1e6, 2)
