@@ -211,6 +211,41 @@ def test_gemm_smallm(q8, monkeypatch, m, path, n, p):
         assert np.array_equal(down(Y).view(np.uint32), Yh.view(np.uint32))
 
 
+def _vrow_sweep_cases():
+    rng = np.random.default_rng(2026)
+    cases = []
+    for k in range(24):
+        n = 256 * int(rng.integers(1, 33))               # one row per super-row
+        p = int(rng.integers(1, 5000))
+        cases.append((n, p, 2 + k % 2, "1" if k % 3 == 0 else "2"))
+    return cases
+
+
+@pytest.mark.parametrize("n,p,m,nw", _vrow_sweep_cases(), ids=lambda v: str(v))
+def test_gemm_vrow_sweep(q8, monkeypatch, n, p, m, nw):
+    """Seeded random shapes on the vector units' row-and-block-pair kernel
+    (m = 2, 3; one or two waves per workgroup): every output against the
+    oracle, and bitwise repeatable, so that row tiles split over workgroups
+    at many different points are checked."""
+    import torch
+    monkeypatch.setenv("Q8GEMV_SMALLM_VROW_NW", nw)
+    log("gemm vrow sweep n=%d p=%d m=%d nw=%s" % (n, p, m, nw))
+    rng = np.random.default_rng(n * 7919 + p * 31 + m)
+    w = synth.q8_weights(n, p, rng)
+    X = synth.activations(n, rng, m).reshape(m, n)
+    wd = w_dev(w, n, p)
+    Xd = up(X)
+    Y = torch.full((m, p), float("nan"), dtype=torch.float32, device="cuda")
+    q8.gemm_smallm(Xd, wd, Y)
+    Yh = down(Y).copy()
+    _, Y64, MAG = oracle.gemm(w, X, m, n, p)
+    for i in range(m):
+        parity(Yh[i], Y64[i], MAG[i], "vrow sweep row %d" % i)
+    Y.fill_(float("nan"))
+    q8.gemm_smallm(Xd, wd, Y)
+    assert np.array_equal(down(Y).view(np.uint32), Yh.view(np.uint32))
+
+
 @pytest.mark.parametrize("m", [2, 3, 16])
 def test_gemm_identical_rows(q8, m):
     """m equal rows of X give m bitwise-equal rows of Y (m = 2, 3 on the
