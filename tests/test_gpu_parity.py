@@ -246,6 +246,39 @@ def test_gemm_vrow_sweep(q8, monkeypatch, n, p, m, nw):
     assert np.array_equal(down(Y).view(np.uint32), Yh.view(np.uint32))
 
 
+def _mfma_sweep_cases():
+    rng = np.random.default_rng(4242)
+    cases = []
+    for k in range(20):
+        n = 128 * int(rng.integers(1, 65))               # super-rows of one or two rows
+        p = int(rng.integers(1, 4000))
+        cases.append((n, p, int(rng.integers(4, 17))))
+    return cases
+
+
+@pytest.mark.parametrize("n,p,m", _mfma_sweep_cases(), ids=lambda v: str(v))
+def test_gemm_mfma_sweep(q8, n, p, m):
+    """Seeded random shapes on the matrix-core kernel (m = 4..16, the split X
+    in its block-major layout, the last arriver's batched reduction): every
+    output against the oracle, and bitwise repeatable."""
+    import torch
+    log("gemm mfma sweep n=%d p=%d m=%d" % (n, p, m))
+    rng = np.random.default_rng(n * 7919 + p * 31 + m)
+    w = synth.q8_weights(n, p, rng)
+    X = synth.activations(n, rng, m).reshape(m, n)
+    wd = w_dev(w, n, p)
+    Xd = up(X)
+    Y = torch.full((m, p), float("nan"), dtype=torch.float32, device="cuda")
+    q8.gemm_smallm(Xd, wd, Y)
+    Yh = down(Y).copy()
+    _, Y64, MAG = oracle.gemm(w, X, m, n, p)
+    for i in range(m):
+        parity(Yh[i], Y64[i], MAG[i], "mfma sweep row %d" % i)
+    Y.fill_(float("nan"))
+    q8.gemm_smallm(Xd, wd, Y)
+    assert np.array_equal(down(Y).view(np.uint32), Yh.view(np.uint32))
+
+
 @pytest.mark.parametrize("m", [2, 3, 16])
 def test_gemm_identical_rows(q8, m):
     """m equal rows of X give m bitwise-equal rows of Y (m = 2, 3 on the
