@@ -489,7 +489,11 @@ def main():
                    "cache": ("hot: one %.1f MB copy of W, resident in the 256 MB Infinity Cache "
                              "(cold figures: modes_us_per_token.cold_rotation)" % (nbytes / 1e6)
                              if nbytes < (256 << 20) else
-                             "cold: %.0f MB of weights per step, past the 256 MB Infinity Cache"
+                             "partly warm: %.0f MB of weights per step against the 256 MB Infinity "
+                             "Cache, part of which is still cached when the step repeats (two "
+                             "weight sets in turn: modes_us_per_token.two_weight_sets)" % (nbytes / 1e6)
+                             if nbytes < (4 << 30) else
+                             "cold: %.0f MB of weights per step, far past the 256 MB Infinity Cache"
                              % (nbytes / 1e6))},
         "roofline": roofline,
         "modes_us_per_token": modes,
