@@ -2,6 +2,7 @@
 // decode chains (hipGraph record/replay) and the bounded stream wait.
 #include <algorithm>
 #include <chrono>
+#include <cmath>
 #include <cstdint>
 #include <cstdio>
 #include <cstdlib>
@@ -781,10 +782,13 @@ int q8::chain_create_ex(const q8_0_op *ops, int64_t n_ops, uint32_t flags, const
     // CUs (an lm_head, a 7B gate|up) are fastest on unsplit one-wave tiles.
     const Variant v_single = pick_variant(false), v_fused = pick_variant(true);
     const int64_t cus = cu_count(dev);
-    // Stream-K for split launches with more row tiles than CUs:
+    // Stream-K for split launches with more row tiles than CUs whose one-wave
+    // tiles would leave a long tail (below):
     // Q8GEMV_STREAMK=0 turns it off, 2 uses it for every split launch (A/B
     // runs); Q8GEMV_SK_PF sets its groups in flight (1 or 2).
     const int sk_mode = env_int("Q8GEMV_STREAMK", 1);
+    // Q8GEMV_SK_TAIL overrides the tail threshold below (0: every row-rich launch)
+    const double kSkTailGroups = env_int("Q8GEMV_SK_TAIL", 4);
     const int sk_pf = env_int("Q8GEMV_SK_PF", 1) == 2 ? 2 : 1;
     // a one-launch chain: every phase stream-K on the same workgroups, as
     // many as the CUs hold at once (four one-wave workgroups fill a CU's LDS)
@@ -824,10 +828,11 @@ int q8::chain_create_ex(const q8_0_op *ops, int64_t n_ops, uint32_t flags, const
             sk = true;
             v = Variant{1, 1};
         } else if (split || one) {
-            int64_t row_tiles = 0;
+            int64_t row_tiles = 0, tile_groups = 0;
             for (int64_t i = sg.first; i < sg.second; ++i) {
                 const OpDesc d = plan_op(ops[i].x, ops[i].w, ops[i].y, 1, ops[i].n, ops[i].p, false, 1);
                 row_tiles += d.fast_tiles;
+                tile_groups = std::max<int64_t>(tile_groups, d.gsr);
             }
             if (row_tiles > cus) {
                 v = Variant{1, 1};
@@ -835,7 +840,18 @@ int q8::chain_create_ex(const q8_0_op *ops, int64_t n_ops, uint32_t flags, const
                 v = Variant{kWaves, 1};
                 target = std::max<int64_t>(1, cus / std::max<int64_t>(1, row_tiles));
             }
-            sk = sk_mode == 2 || (sk_mode == 1 && row_tiles > cus);
+            // Row-rich launches: one-wave tiles, four per CU, run in waves of
+            // 4 * cus tiles; the last wave's idle slots cost (ceil(w) - w)
+            // tile times, w = row_tiles / (4 * cus).  Stream-K spreads the
+            // (tile, group) items evenly but pays partial sums where tiles
+            // are shared.  It is taken where the one-wave tail would idle
+            // the slots for at least kSkTailGroups group times (measured:
+            // the 7B gate|up, 592 tiles of 14 groups, 5.9 group times, and
+            // lm_head, 2376 of 14, 9.5, are faster on stream-K; the 0.6B
+            // lm_head, 2374 tiles of 4 groups, 2.7, is 5 us faster on tiles).
+            const double waves = (double)row_tiles / (double)(4 * cus);
+            const double tail_groups = (std::ceil(waves) - waves) * (double)tile_groups;
+            sk = sk_mode == 2 || (sk_mode == 1 && row_tiles > cus && tail_groups >= kSkTailGroups);
             // A/B overrides: Q8GEMV_SPLIT_SLICES (slices per row tile), Q8GEMV_VARIANT
             if (const int forced = env_int("Q8GEMV_SPLIT_SLICES", 0); forced > 0) target = forced;
             if (std::getenv("Q8GEMV_VARIANT")) v = v_single;
