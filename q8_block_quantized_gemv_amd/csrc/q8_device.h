@@ -165,6 +165,46 @@ __device__ __forceinline__ float norm_add_inv(const OpDesc &op, int lane, bool w
     return 1.0f / sqrtf(ss / (float)n + op.norm_eps);
 }
 
+// kXNormAdd with NW waves sharing the op: wave `part` of `nparts` sums the
+// squares of s = x + x_res over its contiguous share of the float4s (and
+// writes that share of s with `write`); returns the wave's partial sum.
+__device__ __forceinline__ float norm_add_part(const OpDesc &op, int lane, int part, int nparts,
+                                               bool write) {
+    constexpr int B = 8;   // float4 pairs in flight per lane
+    const int n = op.nb * kQuants, nv = n / 4;
+    const int lo = (int)((int64_t)nv * part / nparts), hi = (int)((int64_t)nv * (part + 1) / nparts);
+    const float4 *a4 = reinterpret_cast<const float4 *>(op.x);
+    const float4 *r4 = reinterpret_cast<const float4 *>(op.x_res);
+    float4 *o4 = reinterpret_cast<float4 *>(op.x_out);
+    float ss = 0.f;
+    for (int i0 = lo; i0 < hi; i0 += kWave * B) {
+        float4 a[B], r[B];
+#pragma unroll
+        for (int e = 0; e < B; ++e) {
+            const int i = i0 + lane + kWave * e;
+            a[e] = make_float4(0.f, 0.f, 0.f, 0.f);
+            r[e] = a[e];
+            if (i < hi) {
+                a[e] = a4[i];
+                r[e] = r4[i];
+            }
+        }
+#pragma unroll
+        for (int e = 0; e < B; ++e) {
+            const int i = i0 + lane + kWave * e;
+            const float4 v = make_float4(a[e].x + r[e].x, a[e].y + r[e].y, a[e].z + r[e].z, a[e].w + r[e].w);
+            ss = fmaf(v.x, v.x, ss);
+            ss = fmaf(v.y, v.y, ss);
+            ss = fmaf(v.z, v.z, ss);
+            ss = fmaf(v.w, v.w, ss);
+            if (write && i < hi) o4[i] = v;
+        }
+    }
+#pragma unroll
+    for (int o = kWave / 2; o > 0; o >>= 1) ss += __shfl_xor(ss, o, kWave);
+    return ss;
+}
+
 // One normalised value of the kXNormAdd input.
 __device__ __forceinline__ float norm_add(float a, float r, float inv, float w) { return (a + r) * inv * w; }
 

@@ -298,6 +298,24 @@ __device__ __forceinline__ void fast_job(const OpDesc &op, const TileJob &job, u
 #pragma unroll
         for (int k = 0; k < RS; ++k) acc[q][k] = 0.f;
 
+    // kXNormAdd with several waves: they share one op, so each sums the
+    // squares of a quarter of x + x_res (the writer workgroup's waves also
+    // store their share of it) and the parts meet in LDS, added in wave
+    // order by every wave.  Every wave of the workgroup reaches the barrier.
+    // (This runs before the first group's loads are issued; with one wave
+    // the norm is computed while they stream, below.)
+    float norm_inv_shared = 0.f;
+    if constexpr (XM == kXNormAdd && NW > 1) {
+        __shared__ float norm_part[NW];
+        const float part = norm_add_part(op, lane, wave, NW, op.x_out && job.writer);
+        if (lane == 0) norm_part[wave] = part;
+        __syncthreads();
+        float ss = norm_part[0];
+#pragma unroll
+        for (int w = 1; w < NW; ++w) ss += norm_part[w];
+        norm_inv_shared = 1.0f / sqrtf(ss / (float)(op.nb * kQuants) + op.norm_eps);
+    }
+
     if (sr0 < nsr) {
         const int G = op.gsr;
         const int64_t srb = op.sr_bytes;
@@ -334,7 +352,10 @@ __device__ __forceinline__ void fast_job(const OpDesc &op, const TileJob &job, u
         };
         if (ng > 0) issue(0);
         float ninv = 0.f;
-        if constexpr (XM == kXNormAdd) ninv = norm_add_inv(op, lane, op.x_out && job.writer && wave == 0);
+        if constexpr (XM == kXNormAdd) {
+            if constexpr (NW > 1) ninv = norm_inv_shared;
+            else ninv = norm_add_inv(op, lane, op.x_out && job.writer && wave == 0);
+        }
         if (PF == 2 && ng > 1) issue(1);
         for (int t = 0; t < ng; ++t) {
             uint8_t *cur = st0 + (t & 1) * SB;
