@@ -423,8 +423,8 @@ int q8_0_gemm_smallm(const float *X, const void *w, float *Y, int64_t m, int64_t
     // m = 2..3 with rows of one super-row (n a multiple of 256) run on the
     // vector units with lanes over (row, block pair): each lane holds the x
     // values of its two blocks in registers, the quants are converted once
-    // for all rows of X, and no split of X is needed (measured 12-18 % faster
-    // than the matrix cores at m = 2 on the 7B shapes, even to 3 % at m = 3,
+    // for all rows of X, and no split of X is needed (measured 16-24 % faster
+    // than the matrix cores at m = 2 on the 7B shapes, 9-17 % at m = 3,
     // slower from m = 4).  Where rows fill super-rows of 1 or 2 (n a multiple
     // of 128) the matrix cores take the other m >= 2: on the vector units
     // with a lane per row, the x values every lane needs come through LDS
@@ -788,7 +788,7 @@ int q8::chain_create_ex(const q8_0_op *ops, int64_t n_ops, uint32_t flags, const
     // runs); Q8GEMV_SK_PF sets its groups in flight (1 or 2).
     const int sk_mode = env_int("Q8GEMV_STREAMK", 1);
     // Q8GEMV_SK_TAIL overrides the tail threshold below (0: every row-rich launch)
-    const double kSkTailGroups = env_int("Q8GEMV_SK_TAIL", 4);
+    const double sk_tail_groups = env_int("Q8GEMV_SK_TAIL", 4);
     const int sk_pf = env_int("Q8GEMV_SK_PF", 1) == 2 ? 2 : 1;
     // a one-launch chain: every phase stream-K on the same workgroups, as
     // many as the CUs hold at once (four one-wave workgroups fill a CU's LDS)
@@ -845,13 +845,13 @@ int q8::chain_create_ex(const q8_0_op *ops, int64_t n_ops, uint32_t flags, const
             // tile times, w = row_tiles / (4 * cus).  Stream-K spreads the
             // (tile, group) items evenly but pays partial sums where tiles
             // are shared.  It is taken where the one-wave tail would idle
-            // the slots for at least kSkTailGroups group times (measured:
+            // the slots for at least sk_tail_groups group times (measured:
             // the 7B gate|up, 592 tiles of 14 groups, 5.9 group times, and
             // lm_head, 2376 of 14, 9.5, are faster on stream-K; the 0.6B
             // lm_head, 2374 tiles of 4 groups, 2.7, is 5 us faster on tiles).
             const double waves = (double)row_tiles / (double)(4 * cus);
             const double tail_groups = (std::ceil(waves) - waves) * (double)tile_groups;
-            sk = sk_mode == 2 || (sk_mode == 1 && row_tiles > cus && tail_groups >= kSkTailGroups);
+            sk = sk_mode == 2 || (sk_mode == 1 && row_tiles > cus && tail_groups >= sk_tail_groups);
             // A/B overrides: Q8GEMV_SPLIT_SLICES (slices per row tile), Q8GEMV_VARIANT
             if (const int forced = env_int("Q8GEMV_SPLIT_SLICES", 0); forced > 0) target = forced;
             if (std::getenv("Q8GEMV_VARIANT")) v = v_single;
