@@ -29,6 +29,9 @@ struct AttnFuse {
     const float *q_norm, *k_norm;
     float *kc_w, *vc_w;
     float eps, theta;
+    // if set: (cos, sin) of every rotation angle, [position][pair], as
+    // launch_rope_table leaves them; else attention computes the angles
+    const double2 *rope;
 };
 
 struct ArgmaxDesc {
@@ -40,6 +43,10 @@ struct ArgmaxDesc {
     uint32_t *cnt;       // arrival counter, zero between launches
     int *pos_dev;        // if set, incremented once the index is written
 };
+
+// (cos, sin) of pos * theta^(-i / half) for every pos < rows and i < half,
+// computed exactly as the rotation kernels compute them, into t[pos][i]
+hipError_t launch_rope_table(double2 *t, int rows, int half, float theta, hipStream_t s);
 
 // pos_dev, when not null, overrides pos (a recorded step reads it per replay)
 hipError_t launch_rms_norm(const float *x, const float *w, float *out, int dim, int rows, float eps,

@@ -267,13 +267,31 @@ __global__ __launch_bounds__(kThreads) void k_add_rms(float *x, const float *y, 
 // Pair (i, i + half) of each head turns by pos * theta^(-i / half); the angle
 // and its sine and cosine are taken in double precision (the page's float32
 // angle loses ~pos * 2^-24 rad), the rotation rounds once to float.
-__device__ __forceinline__ void rotate(double a, double b, int i, int half, int pos, float theta,
-                                       float &ra, float &rb) {
+__device__ __forceinline__ void rope_sincos(int i, int half, int pos, float theta, double &s, double &c) {
     const double ang = (double)pos * pow((double)theta, -(double)i / half);
-    double s, c;
     sincos(ang, &s, &c);
+}
+
+__device__ __forceinline__ void rotate_by(double a, double b, double s, double c, float &ra, float &rb) {
     ra = (float)(a * c - b * s);
     rb = (float)(a * s + b * c);
+}
+
+__device__ __forceinline__ void rotate(double a, double b, int i, int half, int pos, float theta,
+                                       float &ra, float &rb) {
+    double s, c;
+    rope_sincos(i, half, pos, theta, s, c);
+    rotate_by(a, b, s, c, ra, rb);
+}
+
+// The step's table of every angle's (cos, sin): t[pos * half + i].
+__global__ __launch_bounds__(256) void k_rope_table(double2 *t, int rows, int half, float theta) {
+    const int64_t j = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (j >= (int64_t)rows * half) return;
+    const int pos = (int)(j / half), i = (int)(j - (int64_t)pos * half);
+    double s, c;
+    rope_sincos(i, half, pos, theta, s, c);
+    t[j] = make_double2(c, s);
 }
 
 __global__ __launch_bounds__(256) void k_rope(float *x, int head_dim, int heads, const int *pos_dev,
@@ -402,13 +420,23 @@ __global__ __launch_bounds__(kAttnThreads) void k_attention(AttnDesc d, AttnFuse
             const int64_t crow = (int64_t)pos * d.kv_width + kv_off;
             if (tid < HALF) {
                 float ra, rb;
-                rotate(qs[tid], qs[tid + HALF], tid, HALF, pos, f.theta, ra, rb);
+                if (f.rope) {
+                    const double2 cs = f.rope[(int64_t)pos * HALF + tid];
+                    rotate_by(qs[tid], qs[tid + HALF], cs.y, cs.x, ra, rb);
+                } else {
+                    rotate(qs[tid], qs[tid + HALF], tid, HALF, pos, f.theta, ra, rb);
+                }
                 qs[tid] = ra;
                 qs[tid + HALF] = rb;
             } else if (cur && tid >= 128 && tid < 128 + HALF) {
                 const int i = tid - 128;
                 float ra, rb;
-                rotate(kn[i], kn[i + HALF], i, HALF, pos, f.theta, ra, rb);
+                if (f.rope) {
+                    const double2 cs = f.rope[(int64_t)pos * HALF + i];
+                    rotate_by(kn[i], kn[i + HALF], cs.y, cs.x, ra, rb);
+                } else {
+                    rotate(kn[i], kn[i + HALF], i, HALF, pos, f.theta, ra, rb);
+                }
                 kn[i] = ra;
                 kn[i + HALF] = rb;
                 if (writer) {
@@ -709,6 +737,12 @@ hipError_t launch_attention(const AttnDesc &d, hipStream_t s) {
     AttnFuse f;
     std::memset(&f, 0, sizeof f);
     return launch_attention_t<false>(d, f, s);
+}
+
+hipError_t launch_rope_table(double2 *t, int rows, int half, float theta, hipStream_t s) {
+    hipLaunchKernelGGL(k_rope_table, dim3(blocks_for((int64_t)rows * half)), dim3(256), 0, s, t, rows,
+                       half, theta);
+    return hipGetLastError();
 }
 
 hipError_t launch_attention_fused(const AttnDesc &d, const AttnFuse &f, hipStream_t s) {

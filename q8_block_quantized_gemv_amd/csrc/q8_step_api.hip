@@ -187,6 +187,7 @@ struct q8_0_step {
     uint32_t *cnt = nullptr;  // n_heads attention counters, then the argmax counter
     int32_t *pos = nullptr;
     uint32_t *token = nullptr;
+    double2 *rope = nullptr;  // (cos, sin) of every rotation angle, [position][pair]
     int max_chunks = 0, amax_wgs = 0, launches = 0;
     // one_launch: layer 0's q|k|v, then per layer one launch of o, gate|up,
     // down and the next layer's q|k|v (the lm_head after the last layer).
@@ -237,7 +238,7 @@ int issue_step(const q8_0_step *s, hipStream_t st) {
         d.max_chunks = s->max_chunks;
         AttnFuse f;
         f.q = s->q; f.k = s->k; f.v = s->v; f.q_norm = L.q_norm; f.k_norm = L.k_norm;
-        f.kc_w = kc; f.vc_w = vc; f.eps = m.eps; f.theta = m.theta;
+        f.kc_w = kc; f.vc_w = vc; f.eps = m.eps; f.theta = m.theta; f.rope = s->rope;
         ok(launch_attention_fused(d, f, st));
         if (s->one_launch) {
             if ((rc = chain_issue(s->chains[1 + l], st))) return rc;
@@ -318,7 +319,8 @@ int q8_0_step_create(const q8_0_model *m, q8_0_step **out) {
         (size_t)m->inter, (size_t)m->vocab,
         (size_t)(m->n_layers * m->max_seq * s->kv_width), (size_t)(m->n_layers * m->max_seq * s->kv_width),
         (size_t)(m->n_heads * s->max_chunks * (m->head_dim + 2)), (size_t)(2 * s->amax_wgs),
-        (size_t)(m->n_heads + 1), 1, 1};
+        (size_t)(m->n_heads + 1), 1, 1,
+        (size_t)(m->max_seq * (m->head_dim / 2) * 4)};   // double2 per (position, pair)
     std::vector<size_t> offs;
     size_t total = 0;
     for (size_t n : sizes) {
@@ -339,6 +341,15 @@ int q8_0_step_create(const q8_0_model *m, q8_0_step **out) {
     s->cnt = (uint32_t *)(b + offs[nf]);
     s->pos = (int32_t *)(b + offs[nf + 1]);
     s->token = (uint32_t *)(b + offs[nf + 2]);
+    s->rope = (double2 *)(b + offs[nf + 3]);
+    // the rotation angles of every position, once: attention reads them
+    // instead of evaluating pow and sincos in double precision per token
+    if ((e = launch_rope_table(s->rope, (int)m->max_seq, (int)(m->head_dim / 2), m->theta, nullptr)) !=
+            hipSuccess ||
+        (e = hipDeviceSynchronize()) != hipSuccess) {
+        step_free(s);
+        return fail_hip(e, "q8_0_step_create rotation table");
+    }
     // the matvecs: fused where independent.  Each residual add and the norm
     // after it are folded into the next matvec's activation staging
     // (kXNormAdd): it reads the residual stream and the block's output,
