@@ -121,8 +121,9 @@ typedef struct q8_0_step q8_0_step; /* opaque */
 /*
  * Validate the model, allocate the step's device state (activations, the
  * KV caches: n_layers x max_seq x n_kv_heads*head_dim floats each for K
- * and V, workspaces, the position and token words) and record one token's
- * launches into a hipGraph.  Weight pointers are baked into the recording
+ * and V, the rotation angles' (cos, sin) as doubles for every position and
+ * pair: max_seq x head_dim/2 x 16 bytes, workspaces, the position and token
+ * words) and record one token's launches into a hipGraph.  Weight pointers are baked into the recording
  * and must stay valid until q8_0_step_destroy.  The position starts at 0
  * and the token at 0.  max_seq <= Q8_MAX_SEQ.
  */
