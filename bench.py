@@ -31,12 +31,24 @@ sys.path.insert(0, ROOT)
 HBM_PEAK_GBS = 8000.0
 # the sources of the chain's kernel: counters taken on other sources are stale
 KERNEL_SOURCES = [os.path.join(ROOT, "q8_block_quantized_gemv_amd", "csrc", f)
-                  for f in ("q8_gemv.hip", "q8_device.h", "q8_internal.h")]
+                  for f in ("q8_gemv_rc.hip", "q8_rc.h", "q8_block.h", "q8_device.h", "q8_internal.h")]
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_7b_chain.json")
 
 
 def say(msg):
     print("[bench] " + msg, file=sys.stderr, flush=True)
+
+
+def cpu_model() -> str:
+    """The host CPU's model name (from /proc/cpuinfo), for the baselines."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
 
 
 def kernel_digest() -> str:
@@ -96,7 +108,7 @@ def cpu_baseline(data, budget_s: float):
             if t_used >= budget_s:
                 break
     return {"value": round(done_bytes / t_used / 1e9, 4), "unit": "GB/s", "cores": 1,
-            "kind": "oracle",
+            "kind": "oracle", "cpu_model": cpu_model(),
             "sample": "%d ops of the %d-op workload in encode order, %.2f passes (%.1f MB, %.1f s), "
                       "serial float64 C oracle, one host thread" % (
                           ops_done, len(data), ops_done / len(data), done_bytes / 1e6, t_used)}
@@ -126,7 +138,7 @@ def cpu_baseline_threaded(data, budget_s: float, threads: int):
                 if t_used >= budget_s:
                     break
     return {"value": round(done_bytes / t_used / 1e9, 4), "unit": "GB/s", "cores": threads,
-            "kind": "oracle",
+            "kind": "oracle", "cpu_model": cpu_model(),
             "sample": "%d ops of the %d-op workload in encode order, %.2f passes (%.1f MB, %.1f s), "
                       "serial float64 C oracle on contiguous row ranges, %d host threads" % (
                           ops_done, len(data), ops_done / len(data), done_bytes / 1e6, t_used,
@@ -406,12 +418,13 @@ def main():
     launches = chain.launches
     kernel_s = time_steps(lambda: chain.run(q8.MODE_EAGER, stream), args.steps) / args.steps / launches
     achieved = nbytes / launches / kernel_s / 1e9
-    # a chain of one op is that op's standalone launch (four-wave workgroups);
-    # more independent ops share one fused launch.  Template arguments: waves
-    # per workgroup, groups in flight, input mode (0 float activations, 1
-    # activations quantized to Q8_0)
-    kernel = (("k_q8_gemv_fused<1,1,%d>" if len(ops_shape) > 1 else "k_q8_gemv<4,1,%d>")
-              % (1 if args.xq else 0))
+    # a chain of one op is that op's standalone launch (its latency plan);
+    # more independent ops share one fused launch of one-wave tiles of 64
+    # rows.  Template arguments: lanes per row, waves per workgroup, input
+    # mode (0 float activations, 1 activations quantized to Q8_0)
+    mode = 1 if args.xq else 0
+    kernel = ("k_q8_gemv_rc_fused<1,1,%d>" % mode if len(ops_shape) > 1
+              else "k_q8_gemv_rc<C,NWK,%d> (the op's latency plan)" % mode)
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                 "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                 "traffic": measured_traffic(args.workload, kernel),

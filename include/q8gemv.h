@@ -36,7 +36,9 @@
  *   - Results are bitwise reproducible run to run for the same inputs,
  *     shapes and device: every sum runs in a fixed order (the small-batch
  *     product counts arrivals with an atomic counter, but adds partial sums
- *     in a fixed order).
+ *     in a fixed order).  For m = 1 the order depends on n only: every
+ *     launch shape, chain mode and chain flag gives the same bits as
+ *     q8_0_gemv for the same x and w.
  *   - Accuracy: |y - exact| <= 1e-5 * sum_j |w_j x_j| + 1e-6 per output for
  *     finite inputs (float32 arithmetic with a bounded summation depth).
  */
@@ -63,8 +65,7 @@ enum q8_status {
     Q8_ERR_ALIAS = -4,       /* an output overlaps an input */
     Q8_ERR_NO_DEVICE = -5,   /* no HIP device is visible */
     Q8_ERR_HIP = -6,         /* the HIP runtime reported an error (see q8_0_last_error) */
-    Q8_ERR_TIMEOUT = -7,     /* q8_0_stream_wait ran out of time, or a barrier wait of a
-                                Q8_CHAIN_ONE_LAUNCH chain gave up (q8_0_chain_check) */
+    Q8_ERR_TIMEOUT = -7,     /* q8_0_stream_wait ran out of time */
     Q8_ERR_UNSUPPORTED = -8  /* the current device is not gfx950 */
 };
 
@@ -86,6 +87,17 @@ Q8_API int q8_0_gemv(const float *x, const void *w, float *y, int64_t n, int64_t
               void *stream);
 
 /*
+ * q8_0_gemv on an explicit launch shape, for n a multiple of 256 (else
+ * Q8_ERR_SHAPE): lanes_per_row (1, 2 or 4) lanes share each row, so a wave
+ * covers 64 / lanes_per_row rows, and `waves` (1, 2 or 4) waves per
+ * workgroup split each row's groups.  The result is bitwise identical to
+ * q8_0_gemv's for every shape; the shape only changes the launch (for
+ * measurements and for tests of that identity).  Allocates nothing.
+ */
+Q8_API int q8_0_gemv_shaped(const float *x, const void *w, float *y, int64_t n, int64_t p,
+                            int lanes_per_row, int waves, void *stream);
+
+/*
  * Y = X W^T for m in 1..16 activation rows in one pass over W: the small-batch
  * matvec of multi-sequence decode (page "Metal Backend Optimizations",
  * section 0.3, the batched-matvec kernel family left open for 2..8 tokens;
@@ -95,6 +107,22 @@ Q8_API int q8_0_gemv(const float *x, const void *w, float *y, int64_t n, int64_t
  */
 Q8_API int q8_0_gemm_smallm(const float *X, const void *w, float *Y, int64_t m,
                      int64_t n, int64_t p, void *stream);
+
+/* Small-batch kernels (q8_0_gemm_smallm_kernel). */
+#define Q8_SMALLM_AUTO 0  /* the choice q8_0_gemm_smallm makes */
+#define Q8_SMALLM_VALU 1  /* vector units, a lane per row, up to 4 rows of X per pass over W */
+#define Q8_SMALLM_MFMA 2  /* bf16 matrix cores on X split exactly in three parts; n % 128 == 0 */
+#define Q8_SMALLM_VROW 3  /* vector units, lanes over a row and a block pair, two waves per
+                             workgroup; n % 256 == 0 and m <= 3 */
+#define Q8_SMALLM_VROW1 4 /* the same with one wave per workgroup */
+
+/*
+ * q8_0_gemm_smallm on a named kernel (for measurements and for tests of each
+ * kernel); Q8_ERR_SHAPE if that kernel does not take (m, n).  Each kernel
+ * meets the same accuracy bar; their roundings differ.
+ */
+Q8_API int q8_0_gemm_smallm_kernel(const float *X, const void *w, float *Y, int64_t m,
+                                   int64_t n, int64_t p, int kernel, void *stream);
 
 /*
  * One decode step's chain of matvecs, recorded once and replayed per token
@@ -111,20 +139,14 @@ typedef struct q8_0_op {
 
 typedef struct q8_0_chain q8_0_chain; /* opaque */
 
-/* chain_create flags (PER_OP and SPLIT_K may be combined) */
+/* chain_create flags (may be combined) */
 #define Q8_CHAIN_FUSE 0u    /* merge runs of mutually independent ops into one launch */
 #define Q8_CHAIN_PER_OP 1u  /* one kernel launch per op, in array order */
 #define Q8_CHAIN_SPLIT_K 2u /* for ops that wait on each other (a real decode step): plan
-                               every op for latency -- its K split over more waves, across
-                               workgroups when it has few rows; results stay bitwise
-                               reproducible but round differently from q8_0_gemv */
+                               every launch for latency -- short row tiles, each row's groups
+                               split over the waves of a workgroup -- rather than for the
+                               steady state of a long launch; the same bits either way */
 #define Q8_CHAIN_XQ 4u      /* every op as q8_0_gemv_q8q8: x quantized to Q8_0, integer dots */
-#define Q8_CHAIN_ONE_LAUNCH 8u /* the whole chain as ONE kernel launch: each run of mutually
-                               independent ops is a phase, split stream-K style over workgroups
-                               that all stay resident, and a phase starts once every
-                               workgroup has finished the one before (a device-wide barrier).
-                               Rounds like Q8_CHAIN_SPLIT_K; not with Q8_CHAIN_XQ or
-                               Q8_CHAIN_PER_OP */
 
 /* decode_chain modes */
 #define Q8_MODE_GRAPH 0     /* replay the recorded hipGraph: one host call per token */
@@ -139,10 +161,11 @@ typedef struct q8_0_chain q8_0_chain; /* opaque */
  * with Q8_CHAIN_FUSE, maximal runs of ops with no such overlap share one
  * launch.  The pointers in `ops` are baked into the recording: they must stay
  * valid, at the same addresses, until q8_0_chain_destroy.  The handle owns a
- * small device table (op descriptors, the tile schedule and, with
- * Q8_CHAIN_SPLIT_K, the partial sums of split ops), a private capture stream
- * and the graph; a token's replay allocates nothing.  Replays of one chain
- * must not overlap in time (they share that table and their outputs).
+ * small device table (op descriptors and the tile schedule), a private
+ * capture stream and the graph; a token's replay allocates nothing.  Every
+ * op's outputs are bitwise those of q8_0_gemv (q8_0_gemv_q8q8 with
+ * Q8_CHAIN_XQ), whatever the flags and mode.  Replays of one chain must not
+ * overlap in time (they share their outputs).
  * On failure *out is set to NULL and nothing is leaked.
  */
 Q8_API int q8_0_chain_create(const q8_0_op *ops, int64_t n_ops, uint32_t flags,
@@ -177,14 +200,6 @@ Q8_API int q8_0_decode_chain(q8_0_chain *chain, int mode, void *stream);
 
 /* Kernel launches one token costs (1 .. n_ops); negative status on a bad handle. */
 Q8_API int q8_0_chain_launches(const q8_0_chain *chain);
-
-/* Q8_OK, or Q8_ERR_TIMEOUT if a barrier wait of a Q8_CHAIN_ONE_LAUNCH chain
- * gave up (seconds without progress: the GPU was shared with work that kept
- * the chain's workgroups from all being resident) since the chain was
- * created; its outputs since then are not to be trusted.  Reads one word
- * from the device and waits for nothing else: call it once the replays of
- * interest have finished.  Chains without Q8_CHAIN_ONE_LAUNCH return Q8_OK. */
-Q8_API int q8_0_chain_check(const q8_0_chain *chain);
 
 /* Release the handle (NULL is accepted).  The caller must make sure no
  * replay is still running. */

@@ -93,12 +93,9 @@ Q8_API int q8_0_argmax(const float *x, int64_t n, uint32_t *out, void *stream);
  * small kernels are fused where one feeds the next: the embedding row with
  * the first norm, each residual add with the norm after it, the per-head
  * q/k norms with the rotary embedding and the cache append, and argmax with
- * the position advance.  A token is 5 n_layers + 3 launches.  With the
- * environment variable Q8GEMV_ONE_LAUNCH=1 at q8_0_step_create, the
- * matvecs between one attention and the next (o; gate, up; down; the next
- * layer's q, k, v, or the lm_head) run as one Q8_CHAIN_ONE_LAUNCH launch
- * instead: 2 n_layers + 3 launches (embed+norm, layer 0's q|k|v, per layer
- * attention and that launch, argmax), the same results within the bar.
+ * the position advance.  A token is 5 n_layers + 3 launches.  Every matvec
+ * launch is planned for latency (Q8_CHAIN_SPLIT_K); its outputs are bitwise
+ * those of q8_0_gemv on the same inputs.
  */
 typedef struct q8_0_layer_w {
     const void *wq, *wk, *wv, *wo;   /* Q8_0, 16-B aligned, as q8_0_gemv's w */
@@ -144,9 +141,6 @@ Q8_API int q8_0_step_run(q8_0_step *s, int mode, void *stream);
 /* Kernel launches one token costs. */
 Q8_API int q8_0_step_launches(const q8_0_step *s);
 
-/* q8_0_chain_check over the step's matvec launches: Q8_ERR_TIMEOUT if a
- * barrier wait of one of them gave up since the step was created. */
-Q8_API int q8_0_step_check(const q8_0_step *s);
 
 /* Device buffers of the step, for reading results. */
 typedef struct q8_0_step_bufs {

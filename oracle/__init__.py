@@ -186,6 +186,34 @@ def gemv_rows(w, x, n: int, rows: Iterable[int]):
     return default().gemv_rows(w, x, n, rows)
 
 
+def gemv_threaded(w, x, n: int, p: int, threads: Optional[int] = None):
+    """gemv() with contiguous row ranges on a pool of host threads (the C
+    call releases the GIL).  Every row is the same serial oracle on the same
+    bytes, so the results equal gemv()'s exactly."""
+    from concurrent.futures import ThreadPoolExecutor
+    o = default()
+    w = _as_w(w)
+    x = np.ascontiguousarray(x, dtype=np.float32).reshape(-1)
+    if w.size < p * row_bytes(n) or x.size < n:
+        raise ValueError("buffer too small for the stated shape")
+    threads = max(1, min(threads or min(16, os.cpu_count() or 1), p))
+    y = np.empty(p, np.float32)
+    y64 = np.empty(p, np.float64)
+    mag = np.empty(p, np.float64)
+    rb = row_bytes(n)
+    cuts = [p * k // threads for k in range(threads + 1)]
+
+    def part(k):
+        a, b = cuts[k], cuts[k + 1]
+        if b > a and o.lib.q8o_gemv(_ptr(w) + a * rb, _ptr(x), n, b - a, _ptr(y[a:]), _ptr(y64[a:]),
+                                    _ptr(mag[a:])) != 0:
+            raise ValueError("oracle rejected the shape")
+
+    with ThreadPoolExecutor(max_workers=threads) as pool:
+        list(pool.map(part, range(threads)))
+    return y, y64, mag
+
+
 def gemm(w, X, m: int, n: int, p: int):
     return default().gemm(w, X, m, n, p)
 

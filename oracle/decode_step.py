@@ -121,7 +121,7 @@ def _r32(a) -> np.ndarray:
     return np.asarray(a, dtype=np.float64).astype(np.float32)
 
 
-def decode_step(cfg: dict, w: dict, kc: list, vc: list, token: int, pos: int):
+def decode_step(cfg: dict, w: dict, kc: list, vc: list, token: int, pos: int, matvec=None):
     """One decode step of a Qwen3-style model in the order of section "One
     command buffer": per layer norm, q/k/v projections, per-head q and k
     norms, rotary embedding at pos, cache append at pos, attention over pos + 1
@@ -130,6 +130,8 @@ def decode_step(cfg: dict, w: dict, kc: list, vc: list, token: int, pos: int):
     and argmax.  The Q8_0 projections are the oracle's matvec.
 
     kc, vc: per layer float32 (max_seq, kv_width) caches, updated in place.
+    matvec: the Q8_0 matvec to use, (w, x, n, p) -> (y, y64, mag) (default
+    the serial oracle; oracle.gemv_threaded gives the same results).
     Returns (next token, logits float32, logits float64, logits magnitude
     sum_j |w_j x_j| per row, final residual x float32).
     """
@@ -138,8 +140,10 @@ def decode_step(cfg: dict, w: dict, kc: list, vc: list, token: int, pos: int):
     eps, theta, vocab = cfg["eps"], cfg["theta"], cfg["vocab"]
     qw, kvw = nh * hd, nkv * hd
 
+    gemv = matvec or _q8_gemv
+
     def mv(wt, x, n, p):
-        return _q8_gemv(wt, x, n, p)[0]
+        return gemv(wt, x, n, p)[0]
 
     x = (np.asarray(w["embed"], np.float32).reshape(vocab, hid)[token].copy()
          if 0 <= token < vocab else np.zeros(hid, np.float32))
@@ -159,5 +163,5 @@ def decode_step(cfg: dict, w: dict, kc: list, vc: list, token: int, pos: int):
         h = _r32(silu_hadamard(mv(L["wgate"], xn, hid, inter), mv(L["wup"], xn, hid, inter)))
         x = _r32(add_inplace(x, mv(L["wdown"], h, inter, hid)))
     xn = _r32(rms_norm_rows(x, w["out_norm"], hid, eps)).reshape(-1)
-    y, y64, mag = _q8_gemv(w["lm_head"], xn, hid, vocab)
+    y, y64, mag = gemv(w["lm_head"], xn, hid, vocab)
     return argmax_row(y), y, y64, mag, x

@@ -7,7 +7,9 @@ implementation: if the library is missing, importing this package raises.
 
 The names follow the C ABI:
     gemv(x, w, y=None, stream=None)            -> q8_0_gemv
+    gemv(x, w, shape=(c, waves))               -> q8_0_gemv_shaped
     gemm_smallm(X, w, Y=None, stream=None)     -> q8_0_gemm_smallm
+    gemm_smallm(X, w, kernel=SMALLM_MFMA)      -> q8_0_gemm_smallm_kernel
     gemv_q8q8(x, w, y=None), quantize(x)       -> q8_0_gemv_q8q8, q8_0_quantize
     Chain(ops, fuse=True, split_k=False) .run  -> q8_0_chain_create / q8_0_decode_chain
     stream_wait(stream, timeout_ms)            -> q8_0_stream_wait
@@ -38,20 +40,26 @@ Q8_CHAIN_FUSE = 0
 Q8_CHAIN_PER_OP = 1
 Q8_CHAIN_SPLIT_K = 2
 Q8_CHAIN_XQ = 4
-Q8_CHAIN_ONE_LAUNCH = 8
 MODE_GRAPH = 0
 MODE_EAGER = 1
 MODE_SYNC_EACH = 2
 
+SMALLM_AUTO = 0
+SMALLM_VALU = 1
+SMALLM_MFMA = 2
+SMALLM_VROW = 3
+SMALLM_VROW1 = 4
+
 BLOCK_QUANTS = 32
 BLOCK_BYTES = 34
 
-EXPORTS = ("q8_0_gemv", "q8_0_gemm_smallm", "q8_0_chain_create", "q8_0_decode_chain",
-           "q8_0_chain_launches", "q8_0_chain_check", "q8_0_chain_destroy", "q8_0_stream_wait",
+EXPORTS = ("q8_0_gemv", "q8_0_gemv_shaped", "q8_0_gemm_smallm", "q8_0_gemm_smallm_kernel",
+           "q8_0_chain_create", "q8_0_decode_chain",
+           "q8_0_chain_launches", "q8_0_chain_destroy", "q8_0_stream_wait",
            "q8_0_status_string", "q8_0_last_error", "q8_0_gemv_q8q8", "q8_0_quantize",
            "q8_0_rms_norm", "q8_0_rope", "q8_0_append_kv", "q8_0_attention_decode",
            "q8_0_add_inplace", "q8_0_silu_hadamard", "q8_0_argmax",
-           "q8_0_step_create", "q8_0_step_reset", "q8_0_step_run", "q8_0_step_launches", "q8_0_step_check",
+           "q8_0_step_create", "q8_0_step_reset", "q8_0_step_run", "q8_0_step_launches",
            "q8_0_step_buffers", "q8_0_step_destroy")
 
 NO_INDEX = 0xFFFFFFFF   # argmax of a row of NaN
@@ -95,12 +103,13 @@ def _load():
     lib = ctypes.CDLL(LIBRARY)
     vp, i64 = ctypes.c_void_p, ctypes.c_int64
     lib.q8_0_gemv.argtypes = [vp, vp, vp, i64, i64, vp]
+    lib.q8_0_gemv_shaped.argtypes = [vp, vp, vp, i64, i64, ctypes.c_int, ctypes.c_int, vp]
     lib.q8_0_gemm_smallm.argtypes = [vp, vp, vp, i64, i64, i64, vp]
+    lib.q8_0_gemm_smallm_kernel.argtypes = [vp, vp, vp, i64, i64, i64, ctypes.c_int, vp]
     lib.q8_0_chain_create.argtypes = [ctypes.POINTER(Q8Op), i64, ctypes.c_uint32,
                                       ctypes.POINTER(vp)]
     lib.q8_0_decode_chain.argtypes = [vp, ctypes.c_int, vp]
     lib.q8_0_chain_launches.argtypes = [vp]
-    lib.q8_0_chain_check.argtypes = [vp]
     lib.q8_0_chain_destroy.argtypes = [vp]
     lib.q8_0_stream_wait.argtypes = [vp, i64]
     lib.q8_0_status_string.argtypes = [ctypes.c_int]
@@ -121,7 +130,6 @@ def _load():
     lib.q8_0_step_reset.argtypes = [vp, i64, u32, vp]
     lib.q8_0_step_run.argtypes = [vp, i32, vp]
     lib.q8_0_step_launches.argtypes = [vp]
-    lib.q8_0_step_check.argtypes = [vp]
     lib.q8_0_step_buffers.argtypes = [vp, ctypes.POINTER(Q8StepBufs)]
     lib.q8_0_step_destroy.argtypes = [vp]
     for name in EXPORTS:
@@ -191,8 +199,11 @@ def weight_shape(w) -> Tuple[int, int]:
     return int(w.shape[0]), int(w.shape[1]) // BLOCK_BYTES * BLOCK_QUANTS
 
 
-def gemv(x, w, y=None, stream=None):
-    """y = W x.  x float32 (n,), w uint8 (p, n/32*34); returns y float32 (p,)."""
+def gemv(x, w, y=None, stream=None, shape=None):
+    """y = W x.  x float32 (n,), w uint8 (p, n/32*34); returns y float32 (p,).
+
+    shape=(lanes_per_row, waves) launches on that explicit shape
+    (q8_0_gemv_shaped, n a multiple of 256): the same bits, another launch."""
     torch = _torch()
     _need(x, torch.float32, "x")
     _need(w, torch.uint8, "w")
@@ -204,7 +215,12 @@ def gemv(x, w, y=None, stream=None):
     _need(y, torch.float32, "y")
     if y.numel() != p:
         raise ValueError("y has %d elements, w has %d rows" % (y.numel(), p))
-    check(lib.q8_0_gemv(x.data_ptr(), w.data_ptr(), y.data_ptr(), n, p, _stream_handle(stream)))
+    if shape is None:
+        check(lib.q8_0_gemv(x.data_ptr(), w.data_ptr(), y.data_ptr(), n, p, _stream_handle(stream)))
+    else:
+        c, waves = shape
+        check(lib.q8_0_gemv_shaped(x.data_ptr(), w.data_ptr(), y.data_ptr(), n, p, int(c), int(waves),
+                                   _stream_handle(stream)))
     return y
 
 
@@ -239,8 +255,10 @@ def quantize(x, xq=None, stream=None):
     return xq
 
 
-def gemm_smallm(X, w, Y=None, stream=None):
-    """Y = X W^T for X float32 (m, n), m in 1..16; returns Y float32 (m, p)."""
+def gemm_smallm(X, w, Y=None, stream=None, kernel=None):
+    """Y = X W^T for X float32 (m, n), m in 1..16; returns Y float32 (m, p).
+
+    kernel=SMALLM_* runs a named kernel (q8_0_gemm_smallm_kernel)."""
     torch = _torch()
     _need(X, torch.float32, "X")
     _need(w, torch.uint8, "w")
@@ -253,8 +271,12 @@ def gemm_smallm(X, w, Y=None, stream=None):
     _need(Y, torch.float32, "Y")
     if tuple(Y.shape) != (m, p):
         raise ValueError("Y must be (%d, %d)" % (m, p))
-    check(lib.q8_0_gemm_smallm(X.data_ptr(), w.data_ptr(), Y.data_ptr(), m, n, p,
-                               _stream_handle(stream)))
+    if kernel is None:
+        check(lib.q8_0_gemm_smallm(X.data_ptr(), w.data_ptr(), Y.data_ptr(), m, n, p,
+                                   _stream_handle(stream)))
+    else:
+        check(lib.q8_0_gemm_smallm_kernel(X.data_ptr(), w.data_ptr(), Y.data_ptr(), m, n, p, int(kernel),
+                                          _stream_handle(stream)))
     return Y
 
 
@@ -270,8 +292,7 @@ class Chain:
     keeps references to them.
     """
 
-    def __init__(self, ops: Sequence, fuse: bool = True, split_k: bool = False, xq: bool = False,
-                 one_launch: bool = False):
+    def __init__(self, ops: Sequence, fuse: bool = True, split_k: bool = False, xq: bool = False):
         torch = _torch()
         arr = (Q8Op * len(ops))()
         self._keep = []
@@ -286,7 +307,7 @@ class Chain:
             self._keep.append((x, w, y))
         h = ctypes.c_void_p()
         flags = ((Q8_CHAIN_FUSE if fuse else Q8_CHAIN_PER_OP) | (Q8_CHAIN_SPLIT_K if split_k else 0) |
-                 (Q8_CHAIN_XQ if xq else 0) | (Q8_CHAIN_ONE_LAUNCH if one_launch else 0))
+                 (Q8_CHAIN_XQ if xq else 0))
         check(lib.q8_0_chain_create(arr, len(ops), flags, ctypes.byref(h)))
         self._h = h
         self.n_ops = len(ops)
@@ -299,13 +320,6 @@ class Chain:
         if self._h is None:
             raise RuntimeError("chain is closed")
         check(lib.q8_0_decode_chain(self._h, mode, _stream_handle(stream)))
-
-    def check(self) -> None:
-        """Raise Q8Error (Q8_ERR_TIMEOUT) if a barrier wait of a one-launch
-        chain gave up since the chain was created."""
-        if self._h is None:
-            raise RuntimeError("chain is closed")
-        check(lib.q8_0_chain_check(self._h))
 
     def close(self) -> None:
         if getattr(self, "_h", None) is not None:
@@ -517,11 +531,6 @@ class Step:
 
     def run(self, mode: int = MODE_GRAPH, stream=None) -> None:
         check(lib.q8_0_step_run(self._handle(), int(mode), _stream_handle(stream)))
-
-    def check(self) -> None:
-        """Raise Q8Error (Q8_ERR_TIMEOUT) if a barrier wait of one of the
-        step's one-launch matvec chains gave up since the step was created."""
-        check(lib.q8_0_step_check(self._handle()))
 
     def buffer(self, name: str):
         """A device tensor viewing one of the step's buffers (token, pos, x,

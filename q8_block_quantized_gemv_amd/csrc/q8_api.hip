@@ -127,6 +127,8 @@ int workspace_for(int dev, hipStream_t s, size_t ws_bytes, size_t cnt_n, float *
 
 namespace {
 
+constexpr int kLdsPerCu = 160 * 1024;
+
 int64_t w_bytes(int64_t n, int64_t p) { return p * (n / kQuants) * kBlockBytes; }
 
 // Argument checks shared by every entry point; touches no device state.
@@ -155,22 +157,9 @@ int64_t gcd64(int64_t a, int64_t b) {
     return a;
 }
 
-// Kernel shape per launch kind.  Q8GEMV_VARIANT=nw<1|2|4>pf<1|2> (read at
-// each planning call) overrides it for A/B measurements.
-Variant pick_variant(bool fused) {
-    Variant v = fused ? Variant{1, 1} : Variant{4, 1};
-    if (const char *e = std::getenv("Q8GEMV_VARIANT")) {
-        int nw = 0, pf = 0;
-        if (std::sscanf(e, "nw%dpf%d", &nw, &pf) == 2 && (nw == 1 || nw == 2 || nw == 4) &&
-            (pf == 1 || pf == 2))
-            v = Variant{nw, pf};
-    }
-    return v;
-}
-
-// Waves that split one row tile's groups (ks <= nw).  A standalone launch
-// wants many workgroups; inside a fused chain the other ops fill the GPU, so
-// the choice only has to keep the waves of a workgroup evenly loaded.
+// rs > 1: waves that split one row tile's groups (ks <= nw).  A standalone
+// launch wants many workgroups; inside a fused launch the other ops fill the
+// GPU, so the choice only has to keep the waves of a workgroup evenly loaded.
 int choose_ks(int64_t gsr, int64_t nsr, bool standalone, int nw) {
     auto eff = [&](int ks) {
         const int64_t per = (gsr + ks - 1) / ks;
@@ -193,26 +182,9 @@ int choose_ks(int64_t gsr, int64_t nsr, bool standalone, int nw) {
     return best;
 }
 
-// K slices across workgroups (SPLIT_K chains): up to `target` slices, at
-// least one group each, at most kMaxSlices.  With one wave per row tile
-// (ks == 1) the wave owns all kSlots slots and any run of groups can be a
-// slice; with ks > 1 a slice holds a multiple of kSlots groups.
-void plan_slices(OpDesc &d, int64_t target) {
-    if (target <= 1 || d.gsr <= 1) return;
-    const bool any_run = d.ks == 1;
-    int64_t S = std::min<int64_t>(std::min<int64_t>(target, kMaxSlices), d.gsr);
-    if (!any_run) S = std::min<int64_t>(S, (d.gsr + kSlots - 1) / kSlots);
-    if (S <= 1) return;
-    int64_t per = (d.gsr + S - 1) / S;
-    if (!any_run) per = (per + kSlots - 1) / kSlots * kSlots;
-    S = (d.gsr + per - 1) / per;
-    if (S <= 1) return;
-    d.slices = (int32_t)S;
-    d.slice_groups = (int32_t)per;
-}
-
+// The op's shape fields.  rs > 1: planned for workgroups of nw waves.
 OpDesc plan_op(const float *x, const void *w, float *y, int64_t m, int64_t n, int64_t p,
-               bool standalone, int nw = kWaves, int64_t slices = 1) {
+               bool standalone, int nw) {
     OpDesc d;
     std::memset(&d, 0, sizeof d);
     const int64_t nb = n / kQuants;
@@ -226,28 +198,75 @@ OpDesc plan_op(const float *x, const void *w, float *y, int64_t m, int64_t n, in
     d.nsr = (int32_t)(p / rs);
     d.gsr = (int32_t)(rs * nb / kGroupBlocks);
     d.sr_bytes = rs * nb * kBlockBytes;
-    d.ks = choose_ks(d.gsr, d.nsr, standalone, nw);
-    d.slices = 1;
-    d.slice_groups = d.gsr;
-    plan_slices(d, slices);
-    d.fast_tiles = (int32_t)fast_tiles_for(d.nsr, d.ks, nw, d.slices);
-    d.tail_row0 = (int32_t)(d.nsr * rs);
     d.m = (int32_t)m;
     d.x_stride = n;
     d.y_stride = p;
+    if (rs == 1) {
+        d.ks = 1;
+        d.fast_tiles = (int32_t)rc_tiles_for(p, 1);
+        d.tail_row0 = (int32_t)p;
+    } else {
+        d.ks = choose_ks(d.gsr, d.nsr, standalone, nw);
+        d.fast_tiles = (int32_t)fast_tiles_for(d.nsr, d.ks, nw);
+        d.tail_row0 = (int32_t)(d.nsr * rs);
+    }
     return d;
 }
 
-int64_t tiles_of(const OpDesc &d, int nw = kWaves) {
+// rs > 1: every workgroup of a launch, fast tiles then tail tiles.
+int64_t tiles_of(const OpDesc &d, int nw) {
     return (int64_t)d.fast_tiles + tail_tiles_for((int64_t)d.p - d.tail_row0, nw);
 }
 
+// Launch shape of the rows-and-group-slots kernel for a launch that waits
+// on the one before it: `rows` rows of G groups (one op, or independent ops
+// of one width) read in mode xmode, on `cus` CUs.  From a sweep of lone
+// launches at the decode shapes (0.6B and 7B projections, lm_heads):
+//  * tiles of 16 rows (C = 4) with the groups split over NWK waves by slot,
+//    as many waves as there are group columns (up to 4), when one wave of
+//    such workgroups covers the rows (a row-poor op: every wave then streams
+//    its columns at once, e.g. 7B q/o/down, every 0.6B projection);
+//  * tiles of 32 rows with four waves when that still fits (7B q|k|v);
+//  * otherwise one-wave tiles of 16 rows if they are all resident at once
+//    (7B gate), else two-wave tiles (7B gate|up, lm_heads: fewer columns per
+//    wave shortens the last wave of tiles).
+RcShape plan_rc_latency(int64_t rows, int64_t G, int xmode, int64_t cus) {
+    auto resident = [&](RcShape sh) {
+        const int b = gemv_rc_lds_bytes(sh, xmode);
+        return b > 0 ? cus * std::max(1, kLdsPerCu / b) : 0;
+    };
+    const int64_t J4 = (G + 3) / 4;
+    const int n4 = J4 >= 3 ? 4 : (int)J4;
+    const int64_t t4 = (rows + 15) / 16;
+    if (t4 <= resident({4, n4})) return {4, n4};
+    if ((G + 1) / 2 >= 4 && (rows + 31) / 32 <= resident({2, 4})) return {2, 4};
+    if (t4 <= resident({4, 1})) return {4, 1};
+    return {4, J4 >= 2 ? 2 : 1};
+}
+
+// Launch shape of a fused launch of independent ops (a throughput launch):
+// one-wave tiles of 64 rows, the steady-state layout.
+constexpr RcShape kFuseShape{1, 1};
+
+bool shape_ok(int c, int nwk) {
+    return (c == 1 || c == 2 || c == 4) && (nwk == 1 || nwk == 2 || nwk == 4);
+}
+
+// One matvec: rs == 1 on the rows-and-group-slots kernel in `sh` (or its
+// latency plan when sh.c == 0); rs > 1 on four-wave super-row workgroups.
 int gemv_launch(const float *x, const void *w, float *y, int64_t n, int64_t p, hipStream_t s,
-                bool xq = false) {
-    const Variant v = pick_variant(false);
-    const OpDesc d = plan_op(x, w, y, 1, n, p, true, v.nw);
-    hipError_t e = launch_gemv_single(d, v, tiles_of(d, v.nw), s, xq ? kXQuant : kXFloat);
-    if (e != hipSuccess) return fail_hip(e, xq ? "q8_0_gemv_q8q8 launch" : "q8_0_gemv launch");
+                int xmode, RcShape sh, const char *what) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return fail_hip(e, "hipGetDevice");
+    OpDesc d = plan_op(x, w, y, 1, n, p, true, kWaves);
+    if (d.rs == 1) {
+        if (sh.c == 0) sh = plan_rc_latency(p, d.gsr, xmode, cu_count(dev));
+        e = launch_gemv_rc(d, sh, rc_tiles_for(p, sh.c), s, xmode);
+    } else {
+        e = launch_gemv_single(d, Variant{kWaves, 1}, tiles_of(d, kWaves), s, xmode);
+    }
+    if (e != hipSuccess) return fail_hip(e, what);
     return Q8_OK;
 }
 
@@ -273,18 +292,11 @@ GemmDesc plan_gemm(const float *X, const void *w, float *Y, int64_t m, int64_t n
     return d;
 }
 
-int env_int(const char *name, int dflt) {
-    const char *ev = std::getenv(name);
-    return ev ? std::atoi(ev) : dflt;
-}
-
 // Stream-K split: up to `wpc` one-wave workgroups per CU, each an equal
 // contiguous range of at least `min_items` (row tile, group) items, so that
 // short ranges do not multiply the partial sums.  Sets fast_wgs and maxc
 // and returns the bytes of partial slots the split needs.
 size_t plan_streamk(GemmDesc &d, int dev, int wpc, int min_items) {
-    wpc = std::max(1, env_int("Q8GEMV_SMALLM_WPC", wpc));
-    min_items = std::max(1, env_int("Q8GEMV_SMALLM_MINIT", min_items));
     const int64_t items = (int64_t)d.row_tiles * d.gsr;
     const int64_t slots = (int64_t)wpc * cu_count(dev);
     const int64_t wgs = std::max<int64_t>(1, std::min({items, slots, items / min_items}));
@@ -317,7 +329,7 @@ int smallm_valu(const float *X, const void *w, float *Y, int64_t m, int64_t n, i
 // m = 2..3 rows where every row is one super-row: the vector units, lanes
 // over (row, block pair); one launch, no split of X.
 int smallm_vrow(const float *X, const void *w, float *Y, int64_t m, int64_t n, int64_t p,
-                hipStream_t s) {
+                hipStream_t s, int nw) {
     GemmDesc d = plan_gemm(X, w, Y, m, n, p);
     int dev = 0;
     hipError_t e = hipGetDevice(&dev);
@@ -328,12 +340,10 @@ int smallm_vrow(const float *X, const void *w, float *Y, int64_t m, int64_t n, i
     int rc = workspace_for(dev, s, std::max<size_t>(part_bytes, 256), (size_t)d.row_tiles, &ws, &d.cnt);
     if (rc) return rc;
     d.ws = ws;
-    // Two waves per workgroup share its stages, each taking half the rows of
-    // every group: two waves per SIMD where one wave's stages fill a quarter
-    // of the LDS (measured 5-10 % faster than one wave; four waves, held to
-    // two per SIMD by their registers, slower).  Q8GEMV_SMALLM_VROW_NW=1
-    // selects one wave for A/B runs.
-    const int nw = env_int("Q8GEMV_SMALLM_VROW_NW", 2) == 1 ? 1 : 2;
+    // nw = 2 (the default): two waves per workgroup share its stages, each
+    // taking half the rows of every group -- two waves per SIMD where one
+    // wave's stages fill a quarter of the LDS (measured 5-10 % faster than
+    // one wave; four waves, held to two per SIMD by their registers, slower)
     e = launch_gemm_vrow(d, nw, s);
     if (e != hipSuccess) return fail_hip(e, "q8_0_gemm_smallm launch");
     return Q8_OK;
@@ -389,14 +399,27 @@ int q8_0_gemv(const float *x, const void *w, float *y, int64_t n, int64_t p, voi
     int rc = validate(x, w, y, 1, n, p, "q8_0_gemv");
     if (rc) return rc;
     if ((rc = check_device())) return rc;
-    return gemv_launch(x, w, y, n, p, (hipStream_t)stream);
+    return gemv_launch(x, w, y, n, p, (hipStream_t)stream, kXFloat, RcShape{0, 0}, "q8_0_gemv launch");
+}
+
+int q8_0_gemv_shaped(const float *x, const void *w, float *y, int64_t n, int64_t p, int lanes_per_row,
+                     int waves, void *stream) {
+    int rc = validate(x, w, y, 1, n, p, "q8_0_gemv_shaped");
+    if (rc) return rc;
+    if (!shape_ok(lanes_per_row, waves))
+        return fail(Q8_ERR_INVALID_ARG, "q8_0_gemv_shaped: lanes_per_row and waves must each be 1, 2 or 4");
+    if (n % (kQuants * kGroupBlocks))
+        return fail(Q8_ERR_SHAPE, "q8_0_gemv_shaped: n must be a multiple of 256 for an explicit launch shape");
+    if ((rc = check_device())) return rc;
+    return gemv_launch(x, w, y, n, p, (hipStream_t)stream, kXFloat, RcShape{lanes_per_row, waves},
+                       "q8_0_gemv_shaped launch");
 }
 
 int q8_0_gemv_q8q8(const float *x, const void *w, float *y, int64_t n, int64_t p, void *stream) {
     int rc = validate(x, w, y, 1, n, p, "q8_0_gemv_q8q8");
     if (rc) return rc;
     if ((rc = check_device())) return rc;
-    return gemv_launch(x, w, y, n, p, (hipStream_t)stream, true);
+    return gemv_launch(x, w, y, n, p, (hipStream_t)stream, kXQuant, RcShape{0, 0}, "q8_0_gemv_q8q8 launch");
 }
 
 int q8_0_quantize(const float *x, void *xq, int64_t n, void *stream) {
@@ -412,14 +435,23 @@ int q8_0_quantize(const float *x, void *xq, int64_t n, void *stream) {
     return e == hipSuccess ? Q8_OK : fail_hip(e, "q8_0_quantize launch");
 }
 
-int q8_0_gemm_smallm(const float *X, const void *w, float *Y, int64_t m, int64_t n, int64_t p,
-                     void *stream) {
+int q8_0_gemm_smallm_kernel(const float *X, const void *w, float *Y, int64_t m, int64_t n, int64_t p,
+                            int kernel, void *stream) {
     int rc = validate(X, w, Y, m, n, p, "q8_0_gemm_smallm");
     if (rc) return rc;
+    if (kernel < Q8_SMALLM_AUTO || kernel > Q8_SMALLM_VROW1)
+        return fail(Q8_ERR_INVALID_ARG, "q8_0_gemm_smallm_kernel: unknown kernel");
+    const int64_t rs = kGroupBlocks / gcd64(n / kQuants, kGroupBlocks);
+    const bool mfma_ok = rs <= 2, vrow_ok = rs == 1 && m >= 2 && m <= kVrowMaxM;
+    if ((kernel == Q8_SMALLM_MFMA && !(mfma_ok && m >= 2)) ||
+        ((kernel == Q8_SMALLM_VROW || kernel == Q8_SMALLM_VROW1) && !vrow_ok) ||
+        (kernel == Q8_SMALLM_VALU && m < 2))
+        return fail(Q8_ERR_SHAPE, "q8_0_gemm_smallm_kernel: this kernel does not take m=" + std::to_string(m) +
+                                      ", n=" + std::to_string(n));
     if ((rc = check_device())) return rc;
     hipStream_t s = (hipStream_t)stream;
-    if (m == 1) return gemv_launch(X, w, Y, n, p, s);
-    const int64_t rs = kGroupBlocks / gcd64(n / kQuants, kGroupBlocks);
+    if (m == 1)
+        return gemv_launch(X, w, Y, n, p, s, kXFloat, RcShape{0, 0}, "q8_0_gemm_smallm launch");
     // m = 2..3 with rows of one super-row (n a multiple of 256) run on the
     // vector units with lanes over (row, block pair): each lane holds the x
     // values of its two blocks in registers, the quants are converted once
@@ -430,24 +462,24 @@ int q8_0_gemm_smallm(const float *X, const void *w, float *Y, int64_t m, int64_t
     // with a lane per row, the x values every lane needs come through LDS
     // broadcast reads, m of them per quant and lane.  Other widths run on the
     // vector units with a lane per row, kValuMaxM rows of X per pass over W.
-    // Q8GEMV_SMALLM_PATH=valu|mfma|vrow overrides.
-    bool mfma = rs <= 2;
-    bool vrow = rs == 1 && m <= kVrowMaxM;
-    if (const char *ev = std::getenv("Q8GEMV_SMALLM_PATH")) {
-        if (!std::strcmp(ev, "valu")) mfma = vrow = false;
-        else if (!std::strcmp(ev, "mfma") && rs <= 2) mfma = true, vrow = false;
-        else if (!std::strcmp(ev, "vrow")) vrow = rs == 1 && m <= kVrowMaxM;
-    }
-    if (vrow) return smallm_vrow(X, w, Y, m, n, p, s);
-    if (mfma) return smallm_mfma(X, w, Y, m, n, p, s);
+    if (kernel == Q8_SMALLM_AUTO) kernel = vrow_ok ? Q8_SMALLM_VROW : mfma_ok ? Q8_SMALLM_MFMA : Q8_SMALLM_VALU;
+    if (kernel == Q8_SMALLM_VROW) return smallm_vrow(X, w, Y, m, n, p, s, 2);
+    if (kernel == Q8_SMALLM_VROW1) return smallm_vrow(X, w, Y, m, n, p, s, 1);
+    if (kernel == Q8_SMALLM_MFMA) return smallm_mfma(X, w, Y, m, n, p, s);
     // vector units: one pass over W per kValuMaxM rows of X
     for (int64_t i0 = 0; i0 < m; i0 += kValuMaxM) {
         const int64_t mi = std::min<int64_t>(kValuMaxM, m - i0);
-        rc = mi == 1 ? gemv_launch(X + i0 * n, w, Y + i0 * p, n, p, s)
+        rc = mi == 1 ? gemv_launch(X + i0 * n, w, Y + i0 * p, n, p, s, kXFloat, RcShape{0, 0},
+                                   "q8_0_gemm_smallm launch")
                      : smallm_valu(X + i0 * n, w, Y + i0 * p, mi, n, p, s);
         if (rc) return rc;
     }
     return Q8_OK;
+}
+
+int q8_0_gemm_smallm(const float *X, const void *w, float *Y, int64_t m, int64_t n, int64_t p,
+                     void *stream) {
+    return q8_0_gemm_smallm_kernel(X, w, Y, m, n, p, Q8_SMALLM_AUTO, stream);
 }
 
 int q8_0_stream_wait(void *stream, int64_t timeout_ms) {
@@ -475,26 +507,16 @@ struct q8_0_chain {
     std::vector<q8_0_op> ops;
     // one entry per kernel launch of a token
     struct Launch {
-        bool fused;
-        bool sk;              // stream-K launch (d_ops, d_pieces, d_begin; d_tiles = tail tiles)
-        bool phased;          // one launch of n_phases phases (d_phases, d_bar, d_err)
+        enum Kind { kSingleRc, kSingleSuperrow, kFusedRc, kFusedMixed } kind;
         int xmode;            // XMode: how the activations are read
-        Variant v;
-        OpDesc single;        // per-op launch
-        const OpDesc *d_ops;  // fused launch
+        RcShape shape;        // kSingleRc, kFusedRc
+        OpDesc single;        // single-op launches
+        const OpDesc *d_ops;  // fused launches: op table and tiles
         const Tile *d_tiles;
-        const Piece *d_pieces;
-        const uint32_t *d_begin;
-        int64_t n_sk;         // stream-K workgroups (the tail tiles' follow)
-        const PhaseDesc *d_phases;
-        int n_phases;
-        uint32_t *d_sync;     // barrier state (kPhasedSyncBytes)
-        uint32_t per, nx;     // workgroups per XCD, XCDs
         int64_t grid;
     };
     std::vector<Launch> launches;
     void *d_table = nullptr;
-    uint32_t *d_err = nullptr;   // one-launch chains: the barrier timeout flag
     hipStream_t capture = nullptr;
     hipGraph_t graph = nullptr;
     hipGraphExec_t exec = nullptr;
@@ -503,12 +525,14 @@ struct q8_0_chain {
 namespace {
 
 hipError_t issue(const q8_0_chain::Launch &L, hipStream_t s) {
-    if (L.phased) return launch_gemv_phased(L.d_phases, L.n_phases, L.d_sync, L.per, L.nx, L.grid, L.v.pf, s);
-    if (L.sk)
-        return launch_gemv_streamk(L.d_ops, L.d_pieces, L.d_begin, L.d_tiles, L.n_sk, L.grid - L.n_sk,
-                                   L.v.pf, s, L.xmode);
-    if (L.fused) return launch_gemv_fused(L.d_ops, L.d_tiles, L.v, L.grid, s, L.xmode);
-    return launch_gemv_single(L.single, L.v, L.grid, s, L.xmode);
+    switch (L.kind) {
+        case q8_0_chain::Launch::kSingleRc: return launch_gemv_rc(L.single, L.shape, L.grid, s, L.xmode);
+        case q8_0_chain::Launch::kSingleSuperrow:
+            return launch_gemv_single(L.single, Variant{kWaves, 1}, L.grid, s, L.xmode);
+        case q8_0_chain::Launch::kFusedRc: return launch_gemv_rc_fused(L.d_ops, L.d_tiles, L.shape, L.grid, s, L.xmode);
+        case q8_0_chain::Launch::kFusedMixed: return launch_gemv_fused(L.d_ops, L.d_tiles, Variant{1, 1}, L.grid, s, L.xmode);
+    }
+    return hipErrorInvalidValue;
 }
 
 void chain_free(q8_0_chain *c) {
@@ -563,125 +587,6 @@ bool depends(const q8_0_op &a, const q8_0_op &b, const OpExtra *ea = nullptr,
     return false;
 }
 
-// How the one-launch kernel's `wgs` workgroups spread over the XCDs of
-// device `dev`: a census launch of the same kernel and grid, once per
-// (device, wgs).  Sets *per and *nx and returns true when every XCD holds
-// the same number (the two-level barrier counts on it).
-bool phased_split(int dev, int64_t wgs, uint32_t *per, uint32_t *nx) {
-    static std::mutex mu;
-    static std::map<std::pair<int, int64_t>, std::pair<uint32_t, uint32_t>> known;
-    std::lock_guard<std::mutex> lock(mu);
-    const auto key = std::make_pair(dev, wgs);
-    auto it = known.find(key);
-    if (it == known.end()) {
-        uint32_t p = 0, n = 0;
-        uint32_t *d = nullptr;
-        if (hipMalloc(&d, (size_t)wgs * sizeof(uint32_t)) == hipSuccess) {
-            std::vector<uint32_t> h((size_t)wgs, 0xFFFFFFFFu);
-            if (launch_gemv_phased_census(d, wgs, nullptr) == hipSuccess &&
-                hipMemcpy(h.data(), d, h.size() * sizeof(uint32_t), hipMemcpyDeviceToHost) == hipSuccess) {
-                std::map<uint32_t, int64_t> count;
-                for (uint32_t x : h) count[x]++;
-                bool even = !count.empty() && count.size() <= 16 && count.rbegin()->first < 16;
-                for (auto &kv : count) even = even && kv.second * (int64_t)count.size() == wgs;
-                if (even) { n = (uint32_t)count.size(); p = (uint32_t)(wgs / n); }
-            }
-            (void)hipFree(d);
-        }
-        it = known.emplace(key, std::make_pair(p, n)).first;
-    }
-    *per = it->second.first;
-    *nx = it->second.second;
-    return *nx > 0;
-}
-
-// Stream-K schedule of a launch's ops on `wgs` one-wave workgroups: all
-// (op, row tile, group) items, in that order, are cut into wgs equal
-// contiguous ranges (workgroup b takes [b*N/wgs, (b+1)*N/wgs)), and each
-// range into pieces where it crosses a row tile.  The pieces of one row tile
-// are numbered in workgroup order (their partial slots); maxc[i] is op i's
-// largest number of pieces on one row tile.  begin holds wgs + 1 offsets.
-void plan_pieces(const std::vector<OpDesc> &ds, int64_t wgs, std::vector<Piece> &pieces,
-                 std::vector<uint32_t> &begin, std::vector<int32_t> &maxc) {
-    const size_t n_ops = ds.size();
-    std::vector<int64_t> off(n_ops + 1, 0);
-    std::vector<std::vector<uint32_t>> count(n_ops);
-    for (size_t i = 0; i < n_ops; ++i) {
-        const int64_t tiles = ((int64_t)ds[i].nsr + kWave - 1) / kWave;
-        off[i + 1] = off[i] + tiles * ds[i].gsr;
-        count[i].assign((size_t)tiles, 0u);
-    }
-    const int64_t N = off[n_ops];
-    pieces.clear();
-    begin.assign((size_t)wgs + 1, 0u);
-    size_t i = 0;
-    for (int64_t b = 0; b < wgs; ++b) {
-        begin[(size_t)b] = (uint32_t)pieces.size();
-        int64_t lo = b * N / wgs;
-        const int64_t hi = (b + 1) * N / wgs;
-        while (lo < hi) {
-            while (off[i + 1] <= lo) ++i;
-            const int64_t G = ds[i].gsr;
-            const int64_t local = lo - off[i];
-            const int64_t tile = local / G;
-            const int64_t g0 = local - tile * G;
-            const int64_t g1 = std::min<int64_t>(G, g0 + (hi - lo));
-            Piece pc;
-            pc.op = (uint32_t)i;
-            pc.tile = (uint32_t)tile;
-            pc.g0 = (uint32_t)g0;
-            pc.g1 = (uint32_t)g1;
-            pc.slot = count[i][(size_t)tile]++;
-            pc.nslots = 0;
-            pieces.push_back(pc);
-            lo += g1 - g0;
-        }
-    }
-    begin[(size_t)wgs] = (uint32_t)pieces.size();
-    maxc.assign(n_ops, 1);
-    for (auto &pc : pieces) {
-        pc.nslots = count[pc.op][pc.tile];
-        maxc[pc.op] = std::max<int32_t>(maxc[pc.op], (int32_t)pc.nslots);
-    }
-}
-
-// Does phase k (segment k) of a one-launch chain read memory that an earlier
-// phase j read and a phase in [j, k) wrote?  Then a CU may still hold
-// phase j's copy in its L1.  Ranges are widened to whole 128-byte lines.
-bool phase_rereads(const q8_0_op *ops, const OpExtra *extra,
-                   const std::vector<std::pair<int64_t, int64_t>> &segs, size_t k) {
-    auto line = [](const void *p, int64_t n, uintptr_t &a, uintptr_t &b) {
-        a = (uintptr_t)p & ~(uintptr_t)127;
-        b = ((uintptr_t)p + (uintptr_t)n + 127) & ~(uintptr_t)127;
-    };
-    auto meet = [&](const void *p, int64_t n, const void *q, int64_t m) {
-        uintptr_t a0, a1, b0, b1;
-        line(p, n, a0, a1);
-        line(q, m, b0, b1);
-        return a0 < b1 && b0 < a1;
-    };
-    auto ex = [&](int64_t i) { return extra ? &extra[i] : nullptr; };
-    if (segs.back().second > 512) return k > 0;   // long chains: every barrier acquires
-    for (int64_t i = segs[k].first; i < segs[k].second; ++i) {
-        const Ranges R = ranges_of(ops[i], ex(i));
-        for (int r = 0; r < R.nr; ++r)
-            for (size_t j = 0; j < k; ++j)
-                for (int64_t a = segs[j].first; a < segs[j].second; ++a) {
-                    const Ranges A = ranges_of(ops[a], ex(a));
-                    for (int ra = 0; ra < A.nr; ++ra) {
-                        if (!meet(R.r[r], R.rn[r], A.r[ra], A.rn[ra])) continue;
-                        for (size_t w = j; w < k; ++w)
-                            for (int64_t b = segs[w].first; b < segs[w].second; ++b) {
-                                const Ranges B = ranges_of(ops[b], ex(b));
-                                for (int wb = 0; wb < B.nw; ++wb)
-                                    if (meet(R.r[r], R.rn[r], B.w[wb], B.wn[wb])) return true;
-                            }
-                    }
-                }
-    }
-    return false;
-}
-
 void set_extra(OpDesc &d, const OpExtra *e) {
     if (!e) return;
     d.x_up = e->x_up;
@@ -701,6 +606,23 @@ int q8::chain_issue(const q8_0_chain *c, hipStream_t s) {
     return Q8_OK;
 }
 
+std::vector<std::pair<int64_t, int64_t>> q8::chain_segments(const q8_0_op *ops, int64_t n_ops, bool per_op,
+                                                            const OpExtra *extra) {
+    std::vector<std::pair<int64_t, int64_t>> segs;
+    if (per_op) {
+        for (int64_t i = 0; i < n_ops; ++i) segs.push_back({i, i + 1});
+        return segs;
+    }
+    int64_t b = 0;
+    for (int64_t i = 1; i <= n_ops; ++i) {
+        bool cut = (i == n_ops);
+        for (int64_t j = b; !cut && j < i; ++j)
+            cut = depends(ops[j], ops[i], extra ? &extra[j] : nullptr, extra ? &extra[i] : nullptr);
+        if (cut) { segs.push_back({b, i}); b = i; }
+    }
+    return segs;
+}
+
 extern "C" {
 
 int q8_0_chain_create(const q8_0_op *ops, int64_t n_ops, uint32_t flags, q8_0_chain **out) {
@@ -715,11 +637,8 @@ int q8::chain_create_ex(const q8_0_op *ops, int64_t n_ops, uint32_t flags, const
     *out = nullptr;
     if (!ops || n_ops <= 0 || n_ops > Q8_MAX_CHAIN_OPS)
         return fail(Q8_ERR_INVALID_ARG, "q8_0_chain_create: need 1..65535 ops");
-    if (flags & ~(uint32_t)(Q8_CHAIN_PER_OP | Q8_CHAIN_SPLIT_K | Q8_CHAIN_XQ | Q8_CHAIN_ONE_LAUNCH))
+    if (flags & ~(uint32_t)(Q8_CHAIN_PER_OP | Q8_CHAIN_SPLIT_K | Q8_CHAIN_XQ))
         return fail(Q8_ERR_INVALID_ARG, "q8_0_chain_create: unknown flags");
-    const bool one = (flags & Q8_CHAIN_ONE_LAUNCH) != 0;
-    if (one && (flags & (Q8_CHAIN_XQ | Q8_CHAIN_PER_OP)))
-        return fail(Q8_ERR_INVALID_ARG, "q8_0_chain_create: Q8_CHAIN_ONE_LAUNCH takes neither XQ nor PER_OP");
     const int emode = extra ? extra[0].mode : kXFloat;
     if (extra && (flags & Q8_CHAIN_XQ))
         return fail(Q8_ERR_INVALID_ARG, "q8_0_chain_create: these inputs have no integer form");
@@ -731,10 +650,8 @@ int q8::chain_create_ex(const q8_0_op *ops, int64_t n_ops, uint32_t flags, const
         if (!extra) continue;
         const OpExtra &e = extra[i];
         const int64_t xb = 4 * ops[i].n, yb = 4 * ops[i].p;
-        // one-launch chains take a mode per phase (kXFloat: none)
-        bool ok = one || e.mode == emode;
-        if (e.mode == kXFloat) ok = one;
-        else if (e.mode == kXSiluUp) ok = ok && a16(e.x_up) && !overlaps(ops[i].y, yb, e.x_up, xb);
+        bool ok = e.mode == emode;
+        if (e.mode == kXSiluUp) ok = ok && a16(e.x_up) && !overlaps(ops[i].y, yb, e.x_up, xb);
         else if (e.mode == kXNormAdd)   // (the writer of x_out needs a fast tile: p >= 8)
             ok = ok && a16(e.x_res) && a16(e.norm_w) && (!e.x_out || (a16(e.x_out) && ops[i].p >= 8)) &&
                  !overlaps(ops[i].y, yb, e.x_res, xb) &&
@@ -751,227 +668,116 @@ int q8::chain_create_ex(const q8_0_op *ops, int64_t n_ops, uint32_t flags, const
     c->device = dev;
     c->flags = flags;
     c->ops.assign(ops, ops + n_ops);
-
-    // ---- plan: runs of mutually independent ops (or single ops)
+    const int xmode = (flags & Q8_CHAIN_XQ) ? kXQuant : emode;
     const bool per_op = (flags & Q8_CHAIN_PER_OP) != 0;
-    const bool split = (flags & Q8_CHAIN_SPLIT_K) != 0;
-    std::vector<std::pair<int64_t, int64_t>> segs;  // [begin, end)
-    if (per_op) {
-        for (int64_t i = 0; i < n_ops; ++i) segs.push_back({i, i + 1});
-    } else {
-        int64_t b = 0;
-        for (int64_t i = 1; i <= n_ops; ++i) {
-            bool cut = (i == n_ops);
-            // (a one-launch chain's phase reads its activations in one mode)
-            if (one && extra && extra[i].mode != extra[b].mode) cut = true;
-            for (int64_t j = b; !cut && j < i; ++j)
-                cut = depends(ops[j], ops[i], extra ? &extra[j] : nullptr, extra ? &extra[i] : nullptr);
-            if (cut) { segs.push_back({b, i}); b = i; }
-        }
-    }
-
-    // ---- fused segments: op table + tile schedule in one device block;
-    // with SPLIT_K every op is planned like a standalone launch (four-wave
-    // workgroups, groups split over the waves) and row-poor ops are split
-    // across workgroups too, their partial sums in the same device block
-    // SPLIT_K (ops that wait on each other).  Measured on the decode step's
-    // shapes: while a launch's row tiles (64 super-rows) fit on the CUs, four-
-    // wave workgroups splitting a tile's groups in LDS, with K further sliced
-    // across workgroups until there is one workgroup per CU, are fastest (a
-    // workgroup's stages fill a CU's LDS); launches with more row tiles than
-    // CUs (an lm_head, a 7B gate|up) are fastest on unsplit one-wave tiles.
-    const Variant v_single = pick_variant(false), v_fused = pick_variant(true);
+    const bool latency = (flags & Q8_CHAIN_SPLIT_K) != 0;
     const int64_t cus = cu_count(dev);
-    // Stream-K for split launches with more row tiles than CUs whose one-wave
-    // tiles would leave a long tail (below):
-    // Q8GEMV_STREAMK=0 turns it off, 2 uses it for every split launch (A/B
-    // runs); Q8GEMV_SK_PF sets its groups in flight (1 or 2).
-    const int sk_mode = env_int("Q8GEMV_STREAMK", 1);
-    // Q8GEMV_SK_TAIL overrides the tail threshold below (0: every row-rich launch)
-    const double sk_tail_groups = env_int("Q8GEMV_SK_TAIL", 4);
-    const int sk_pf = env_int("Q8GEMV_SK_PF", 1) == 2 ? 2 : 1;
-    // a one-launch chain: every phase stream-K on the same workgroups, as
-    // many as the CUs hold at once (four one-wave workgroups fill a CU's LDS)
-    // (where the census finds the workgroups unevenly spread over the XCDs,
-    // the phases become launches of their own, planned like SPLIT_K)
-    int64_t one_wgs = 0;
-    uint32_t xcc_per = 0, xcc_n = 0;
-    bool phased = false;
-    if (one) {
-        const int per_cu = std::min(4, gemv_phased_blocks_per_cu(1));
-        if (per_cu < 1) { chain_free(c); return fail(Q8_ERR_HIP, "q8_0_chain_create: occupancy query failed"); }
-        one_wgs = per_cu * cus;
-        phased = phased_split(dev, one_wgs, &xcc_per, &xcc_n);
-    }
+
+    // ---- plan: runs of mutually independent ops (or single ops).  Every
+    // plan computes each op's outputs in the same fixed order, so the chain
+    // gives the bits of standalone calls whatever the launch shapes.
+    const auto segs = chain_segments(ops, n_ops, per_op, extra);
     std::vector<OpDesc> h_ops;
     std::vector<Tile> h_tiles;
-    std::vector<Piece> h_pieces;
-    std::vector<uint32_t> h_begin;
     struct SegInfo {
+        q8_0_chain::Launch L;
         size_t op0, tile0;
-        int64_t ntiles;
-        bool fused;
-        OpDesc single;
-        Variant v;
-        bool sk;
-        size_t piece0, begin0;
-        int64_t n_sk;
-        int xmode;   // one-launch phases
     };
     std::vector<SegInfo> info;
     for (auto &sg : segs) {
-        const bool fused = !per_op && (sg.second - sg.first > 1);
-        int64_t target = 1;
-        Variant v = fused ? v_fused : v_single;
-        bool sk = false;
-        if (phased) {
-            sk = true;
-            v = Variant{1, 1};
-        } else if (split || one) {
-            int64_t row_tiles = 0, tile_groups = 0;
-            for (int64_t i = sg.first; i < sg.second; ++i) {
-                const OpDesc d = plan_op(ops[i].x, ops[i].w, ops[i].y, 1, ops[i].n, ops[i].p, false, 1);
-                row_tiles += d.fast_tiles;
-                tile_groups = std::max<int64_t>(tile_groups, d.gsr);
-            }
-            if (row_tiles > cus) {
-                v = Variant{1, 1};
+        SegInfo si;
+        std::memset(&si, 0, sizeof si);
+        si.L.xmode = xmode;
+        si.op0 = h_ops.size();
+        si.tile0 = h_tiles.size();
+        const auto ex = [&](int64_t i) { return extra ? &extra[i] : nullptr; };
+        if (sg.second - sg.first == 1) {
+            // one op: planned as a standalone call (a latency launch)
+            const q8_0_op &o = ops[sg.first];
+            OpDesc d = plan_op(o.x, o.w, o.y, 1, o.n, o.p, true, kWaves);
+            set_extra(d, ex(sg.first));
+            si.L.single = d;
+            if (d.rs == 1) {
+                si.L.kind = q8_0_chain::Launch::kSingleRc;
+                si.L.shape = plan_rc_latency(d.p, d.gsr, xmode, cus);
+                si.L.grid = rc_tiles_for(d.p, si.L.shape.c);
             } else {
-                v = Variant{kWaves, 1};
-                target = std::max<int64_t>(1, cus / std::max<int64_t>(1, row_tiles));
+                si.L.kind = q8_0_chain::Launch::kSingleSuperrow;
+                si.L.grid = tiles_of(d, kWaves);
             }
-            // Row-rich launches: one-wave tiles, four per CU, run in waves of
-            // 4 * cus tiles; the last wave's idle slots cost (ceil(w) - w)
-            // tile times, w = row_tiles / (4 * cus).  Stream-K spreads the
-            // (tile, group) items evenly but pays partial sums where tiles
-            // are shared.  It is taken where the one-wave tail would idle
-            // the slots for at least sk_tail_groups group times (measured:
-            // the 7B gate|up, 592 tiles of 14 groups, 5.9 group times, and
-            // lm_head, 2376 of 14, 9.5, are faster on stream-K; the 0.6B
-            // lm_head, 2374 tiles of 4 groups, 2.7, is 5 us faster on tiles).
-            const double waves = (double)row_tiles / (double)(4 * cus);
-            const double tail_groups = (std::ceil(waves) - waves) * (double)tile_groups;
-            sk = sk_mode == 2 || (sk_mode == 1 && row_tiles > cus && tail_groups >= sk_tail_groups);
-            // A/B overrides: Q8GEMV_SPLIT_SLICES (slices per row tile), Q8GEMV_VARIANT
-            if (const int forced = env_int("Q8GEMV_SPLIT_SLICES", 0); forced > 0) target = forced;
-            if (std::getenv("Q8GEMV_VARIANT")) v = v_single;
-            if (sk) v = Variant{1, sk_pf};
+            info.push_back(si);
+            continue;
         }
-        // four-wave split workgroups take the standalone K split inside the workgroup
-        const bool standalone = (!(split || one) && !fused) || ((split || one) && v.nw > 1);
-        SegInfo si{h_ops.size(), h_tiles.size(), 0, fused, OpDesc{}, v, sk, h_pieces.size(), h_begin.size(), 0,
-                   extra ? extra[sg.first].mode : kXFloat};
-        if (sk) {
-            // one-wave workgroups, four per CU (their two stages fill its LDS),
-            // each at least kSkMinItems (row tile, group) items
-            constexpr int64_t kSkMinItems = 2;
-            std::vector<OpDesc> ds;
-            int64_t items = 0;
-            for (int64_t i = sg.first; i < sg.second; ++i) {
-                const q8_0_op &o = ops[i];
-                OpDesc d = plan_op(o.x, o.w, o.y, 1, o.n, o.p, false, 1);
-                set_extra(d, extra ? &extra[i] : nullptr);
-                items += (int64_t)d.fast_tiles * d.gsr;
-                ds.push_back(d);
-            }
-            const int64_t wgs = std::min<int64_t>(phased ? one_wgs : 4 * cus, std::max<int64_t>(1, items / kSkMinItems));
-            std::vector<Piece> pcs;
-            std::vector<uint32_t> bg;
-            std::vector<int32_t> maxc;
-            plan_pieces(ds, items > 0 ? wgs : 0, pcs, bg, maxc);
-            for (size_t i = 0; i < ds.size(); ++i) {
-                if (maxc[i] > 1) ds[i].sk_slots = maxc[i];
-                h_ops.push_back(ds[i]);
-                const int64_t tt = tail_tiles_for((int64_t)ds[i].p - ds[i].tail_row0, 1);
-                for (int64_t t = 0; t < tt; ++t) h_tiles.push_back({(uint32_t)i, (uint32_t)t | kTailBit});
-            }
-            h_pieces.insert(h_pieces.end(), pcs.begin(), pcs.end());
-            h_begin.insert(h_begin.end(), bg.begin(), bg.end());
-            si.n_sk = items > 0 ? wgs : 0;
-            si.ntiles = (int64_t)(h_tiles.size() - si.tile0);
-        } else if (fused) {
-            // tiles sorted by decreasing weight bytes so that the smallest
-            // tiles finish the launch (ties keep encode order)
+        // several independent ops in one launch
+        bool all_rc = true, one_width = true;
+        int64_t rows = 0;
+        for (int64_t i = sg.first; i < sg.second; ++i) {
+            all_rc = all_rc && ops[i].n % (kQuants * kGroupBlocks) == 0;
+            one_width = one_width && ops[i].n == ops[sg.first].n;
+            rows += ops[i].p;
+        }
+        if (all_rc) {
+            // SPLIT_K (ops that wait on the launch before): the latency plan
+            // over all the launch's rows when they share a width; otherwise
+            // the steady-state one-wave tiles, largest tiles first so that
+            // the smallest finish the launch
+            const RcShape sh = latency && one_width
+                                   ? plan_rc_latency(rows, ops[sg.first].n / (kQuants * kGroupBlocks), xmode, cus)
+                                   : kFuseShape;
             struct Item { Tile t; int64_t bytes; };
             std::vector<Item> items;
             for (int64_t i = sg.first; i < sg.second; ++i) {
                 const q8_0_op &o = ops[i];
-                OpDesc d = plan_op(o.x, o.w, o.y, 1, o.n, o.p, standalone, v.nw, target);
-                set_extra(d, extra ? &extra[i] : nullptr);
+                OpDesc d = plan_op(o.x, o.w, o.y, 1, o.n, o.p, false, 1);
+                set_extra(d, ex(i));
                 const uint32_t oi = (uint32_t)(h_ops.size() - si.op0);
                 h_ops.push_back(d);
-                const int64_t fb = (int64_t)(v.nw / d.ks) * kWave *
-                                   (d.slices > 1 ? (int64_t)d.slice_groups * kGroupBytes : d.sr_bytes);
+                const int64_t tb = (int64_t)(kWave / sh.c) * d.sr_bytes;
+                const int64_t nt = rc_tiles_for(d.p, sh.c);
+                for (int64_t t = 0; t < nt; ++t) items.push_back({{oi, (uint32_t)t}, tb});
+            }
+            if (!(latency && one_width))
+                std::stable_sort(items.begin(), items.end(),
+                                 [](const Item &a, const Item &b) { return a.bytes > b.bytes; });
+            for (auto &it : items) h_tiles.push_back(it.t);
+            si.L.kind = q8_0_chain::Launch::kFusedRc;
+            si.L.shape = sh;
+            si.L.grid = (int64_t)items.size();
+        } else {
+            // widths that are not all multiples of 256: one-wave workgroups,
+            // each tile in its own layout, largest tiles first
+            struct Item { Tile t; int64_t bytes; };
+            std::vector<Item> items;
+            for (int64_t i = sg.first; i < sg.second; ++i) {
+                const q8_0_op &o = ops[i];
+                OpDesc d = plan_op(o.x, o.w, o.y, 1, o.n, o.p, false, 1);
+                set_extra(d, ex(i));
+                const uint32_t oi = (uint32_t)(h_ops.size() - si.op0);
+                h_ops.push_back(d);
+                const int64_t fb = (int64_t)kWave * d.sr_bytes;
                 for (int64_t t = 0; t < d.fast_tiles; ++t) items.push_back({{oi, (uint32_t)t}, fb});
-                const int64_t tt = tail_tiles_for((int64_t)d.p - d.tail_row0, v.nw);
+                const int64_t tt = tail_tiles_for((int64_t)d.p - d.tail_row0, 1);
                 for (int64_t t = 0; t < tt; ++t)
-                    items.push_back({{oi, (uint32_t)t | kTailBit}, (int64_t)v.nw * d.nb * kBlockBytes});
+                    items.push_back({{oi, (uint32_t)t | kTailBit}, (int64_t)d.nb * kBlockBytes});
             }
             std::stable_sort(items.begin(), items.end(),
                              [](const Item &a, const Item &b) { return a.bytes > b.bytes; });
             for (auto &it : items) h_tiles.push_back(it.t);
-            si.ntiles = (int64_t)items.size();
-        } else {
-            const q8_0_op &o = ops[sg.first];
-            si.single = plan_op(o.x, o.w, o.y, 1, o.n, o.p, standalone, v.nw, target);
-            set_extra(si.single, extra ? &extra[sg.first] : nullptr);
+            si.L.kind = q8_0_chain::Launch::kFusedMixed;
+            si.L.grid = (int64_t)items.size();
         }
         info.push_back(si);
     }
-    // device block: op descriptors, tiles, pieces, piece offsets, then the
-    // K-split partials and counters
-    auto up256 = [](size_t x) { return (x + 255) / 256 * 256; };
+    // device block: op descriptors, then tiles
     const size_t ob = h_ops.size() * sizeof(OpDesc);
-    const size_t tb = h_tiles.size() * sizeof(Tile);
-    const size_t pb = h_pieces.size() * sizeof(Piece);
-    const size_t bb = h_begin.size() * sizeof(uint32_t);
-    const size_t t_at = ob, p_at = up256(ob + tb), b_at = up256(p_at + pb);
-    // one-launch chains: the phase table, a barrier counter per phase, the
-    // timeout flag
-    const size_t nph = phased ? segs.size() : 0;
-    const size_t ph_at = up256(b_at + bb), sync_at = up256(ph_at + nph * sizeof(PhaseDesc));
-    size_t wb = phased ? up256(sync_at + kPhasedSyncBytes) : up256(b_at + bb);   // running end of the block
-    std::vector<std::pair<OpDesc *, size_t>> ws;  // (op, offset of its partials)
-    auto part_bytes = [](const OpDesc &d) {
-        return (size_t)std::max(d.slices, d.sk_slots) * d.nsr * d.rs * sizeof(float);
-    };
-    auto reserve = [&](OpDesc &d) {
-        if (d.slices <= 1 && d.sk_slots <= 1) return;
-        ws.push_back({&d, wb});
-        const size_t cnt = (size_t)((d.nsr + kWave - 1) / kWave) * sizeof(uint32_t);
-        wb += up256(part_bytes(d)) + up256(cnt);
-    };
-    for (auto &d : h_ops) reserve(d);
-    for (auto &si : info)
-        if (!si.fused && !si.sk) reserve(si.single);
-    const size_t total = wb;
+    const size_t t_at = (ob + 255) / 256 * 256;
+    const size_t total = h_tiles.empty() ? ob : t_at + h_tiles.size() * sizeof(Tile);
     if (total) {
         hipError_t e = hipMalloc(&c->d_table, total);
         if (e != hipSuccess) { chain_free(c); return fail_hip(e, "q8_0_chain_create hipMalloc"); }
-        char *base = (char *)c->d_table;
-        for (auto &pw : ws) {
-            OpDesc &d = *pw.first;
-            d.part = (float *)(base + pw.second);
-            d.cnt = (uint32_t *)(base + pw.second + up256(part_bytes(d)));
-        }
-        std::vector<char> host(total, 0);   // counters start at zero
+        std::vector<char> host(total, 0);
         if (ob) std::memcpy(host.data(), h_ops.data(), ob);
-        if (tb) std::memcpy(host.data() + t_at, h_tiles.data(), tb);
-        if (pb) std::memcpy(host.data() + p_at, h_pieces.data(), pb);
-        if (bb) std::memcpy(host.data() + b_at, h_begin.data(), bb);
-        for (size_t k = 0; k < nph; ++k) {
-            PhaseDesc ph;
-            std::memset(&ph, 0, sizeof ph);
-            ph.ops = (const OpDesc *)base + info[k].op0;
-            ph.pieces = (const Piece *)(base + p_at) + info[k].piece0;
-            ph.begin = (const uint32_t *)(base + b_at) + info[k].begin0;
-            ph.tails = (const Tile *)(base + t_at) + info[k].tile0;
-            ph.n_sk = (int32_t)info[k].n_sk;
-            ph.n_tail = (int32_t)info[k].ntiles;
-            ph.xmode = info[k].xmode;
-            ph.acquire = phase_rereads(ops, extra, segs, k) ? 1 : 0;
-            std::memcpy(host.data() + ph_at + k * sizeof(PhaseDesc), &ph, sizeof ph);
-        }
+        if (!h_tiles.empty()) std::memcpy(host.data() + t_at, h_tiles.data(), h_tiles.size() * sizeof(Tile));
         if ((e = hipMemcpy(c->d_table, host.data(), host.size(), hipMemcpyHostToDevice)) != hipSuccess) {
             chain_free(c);
             return fail_hip(e, "q8_0_chain_create hipMemcpy");
@@ -979,44 +785,11 @@ int q8::chain_create_ex(const q8_0_op *ops, int64_t n_ops, uint32_t flags, const
     }
     const OpDesc *d_ops = (const OpDesc *)c->d_table;
     const Tile *d_tiles = (const Tile *)((const char *)c->d_table + t_at);
-    const Piece *d_pieces = (const Piece *)((const char *)c->d_table + p_at);
-    const uint32_t *d_begin = (const uint32_t *)((const char *)c->d_table + b_at);
-    if (phased) {
-        q8_0_chain::Launch L;
-        std::memset(&L, 0, sizeof L);
-        L.phased = true;
-        L.v = Variant{1, 1};
-        L.d_phases = (const PhaseDesc *)((const char *)c->d_table + ph_at);
-        L.n_phases = (int)nph;
-        L.d_sync = (uint32_t *)((char *)c->d_table + sync_at);
-        L.per = xcc_per;
-        L.nx = xcc_n;
-        L.grid = one_wgs;
-        c->d_err = L.d_sync + kPhasedSyncErr;
-        c->launches.push_back(L);
-    }
-    for (size_t k = 0; k < segs.size() && !phased; ++k) {
-        q8_0_chain::Launch L;
-        std::memset(&L, 0, sizeof L);
-        L.xmode = (flags & Q8_CHAIN_XQ) ? kXQuant : info[k].xmode;
-        L.v = info[k].v;
-        if (info[k].sk) {
-            L.sk = true;
-            L.d_ops = d_ops + info[k].op0;
-            L.d_tiles = d_tiles + info[k].tile0;
-            L.d_pieces = d_pieces + info[k].piece0;
-            L.d_begin = d_begin + info[k].begin0;
-            L.n_sk = info[k].n_sk;
-            L.grid = info[k].n_sk + info[k].ntiles;
-        } else if (info[k].fused) {
-            L.fused = true;
-            L.d_ops = d_ops + info[k].op0;
-            L.d_tiles = d_tiles + info[k].tile0;
-            L.grid = info[k].ntiles;
-        } else {
-            L.fused = false;
-            L.single = info[k].single;
-            L.grid = tiles_of(L.single, L.v.nw);
+    for (auto &si : info) {
+        q8_0_chain::Launch L = si.L;
+        if (L.kind == q8_0_chain::Launch::kFusedRc || L.kind == q8_0_chain::Launch::kFusedMixed) {
+            L.d_ops = d_ops + si.op0;
+            L.d_tiles = d_tiles + si.tile0;
         }
         c->launches.push_back(L);
     }
@@ -1064,16 +837,6 @@ int q8_0_decode_chain(q8_0_chain *c, int mode, void *stream) {
         if (mode == Q8_MODE_SYNC_EACH && (e = hipStreamSynchronize(s)) != hipSuccess)
             return fail_hip(e, "hipStreamSynchronize");
     }
-    return Q8_OK;
-}
-
-int q8_0_chain_check(const q8_0_chain *c) {
-    if (!c) return fail(Q8_ERR_INVALID_ARG, "q8_0_chain_check: null chain");
-    if (!c->d_err) return Q8_OK;
-    uint32_t err = 0;
-    const hipError_t e = hipMemcpy(&err, c->d_err, sizeof err, hipMemcpyDeviceToHost);
-    if (e != hipSuccess) return fail_hip(e, "q8_0_chain_check hipMemcpy");
-    if (err) return fail(Q8_ERR_TIMEOUT, "q8_0_chain_check: a barrier wait of the one-launch chain gave up");
     return Q8_OK;
 }
 

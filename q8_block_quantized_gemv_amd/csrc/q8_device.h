@@ -128,48 +128,23 @@ __device__ __forceinline__ void dma_group_x(const uint8_t *g, const uint32_t (&o
 // The SwiGLU product, as the step's silu_hadamard kernel computes it.
 __device__ __forceinline__ float silu_up(float g, float u) { return (g / (1.0f + expf(-g))) * u; }
 
-// kXNormAdd: 1 / rms of s = x + x_res over the op's n columns, for one wave
-// (lane l takes float4s l, l + 64, ...); with `write`, s also goes to x_out.
-__device__ __forceinline__ float norm_add_inv(const OpDesc &op, int lane, bool write) {
-    constexpr int B = 8;   // float4 pairs in flight per lane
-    const int n = op.nb * kQuants, nv = n / 4;
-    const float4 *a4 = reinterpret_cast<const float4 *>(op.x);
-    const float4 *r4 = reinterpret_cast<const float4 *>(op.x_res);
-    float4 *o4 = reinterpret_cast<float4 *>(op.x_out);
-    float ss = 0.f;
-    for (int i0 = 0; i0 < nv; i0 += kWave * B) {
-        float4 a[B], r[B];
+// kXNormAdd: the squared norm of s = x + x_res over the op's n columns is
+// summed in kNormParts contiguous parts of its float4s; within a part lane l
+// takes float4s lo + l, lo + l + 64, ... in increasing order and the lanes
+// meet in a fixed butterfly; the parts are then added in part order.  Each
+// part's sum is the same bits whichever wave computes it and however many
+// loads it keeps in flight, so inv does not depend on the launch shape.
+constexpr int kNormParts = 4;
+
+__device__ __forceinline__ float wave_sum(float v) {
 #pragma unroll
-        for (int e = 0; e < B; ++e) {
-            const int i = i0 + lane + kWave * e;
-            a[e] = make_float4(0.f, 0.f, 0.f, 0.f);
-            r[e] = a[e];
-            if (i < nv) {
-                a[e] = a4[i];
-                r[e] = r4[i];
-            }
-        }
-#pragma unroll
-        for (int e = 0; e < B; ++e) {
-            const int i = i0 + lane + kWave * e;
-            const float4 v = make_float4(a[e].x + r[e].x, a[e].y + r[e].y, a[e].z + r[e].z, a[e].w + r[e].w);
-            ss = fmaf(v.x, v.x, ss);
-            ss = fmaf(v.y, v.y, ss);
-            ss = fmaf(v.z, v.z, ss);
-            ss = fmaf(v.w, v.w, ss);
-            if (write && i < nv) o4[i] = v;
-        }
-    }
-#pragma unroll
-    for (int o = kWave / 2; o > 0; o >>= 1) ss += __shfl_xor(ss, o, kWave);
-    return 1.0f / sqrtf(ss / (float)n + op.norm_eps);
+    for (int o = kWave / 2; o > 0; o >>= 1) v += __shfl_xor(v, o, kWave);
+    return v;   // the same in every lane: each step adds a pair in both lanes
 }
 
-// kXNormAdd with NW waves sharing the op: wave `part` of `nparts` sums the
-// squares of s = x + x_res over its contiguous share of the float4s (and
-// writes that share of s with `write`); returns the wave's partial sum.
-__device__ __forceinline__ float norm_add_part(const OpDesc &op, int lane, int part, int nparts,
-                                               bool write) {
+// Part `part` of kNormParts (and, with `write`, that part of s stored to
+// x_out); returns the part's sum in every lane.
+__device__ __forceinline__ float norm_add_part(const OpDesc &op, int lane, int part, int nparts, bool write) {
     constexpr int B = 8;   // float4 pairs in flight per lane
     const int n = op.nb * kQuants, nv = n / 4;
     const int lo = (int)((int64_t)nv * part / nparts), hi = (int)((int64_t)nv * (part + 1) / nparts);
@@ -200,9 +175,65 @@ __device__ __forceinline__ float norm_add_part(const OpDesc &op, int lane, int p
             if (write && i < hi) o4[i] = v;
         }
     }
+    return wave_sum(ss);
+}
+
+// All kNormParts parts by one wave, their loads issued together.
+__device__ __forceinline__ void norm_add_parts(const OpDesc &op, int lane, bool write,
+                                               float (&part)[kNormParts]) {
+    constexpr int B = 2;   // float4 pairs in flight per lane and part
+    const int n = op.nb * kQuants, nv = n / 4;
+    const float4 *a4 = reinterpret_cast<const float4 *>(op.x);
+    const float4 *r4 = reinterpret_cast<const float4 *>(op.x_res);
+    float4 *o4 = reinterpret_cast<float4 *>(op.x_out);
+    int lo[kNormParts], hi[kNormParts];
+    float ss[kNormParts];
+    int len = 0;
 #pragma unroll
-    for (int o = kWave / 2; o > 0; o >>= 1) ss += __shfl_xor(ss, o, kWave);
-    return ss;
+    for (int k = 0; k < kNormParts; ++k) {
+        lo[k] = (int)((int64_t)nv * k / kNormParts);
+        hi[k] = (int)((int64_t)nv * (k + 1) / kNormParts);
+        len = max(len, hi[k] - lo[k]);
+        ss[k] = 0.f;
+    }
+    for (int e0 = 0; e0 < len; e0 += kWave * B) {
+        float4 a[kNormParts][B], r[kNormParts][B];
+#pragma unroll
+        for (int k = 0; k < kNormParts; ++k)
+#pragma unroll
+            for (int e = 0; e < B; ++e) {
+                const int i = lo[k] + e0 + lane + kWave * e;
+                a[k][e] = make_float4(0.f, 0.f, 0.f, 0.f);
+                r[k][e] = a[k][e];
+                if (i < hi[k]) {
+                    a[k][e] = a4[i];
+                    r[k][e] = r4[i];
+                }
+            }
+#pragma unroll
+        for (int k = 0; k < kNormParts; ++k)
+#pragma unroll
+            for (int e = 0; e < B; ++e) {
+                const int i = lo[k] + e0 + lane + kWave * e;
+                const float4 v = make_float4(a[k][e].x + r[k][e].x, a[k][e].y + r[k][e].y,
+                                             a[k][e].z + r[k][e].z, a[k][e].w + r[k][e].w);
+                ss[k] = fmaf(v.x, v.x, ss[k]);
+                ss[k] = fmaf(v.y, v.y, ss[k]);
+                ss[k] = fmaf(v.z, v.z, ss[k]);
+                ss[k] = fmaf(v.w, v.w, ss[k]);
+                if (write && i < hi[k]) o4[i] = v;
+            }
+    }
+#pragma unroll
+    for (int k = 0; k < kNormParts; ++k) part[k] = wave_sum(ss[k]);
+}
+
+// 1 / rms of s from its parts.
+__device__ __forceinline__ float norm_inv_from(const float (&part)[kNormParts], const OpDesc &op) {
+    float ss = part[0];
+#pragma unroll
+    for (int k = 1; k < kNormParts; ++k) ss += part[k];
+    return 1.0f / sqrtf(ss / (float)(op.nb * kQuants) + op.norm_eps);
 }
 
 // One normalised value of the kXNormAdd input.
@@ -253,7 +284,11 @@ __device__ void tail_tile(const OpDesc &op, uint32_t tile, int waves) {
     const int64_t row = (int64_t)op.tail_row0 + (int64_t)tile * waves + wave;
     if (row >= op.p) return;
     float inv = 0.f;
-    if constexpr (XM == kXNormAdd) inv = norm_add_inv(op, lane, false);
+    if constexpr (XM == kXNormAdd) {
+        float part[kNormParts];
+        norm_add_parts(op, lane, false, part);
+        inv = norm_inv_from(part, op);
+    }
     const int nb = op.nb;
     const uint8_t *wr = op.w + row * (int64_t)nb * kBlockBytes;
     for (int i = 0; i < op.m; ++i) {

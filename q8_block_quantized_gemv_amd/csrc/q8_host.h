@@ -6,6 +6,8 @@
 #include <stdint.h>
 
 #include <string>
+#include <utility>
+#include <vector>
 
 #include "q8gemv.h"
 
@@ -28,8 +30,7 @@ Q8_HIDDEN int workspace_for(int dev, hipStream_t s, size_t ws_bytes, size_t cnt_
 // activations (XMode) and the extra vectors that takes, n floats each,
 // 16-byte aligned.
 struct OpExtra {
-    int mode = 0;                  // kXSiluUp or kXNormAdd, the same for every op of a chain;
-                                   // Q8_CHAIN_ONE_LAUNCH chains: one per phase, kXFloat for none
+    int mode = 0;                  // kXSiluUp or kXNormAdd, the same for every op of a chain
     const float *x_up = nullptr;   // kXSiluUp: input silu(x) * x_up
     const float *x_res = nullptr;  // kXNormAdd: input rms_norm(x + x_res) * norm_w
     const float *norm_w = nullptr;
@@ -39,6 +40,10 @@ struct OpExtra {
 // q8_0_chain_create with per-op extras (null: plain ops).
 Q8_HIDDEN int chain_create_ex(const q8_0_op *ops, int64_t n_ops, uint32_t flags,
                               const OpExtra *extra, q8_0_chain **out);
+// The launches of a chain before planning: maximal runs [begin, end) of
+// ops that do not depend on one another (one op per run with per_op).
+Q8_HIDDEN std::vector<std::pair<int64_t, int64_t>> chain_segments(const q8_0_op *ops, int64_t n_ops,
+                                                                  bool per_op, const OpExtra *extra);
 // Issue a chain's launches on s, without its graph.
 Q8_HIDDEN int chain_issue(const q8_0_chain *c, hipStream_t s);
 

@@ -32,9 +32,11 @@ constexpr int kStageBytesM = kStageW;              // small batch: W only
 
 // One matvec (or small-batch product) as the kernels see it.  A "super-row"
 // is `rs` consecutive rows whose bytes, taken together, are a whole number of
-// 272-byte groups: rs = 8 / gcd(n/32, 8).  Lane l of a wave owns one
-// super-row; rows that do not fill a last super-row are "tail" rows and take
-// the generic path.
+// 272-byte groups: rs = 8 / gcd(n/32, 8).  rs == 1 (n a multiple of 256):
+// every row is whole groups and the rows-and-group-slots kernel takes the op
+// (q8_gemv_rc.hip).  rs > 1: lane l of a wave owns one super-row
+// (q8_gemv.hip); rows that do not fill a last super-row are "tail" rows and
+// take the generic path.
 struct OpDesc {
     const float *x;      // x, or X row 0 for small batches
     const uint8_t *w;
@@ -47,30 +49,19 @@ struct OpDesc {
     int32_t rs;          // rows per super-row: 1, 2, 4 or 8
     int32_t nsr;         // super-rows handled by the fast path = p / rs
     int32_t gsr;         // groups per super-row = rs * nb / 8
-    int32_t ks;          // waves that split one super-row's groups: 1, 2 or 4
+    int32_t ks;          // rs > 1: waves that split one super-row's groups (1, 2 or 4)
     int32_t fast_tiles;  // workgroup tiles of the fast path
     int32_t tail_row0;   // first tail row = nsr * rs
     int32_t m;           // activation rows (1 for a matvec)
-    // K split across workgroups (matvec only): `slices` workgroups share a
-    // row tile, slice s taking groups [s * slice_groups, (s+1) * slice_groups).
-    // Each parks its per-row partial sums in part[s][row]; the last of them
-    // to arrive (counted in cnt[row tile]) adds the slices in order into y
-    // and clears the counter.  slices == 1: no split, part and cnt unused.
-    int32_t slices;
-    int32_t slice_groups;  // a multiple of kSlots
-    // Stream-K launches (Piece): the most workgroups sharing one row tile;
-    // part then holds sk_slots slots of nsr * rs floats.  0: not stream-K.
-    int32_t sk_slots;
-    float *part;         // max(slices, sk_slots) * nsr * rs floats
-    uint32_t *cnt;       // one per row tile of 64 super-rows, zero between launches
+    int32_t pad0_;
     const float *x_up;   // kXSiluUp: the input is silu(x) * x_up, elementwise
     // kXNormAdd: the input is rms_norm(x + x_res) * norm_w over the op's n
-    // columns; the op-local tile 0's first wave also writes x + x_res to x_out
+    // columns; the op-local tile 0's workgroup also writes x + x_res to x_out
     const float *x_res;
     const float *norm_w;
     float *x_out;        // may be null
     float norm_eps;
-    int32_t pad2_;
+    int32_t pad1_;
 };
 
 // How a matvec reads its activations (a compile-time mode of the kernels).
@@ -80,10 +71,15 @@ enum XMode : int {
     kXSiluUp = 2,   // silu(x) * x_up formed per group (the SwiGLU product feeding a down projection)
     kXNormAdd = 3,  // rms_norm(x + x_res) * norm_w formed per group (a residual add and the norm after it)
 };
-constexpr int kMaxSlices = 32;
-// Every row sums its groups into kSlots partial sums (group kk into slot
-// kk % kSlots) and combines them in a fixed tree at the end.
+// rs > 1: every row sums its groups into kSlots partial sums (group kk into
+// slot kk % kSlots, in increasing kk) and combines them as
+// (s0 + s1) + (s2 + s3).
 constexpr int kSlots = 4;
+// rs == 1: kRowSlots partial sums per row (group kk into slot kk % 16, in
+// increasing kk), combined as (L0 + L1) + (L2 + L3) with
+// L_a = (s_a + s_{a+4}) + (s_{a+8} + s_{a+12}).  Every launch shape of the
+// rs == 1 kernel computes exactly this tree.
+constexpr int kRowSlots = 16;
 
 // One workgroup's work in a fused launch.
 struct Tile {
@@ -92,80 +88,89 @@ struct Tile {
 };
 constexpr uint32_t kTailBit = 0x80000000u;
 
-// Stream-K work of a one-wave workgroup: groups [g0, g1) of row tile `tile`
-// (64 super-rows) of op `op`.  A row tile that several workgroups share
-// (nslots > 1) has each park its partial sums in slot `slot` of the op's
-// partials; the last of them to arrive adds the slots in slot order.
-struct Piece {
-    uint32_t op;
-    uint32_t tile;
-    uint32_t g0, g1;
-    uint32_t slot, nslots;
-};
-
-// One phase of a one-launch chain: a stream-K schedule (pieces, then tail
-// tiles) of mutually independent ops that read their activations in one
-// mode.  The phases run in order, separated by device-wide barriers.
-struct PhaseDesc {
-    const OpDesc *ops;
-    const Piece *pieces;
-    const uint32_t *begin;   // n_sk + 1 piece offsets
-    const Tile *tails;
-    int32_t n_sk;            // workgroups with pieces (the first n_sk of the launch)
-    int32_t n_tail;          // tail tiles, taken round robin by all workgroups
-    int32_t xmode;           // XMode (kXFloat, kXSiluUp or kXNormAdd)
-    // 1: this phase reads memory that an earlier phase of the launch read
-    // and a later one rewrote, so every wave drops its CU's cached lines at
-    // the barrier before it (an agent-scope acquire) -- otherwise only the
-    // XCD leaders do, for the L2s
-    int32_t acquire;
-};
-
-// Matvec kernel shape: waves per workgroup (1, 2 or 4) and groups each wave
-// keeps in flight ahead of the one it computes (1 or 2).
+// rs > 1 kernel shape: waves per workgroup (1 or 4); each wave keeps one
+// group in flight ahead of the one it computes.
 struct Variant {
     int nw;
     int pf;
 };
 
-// Fast tiles cover (nw / ks) * 64 super-rows each (times the K slices).
-inline int64_t fast_tiles_for(int64_t nsr, int ks, int nw = kWaves, int slices = 1) {
+// Shape of a launch of the rs == 1 kernel: C lanes per row (1, 2 or 4) so a
+// wave covers 64 / C rows, and NWK waves per workgroup (1, 2 or 4) that
+// share a tile's rows and split its groups by slot (wave w takes the group
+// columns j = w, w + NWK, ...).
+struct RcShape {
+    int c;
+    int nwk;
+};
+
+// rs > 1: fast tiles cover (nw / ks) * 64 super-rows each.
+inline int64_t fast_tiles_for(int64_t nsr, int ks, int nw = kWaves) {
     const int64_t per = (int64_t)(nw / ks) * kWave;
-    return (nsr + per - 1) / per * slices;
+    return (nsr + per - 1) / per;
 }
 // Tail tiles take one row per wave.
 inline int64_t tail_tiles_for(int64_t tail_rows, int nw = kWaves) {
     return (tail_rows + nw - 1) / nw;
 }
+// rs == 1: tiles of 64 / C rows.
+inline int64_t rc_tiles_for(int64_t p, int c) {
+    const int64_t rows = kWave / c;
+    return (p + rows - 1) / rows;
+}
 
-// Matvec launchers (q8_gemv.hip).  All return the hipError_t of the launch.
-// xmode: how the activations are read (XMode).
+// Matvec launchers.  All return the hipError_t of the launch.  xmode: how
+// the activations are read (XMode).
+// rs > 1 ops (q8_gemv.hip): one op on workgroups of v.nw waves (1 or 4).
 hipError_t launch_gemv_single(const OpDesc &op, const Variant &v, int64_t grid, hipStream_t s,
                               int xmode = kXFloat);
+// A table of tiles of independent ops of any width, on one-wave workgroups
+// (v = {1, 1}): rs == 1 tiles in RcShape {1, 1}, the others as super-rows.
 hipError_t launch_gemv_fused(const OpDesc *d_ops, const Tile *d_tiles, const Variant &v,
                              int64_t grid, hipStream_t s, int xmode = kXFloat);
-// Stream-K launch of one-wave workgroups: workgroup b < n_sk walks pieces
-// [begin[b], begin[b+1]); the n_tail workgroups after them run tails[b - n_sk]
-// (tail tiles).  pf: groups in flight per wave (1 or 2).
-hipError_t launch_gemv_streamk(const OpDesc *d_ops, const Piece *d_pieces, const uint32_t *d_begin,
-                               const Tile *d_tails, int64_t n_sk, int64_t n_tail, int pf,
-                               hipStream_t s, int xmode = kXFloat);
-// One launch of a whole chain of dependent phases on `wgs` one-wave
-// workgroups, all of which must be resident at once (wgs <= the CUs times
-// gemv_phased_blocks_per_cu()), `per` of them on each of `nx` XCDs
-// (per * nx == wgs, as the census found).  d_sync: kPhasedSyncBytes of
-// barrier state, zero when first used and kept between launches; its word
-// kPhasedSyncErr is set to 1 if a barrier wait gave up.
-constexpr int kPhasedSyncBytes = 64 * 4 * 34;
-constexpr int kPhasedSyncErr = 64 * 33;
-hipError_t launch_gemv_phased(const PhaseDesc *d_phases, int n_phases, uint32_t *d_sync, uint32_t per,
-                              uint32_t nx, int64_t wgs, int pf, hipStream_t s);
-// The same kernel with no phases: workgroup b writes the XCD it runs on to
-// d_census[b] (wgs words).
-hipError_t launch_gemv_phased_census(uint32_t *d_census, int64_t wgs, hipStream_t s);
-// Workgroups of the one-launch kernel that fit on one CU at once (0 on error
-// or for a pf it is not built with; it has pf = 1 only).
-int gemv_phased_blocks_per_cu(int pf);
+// rs == 1 ops (q8_gemv_rc.hip, built once per mode M: the entry points
+// below with the mode's number appended).  One op: grid =
+// rc_tiles_for(p, c) workgroups.  A table of tiles of independent rs == 1
+// ops read in one mode.  LDS bytes of a workgroup (0: no such shape).
+#define Q8_RC_DECLARE(M)                                                                              \
+    hipError_t launch_gemv_rc_##M(const OpDesc &op, RcShape sh, int64_t grid, hipStream_t s);         \
+    hipError_t launch_gemv_rc_fused_##M(const OpDesc *d_ops, const Tile *d_tiles, RcShape sh,         \
+                                        int64_t grid, hipStream_t s);                                 \
+    int gemv_rc_lds_bytes_##M(RcShape sh);
+Q8_RC_DECLARE(0)
+Q8_RC_DECLARE(1)
+Q8_RC_DECLARE(2)
+Q8_RC_DECLARE(3)
+#undef Q8_RC_DECLARE
+
+inline hipError_t launch_gemv_rc(const OpDesc &op, RcShape sh, int64_t grid, hipStream_t s, int xmode) {
+    switch (xmode) {
+        case kXFloat: return launch_gemv_rc_0(op, sh, grid, s);
+        case kXQuant: return launch_gemv_rc_1(op, sh, grid, s);
+        case kXSiluUp: return launch_gemv_rc_2(op, sh, grid, s);
+        case kXNormAdd: return launch_gemv_rc_3(op, sh, grid, s);
+        default: return hipErrorInvalidValue;
+    }
+}
+inline hipError_t launch_gemv_rc_fused(const OpDesc *d_ops, const Tile *d_tiles, RcShape sh, int64_t grid,
+                                       hipStream_t s, int xmode) {
+    switch (xmode) {
+        case kXFloat: return launch_gemv_rc_fused_0(d_ops, d_tiles, sh, grid, s);
+        case kXQuant: return launch_gemv_rc_fused_1(d_ops, d_tiles, sh, grid, s);
+        case kXSiluUp: return launch_gemv_rc_fused_2(d_ops, d_tiles, sh, grid, s);
+        case kXNormAdd: return launch_gemv_rc_fused_3(d_ops, d_tiles, sh, grid, s);
+        default: return hipErrorInvalidValue;
+    }
+}
+inline int gemv_rc_lds_bytes(RcShape sh, int xmode) {
+    switch (xmode) {
+        case kXFloat: return gemv_rc_lds_bytes_0(sh);
+        case kXQuant: return gemv_rc_lds_bytes_1(sh);
+        case kXSiluUp: return gemv_rc_lds_bytes_2(sh);
+        case kXNormAdd: return gemv_rc_lds_bytes_3(sh);
+        default: return 0;
+    }
+}
 // x (n floats, n % 32 == 0) -> n/32 Q8_0 blocks of 34 bytes at xq.
 hipError_t launch_quantize_x(const float *x, void *xq, int64_t n, hipStream_t s);
 

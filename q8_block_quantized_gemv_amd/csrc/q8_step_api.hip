@@ -180,19 +180,13 @@ struct q8_0_step {
     float *x = nullptr, *xn = nullptr, *q = nullptr, *k = nullptr, *v = nullptr, *attn = nullptr;
     float *xa = nullptr, *xb = nullptr;   // the residual stream, alternating between layers
     float *resid = nullptr, *gate = nullptr, *up = nullptr, *logits = nullptr;
-    // one_launch: the down projection's output, so that no memory of a
-    // launch is read, rewritten and read again (o writes resid)
-    float *resid2 = nullptr;
     float *kcache = nullptr, *vcache = nullptr, *attn_ws = nullptr, *amax_ws = nullptr;
     uint32_t *cnt = nullptr;  // n_heads attention counters, then the argmax counter
     int32_t *pos = nullptr;
     uint32_t *token = nullptr;
     double2 *rope = nullptr;  // (cos, sin) of every rotation angle, [position][pair]
     int max_chunks = 0, amax_wgs = 0, launches = 0;
-    // one_launch: layer 0's q|k|v, then per layer one launch of o, gate|up,
-    // down and the next layer's q|k|v (the lm_head after the last layer).
-    // Otherwise per layer q|k|v, o, gate|up, down; then the lm_head.
-    bool one_launch = false;
+    // per layer q|k|v, o, gate|up, down; then the lm_head
     std::vector<q8_0_chain *> chains;
     int64_t steps_since_reset = 0, reset_pos = 0;
     hipStream_t capture = nullptr;
@@ -227,9 +221,8 @@ int issue_step(const q8_0_step *s, hipStream_t st) {
     for (int64_t l = 0; l < m.n_layers && e == hipSuccess; ++l) {
         const q8_0_layer_w &L = s->layers[l];
         float *kc = s->kcache + l * cache_stride, *vc = s->vcache + l * cache_stride;
-        q8_0_chain *const *ch = s->one_launch ? nullptr : &s->chains[4 * l];
-        if (!s->one_launch && (rc = chain_issue(ch[0], st))) return rc;
-        if (s->one_launch && l == 0 && (rc = chain_issue(s->chains[0], st))) return rc;
+        q8_0_chain *const *ch = &s->chains[4 * l];
+        if ((rc = chain_issue(ch[0], st))) return rc;
         AttnDesc d;
         std::memset(&d, 0, sizeof d);
         d.q = nullptr; d.kc = kc; d.vc = vc; d.out = s->attn; d.pos_dev = s->pos;
@@ -240,16 +233,12 @@ int issue_step(const q8_0_step *s, hipStream_t st) {
         f.q = s->q; f.k = s->k; f.v = s->v; f.q_norm = L.q_norm; f.k_norm = L.k_norm;
         f.kc_w = kc; f.vc_w = vc; f.eps = m.eps; f.theta = m.theta; f.rope = s->rope;
         ok(launch_attention_fused(d, f, st));
-        if (s->one_launch) {
-            if ((rc = chain_issue(s->chains[1 + l], st))) return rc;
-            continue;
-        }
         if ((rc = chain_issue(ch[1], st))) return rc;
         if ((rc = chain_issue(ch[2], st))) return rc;
         if ((rc = chain_issue(ch[3], st))) return rc;
     }
     if (e != hipSuccess) return fail_hip(e, "decode step launch");
-    if (!s->one_launch && (rc = chain_issue(s->chains.back(), st))) return rc;
+    if ((rc = chain_issue(s->chains.back(), st))) return rc;
     ArgmaxDesc a;
     a.x = s->logits; a.n = m.vocab; a.out = s->token; a.ws_val = s->amax_ws;
     a.ws_idx = (uint32_t *)(s->amax_ws + s->amax_wgs); a.cnt = s->cnt + m.n_heads;
@@ -315,7 +304,7 @@ int q8_0_step_create(const q8_0_model *m, q8_0_step **out) {
     std::vector<size_t> sizes = {
         (size_t)m->hidden, (size_t)m->hidden, (size_t)m->hidden, (size_t)m->hidden,
         (size_t)s->q_width, (size_t)s->kv_width,
-        (size_t)s->kv_width, (size_t)s->q_width, (size_t)m->hidden, (size_t)m->hidden, (size_t)m->inter,
+        (size_t)s->kv_width, (size_t)s->q_width, (size_t)m->hidden, (size_t)m->inter,
         (size_t)m->inter, (size_t)m->vocab,
         (size_t)(m->n_layers * m->max_seq * s->kv_width), (size_t)(m->n_layers * m->max_seq * s->kv_width),
         (size_t)(m->n_heads * s->max_chunks * (m->head_dim + 2)), (size_t)(2 * s->amax_wgs),
@@ -334,7 +323,7 @@ int q8_0_step_create(const q8_0_model *m, q8_0_step **out) {
         return fail_hip(e, "q8_0_step_create hipMemset");
     }
     char *b = (char *)s->mem;
-    float **fl[] = {&s->x, &s->xn, &s->xa, &s->xb, &s->q, &s->k, &s->v, &s->attn, &s->resid, &s->resid2, &s->gate, &s->up,
+    float **fl[] = {&s->x, &s->xn, &s->xa, &s->xb, &s->q, &s->k, &s->v, &s->attn, &s->resid, &s->gate, &s->up,
                     &s->logits, &s->kcache, &s->vcache, &s->attn_ws, &s->amax_ws};
     const size_t nf = sizeof fl / sizeof fl[0];
     for (size_t i = 0; i < nf; ++i) *fl[i] = (float *)(b + offs[i]);
@@ -381,54 +370,7 @@ int q8_0_step_create(const q8_0_model *m, q8_0_step **out) {
     OpExtra silu;
     silu.mode = kXSiluUp;
     silu.x_up = s->up;
-    // Q8GEMV_ONE_LAUNCH=1: the matvecs between two attentions as one
-    // launch.  Measured slower on the Qwen3-0.6B and 7B shapes (1647 vs 1270
-    // and 3052 vs 2779 us per token): a phase's barrier (3.6 us) and cold
-    // first load cost more than the launch boundary they replace.
-    {
-        const char *ev = std::getenv("Q8GEMV_ONE_LAUNCH");
-        s->one_launch = ev && std::atoi(ev) == 1;
-    }
-    if (s->one_launch) {
-        OpExtra plain;
-        plain.mode = kXFloat;
-        auto reader = [](OpExtra e) { e.x_out = nullptr; return e; };   // one writer per phase
-        rc = mk({{s->xn, s->layers[0].wq, s->q, m->hidden, s->q_width},
-                 {s->xn, s->layers[0].wk, s->k, m->hidden, s->kv_width},
-                 {s->xn, s->layers[0].wv, s->v, m->hidden, s->kv_width}});
-        for (int64_t l = 0; l < m->n_layers && !rc; ++l) {
-            const q8_0_layer_w &L = s->layers[l];
-            std::vector<q8_0_op> ops = {{s->attn, L.wo, s->resid, s->q_width, m->hidden}};
-            std::vector<OpExtra> ex = {plain};
-            const OpExtra e1 = norm_add(L.ffn_norm, oth);
-            ops.push_back({cur, L.wgate, s->gate, m->hidden, m->inter});
-            ops.push_back({cur, L.wup, s->up, m->hidden, m->inter});
-            ex.push_back(e1);
-            ex.push_back(reader(e1));
-            std::swap(cur, oth);
-            ops.push_back({s->gate, L.wdown, s->resid2, m->inter, m->hidden});
-            ex.push_back(silu);
-            if (l + 1 < m->n_layers) {
-                const q8_0_layer_w &N = s->layers[l + 1];
-                const OpExtra e2 = norm_add(N.attn_norm, oth, s->resid2);
-                ops.push_back({cur, N.wq, s->q, m->hidden, s->q_width});
-                ops.push_back({cur, N.wk, s->k, m->hidden, s->kv_width});
-                ops.push_back({cur, N.wv, s->v, m->hidden, s->kv_width});
-                ex.push_back(e2);
-                ex.push_back(reader(e2));
-                ex.push_back(reader(e2));
-                std::swap(cur, oth);
-            } else {
-                ops.push_back({cur, m->lm_head, s->logits, m->hidden, m->vocab});
-                ex.push_back(norm_add(m->out_norm, s->x, s->resid2));
-            }
-            q8_0_chain *c = nullptr;
-            rc = chain_create_ex(ops.data(), (int64_t)ops.size(), Q8_CHAIN_FUSE | Q8_CHAIN_ONE_LAUNCH,
-                                 ex.data(), &c);
-            if (!rc) s->chains.push_back(c);
-        }
-    }
-    for (int64_t l = 0; l < m->n_layers && !rc && !s->one_launch; ++l) {
+    for (int64_t l = 0; l < m->n_layers && !rc; ++l) {
         const q8_0_layer_w &L = s->layers[l];
         if (l == 0) {
             rc = mk({{s->xn, L.wq, s->q, m->hidden, s->q_width}, {s->xn, L.wk, s->k, m->hidden, s->kv_width},
@@ -448,7 +390,7 @@ int q8_0_step_create(const q8_0_model *m, q8_0_step **out) {
         std::swap(cur, oth);
         if ((rc = mk({{s->gate, L.wdown, s->resid, m->inter, m->hidden}}, &silu))) break;
     }
-    if (!rc && !s->one_launch) {
+    if (!rc) {
         const OpExtra e = norm_add(m->out_norm, s->x);
         rc = mk({{cur, m->lm_head, s->logits, m->hidden, m->vocab}}, &e);
     }
@@ -502,15 +444,6 @@ int q8_0_step_run(q8_0_step *s, int mode, void *stream) {
         return rc;
     }
     ++s->steps_since_reset;
-    return Q8_OK;
-}
-
-int q8_0_step_check(const q8_0_step *s) {
-    if (!s) return fail(Q8_ERR_INVALID_ARG, "q8_0_step_check: null step");
-    for (const q8_0_chain *c : s->chains) {
-        const int rc = q8_0_chain_check(c);
-        if (rc) return rc;
-    }
     return Q8_OK;
 }
 

@@ -120,17 +120,35 @@ def test_chain_validation(q8):
     assert h.value is None
     assert "op 1" in q8.last_error()
     assert q8.lib.q8_0_chain_create(ops, 0, 0, ctypes.byref(h)) == -1
+    assert q8.lib.q8_0_chain_create(ops, 1, 8, ctypes.byref(h)) == -1   # no flag 8 any more
     assert q8.lib.q8_0_chain_create(ops, 1, 16, ctypes.byref(h)) == -1
-    # one launch takes neither the integer path nor one launch per op
-    assert q8.lib.q8_0_chain_create(ops, 1, q8.Q8_CHAIN_ONE_LAUNCH | q8.Q8_CHAIN_XQ, ctypes.byref(h)) == -1
-    assert q8.lib.q8_0_chain_create(ops, 1, q8.Q8_CHAIN_ONE_LAUNCH | q8.Q8_CHAIN_PER_OP, ctypes.byref(h)) == -1
-    assert "ONE_LAUNCH" in q8.last_error()
+    assert "unknown flags" in q8.last_error()
     assert q8.lib.q8_0_chain_create(None, 1, 0, ctypes.byref(h)) == -1
     assert q8.lib.q8_0_decode_chain(None, 0, None) == -1
     assert q8.lib.q8_0_chain_launches(None) == -1
-    assert q8.lib.q8_0_chain_check(None) == -1
-    assert q8.lib.q8_0_step_check(None) == -1
     assert q8.lib.q8_0_chain_destroy(None) == 0
+
+
+@pytest.mark.parametrize("c,waves,n,code", [
+    (3, 1, 256, -1), (1, 3, 256, -1), (0, 1, 256, -1), (8, 1, 256, -1),   # lanes/waves not 1, 2, 4
+    (4, 4, 96, -2), (4, 4, 896, -2),                                        # n not a multiple of 256
+    (4, 4, 0, -2), (1, 1, 33, -2),                                          # as q8_0_gemv
+])
+def test_gemv_shaped_validation(q8, c, waves, n, code):
+    assert q8.lib.q8_0_gemv_shaped(X, W, Y, n, 4, c, waves, None) == code
+    assert q8.last_error() != ""
+
+
+@pytest.mark.parametrize("m,n,kernel,code", [
+    (2, 256, 5, -1), (2, 256, -1, -1),          # unknown kernel
+    (4, 256, 3, -2), (4, 256, 4, -2),           # the row-and-block-pair kernel takes m <= 3
+    (2, 896, 3, -2),                            # ... and rows of whole groups (n % 256 == 0)
+    (2, 96, 2, -2),                             # the matrix cores take rows of 1 or 2 per super-row
+    (1, 256, 2, -2), (1, 256, 1, -2),           # m = 1 is the matvec's
+    (17, 256, 0, -2),                           # m as q8_0_gemm_smallm
+])
+def test_gemm_kernel_validation(q8, m, n, kernel, code):
+    assert q8.lib.q8_0_gemm_smallm_kernel(X, W, Y, m, n, 4, kernel, None) == code
 
 
 def test_no_device_path(q8):

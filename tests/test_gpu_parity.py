@@ -168,46 +168,58 @@ def test_determinism_canaries_and_sign(q8, n, p):
 GEMM_SHAPES = [(256, 130), (896, 70), (896, 71), (3584, 300), (160, 11), (192, 37),
                (18944, 70), (1024, 3072)]
 
-# (m, path): by default m = 2..3 runs on the vector units with lanes over
+# (m, kernel): by default m = 2..3 runs on the vector units with lanes over
 # (row, block pair) where n is a multiple of 256, other m >= 2 on the matrix
 # cores where n is a multiple of 128, and the rest on the vector units with a
-# lane per row (four rows of X per pass); Q8GEMV_SMALLM_PATH=valu forces the
-# lane-per-row kernel for every width, =mfma the matrix cores where they apply.
-# "nw1" keeps the default path but runs the row-and-block-pair kernel with
-# one wave per workgroup instead of two sharing the stages.
+# lane per row (four rows of X per pass).  The named kernels run where they
+# apply and are refused (Q8_ERR_SHAPE) elsewhere; VROW1 is the
+# row-and-block-pair kernel with one wave per workgroup instead of two.
 GEMM_CASES = ([(m, None) for m in (1, 2, 3, 4, 5, 8, 13, 16)] +
-              [(m, "valu") for m in (2, 3, 4, 5, 8, 13, 16)] +
-              [(m, "mfma") for m in (2, 3)] + [(m, "nw1") for m in (2, 3)])
+              [(m, "VALU") for m in (2, 3, 4, 5, 8, 13, 16)] +
+              [(m, "MFMA") for m in (2, 3)] + [(m, "VROW1") for m in (2, 3)])
+
+
+def _kernel_takes(kernel, m, n):
+    nb = n // 32
+    rs = 8 // np.gcd(nb, 8)
+    if kernel == "MFMA":
+        return rs <= 2 and m >= 2
+    if kernel in ("VROW", "VROW1"):
+        return rs == 1 and 2 <= m <= 3
+    return m >= 2
 
 
 @pytest.mark.parametrize("m,path", GEMM_CASES, ids=lambda v: str(v))
 @pytest.mark.parametrize("n,p", GEMM_SHAPES, ids=lambda v: str(v))
-def test_gemm_smallm(q8, monkeypatch, m, path, n, p):
+def test_gemm_smallm(q8, m, path, n, p):
     """Each row of Y against its own oracle matvec; bitwise repeatable.
     (3584, 300) and (18944, 70) have few row tiles, so a row tile's groups
     are split over workgroups and the last to arrive adds the parts;
     (896, 71) has a tail row; (192, 37) and (160, 11) have 4- and 8-row
-    super-rows, which only the vector kernel takes."""
+    super-rows, which only the vector kernel takes (the others refuse them)."""
     import torch
-    if path == "nw1":
-        monkeypatch.setenv("Q8GEMV_SMALLM_VROW_NW", "1")
-    elif path:
-        monkeypatch.setenv("Q8GEMV_SMALLM_PATH", path)
-    log("gemm m=%d n=%d p=%d path=%s" % (m, n, p, path or "default"))
+    log("gemm m=%d n=%d p=%d kernel=%s" % (m, n, p, path or "default"))
+    kernel = getattr(q8, "SMALLM_" + path) if path else None
+    if path and not _kernel_takes(path, m, n):
+        X = torch.zeros((m, n), dtype=torch.float32, device="cuda")
+        with pytest.raises(q8.Q8Error) as ei:
+            q8.gemm_smallm(X, w_dev(synth.q8_weights(n, p, np.random.default_rng(1)), n, p), kernel=kernel)
+        assert ei.value.code == q8.Q8_ERR_SHAPE
+        return
     rng = np.random.default_rng(300 + 11 * m + n + p)
     w = synth.q8_weights(n, p, rng)
     X = synth.activations(n, rng, m).reshape(m, n)
     wd = w_dev(w, n, p)
     Xd = up(X)
     Y = torch.full((m, p), float("nan"), dtype=torch.float32, device="cuda")
-    q8.gemm_smallm(Xd, wd, Y)
+    q8.gemm_smallm(Xd, wd, Y, kernel=kernel)
     Yh = down(Y).copy()
     _, Y64, MAG = oracle.gemm(w, X, m, n, p)
     for i in range(m):
         parity(Yh[i], Y64[i], MAG[i], "gemm row %d" % i)
     for _ in range(2):       # again: split-K counters must have been left at zero
         Y.fill_(float("nan"))
-        q8.gemm_smallm(Xd, wd, Y)
+        q8.gemm_smallm(Xd, wd, Y, kernel=kernel)
         assert np.array_equal(down(Y).view(np.uint32), Yh.view(np.uint32))
 
 
@@ -222,13 +234,13 @@ def _vrow_sweep_cases():
 
 
 @pytest.mark.parametrize("n,p,m,nw", _vrow_sweep_cases(), ids=lambda v: str(v))
-def test_gemm_vrow_sweep(q8, monkeypatch, n, p, m, nw):
+def test_gemm_vrow_sweep(q8, n, p, m, nw):
     """Seeded random shapes on the vector units' row-and-block-pair kernel
     (m = 2, 3; one or two waves per workgroup): every output against the
     oracle, and bitwise repeatable, so that row tiles split over workgroups
     at many different points are checked."""
     import torch
-    monkeypatch.setenv("Q8GEMV_SMALLM_VROW_NW", nw)
+    kernel = q8.SMALLM_VROW1 if nw == "1" else q8.SMALLM_VROW
     log("gemm vrow sweep n=%d p=%d m=%d nw=%s" % (n, p, m, nw))
     rng = np.random.default_rng(n * 7919 + p * 31 + m)
     w = synth.q8_weights(n, p, rng)
@@ -236,13 +248,13 @@ def test_gemm_vrow_sweep(q8, monkeypatch, n, p, m, nw):
     wd = w_dev(w, n, p)
     Xd = up(X)
     Y = torch.full((m, p), float("nan"), dtype=torch.float32, device="cuda")
-    q8.gemm_smallm(Xd, wd, Y)
+    q8.gemm_smallm(Xd, wd, Y, kernel=kernel)
     Yh = down(Y).copy()
     _, Y64, MAG = oracle.gemm(w, X, m, n, p)
     for i in range(m):
         parity(Yh[i], Y64[i], MAG[i], "vrow sweep row %d" % i)
     Y.fill_(float("nan"))
-    q8.gemm_smallm(Xd, wd, Y)
+    q8.gemm_smallm(Xd, wd, Y, kernel=kernel)
     assert np.array_equal(down(Y).view(np.uint32), Yh.view(np.uint32))
 
 
@@ -296,9 +308,9 @@ def test_gemm_identical_rows(q8, m):
     del torch
 
 
-@pytest.mark.parametrize("m,path", [(2, None), (3, None), (5, "valu"), (5, None), (16, None)],
+@pytest.mark.parametrize("m,path", [(2, None), (3, None), (5, "VALU"), (5, None), (16, None)],
                          ids=lambda v: str(v))
-def test_gemm_sign_and_scale(q8, monkeypatch, m, path):
+def test_gemm_sign_and_scale(q8, m, path):
     """Y(4X) = 4 Y(X) bit for bit on every path, and Y(-X) = -Y(X) bit for
     bit on the vector units, whose roundings are all to nearest even (no
     value here is near overflow or the subnormal range).  The matrix cores
@@ -306,18 +318,17 @@ def test_gemm_sign_and_scale(q8, monkeypatch, m, path):
     under negation, so there the sign is checked within the bar.  A row tile
     split over workgroups (p = 300 at n = 3584) is included."""
     import torch
-    if path:
-        monkeypatch.setenv("Q8GEMV_SMALLM_PATH", path)
-    log("gemm sign and scale m=%d path=%s" % (m, path or "default"))
+    kernel = getattr(q8, "SMALLM_" + path) if path else None
+    log("gemm sign and scale m=%d kernel=%s" % (m, path or "default"))
     n, p = 3584, 300
     rng = np.random.default_rng(77 + m)
     w = synth.q8_weights(n, p, rng)
     wd = w_dev(w, n, p)
     X = synth.activations(n, rng, m).reshape(m, n)
-    a = down(q8.gemm_smallm(up(X), wd)).copy()
-    assert np.array_equal(down(q8.gemm_smallm(up(X * 4), wd)), a * 4)
-    neg = down(q8.gemm_smallm(up(-X), wd))
-    if m <= 3 or path == "valu":
+    a = down(q8.gemm_smallm(up(X), wd, kernel=kernel)).copy()
+    assert np.array_equal(down(q8.gemm_smallm(up(X * 4), wd, kernel=kernel)), a * 4)
+    neg = down(q8.gemm_smallm(up(-X), wd, kernel=kernel))
+    if m <= 3 or path == "VALU":
         assert np.array_equal(neg, -a)
     else:
         _, _, MAG = oracle.gemm(w, X, m, n, p)
@@ -368,155 +379,125 @@ def test_chain_modes_equal_standalone(q8, fuse):
     chain.close()
 
 
-# (n, p) for K split across workgroups: row-poor shapes with many groups per
-# row (split into 2..5 slices), super-rows of 2 and 4 rows, a tail row, a
-# shape too short to split, a 7B down projection, and a shape with more row
-# tiles (257) than the GPU has CUs
+# Shapes for chains planned for latency (Q8_CHAIN_SPLIT_K): row-poor ops
+# with many groups per row, super-rows of 2 and 4 rows, a tail row, a 7B
+# down projection, more row tiles than the GPU has CUs, and ops of one width
+# that share a launch (the 3584-wide q, k, v).
 SPLIT_SHAPES = [(2048, 1024), (3072, 1024), (896, 130), (896, 131), (4864, 131), (1088, 5),
-                (3584, 512), (96, 67), (18944, 3584), (1024, 16448)]
+                (3584, 512), (96, 67), (18944, 3584), (1024, 16448), (3584, 3584), (3584, 513)]
 
 
-@pytest.mark.parametrize("sk", ["0", "1", "2"], ids=["sk_off", "sk_auto", "sk_all"])
 @pytest.mark.parametrize("per_op", [False, True], ids=["fused", "per_op"])
-def test_split_k_chain(q8, monkeypatch, per_op, sk):
+def test_split_k_chain(q8, per_op):
     """Q8_CHAIN_SPLIT_K on independent ops and on a dependent pair: every
-    output within the bar against the oracle on the inputs the op actually
-    read, the same bits on every replay and in every mode (the split's
-    arrival counters reset themselves).  Q8GEMV_STREAMK picks the schedule:
-    K slices only, stream-K where row tiles outnumber CUs (the default), or
-    stream-K for every launch (pieces crossing row tiles and ops, row tiles
-    shared by many workgroups, tail rows)."""
+    output equals the standalone q8_0_gemv on the same inputs bit for bit
+    (every launch shape sums in the same order), the same bits on every
+    replay and in every mode, and within the bar against the oracle."""
     import torch
-    monkeypatch.setenv("Q8GEMV_STREAMK", sk)
-    log("split-K chain per_op=%s streamk=%s" % (per_op, sk))
+    log("split-K chain per_op=%s" % per_op)
     rng = np.random.default_rng(77)
     ws = [synth.q8_weights(n, p, rng) for n, p in SPLIT_SHAPES]
     xs = [synth.activations(n, rng) for n, p in SPLIT_SHAPES]
     wd = [w_dev(w, n, p) for w, (n, p) in zip(ws, SPLIT_SHAPES)]
     xd = [up(x) for x in xs]
     ys = [torch.full((p,), float("nan"), dtype=torch.float32, device="cuda") for n, p in SPLIT_SHAPES]
-    # a dependent op: 3072 -> 1024 feeds 1024 -> 3072 (split too: 4 groups per row is not split)
+    # a dependent op: 3072 -> 1024 feeds 1024 -> 3072
     w_dep = synth.q8_weights(1024, 3072, rng)
+    wd_dep = w_dev(w_dep, 1024, 3072)
     y_dep = torch.full((3072,), float("nan"), dtype=torch.float32, device="cuda")
-    ops = list(zip(xd, wd, ys)) + [(ys[1], w_dev(w_dep, 1024, 3072), y_dep)]
+    ops = list(zip(xd, wd, ys)) + [(ys[1], wd_dep, y_dep)]
     chain = q8.Chain(ops, fuse=not per_op, split_k=True)
-    first = None
+    ref = [down(q8.gemv(x, w)).copy() for x, w in zip(xd, wd)]
+    ref.append(down(q8.gemv(up(ref[1]), wd_dep)).copy())
     for mode in (q8.MODE_GRAPH, q8.MODE_EAGER, q8.MODE_GRAPH, q8.MODE_SYNC_EACH):
         for y in ys + [y_dep]:
             y.fill_(float("nan"))
         chain.run(mode)
         q8.stream_wait(timeout_ms=60_000)
-        got = [down(y).copy() for y in ys + [y_dep]]
-        if first is None:
-            first = got
-        for a, b in zip(first, got):
-            assert np.array_equal(a.view(np.uint32), b.view(np.uint32)), mode
+        for i, y in enumerate(ys + [y_dep]):
+            assert np.array_equal(down(y).view(np.uint32), ref[i].view(np.uint32)), (mode, i)
     for i, (n, p) in enumerate(SPLIT_SHAPES):
         _, y64, mag = oracle.gemv(ws[i], xs[i], n, p)
-        parity(first[i], y64, mag, "split-K op %d (%d x %d)" % (i, n, p))
-    _, y64, mag = oracle.gemv(w_dep, first[1], 1024, 3072)
-    parity(first[-1], y64, mag, "split-K dependent op")
+        parity(ref[i], y64, mag, "split-K op %d (%d x %d)" % (i, n, p))
+    _, y64, mag = oracle.gemv(w_dep, ref[1], 1024, 3072)
+    parity(ref[-1], y64, mag, "split-K dependent op")
     chain.close()
 
 
-def test_one_launch_chain(q8, monkeypatch):
-    """Q8_CHAIN_ONE_LAUNCH: four phases in one launch -- the independent
-    split shapes (every super-row size, tail rows, a 7B down projection, more
-    row tiles than CUs), then three ops that each read the one before
-    (1024 -> 3072 -> 16448 -> 131, the last with 4-row super-rows and tail
-    rows).  The same bits as the split chain on the stream-K schedule (the
-    same pieces), on every replay and in every mode; within the bar against
-    the oracle on the inputs each op read; no barrier wait gave up."""
+# n multiple of 256: 4, 12, 14, 74 and 37 groups per row (columns that do and
+# do not fill 2 and 4 lanes), ragged row counts and rows that leave a last
+# tile of one row
+SHAPED = [(1024, 3072), (3072, 1024), (3584, 515), (18944, 70), (9472, 17), (256, 1), (1024, 65)]
+
+
+@pytest.mark.parametrize("n,p", SHAPED, ids=lambda v: str(v))
+def test_every_launch_shape_same_bits(q8, n, p):
+    """q8_0_gemv_shaped on all nine launch shapes (1, 2 or 4 lanes per row x
+    1, 2 or 4 waves per workgroup) gives q8_0_gemv's bits exactly, and those
+    are within the bar against the oracle."""
     import torch
-    log("one-launch chain")
-    rng = np.random.default_rng(91)
-    ws = [synth.q8_weights(n, p, rng) for n, p in SPLIT_SHAPES]
-    xs = [synth.activations(n, rng) for n, p in SPLIT_SHAPES]
-    ys = [torch.full((p,), float("nan"), dtype=torch.float32, device="cuda") for n, p in SPLIT_SHAPES]
-    ops = list(zip([up(x) for x in xs], [w_dev(w, n, p) for w, (n, p) in zip(ws, SPLIT_SHAPES)], ys))
-    dep_shapes = [(1024, 3072), (3072, 16448), (16448, 131)]
-    dep_w = [synth.q8_weights(n, p, rng) for n, p in dep_shapes]
-    dep_y = [torch.full((p,), float("nan"), dtype=torch.float32, device="cuda") for n, p in dep_shapes]
-    src = ys[1]                       # (3072, 1024): its 1024 outputs feed the first dependent op
-    for (n, p), w, y in zip(dep_shapes, dep_w, dep_y):
-        ops.append((src, w_dev(w, n, p), y))
-        src = y
-    outs = ys + dep_y
-    one = q8.Chain(ops, one_launch=True)
-    assert one.launches == 1
-    monkeypatch.setenv("Q8GEMV_STREAMK", "2")
-    ref_chain = q8.Chain(ops, fuse=True, split_k=True)
-    assert ref_chain.launches == 4
-    for y in outs:
-        y.fill_(float("nan"))
-    ref_chain.run(q8.MODE_GRAPH)
-    q8.stream_wait(timeout_ms=60_000)
-    ref = [down(y).copy() for y in outs]
-    for mode in (q8.MODE_GRAPH, q8.MODE_EAGER, q8.MODE_GRAPH, q8.MODE_SYNC_EACH, q8.MODE_GRAPH):
-        for y in outs:
+    log("launch shapes n=%d p=%d" % (n, p))
+    rng = np.random.default_rng(31 * n + p)
+    w = synth.q8_weights(n, p, rng)
+    x = synth.activations(n, rng)
+    wd, xd = w_dev(w, n, p), up(x)
+    ref = down(q8.gemv(xd, wd)).copy()
+    _, y64, mag = oracle.gemv(w, x, n, p)
+    parity(ref, y64, mag, "gemv %dx%d" % (n, p))
+    y = torch.empty(p, dtype=torch.float32, device="cuda")
+    for c in (1, 2, 4):
+        for waves in (1, 2, 4):
             y.fill_(float("nan"))
-        one.run(mode)
-        q8.stream_wait(timeout_ms=60_000)
-        for i, y in enumerate(outs):
-            assert np.array_equal(down(y).view(np.uint32), ref[i].view(np.uint32)), (mode, i)
-    one.check()
-    for i, (n, p) in enumerate(SPLIT_SHAPES):
-        _, y64, mag = oracle.gemv(ws[i], xs[i], n, p)
-        parity(ref[i], y64, mag, "one-launch op %d (%d x %d)" % (i, n, p))
-    x_in = ref[1]
-    for k, ((n, p), w) in enumerate(zip(dep_shapes, dep_w)):
-        _, y64, mag = oracle.gemv(w, x_in, n, p)
-        got = ref[len(SPLIT_SHAPES) + k]
-        parity(got, y64, mag, "one-launch dependent op %d" % k)
-        x_in = got
-    one.close()
-    ref_chain.close()
+            q8.gemv(xd, wd, y, shape=(c, waves))
+            assert np.array_equal(down(y).view(np.uint32), ref.view(np.uint32)), (c, waves)
 
 
-def test_one_launch_reread(q8):
-    """A one-launch chain whose last phase reads memory that its first phase
-    read and its second rewrote: u -> v, v -> u, u -> r (the barrier before
-    the third phase takes the per-wave acquire).  Replayed as a recurrence,
-    each replay checked against the oracle on the u it started from."""
+def test_shaped_refuses_other_widths(q8):
+    """An explicit launch shape needs n % 256 == 0 and lanes/waves in {1,2,4}."""
     import torch
-    log("one-launch reread")
-    rng = np.random.default_rng(92)
-    n = 1024
-    wp, wq, wr = (synth.q8_weights(n, 3072, rng), synth.q8_weights(3072, n, rng), synth.q8_weights(n, 512, rng))
-    u = up(synth.activations(n, rng))
-    v = torch.full((3072,), float("nan"), dtype=torch.float32, device="cuda")
-    r = torch.full((512,), float("nan"), dtype=torch.float32, device="cuda")
-    ch = q8.Chain([(u, w_dev(wp, n, 3072), v), (v, w_dev(wq, 3072, n), u), (u, w_dev(wr, n, 512), r)],
-                  one_launch=True)
-    assert ch.launches == 1
-    for mode in (q8.MODE_GRAPH, q8.MODE_EAGER, q8.MODE_GRAPH):
-        u0 = down(u).copy()
-        ch.run(mode)
-        q8.stream_wait(timeout_ms=60_000)
-        vh, uh, rh = down(v).copy(), down(u).copy(), down(r).copy()
-        _, y64, mag = oracle.gemv(wp, u0, n, 3072)
-        parity(vh, y64, mag, "reread P")
-        _, y64, mag = oracle.gemv(wq, vh, 3072, n)
-        parity(uh, y64, mag, "reread Q")
-        _, y64, mag = oracle.gemv(wr, uh, n, 512)
-        parity(rh, y64, mag, "reread R")
-        u.mul_(1.0 / max(1e-30, float(np.sqrt(np.mean(uh.astype(np.float64) ** 2)))))   # keep u O(1)
-    ch.check()
-    ch.close()
+    w = w_dev(synth.q8_weights(896, 8, np.random.default_rng(3)), 896, 8)
+    x = torch.zeros(896, dtype=torch.float32, device="cuda")
+    with pytest.raises(q8.Q8Error) as ei:
+        q8.gemv(x, w, shape=(4, 4))
+    assert ei.value.code == q8.Q8_ERR_SHAPE
+    w = w_dev(synth.q8_weights(1024, 8, np.random.default_rng(3)), 1024, 8)
+    x = torch.zeros(1024, dtype=torch.float32, device="cuda")
+    with pytest.raises(q8.Q8Error) as ei:
+        q8.gemv(x, w, shape=(3, 1))
+    assert ei.value.code == q8.Q8_ERR_INVALID_ARG
 
 
 def test_stream_wait_timeout_and_ok(q8):
-    """A bounded wait returns OK on an idle stream."""
+    """A bounded wait returns OK on an idle stream; with about 10 ms of
+    matvecs queued (40 launches over 72 MB of weights) a wait of 0 ms returns
+    Q8_ERR_TIMEOUT without cancelling anything, and an unbounded wait then
+    returns OK once they have run (the last output checked)."""
     import torch
     torch.cuda.synchronize()
     assert q8.stream_wait(timeout_ms=1000) == 0
+    n, p = 18944, 3584
+    rng = np.random.default_rng(12)
+    w = synth.q8_weights(n, p, rng)
+    x = synth.activations(n, rng)
+    wd, xd = w_dev(w, n, p), up(x)
+    y = torch.empty(p, dtype=torch.float32, device="cuda")
+    q8.gemv(xd, wd, y)
+    torch.cuda.synchronize()
+    ref = down(y).copy()
+    for _ in range(40):
+        q8.gemv(xd, wd, y)
+    with pytest.raises(q8.Q8Error) as ei:
+        q8.stream_wait(timeout_ms=0)
+    assert ei.value.code == q8.Q8_ERR_TIMEOUT
+    assert q8.stream_wait(timeout_ms=-1) == 0
+    assert np.array_equal(down(y).view(np.uint32), ref.view(np.uint32))
 
 
-def test_widest_rows(q8, monkeypatch):
+def test_widest_rows(q8):
     """n at its maximum (2**20 columns, 32768 blocks, 1.1 MB per row): the
-    matvec, the small batch on the matrix cores (m = 16) and on the vector
-    units (m = 2 over rows and block pairs, m = 3 a lane per row), every
-    output against the oracle."""
+    matvec (on every launch shape: the same bits), the small batch on the
+    matrix cores (m = 16) and on the vector units (m = 2 over rows and block
+    pairs, m = 3 a lane per row), every output against the oracle."""
     import torch
     n, p = 1 << 20, 67
     log("widest rows n=%d p=%d" % (n, p))
@@ -527,15 +508,15 @@ def test_widest_rows(q8, monkeypatch):
     y = torch.full((p,), float("nan"), dtype=torch.float32, device="cuda")
     q8.gemv(up(x), wd, y)
     _, y64, mag = oracle.gemv(w, x, n, p)
-    parity(down(y), y64, mag, "gemv widest")
-    for m, path in ((16, None), (2, None), (3, "valu")):
-        if path:
-            monkeypatch.setenv("Q8GEMV_SMALLM_PATH", path)
-        else:
-            monkeypatch.delenv("Q8GEMV_SMALLM_PATH", raising=False)
+    ref = down(y).copy()
+    parity(ref, y64, mag, "gemv widest")
+    for c, waves in ((1, 1), (4, 4), (2, 2)):
+        q8.gemv(up(x), wd, y, shape=(c, waves))
+        assert np.array_equal(down(y).view(np.uint32), ref.view(np.uint32)), (c, waves)
+    for m, kernel in ((16, None), (2, None), (3, q8.SMALLM_VALU)):
         X = synth.activations(n, rng, m)
         Y = torch.full((m, p), float("nan"), dtype=torch.float32, device="cuda")
-        q8.gemm_smallm(up(X), wd, Y)
+        q8.gemm_smallm(up(X), wd, Y, kernel=kernel)
         _, Y64, MAG = oracle.gemm(w, X, m, n, p)
         Yh = down(Y)
         for i in range(m):

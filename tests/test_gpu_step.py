@@ -34,6 +34,7 @@ import math
 import numpy as np
 import pytest
 
+import oracle
 import synth
 from oracle import decode_step as ods
 from tests.gpu_util import down, log, up
@@ -275,29 +276,18 @@ def _run_tokens(q8, st, mode, pos, token, count):
     return toks, logits, xs
 
 
-@pytest.mark.parametrize("one", ["0", "1"], ids=["per_run", "one_launch"])
-def test_step_launch_count(q8, monkeypatch, one):
-    log("step launches step_tiny one_launch=%s" % one)
-    monkeypatch.setenv("Q8GEMV_ONE_LAUNCH", one)
+def test_step_launch_count(q8):
+    log("step launches step_tiny")
     cfg, _, st = _step(q8, "step_tiny", 64)
-    if one == "1":
-        # embed+norm, layer 0's q|k|v; per layer attention (with the q/k
-        # norms, rotary embedding and cache append) and one launch of o,
-        # gate|up (adds and norms), down (reads silu(gate) * up) and the next
-        # layer's q|k|v (adds and norms) or the lm_head; argmax
-        assert st.launches == cfg["n_layers"] * 2 + 3
-    else:
-        # per layer: q|k|v (fused; from the second layer on it also adds the
-        # residual and norms), attention, o, gate|up (fused, adds and norms),
-        # down; then embed+norm, the lm_head (adds, norms), argmax
-        assert st.launches == cfg["n_layers"] * 5 + 1 + 2
+    # per layer: q|k|v (fused; from the second layer on it also adds the
+    # residual and norms), attention, o, gate|up (fused, adds and norms),
+    # down; then embed+norm, the lm_head (adds, norms), argmax
+    assert st.launches == cfg["n_layers"] * 5 + 1 + 2
     st.close()
 
 
-@pytest.mark.parametrize("one", ["0", "1"], ids=["per_run", "one_launch"])
-def test_step_graph_equals_eager(q8, monkeypatch, one):
-    log("step graph vs eager step_tiny one_launch=%s" % one)
-    monkeypatch.setenv("Q8GEMV_ONE_LAUNCH", one)
+def test_step_graph_equals_eager(q8):
+    log("step graph vs eager step_tiny")
     _, _, st = _step(q8, "step_tiny", 300)
     a = _run_tokens(q8, st, q8.MODE_EAGER, 0, 7, 6)
     kc_a = down(st.buffer("k_cache")).copy()
@@ -310,15 +300,14 @@ def test_step_graph_equals_eager(q8, monkeypatch, one):
         assert np.array_equal(xa, xb)
     assert np.array_equal(kc_a, kc_b)
     assert int(down(st.buffer("pos"))[0]) == 6
-    st.check()
     st.close()
 
 
 STEP_BAR = 1e-4
 
 
-def _compare_step(cfg, w, kc, vc, tok_in, pos, logits, x, tok_gpu, label):
-    tok_ref, y, y64, mag, x_ref = ods.decode_step(cfg, w, kc, vc, tok_in, pos)
+def _compare_step(cfg, w, kc, vc, tok_in, pos, logits, x, tok_gpu, label, matvec=None):
+    tok_ref, y, y64, mag, x_ref = ods.decode_step(cfg, w, kc, vc, tok_in, pos, matvec)
     rms = float(np.sqrt(np.mean(y64 * y64)))
     bar = STEP_BAR * (mag + rms)
     _check(logits, y64, bar, "%s logits pos %d" % (label, pos))
@@ -333,28 +322,14 @@ def _compare_step(cfg, w, kc, vc, tok_in, pos, logits, x, tok_gpu, label):
     return tok_gpu
 
 
-@pytest.mark.parametrize("name,max_seq,pos0,count,env", [
-    ("step_tiny", 64, 0, 5, ""), ("step_gqa4", 64, 0, 4, ""), ("step_gqa4", 1100, 1000, 3, ""),
-    ("step_hd192", 300, 126, 4, ""), ("step_hd256", 200, 0, 3, ""), ("step_hd256", 200, 127, 3, ""),
-    # the matvecs between two attentions as one launch (phases with 1-,
-    # 2-, 4- and 8-row super-rows, tail rows, every input mode); and every
-    # projection on the stream-K schedule (at these sizes the default keeps
-    # it for launches with more row tiles than CUs)
-    ("step_tiny", 64, 0, 5, "Q8GEMV_ONE_LAUNCH=1"), ("step_gqa4", 64, 0, 4, "Q8GEMV_ONE_LAUNCH=1"),
-    ("step_hd192", 300, 126, 4, "Q8GEMV_ONE_LAUNCH=1"), ("step_hd256", 200, 127, 3, "Q8GEMV_ONE_LAUNCH=1"),
-    ("step_tiny", 64, 0, 4, "Q8GEMV_STREAMK=2"), ("step_hd192", 300, 126, 3, "Q8GEMV_STREAMK=2"),
-], ids=str)
-def test_step_matches_oracle(q8, monkeypatch, name, max_seq, pos0, count, env):
-    for kv in filter(None, env.split(",")):
-        k, v = kv.split("=")
-        monkeypatch.setenv(k, v)
-    log("step vs oracle %s max_seq=%d pos0=%d env=%s" % (name, max_seq, pos0, env))
+def _step_vs_oracle(q8, name, max_seq, pos0, count, matvec=None):
     cfg, w, st = _step(q8, name, max_seq)
     kc, vc = _oracle_caches(cfg)
     toks, logits, xs = _run_tokens(q8, st, q8.MODE_GRAPH, pos0, 11, count)
     tok_in = 11
     for i in range(count):
-        _compare_step(cfg, w, kc, vc, tok_in, pos0 + i, logits[i], xs[i], toks[i], name)
+        log("  oracle %s token %d of %d" % (name, i + 1, count))
+        _compare_step(cfg, w, kc, vc, tok_in, pos0 + i, logits[i], xs[i], toks[i], name, matvec)
         tok_in = toks[i]    # teacher-forced on the GPU's token
     kvw = cfg["n_kv_heads"] * cfg["head_dim"]
     kc_gpu = down(st.buffer("k_cache")).reshape(cfg["n_layers"], max_seq, kvw)
@@ -363,8 +338,32 @@ def test_step_matches_oracle(q8, monkeypatch, name, max_seq, pos0, count, env):
         _check(kc_gpu[l, pos0:pos0 + count], ref,
                STEP_BAR * (np.abs(ref) + float(np.sqrt(np.mean(ref ** 2)))), "k cache layer %d" % l)
         assert not np.any(kc_gpu[l, :pos0]) and not np.any(kc_gpu[l, pos0 + count:])
-    st.check()
     st.close()
+
+
+@pytest.mark.parametrize("name,max_seq,pos0,count", [
+    ("step_tiny", 64, 0, 5), ("step_gqa4", 64, 0, 4), ("step_gqa4", 1100, 1000, 3),
+    ("step_hd192", 300, 126, 4), ("step_hd256", 200, 0, 3), ("step_hd256", 200, 127, 3),
+], ids=str)
+def test_step_matches_oracle(q8, name, max_seq, pos0, count):
+    log("step vs oracle %s max_seq=%d pos0=%d" % (name, max_seq, pos0))
+    _step_vs_oracle(q8, name, max_seq, pos0, count)
+
+
+@pytest.mark.parametrize("name,max_seq,pos0,count", [
+    ("qwen3_0.6b", 1024, 0, 2), ("qwen3_0.6b", 1024, 511, 2), ("7b", 64, 0, 1),
+], ids=str)
+def test_step_benchmarked_shapes(q8, name, max_seq, pos0, count):
+    """The step at the shapes the bench times (page "IV.4: One command buffer
+    per token", sections "The correctness ladder" and "Running it"): the
+    Qwen3-0.6B shape (28 layers, hidden 1024, 16 query heads on 8 KV heads,
+    vocabulary 151936) from position 0 and from 511, and the 7B-class shape
+    (hidden 3584, 28 on 4 heads, intermediate 18944) from 0, every logit and
+    the residual against the oracle step, whose matvecs run on host threads."""
+    import torch
+    log("step vs oracle %s max_seq=%d pos0=%d" % (name, max_seq, pos0))
+    _step_vs_oracle(q8, name, max_seq, pos0, count, matvec=oracle.gemv_threaded)
+    torch.cuda.empty_cache()
 
 
 def test_step_refuses_past_max_seq(q8):
