@@ -420,11 +420,12 @@ def main():
     achieved = nbytes / launches / kernel_s / 1e9
     # a chain of one op is that op's standalone launch (its latency plan);
     # more independent ops share one fused launch of one-wave tiles of 64
-    # rows.  Template arguments: lanes per row, waves per workgroup, input
-    # mode (0 float activations, 1 activations quantized to Q8_0)
+    # rows.  Template arguments: lanes per row, waves per workgroup, weight
+    # stages in LDS, build mode (0 float activations, 1 activations
+    # quantized to Q8_0)
     mode = 1 if args.xq else 0
-    kernel = ("k_q8_gemv_rc_fused<1,1,%d>" % mode if len(ops_shape) > 1
-              else "k_q8_gemv_rc<C,NWK,%d> (the op's latency plan)" % mode)
+    kernel = ("k_q8_gemv_rc_fused<1,1,2,%d>" % mode if len(ops_shape) > 1
+              else "k_q8_gemv_rc<C,NWK,NST,%d> (the op's latency plan)" % mode)
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                 "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                 "traffic": measured_traffic(args.workload, kernel),

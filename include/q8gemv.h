@@ -89,13 +89,16 @@ Q8_API int q8_0_gemv(const float *x, const void *w, float *y, int64_t n, int64_t
 /*
  * q8_0_gemv on an explicit launch shape, for n a multiple of 256 (else
  * Q8_ERR_SHAPE): lanes_per_row (1, 2 or 4) lanes share each row, so a wave
- * covers 64 / lanes_per_row rows, and `waves` (1, 2 or 4) waves per
- * workgroup split each row's groups.  The result is bitwise identical to
- * q8_0_gemv's for every shape; the shape only changes the launch (for
- * measurements and for tests of that identity).  Allocates nothing.
+ * covers 64 / lanes_per_row rows; `waves` (1, 2 or 4) waves per workgroup
+ * split each row's groups; each wave stages its weights in `stages` (1 or 2)
+ * LDS buffers of 17 KiB.  Shapes whose workgroup would need more than
+ * 160 KiB of LDS are refused (Q8_ERR_INVALID_ARG).  The result is bitwise
+ * identical to q8_0_gemv's for every shape; the shape only changes the
+ * launch (for measurements and for tests of that identity).  Allocates
+ * nothing.
  */
 Q8_API int q8_0_gemv_shaped(const float *x, const void *w, float *y, int64_t n, int64_t p,
-                            int lanes_per_row, int waves, void *stream);
+                            int lanes_per_row, int waves, int stages, void *stream);
 
 /*
  * Y = X W^T for m in 1..16 activation rows in one pass over W: the small-batch

@@ -7,7 +7,7 @@ implementation: if the library is missing, importing this package raises.
 
 The names follow the C ABI:
     gemv(x, w, y=None, stream=None)            -> q8_0_gemv
-    gemv(x, w, shape=(c, waves))               -> q8_0_gemv_shaped
+    gemv(x, w, shape=(c, waves, stages))       -> q8_0_gemv_shaped
     gemm_smallm(X, w, Y=None, stream=None)     -> q8_0_gemm_smallm
     gemm_smallm(X, w, kernel=SMALLM_MFMA)      -> q8_0_gemm_smallm_kernel
     gemv_q8q8(x, w, y=None), quantize(x)       -> q8_0_gemv_q8q8, q8_0_quantize
@@ -103,7 +103,7 @@ def _load():
     lib = ctypes.CDLL(LIBRARY)
     vp, i64 = ctypes.c_void_p, ctypes.c_int64
     lib.q8_0_gemv.argtypes = [vp, vp, vp, i64, i64, vp]
-    lib.q8_0_gemv_shaped.argtypes = [vp, vp, vp, i64, i64, ctypes.c_int, ctypes.c_int, vp]
+    lib.q8_0_gemv_shaped.argtypes = [vp, vp, vp, i64, i64, ctypes.c_int, ctypes.c_int, ctypes.c_int, vp]
     lib.q8_0_gemm_smallm.argtypes = [vp, vp, vp, i64, i64, i64, vp]
     lib.q8_0_gemm_smallm_kernel.argtypes = [vp, vp, vp, i64, i64, i64, ctypes.c_int, vp]
     lib.q8_0_chain_create.argtypes = [ctypes.POINTER(Q8Op), i64, ctypes.c_uint32,
@@ -202,7 +202,7 @@ def weight_shape(w) -> Tuple[int, int]:
 def gemv(x, w, y=None, stream=None, shape=None):
     """y = W x.  x float32 (n,), w uint8 (p, n/32*34); returns y float32 (p,).
 
-    shape=(lanes_per_row, waves) launches on that explicit shape
+    shape=(lanes_per_row, waves, stages) launches on that explicit shape
     (q8_0_gemv_shaped, n a multiple of 256): the same bits, another launch."""
     torch = _torch()
     _need(x, torch.float32, "x")
@@ -218,9 +218,9 @@ def gemv(x, w, y=None, stream=None, shape=None):
     if shape is None:
         check(lib.q8_0_gemv(x.data_ptr(), w.data_ptr(), y.data_ptr(), n, p, _stream_handle(stream)))
     else:
-        c, waves = shape
+        c, waves, stages = shape
         check(lib.q8_0_gemv_shaped(x.data_ptr(), w.data_ptr(), y.data_ptr(), n, p, int(c), int(waves),
-                                   _stream_handle(stream)))
+                                   int(stages), _stream_handle(stream)))
     return y
 
 

@@ -1,7 +1,7 @@
 """Build the HIP library in-tree: q8_block_quantized_gemv_amd/libq8gemv.so.
 
 gfx950 only; packed FP32 instructions are switched off in device code.  Each
-source (and each activation mode of q8_gemv_rc.hip) compiles to an object of
+source (and each build mode of q8_gemv_rc.hip) compiles to an object of
 its own, in parallel, under _build/; the objects are then linked.
 """
 from __future__ import annotations
@@ -20,7 +20,7 @@ HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 # (source, extra flags, object name)
 UNITS = [("q8_gemv.hip", (), "q8_gemv")] + \
-        [("q8_gemv_rc.hip", ("-DQ8_RC_XMODE=%d" % m,), "q8_gemv_rc_%d" % m) for m in range(4)] + \
+        [("q8_gemv_rc.hip", ("-DQ8_RC_MODE=%d" % m,), "q8_gemv_rc_%d" % m) for m in range(7)] + \
         [("q8_gemm.hip", (), "q8_gemm"), ("q8_step.hip", (), "q8_step"),
          ("q8_api.hip", (), "q8_api"), ("q8_step_api.hip", (), "q8_step_api")]
 SOURCES = sorted({os.path.join(CSRC, u[0]) for u in UNITS})

@@ -221,35 +221,42 @@ int64_t tiles_of(const OpDesc &d, int nw) {
 // Launch shape of the rows-and-group-slots kernel for a launch that waits
 // on the one before it: `rows` rows of G groups (one op, or independent ops
 // of one width) read in mode xmode, on `cus` CUs.  From a sweep of lone
-// launches at the decode shapes (0.6B and 7B projections, lm_heads):
+// launches at the decode shapes (0.6B and 7B projections, lm_heads, in each
+// input mode):
 //  * tiles of 16 rows (C = 4) with the groups split over NWK waves by slot,
 //    as many waves as there are group columns (up to 4), when one wave of
 //    such workgroups covers the rows (a row-poor op: every wave then streams
 //    its columns at once, e.g. 7B q/o/down, every 0.6B projection);
 //  * tiles of 32 rows with four waves when that still fits (7B q|k|v);
 //  * otherwise one-wave tiles of 16 rows if they are all resident at once
-//    (7B gate), else two-wave tiles (7B gate|up, lm_heads: fewer columns per
-//    wave shortens the last wave of tiles).
-RcShape plan_rc_latency(int64_t rows, int64_t G, int xmode, int64_t cus) {
+//    (7B gate), else two-wave tiles (lm_heads: fewer columns per wave
+//    shortens the last wave of tiles) -- except where every workgroup first
+//    sums the squares of x + x_res over the whole row (kXNormAdd), and for
+//    the gate|up pair (kYSwiGLU, two waves per tile already): there
+//    one-wave tiles of 32 rows, half the workgroups, are fastest.
+// One W stage per wave: twice the waves fit, which measured faster than a
+// second stage at every one of these shapes.
+RcShape plan_rc_latency(int64_t rows, int64_t G, int xmode, int ymode, int64_t cus) {
     auto resident = [&](RcShape sh) {
-        const int b = gemv_rc_lds_bytes(sh, xmode);
+        const int b = gemv_rc_lds_bytes(sh, xmode, ymode);
         return b > 0 ? cus * std::max(1, kLdsPerCu / b) : 0;
     };
     const int64_t J4 = (G + 3) / 4;
     const int n4 = J4 >= 3 ? 4 : (int)J4;
     const int64_t t4 = (rows + 15) / 16;
-    if (t4 <= resident({4, n4})) return {4, n4};
-    if ((G + 1) / 2 >= 4 && (rows + 31) / 32 <= resident({2, 4})) return {2, 4};
-    if (t4 <= resident({4, 1})) return {4, 1};
-    return {4, J4 >= 2 ? 2 : 1};
+    if (t4 <= resident({4, n4, 1})) return {4, n4, 1};
+    if ((G + 1) / 2 >= 4 && (rows + 31) / 32 <= resident({2, 4, 1})) return {2, 4, 1};
+    if (xmode == kXNormAdd || ymode == kYSwiGLU) return {2, 1, 1};
+    if (t4 <= resident({4, 1, 1})) return {4, 1, 1};
+    return {4, J4 >= 2 ? 2 : 1, 1};
 }
 
 // Launch shape of a fused launch of independent ops (a throughput launch):
-// one-wave tiles of 64 rows, the steady-state layout.
-constexpr RcShape kFuseShape{1, 1};
+// one-wave tiles of 64 rows with two W stages, the steady-state layout.
+constexpr RcShape kFuseShape{1, 1, 2};
 
-bool shape_ok(int c, int nwk) {
-    return (c == 1 || c == 2 || c == 4) && (nwk == 1 || nwk == 2 || nwk == 4);
+bool shape_ok(int c, int nwk, int nst) {
+    return (c == 1 || c == 2 || c == 4) && (nwk == 1 || nwk == 2 || nwk == 4) && (nst == 1 || nst == 2);
 }
 
 // One matvec: rs == 1 on the rows-and-group-slots kernel in `sh` (or its
@@ -261,7 +268,7 @@ int gemv_launch(const float *x, const void *w, float *y, int64_t n, int64_t p, h
     if (e != hipSuccess) return fail_hip(e, "hipGetDevice");
     OpDesc d = plan_op(x, w, y, 1, n, p, true, kWaves);
     if (d.rs == 1) {
-        if (sh.c == 0) sh = plan_rc_latency(p, d.gsr, xmode, cu_count(dev));
+        if (sh.c == 0) sh = plan_rc_latency(p, d.gsr, xmode, kYPlain, cu_count(dev));
         e = launch_gemv_rc(d, sh, rc_tiles_for(p, sh.c), s, xmode);
     } else {
         e = launch_gemv_single(d, Variant{kWaves, 1}, tiles_of(d, kWaves), s, xmode);
@@ -399,27 +406,28 @@ int q8_0_gemv(const float *x, const void *w, float *y, int64_t n, int64_t p, voi
     int rc = validate(x, w, y, 1, n, p, "q8_0_gemv");
     if (rc) return rc;
     if ((rc = check_device())) return rc;
-    return gemv_launch(x, w, y, n, p, (hipStream_t)stream, kXFloat, RcShape{0, 0}, "q8_0_gemv launch");
+    return gemv_launch(x, w, y, n, p, (hipStream_t)stream, kXFloat, RcShape{0, 0, 0}, "q8_0_gemv launch");
 }
 
 int q8_0_gemv_shaped(const float *x, const void *w, float *y, int64_t n, int64_t p, int lanes_per_row,
-                     int waves, void *stream) {
+                     int waves, int stages, void *stream) {
     int rc = validate(x, w, y, 1, n, p, "q8_0_gemv_shaped");
     if (rc) return rc;
-    if (!shape_ok(lanes_per_row, waves))
-        return fail(Q8_ERR_INVALID_ARG, "q8_0_gemv_shaped: lanes_per_row and waves must each be 1, 2 or 4");
+    const RcShape sh{lanes_per_row, waves, stages};
+    if (!shape_ok(lanes_per_row, waves, stages) || gemv_rc_lds_bytes(sh, kXFloat) == 0)
+        return fail(Q8_ERR_INVALID_ARG, "q8_0_gemv_shaped: lanes_per_row and waves must each be 1, 2 or 4, "
+                                        "stages 1 or 2, and the workgroup's LDS must fit in 160 KiB");
     if (n % (kQuants * kGroupBlocks))
         return fail(Q8_ERR_SHAPE, "q8_0_gemv_shaped: n must be a multiple of 256 for an explicit launch shape");
     if ((rc = check_device())) return rc;
-    return gemv_launch(x, w, y, n, p, (hipStream_t)stream, kXFloat, RcShape{lanes_per_row, waves},
-                       "q8_0_gemv_shaped launch");
+    return gemv_launch(x, w, y, n, p, (hipStream_t)stream, kXFloat, sh, "q8_0_gemv_shaped launch");
 }
 
 int q8_0_gemv_q8q8(const float *x, const void *w, float *y, int64_t n, int64_t p, void *stream) {
     int rc = validate(x, w, y, 1, n, p, "q8_0_gemv_q8q8");
     if (rc) return rc;
     if ((rc = check_device())) return rc;
-    return gemv_launch(x, w, y, n, p, (hipStream_t)stream, kXQuant, RcShape{0, 0}, "q8_0_gemv_q8q8 launch");
+    return gemv_launch(x, w, y, n, p, (hipStream_t)stream, kXQuant, RcShape{0, 0, 0}, "q8_0_gemv_q8q8 launch");
 }
 
 int q8_0_quantize(const float *x, void *xq, int64_t n, void *stream) {
@@ -451,7 +459,7 @@ int q8_0_gemm_smallm_kernel(const float *X, const void *w, float *Y, int64_t m, 
     if ((rc = check_device())) return rc;
     hipStream_t s = (hipStream_t)stream;
     if (m == 1)
-        return gemv_launch(X, w, Y, n, p, s, kXFloat, RcShape{0, 0}, "q8_0_gemm_smallm launch");
+        return gemv_launch(X, w, Y, n, p, s, kXFloat, RcShape{0, 0, 0}, "q8_0_gemm_smallm launch");
     // m = 2..3 with rows of one super-row (n a multiple of 256) run on the
     // vector units with lanes over (row, block pair): each lane holds the x
     // values of its two blocks in registers, the quants are converted once
@@ -469,7 +477,7 @@ int q8_0_gemm_smallm_kernel(const float *X, const void *w, float *Y, int64_t m, 
     // vector units: one pass over W per kValuMaxM rows of X
     for (int64_t i0 = 0; i0 < m; i0 += kValuMaxM) {
         const int64_t mi = std::min<int64_t>(kValuMaxM, m - i0);
-        rc = mi == 1 ? gemv_launch(X + i0 * n, w, Y + i0 * p, n, p, s, kXFloat, RcShape{0, 0},
+        rc = mi == 1 ? gemv_launch(X + i0 * n, w, Y + i0 * p, n, p, s, kXFloat, RcShape{0, 0, 0},
                                    "q8_0_gemm_smallm launch")
                      : smallm_valu(X + i0 * n, w, Y + i0 * p, mi, n, p, s);
         if (rc) return rc;
@@ -509,6 +517,7 @@ struct q8_0_chain {
     struct Launch {
         enum Kind { kSingleRc, kSingleSuperrow, kFusedRc, kFusedMixed } kind;
         int xmode;            // XMode: how the activations are read
+        int ymode;            // YMode: what is written
         RcShape shape;        // kSingleRc, kFusedRc
         OpDesc single;        // single-op launches
         const OpDesc *d_ops;  // fused launches: op table and tiles
@@ -526,10 +535,11 @@ namespace {
 
 hipError_t issue(const q8_0_chain::Launch &L, hipStream_t s) {
     switch (L.kind) {
-        case q8_0_chain::Launch::kSingleRc: return launch_gemv_rc(L.single, L.shape, L.grid, s, L.xmode);
+        case q8_0_chain::Launch::kSingleRc: return launch_gemv_rc(L.single, L.shape, L.grid, s, L.xmode, L.ymode);
         case q8_0_chain::Launch::kSingleSuperrow:
             return launch_gemv_single(L.single, Variant{kWaves, 1}, L.grid, s, L.xmode);
-        case q8_0_chain::Launch::kFusedRc: return launch_gemv_rc_fused(L.d_ops, L.d_tiles, L.shape, L.grid, s, L.xmode);
+        case q8_0_chain::Launch::kFusedRc:
+            return launch_gemv_rc_fused(L.d_ops, L.d_tiles, L.shape, L.grid, s, L.xmode, L.ymode);
         case q8_0_chain::Launch::kFusedMixed: return launch_gemv_fused(L.d_ops, L.d_tiles, Variant{1, 1}, L.grid, s, L.xmode);
     }
     return hipErrorInvalidValue;
@@ -546,11 +556,11 @@ void chain_free(q8_0_chain *c) {
 
 // The memory an op reads and writes, as (pointer, bytes) ranges.
 struct Ranges {
-    const void *r[5];
-    int64_t rn[5];
+    const void *r[7];
+    int64_t rn[7];
     int nr = 0;
-    const void *w[2];
-    int64_t wn[2];
+    const void *w[3];
+    int64_t wn[3];
     int nw = 0;
 };
 
@@ -563,9 +573,13 @@ Ranges ranges_of(const q8_0_op &o, const OpExtra *e) {
     wr(o.y, 4 * o.p);
     if (e) {
         rd(e->x_up, 4 * o.n);
-        rd(e->x_res, 4 * o.n);
-        rd(e->norm_w, 4 * o.n);
-        wr(e->x_out, 4 * o.n);
+        const int64_t en = 4 * (e->out_mode == kYResAdd ? o.p : o.n);   // residual vectors are outputs' length
+        rd(e->x_res, en);
+        rd(e->norm_w, en);
+        wr(e->x_out, en);
+        rd(e->w2, w_bytes(o.n, o.p));
+        if (e->out_mode == kYResAdd) wr(e->psum, 4 * (o.p / kPsumRows));
+        else if (e->mode == kXNormScale) rd(e->psum, 4 * (o.n / kPsumRows));
     }
     return g;
 }
@@ -594,6 +608,9 @@ void set_extra(OpDesc &d, const OpExtra *e) {
     d.norm_w = e->norm_w;
     d.x_out = e->x_out;
     d.norm_eps = e->eps;
+    d.psum = e->psum;
+    d.psum_n = e->mode == kXNormScale ? (int32_t)(d.nb * kQuants / kPsumRows) : 0;
+    d.w2 = (const uint8_t *)e->w2;
 }
 
 }  // namespace
@@ -640,25 +657,45 @@ int q8::chain_create_ex(const q8_0_op *ops, int64_t n_ops, uint32_t flags, const
     if (flags & ~(uint32_t)(Q8_CHAIN_PER_OP | Q8_CHAIN_SPLIT_K | Q8_CHAIN_XQ))
         return fail(Q8_ERR_INVALID_ARG, "q8_0_chain_create: unknown flags");
     const int emode = extra ? extra[0].mode : kXFloat;
+    const int eout = extra ? extra[0].out_mode : kYPlain;
     if (extra && (flags & Q8_CHAIN_XQ))
         return fail(Q8_ERR_INVALID_ARG, "q8_0_chain_create: these inputs have no integer form");
     auto a16 = [](const void *p) { return p && ((uintptr_t)p & 15u) == 0; };
+    auto a4 = [](const void *p) { return p && ((uintptr_t)p & 3u) == 0; };
     for (int64_t i = 0; i < n_ops; ++i) {
         const std::string what = "q8_0_chain_create op " + std::to_string(i);
         int rc = validate(ops[i].x, ops[i].w, ops[i].y, 1, ops[i].n, ops[i].p, what.c_str());
         if (rc) return rc;
         if (!extra) continue;
         const OpExtra &e = extra[i];
-        const int64_t xb = 4 * ops[i].n, yb = 4 * ops[i].p;
-        bool ok = e.mode == emode;
+        const int64_t n = ops[i].n, p = ops[i].p, xb = 4 * n, yb = 4 * p;
+        const bool whole = n % (kQuants * kGroupBlocks) == 0;   // rows of whole groups
+        bool ok = e.mode == emode && e.out_mode == eout;
         if (e.mode == kXSiluUp) ok = ok && a16(e.x_up) && !overlaps(ops[i].y, yb, e.x_up, xb);
         else if (e.mode == kXNormAdd)   // (the writer of x_out needs a fast tile: p >= 8)
-            ok = ok && a16(e.x_res) && a16(e.norm_w) && (!e.x_out || (a16(e.x_out) && ops[i].p >= 8)) &&
+            ok = ok && a16(e.x_res) && a16(e.norm_w) && (!e.x_out || (a16(e.x_out) && p >= 8)) &&
                  !overlaps(ops[i].y, yb, e.x_res, xb) &&
                  !(e.x_out && (overlaps(e.x_out, xb, ops[i].x, xb) || overlaps(e.x_out, xb, e.x_res, xb) ||
                                overlaps(e.x_out, xb, ops[i].y, yb)));
-        else ok = false;
-        if (!ok) return fail(Q8_ERR_INVALID_ARG, what + ": extra inputs missing, misaligned or aliased");
+        else if (e.mode == kXNormScale)
+            ok = ok && whole && a16(e.psum) && !overlaps(ops[i].y, yb, e.psum, 4 * (n / kPsumRows));
+        else ok = ok && e.mode == kXFloat;
+        if (e.out_mode == kYResAdd) {
+            const int64_t sb = 4 * (p / kPsumRows);
+            ok = ok && whole && p % kPsumRows == 0 && a4(e.x_res) && a4(e.psum) && e.mode == kXFloat &&
+                 !overlaps(ops[i].y, yb, e.x_res, yb) && !overlaps(e.psum, sb, ops[i].y, yb) &&
+                 !overlaps(e.psum, sb, ops[i].x, xb) && !overlaps(e.psum, sb, e.x_res, yb) &&
+                 (!e.x_out == !e.norm_w) &&
+                 !(e.x_out && (!a4(e.x_out) || !a4(e.norm_w) || overlaps(e.x_out, yb, ops[i].x, xb) ||
+                               overlaps(e.x_out, yb, ops[i].y, yb) || overlaps(e.x_out, yb, e.x_res, yb) ||
+                               overlaps(e.x_out, yb, e.psum, sb)));
+        }
+        else if (e.out_mode == kYSwiGLU)
+            ok = ok && whole && a16(e.w2) && (e.mode == kXFloat || e.mode == kXNormScale) &&
+                 !overlaps(ops[i].y, yb, e.w2, w_bytes(n, p));
+        else ok = ok && e.out_mode == kYPlain;
+        if (!ok) return fail(Q8_ERR_INVALID_ARG, what + ": extra inputs missing, misaligned, aliased or not "
+                                                        "supported for this width");
     }
     int dev = 0;
     int rc = check_device(&dev);
@@ -669,6 +706,7 @@ int q8::chain_create_ex(const q8_0_op *ops, int64_t n_ops, uint32_t flags, const
     c->flags = flags;
     c->ops.assign(ops, ops + n_ops);
     const int xmode = (flags & Q8_CHAIN_XQ) ? kXQuant : emode;
+    const int ymode = eout;
     const bool per_op = (flags & Q8_CHAIN_PER_OP) != 0;
     const bool latency = (flags & Q8_CHAIN_SPLIT_K) != 0;
     const int64_t cus = cu_count(dev);
@@ -688,6 +726,7 @@ int q8::chain_create_ex(const q8_0_op *ops, int64_t n_ops, uint32_t flags, const
         SegInfo si;
         std::memset(&si, 0, sizeof si);
         si.L.xmode = xmode;
+        si.L.ymode = ymode;
         si.op0 = h_ops.size();
         si.tile0 = h_tiles.size();
         const auto ex = [&](int64_t i) { return extra ? &extra[i] : nullptr; };
@@ -699,7 +738,7 @@ int q8::chain_create_ex(const q8_0_op *ops, int64_t n_ops, uint32_t flags, const
             si.L.single = d;
             if (d.rs == 1) {
                 si.L.kind = q8_0_chain::Launch::kSingleRc;
-                si.L.shape = plan_rc_latency(d.p, d.gsr, xmode, cus);
+                si.L.shape = plan_rc_latency(d.p, d.gsr, xmode, ymode, cus);
                 si.L.grid = rc_tiles_for(d.p, si.L.shape.c);
             } else {
                 si.L.kind = q8_0_chain::Launch::kSingleSuperrow;
@@ -722,7 +761,7 @@ int q8::chain_create_ex(const q8_0_op *ops, int64_t n_ops, uint32_t flags, const
             // the steady-state one-wave tiles, largest tiles first so that
             // the smallest finish the launch
             const RcShape sh = latency && one_width
-                                   ? plan_rc_latency(rows, ops[sg.first].n / (kQuants * kGroupBlocks), xmode, cus)
+                                   ? plan_rc_latency(rows, ops[sg.first].n / (kQuants * kGroupBlocks), xmode, ymode, cus)
                                    : kFuseShape;
             struct Item { Tile t; int64_t bytes; };
             std::vector<Item> items;
@@ -745,7 +784,11 @@ int q8::chain_create_ex(const q8_0_op *ops, int64_t n_ops, uint32_t flags, const
             si.L.grid = (int64_t)items.size();
         } else {
             // widths that are not all multiples of 256: one-wave workgroups,
-            // each tile in its own layout, largest tiles first
+            // each tile in its own layout, largest tiles first (plain output)
+            if (ymode != kYPlain) {
+                chain_free(c);
+                return fail(Q8_ERR_INVALID_ARG, "q8_0_chain_create: output modes need n % 256 == 0");
+            }
             struct Item { Tile t; int64_t bytes; };
             std::vector<Item> items;
             for (int64_t i = sg.first; i < sg.second; ++i) {

@@ -26,16 +26,22 @@ Q8_HIDDEN int cu_count(int dev);
 // stream s on device dev, kept across calls (grown when too small).
 Q8_HIDDEN int workspace_for(int dev, hipStream_t s, size_t ws_bytes, size_t cnt_n, float **ws_out,
                             uint32_t **cnt_out);
-// Per-op inputs of the decode step's chains (internal): how the op reads its
-// activations (XMode) and the extra vectors that takes, n floats each,
-// 16-byte aligned.
+// Per-op inputs and outputs of the decode step's chains (internal): how
+// the op reads its activations (XMode) and writes its result (YMode), and
+// the extra vectors those take (n floats each for the inputs, 16-byte
+// aligned).  Every op of one chain reads and writes in the same modes.
 struct OpExtra {
-    int mode = 0;                  // kXSiluUp or kXNormAdd, the same for every op of a chain
+    int mode = 0;                  // XMode: kXSiluUp, kXNormAdd or kXNormScale (kXFloat: none)
+    int out_mode = 0;              // YMode: kYResAdd or kYSwiGLU (kYPlain: none)
     const float *x_up = nullptr;   // kXSiluUp: input silu(x) * x_up
-    const float *x_res = nullptr;  // kXNormAdd: input rms_norm(x + x_res) * norm_w
-    const float *norm_w = nullptr;
-    float *x_out = nullptr;        // kXNormAdd: x + x_res written here (may be null)
-    float eps = 0.f;
+    const float *x_res = nullptr;  // kXNormAdd: input rms_norm(x + x_res) * norm_w;
+                                   // kYResAdd: output x_res + W x (p floats)
+    const float *norm_w = nullptr; // kXNormAdd: the gain (n floats); kYResAdd: the gain for x_out (p)
+    float *x_out = nullptr;        // kXNormAdd: x + x_res written here; kYResAdd: y * norm_w (may be null)
+    float eps = 0.f;               // kXNormAdd, kXNormScale
+    float *psum = nullptr;         // kYResAdd: p/16 block sums of y^2 out; kXNormScale: n/16 in
+                                   // (kXNormScale: x is the producer's x_out, gain already applied)
+    const void *w2 = nullptr;      // kYSwiGLU: the up matrix (as w); y = silu(W x) * (W2 x)
 };
 // q8_0_chain_create with per-op extras (null: plain ops).
 Q8_HIDDEN int chain_create_ex(const q8_0_op *ops, int64_t n_ops, uint32_t flags,

@@ -61,7 +61,16 @@ struct OpDesc {
     const float *norm_w;
     float *x_out;        // may be null
     float norm_eps;
-    int32_t pad1_;
+    // kXNormScale: x holds v * g (a gain applied by the producer) and the
+    // input is x * inv, inv = 1 / sqrt(ss / n + norm_eps), ss the sum of the
+    // psum_n floats at psum (the block sums of v^2, as kYResAdd writes them);
+    // inv scales each row result.
+    // kYResAdd: y = x_res + W x, psum[row / 16] = sum of y^2 over each
+    // 16-row block, and (x_out not null) x_out = y * norm_w, p floats.
+    // kYSwiGLU: rows of w2 too; y = silu(W x) * (W2 x).
+    int32_t psum_n;
+    float *psum;
+    const uint8_t *w2;
 };
 
 // How a matvec reads its activations (a compile-time mode of the kernels).
@@ -70,7 +79,16 @@ enum XMode : int {
     kXQuant = 1,    // x quantized to Q8_0 per group, integer dots
     kXSiluUp = 2,   // silu(x) * x_up formed per group (the SwiGLU product feeding a down projection)
     kXNormAdd = 3,  // rms_norm(x + x_res) * norm_w formed per group (a residual add and the norm after it)
+    kXNormScale = 4,  // x * inv, x gain-scaled by the producer, inv from the block sums it left in psum
 };
+// What a matvec writes (a compile-time mode of the rows-and-group-slots kernel).
+enum YMode : int {
+    kYPlain = 0,    // y = W x
+    kYResAdd = 1,   // y = x_res + W x, 16-row block sums of y^2 in psum, y * norm_w in x_out (a residual add)
+    kYSwiGLU = 2,   // y = silu(W x) * (W2 x): gate and up rows computed together
+};
+// Rows per block of the squared-norm partial sums (kYResAdd / kXNormScale).
+constexpr int kPsumRows = 16;
 // rs > 1: every row sums its groups into kSlots partial sums (group kk into
 // slot kk % kSlots, in increasing kk) and combines them as
 // (s0 + s1) + (s2 + s3).
@@ -96,12 +114,13 @@ struct Variant {
 };
 
 // Shape of a launch of the rs == 1 kernel: C lanes per row (1, 2 or 4) so a
-// wave covers 64 / C rows, and NWK waves per workgroup (1, 2 or 4) that
-// share a tile's rows and split its groups by slot (wave w takes the group
-// columns j = w, w + NWK, ...).
+// wave covers 64 / C rows, NWK waves per workgroup (1, 2 or 4) that share a
+// tile's rows and split its groups by slot (wave w takes the group columns
+// j = w, w + NWK, ...), and NST W stages per wave (1 or 2).
 struct RcShape {
     int c;
     int nwk;
+    int nst;
 };
 
 // rs > 1: fast tiles cover (nw / ks) * 64 super-rows each.
@@ -125,13 +144,24 @@ inline int64_t rc_tiles_for(int64_t p, int c) {
 hipError_t launch_gemv_single(const OpDesc &op, const Variant &v, int64_t grid, hipStream_t s,
                               int xmode = kXFloat);
 // A table of tiles of independent ops of any width, on one-wave workgroups
-// (v = {1, 1}): rs == 1 tiles in RcShape {1, 1}, the others as super-rows.
+// (v = {1, 1}): rs == 1 tiles in RcShape {1, 1, 2}, the others as super-rows.
 hipError_t launch_gemv_fused(const OpDesc *d_ops, const Tile *d_tiles, const Variant &v,
                              int64_t grid, hipStream_t s, int xmode = kXFloat);
-// rs == 1 ops (q8_gemv_rc.hip, built once per mode M: the entry points
-// below with the mode's number appended).  One op: grid =
+// rs == 1 ops (q8_gemv_rc.hip, built once per build mode M -- a pair of
+// input and output modes, kBuildModes -- with the entry points below with
+// the mode's number appended).  One op: grid =
 // rc_tiles_for(p, c) workgroups.  A table of tiles of independent rs == 1
-// ops read in one mode.  LDS bytes of a workgroup (0: no such shape).
+// ops read in one mode.  LDS bytes of a workgroup (0: no such shape, or one
+// whose LDS does not fit a workgroup).
+// build mode -> (XMode, YMode)
+constexpr int kBuildModes = 7;
+constexpr int kBuildX[kBuildModes] = {kXFloat, kXQuant, kXSiluUp, kXNormAdd, kXNormScale, kXFloat, kXNormScale};
+constexpr int kBuildY[kBuildModes] = {kYPlain, kYPlain, kYPlain, kYPlain, kYPlain, kYResAdd, kYSwiGLU};
+inline int build_mode(int xmode, int ymode) {
+    for (int m = 0; m < kBuildModes; ++m)
+        if (kBuildX[m] == xmode && kBuildY[m] == ymode) return m;
+    return -1;
+}
 #define Q8_RC_DECLARE(M)                                                                              \
     hipError_t launch_gemv_rc_##M(const OpDesc &op, RcShape sh, int64_t grid, hipStream_t s);         \
     hipError_t launch_gemv_rc_fused_##M(const OpDesc *d_ops, const Tile *d_tiles, RcShape sh,         \
@@ -141,36 +171,37 @@ Q8_RC_DECLARE(0)
 Q8_RC_DECLARE(1)
 Q8_RC_DECLARE(2)
 Q8_RC_DECLARE(3)
+Q8_RC_DECLARE(4)
+Q8_RC_DECLARE(5)
+Q8_RC_DECLARE(6)
 #undef Q8_RC_DECLARE
 
-inline hipError_t launch_gemv_rc(const OpDesc &op, RcShape sh, int64_t grid, hipStream_t s, int xmode) {
-    switch (xmode) {
-        case kXFloat: return launch_gemv_rc_0(op, sh, grid, s);
-        case kXQuant: return launch_gemv_rc_1(op, sh, grid, s);
-        case kXSiluUp: return launch_gemv_rc_2(op, sh, grid, s);
-        case kXNormAdd: return launch_gemv_rc_3(op, sh, grid, s);
-        default: return hipErrorInvalidValue;
+#define Q8_RC_SWITCH(F, ...)                            \
+    switch (build_mode(xmode, ymode)) {                 \
+        case 0: return F##0(__VA_ARGS__);               \
+        case 1: return F##1(__VA_ARGS__);               \
+        case 2: return F##2(__VA_ARGS__);               \
+        case 3: return F##3(__VA_ARGS__);               \
+        case 4: return F##4(__VA_ARGS__);               \
+        case 5: return F##5(__VA_ARGS__);               \
+        case 6: return F##6(__VA_ARGS__);               \
+        default: break;                                 \
     }
+inline hipError_t launch_gemv_rc(const OpDesc &op, RcShape sh, int64_t grid, hipStream_t s, int xmode,
+                                 int ymode = kYPlain) {
+    Q8_RC_SWITCH(launch_gemv_rc_, op, sh, grid, s)
+    return hipErrorInvalidValue;
 }
 inline hipError_t launch_gemv_rc_fused(const OpDesc *d_ops, const Tile *d_tiles, RcShape sh, int64_t grid,
-                                       hipStream_t s, int xmode) {
-    switch (xmode) {
-        case kXFloat: return launch_gemv_rc_fused_0(d_ops, d_tiles, sh, grid, s);
-        case kXQuant: return launch_gemv_rc_fused_1(d_ops, d_tiles, sh, grid, s);
-        case kXSiluUp: return launch_gemv_rc_fused_2(d_ops, d_tiles, sh, grid, s);
-        case kXNormAdd: return launch_gemv_rc_fused_3(d_ops, d_tiles, sh, grid, s);
-        default: return hipErrorInvalidValue;
-    }
+                                       hipStream_t s, int xmode, int ymode = kYPlain) {
+    Q8_RC_SWITCH(launch_gemv_rc_fused_, d_ops, d_tiles, sh, grid, s)
+    return hipErrorInvalidValue;
 }
-inline int gemv_rc_lds_bytes(RcShape sh, int xmode) {
-    switch (xmode) {
-        case kXFloat: return gemv_rc_lds_bytes_0(sh);
-        case kXQuant: return gemv_rc_lds_bytes_1(sh);
-        case kXSiluUp: return gemv_rc_lds_bytes_2(sh);
-        case kXNormAdd: return gemv_rc_lds_bytes_3(sh);
-        default: return 0;
-    }
+inline int gemv_rc_lds_bytes(RcShape sh, int xmode, int ymode = kYPlain) {
+    Q8_RC_SWITCH(gemv_rc_lds_bytes_, sh)
+    return 0;
 }
+#undef Q8_RC_SWITCH
 // x (n floats, n % 32 == 0) -> n/32 Q8_0 blocks of 34 bytes at xq.
 hipError_t launch_quantize_x(const float *x, void *xq, int64_t n, hipStream_t s);
 

@@ -16,9 +16,11 @@
 //    (global_load_lds_dwordx4): load i of lane l carries chunk (64i + l) of
 //    the column's R runs of C*272 contiguous bytes, so every load
 //    instruction reads whole contiguous KiB, and lane l finds its own group
-//    at LDS offset 272*l.  The lane copies it into registers, and the stage
-//    is refilled with the next column at once: one group per lane in
-//    flight while the current one is computed, in 17 KiB of LDS per wave.
+//    at LDS offset 272*l.  The lane copies it into registers and the next
+//    column's loads are issued while the current one is computed: with
+//    NST = 2 W stages into the other stage at once, with NST = 1 into the
+//    same stage once its reads have completed (17 KiB of LDS per wave
+//    instead of 34, so twice the waves fit on a CU).
 //  * The column's C x slices (1 KiB each) ride along as C more direct loads
 //    into a double-buffered x stage; a lane reads its slice with LDS
 //    broadcast reads.
@@ -30,6 +32,18 @@
 //    row the last steps run across the row's lanes in a fixed butterfly.
 // The arithmetic (q8_block.h), the slot of every group and the final tree
 // do not depend on (C, NWK): every launch shape gives the same bits.
+//
+// Input mode kXNormScale: x arrives already multiplied by the norm's gain
+// (the producer wrote it so), and the norm's 1 / rms, a scalar, multiplies
+// each row result instead of each x element: rms_norm(x) * g . w =
+// inv * ((x * g) . w).  Its tiles are the float tiles plus one multiply.
+//
+// Output modes (YMode): y = W x; a residual add (y = x_res + W x, with the
+// sums of y^2 over fixed 16-row blocks for the norm the next matvec applies,
+// and, if x_out is set, y * norm_w there: the next matvec's input); and the
+// SwiGLU pair, where the workgroup's waves come in two halves that compute
+// the same rows of W (gate) and W2 (up) and the first half writes
+// silu(gate) * up.
 #pragma once
 
 #include "q8_block.h"
@@ -41,15 +55,22 @@ namespace {
 // different LDS banks.
 constexpr int kXSlice = kStageX + 16;
 
-template <int C, int XM>
+template <int C, int XM, int NST>
 struct RcLds {
     static constexpr int kX = C * kXSlice;                  // one x stage
-    static constexpr int kUp = XM == kXSiluUp ? kX : 0;     // its up slices
-    static constexpr int kWaveBytes = kStageW + 2 * (kX + kUp);
+    // its up slices (kXSiluUp)
+    static constexpr int kUp = XM == kXSiluUp ? kX : 0;
+    static constexpr int kWaveBytes = NST * kStageW + 2 * (kX + kUp);
 };
 
-template <int C, int NWK, int XM>
-constexpr int rc_lds_bytes() { return NWK * RcLds<C, XM>::kWaveBytes; }
+// waves of a workgroup: NWK, twice that for the SwiGLU pair
+template <int NWK, int YM>
+constexpr int rc_waves() { return YM == kYSwiGLU ? 2 * NWK : NWK; }
+
+template <int C, int NWK, int XM, int NST, int YM = kYPlain>
+constexpr int rc_lds_bytes() { return rc_waves<NWK, YM>() * RcLds<C, XM, NST>::kWaveBytes; }
+// LDS a workgroup may have on gfx950
+constexpr int kMaxLds = 160 * 1024;
 
 // kXNormAdd with NWK waves: wave w sums the squares of parts w, w + NWK, ...
 // of x + x_res (and, in the writer workgroup, stores those parts to x_out);
@@ -77,27 +98,48 @@ __device__ __forceinline__ float rc_norm_inv(const OpDesc &op, int lane, int wav
     return norm_inv_from(part, op);
 }
 
+// kXNormScale: 1 / rms of the op's x from the producer's block sums of x^2
+// (op.psum_n floats, a multiple of 4, 16-byte aligned), added in a fixed
+// order: lane l takes the float4s l, l + 64, ... in turn (each as
+// (a + b) + (c + d)), then the lanes meet in the fixed butterfly.
+__device__ __forceinline__ float psum_inv(const OpDesc &op, int lane) {
+    const float4 *p4 = reinterpret_cast<const float4 *>(op.psum);
+    const int n4 = op.psum_n / 4;
+    float ss = 0.f;
+    for (int i = lane; i < n4; i += kWave) {
+        const float4 v = p4[i];
+        ss += (v.x + v.y) + (v.z + v.w);
+    }
+    ss = wave_sum(ss);
+    return 1.0f / sqrtf(ss / (float)(op.nb * kQuants) + op.norm_eps);
+}
+
 // Tile `tile` (rows tile*R ..) of op, all its groups, on a workgroup of NWK
 // waves whose LDS is `lds` (rc_lds_bytes).  writer (kXNormAdd): this
 // workgroup also writes x + x_res to op.x_out.
-template <int C, int NWK, int XM>
+template <int C, int NWK, int XM, int NST, int YM = kYPlain>
 __device__ __forceinline__ void rc_tile(const OpDesc &op, int64_t tile, uint8_t *lds, bool writer) {
-    using L = RcLds<C, XM>;
+    using L = RcLds<C, XM, NST>;
+    static_assert(NST == 1 || NST == 2, "W stages per wave");
+    static_assert(YM != kYSwiGLU || XM != kXNormAdd, "the pair does not take the norm-add input");
     constexpr int R = kWave / C;          // rows of the tile
     constexpr int U = kRowSlots / C;      // slots a lane owns in its row
     static_assert(C == 1 || C == 2 || C == 4, "lanes per row");
     static_assert(U % NWK == 0, "every slot needs exactly one owner wave");
     const int lane = lane_id();
     const int wave = wave_id();
+    // kYSwiGLU: waves [0, NWK) take the rows of W (gate), [NWK, 2 NWK) of W2 (up)
+    const int half = YM == kYSwiGLU ? wave / NWK : 0;
+    const int wk = wave - half * NWK;    // the wave's place among the NWK sharing its rows
     const int r = lane / C, c = lane % C;
     const int64_t row0 = tile * R;
     const int last = (int)min((int64_t)op.p - 1 - row0, (int64_t)R - 1);   // rows past p re-read this one
     const int G = op.gsr;                 // groups per row
     const int J = (G + C - 1) / C;        // group columns
     const int64_t RB = op.sr_bytes;       // bytes per row
-    uint8_t *wst = lds + wave * L::kWaveBytes;
-    uint8_t *xst = wst + kStageW;         // two x stages, then (kXSiluUp) two up stages
-    const uint8_t *wbase = uniform_ptr(op.w + row0 * RB);
+    uint8_t *wst = lds + wave * L::kWaveBytes;   // NST W stages
+    uint8_t *xst = wst + NST * kStageW;          // two x stages, then (kXSiluUp) two up stages
+    const uint8_t *wbase = uniform_ptr((half ? op.w2 : op.w) + row0 * RB);
 
     // Per load i: the owner lane s = (64i + lane) / 17 of the chunk this lane
     // carries, as (row part of the byte offset + chunk offset) and the
@@ -116,12 +158,12 @@ __device__ __forceinline__ void rc_tile(const OpDesc &op, int64_t tile, uint8_t 
 #pragma unroll
     for (int u = 0; u < U; ++u) acc[u] = 0.f;
 
-    // this wave's group columns j = wave + NWK * t, t < nt
-    const int nt = J > wave ? (J - wave + NWK - 1) / NWK : 0;
+    // this wave's group columns j = wk + NWK * t, t < nt
+    const int nt = J > wk ? (J - wk + NWK - 1) / NWK : 0;
     float4 na[C], nr[C], nw[C];   // kXNormAdd: x, x_res and gain of the column, prefetched
     auto issue = [&](int t) {
-        const int j = wave + NWK * t;
-        const uint32_t l0 = __builtin_amdgcn_readfirstlane(lds_addr(wst));
+        const int j = wk + NWK * t;
+        const uint32_t l0 = __builtin_amdgcn_readfirstlane(lds_addr(wst + (t % NST) * kStageW));
 #pragma unroll
         for (int i = 0; i < kGroupChunks; ++i) {
             const uint32_t kk = min((uint32_t)(C * j) + cs[i], (uint32_t)(G - 1));
@@ -144,14 +186,15 @@ __device__ __forceinline__ void rc_tile(const OpDesc &op, int64_t tile, uint8_t 
         }
     };
 
-    // kXNormAdd: one wave computes the norm while its first column streams
-    // in; several waves share it before their first loads (measured faster)
+    // kXNormAdd, kXNormScale: the norm is computed while the first column
+    // streams in (kXNormScale: by the waves that write the rows)
     float ninv = 0.f;
-    if constexpr (XM == kXNormAdd && NWK > 1) ninv = rc_norm_inv<NWK>(op, lane, wave, op.x_out && writer);
     if (nt > 0) issue(0);
-    if constexpr (XM == kXNormAdd && NWK == 1) ninv = rc_norm_inv<1>(op, lane, wave, op.x_out && writer);
+    if constexpr (XM == kXNormAdd) ninv = rc_norm_inv<NWK>(op, lane, wave, op.x_out && writer);
+    if constexpr (XM == kXNormScale)
+        if (wk == 0) ninv = psum_inv(op, lane);
     for (int t = 0; t < nt; ++t) {
-        const int j = wave + NWK * t;
+        const int j = wk + NWK * t;
         uint8_t *xs = xst + (t & 1) * L::kX;
         wait_vm_asm<0>();   // this column's W and x have landed (nothing else is in flight)
         if constexpr (XM == kXNormAdd) {
@@ -162,10 +205,10 @@ __device__ __forceinline__ void rc_tile(const OpDesc &op, int64_t tile, uint8_t 
                     norm_add(na[cc].z, nr[cc].z, ninv, nw[cc].z), norm_add(na[cc].w, nr[cc].w, ninv, nw[cc].w));
         }
         uint32_t D[68];
-        read_group(wst, lane, D);
-        // the stage is in registers (and the LDS writes above are done):
-        // refill it with the next column
-        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+        read_group(wst + (t % NST) * kStageW, lane, D);
+        // the next column: into the other stage at once, or into this one
+        // once its reads (and the LDS writes above) have completed
+        if constexpr (NST == 1) asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
         if (t + 1 < nt) issue(t + 1);
         if constexpr (XM == kXSiluUp) {   // the x slices become silu(gate) * up in place
 #pragma unroll
@@ -191,38 +234,71 @@ __device__ __forceinline__ void rc_tile(const OpDesc &op, int64_t tile, uint8_t 
         }
     }
 
-    // slots of other waves meet in wave 0: slot u of lane l of its owner wave
-    // (u % NWK) is parked at float u*64 + l of that wave's W stage, idle now
-    // (its last column was read into registers before it was computed)
+    // slots of other waves meet in the half's first wave: slot u of lane l
+    // of its owner wave (u % NWK) is parked at float u*64 + l of that wave's
+    // first W stage, idle now (its last column was read into registers, and
+    // those reads have completed, before it was computed)
     if constexpr (NWK > 1) {
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
         float *mine = reinterpret_cast<float *>(wst);
 #pragma unroll
         for (int u = 0; u < U; ++u)
-            if (u % NWK == wave) mine[u * kWave + lane] = acc[u];
+            if (u % NWK == wk) mine[u * kWave + lane] = acc[u];
         __syncthreads();
-        if (wave != 0) return;
+        if (wk == 0) {
 #pragma unroll
-        for (int u = 0; u < U; ++u)
-            if (u % NWK != 0)
-                acc[u] = reinterpret_cast<const float *>(lds + (u % NWK) * L::kWaveBytes)[u * kWave + lane];
+            for (int u = 0; u < U; ++u)
+                if (u % NWK != 0)
+                    acc[u] = reinterpret_cast<const float *>(lds + (half * NWK + u % NWK) * L::kWaveBytes)
+                        [u * kWave + lane];
+        }
     }
     // lane c holds slots C*u + c
-    float row;
-    if constexpr (C == 1) {
-        float La[4];
+    float row = 0.f;
+    if (wk == 0) {
+        if constexpr (C == 1) {
+            float La[4];
 #pragma unroll
-        for (int a = 0; a < 4; ++a) La[a] = (acc[a] + acc[a + 4]) + (acc[a + 8] + acc[a + 12]);
-        row = (La[0] + La[1]) + (La[2] + La[3]);
-    } else if constexpr (C == 2) {
-        // L_c from u = 0, 2, 4, 6 and L_{c+2} from u = 1, 3, 5, 7
-        const float La = (acc[0] + acc[2]) + (acc[4] + acc[6]);
-        const float Lb = (acc[1] + acc[3]) + (acc[5] + acc[7]);
-        const float La1 = __shfl_xor(La, 1, kWave), Lb1 = __shfl_xor(Lb, 1, kWave);
-        row = (La + La1) + (Lb + Lb1);   // used by c == 0: (L0 + L1) + (L2 + L3)
-    } else {
-        const float La = (acc[0] + acc[1]) + (acc[2] + acc[3]);   // L_c
-        const float pair = La + __shfl_xor(La, 1, kWave);           // c = 0: L0 + L1, c = 2: L2 + L3
-        row = pair + __shfl_xor(pair, 2, kWave);
+            for (int a = 0; a < 4; ++a) La[a] = (acc[a] + acc[a + 4]) + (acc[a + 8] + acc[a + 12]);
+            row = (La[0] + La[1]) + (La[2] + La[3]);
+        } else if constexpr (C == 2) {
+            // L_c from u = 0, 2, 4, 6 and L_{c+2} from u = 1, 3, 5, 7
+            const float La = (acc[0] + acc[2]) + (acc[4] + acc[6]);
+            const float Lb = (acc[1] + acc[3]) + (acc[5] + acc[7]);
+            const float La1 = __shfl_xor(La, 1, kWave), Lb1 = __shfl_xor(Lb, 1, kWave);
+            row = (La + La1) + (Lb + Lb1);   // used by c == 0: (L0 + L1) + (L2 + L3)
+        } else {
+            const float La = (acc[0] + acc[1]) + (acc[2] + acc[3]);   // L_c
+            const float pair = La + __shfl_xor(La, 1, kWave);           // c = 0: L0 + L1, c = 2: L2 + L3
+            row = pair + __shfl_xor(pair, 2, kWave);
+        }
+        if constexpr (XM == kXNormScale) row *= ninv;
+    }
+    if constexpr (YM == kYSwiGLU) {
+        // the up half's first wave hands its rows to the gate half's
+        __shared__ float up_rows[kWave];
+        if (half == 1 && wk == 0 && c == 0) up_rows[r] = row;
+        __syncthreads();
+        if (half == 0 && wk == 0 && c == 0 && r <= last) op.y[row0 + r] = silu_up(row, up_rows[r]);
+        return;
+    }
+    if (wk != 0) return;
+    if constexpr (YM == kYResAdd) {
+        // y = x_res + W x (and y * norm_w, the next matvec's input); the
+        // squares of a 16-row block meet in a fixed butterfly over the row
+        // index (lanes C apart), the same tree for every C, and the block's
+        // first row stores the sum
+        float out = 0.f;
+        if (c == 0 && r <= last) {
+            out = op.x_res[row0 + r] + row;
+            op.y[row0 + r] = out;
+            if (op.x_out) op.x_out[row0 + r] = out * op.norm_w[row0 + r];
+        }
+        float sq = out * out;
+#pragma unroll
+        for (int o = 1; o < kPsumRows; o <<= 1) sq += __shfl_xor(sq, o * C, kWave);
+        if (c == 0 && r % kPsumRows == 0 && r <= last) op.psum[(row0 + r) / kPsumRows] = sq;
+        return;
     }
     if (c == 0 && r <= last) op.y[row0 + r] = row;
 }

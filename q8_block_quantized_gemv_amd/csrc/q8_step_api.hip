@@ -179,6 +179,11 @@ struct q8_0_step {
     void *mem = nullptr;      // one device allocation for everything below
     float *x = nullptr, *xn = nullptr, *q = nullptr, *k = nullptr, *v = nullptr, *attn = nullptr;
     float *xa = nullptr, *xb = nullptr;   // the residual stream, alternating between layers
+    // fused residual path (widths multiples of 256): the squared norm's
+    // 16-row block sums, left by o and by down for the matvecs after them,
+    // and the residual stream times the next norm's gain (their input)
+    float *psum_o = nullptr, *psum_d = nullptr, *xg = nullptr;
+    bool fused_residual = false;
     float *resid = nullptr, *gate = nullptr, *up = nullptr, *logits = nullptr;
     float *kcache = nullptr, *vcache = nullptr, *attn_ws = nullptr, *amax_ws = nullptr;
     uint32_t *cnt = nullptr;  // n_heads attention counters, then the argmax counter
@@ -309,7 +314,8 @@ int q8_0_step_create(const q8_0_model *m, q8_0_step **out) {
         (size_t)(m->n_layers * m->max_seq * s->kv_width), (size_t)(m->n_layers * m->max_seq * s->kv_width),
         (size_t)(m->n_heads * s->max_chunks * (m->head_dim + 2)), (size_t)(2 * s->amax_wgs),
         (size_t)(m->n_heads + 1), 1, 1,
-        (size_t)(m->max_seq * (m->head_dim / 2) * 4)};   // double2 per (position, pair)
+        (size_t)(m->max_seq * (m->head_dim / 2) * 4),   // double2 per (position, pair)
+        (size_t)(m->hidden / kPsumRows + 1), (size_t)(m->hidden / kPsumRows + 1), (size_t)m->hidden};
     std::vector<size_t> offs;
     size_t total = 0;
     for (size_t n : sizes) {
@@ -331,6 +337,9 @@ int q8_0_step_create(const q8_0_model *m, q8_0_step **out) {
     s->pos = (int32_t *)(b + offs[nf + 1]);
     s->token = (uint32_t *)(b + offs[nf + 2]);
     s->rope = (double2 *)(b + offs[nf + 3]);
+    s->psum_o = (float *)(b + offs[nf + 4]);
+    s->psum_d = (float *)(b + offs[nf + 5]);
+    s->xg = (float *)(b + offs[nf + 6]);
     // the rotation angles of every position, once: attention reads them
     // instead of evaluating pow and sincos in double precision per token
     if ((e = launch_rope_table(s->rope, (int)m->max_seq, (int)(m->head_dim / 2), m->theta, nullptr)) !=
@@ -367,32 +376,89 @@ int q8_0_step_create(const q8_0_model *m, q8_0_step **out) {
         return e;
     };
     float *cur = s->xa, *oth = s->xb;
-    OpExtra silu;
-    silu.mode = kXSiluUp;
-    silu.x_up = s->up;
-    for (int64_t l = 0; l < m->n_layers && !rc; ++l) {
-        const q8_0_layer_w &L = s->layers[l];
-        if (l == 0) {
-            rc = mk({{s->xn, L.wq, s->q, m->hidden, s->q_width}, {s->xn, L.wk, s->k, m->hidden, s->kv_width},
-                     {s->xn, L.wv, s->v, m->hidden, s->kv_width}});
-        } else {
-            const OpExtra e = norm_add(L.attn_norm, oth);
-            rc = mk({{cur, L.wq, s->q, m->hidden, s->q_width}, {cur, L.wk, s->k, m->hidden, s->kv_width},
-                     {cur, L.wv, s->v, m->hidden, s->kv_width}}, &e);
-            std::swap(cur, oth);
+    // Where every projection's rows are whole 272-byte groups (hidden, inter
+    // and the query width multiples of 256), the residual adds move into the
+    // matvecs that produce them: o and down write the new residual stream
+    // v = x_res + W x, the sums of v^2 over 16-row blocks and v times the
+    // next norm's gain (kYResAdd); the matvecs after them read that product
+    // and scale each row result by 1 / rms(v) from those sums (kXNormScale)
+    // -- no workgroup re-reads the whole stream for its norm.  gate and up run as one pair whose workgroups
+    // compute the same rows of both and write silu(gate) * up (kYSwiGLU), so
+    // down reads a plain input.  Other widths take the inputs apart in each
+    // consumer instead (kXNormAdd, kXSiluUp).
+    const auto whole = [](int64_t v) { return v % (kQuants * kGroupBlocks) == 0; };
+    s->fused_residual = whole(m->hidden) && whole(m->inter) && whole(s->q_width);
+    if (s->fused_residual) {
+        auto norm_scale = [&](float *psum) {
+            OpExtra e;
+            e.mode = kXNormScale;
+            e.psum = psum;
+            e.eps = m->eps;
+            return e;
+        };
+        // out = res + W x, and xg = out * gain for the next matvec
+        auto res_add = [&](const float *res, float *psum, const float *gain) {
+            OpExtra e;
+            e.out_mode = kYResAdd;
+            e.x_res = res;
+            e.psum = psum;
+            e.norm_w = gain;
+            e.x_out = s->xg;
+            return e;
+        };
+        for (int64_t l = 0; l < m->n_layers && !rc; ++l) {
+            const q8_0_layer_w &L = s->layers[l];
+            if (l == 0) {
+                rc = mk({{s->xn, L.wq, s->q, m->hidden, s->q_width}, {s->xn, L.wk, s->k, m->hidden, s->kv_width},
+                         {s->xn, L.wv, s->v, m->hidden, s->kv_width}});
+            } else {
+                const OpExtra e = norm_scale(s->psum_d);   // attn_norm(cur), from xg = cur * attn_norm
+                rc = mk({{s->xg, L.wq, s->q, m->hidden, s->q_width}, {s->xg, L.wk, s->k, m->hidden, s->kv_width},
+                         {s->xg, L.wv, s->v, m->hidden, s->kv_width}}, &e);
+            }
+            if (rc) break;
+            const OpExtra eo = res_add(cur, s->psum_o, L.ffn_norm);   // oth = cur + Wo attn
+            if ((rc = mk({{s->attn, L.wo, oth, s->q_width, m->hidden}}, &eo))) break;
+            OpExtra eg = norm_scale(s->psum_o);   // gate = silu(Wg n) * (Wu n), n = ffn_norm(oth)
+            eg.out_mode = kYSwiGLU;
+            eg.w2 = L.wup;
+            if ((rc = mk({{s->xg, L.wgate, s->gate, m->hidden, m->inter}}, &eg))) break;
+            const float *next = l + 1 < m->n_layers ? s->layers[l + 1].attn_norm : m->out_norm;
+            const OpExtra ed = res_add(oth, s->psum_d, next);          // cur = oth + Wd gate
+            if ((rc = mk({{s->gate, L.wdown, cur, m->inter, m->hidden}}, &ed))) break;
         }
-        if (rc) break;
-        if ((rc = mk({{s->attn, L.wo, s->resid, s->q_width, m->hidden}}))) break;
-        const OpExtra e = norm_add(L.ffn_norm, oth);
-        if ((rc = mk({{cur, L.wgate, s->gate, m->hidden, m->inter}, {cur, L.wup, s->up, m->hidden, m->inter}},
-                     &e)))
-            break;
-        std::swap(cur, oth);
-        if ((rc = mk({{s->gate, L.wdown, s->resid, m->inter, m->hidden}}, &silu))) break;
-    }
-    if (!rc) {
-        const OpExtra e = norm_add(m->out_norm, s->x);
-        rc = mk({{cur, m->lm_head, s->logits, m->hidden, m->vocab}}, &e);
+        if (!rc) {
+            const OpExtra e = norm_scale(s->psum_d);   // out_norm(cur)
+            rc = mk({{s->xg, m->lm_head, s->logits, m->hidden, m->vocab}}, &e);
+        }
+    } else {
+        OpExtra silu;
+        silu.mode = kXSiluUp;
+        silu.x_up = s->up;
+        for (int64_t l = 0; l < m->n_layers && !rc; ++l) {
+            const q8_0_layer_w &L = s->layers[l];
+            if (l == 0) {
+                rc = mk({{s->xn, L.wq, s->q, m->hidden, s->q_width}, {s->xn, L.wk, s->k, m->hidden, s->kv_width},
+                         {s->xn, L.wv, s->v, m->hidden, s->kv_width}});
+            } else {
+                const OpExtra e = norm_add(L.attn_norm, oth);
+                rc = mk({{cur, L.wq, s->q, m->hidden, s->q_width}, {cur, L.wk, s->k, m->hidden, s->kv_width},
+                         {cur, L.wv, s->v, m->hidden, s->kv_width}}, &e);
+                std::swap(cur, oth);
+            }
+            if (rc) break;
+            if ((rc = mk({{s->attn, L.wo, s->resid, s->q_width, m->hidden}}))) break;
+            const OpExtra e = norm_add(L.ffn_norm, oth);
+            if ((rc = mk({{cur, L.wgate, s->gate, m->hidden, m->inter}, {cur, L.wup, s->up, m->hidden, m->inter}},
+                         &e)))
+                break;
+            std::swap(cur, oth);
+            if ((rc = mk({{s->gate, L.wdown, s->resid, m->inter, m->hidden}}, &silu))) break;
+        }
+        if (!rc) {
+            const OpExtra e = norm_add(m->out_norm, s->x);
+            rc = mk({{cur, m->lm_head, s->logits, m->hidden, m->vocab}}, &e);
+        }
     }
     if (rc) { std::string why = "q8_0_step_create: " + std::string(q8_0_last_error()); step_free(s); return fail(rc, why); }
     s->launches = 0;
@@ -456,7 +522,7 @@ int q8_0_step_buffers(const q8_0_step *s, q8_0_step_bufs *out) {
     if (!s || !out) return fail(Q8_ERR_INVALID_ARG, "q8_0_step_buffers: null pointer");
     out->token = s->token;
     out->pos = s->pos;
-    out->x = s->x;
+    out->x = s->fused_residual ? s->xa : s->x;   // the residual stream after the last layer
     out->logits = s->logits;
     out->k_cache = s->kcache;
     out->v_cache = s->vcache;

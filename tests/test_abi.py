@@ -129,13 +129,15 @@ def test_chain_validation(q8):
     assert q8.lib.q8_0_chain_destroy(None) == 0
 
 
-@pytest.mark.parametrize("c,waves,n,code", [
-    (3, 1, 256, -1), (1, 3, 256, -1), (0, 1, 256, -1), (8, 1, 256, -1),   # lanes/waves not 1, 2, 4
-    (4, 4, 96, -2), (4, 4, 896, -2),                                        # n not a multiple of 256
-    (4, 4, 0, -2), (1, 1, 33, -2),                                          # as q8_0_gemv
+@pytest.mark.parametrize("c,waves,st,n,code", [
+    (3, 1, 1, 256, -1), (1, 3, 1, 256, -1), (0, 1, 1, 256, -1), (8, 1, 1, 256, -1),  # not 1, 2, 4
+    (1, 1, 0, 256, -1), (1, 1, 3, 256, -1),                                        # stages not 1, 2
+    (4, 4, 2, 256, -1),                                                            # LDS past 160 KiB
+    (4, 4, 1, 96, -2), (4, 4, 1, 896, -2),                                         # n % 256 != 0
+    (4, 4, 1, 0, -2), (1, 1, 1, 33, -2),                                           # as q8_0_gemv
 ])
-def test_gemv_shaped_validation(q8, c, waves, n, code):
-    assert q8.lib.q8_0_gemv_shaped(X, W, Y, n, 4, c, waves, None) == code
+def test_gemv_shaped_validation(q8, c, waves, st, n, code):
+    assert q8.lib.q8_0_gemv_shaped(X, W, Y, n, 4, c, waves, st, None) == code
     assert q8.last_error() != ""
 
 
