@@ -29,8 +29,8 @@ struct AttnFuse {
     const float *q_norm, *k_norm;
     float *kc_w, *vc_w;
     float eps, theta;
-    // if set: (cos, sin) of every rotation angle, [position][pair], as
-    // launch_rope_table leaves them; else attention computes the angles
+    // (cos, sin) of every rotation angle, [position][pair], as
+    // launch_rope_table leaves them (required)
     const double2 *rope;
 };
 

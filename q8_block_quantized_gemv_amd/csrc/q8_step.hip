@@ -42,10 +42,34 @@ __device__ __forceinline__ float wave_sum(float v) {
     return v;
 }
 
-__device__ __forceinline__ float wave_max(float v) {
-#pragma unroll
-    for (int o = kWave / 2; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, kWave));
-    return v;
+// A whole-wave reduction of v by op, the result in every lane, in a fixed
+// order: pairs, quads, 8- and 16-lane rows through DPP (no LDS), the two
+// rows of each 32-lane half through one swizzle, the halves through two
+// reads of lanes 0 and 32.
+template <typename Op>
+__device__ __forceinline__ float dpp_reduce(float v, Op op) {
+    auto dpp = [](float x, int ctrl) -> float {
+        switch (ctrl) {   // (the control must be a constant of the instruction)
+            case 0: return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0xB1, 0xF, 0xF, false));
+            case 1: return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x4E, 0xF, 0xF, false));
+            case 2: return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x141, 0xF, 0xF, false));
+            default: return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x140, 0xF, 0xF, false));
+        }
+    };
+    v = op(v, dpp(v, 0));   // quad_perm [1,0,3,2]: lane ^ 1
+    v = op(v, dpp(v, 1));   // quad_perm [2,3,0,1]: lane ^ 2
+    v = op(v, dpp(v, 2));   // row_half_mirror: the other quad of 8
+    v = op(v, dpp(v, 3));   // row_mirror: the other 8 of 16
+    v = op(v, __builtin_bit_cast(float, __builtin_amdgcn_ds_swizzle(__builtin_bit_cast(int, v), 0x401F)));   // lane ^ 16
+    const float lo = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 0));
+    const float hi = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 32));
+    return op(lo, hi);
+}
+__device__ __forceinline__ float dpp_sum(float v) {
+    return dpp_reduce(v, [](float a, float b) { return a + b; });
+}
+__device__ __forceinline__ float dpp_max(float v) {
+    return dpp_reduce(v, [](float a, float b) { return fmaxf(a, b); });
 }
 
 __device__ __forceinline__ int position(const int *pos_dev, int pos) {
@@ -329,7 +353,10 @@ __global__ __launch_bounds__(256) void k_append_kv(const float *k, const float *
 // Scores: a row is read by L lanes with float4 loads (L = HD/4 rounded up
 // to a power of two), 64/L rows per wave at a time, every row of a lane's
 // share loaded before any is reduced.  Values: thread (column float4,
-// row group) accumulates its rows, the row groups meet in LDS.
+// row group) accumulates its rows, the row groups meet in LDS.  Once the
+// position is read, every load of the chunk that depends on nothing else
+// (keys, the first batch of values, q/k/v, norm gains, rotation angles)
+// is issued at once, so a short chunk costs two memory round trips.
 // FUSED (a recorded token): the q head arrives raw and is normed (q_norm)
 // and rotated here; the chunk holding the token's own row (pos = seq - 1)
 // norms and rotates that row's key from the raw k and takes its value from
@@ -352,12 +379,12 @@ __global__ __launch_bounds__(kAttnThreads) void k_attention(AttnDesc d, AttnFuse
     constexpr int RPT = (kAttnChunk + RG - 1) / RG;              // rows per thread
     constexpr int VB = RPT < 16 ? RPT : 16;                      // value loads in flight
     __shared__ float sc[kAttnChunk];
+    __shared__ float pt[kAttnWaves * SB * 65];   // each wave's partial-dot tile
     __shared__ float red[2 * kAttnWaves];
     __shared__ float4 accp[kAttnThreads];
     __shared__ uint32_t prev;
-    __shared__ __attribute__((aligned(16))) float qs[FUSED ? HD : 4];
-    __shared__ __attribute__((aligned(16))) float kn[FUSED ? HD : 4];
-    __shared__ __attribute__((aligned(16))) float vn[FUSED ? HD : 4];
+    __shared__ __attribute__((aligned(16))) float qs[FUSED ? kAttnWaves * HD : 4];   // per wave
+    __shared__ __attribute__((aligned(16))) float kn[FUSED ? kAttnWaves * HD : 4];
     const int head = blockIdx.x % d.n_heads;
     const int c = blockIdx.x / d.n_heads;
     const int seq = d.pos_dev ? min(*d.pos_dev + 1, d.seq) : d.seq;
@@ -370,108 +397,155 @@ __global__ __launch_bounds__(kAttnThreads) void k_attention(AttnDesc d, AttnFuse
     const int pos = seq - 1;
     const bool cur = FUSED && pos >= t0 && pos < t0 + rows;   // this chunk holds the token's row
     const int rcur = pos - t0;
+    const bool writer = cur && head % d.kv_group == 0;        // stores the row into the caches
+    const int64_t crow = (int64_t)pos * d.kv_width + kv_off;
+    // ---- every read of the chunk that depends only on the position is
+    // issued here at once: keys, the first batch of values, the raw q/k/v,
+    // the norm gains and the rotation angles.  The token's own row is not in
+    // the caches yet: its key and value are skipped here (they read as zero)
+    // and enter once, from the raw k and v.
+    const int g = lane / L, col = lane % L;
+    const bool colv = col < NV;
+    const float *kbase = d.kc + (int64_t)t0 * d.kv_width + kv_off + 4 * col;
+    float4 kv[SB];
+    auto load_keys = [&](int p0) {
+#pragma unroll
+        for (int b = 0; b < SB; ++b) {
+            const int r = (p0 + b) * RPP + wv * RPW + g;
+            kv[b] = make_float4(0.f, 0.f, 0.f, 0.f);
+            if (colv && r < rows && !(cur && r == rcur))
+                kv[b] = *(const float4 *)(kbase + (int64_t)r * d.kv_width);
+        }
+    };
+    const int vcol = tid % NV, rg = tid / NV;
+    const float *vbase = d.vc + (int64_t)t0 * d.kv_width + kv_off + 4 * vcol;
+    float4 vv[VB];
+    auto load_vals = [&](int r0) {
+#pragma unroll
+        for (int b = 0; b < VB; ++b) {
+            const int r = rg + (r0 + b) * RG;
+            vv[b] = make_float4(0.f, 0.f, 0.f, 0.f);
+            if (rg < RG && r < rows && !(cur && r == rcur))
+                vv[b] = *(const float4 *)(vbase + (int64_t)r * d.kv_width);
+        }
+    };
+    load_keys(0);
+    load_vals(0);
+    // FUSED: each wave norms and rotates its own copy of q (and k): lane l
+    // holds the pairs (i, i + HALF), i = l + 64 j < HALF
+    constexpr int NP = (HALF + kWave - 1) / kWave;
+    float qa[NP], qb[NP], ka[NP], kb[NP], qga[NP], qgb[NP], kga[NP], kgb[NP];
+    double2 cs[NP];
+    float4 vn4 = make_float4(0.f, 0.f, 0.f, 0.f);   // the token's raw value, column vcol
+    float4 q4 = make_float4(0.f, 0.f, 0.f, 0.f);
+    if (FUSED) {
+        const float *qh = f.q + (int64_t)head * HD;
+#pragma unroll
+        for (int j = 0; j < NP; ++j) {
+            const int i = lane + kWave * j;
+            qa[j] = qb[j] = ka[j] = kb[j] = qga[j] = qgb[j] = kga[j] = kgb[j] = 0.f;
+            cs[j] = make_double2(1.0, 0.0);
+            if (i < HALF) {
+                qa[j] = qh[i];
+                qb[j] = qh[i + HALF];
+                qga[j] = f.q_norm[i];
+                qgb[j] = f.q_norm[i + HALF];
+                cs[j] = f.rope[(int64_t)pos * HALF + i];
+                if (cur) {
+                    ka[j] = f.k[kv_off + i];
+                    kb[j] = f.k[kv_off + i + HALF];
+                    kga[j] = f.k_norm[i];
+                    kgb[j] = f.k_norm[i + HALF];
+                }
+            }
+        }
+        if (cur) vn4 = *(const float4 *)(f.v + kv_off + 4 * vcol);
+    } else if (colv) {
+        q4 = ((const float4 *)(d.q + (int64_t)head * HD))[col];
+    }
     // ---- scores
+    float s_cur = 0.f;   // the token's own score (FUSED)
     {
-        const int g = lane / L, col = lane % L;
-        const bool colv = col < NV;
-        const float *kbase = d.kc + (int64_t)t0 * d.kv_width + kv_off + 4 * col;
-        float4 kv[SB];
-        auto load_keys = [&](int p0) {
-#pragma unroll
-            for (int b = 0; b < SB; ++b) {
-                const int r = (p0 + b) * RPP + wv * RPW + g;
-                kv[b] = make_float4(0.f, 0.f, 0.f, 0.f);
-                if (colv && r < rows && !(cur && r == rcur))
-                    kv[b] = *(const float4 *)(kbase + (int64_t)r * d.kv_width);
-            }
-        };
-        load_keys(0);   // in flight while the query is prepared
-        float4 q4 = make_float4(0.f, 0.f, 0.f, 0.f);
         if (FUSED) {
-            float qv = 0.f, kr = 0.f, vr = 0.f;
-            if (tid < HD) {
-                qv = f.q[(int64_t)head * HD + tid];
-                if (cur) {
-                    kr = f.k[kv_off + tid];
-                    vr = f.v[kv_off + tid];
-                }
-            }
-            const float sq = wave_sum(qv * qv), sk = wave_sum(kr * kr);
-            if (lane == 0) {
-                red[wv] = sq;
-                red[kAttnWaves + wv] = sk;
-            }
-            __syncthreads();
-            float SQ = red[0], SK = red[kAttnWaves];
+            float sq = 0.f, sk = 0.f;
 #pragma unroll
-            for (int w = 1; w < HD / kWave; ++w) {
-                SQ += red[w];
-                SK += red[kAttnWaves + w];
+            for (int j = 0; j < NP; ++j) {
+                sq = fmaf(qa[j], qa[j], sq);
+                sq = fmaf(qb[j], qb[j], sq);
+                sk = fmaf(ka[j], ka[j], sk);
+                sk = fmaf(kb[j], kb[j], sk);
             }
-            if (tid < HD) {
-                qs[tid] = qv * rms_inv(SQ, HD, f.eps) * f.q_norm[tid];
-                if (cur) {
-                    kn[tid] = kr * rms_inv(SK, HD, f.eps) * f.k_norm[tid];
-                    vn[tid] = vr;
-                }
-            }
-            __syncthreads();
-            const bool writer = cur && head % d.kv_group == 0;
-            const int64_t crow = (int64_t)pos * d.kv_width + kv_off;
-            if (tid < HALF) {
-                float ra, rb;
-                if (f.rope) {
-                    const double2 cs = f.rope[(int64_t)pos * HALF + tid];
-                    rotate_by(qs[tid], qs[tid + HALF], cs.y, cs.x, ra, rb);
-                } else {
-                    rotate(qs[tid], qs[tid + HALF], tid, HALF, pos, f.theta, ra, rb);
-                }
-                qs[tid] = ra;
-                qs[tid + HALF] = rb;
-            } else if (cur && tid >= 128 && tid < 128 + HALF) {
-                const int i = tid - 128;
-                float ra, rb;
-                if (f.rope) {
-                    const double2 cs = f.rope[(int64_t)pos * HALF + i];
-                    rotate_by(kn[i], kn[i + HALF], cs.y, cs.x, ra, rb);
-                } else {
-                    rotate(kn[i], kn[i + HALF], i, HALF, pos, f.theta, ra, rb);
-                }
-                kn[i] = ra;
-                kn[i + HALF] = rb;
-                if (writer) {
-                    f.kc_w[crow + i] = ra;
-                    f.kc_w[crow + i + HALF] = rb;
+            const float iq = rms_inv(dpp_sum(sq), HD, f.eps);
+            const float ik = cur ? rms_inv(dpp_sum(sk), HD, f.eps) : 0.f;
+            float *qw = qs + wv * HD, *kw = kn + wv * HD;   // this wave's copies
+#pragma unroll
+            for (int j = 0; j < NP; ++j) {
+                const int i = lane + kWave * j;
+                if (i < HALF) {
+                    float ra, rb;
+                    rotate_by(qa[j] * iq * qga[j], qb[j] * iq * qgb[j], cs[j].y, cs[j].x, ra, rb);
+                    qw[i] = ra;
+                    qw[i + HALF] = rb;
+                    if (cur) {
+                        rotate_by(ka[j] * ik * kga[j], kb[j] * ik * kgb[j], cs[j].y, cs[j].x, ra, rb);
+                        kw[i] = ra;
+                        kw[i + HALF] = rb;
+                        if (writer && wv == 0) {
+                            f.kc_w[crow + i] = ra;
+                            f.kc_w[crow + i + HALF] = rb;
+                        }
+                    }
                 }
             }
-            if (writer && tid < HD) f.vc_w[crow + tid] = vn[tid];
-            __syncthreads();
-            if (colv) q4 = ((const float4 *)qs)[col];
-        } else if (colv) {
-            q4 = ((const float4 *)(d.q + (int64_t)head * HD))[col];
+            if (writer && tid < NV) *(float4 *)(f.vc_w + crow + 4 * vcol) = vn4;
+            __builtin_amdgcn_wave_barrier();
+            if (colv) q4 = ((const float4 *)qw)[col];
+            if (cur) {   // q . k of the token's row: every group of L lanes holds it whole
+                const float4 k4 = colv ? ((const float4 *)kw)[col] : make_float4(0.f, 0.f, 0.f, 0.f);
+                float dc = q4.x * k4.x;
+                dc = fmaf(q4.y, k4.y, dc);
+                dc = fmaf(q4.z, k4.z, dc);
+                dc = fmaf(q4.w, k4.w, dc);
+                s_cur = dpp_sum(dc) * (1.0f / RPW);   // the RPW equal group sums, an exact multiple
+            }
         }
         const float scale = 1.0f / sqrtf((float)HD);
+        // A lane's SB partial dots (one per pass of the batch) go to the
+        // wave's tile P[b][lane] (rows of 65 floats: both the writes and the
+        // transposed reads below hit distinct banks); lane j then adds the SB
+        // partials of row (pass b, group g), columns [h SB, h SB + SB), for
+        // j = (g LG + h) SB + b, and the LG lanes of a row meet in a
+        // butterfly over h.
+        constexpr int LG = L / SB;
+        static_assert(SB <= L && L % SB == 0, "passes per batch within a row's lanes");
+        float *P = pt + wv * (SB * 65);
+        const int rb = lane % SB, rgh = lane / SB;   // (b, g LG + h) of the row part this lane adds
         for (int p0 = 0; p0 < PASSES; p0 += SB) {
             if (p0 > 0) load_keys(p0);
 #pragma unroll
             for (int b = 0; b < SB; ++b) {
-                const int r = (p0 + b) * RPP + wv * RPW + g;
-                if (cur && r == rcur && colv) kv[b] = ((const float4 *)kn)[col];
                 float dot = q4.x * kv[b].x;
                 dot = fmaf(q4.y, kv[b].y, dot);
                 dot = fmaf(q4.z, kv[b].z, dot);
-                dot = fmaf(q4.w, kv[b].w, dot);
-#pragma unroll
-                for (int o = L / 2; o > 0; o >>= 1) dot += __shfl_xor(dot, o, kWave);
-                if (col == 0 && r < rows) sc[r] = dot * scale;
+                P[b * 65 + lane] = fmaf(q4.w, kv[b].w, dot);
             }
+            __builtin_amdgcn_wave_barrier();
+            float part = 0.f;
+#pragma unroll
+            for (int k = 0; k < SB; ++k) part += P[rb * 65 + rgh * SB + k];
+#pragma unroll
+            for (int o = SB; o < LG * SB; o <<= 1) part += __shfl_xor(part, o, kWave);
+            __builtin_amdgcn_wave_barrier();   // (the tile is rewritten by the next batch)
+            const int gg = rgh / LG;
+            const int r = (p0 + rb) * RPP + wv * RPW + gg;
+            if (rgh % LG == 0 && r < rows) sc[r] = (cur && r == rcur ? s_cur : part) * scale;
         }
     }
     __syncthreads();
     // ---- local max and sum over the chunk
     float m = -INFINITY;
     for (int r = tid; r < rows; r += kAttnThreads) m = fmaxf(m, sc[r]);
-    m = wave_max(m);
+    m = dpp_max(m);
     if (lane == 0) red[wv] = m;
     __syncthreads();
     m = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
@@ -482,29 +556,22 @@ __global__ __launch_bounds__(kAttnThreads) void k_attention(AttnDesc d, AttnFuse
         sc[r] = e;
         s += e;
     }
-    s = wave_sum(s);
+    s = dpp_sum(s);
     if (lane == 0) red[wv] = s;
     __syncthreads();
     s = (red[0] + red[1]) + (red[2] + red[3]);
-    // ---- acc over the chunk's values
+    // ---- acc over the chunk's values (thread (vcol, rg) takes rows rg, rg + RG, ...)
     {
-        const int col = tid % NV, rg = tid / NV;
         float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
         if (rg < RG) {
-            const float *vbase = d.vc + (int64_t)t0 * d.kv_width + kv_off + 4 * col;
             for (int r0 = 0; r0 < RPT; r0 += VB) {
-                float4 vv[VB];
+                if (r0 > 0) load_vals(r0);
                 float ee[VB];
 #pragma unroll
                 for (int b = 0; b < VB; ++b) {
                     const int r = rg + (r0 + b) * RG;
-                    vv[b] = make_float4(0.f, 0.f, 0.f, 0.f);
-                    ee[b] = 0.f;
-                    if (r < rows) {
-                        if (cur && r == rcur) vv[b] = ((const float4 *)vn)[col];
-                        else vv[b] = *(const float4 *)(vbase + (int64_t)r * d.kv_width);
-                        ee[b] = sc[r];
-                    }
+                    const float e = sc[min(r, kAttnChunk - 1)];
+                    ee[b] = r < rows ? e : 0.f;
                 }
 #pragma unroll
                 for (int b = 0; b < VB; ++b) {
@@ -513,6 +580,13 @@ __global__ __launch_bounds__(kAttnThreads) void k_attention(AttnDesc d, AttnFuse
                     acc.z = fmaf(ee[b], vv[b].z, acc.z);
                     acc.w = fmaf(ee[b], vv[b].w, acc.w);
                 }
+            }
+            if (cur && rg == rcur % RG) {   // the token's own value, after the cached rows
+                const float e = sc[rcur];
+                acc.x = fmaf(e, vn4.x, acc.x);
+                acc.y = fmaf(e, vn4.y, acc.y);
+                acc.z = fmaf(e, vn4.z, acc.z);
+                acc.w = fmaf(e, vn4.w, acc.w);
             }
         }
         accp[tid] = acc;
@@ -746,6 +820,7 @@ hipError_t launch_rope_table(double2 *t, int rows, int half, float theta, hipStr
 }
 
 hipError_t launch_attention_fused(const AttnDesc &d, const AttnFuse &f, hipStream_t s) {
+    if (!f.rope) return hipErrorInvalidValue;
     return launch_attention_t<true>(d, f, s);
 }
 
