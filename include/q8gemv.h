@@ -28,11 +28,14 @@
  *   - y (Y) must not overlap x (X) or w.
  *   - Sizes: n is a positive multiple of 32 and at most Q8_MAX_N; p is
  *     positive and at most Q8_MAX_P; small-batch m is in 1..Q8_MAX_M.
- *   - q8_0_gemv allocates no device memory.  q8_0_gemm_smallm (m >= 2) uses
- *     a workspace per (device, stream) that the library allocates on first
- *     use and grows when a larger shape needs more (hipMalloc/hipFree, which
- *     synchronize the device); it is kept until the process ends.  Calls on
- *     one stream share it in stream order.
+ *   - No entry point allocates, frees or synchronizes device memory on its
+ *     own except q8_0_chain_create/destroy (and, in q8step.h, the step's
+ *     create/destroy), which own what they allocate.  Calls whose kernels
+ *     need scratch memory (the small-batch product; in q8step.h the
+ *     standalone attention and argmax) take a caller-owned device workspace
+ *     whose size a host-only query returns; it is 256-byte aligned, may hold
+ *     anything beforehand (each call clears what must start at zero), and
+ *     must not be used by two calls that may overlap.
  *   - Results are bitwise reproducible run to run for the same inputs,
  *     shapes and device: every sum runs in a fixed order (the small-batch
  *     product counts arrivals with an atomic counter, but adds partial sums
@@ -45,6 +48,7 @@
 #ifndef Q8GEMV_H
 #define Q8GEMV_H
 
+#include <stddef.h>
 #include <stdint.h>
 
 /* Only the entry points below are exported from libq8gemv.so. */
@@ -107,9 +111,22 @@ Q8_API int q8_0_gemv_shaped(const float *x, const void *w, float *y, int64_t n, 
  * page "minfer Metal Backend Design", section 4.4, the matmul tiers).
  *   X : float32[m][n] row-major, device.   Y : float32[m][p] row-major, device.
  * Each Y[i] equals what q8_0_gemv gives for x = X[i] to the same accuracy.
+ * workspace: a device buffer of at least the bytes q8_0_gemm_smallm_workspace
+ * gives for (m, n, p, Q8_SMALLM_AUTO) on the current device (0 for m = 1:
+ * then it may be NULL); 256-byte aligned, not overlapping X, w or Y
+ * (Q8_ERR_ALIGN, Q8_ERR_INVALID_ARG if too small, Q8_ERR_ALIAS).  Its
+ * contents before the call do not matter; calls that may run at the same
+ * time need workspaces of their own.
  */
 Q8_API int q8_0_gemm_smallm(const float *X, const void *w, float *Y, int64_t m,
-                     int64_t n, int64_t p, void *stream);
+                     int64_t n, int64_t p, void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * *bytes = the workspace q8_0_gemm_smallm(_kernel) needs for (m, n, p) with
+ * `kernel` on the current device (its CU count sets the split of the work).
+ * Enqueues nothing.  Q8_ERR_SHAPE if the kernel does not take the shape.
+ */
+Q8_API int q8_0_gemm_smallm_workspace(int64_t m, int64_t n, int64_t p, int kernel, size_t *bytes);
 
 /* Small-batch kernels (q8_0_gemm_smallm_kernel). */
 #define Q8_SMALLM_AUTO 0  /* the choice q8_0_gemm_smallm makes */
@@ -125,7 +142,8 @@ Q8_API int q8_0_gemm_smallm(const float *X, const void *w, float *Y, int64_t m,
  * meets the same accuracy bar; their roundings differ.
  */
 Q8_API int q8_0_gemm_smallm_kernel(const float *X, const void *w, float *Y, int64_t m,
-                                   int64_t n, int64_t p, int kernel, void *stream);
+                                   int64_t n, int64_t p, int kernel, void *workspace,
+                                   size_t workspace_bytes, void *stream);
 
 /*
  * One decode step's chain of matvecs, recorded once and replayed per token

@@ -59,13 +59,18 @@ Q8_API int q8_0_append_kv(const float *k, const float *v, float *kc, float *vc, 
  *   out[h] = sum_{t < seq} softmax_t(q_h . k_t / sqrt(head_dim)) v_t
  * n_heads a multiple of kv_group; kv_width >= (n_heads / kv_group) *
  * head_dim and a multiple of 4; q, kc and vc 16-byte aligned (Q8_ERR_ALIGN
- * otherwise); 1 <= seq <= Q8_MAX_SEQ.  Uses a library workspace per
- * (device, stream), allocated on first use and grown when needed, like
- * q8_0_gemm_smallm.  Bitwise reproducible for the same inputs and shape.
+ * otherwise); 1 <= seq <= Q8_MAX_SEQ.  workspace: a 256-byte aligned device
+ * buffer of at least q8_0_attention_workspace's bytes, not overlapping q or
+ * out, its contents before the call immaterial (the chunks' partial
+ * softmaxes and arrival counters).  Bitwise reproducible for the same inputs
+ * and shape.
  */
 Q8_API int q8_0_attention_decode(const float *q, const float *kc, const float *vc, float *out,
                           int64_t seq, int64_t kv_width, int64_t head_dim, int64_t n_heads,
-                          int64_t kv_group, void *stream);
+                          int64_t kv_group, void *workspace, size_t workspace_bytes, void *stream);
+
+/* *bytes = the workspace q8_0_attention_decode needs (host only). */
+Q8_API int q8_0_attention_workspace(int64_t seq, int64_t head_dim, int64_t n_heads, size_t *bytes);
 
 /* add_inplace: x[i] += y[i] for i < n. */
 Q8_API int q8_0_add_inplace(float *x, const float *y, int64_t n, void *stream);
@@ -76,9 +81,15 @@ Q8_API int q8_0_silu_hadamard(const float *gate, const float *up, float *out, in
 /*
  * argmax_row: *out (device uint32) = the index of the largest of x[0..n):
  * ties to the lowest index, NaN never wins, 0xFFFFFFFF if every value is
- * NaN.  Exact.  Uses a library workspace per (device, stream).
+ * NaN.  Exact.  workspace: a 256-byte aligned device buffer of at least
+ * q8_0_argmax_workspace's bytes, not overlapping x or out, its contents
+ * before the call immaterial (the workgroups' winners and a counter).
  */
-Q8_API int q8_0_argmax(const float *x, int64_t n, uint32_t *out, void *stream);
+Q8_API int q8_0_argmax(const float *x, int64_t n, uint32_t *out, void *workspace,
+                       size_t workspace_bytes, void *stream);
+
+/* *bytes = the workspace q8_0_argmax needs (host only). */
+Q8_API int q8_0_argmax_workspace(int64_t n, size_t *bytes);
 
 /*
  * A whole decode step of a Qwen3-style model (section "One command buffer"):

@@ -8,13 +8,18 @@ implementation: if the library is missing, importing this package raises.
 The names follow the C ABI:
     gemv(x, w, y=None, stream=None)            -> q8_0_gemv
     gemv(x, w, shape=(c, waves, stages))       -> q8_0_gemv_shaped
-    gemm_smallm(X, w, Y=None, stream=None)     -> q8_0_gemm_smallm
+    gemm_smallm(X, w, Y=None, stream=None)     -> q8_0_gemm_smallm (+ _workspace)
     gemm_smallm(X, w, kernel=SMALLM_MFMA)      -> q8_0_gemm_smallm_kernel
     gemv_q8q8(x, w, y=None), quantize(x)       -> q8_0_gemv_q8q8, q8_0_quantize
     Chain(ops, fuse=True, split_k=False) .run  -> q8_0_chain_create / q8_0_decode_chain
     stream_wait(stream, timeout_ms)            -> q8_0_stream_wait
     rms_norm, rope, append_kv, attention_decode, add_inplace,
     silu_hadamard, argmax                      -> the q8_0_* calls of include/q8step.h
+
+Calls whose kernels need scratch memory take a caller-owned device
+workspace (workspace=, a uint8 tensor); when none is given the binding
+allocates one of the size the library's query returns, on the call's
+stream, through torch's allocator -- the library itself allocates nothing.
     Step(cfg, weights) .reset/.run             -> q8_0_step_create / _reset / _run
 """
 from __future__ import annotations
@@ -54,6 +59,7 @@ BLOCK_QUANTS = 32
 BLOCK_BYTES = 34
 
 EXPORTS = ("q8_0_gemv", "q8_0_gemv_shaped", "q8_0_gemm_smallm", "q8_0_gemm_smallm_kernel",
+           "q8_0_gemm_smallm_workspace", "q8_0_attention_workspace", "q8_0_argmax_workspace",
            "q8_0_chain_create", "q8_0_decode_chain",
            "q8_0_chain_launches", "q8_0_chain_destroy", "q8_0_stream_wait",
            "q8_0_status_string", "q8_0_last_error", "q8_0_gemv_q8q8", "q8_0_quantize",
@@ -104,8 +110,12 @@ def _load():
     vp, i64 = ctypes.c_void_p, ctypes.c_int64
     lib.q8_0_gemv.argtypes = [vp, vp, vp, i64, i64, vp]
     lib.q8_0_gemv_shaped.argtypes = [vp, vp, vp, i64, i64, ctypes.c_int, ctypes.c_int, ctypes.c_int, vp]
-    lib.q8_0_gemm_smallm.argtypes = [vp, vp, vp, i64, i64, i64, vp]
-    lib.q8_0_gemm_smallm_kernel.argtypes = [vp, vp, vp, i64, i64, i64, ctypes.c_int, vp]
+    sz = ctypes.c_size_t
+    lib.q8_0_gemm_smallm.argtypes = [vp, vp, vp, i64, i64, i64, vp, sz, vp]
+    lib.q8_0_gemm_smallm_kernel.argtypes = [vp, vp, vp, i64, i64, i64, ctypes.c_int, vp, sz, vp]
+    lib.q8_0_gemm_smallm_workspace.argtypes = [i64, i64, i64, ctypes.c_int, ctypes.POINTER(sz)]
+    lib.q8_0_attention_workspace.argtypes = [i64, i64, i64, ctypes.POINTER(sz)]
+    lib.q8_0_argmax_workspace.argtypes = [i64, ctypes.POINTER(sz)]
     lib.q8_0_chain_create.argtypes = [ctypes.POINTER(Q8Op), i64, ctypes.c_uint32,
                                       ctypes.POINTER(vp)]
     lib.q8_0_decode_chain.argtypes = [vp, ctypes.c_int, vp]
@@ -122,10 +132,10 @@ def _load():
     lib.q8_0_rms_norm.argtypes = [vp, vp, vp, i64, i64, f32, vp]
     lib.q8_0_rope.argtypes = [vp, i64, i64, i64, f32, vp]
     lib.q8_0_append_kv.argtypes = [vp, vp, vp, vp, i64, i64, vp]
-    lib.q8_0_attention_decode.argtypes = [vp, vp, vp, vp, i64, i64, i64, i64, i64, vp]
+    lib.q8_0_attention_decode.argtypes = [vp, vp, vp, vp, i64, i64, i64, i64, i64, vp, sz, vp]
     lib.q8_0_add_inplace.argtypes = [vp, vp, i64, vp]
     lib.q8_0_silu_hadamard.argtypes = [vp, vp, vp, i64, vp]
-    lib.q8_0_argmax.argtypes = [vp, i64, vp, vp]
+    lib.q8_0_argmax.argtypes = [vp, i64, vp, vp, sz, vp]
     lib.q8_0_step_create.argtypes = [ctypes.POINTER(Q8Model), ctypes.POINTER(vp)]
     lib.q8_0_step_reset.argtypes = [vp, i64, u32, vp]
     lib.q8_0_step_run.argtypes = [vp, i32, vp]
@@ -161,8 +171,28 @@ def gemv_raw(x: int, w: int, y: int, n: int, p: int, stream: int = 0) -> int:
     return lib.q8_0_gemv(x, w, y, n, p, stream)
 
 
-def gemm_smallm_raw(X: int, w: int, Y: int, m: int, n: int, p: int, stream: int = 0) -> int:
-    return lib.q8_0_gemm_smallm(X, w, Y, m, n, p, stream)
+def gemm_smallm_raw(X: int, w: int, Y: int, m: int, n: int, p: int, ws: int = 0, ws_bytes: int = 0,
+                    stream: int = 0) -> int:
+    return lib.q8_0_gemm_smallm(X, w, Y, m, n, p, ws, ws_bytes, stream)
+
+
+def _size_query(fn, *args) -> int:
+    out = ctypes.c_size_t(0)
+    check(fn(*args, ctypes.byref(out)))
+    return int(out.value)
+
+
+def gemm_smallm_workspace(m: int, n: int, p: int, kernel: int = SMALLM_AUTO) -> int:
+    """Workspace bytes q8_0_gemm_smallm needs on the current device."""
+    return _size_query(lib.q8_0_gemm_smallm_workspace, int(m), int(n), int(p), int(kernel))
+
+
+def attention_workspace(seq: int, head_dim: int, n_heads: int) -> int:
+    return _size_query(lib.q8_0_attention_workspace, int(seq), int(head_dim), int(n_heads))
+
+
+def argmax_workspace(n: int) -> int:
+    return _size_query(lib.q8_0_argmax_workspace, int(n))
 
 
 # ------------------------------------------------------------------ torch marshalling
@@ -255,10 +285,31 @@ def quantize(x, xq=None, stream=None):
     return xq
 
 
-def gemm_smallm(X, w, Y=None, stream=None, kernel=None):
+def _workspace(nbytes: int, device, stream, given):
+    """The caller's workspace (a uint8 device tensor), or one of nbytes
+    allocated on the call's stream (so torch's allocator reuses it only after
+    the work queued there)."""
+    torch = _torch()
+    if given is not None:
+        _need(given, torch.uint8, "workspace")
+        return given
+    if nbytes == 0:
+        return None
+    if isinstance(stream, torch.cuda.Stream):
+        with torch.cuda.stream(stream):
+            return torch.empty(nbytes, dtype=torch.uint8, device=device)
+    return torch.empty(nbytes, dtype=torch.uint8, device=device)
+
+
+def _ws_args(ws):
+    return (0, 0) if ws is None else (ws.data_ptr(), ws.numel())
+
+
+def gemm_smallm(X, w, Y=None, stream=None, kernel=None, workspace=None):
     """Y = X W^T for X float32 (m, n), m in 1..16; returns Y float32 (m, p).
 
-    kernel=SMALLM_* runs a named kernel (q8_0_gemm_smallm_kernel)."""
+    kernel=SMALLM_* runs a named kernel (q8_0_gemm_smallm_kernel);
+    workspace: a uint8 device tensor of at least gemm_smallm_workspace bytes."""
     torch = _torch()
     _need(X, torch.float32, "X")
     _need(w, torch.uint8, "w")
@@ -271,11 +322,15 @@ def gemm_smallm(X, w, Y=None, stream=None, kernel=None):
     _need(Y, torch.float32, "Y")
     if tuple(Y.shape) != (m, p):
         raise ValueError("Y must be (%d, %d)" % (m, p))
+    k = SMALLM_AUTO if kernel is None else int(kernel)
+    ws = _workspace(gemm_smallm_workspace(m, n, p, k) if workspace is None else 0, X.device, stream,
+                    workspace)
+    wp, wn = _ws_args(ws)
     if kernel is None:
-        check(lib.q8_0_gemm_smallm(X.data_ptr(), w.data_ptr(), Y.data_ptr(), m, n, p,
+        check(lib.q8_0_gemm_smallm(X.data_ptr(), w.data_ptr(), Y.data_ptr(), m, n, p, wp, wn,
                                    _stream_handle(stream)))
     else:
-        check(lib.q8_0_gemm_smallm_kernel(X.data_ptr(), w.data_ptr(), Y.data_ptr(), m, n, p, int(kernel),
+        check(lib.q8_0_gemm_smallm_kernel(X.data_ptr(), w.data_ptr(), Y.data_ptr(), m, n, p, k, wp, wn,
                                           _stream_handle(stream)))
     return Y
 
@@ -381,7 +436,8 @@ def append_kv(k, v, kc, vc, pos: int, stream=None):
                              int(pos), _stream_handle(stream)))
 
 
-def attention_decode(q, kc, vc, seq: int, head_dim: int, kv_group: int, out=None, stream=None):
+def attention_decode(q, kc, vc, seq: int, head_dim: int, kv_group: int, out=None, stream=None,
+                     workspace=None):
     """Decode attention of q (n_heads, head_dim) over the first seq rows of
     the caches kc, vc (rows, kv_width); returns out (n_heads, head_dim)."""
     torch = _torch()
@@ -399,8 +455,11 @@ def attention_decode(q, kc, vc, seq: int, head_dim: int, kv_group: int, out=None
     if out is None:
         out = torch.empty((n_heads, head_dim), dtype=torch.float32, device=q.device)
     _f32(out, "out", n_heads * head_dim)
+    ws = _workspace(attention_workspace(seq, head_dim, n_heads) if workspace is None else 0, q.device, stream,
+                    workspace)
+    wp, wn = _ws_args(ws)
     check(lib.q8_0_attention_decode(q.data_ptr(), kc.data_ptr(), vc.data_ptr(), out.data_ptr(),
-                                    int(seq), kv_width, head_dim, n_heads, int(kv_group),
+                                    int(seq), kv_width, head_dim, n_heads, int(kv_group), wp, wn,
                                     _stream_handle(stream)))
     return out
 
@@ -424,7 +483,7 @@ def silu_hadamard(gate, up, out=None, stream=None):
     return out
 
 
-def argmax(x, out=None, stream=None):
+def argmax(x, out=None, stream=None, workspace=None):
     """Index of the largest value of x (ties to the lowest index, NaN never
     wins) into out, a one-element int32 device tensor holding the uint32
     index (NO_INDEX, read as -1, when every value is NaN)."""
@@ -433,7 +492,9 @@ def argmax(x, out=None, stream=None):
     if out is None:
         out = torch.empty(1, dtype=torch.int32, device=x.device)
     _need(out, torch.int32, "out")
-    check(lib.q8_0_argmax(x.data_ptr(), x.numel(), out.data_ptr(), _stream_handle(stream)))
+    ws = _workspace(argmax_workspace(x.numel()) if workspace is None else 0, x.device, stream, workspace)
+    wp, wn = _ws_args(ws)
+    check(lib.q8_0_argmax(x.data_ptr(), x.numel(), out.data_ptr(), wp, wn, _stream_handle(stream)))
     return out
 
 

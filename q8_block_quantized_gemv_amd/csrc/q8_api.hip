@@ -81,47 +81,6 @@ int cu_count(int dev) {
     return cus[dev];
 }
 
-// Split-K workspace of the small-batch product, one per (device, stream):
-// calls on one stream run in order and may share it; calls on different
-// streams get different ones.  Grown on demand (hipFree synchronizes the
-// device first), kept until the process ends.  The arrival counters are
-// zeroed once here and left at zero by every launch.
-struct Workspace {
-    float *ws = nullptr;
-    size_t ws_bytes = 0;
-    uint32_t *cnt = nullptr;
-    size_t cnt_n = 0;
-};
-
-int workspace_for(int dev, hipStream_t s, size_t ws_bytes, size_t cnt_n, float **ws_out,
-                  uint32_t **cnt_out) {
-    static std::mutex mu;
-    static std::map<std::pair<int, hipStream_t>, Workspace> pool;
-    std::lock_guard<std::mutex> lk(mu);
-    Workspace &W = pool[{dev, s}];
-    hipError_t e;
-    if (W.ws_bytes < ws_bytes) {
-        if (W.ws && (e = hipFree(W.ws)) != hipSuccess) return fail_hip(e, "hipFree");
-        W.ws = nullptr;
-        W.ws_bytes = 0;
-        if ((e = hipMalloc(&W.ws, ws_bytes)) != hipSuccess) return fail_hip(e, "workspace hipMalloc");
-        W.ws_bytes = ws_bytes;
-    }
-    if (W.cnt_n < cnt_n) {
-        if (W.cnt && (e = hipFree(W.cnt)) != hipSuccess) return fail_hip(e, "hipFree");
-        W.cnt = nullptr;
-        W.cnt_n = 0;
-        if ((e = hipMalloc(&W.cnt, cnt_n * sizeof(uint32_t))) != hipSuccess)
-            return fail_hip(e, "counter hipMalloc");
-        if ((e = hipMemset(W.cnt, 0, cnt_n * sizeof(uint32_t))) != hipSuccess ||
-            (e = hipDeviceSynchronize()) != hipSuccess)
-            return fail_hip(e, "counter hipMemset");
-        W.cnt_n = cnt_n;
-    }
-    *ws_out = W.ws;
-    *cnt_out = W.cnt;
-    return Q8_OK;
-}
 
 }  // namespace q8
 
@@ -301,82 +260,124 @@ GemmDesc plan_gemm(const float *X, const void *w, float *Y, int64_t m, int64_t n
 
 // Stream-K split: up to `wpc` one-wave workgroups per CU, each an equal
 // contiguous range of at least `min_items` (row tile, group) items, so that
-// short ranges do not multiply the partial sums.  Sets fast_wgs and maxc
-// and returns the bytes of partial slots the split needs.
-size_t plan_streamk(GemmDesc &d, int dev, int wpc, int min_items) {
+// short ranges do not multiply the partial sums.  Sets fast_wgs and returns
+// the bytes of partial slots the split needs (two per workgroup).
+size_t plan_streamk(GemmDesc &d, int64_t cus, int wpc, int min_items) {
     const int64_t items = (int64_t)d.row_tiles * d.gsr;
-    const int64_t slots = (int64_t)wpc * cu_count(dev);
+    const int64_t slots = (int64_t)wpc * cus;
     const int64_t wgs = std::max<int64_t>(1, std::min({items, slots, items / min_items}));
     d.fast_wgs = (int32_t)wgs;
-    // a row tile's contributors: at most ceil(G / per) + 1, per = items per workgroup
-    const int64_t per = std::max<int64_t>(1, items / wgs);
-    d.maxc = (int32_t)std::min<int64_t>(wgs, (d.gsr + per - 1) / per + 1);
-    return (size_t)d.row_tiles * d.maxc * 16 * kWave * d.rs * sizeof(float);
+    return (size_t)(2 * wgs) * d.m * kWave * d.rs * sizeof(float);
 }
 
-// m = 2..4 rows on the vector units.
-int smallm_valu(const float *X, const void *w, float *Y, int64_t m, int64_t n, int64_t p,
-                hipStream_t s) {
-    GemmDesc d = plan_gemm(X, w, Y, m, n, p);
-    int dev = 0;
-    hipError_t e = hipGetDevice(&dev);
-    if (e != hipSuccess) return fail_hip(e, "hipGetDevice");
-    // as many workgroups per CU as their double-buffered stages fit in 160 KiB of LDS
-    const int wpc = (160 * 1024) / gemm_valu_stage_bytes((int)m);
-    const size_t part_bytes = plan_streamk(d, dev, wpc, 4);
-    float *ws = nullptr;
-    int rc = workspace_for(dev, s, std::max<size_t>(part_bytes, 256), (size_t)d.row_tiles, &ws, &d.cnt);
-    if (rc) return rc;
-    d.ws = ws;
-    e = launch_gemm_valu(d, (int64_t)d.fast_wgs + (p - d.tail_row0), s);
+// A small-batch product's workspace, every piece 256-byte aligned: the
+// per-row-tile arrival counters (cleared by each call), then (matrix cores)
+// X split into bf16 parts, then the partial slots.
+struct SmallmWs {
+    size_t cnt = 0, xs = 0, part = 0, bytes = 0;   // offsets and total
+};
+size_t align256(size_t b) { return (b + 255) / 256 * 256; }
+
+// A resolved kernel (never Q8_SMALLM_AUTO) for m rows: its plan and
+// workspace.  m = 1 needs none.
+SmallmWs smallm_plan(GemmDesc &d, int kernel, int64_t cus) {
+    SmallmWs L;
+    if (d.m == 1) return L;
+    size_t part = 0, xs = 0;
+    if (kernel == Q8_SMALLM_MFMA) {
+        part = plan_streamk(d, cus, 4, 4);   // four double-buffered one-wave workgroups fill a CU's LDS
+        xs = (size_t)d.nb * kXPartsBytesPerBlock;
+    } else {
+        // as many workgroups per CU as their double-buffered stages fit in 160 KiB of LDS
+        part = plan_streamk(d, cus, (160 * 1024) / gemm_valu_stage_bytes(d.m), 4);
+    }
+    L.cnt = 0;
+    L.xs = align256((size_t)d.row_tiles * sizeof(uint32_t));
+    L.part = L.xs + align256(xs);
+    L.bytes = L.part + align256(part);
+    return L;
+}
+
+// The kernel a small-batch call runs (AUTO resolved), or an error status
+// (negative).
+int smallm_kernel(int kernel, int64_t m, int64_t n, const char *what) {
+    if (kernel < Q8_SMALLM_AUTO || kernel > Q8_SMALLM_VROW1)
+        return fail(Q8_ERR_INVALID_ARG, std::string(what) + ": unknown kernel");
+    const int64_t rs = kGroupBlocks / gcd64(n / kQuants, kGroupBlocks);
+    const bool mfma_ok = rs <= 2, vrow_ok = rs == 1 && m >= 2 && m <= kVrowMaxM;
+    if ((kernel == Q8_SMALLM_MFMA && !(mfma_ok && m >= 2)) ||
+        ((kernel == Q8_SMALLM_VROW || kernel == Q8_SMALLM_VROW1) && !vrow_ok) ||
+        (kernel == Q8_SMALLM_VALU && m < 2))
+        return fail(Q8_ERR_SHAPE, std::string(what) + ": this kernel does not take m=" + std::to_string(m) +
+                                       ", n=" + std::to_string(n));
+    // m = 2..3 with rows of one super-row (n a multiple of 256) run on the
+    // vector units with lanes over (row, block pair): each lane holds the x
+    // values of its two blocks in registers, the quants are converted once
+    // for all rows of X, and no split of X is needed (measured 16-24 % faster
+    // than the matrix cores at m = 2 on the 7B shapes, 9-17 % at m = 3,
+    // slower from m = 4).  Where rows fill super-rows of 1 or 2 (n a multiple
+    // of 128) the matrix cores take the other m >= 2: on the vector units
+    // with a lane per row, the x values every lane needs come through LDS
+    // broadcast reads, m of them per quant and lane.  Other widths run on the
+    // vector units with a lane per row, kValuMaxM rows of X per pass over W.
+    if (kernel == Q8_SMALLM_AUTO) kernel = vrow_ok ? Q8_SMALLM_VROW : mfma_ok ? Q8_SMALLM_MFMA : Q8_SMALLM_VALU;
+    return kernel;
+}
+
+// Workspace bytes of a call (the largest of its launches; they run in order
+// on one stream and share it).
+size_t smallm_bytes(const float *X, const void *w, float *Y, int64_t m, int64_t n, int64_t p, int kernel,
+                    int64_t cus) {
+    if (m == 1) return 0;
+    const int64_t mi = kernel == Q8_SMALLM_VALU ? std::min<int64_t>(kValuMaxM, m) : m;
+    GemmDesc d = plan_gemm(X, w, Y, mi, n, p);
+    return smallm_plan(d, kernel, cus).bytes;
+}
+
+// One launch of a resolved kernel for mi rows on the workspace ws.
+int smallm_launch(const float *X, const void *w, float *Y, int64_t mi, int64_t n, int64_t p, int kernel,
+                  uint8_t *ws, int64_t cus, hipStream_t s) {
+    GemmDesc d = plan_gemm(X, w, Y, mi, n, p);
+    const SmallmWs L = smallm_plan(d, kernel, cus);
+    d.cnt = (uint32_t *)(ws + L.cnt);
+    d.ws = (float *)(ws + L.part);
+    hipError_t e;
+    if (kernel == Q8_SMALLM_MFMA) {
+        d.xs = (const bf16x8 *)(ws + L.xs);
+        e = launch_split_x(X, ws + L.xs, (int)mi, (int)n, d.cnt, d.row_tiles, s);
+        if (e != hipSuccess) return fail_hip(e, "q8_0_gemm_smallm split launch");
+        e = launch_gemm_mfma(d, (int64_t)d.fast_wgs + (p - d.tail_row0), s);
+    } else {
+        e = launch_zero_u32(d.cnt, d.row_tiles, s);
+        if (e != hipSuccess) return fail_hip(e, "q8_0_gemm_smallm counter launch");
+        if (kernel == Q8_SMALLM_VROW || kernel == Q8_SMALLM_VROW1)
+            // two waves per workgroup (the default) share its stages, each
+            // taking half the rows of every group -- two waves per SIMD where
+            // one wave's stages fill a quarter of the LDS (measured 5-10 %
+            // faster than one wave; four waves, held to two per SIMD by their
+            // registers, slower)
+            e = launch_gemm_vrow(d, kernel == Q8_SMALLM_VROW ? 2 : 1, s);
+        else
+            e = launch_gemm_valu(d, (int64_t)d.fast_wgs + (p - d.tail_row0), s);
+    }
     if (e != hipSuccess) return fail_hip(e, "q8_0_gemm_smallm launch");
     return Q8_OK;
 }
 
-// m = 2..3 rows where every row is one super-row: the vector units, lanes
-// over (row, block pair); one launch, no split of X.
-int smallm_vrow(const float *X, const void *w, float *Y, int64_t m, int64_t n, int64_t p,
-                hipStream_t s, int nw) {
-    GemmDesc d = plan_gemm(X, w, Y, m, n, p);
-    int dev = 0;
-    hipError_t e = hipGetDevice(&dev);
-    if (e != hipSuccess) return fail_hip(e, "hipGetDevice");
-    const int wpc = (160 * 1024) / gemm_valu_stage_bytes((int)m);
-    const size_t part_bytes = plan_streamk(d, dev, wpc, 4);
-    float *ws = nullptr;
-    int rc = workspace_for(dev, s, std::max<size_t>(part_bytes, 256), (size_t)d.row_tiles, &ws, &d.cnt);
-    if (rc) return rc;
-    d.ws = ws;
-    // nw = 2 (the default): two waves per workgroup share its stages, each
-    // taking half the rows of every group -- two waves per SIMD where one
-    // wave's stages fill a quarter of the LDS (measured 5-10 % faster than
-    // one wave; four waves, held to two per SIMD by their registers, slower)
-    e = launch_gemm_vrow(d, nw, s);
-    if (e != hipSuccess) return fail_hip(e, "q8_0_gemm_smallm launch");
-    return Q8_OK;
-}
-
-// m = 2..16 rows on the matrix cores (rows of 1 or 2 per super-row).
-int smallm_mfma(const float *X, const void *w, float *Y, int64_t m, int64_t n, int64_t p,
-                hipStream_t s) {
-    GemmDesc d = plan_gemm(X, w, Y, m, n, p);
-    int dev = 0;
-    hipError_t e = hipGetDevice(&dev);
-    if (e != hipSuccess) return fail_hip(e, "hipGetDevice");
-    // four double-buffered one-wave workgroups fill a CU's LDS
-    const size_t part_bytes = plan_streamk(d, dev, 4, 4);
-    // workspace: the split X (3 KiB per block of 32 columns, 256-B aligned), then the
-    // partial slots
-    const size_t xs_bytes = ((size_t)(n / kQuants) * kXPartsBytesPerBlock + 255) / 256 * 256;
-    float *ws = nullptr;
-    int rc = workspace_for(dev, s, xs_bytes + part_bytes, (size_t)d.row_tiles, &ws, &d.cnt);
-    if (rc) return rc;
-    d.xs = (const bf16x8 *)ws;
-    d.ws = (float *)((char *)ws + xs_bytes);
-    e = launch_split_x(X, ws, (int)m, (int)n, s);
-    if (e != hipSuccess) return fail_hip(e, "q8_0_gemm_smallm split launch");
-    e = launch_gemm_mfma(d, (int64_t)d.fast_wgs + (p - d.tail_row0), s);
-    if (e != hipSuccess) return fail_hip(e, "q8_0_gemm_smallm launch");
+// The whole call: m = 1 is the matvec; the vector-unit kernel takes
+// kValuMaxM rows of X per pass over W; the others take all m at once.
+int smallm_run(const float *X, const void *w, float *Y, int64_t m, int64_t n, int64_t p, int kernel,
+               uint8_t *ws, int64_t cus, hipStream_t s) {
+    if (m == 1)
+        return gemv_launch(X, w, Y, n, p, s, kXFloat, RcShape{0, 0, 0}, "q8_0_gemm_smallm launch");
+    if (kernel != Q8_SMALLM_VALU) return smallm_launch(X, w, Y, m, n, p, kernel, ws, cus, s);
+    for (int64_t i0 = 0; i0 < m; i0 += kValuMaxM) {
+        const int64_t mi = std::min<int64_t>(kValuMaxM, m - i0);
+        const int rc = mi == 1 ? gemv_launch(X + i0 * n, w, Y + i0 * p, n, p, s, kXFloat, RcShape{0, 0, 0},
+                                             "q8_0_gemm_smallm launch")
+                               : smallm_launch(X + i0 * n, w, Y + i0 * p, mi, n, p, kernel, ws, cus, s);
+        if (rc) return rc;
+    }
     return Q8_OK;
 }
 
@@ -443,51 +444,50 @@ int q8_0_quantize(const float *x, void *xq, int64_t n, void *stream) {
     return e == hipSuccess ? Q8_OK : fail_hip(e, "q8_0_quantize launch");
 }
 
-int q8_0_gemm_smallm_kernel(const float *X, const void *w, float *Y, int64_t m, int64_t n, int64_t p,
-                            int kernel, void *stream) {
-    int rc = validate(X, w, Y, m, n, p, "q8_0_gemm_smallm");
+int q8_0_gemm_smallm_workspace(int64_t m, int64_t n, int64_t p, int kernel, size_t *bytes) {
+    if (!bytes) return fail(Q8_ERR_INVALID_ARG, "q8_0_gemm_smallm_workspace: bytes is null");
+    *bytes = 0;
+    if (n <= 0 || n % kQuants != 0 || n > Q8_MAX_N || p <= 0 || p > Q8_MAX_P || m < 1 || m > Q8_MAX_M)
+        return fail(Q8_ERR_SHAPE, "q8_0_gemm_smallm_workspace: shape out of range");
+    const int k = smallm_kernel(kernel, m, n, "q8_0_gemm_smallm_workspace");
+    if (k < 0) return k;
+    int dev = 0;
+    int rc = check_device(&dev);
     if (rc) return rc;
-    if (kernel < Q8_SMALLM_AUTO || kernel > Q8_SMALLM_VROW1)
-        return fail(Q8_ERR_INVALID_ARG, "q8_0_gemm_smallm_kernel: unknown kernel");
-    const int64_t rs = kGroupBlocks / gcd64(n / kQuants, kGroupBlocks);
-    const bool mfma_ok = rs <= 2, vrow_ok = rs == 1 && m >= 2 && m <= kVrowMaxM;
-    if ((kernel == Q8_SMALLM_MFMA && !(mfma_ok && m >= 2)) ||
-        ((kernel == Q8_SMALLM_VROW || kernel == Q8_SMALLM_VROW1) && !vrow_ok) ||
-        (kernel == Q8_SMALLM_VALU && m < 2))
-        return fail(Q8_ERR_SHAPE, "q8_0_gemm_smallm_kernel: this kernel does not take m=" + std::to_string(m) +
-                                      ", n=" + std::to_string(n));
-    if ((rc = check_device())) return rc;
-    hipStream_t s = (hipStream_t)stream;
-    if (m == 1)
-        return gemv_launch(X, w, Y, n, p, s, kXFloat, RcShape{0, 0, 0}, "q8_0_gemm_smallm launch");
-    // m = 2..3 with rows of one super-row (n a multiple of 256) run on the
-    // vector units with lanes over (row, block pair): each lane holds the x
-    // values of its two blocks in registers, the quants are converted once
-    // for all rows of X, and no split of X is needed (measured 16-24 % faster
-    // than the matrix cores at m = 2 on the 7B shapes, 9-17 % at m = 3,
-    // slower from m = 4).  Where rows fill super-rows of 1 or 2 (n a multiple
-    // of 128) the matrix cores take the other m >= 2: on the vector units
-    // with a lane per row, the x values every lane needs come through LDS
-    // broadcast reads, m of them per quant and lane.  Other widths run on the
-    // vector units with a lane per row, kValuMaxM rows of X per pass over W.
-    if (kernel == Q8_SMALLM_AUTO) kernel = vrow_ok ? Q8_SMALLM_VROW : mfma_ok ? Q8_SMALLM_MFMA : Q8_SMALLM_VALU;
-    if (kernel == Q8_SMALLM_VROW) return smallm_vrow(X, w, Y, m, n, p, s, 2);
-    if (kernel == Q8_SMALLM_VROW1) return smallm_vrow(X, w, Y, m, n, p, s, 1);
-    if (kernel == Q8_SMALLM_MFMA) return smallm_mfma(X, w, Y, m, n, p, s);
-    // vector units: one pass over W per kValuMaxM rows of X
-    for (int64_t i0 = 0; i0 < m; i0 += kValuMaxM) {
-        const int64_t mi = std::min<int64_t>(kValuMaxM, m - i0);
-        rc = mi == 1 ? gemv_launch(X + i0 * n, w, Y + i0 * p, n, p, s, kXFloat, RcShape{0, 0, 0},
-                                   "q8_0_gemm_smallm launch")
-                     : smallm_valu(X + i0 * n, w, Y + i0 * p, mi, n, p, s);
-        if (rc) return rc;
-    }
+    // (the plan reads only shapes; these pointers are never dereferenced)
+    static const float kDummyX[4] = {0.f, 0.f, 0.f, 0.f};
+    *bytes = smallm_bytes(kDummyX, kDummyX, nullptr, m, n, p, k, cu_count(dev));
     return Q8_OK;
 }
 
+int q8_0_gemm_smallm_kernel(const float *X, const void *w, float *Y, int64_t m, int64_t n, int64_t p,
+                            int kernel, void *workspace, size_t workspace_bytes, void *stream) {
+    int rc = validate(X, w, Y, m, n, p, "q8_0_gemm_smallm");
+    if (rc) return rc;
+    const int k = smallm_kernel(kernel, m, n, "q8_0_gemm_smallm_kernel");
+    if (k < 0) return k;
+    int dev = 0;
+    if ((rc = check_device(&dev))) return rc;
+    const int64_t cus = cu_count(dev);
+    const size_t need = smallm_bytes(X, w, Y, m, n, p, k, cus);
+    if (need > 0) {
+        if (!workspace || ((uintptr_t)workspace & 255u))
+            return fail(Q8_ERR_ALIGN, "q8_0_gemm_smallm: the workspace must be a 256-byte aligned device buffer");
+        if (workspace_bytes < need)
+            return fail(Q8_ERR_INVALID_ARG, "q8_0_gemm_smallm: the workspace holds " + std::to_string(workspace_bytes) +
+                                                " bytes, the call needs " + std::to_string(need) +
+                                                " (q8_0_gemm_smallm_workspace)");
+        const int64_t nb = (int64_t)need;
+        if (overlaps(workspace, nb, X, 4 * m * n) || overlaps(workspace, nb, w, w_bytes(n, p)) ||
+            overlaps(workspace, nb, Y, 4 * m * p))
+            return fail(Q8_ERR_ALIAS, "q8_0_gemm_smallm: the workspace overlaps X, w or Y");
+    }
+    return smallm_run(X, w, Y, m, n, p, k, (uint8_t *)workspace, cus, (hipStream_t)stream);
+}
+
 int q8_0_gemm_smallm(const float *X, const void *w, float *Y, int64_t m, int64_t n, int64_t p,
-                     void *stream) {
-    return q8_0_gemm_smallm_kernel(X, w, Y, m, n, p, Q8_SMALLM_AUTO, stream);
+                     void *workspace, size_t workspace_bytes, void *stream) {
+    return q8_0_gemm_smallm_kernel(X, w, Y, m, n, p, Q8_SMALLM_AUTO, workspace, workspace_bytes, stream);
 }
 
 int q8_0_stream_wait(void *stream, int64_t timeout_ms) {

@@ -16,9 +16,10 @@ struct XParts {
 // A small-batch product (2 <= m <= 16) as its kernels see it.  Workgroups
 // are one wave.  The work is row_tiles (64 super-rows each) x gsr groups of
 // items, split stream-K style into fast_wgs equal contiguous ranges; a row
-// tile shared by several workgroups goes through `maxc` partial slots
-// (16 * 64 * rs floats each) of the workspace `ws` and the per-row-tile
-// arrival counters `cnt` (zero between launches).
+// tile shared by several workgroups goes through partial slots of the
+// workspace `ws` (two per workgroup, m * 64 * rs floats each: its first and
+// its last tile) and the per-row-tile arrival counters `cnt` (zero between
+// launches).
 struct GemmDesc {
     const float *X;
     const bf16x8 *xs;    // X split into exact bf16 parts, 3 KiB per block (k_split_x)
@@ -29,11 +30,9 @@ struct GemmDesc {
     int64_t sr_bytes;
     int32_t n, nb, p, m;
     int32_t rs, nsr, gsr;
-    int32_t maxc;        // partial slots per row tile (>= contributors of any tile)
     int32_t row_tiles;   // ceil(nsr / 64)
     int32_t fast_wgs;    // stream-K workgroups; the tail rows follow, one per workgroup
     int32_t tail_row0;
-    int32_t pad_;
 };
 
 hipError_t launch_gemm_mfma(const GemmDesc &d, int64_t grid, hipStream_t s);
@@ -47,7 +46,10 @@ constexpr int kVrowMaxM = 3;
 constexpr int kValuMaxM = 4;
 // X (m x n) -> the bf16 parts the matrix-core kernel reads: kXPartsBytesPerBlock
 // bytes per block of 32 columns, for up to 16 rows
-hipError_t launch_split_x(const float *X, void *xs, int m, int n, hipStream_t s);
+// (and zeroes the product's cnt_n arrival counters in the same launch)
+hipError_t launch_split_x(const float *X, void *xs, int m, int n, uint32_t *cnt, int64_t cnt_n, hipStream_t s);
+// p[0 .. n) = 0 (a fill kernel: no memset node, so it may be captured)
+hipError_t launch_zero_u32(uint32_t *p, int64_t n, hipStream_t s);
 constexpr int64_t kXPartsBytesPerBlock = 3 * 16 * 4 * 16;   // parts x rows x column groups x bf16x8
 
 }  // namespace q8

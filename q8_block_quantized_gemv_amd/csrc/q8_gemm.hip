@@ -56,11 +56,17 @@ __device__ __forceinline__ int64_t xpart_index(int b, int part, int i, int g) {
     return ((int64_t)b * 3 + part) * 64 + i * 4 + g;
 }
 
+// Threads past the split zero the product's cnt_n arrival counters.
 __global__ __launch_bounds__(256) void k_split_x(const float *__restrict__ X,
-                                                 bf16x8 *__restrict__ xs, int m, int n) {
+                                                 bf16x8 *__restrict__ xs, int m, int n,
+                                                 uint32_t *__restrict__ cnt, int64_t cnt_n) {
     const int nb = n / kQuants;
     const int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x;   // (i, b, g)
-    if (t >= (int64_t)m * nb * 4) return;
+    const int64_t items = (int64_t)m * nb * 4;
+    if (t >= items) {
+        if (t - items < cnt_n) cnt[t - items] = 0u;
+        return;
+    }
     const int g = (int)(t & 3), b = (int)((t >> 2) % nb), i = (int)((t >> 2) / nb);
     const float4 *src = reinterpret_cast<const float4 *>(X) + 2 * t;
     const float4 v0 = src[0], v1 = src[1];
@@ -70,6 +76,11 @@ __global__ __launch_bounds__(256) void k_split_x(const float *__restrict__ X,
     xs[xpart_index(b, 0, i, g)] = o.h;
     xs[xpart_index(b, 1, i, g)] = o.m;
     xs[xpart_index(b, 2, i, g)] = o.l;
+}
+
+__global__ __launch_bounds__(256) void k_zero_u32(uint32_t *__restrict__ p, int64_t n) {
+    const int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (t < n) p[t] = 0u;
 }
 
 // The A operand of block K of group kk for lane (i, g).  Rows i >= m load
@@ -295,27 +306,30 @@ __device__ __forceinline__ void store_tile(const GemmDesc &d, int64_t sr0, int l
     }
 }
 
-// A row tile shared by several workgroups: each parks its share in slot
-// `rank` of the tile's partials (16 X rows x 64 * RS W rows of floats) and
-// counts its arrival; the last of `contributors` to arrive adds the slots in
-// rank order and stores Y.  Partials are written and read with device-scope
-// (sc1) accesses, coherent across the XCDs' L2s by themselves (no fence has
-// to write back or invalidate a whole L2); the wait before the counter makes
+// A row tile shared by several workgroups: each parks its share (m X rows x
+// 64 * RS W rows of floats) in a slot of its own and counts its arrival; the
+// last of `contributors` to arrive adds the shares in workgroup order and
+// stores Y.  A workgroup's items are contiguous, so only its first and last
+// row tiles can be shared: workgroup q owns slots 2q (its first tile) and
+// 2q + 1 (its last).  Partials are written and read with device-scope (sc1)
+// accesses, coherent across the XCDs' L2s by themselves (no fence has to
+// write back or invalidate a whole L2); the wait before the counter makes
 // this share's stores complete before its arrival is counted.
 template <int RS>
-__device__ __forceinline__ float *partial_slot(const GemmDesc &d, int rt, int rank) {
-    constexpr int kSlot = 16 * kWave * RS;
-    return d.ws + ((int64_t)rt * d.maxc + rank) * kSlot;
+__device__ __forceinline__ float *partial_slot(const GemmDesc &d, int rt, int64_t q) {
+    const int64_t N = (int64_t)d.row_tiles * d.gsr;
+    const int64_t first_rt = sk_first_item(q, N, d.fast_wgs) / d.gsr;
+    return d.ws + (2 * q + (rt == first_rt ? 0 : 1)) * ((int64_t)d.m * kWave * RS);
 }
 
 __device__ __forceinline__ void store_partial(float *p, float v) {
     __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-// Called by every lane once this share's partial is stored.
+// Called by every lane once this share's partial is stored; `first` is the
+// tile's first contributing workgroup.
 template <int RS>
-__device__ void arrive_reduce(const GemmDesc &d, int rt, int contributors, int lane) {
-    constexpr int kSlot = 16 * kWave * RS;
+__device__ void arrive_reduce(const GemmDesc &d, int rt, int64_t first, int contributors, int lane) {
     __builtin_amdgcn_s_waitcnt(0);
     asm volatile("" ::: "memory");
     uint32_t prev = 0;
@@ -324,13 +338,12 @@ __device__ void arrive_reduce(const GemmDesc &d, int rt, int contributors, int l
     prev = __shfl(prev, 0, kWave);
     if (prev != (uint32_t)contributors - 1) return;
     asm volatile("" ::: "memory");
-    const float *slots = partial_slot<RS>(d, rt, 0);
     const int64_t sr0 = (int64_t)rt * kWave;
-    // A lane sums kIdx outputs at a time, kBatch slots of each in flight
-    // (32 loads per round trip); every sum still runs in rank order.  Past
-    // the last rank the slot index is clamped and the value dropped; outputs
-    // past the last row of X are not loaded, rows past the matrix's last
-    // row are loaded (in the slot) but not stored.
+    // A lane sums kIdx outputs at a time, kBatch shares of each in flight
+    // (32 loads per round trip); every sum still runs in workgroup order.
+    // Past the last contributor the share index is clamped and the value
+    // dropped; rows past the matrix's last row are loaded (in the slot) but
+    // not stored.
     constexpr int kBatch = 8, kIdx = 4;
     const int total = d.m * (kWave * RS);
     for (int idx0 = lane; idx0 < total; idx0 += kIdx * kWave) {
@@ -338,17 +351,17 @@ __device__ void arrive_reduce(const GemmDesc &d, int rt, int contributors, int l
 #pragma unroll
         for (int k = 0; k < kIdx; ++k) v[k] = 0.f;
         for (int q0 = 0; q0 < contributors; q0 += kBatch) {
+            const float *src[kBatch];
+#pragma unroll
+            for (int u = 0; u < kBatch; ++u) src[u] = partial_slot<RS>(d, rt, first + min(q0 + u, contributors - 1));
             float t[kIdx][kBatch];
 #pragma unroll
             for (int k = 0; k < kIdx; ++k) {
                 const int idx = idx0 + k * kWave;
 #pragma unroll
-                for (int u = 0; u < kBatch; ++u) {
-                    const int q = min(q0 + u, contributors - 1);
-                    t[k][u] = idx < total ? __hip_atomic_load(slots + (int64_t)q * kSlot + idx,
-                                                              __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
+                for (int u = 0; u < kBatch; ++u)
+                    t[k][u] = idx < total ? __hip_atomic_load(src[u] + idx, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
                                           : 0.f;
-                }
             }
 #pragma unroll
             for (int k = 0; k < kIdx; ++k)
@@ -370,10 +383,10 @@ __device__ void arrive_reduce(const GemmDesc &d, int rt, int contributors, int l
 
 // The matrix-core share: lane (j, g) holds C[4g + e][16t + j] of tile t.
 template <int RS>
-__device__ void partial_tile(const GemmDesc &d, int rt, int rank, int contributors, int lane,
+__device__ void partial_tile(const GemmDesc &d, int rt, int64_t b, int64_t first, int contributors, int lane,
                              const f32x4 (&acc)[4][RS]) {
     const int j = lane & 15, g = lane >> 4;
-    float *mine = partial_slot<RS>(d, rt, rank);
+    float *mine = partial_slot<RS>(d, rt, b);
 #pragma unroll
     for (int t = 0; t < 4; ++t)
 #pragma unroll
@@ -383,7 +396,7 @@ __device__ void partial_tile(const GemmDesc &d, int rt, int rank, int contributo
                 if (4 * g + e < d.m)
                     store_partial(mine + (4 * g + e) * (kWave * RS) + (16 * t + j) * RS + k,
                                   acc[t][k][e]);
-    arrive_reduce<RS>(d, rt, contributors, lane);
+    arrive_reduce<RS>(d, rt, first, contributors, lane);
 }
 
 // Workgroup b's range of (row tile, group) items.
@@ -408,7 +421,7 @@ __device__ void gemm_streamk(const GemmDesc &d, int64_t b, uint8_t *stage) {
         } else {
             const int64_t first = sk_owner((int64_t)rt * G, N, W);
             const int64_t contributors = sk_owner((int64_t)rt * G + G - 1, N, W) - first + 1;
-            partial_tile<RS>(d, rt, (int)(b - first), (int)contributors, lane, acc);
+            partial_tile<RS>(d, rt, b, first, (int)contributors, lane, acc);
         }
         it += g1 - g0;
     }
@@ -559,14 +572,14 @@ __device__ void vsmall_streamk(const GemmDesc &d, int64_t b, uint8_t *stage) {
         } else {
             const int64_t first = sk_owner((int64_t)rt * G, N, W);
             const int64_t contributors = sk_owner((int64_t)rt * G + G - 1, N, W) - first + 1;
-            float *mine = partial_slot<RS>(d, rt, (int)(b - first));
+            float *mine = partial_slot<RS>(d, rt, b);
 #pragma unroll
             for (int i = 0; i < M; ++i)
 #pragma unroll
                 for (int k = 0; k < RS; ++k)
                     store_partial(mine + i * (kWave * RS) + lane * RS + k,
                                   combine_slots(acc[i][0][k], acc[i][1][k], acc[i][2][k], acc[i][3][k]));
-            arrive_reduce<RS>(d, rt, (int)contributors, lane);
+            arrive_reduce<RS>(d, rt, first, (int)contributors, lane);
         }
         it += g1 - g0;
     }
@@ -753,7 +766,7 @@ __device__ void vrow_streamk(const GemmDesc &d, int64_t b, uint8_t *stage) {
         } else {
             const int64_t first = sk_owner((int64_t)rt * G, N, W);
             const int64_t contributors = sk_owner((int64_t)rt * G + G - 1, N, W) - first + 1;
-            float *mine = partial_slot<1>(d, rt, (int)(b - first));
+            float *mine = partial_slot<1>(d, rt, b);
             if (holder)
 #pragma unroll
                 for (int i = 0; i < M; ++i) store_partial(mine + i * kWave + row, out[i]);
@@ -761,9 +774,9 @@ __device__ void vrow_streamk(const GemmDesc &d, int64_t b, uint8_t *stage) {
                 // every wave's share is stored before wave 0 counts the arrival
                 __builtin_amdgcn_s_waitcnt(0);
                 __syncthreads();
-                if (wave == 0) arrive_reduce<1>(d, rt, (int)contributors, lane);
+                if (wave == 0) arrive_reduce<1>(d, rt, first, (int)contributors, lane);
             } else {
-                arrive_reduce<1>(d, rt, (int)contributors, lane);
+                arrive_reduce<1>(d, rt, first, (int)contributors, lane);
             }
         }
         it += g1 - g0;
@@ -807,10 +820,16 @@ __global__ __launch_bounds__(NW * kWave) void k_q8_gemm_vrow(GemmDesc d) {
 
 }  // namespace
 
-hipError_t launch_split_x(const float *X, void *xs, int m, int n, hipStream_t s) {
-    const int64_t items = (int64_t)m * (n / kQuants) * 4;
+hipError_t launch_split_x(const float *X, void *xs, int m, int n, uint32_t *cnt, int64_t cnt_n, hipStream_t s) {
+    const int64_t items = (int64_t)m * (n / kQuants) * 4 + cnt_n;
     hipLaunchKernelGGL(k_split_x, dim3((unsigned)((items + 255) / 256)), dim3(256), 0, s, X,
-                       (bf16x8 *)xs, m, n);
+                       (bf16x8 *)xs, m, n, cnt, cnt_n);
+    return hipGetLastError();
+}
+
+hipError_t launch_zero_u32(uint32_t *p, int64_t n, hipStream_t s) {
+    if (n <= 0) return hipSuccess;
+    hipLaunchKernelGGL(k_zero_u32, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, p, n);
     return hipGetLastError();
 }
 

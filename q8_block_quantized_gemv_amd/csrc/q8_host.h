@@ -22,10 +22,6 @@ Q8_HIDDEN bool overlaps(const void *a, int64_t na, const void *b, int64_t nb);
 // The current device exists and is gfx950 (Q8_OK), else a status.
 Q8_HIDDEN int check_device(int *dev_out = nullptr);
 Q8_HIDDEN int cu_count(int dev);
-// A scratch buffer of at least ws_bytes and cnt_n zeroed counters for
-// stream s on device dev, kept across calls (grown when too small).
-Q8_HIDDEN int workspace_for(int dev, hipStream_t s, size_t ws_bytes, size_t cnt_n, float **ws_out,
-                            uint32_t **cnt_out);
 // Per-op inputs and outputs of the decode step's chains (internal): how
 // the op reads its activations (XMode) and writes its result (YMode), and
 // the extra vectors those take (n floats each for the inputs, 16-byte

@@ -10,6 +10,7 @@
 #include <vector>
 
 #include "q8step.h"
+#include "q8_gemm.h"
 #include "q8_host.h"
 #include "q8_step.h"
 
@@ -29,6 +30,29 @@ int argmax_wgs(int64_t n) {
 }
 
 int attn_chunks(int64_t seq) { return (int)((seq + kAttnChunk - 1) / kAttnChunk); }
+
+size_t align256(size_t b) { return (b + 255) / 256 * 256; }
+
+// The standalone calls' workspaces, 256-byte aligned pieces: attention's
+// per-head arrival counters, then each (head, chunk)'s (m, s, acc[head_dim]);
+// argmax's arrival counter, then each workgroup's winning value and index.
+size_t attn_ws_bytes(int64_t seq, int64_t head_dim, int64_t n_heads) {
+    return align256(4 * (size_t)n_heads) +
+           align256((size_t)n_heads * attn_chunks(seq) * (head_dim + 2) * sizeof(float));
+}
+size_t argmax_ws_bytes(int64_t n) {
+    const size_t wgs = (size_t)argmax_wgs(n);
+    return 256 + align256(4 * wgs) + align256(4 * wgs);
+}
+
+int check_workspace(const void *ws, size_t have, size_t need, const char *what) {
+    if (!ws || ((uintptr_t)ws & 255u))
+        return fail(Q8_ERR_ALIGN, std::string(what) + ": the workspace must be a 256-byte aligned device buffer");
+    if (have < need)
+        return fail(Q8_ERR_INVALID_ARG, std::string(what) + ": the workspace holds " + std::to_string(have) +
+                                            " bytes, the call needs " + std::to_string(need));
+    return Q8_OK;
+}
 
 bool head_dim_ok(int64_t hd) { return hd == 64 || hd == 128 || hd == 192 || hd == 256; }
 
@@ -103,23 +127,38 @@ int q8_0_append_kv(const float *k, const float *v, float *kc, float *vc, int64_t
     return e == hipSuccess ? Q8_OK : fail_hip(e, "q8_0_append_kv launch");
 }
 
+int q8_0_attention_workspace(int64_t seq, int64_t head_dim, int64_t n_heads, size_t *bytes) {
+    if (!bytes) return fail(Q8_ERR_INVALID_ARG, "q8_0_attention_workspace: bytes is null");
+    *bytes = 0;
+    if (seq < 1 || seq > INT32_MAX / 2 || head_dim < 1 || head_dim > 256 || n_heads < 1 || n_heads > 65536)
+        return fail(Q8_ERR_SHAPE, "q8_0_attention_workspace: shape out of range");
+    *bytes = attn_ws_bytes(seq, head_dim, n_heads);
+    return Q8_OK;
+}
+
 int q8_0_attention_decode(const float *q, const float *kc, const float *vc, float *out, int64_t seq,
                           int64_t kv_width, int64_t head_dim, int64_t n_heads, int64_t kv_group,
-                          void *stream) {
+                          void *workspace, size_t workspace_bytes, void *stream) {
     int rc = check_attention(q, kc, vc, out, seq, kv_width, head_dim, n_heads, kv_group,
                              "q8_0_attention_decode");
     if (rc) return rc;
-    int dev = 0;
-    if ((rc = check_device(&dev))) return rc;
+    const size_t need = attn_ws_bytes(seq, head_dim, n_heads);
+    if ((rc = check_workspace(workspace, workspace_bytes, need, "q8_0_attention_decode"))) return rc;
+    if (overlaps(workspace, (int64_t)need, out, 4 * n_heads * head_dim) ||
+        overlaps(workspace, (int64_t)need, q, 4 * n_heads * head_dim))
+        return fail(Q8_ERR_ALIAS, "q8_0_attention_decode: the workspace overlaps q or out");
+    if ((rc = check_device())) return rc;
     hipStream_t s = (hipStream_t)stream;
     AttnDesc d;
     std::memset(&d, 0, sizeof d);
     d.q = q; d.kc = kc; d.vc = vc; d.out = out; d.pos_dev = nullptr;
     d.seq = (int)seq; d.kv_width = (int)kv_width; d.head_dim = (int)head_dim;
     d.n_heads = (int)n_heads; d.kv_group = (int)kv_group; d.max_chunks = attn_chunks(seq);
-    const size_t bytes = (size_t)n_heads * d.max_chunks * (head_dim + 2) * sizeof(float);
-    if ((rc = workspace_for(dev, s, bytes, (size_t)n_heads, &d.ws, &d.cnt))) return rc;
-    hipError_t e = launch_attention(d, s);
+    d.cnt = (uint32_t *)workspace;
+    d.ws = (float *)((uint8_t *)workspace + align256(4 * (size_t)n_heads));
+    hipError_t e = hipSuccess;
+    if (d.max_chunks > 1) e = launch_zero_u32(d.cnt, n_heads, s);   // the chunks' arrival counters
+    if (e == hipSuccess) e = launch_attention(d, s);
     return e == hipSuccess ? Q8_OK : fail_hip(e, "q8_0_attention_decode launch");
 }
 
@@ -148,23 +187,35 @@ int q8_0_silu_hadamard(const float *gate, const float *up, float *out, int64_t n
     return e == hipSuccess ? Q8_OK : fail_hip(e, "q8_0_silu_hadamard launch");
 }
 
-int q8_0_argmax(const float *x, int64_t n, uint32_t *out, void *stream) {
+int q8_0_argmax_workspace(int64_t n, size_t *bytes) {
+    if (!bytes) return fail(Q8_ERR_INVALID_ARG, "q8_0_argmax_workspace: bytes is null");
+    *bytes = 0;
+    if (n < 1 || n > INT32_MAX) return fail(Q8_ERR_SHAPE, "q8_0_argmax_workspace: n out of range");
+    *bytes = argmax_ws_bytes(n);
+    return Q8_OK;
+}
+
+int q8_0_argmax(const float *x, int64_t n, uint32_t *out, void *workspace, size_t workspace_bytes,
+                void *stream) {
     if (!x || !out) return fail(Q8_ERR_INVALID_ARG, "q8_0_argmax: null pointer");
     if (n < 1 || n > INT32_MAX) return fail(Q8_ERR_SHAPE, "q8_0_argmax: n out of range");
     if (!aligned4(x) || !aligned4(out)) return fail(Q8_ERR_ALIGN, "q8_0_argmax: alignment");
     if (overlaps(out, 4, x, 4 * n)) return fail(Q8_ERR_ALIAS, "q8_0_argmax: out overlaps x");
-    int dev = 0;
-    int rc = check_device(&dev);
+    const size_t need = argmax_ws_bytes(n);
+    int rc = check_workspace(workspace, workspace_bytes, need, "q8_0_argmax");
     if (rc) return rc;
+    if (overlaps(workspace, (int64_t)need, out, 4) || overlaps(workspace, (int64_t)need, x, 4 * n))
+        return fail(Q8_ERR_ALIAS, "q8_0_argmax: the workspace overlaps x or out");
+    if ((rc = check_device())) return rc;
     hipStream_t s = (hipStream_t)stream;
     const int wgs = argmax_wgs(n);
     ArgmaxDesc d;
     d.x = x; d.n = n; d.out = out; d.pos_dev = nullptr;
-    float *ws = nullptr;
-    if ((rc = workspace_for(dev, s, (size_t)wgs * 8, 1, &ws, &d.cnt))) return rc;
-    d.ws_val = ws;
-    d.ws_idx = (uint32_t *)(ws + wgs);
-    hipError_t e = launch_argmax(d, wgs, s);
+    d.cnt = (uint32_t *)workspace;
+    d.ws_val = (float *)((uint8_t *)workspace + 256);
+    d.ws_idx = (uint32_t *)((uint8_t *)workspace + 256 + align256(4 * (size_t)wgs));
+    hipError_t e = launch_zero_u32(d.cnt, 1, s);   // the arrival counter
+    if (e == hipSuccess) e = launch_argmax(d, wgs, s);
     return e == hipSuccess ? Q8_OK : fail_hip(e, "q8_0_argmax launch");
 }
 

@@ -150,7 +150,7 @@ def test_gemv_shaped_validation(q8, c, waves, st, n, code):
     (17, 256, 0, -2),                           # m as q8_0_gemm_smallm
 ])
 def test_gemm_kernel_validation(q8, m, n, kernel, code):
-    assert q8.lib.q8_0_gemm_smallm_kernel(X, W, Y, m, n, 4, kernel, None) == code
+    assert q8.lib.q8_0_gemm_smallm_kernel(X, W, Y, m, n, 4, kernel, None, 0, None) == code
 
 
 def test_no_device_path(q8):
@@ -161,7 +161,9 @@ def test_no_device_path(q8):
     assert q8.gemv_raw(X, W, Y, 64, 4) == -5
     assert q8.gemm_smallm_raw(X, W, Y, 2, 64, 4) == -5
     assert q8.lib.q8_0_rms_norm(X, W, Y, 64, 1, 1e-6, None) == -5
-    assert q8.lib.q8_0_argmax(X, 8, Y, None) == -5
+    assert q8.lib.q8_0_argmax(X, 8, Y, WS, 1 << 20, None) == -5
+    assert q8.lib.q8_0_attention_decode(X, W, F, Y, 8, 128, 64, 2, 1, WS, 1 << 20, None) == -5
+    assert q8.lib.q8_0_gemm_smallm(X, W, Y, 2, 64, 4, WS, 1 << 20, None) == -5
     layers = (q8.Q8LayerW * 1)(_layer(q8))
     h = ctypes.c_void_p()
     assert q8.lib.q8_0_step_create(ctypes.byref(_model(q8, layers)), ctypes.byref(h)) == -5
@@ -169,6 +171,7 @@ def test_no_device_path(q8):
 
 # ------------------------------------------------------------------ the decode-step calls
 F = 0x40000000   # another fake, 256-B aligned address
+WS = 0x50000000  # a fake workspace
 
 
 @pytest.mark.parametrize("call,code", [
@@ -188,23 +191,23 @@ F = 0x40000000   # another fake, 256-B aligned address
     (lambda L: L.q8_0_append_kv(X, 0, Y, F, 64, 0, None), -1),
     (lambda L: L.q8_0_append_kv(X, W, Y, F, 64, 65536, None), -2),
     (lambda L: L.q8_0_append_kv(X, W, Y + 2, F, 64, 0, None), -3),
-    (lambda L: L.q8_0_attention_decode(X, W, F, 0, 8, 128, 64, 2, 1, None), -1),
-    (lambda L: L.q8_0_attention_decode(X, W, F, Y, 8, 128, 96, 2, 1, None), -2),   # head_dim
-    (lambda L: L.q8_0_attention_decode(X, W, F, Y, 8, 128, 64, 3, 2, None), -2),   # n_heads % group
-    (lambda L: L.q8_0_attention_decode(X, W, F, Y, 8, 64, 64, 2, 1, None), -2),    # kv_width
-    (lambda L: L.q8_0_attention_decode(X, W, F, Y, 0, 128, 64, 2, 1, None), -2),
-    (lambda L: L.q8_0_attention_decode(X, W, F, Y, 65537, 128, 64, 2, 1, None), -2),
-    (lambda L: L.q8_0_attention_decode(X, W, F, X + 4, 8, 128, 64, 2, 1, None), -4),
-    (lambda L: L.q8_0_attention_decode(X + 4, W, F, Y, 8, 128, 64, 2, 1, None), -3),  # q not 16-B
-    (lambda L: L.q8_0_attention_decode(X, W, F, Y, 8, 130, 64, 2, 1, None), -3),      # kv_width % 4
+    (lambda L: L.q8_0_attention_decode(X, W, F, 0, 8, 128, 64, 2, 1, None, 0, None), -1),
+    (lambda L: L.q8_0_attention_decode(X, W, F, Y, 8, 128, 96, 2, 1, None, 0, None), -2),   # head_dim
+    (lambda L: L.q8_0_attention_decode(X, W, F, Y, 8, 128, 64, 3, 2, None, 0, None), -2),   # n_heads % group
+    (lambda L: L.q8_0_attention_decode(X, W, F, Y, 8, 64, 64, 2, 1, None, 0, None), -2),    # kv_width
+    (lambda L: L.q8_0_attention_decode(X, W, F, Y, 0, 128, 64, 2, 1, None, 0, None), -2),
+    (lambda L: L.q8_0_attention_decode(X, W, F, Y, 65537, 128, 64, 2, 1, None, 0, None), -2),
+    (lambda L: L.q8_0_attention_decode(X, W, F, X + 4, 8, 128, 64, 2, 1, None, 0, None), -4),
+    (lambda L: L.q8_0_attention_decode(X + 4, W, F, Y, 8, 128, 64, 2, 1, None, 0, None), -3),  # q not 16-B
+    (lambda L: L.q8_0_attention_decode(X, W, F, Y, 8, 130, 64, 2, 1, None, 0, None), -3),      # kv_width % 4
     (lambda L: L.q8_0_add_inplace(X, 0, 8, None), -1),
     (lambda L: L.q8_0_add_inplace(X, X + 4, 8, None), -4),
     (lambda L: L.q8_0_add_inplace(X, Y, 0, None), -2),
     (lambda L: L.q8_0_silu_hadamard(X, W, X + 4, 8, None), -4),
     (lambda L: L.q8_0_silu_hadamard(X, W, Y, -3, None), -2),
-    (lambda L: L.q8_0_argmax(X, 0, Y, None), -2),
-    (lambda L: L.q8_0_argmax(X, 8, X + 4, None), -4),
-    (lambda L: L.q8_0_argmax(X, 8, Y + 1, None), -3),
+    (lambda L: L.q8_0_argmax(X, 0, Y, None, 0, None), -2),
+    (lambda L: L.q8_0_argmax(X, 8, X + 4, None, 0, None), -4),
+    (lambda L: L.q8_0_argmax(X, 8, Y + 1, None, 0, None), -3),
 ])
 def test_step_op_validation(q8, call, code):
     assert call(q8.lib) == code
@@ -250,3 +253,63 @@ def test_step_create_null_weight(q8):
     assert q8.lib.q8_0_step_reset(None, 0, 0, None) == -1
     assert q8.lib.q8_0_step_launches(None) == -1
     assert q8.lib.q8_0_step_destroy(None) == 0
+
+
+# ------------------------------------------------------------------ caller-owned workspaces
+def _align256(b):
+    return (b + 255) // 256 * 256
+
+
+def _query(fn, *args):
+    out = ctypes.c_size_t(0)
+    rc = fn(*args, ctypes.byref(out))
+    return rc, out.value
+
+
+@pytest.mark.parametrize("seq,hd,nh", [(1, 64, 1), (128, 128, 16), (129, 128, 16), (2048, 128, 28),
+                                       (4097, 256, 3)])
+def test_attention_workspace_size(q8, seq, hd, nh):
+    """Per-head arrival counters, then (m, s, acc[head_dim]) per (head, chunk of 128 rows)."""
+    rc, b = _query(q8.lib.q8_0_attention_workspace, seq, hd, nh)
+    assert rc == 0
+    chunks = -(-seq // 128)
+    assert b == _align256(4 * nh) + _align256(4 * nh * chunks * (hd + 2))
+
+
+@pytest.mark.parametrize("n", [1, 4096, 4097, 151936, 1 << 20, (1 << 31) - 1])
+def test_argmax_workspace_size(q8, n):
+    """A counter, then one (value, index) per workgroup of up to 4096 values (at most 256)."""
+    rc, b = _query(q8.lib.q8_0_argmax_workspace, n)
+    assert rc == 0
+    wgs = max(1, min(256, -(-n // 4096)))
+    assert b == 256 + 2 * _align256(4 * wgs)
+
+
+def test_workspace_queries_refuse(q8):
+    L = q8.lib
+    assert L.q8_0_attention_workspace(8, 64, 2, None) == -1
+    assert _query(L.q8_0_attention_workspace, 0, 64, 2)[0] == -2
+    assert _query(L.q8_0_attention_workspace, 8, 0, 2)[0] == -2
+    assert L.q8_0_argmax_workspace(8, None) == -1
+    assert _query(L.q8_0_argmax_workspace, 0)[0] == -2
+    assert L.q8_0_gemm_smallm_workspace(2, 256, 4, 0, None) == -1
+    assert _query(L.q8_0_gemm_smallm_workspace, 17, 256, 4, 0)[0] == -2
+    assert _query(L.q8_0_gemm_smallm_workspace, 2, 48, 4, 0)[0] == -2
+    assert _query(L.q8_0_gemm_smallm_workspace, 2, 256, 4, 9)[0] == -1     # unknown kernel
+    assert _query(L.q8_0_gemm_smallm_workspace, 4, 256, 4, 3)[0] == -2     # kernel does not take m
+
+
+@pytest.mark.parametrize("call,code", [
+    # null, misaligned, too small, overlapping an operand
+    (lambda L: L.q8_0_attention_decode(X, W, F, Y, 200, 128, 64, 2, 1, None, 1 << 20, None), -3),
+    (lambda L: L.q8_0_attention_decode(X, W, F, Y, 200, 128, 64, 2, 1, WS + 16, 1 << 20, None), -3),
+    (lambda L: L.q8_0_attention_decode(X, W, F, Y, 200, 128, 64, 2, 1, WS, 256, None), -1),
+    (lambda L: L.q8_0_attention_decode(X, W, F, Y, 200, 128, 64, 2, 1, Y - 256, 1 << 20, None), -4),
+    (lambda L: L.q8_0_argmax(X, 8, Y, None, 1 << 20, None), -3),
+    (lambda L: L.q8_0_argmax(X, 8, Y, WS + 4, 1 << 20, None), -3),
+    (lambda L: L.q8_0_argmax(X, 8, Y, WS, 100, None), -1),
+    (lambda L: L.q8_0_argmax(X, 8, Y, X - 512, 1 << 20, None), -4),
+])
+def test_workspace_validation(q8, call, code):
+    assert call(q8.lib) == code
+    assert "workspace" in q8.last_error()
