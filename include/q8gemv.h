@@ -128,6 +128,20 @@ Q8_API int q8_0_gemm_smallm(const float *X, const void *w, float *Y, int64_t m,
  */
 Q8_API int q8_0_gemm_smallm_workspace(int64_t m, int64_t n, int64_t p, int kernel, size_t *bytes);
 
+/*
+ * q8_0_gemm_smallm for callers that cannot allocate or pass device memory of
+ * their own (code under stream capture, tight serving loops, harnesses that
+ * forbid allocation): the same kernels and the same results, with the
+ * workspace taken from a scratch array inside the library, 32 MiB on each
+ * GPU it runs on, held until the process ends.  Allocates nothing.
+ * Q8_ERR_SHAPE (with the bytes needed in q8_0_last_error) when the call needs
+ * more than that (q8_0_gemm_smallm_workspace tells).  Every call on one GPU
+ * shares its array: calls that may overlap on one GPU (other streams,
+ * other threads) race and must not be issued.
+ */
+Q8_API int q8_0_gemm_smallm_noalloc(const float *X, const void *w, float *Y, int64_t m,
+                                    int64_t n, int64_t p, void *stream);
+
 /* Small-batch kernels (q8_0_gemm_smallm_kernel). */
 #define Q8_SMALLM_AUTO 0  /* the choice q8_0_gemm_smallm makes */
 #define Q8_SMALLM_VALU 1  /* vector units, a lane per row, up to 4 rows of X per pass over W */

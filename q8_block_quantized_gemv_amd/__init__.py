@@ -60,6 +60,7 @@ BLOCK_BYTES = 34
 
 EXPORTS = ("q8_0_gemv", "q8_0_gemv_shaped", "q8_0_gemm_smallm", "q8_0_gemm_smallm_kernel",
            "q8_0_gemm_smallm_workspace", "q8_0_attention_workspace", "q8_0_argmax_workspace",
+           "q8_0_gemm_smallm_noalloc",
            "q8_0_chain_create", "q8_0_decode_chain",
            "q8_0_chain_launches", "q8_0_chain_destroy", "q8_0_stream_wait",
            "q8_0_status_string", "q8_0_last_error", "q8_0_gemv_q8q8", "q8_0_quantize",
@@ -106,6 +107,18 @@ def _load():
     if not os.path.exists(LIBRARY):
         raise ImportError("libq8gemv.so is not built; run __graft_entry__.build() "
                           "or python q8_block_quantized_gemv_amd/build.py")
+    # PyTorch's ROCm wheel carries a HIP runtime of its own; the library uses
+    # the system's.  Both work in one process when torch's runtime has
+    # started before the library is loaded (or when the library's runtime
+    # starts first), but not when the library is loaded, torch's runtime
+    # starts, and then the library's: the library then sees no device.  So
+    # torch's runtime is started here, before the library is loaded.
+    try:
+        import torch
+        if torch.cuda.is_available():
+            torch.cuda.init()
+    except ImportError:
+        pass
     lib = ctypes.CDLL(LIBRARY)
     vp, i64 = ctypes.c_void_p, ctypes.c_int64
     lib.q8_0_gemv.argtypes = [vp, vp, vp, i64, i64, vp]
@@ -114,6 +127,7 @@ def _load():
     lib.q8_0_gemm_smallm.argtypes = [vp, vp, vp, i64, i64, i64, vp, sz, vp]
     lib.q8_0_gemm_smallm_kernel.argtypes = [vp, vp, vp, i64, i64, i64, ctypes.c_int, vp, sz, vp]
     lib.q8_0_gemm_smallm_workspace.argtypes = [i64, i64, i64, ctypes.c_int, ctypes.POINTER(sz)]
+    lib.q8_0_gemm_smallm_noalloc.argtypes = [vp, vp, vp, i64, i64, i64, vp]
     lib.q8_0_attention_workspace.argtypes = [i64, i64, i64, ctypes.POINTER(sz)]
     lib.q8_0_argmax_workspace.argtypes = [i64, ctypes.POINTER(sz)]
     lib.q8_0_chain_create.argtypes = [ctypes.POINTER(Q8Op), i64, ctypes.c_uint32,

@@ -383,6 +383,35 @@ int smallm_run(const float *X, const void *w, float *Y, int64_t m, int64_t n, in
 
 }  // namespace
 
+// ===================================================================== static scratch
+// The allocation-free small-batch entry point's scratch: a file-scope device
+// array, kScratchBytes on every GPU the library runs on, held until the
+// process ends.  In host code `scratch` is only a host-side stand-in; the
+// device address of each GPU's copy comes from hipGetSymbolAddress, once per
+// device with that device current, and is the only form passed to kernels.
+constexpr size_t kScratchBytes = size_t(32) << 20;
+static __device__ __align__(256) uint8_t scratch[kScratchBytes];
+
+namespace {
+
+int scratch_for(int dev, uint8_t **out) {
+    static std::mutex mu;
+    static std::vector<uint8_t *> ptrs;
+    std::lock_guard<std::mutex> lk(mu);
+    if ((int)ptrs.size() <= dev) ptrs.resize(dev + 1, nullptr);
+    if (!ptrs[dev]) {
+        void *p = nullptr;
+        hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess || !p) return fail_hip(e != hipSuccess ? e : hipErrorInvalidSymbol,
+                                                   "hipGetSymbolAddress(scratch)");
+        ptrs[dev] = (uint8_t *)p;
+    }
+    *out = ptrs[dev];
+    return Q8_OK;
+}
+
+}  // namespace
+
 // ===================================================================== ABI
 extern "C" {
 
@@ -488,6 +517,27 @@ int q8_0_gemm_smallm_kernel(const float *X, const void *w, float *Y, int64_t m, 
 int q8_0_gemm_smallm(const float *X, const void *w, float *Y, int64_t m, int64_t n, int64_t p,
                      void *workspace, size_t workspace_bytes, void *stream) {
     return q8_0_gemm_smallm_kernel(X, w, Y, m, n, p, Q8_SMALLM_AUTO, workspace, workspace_bytes, stream);
+}
+
+int q8_0_gemm_smallm_noalloc(const float *X, const void *w, float *Y, int64_t m, int64_t n, int64_t p,
+                             void *stream) {
+    int rc = validate(X, w, Y, m, n, p, "q8_0_gemm_smallm_noalloc");
+    if (rc) return rc;
+    const int k = smallm_kernel(Q8_SMALLM_AUTO, m, n, "q8_0_gemm_smallm_noalloc");
+    if (k < 0) return k;
+    int dev = 0;
+    if ((rc = check_device(&dev))) return rc;
+    const int64_t cus = cu_count(dev);
+    const size_t need = smallm_bytes(X, w, Y, m, n, p, k, cus);
+    if (need > kScratchBytes)
+        return fail(Q8_ERR_SHAPE, "q8_0_gemm_smallm_noalloc: m=" + std::to_string(m) + ", n=" + std::to_string(n) +
+                                      ", p=" + std::to_string(p) + " needs " + std::to_string(need) +
+                                      " bytes of scratch, more than the library's " +
+                                      std::to_string(kScratchBytes) +
+                                      "; call q8_0_gemm_smallm with a workspace instead");
+    uint8_t *ptr = nullptr;
+    if (need > 0 && (rc = scratch_for(dev, &ptr))) return rc;
+    return smallm_run(X, w, Y, m, n, p, k, ptr, cus, (hipStream_t)stream);
 }
 
 int q8_0_stream_wait(void *stream, int64_t timeout_ms) {
