@@ -419,13 +419,22 @@ def main():
     kernel_s = time_steps(lambda: chain.run(q8.MODE_EAGER, stream), args.steps) / args.steps / launches
     achieved = nbytes / launches / kernel_s / 1e9
     # a chain of one op is that op's standalone launch (its latency plan);
-    # more independent ops share one fused launch of one-wave tiles of 64
-    # rows.  Template arguments: lanes per row, waves per workgroup, weight
-    # stages in LDS, build mode (0 float activations, 1 activations
-    # quantized to Q8_0)
+    # more independent ops share one fused launch of one-wave tiles with two
+    # weight stages: two lanes per row where the chain's byte-weighted mean
+    # row is 8 groups or more, else one (the library's rule); widths that
+    # are not whole groups take the mixed-width kernel.  Template arguments:
+    # lanes per row, waves per workgroup, weight stages in LDS, build mode
+    # (0 float activations, 1 activations quantized to Q8_0)
     mode = 1 if args.xq else 0
-    kernel = ("k_q8_gemv_rc_fused<1,1,2,%d>" % mode if len(ops_shape) > 1
-              else "k_q8_gemv_rc<C,NWK,NST,%d> (the op's latency plan)" % mode)
+    whole = all(o.n % 256 == 0 for o in ops_shape)
+    wb = [synth.workload_bytes([o]) for o in ops_shape]
+    mean_groups = sum(b * (o.n // 256) for b, o in zip(wb, ops_shape)) / sum(wb)
+    if len(ops_shape) == 1:
+        kernel = "k_q8_gemv_rc<C,NWK,NST,%d> (the op's latency plan)" % mode
+    elif whole:
+        kernel = "k_q8_gemv_rc_fused<%d,1,2,%d>" % (2 if mean_groups >= 8.0 else 1, mode)
+    else:
+        kernel = "k_q8_gemv_mixed<%d>" % mode
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                 "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                 "traffic": measured_traffic(args.workload, kernel),

@@ -211,8 +211,16 @@ RcShape plan_rc_latency(int64_t rows, int64_t G, int xmode, int ymode, int64_t c
 }
 
 // Launch shape of a fused launch of independent ops (a throughput launch):
-// one-wave tiles of 64 rows with two W stages, the steady-state layout.
-constexpr RcShape kFuseShape{1, 1, 2};
+// one-wave tiles with two W stages, the steady-state layout, and one lane
+// per row when rows are short, two when they are long, by the launch's
+// byte-weighted mean of groups per row G.  Measured on the decode chains
+// (kernel time per token): the 0.6B chain (G ~ 5.5) 108 us with one lane,
+// 115 with two; the 7B chain (G ~ 20) 1226 us with one lane, 1190 with two.
+// Two lanes give each row twice the contiguous bytes per load and the
+// workgroup half the rows, but halve the group columns a tile streams.
+RcShape fuse_shape(double mean_groups) {
+    return mean_groups >= 8.0 ? RcShape{2, 1, 2} : RcShape{1, 1, 2};
+}
 
 bool shape_ok(int c, int nwk, int nst) {
     return (c == 1 || c == 2 || c == 4) && (nwk == 1 || nwk == 2 || nwk == 4) && (nst == 1 || nst == 2);
@@ -800,10 +808,14 @@ int q8::chain_create_ex(const q8_0_op *ops, int64_t n_ops, uint32_t flags, const
         // several independent ops in one launch
         bool all_rc = true, one_width = true;
         int64_t rows = 0;
+        double wsum = 0.0, wg = 0.0;   // bytes, and bytes x groups per row
         for (int64_t i = sg.first; i < sg.second; ++i) {
             all_rc = all_rc && ops[i].n % (kQuants * kGroupBlocks) == 0;
             one_width = one_width && ops[i].n == ops[sg.first].n;
             rows += ops[i].p;
+            const double bytes = (double)w_bytes(ops[i].n, ops[i].p);
+            wsum += bytes;
+            wg += bytes * (double)(ops[i].n / (kQuants * kGroupBlocks));
         }
         if (all_rc) {
             // SPLIT_K (ops that wait on the launch before): the latency plan
@@ -812,7 +824,7 @@ int q8::chain_create_ex(const q8_0_op *ops, int64_t n_ops, uint32_t flags, const
             // the smallest finish the launch
             const RcShape sh = latency && one_width
                                    ? plan_rc_latency(rows, ops[sg.first].n / (kQuants * kGroupBlocks), xmode, ymode, cus)
-                                   : kFuseShape;
+                                   : fuse_shape(wg / wsum);
             struct Item { Tile t; int64_t bytes; };
             std::vector<Item> items;
             for (int64_t i = sg.first; i < sg.second; ++i) {
