@@ -167,26 +167,29 @@ def bench_smallm(args, q8, synth, torch, np):
             _, X = synth.generate_smallm(shape, m)
             Xd = torch.from_numpy(X).to("cuda")
             Y = torch.empty((m, shape.p), dtype=torch.float32, device="cuda")
+            # the caller-owned workspace, allocated once per case
+            ws = torch.empty(max(1, q8.gemm_smallm_workspace(m, shape.n, shape.p)), dtype=torch.uint8,
+                             device="cuda")
             if not cases:   # the first case: settle the GPU before anything is timed
                 ring = iter(range(1 << 62))
-                settle(lambda: q8.gemm_smallm(Xd, wd[next(ring) % copies], Y, stream),
+                settle(lambda: q8.gemm_smallm(Xd, wd[next(ring) % copies], Y, stream, workspace=ws),
                        torch.cuda.synchronize)
             for i in range(copies):
-                q8.gemm_smallm(Xd, wd[i], Y, stream)
+                q8.gemm_smallm(Xd, wd[i], Y, stream, workspace=ws)
             k = max(copies * 4, 20)
             torch.cuda.synchronize()
             e0 = torch.cuda.Event(enable_timing=True)
             e1 = torch.cuda.Event(enable_timing=True)
             e0.record(stream)
             for i in range(k):
-                q8.gemm_smallm(Xd, wd[i % copies], Y, stream)
+                q8.gemm_smallm(Xd, wd[i % copies], Y, stream, workspace=ws)
             e1.record(stream)
             torch.cuda.synchronize()
             t = e0.elapsed_time(e1) / 1e3 / k
             nbytes = synth.workload_bytes([shape], m)
             t_hbm = nbytes / 8e12
             if m <= 3 and shape.n % 256 == 0:
-                kernel, unit = "k_q8_gemm_vrow<%d>" % m, "alu"
+                kernel, unit = "k_zero_u32 + k_q8_gemm_vrow<%d,2>" % m, "alu"
                 t_cmp = (1 + m) * shape.n * shape.p / VALU_LANE_OPS
             else:
                 kernel, unit = "k_split_x + k_q8_gemm_mfma<1>", "mfma"

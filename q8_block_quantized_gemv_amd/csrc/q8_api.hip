@@ -1,6 +1,7 @@
 // q8_api.hip -- the C ABI of include/q8gemv.h: validation, launch planning,
 // decode chains (hipGraph record/replay) and the bounded stream wait.
 #include <algorithm>
+#include <atomic>
 #include <chrono>
 #include <cmath>
 #include <cstdint>
@@ -9,6 +10,7 @@
 #include <cstring>
 #include <map>
 #include <mutex>
+#include <random>
 #include <string>
 #include <thread>
 #include <vector>
@@ -279,8 +281,9 @@ size_t plan_streamk(GemmDesc &d, int64_t cus, int wpc, int min_items) {
 }
 
 // A small-batch product's workspace, every piece 256-byte aligned: the
-// per-row-tile arrival counters (cleared by each call), then (matrix cores)
-// X split into bf16 parts, then the partial slots.
+// per-row-tile arrival counters (8 bytes each, tagged with the call's epoch,
+// so they need no clearing), then (matrix cores) X split into bf16 parts,
+// then the partial slots.
 struct SmallmWs {
     size_t cnt = 0, xs = 0, part = 0, bytes = 0;   // offsets and total
 };
@@ -300,7 +303,7 @@ SmallmWs smallm_plan(GemmDesc &d, int kernel, int64_t cus) {
         part = plan_streamk(d, cus, (160 * 1024) / gemm_valu_stage_bytes(d.m), 4);
     }
     L.cnt = 0;
-    L.xs = align256((size_t)d.row_tiles * sizeof(uint32_t));
+    L.xs = align256((size_t)d.row_tiles * sizeof(unsigned long long));
     L.part = L.xs + align256(xs);
     L.bytes = L.part + align256(part);
     return L;
@@ -342,22 +345,30 @@ size_t smallm_bytes(const float *X, const void *w, float *Y, int64_t m, int64_t 
     return smallm_plan(d, kernel, cus).bytes;
 }
 
+// A call's tag for its arrival counters: distinct for 2^32 - 1 calls of the
+// process, from a start that differs between processes, never 0.
+uint32_t next_epoch() {
+    static std::atomic<uint32_t> e{(uint32_t)std::random_device{}() | 1u};
+    uint32_t v;
+    do v = e.fetch_add(1u, std::memory_order_relaxed); while (v == 0u);
+    return v;
+}
+
 // One launch of a resolved kernel for mi rows on the workspace ws.
 int smallm_launch(const float *X, const void *w, float *Y, int64_t mi, int64_t n, int64_t p, int kernel,
                   uint8_t *ws, int64_t cus, hipStream_t s) {
     GemmDesc d = plan_gemm(X, w, Y, mi, n, p);
     const SmallmWs L = smallm_plan(d, kernel, cus);
-    d.cnt = (uint32_t *)(ws + L.cnt);
+    d.cnt = (unsigned long long *)(ws + L.cnt);
     d.ws = (float *)(ws + L.part);
+    d.epoch = next_epoch();
     hipError_t e;
     if (kernel == Q8_SMALLM_MFMA) {
         d.xs = (const bf16x8 *)(ws + L.xs);
-        e = launch_split_x(X, ws + L.xs, (int)mi, (int)n, d.cnt, d.row_tiles, s);
+        e = launch_split_x(X, ws + L.xs, (int)mi, (int)n, s);
         if (e != hipSuccess) return fail_hip(e, "q8_0_gemm_smallm split launch");
         e = launch_gemm_mfma(d, (int64_t)d.fast_wgs + (p - d.tail_row0), s);
     } else {
-        e = launch_zero_u32(d.cnt, d.row_tiles, s);
-        if (e != hipSuccess) return fail_hip(e, "q8_0_gemm_smallm counter launch");
         if (kernel == Q8_SMALLM_VROW || kernel == Q8_SMALLM_VROW1)
             // two waves per workgroup (the default) share its stages, each
             // taking half the rows of every group -- two waves per SIMD where

@@ -18,21 +18,22 @@ struct XParts {
 // items, split stream-K style into fast_wgs equal contiguous ranges; a row
 // tile shared by several workgroups goes through partial slots of the
 // workspace `ws` (two per workgroup, m * 64 * rs floats each: its first and
-// its last tile) and the per-row-tile arrival counters `cnt` (zero between
-// launches).
+// its last tile) and the per-row-tile arrival counters `cnt`, tagged with the
+// call's epoch so that they need no clearing.
 struct GemmDesc {
     const float *X;
     const bf16x8 *xs;    // X split into exact bf16 parts, 3 KiB per block (k_split_x)
     const uint8_t *w;
     float *Y;
     float *ws;
-    uint32_t *cnt;
+    unsigned long long *cnt;   // per row tile: the epoch (high 32 bits) and the arrivals
     int64_t sr_bytes;
     int32_t n, nb, p, m;
     int32_t rs, nsr, gsr;
     int32_t row_tiles;   // ceil(nsr / 64)
     int32_t fast_wgs;    // stream-K workgroups; the tail rows follow, one per workgroup
     int32_t tail_row0;
+    uint32_t epoch;      // this call's tag on the arrival counters (never 0)
 };
 
 hipError_t launch_gemm_mfma(const GemmDesc &d, int64_t grid, hipStream_t s);
@@ -46,8 +47,7 @@ constexpr int kVrowMaxM = 3;
 constexpr int kValuMaxM = 4;
 // X (m x n) -> the bf16 parts the matrix-core kernel reads: kXPartsBytesPerBlock
 // bytes per block of 32 columns, for up to 16 rows
-// (and zeroes the product's cnt_n arrival counters in the same launch)
-hipError_t launch_split_x(const float *X, void *xs, int m, int n, uint32_t *cnt, int64_t cnt_n, hipStream_t s);
+hipError_t launch_split_x(const float *X, void *xs, int m, int n, hipStream_t s);
 // p[0 .. n) = 0 (a fill kernel: no memset node, so it may be captured)
 hipError_t launch_zero_u32(uint32_t *p, int64_t n, hipStream_t s);
 constexpr int64_t kXPartsBytesPerBlock = 3 * 16 * 4 * 16;   // parts x rows x column groups x bf16x8

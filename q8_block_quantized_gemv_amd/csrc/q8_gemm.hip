@@ -56,17 +56,11 @@ __device__ __forceinline__ int64_t xpart_index(int b, int part, int i, int g) {
     return ((int64_t)b * 3 + part) * 64 + i * 4 + g;
 }
 
-// Threads past the split zero the product's cnt_n arrival counters.
 __global__ __launch_bounds__(256) void k_split_x(const float *__restrict__ X,
-                                                 bf16x8 *__restrict__ xs, int m, int n,
-                                                 uint32_t *__restrict__ cnt, int64_t cnt_n) {
+                                                 bf16x8 *__restrict__ xs, int m, int n) {
     const int nb = n / kQuants;
     const int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x;   // (i, b, g)
-    const int64_t items = (int64_t)m * nb * 4;
-    if (t >= items) {
-        if (t - items < cnt_n) cnt[t - items] = 0u;
-        return;
-    }
+    if (t >= (int64_t)m * nb * 4) return;
     const int g = (int)(t & 3), b = (int)((t >> 2) % nb), i = (int)((t >> 2) / nb);
     const float4 *src = reinterpret_cast<const float4 *>(X) + 2 * t;
     const float4 v0 = src[0], v1 = src[1];
@@ -311,19 +305,42 @@ __device__ __forceinline__ void store_tile(const GemmDesc &d, int64_t sr0, int l
 // last of `contributors` to arrive adds the shares in workgroup order and
 // stores Y.  A workgroup's items are contiguous, so only its first and last
 // row tiles can be shared: workgroup q owns slots 2q (its first tile) and
-// 2q + 1 (its last).  Partials are written and read with device-scope (sc1)
+// 2q + 1 (its last).  Of a tile's contributors only the first can hold it as
+// its last tile.  Partials are written and read with device-scope (sc1)
 // accesses, coherent across the XCDs' L2s by themselves (no fence has to
 // write back or invalidate a whole L2); the wait before the counter makes
 // this share's stores complete before its arrival is counted.
 template <int RS>
-__device__ __forceinline__ float *partial_slot(const GemmDesc &d, int rt, int64_t q) {
-    const int64_t N = (int64_t)d.row_tiles * d.gsr;
-    const int64_t first_rt = sk_first_item(q, N, d.fast_wgs) / d.gsr;
-    return d.ws + (2 * q + (rt == first_rt ? 0 : 1)) * ((int64_t)d.m * kWave * RS);
+__device__ __forceinline__ float *partial_slot(const GemmDesc &d, int64_t q, int last) {
+    return d.ws + (2 * q + last) * ((int64_t)d.m * kWave * RS);
 }
 
 __device__ __forceinline__ void store_partial(float *p, float v) {
     __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Arrival at tile rt's counter: 64 bits, the call's epoch above the count of
+// arrivals.  An arrival adds one; if the counter held another epoch (an
+// earlier call's, or whatever the workspace held), this call's epoch with no
+// arrivals is swapped in -- unless another arrival of the call already did
+// -- and the arrival is made again.  So no call has to clear the counters
+// and the last to arrive needs no reset; only arrivals that meet an old
+// epoch take the extra round trips.  Returns the call's arrivals before this
+// one.  (Only this call's arrivals set its epoch, so the second add always
+// meets it.)
+__device__ __forceinline__ uint32_t arrive(const GemmDesc &d, int rt) {
+    unsigned long long *c = d.cnt + rt;
+    constexpr unsigned long long kHi = 0xFFFFFFFF00000000ull;
+    const unsigned long long tag = (unsigned long long)d.epoch << 32;
+    for (;;) {
+        const unsigned long long old = __hip_atomic_fetch_add(c, 1ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        if ((old & kHi) == tag) return (uint32_t)old;
+        unsigned long long cur = old + 1ull;
+        while ((cur & kHi) != tag &&
+               !__hip_atomic_compare_exchange_strong(c, &cur, tag, __ATOMIC_RELAXED, __ATOMIC_RELAXED,
+                                                    __HIP_MEMORY_SCOPE_AGENT)) {
+        }
+    }
 }
 
 // Called by every lane once this share's partial is stored; `first` is the
@@ -333,12 +350,15 @@ __device__ void arrive_reduce(const GemmDesc &d, int rt, int64_t first, int cont
     __builtin_amdgcn_s_waitcnt(0);
     asm volatile("" ::: "memory");
     uint32_t prev = 0;
-    if (lane == 0)
-        prev = __hip_atomic_fetch_add(d.cnt + rt, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (lane == 0) prev = arrive(d, rt);
     prev = __shfl(prev, 0, kWave);
     if (prev != (uint32_t)contributors - 1) return;
     asm volatile("" ::: "memory");
     const int64_t sr0 = (int64_t)rt * kWave;
+    // the first contributor's share is in its last-tile slot when its range
+    // began before this tile
+    const int64_t N = (int64_t)d.row_tiles * d.gsr;
+    const int first_last = sk_first_item(first, N, d.fast_wgs) < (int64_t)rt * d.gsr ? 1 : 0;
     // A lane sums kIdx outputs at a time, kBatch shares of each in flight
     // (32 loads per round trip); every sum still runs in workgroup order.
     // Past the last contributor the share index is clamped and the value
@@ -353,7 +373,10 @@ __device__ void arrive_reduce(const GemmDesc &d, int rt, int64_t first, int cont
         for (int q0 = 0; q0 < contributors; q0 += kBatch) {
             const float *src[kBatch];
 #pragma unroll
-            for (int u = 0; u < kBatch; ++u) src[u] = partial_slot<RS>(d, rt, first + min(q0 + u, contributors - 1));
+            for (int u = 0; u < kBatch; ++u) {
+                const int q = min(q0 + u, contributors - 1);
+                src[u] = partial_slot<RS>(d, first + q, q == 0 ? first_last : 0);
+            }
             float t[kIdx][kBatch];
 #pragma unroll
             for (int k = 0; k < kIdx; ++k) {
@@ -377,16 +400,14 @@ __device__ void arrive_reduce(const GemmDesc &d, int rt, int64_t first, int cont
             if (idx < total && sr0 + rr / RS < d.nsr) d.Y[(int64_t)ii * d.p + sr0 * RS + rr] = v[k];
         }
     }
-    if (lane == 0)   // ready for the next launch
-        __hip_atomic_store(d.cnt + rt, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 // The matrix-core share: lane (j, g) holds C[4g + e][16t + j] of tile t.
 template <int RS>
-__device__ void partial_tile(const GemmDesc &d, int rt, int64_t b, int64_t first, int contributors, int lane,
-                             const f32x4 (&acc)[4][RS]) {
+__device__ void partial_tile(const GemmDesc &d, int rt, int64_t b, int last, int64_t first, int contributors,
+                             int lane, const f32x4 (&acc)[4][RS]) {
     const int j = lane & 15, g = lane >> 4;
-    float *mine = partial_slot<RS>(d, rt, b);
+    float *mine = partial_slot<RS>(d, b, last);
 #pragma unroll
     for (int t = 0; t < 4; ++t)
 #pragma unroll
@@ -404,7 +425,8 @@ template <int RS>
 __device__ void gemm_streamk(const GemmDesc &d, int64_t b, uint8_t *stage) {
     const int lane = lane_id();
     const int64_t G = d.gsr, N = (int64_t)d.row_tiles * G, W = d.fast_wgs;
-    int64_t it = sk_first_item(b, N, W);
+    const int64_t it0 = sk_first_item(b, N, W);
+    int64_t it = it0;
     const int64_t end = sk_first_item(b + 1, N, W);
     while (it < end) {
         const int rt = (int)(it / G);
@@ -421,7 +443,7 @@ __device__ void gemm_streamk(const GemmDesc &d, int64_t b, uint8_t *stage) {
         } else {
             const int64_t first = sk_owner((int64_t)rt * G, N, W);
             const int64_t contributors = sk_owner((int64_t)rt * G + G - 1, N, W) - first + 1;
-            partial_tile<RS>(d, rt, b, first, (int)contributors, lane, acc);
+            partial_tile<RS>(d, rt, b, it != it0, first, (int)contributors, lane, acc);
         }
         it += g1 - g0;
     }
@@ -546,7 +568,8 @@ template <int RS, int M>
 __device__ void vsmall_streamk(const GemmDesc &d, int64_t b, uint8_t *stage) {
     const int lane = lane_id();
     const int64_t G = d.gsr, N = (int64_t)d.row_tiles * G, W = d.fast_wgs;
-    int64_t it = sk_first_item(b, N, W);
+    const int64_t it0 = sk_first_item(b, N, W);
+    int64_t it = it0;
     const int64_t end = sk_first_item(b + 1, N, W);
     while (it < end) {
         const int rt = (int)(it / G);
@@ -572,7 +595,7 @@ __device__ void vsmall_streamk(const GemmDesc &d, int64_t b, uint8_t *stage) {
         } else {
             const int64_t first = sk_owner((int64_t)rt * G, N, W);
             const int64_t contributors = sk_owner((int64_t)rt * G + G - 1, N, W) - first + 1;
-            float *mine = partial_slot<RS>(d, rt, b);
+            float *mine = partial_slot<RS>(d, b, it != it0);
 #pragma unroll
             for (int i = 0; i < M; ++i)
 #pragma unroll
@@ -727,7 +750,8 @@ __device__ void vrow_streamk(const GemmDesc &d, int64_t b, uint8_t *stage) {
     const int wave = NW > 1 ? wave_id() : 0;
     const int r = lane >> 2, c = lane & 3;
     const int64_t G = d.gsr, N = (int64_t)d.row_tiles * G, W = d.fast_wgs;
-    int64_t it = sk_first_item(b, N, W);
+    const int64_t it0 = sk_first_item(b, N, W);
+    int64_t it = it0;
     const int64_t end = sk_first_item(b + 1, N, W);
     while (it < end) {
         const int rt = (int)(it / G);
@@ -766,7 +790,7 @@ __device__ void vrow_streamk(const GemmDesc &d, int64_t b, uint8_t *stage) {
         } else {
             const int64_t first = sk_owner((int64_t)rt * G, N, W);
             const int64_t contributors = sk_owner((int64_t)rt * G + G - 1, N, W) - first + 1;
-            float *mine = partial_slot<1>(d, rt, b);
+            float *mine = partial_slot<1>(d, b, it != it0);
             if (holder)
 #pragma unroll
                 for (int i = 0; i < M; ++i) store_partial(mine + i * kWave + row, out[i]);
@@ -820,10 +844,10 @@ __global__ __launch_bounds__(NW * kWave) void k_q8_gemm_vrow(GemmDesc d) {
 
 }  // namespace
 
-hipError_t launch_split_x(const float *X, void *xs, int m, int n, uint32_t *cnt, int64_t cnt_n, hipStream_t s) {
-    const int64_t items = (int64_t)m * (n / kQuants) * 4 + cnt_n;
+hipError_t launch_split_x(const float *X, void *xs, int m, int n, hipStream_t s) {
+    const int64_t items = (int64_t)m * (n / kQuants) * 4;
     hipLaunchKernelGGL(k_split_x, dim3((unsigned)((items + 255) / 256)), dim3(256), 0, s, X,
-                       (bf16x8 *)xs, m, n, cnt, cnt_n);
+                       (bf16x8 *)xs, m, n);
     return hipGetLastError();
 }
 
