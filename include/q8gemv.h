@@ -233,6 +233,52 @@ Q8_API int q8_0_quantize(const float *x, void *xq, int64_t n, void *stream);
 /* Run one token's chain on `stream` in the given mode. */
 Q8_API int q8_0_decode_chain(q8_0_chain *chain, int mode, void *stream);
 
+/*
+ * Launch plans, host only (nothing is enqueued, no device is needed): how
+ * q8_0_gemv and q8_0_chain_create would launch on a GPU of `cus` compute
+ * units (256 on MI355X).  For inspection and for tests of the planners.
+ *
+ * q8_0_gemv_plan: rows of whole 272-byte groups (n % 256 == 0) run on the
+ * rows-and-group-slots kernel with `lanes_per_row` (1, 2, 4) lanes per row,
+ * `waves` (1, 2, 4) waves sharing a tile's rows and `stages` (1, 2) weight
+ * stages, one workgroup per tile of 64 / lanes_per_row rows; other widths on
+ * the super-row kernel (lanes_per_row = stages = 0, `waves` per workgroup).
+ */
+Q8_API int q8_0_gemv_plan(int64_t n, int64_t p, int64_t cus, int *lanes_per_row, int *waves,
+                          int *stages, int64_t *workgroups);
+
+#define Q8_LAUNCH_ROWS 0         /* one op, rows-and-group-slots kernel (its latency plan) */
+#define Q8_LAUNCH_SUPERROWS 1    /* one op of another width, super-row kernel */
+#define Q8_LAUNCH_FUSED 2        /* independent ops of whole-group rows in one launch */
+#define Q8_LAUNCH_FUSED_MIXED 3  /* independent ops of mixed widths in one launch */
+
+/* One launch of a chain's token. */
+typedef struct q8_0_launch_plan {
+    int32_t kind;           /* Q8_LAUNCH_* */
+    int32_t lanes_per_row;  /* as q8_0_gemv_plan (0: super-row kernel) */
+    int32_t waves;
+    int32_t stages;
+    int64_t first_op;       /* the launch computes ops[first_op .. first_op + n_ops) */
+    int64_t n_ops;
+    int64_t workgroups;
+    int64_t first_tile;     /* fused launches: workgroup g does item first_tile + g of the
+                               tile lists; -1 for one-op launches */
+} q8_0_launch_plan;
+
+/*
+ * q8_0_chain_plan: the launches q8_0_chain_create(ops, n_ops, flags) would
+ * record, in order, and for fused launches the item of every workgroup:
+ * tile_op[k] = the op (index into ops), tile_id[k] = the tile within it (of
+ * 64 / lanes_per_row rows; in mixed launches bit 31 marks a tail tile, rows
+ * past the op's super-rows).  The same validation as q8_0_chain_create (the
+ * pointers are compared, never dereferenced).  *n_launches and *n_tiles are
+ * always set; the arrays are filled only when they are given and hold that
+ * many entries.
+ */
+Q8_API int q8_0_chain_plan(const q8_0_op *ops, int64_t n_ops, uint32_t flags, int64_t cus,
+                           q8_0_launch_plan *launches, int64_t max_launches, int64_t *n_launches,
+                           int64_t *tile_op, uint32_t *tile_id, int64_t max_tiles, int64_t *n_tiles);
+
 /* Kernel launches one token costs (1 .. n_ops); negative status on a bad handle. */
 Q8_API int q8_0_chain_launches(const q8_0_chain *chain);
 

@@ -60,7 +60,7 @@ BLOCK_BYTES = 34
 
 EXPORTS = ("q8_0_gemv", "q8_0_gemv_shaped", "q8_0_gemm_smallm", "q8_0_gemm_smallm_kernel",
            "q8_0_gemm_smallm_workspace", "q8_0_attention_workspace", "q8_0_argmax_workspace",
-           "q8_0_gemm_smallm_noalloc",
+           "q8_0_gemm_smallm_noalloc", "q8_0_gemv_plan", "q8_0_chain_plan",
            "q8_0_chain_create", "q8_0_decode_chain",
            "q8_0_chain_launches", "q8_0_chain_destroy", "q8_0_stream_wait",
            "q8_0_status_string", "q8_0_last_error", "q8_0_gemv_q8q8", "q8_0_quantize",
@@ -82,6 +82,16 @@ class Q8Error(RuntimeError):
 class Q8Op(ctypes.Structure):
     _fields_ = [("x", ctypes.c_void_p), ("w", ctypes.c_void_p), ("y", ctypes.c_void_p),
                 ("n", ctypes.c_int64), ("p", ctypes.c_int64)]
+
+
+class Q8LaunchPlan(ctypes.Structure):
+    _fields_ = [("kind", ctypes.c_int32), ("lanes_per_row", ctypes.c_int32), ("waves", ctypes.c_int32),
+                ("stages", ctypes.c_int32), ("first_op", ctypes.c_int64), ("n_ops", ctypes.c_int64),
+                ("workgroups", ctypes.c_int64), ("first_tile", ctypes.c_int64)]
+
+
+LAUNCH_ROWS, LAUNCH_SUPERROWS, LAUNCH_FUSED, LAUNCH_FUSED_MIXED = 0, 1, 2, 3
+TAIL_BIT = 0x80000000
 
 
 class Q8LayerW(ctypes.Structure):
@@ -128,6 +138,12 @@ def _load():
     lib.q8_0_gemm_smallm_kernel.argtypes = [vp, vp, vp, i64, i64, i64, ctypes.c_int, vp, sz, vp]
     lib.q8_0_gemm_smallm_workspace.argtypes = [i64, i64, i64, ctypes.c_int, ctypes.POINTER(sz)]
     lib.q8_0_gemm_smallm_noalloc.argtypes = [vp, vp, vp, i64, i64, i64, vp]
+    ip = ctypes.POINTER(ctypes.c_int)
+    lib.q8_0_gemv_plan.argtypes = [i64, i64, i64, ip, ip, ip, ctypes.POINTER(i64)]
+    lib.q8_0_chain_plan.argtypes = [ctypes.POINTER(Q8Op), i64, ctypes.c_uint32, i64,
+                                    ctypes.POINTER(Q8LaunchPlan), i64, ctypes.POINTER(i64),
+                                    ctypes.POINTER(i64), ctypes.POINTER(ctypes.c_uint32), i64,
+                                    ctypes.POINTER(i64)]
     lib.q8_0_attention_workspace.argtypes = [i64, i64, i64, ctypes.POINTER(sz)]
     lib.q8_0_argmax_workspace.argtypes = [i64, ctypes.POINTER(sz)]
     lib.q8_0_chain_create.argtypes = [ctypes.POINTER(Q8Op), i64, ctypes.c_uint32,
@@ -207,6 +223,33 @@ def attention_workspace(seq: int, head_dim: int, n_heads: int) -> int:
 
 def argmax_workspace(n: int) -> int:
     return _size_query(lib.q8_0_argmax_workspace, int(n))
+
+
+def gemv_plan(n: int, p: int, cus: int = 256):
+    """(lanes_per_row, waves, stages, workgroups) of q8_0_gemv for (n, p) on a
+    GPU of `cus` compute units (host only)."""
+    c, w, st, g = ctypes.c_int(), ctypes.c_int(), ctypes.c_int(), ctypes.c_int64()
+    check(lib.q8_0_gemv_plan(int(n), int(p), int(cus), ctypes.byref(c), ctypes.byref(w), ctypes.byref(st),
+                             ctypes.byref(g)))
+    return c.value, w.value, st.value, g.value
+
+
+def chain_plan(ops, flags: int = 0, cus: int = 256):
+    """The launches q8_0_chain_create would record for ops, a sequence of
+    (x, w, y, n, p) with raw device addresses (compared, never read): a list
+    of dicts, and for fused launches each workgroup's (op, tile) items as two
+    lists.  Host only."""
+    arr = (Q8Op * len(ops))(*[Q8Op(int(x), int(w), int(y), int(n), int(p)) for x, w, y, n, p in ops])
+    nl, nt = ctypes.c_int64(), ctypes.c_int64()
+    check(lib.q8_0_chain_plan(arr, len(ops), flags, cus, None, 0, ctypes.byref(nl), None, None, 0,
+                              ctypes.byref(nt)))
+    L = (Q8LaunchPlan * max(1, nl.value))()
+    top = (ctypes.c_int64 * max(1, nt.value))()
+    tid = (ctypes.c_uint32 * max(1, nt.value))()
+    check(lib.q8_0_chain_plan(arr, len(ops), flags, cus, L, nl.value, ctypes.byref(nl), top, tid, nt.value,
+                              ctypes.byref(nt)))
+    launches = [{f: getattr(L[k], f) for f, _ in Q8LaunchPlan._fields_} for k in range(nl.value)]
+    return launches, list(top[:nt.value]), list(tid[:nt.value])
 
 
 # ------------------------------------------------------------------ torch marshalling

@@ -682,58 +682,32 @@ void set_extra(OpDesc &d, const OpExtra *e) {
     d.w2 = (const uint8_t *)e->w2;
 }
 
-}  // namespace
+struct ChainPlan {
+    struct SegInfo {
+        q8_0_chain::Launch L;
+        size_t op0, tile0;   // the launch's op descriptors and tiles in h_ops, h_tiles
+        int64_t first, n;    // its ops: ops[first .. first + n)
+    };
+    std::vector<OpDesc> h_ops;
+    std::vector<Tile> h_tiles;
+    std::vector<SegInfo> info;
+};
 
-int q8::chain_issue(const q8_0_chain *c, hipStream_t s) {
-    for (const auto &L : c->launches) {
-        hipError_t e = issue(L, s);
-        if (e != hipSuccess) return fail_hip(e, "chain launch");
-    }
-    return Q8_OK;
-}
-
-std::vector<std::pair<int64_t, int64_t>> q8::chain_segments(const q8_0_op *ops, int64_t n_ops, bool per_op,
-                                                            const OpExtra *extra) {
-    std::vector<std::pair<int64_t, int64_t>> segs;
-    if (per_op) {
-        for (int64_t i = 0; i < n_ops; ++i) segs.push_back({i, i + 1});
-        return segs;
-    }
-    int64_t b = 0;
-    for (int64_t i = 1; i <= n_ops; ++i) {
-        bool cut = (i == n_ops);
-        for (int64_t j = b; !cut && j < i; ++j)
-            cut = depends(ops[j], ops[i], extra ? &extra[j] : nullptr, extra ? &extra[i] : nullptr);
-        if (cut) { segs.push_back({b, i}); b = i; }
-    }
-    return segs;
-}
-
-extern "C" {
-
-int q8_0_chain_create(const q8_0_op *ops, int64_t n_ops, uint32_t flags, q8_0_chain **out) {
-    return q8::chain_create_ex(ops, n_ops, flags, nullptr, out);
-}
-
-}  // extern "C"
-
-int q8::chain_create_ex(const q8_0_op *ops, int64_t n_ops, uint32_t flags, const OpExtra *extra,
-                        q8_0_chain **out) {
-    if (!out) return fail(Q8_ERR_INVALID_ARG, "q8_0_chain_create: out is null");
-    *out = nullptr;
+// Argument checks of a chain (touch no device state).
+int validate_chain(const q8_0_op *ops, int64_t n_ops, uint32_t flags, const OpExtra *extra, const char *what) {
     if (!ops || n_ops <= 0 || n_ops > Q8_MAX_CHAIN_OPS)
-        return fail(Q8_ERR_INVALID_ARG, "q8_0_chain_create: need 1..65535 ops");
+        return fail(Q8_ERR_INVALID_ARG, std::string(what) + ": need 1..65535 ops");
     if (flags & ~(uint32_t)(Q8_CHAIN_PER_OP | Q8_CHAIN_SPLIT_K | Q8_CHAIN_XQ))
-        return fail(Q8_ERR_INVALID_ARG, "q8_0_chain_create: unknown flags");
+        return fail(Q8_ERR_INVALID_ARG, std::string(what) + ": unknown flags");
     const int emode = extra ? extra[0].mode : kXFloat;
     const int eout = extra ? extra[0].out_mode : kYPlain;
     if (extra && (flags & Q8_CHAIN_XQ))
-        return fail(Q8_ERR_INVALID_ARG, "q8_0_chain_create: these inputs have no integer form");
+        return fail(Q8_ERR_INVALID_ARG, std::string(what) + ": these inputs have no integer form");
     auto a16 = [](const void *p) { return p && ((uintptr_t)p & 15u) == 0; };
     auto a4 = [](const void *p) { return p && ((uintptr_t)p & 3u) == 0; };
     for (int64_t i = 0; i < n_ops; ++i) {
-        const std::string what = "q8_0_chain_create op " + std::to_string(i);
-        int rc = validate(ops[i].x, ops[i].w, ops[i].y, 1, ops[i].n, ops[i].p, what.c_str());
+        const std::string tag = std::string(what) + " op " + std::to_string(i);
+        int rc = validate(ops[i].x, ops[i].w, ops[i].y, 1, ops[i].n, ops[i].p, tag.c_str());
         if (rc) return rc;
         if (!extra) continue;
         const OpExtra &e = extra[i];
@@ -763,37 +737,34 @@ int q8::chain_create_ex(const q8_0_op *ops, int64_t n_ops, uint32_t flags, const
             ok = ok && whole && a16(e.w2) && (e.mode == kXFloat || e.mode == kXNormScale) &&
                  !overlaps(ops[i].y, yb, e.w2, w_bytes(n, p));
         else ok = ok && e.out_mode == kYPlain;
-        if (!ok) return fail(Q8_ERR_INVALID_ARG, what + ": extra inputs missing, misaligned, aliased or not "
+        if (!ok) return fail(Q8_ERR_INVALID_ARG, tag + ": extra inputs missing, misaligned, aliased or not "
                                                         "supported for this width");
     }
-    int dev = 0;
-    int rc = check_device(&dev);
-    if (rc) return rc;
+    return Q8_OK;
+}
 
-    q8_0_chain *c = new q8_0_chain();
-    c->device = dev;
-    c->flags = flags;
-    c->ops.assign(ops, ops + n_ops);
+// The launches of a chain on a GPU of `cus` compute units: the op
+// descriptors and tile tables of fused launches, and each launch with its
+// kind, shape and grid (device pointers left unset).  Host only.
+int plan_chain(const q8_0_op *ops, int64_t n_ops, uint32_t flags, const OpExtra *extra, int64_t cus,
+               const char *what, ChainPlan &plan) {
+    // Runs of mutually independent ops (or single ops).  Every plan
+    // computes each op's outputs in the same fixed order, so the chain gives
+    // the bits of standalone calls whatever the launch shapes.
+    const int emode = extra ? extra[0].mode : kXFloat;
     const int xmode = (flags & Q8_CHAIN_XQ) ? kXQuant : emode;
-    const int ymode = eout;
+    const int ymode = extra ? extra[0].out_mode : kYPlain;
     const bool per_op = (flags & Q8_CHAIN_PER_OP) != 0;
     const bool latency = (flags & Q8_CHAIN_SPLIT_K) != 0;
-    const int64_t cus = cu_count(dev);
-
-    // ---- plan: runs of mutually independent ops (or single ops).  Every
-    // plan computes each op's outputs in the same fixed order, so the chain
-    // gives the bits of standalone calls whatever the launch shapes.
     const auto segs = chain_segments(ops, n_ops, per_op, extra);
-    std::vector<OpDesc> h_ops;
-    std::vector<Tile> h_tiles;
-    struct SegInfo {
-        q8_0_chain::Launch L;
-        size_t op0, tile0;
-    };
-    std::vector<SegInfo> info;
+    std::vector<OpDesc> &h_ops = plan.h_ops;
+    std::vector<Tile> &h_tiles = plan.h_tiles;
+    auto &info = plan.info;
     for (auto &sg : segs) {
-        SegInfo si;
+        ChainPlan::SegInfo si;
         std::memset(&si, 0, sizeof si);
+        si.first = sg.first;
+        si.n = sg.second - sg.first;
         si.L.xmode = xmode;
         si.L.ymode = ymode;
         si.op0 = h_ops.size();
@@ -858,10 +829,8 @@ int q8::chain_create_ex(const q8_0_op *ops, int64_t n_ops, uint32_t flags, const
         } else {
             // widths that are not all multiples of 256: one-wave workgroups,
             // each tile in its own layout, largest tiles first (plain output)
-            if (ymode != kYPlain) {
-                chain_free(c);
-                return fail(Q8_ERR_INVALID_ARG, "q8_0_chain_create: output modes need n % 256 == 0");
-            }
+            if (ymode != kYPlain)
+                return fail(Q8_ERR_INVALID_ARG, std::string(what) + ": output modes need n % 256 == 0");
             struct Item { Tile t; int64_t bytes; };
             std::vector<Item> items;
             for (int64_t i = sg.first; i < sg.second; ++i) {
@@ -884,6 +853,148 @@ int q8::chain_create_ex(const q8_0_op *ops, int64_t n_ops, uint32_t flags, const
         }
         info.push_back(si);
     }
+    return Q8_OK;
+}
+}  // namespace
+
+int q8::chain_issue(const q8_0_chain *c, hipStream_t s) {
+    for (const auto &L : c->launches) {
+        hipError_t e = issue(L, s);
+        if (e != hipSuccess) return fail_hip(e, "chain launch");
+    }
+    return Q8_OK;
+}
+
+std::vector<std::pair<int64_t, int64_t>> q8::chain_segments(const q8_0_op *ops, int64_t n_ops, bool per_op,
+                                                            const OpExtra *extra) {
+    std::vector<std::pair<int64_t, int64_t>> segs;
+    if (per_op) {
+        for (int64_t i = 0; i < n_ops; ++i) segs.push_back({i, i + 1});
+        return segs;
+    }
+    int64_t b = 0;
+    for (int64_t i = 1; i <= n_ops; ++i) {
+        bool cut = (i == n_ops);
+        for (int64_t j = b; !cut && j < i; ++j)
+            cut = depends(ops[j], ops[i], extra ? &extra[j] : nullptr, extra ? &extra[i] : nullptr);
+        if (cut) { segs.push_back({b, i}); b = i; }
+    }
+    return segs;
+}
+
+extern "C" {
+
+int q8_0_chain_create(const q8_0_op *ops, int64_t n_ops, uint32_t flags, q8_0_chain **out) {
+    return q8::chain_create_ex(ops, n_ops, flags, nullptr, out);
+}
+
+int q8_0_chain_plan(const q8_0_op *ops, int64_t n_ops, uint32_t flags, int64_t cus, q8_0_launch_plan *launches,
+                    int64_t max_launches, int64_t *n_launches, int64_t *tile_op, uint32_t *tile_id,
+                    int64_t max_tiles, int64_t *n_tiles) {
+    if (!n_launches || !n_tiles) return fail(Q8_ERR_INVALID_ARG, "q8_0_chain_plan: n_launches and n_tiles are needed");
+    *n_launches = 0;
+    *n_tiles = 0;
+    if (cus < 1 || cus > 4096) return fail(Q8_ERR_INVALID_ARG, "q8_0_chain_plan: cus must be in 1..4096");
+    int rc = validate_chain(ops, n_ops, flags, nullptr, "q8_0_chain_plan");
+    if (rc) return rc;
+    ChainPlan plan;
+    if ((rc = plan_chain(ops, n_ops, flags, nullptr, cus, "q8_0_chain_plan", plan))) return rc;
+    *n_launches = (int64_t)plan.info.size();
+    *n_tiles = (int64_t)plan.h_tiles.size();
+    if (launches && max_launches >= *n_launches) {
+        for (size_t k = 0; k < plan.info.size(); ++k) {
+            const auto &si = plan.info[k];
+            q8_0_launch_plan &o = launches[k];
+            std::memset(&o, 0, sizeof o);
+            o.first_op = si.first;
+            o.n_ops = si.n;
+            o.workgroups = si.L.grid;
+            o.first_tile = -1;
+            switch (si.L.kind) {
+                case q8_0_chain::Launch::kSingleRc:
+                    o.kind = Q8_LAUNCH_ROWS;
+                    break;
+                case q8_0_chain::Launch::kSingleSuperrow:
+                    o.kind = Q8_LAUNCH_SUPERROWS;
+                    o.waves = kWaves;
+                    break;
+                case q8_0_chain::Launch::kFusedRc:
+                    o.kind = Q8_LAUNCH_FUSED;
+                    o.first_tile = (int64_t)si.tile0;
+                    break;
+                case q8_0_chain::Launch::kFusedMixed:
+                    o.kind = Q8_LAUNCH_FUSED_MIXED;
+                    o.first_tile = (int64_t)si.tile0;
+                    o.lanes_per_row = 1;   // rc tiles of one lane per row, one wave, two stages
+                    o.waves = 1;
+                    o.stages = 2;
+                    break;
+            }
+            if (si.L.kind == q8_0_chain::Launch::kSingleRc || si.L.kind == q8_0_chain::Launch::kFusedRc) {
+                o.lanes_per_row = si.L.shape.c;
+                o.waves = si.L.shape.nwk;
+                o.stages = si.L.shape.nst;
+            }
+        }
+    }
+    if (tile_op && tile_id && max_tiles >= *n_tiles) {
+        for (const auto &si : plan.info) {
+            if (si.L.kind != q8_0_chain::Launch::kFusedRc && si.L.kind != q8_0_chain::Launch::kFusedMixed) continue;
+            for (int64_t g = 0; g < si.L.grid; ++g) {
+                const Tile &t = plan.h_tiles[si.tile0 + g];
+                tile_op[si.tile0 + g] = si.first + (int64_t)t.op;
+                tile_id[si.tile0 + g] = t.tile;
+            }
+        }
+    }
+    return Q8_OK;
+}
+
+int q8_0_gemv_plan(int64_t n, int64_t p, int64_t cus, int *lanes_per_row, int *waves, int *stages,
+                   int64_t *workgroups) {
+    if (!lanes_per_row || !waves || !stages || !workgroups)
+        return fail(Q8_ERR_INVALID_ARG, "q8_0_gemv_plan: null output");
+    if (n <= 0 || n % kQuants != 0 || n > Q8_MAX_N || p <= 0 || p > Q8_MAX_P)
+        return fail(Q8_ERR_SHAPE, "q8_0_gemv_plan: shape out of range");
+    if (cus < 1 || cus > 4096) return fail(Q8_ERR_INVALID_ARG, "q8_0_gemv_plan: cus must be in 1..4096");
+    // (the plan reads only shapes; these pointers are never dereferenced)
+    static const float kDummy[4] = {0.f, 0.f, 0.f, 0.f};
+    OpDesc d = plan_op(kDummy, kDummy, nullptr, 1, n, p, true, kWaves);
+    if (d.rs == 1) {
+        const RcShape sh = plan_rc_latency(p, d.gsr, kXFloat, kYPlain, cus);
+        *lanes_per_row = sh.c;
+        *waves = sh.nwk;
+        *stages = sh.nst;
+        *workgroups = rc_tiles_for(p, sh.c);
+    } else {
+        *lanes_per_row = 0;
+        *waves = kWaves;
+        *stages = 0;
+        *workgroups = tiles_of(d, kWaves);
+    }
+    return Q8_OK;
+}
+
+}  // extern "C"
+
+int q8::chain_create_ex(const q8_0_op *ops, int64_t n_ops, uint32_t flags, const OpExtra *extra,
+                        q8_0_chain **out) {
+    if (!out) return fail(Q8_ERR_INVALID_ARG, "q8_0_chain_create: out is null");
+    *out = nullptr;
+    int rc = validate_chain(ops, n_ops, flags, extra, "q8_0_chain_create");
+    if (rc) return rc;
+    int dev = 0;
+    if ((rc = check_device(&dev))) return rc;
+    ChainPlan plan;
+    if ((rc = plan_chain(ops, n_ops, flags, extra, cu_count(dev), "q8_0_chain_create", plan))) return rc;
+    const std::vector<OpDesc> &h_ops = plan.h_ops;
+    const std::vector<Tile> &h_tiles = plan.h_tiles;
+    const auto &info = plan.info;
+
+    q8_0_chain *c = new q8_0_chain();
+    c->device = dev;
+    c->flags = flags;
+    c->ops.assign(ops, ops + n_ops);
     // device block: op descriptors, then tiles
     const size_t ob = h_ops.size() * sizeof(OpDesc);
     const size_t t_at = (ob + 255) / 256 * 256;
