@@ -189,7 +189,7 @@ def bench_smallm(args, q8, synth, torch, np):
             nbytes = synth.workload_bytes([shape], m)
             t_hbm = nbytes / 8e12
             if m <= 3 and shape.n % 256 == 0:
-                kernel, unit = "k_zero_u32 + k_q8_gemm_vrow<%d,2>" % m, "alu"
+                kernel, unit = "k_q8_gemm_vrow<%d,2>" % m, "alu"
                 t_cmp = (1 + m) * shape.n * shape.p / VALU_LANE_OPS
             else:
                 kernel, unit = "k_split_x + k_q8_gemm_mfma<1>", "mfma"

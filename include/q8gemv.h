@@ -34,8 +34,9 @@
  *     need scratch memory (the small-batch product; in q8step.h the
  *     standalone attention and argmax) take a caller-owned device workspace
  *     whose size a host-only query returns; it is 256-byte aligned, may hold
- *     anything beforehand (each call clears what must start at zero), and
- *     must not be used by two calls that may overlap.
+ *     anything beforehand (the small-batch arrival counters carry a per-call
+ *     tag; attention and argmax clear theirs), and must not be used by two
+ *     calls that may overlap.
  *   - Results are bitwise reproducible run to run for the same inputs,
  *     shapes and device: every sum runs in a fixed order (the small-batch
  *     product counts arrivals with an atomic counter, but adds partial sums
