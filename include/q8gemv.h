@@ -242,11 +242,13 @@ Q8_API int q8_0_decode_chain(q8_0_chain *chain, int mode, void *stream);
  * q8_0_gemv_plan: rows of whole 272-byte groups (n % 256 == 0) run on the
  * rows-and-group-slots kernel with `lanes_per_row` (1, 2, 4) lanes per row,
  * `waves` (1, 2, 4) waves sharing a tile's rows and `stages` (1, 2) weight
- * stages, one workgroup per tile of 64 / lanes_per_row rows; other widths on
- * the super-row kernel (lanes_per_row = stages = 0, `waves` per workgroup).
+ * stages, one workgroup per tile of `tile_rows` rows (at most
+ * 64 / lanes_per_row: fewer where that spreads the tiles evenly over the
+ * CUs); other widths on the super-row kernel (lanes_per_row = stages =
+ * tile_rows = 0, `waves` per workgroup).
  */
 Q8_API int q8_0_gemv_plan(int64_t n, int64_t p, int64_t cus, int *lanes_per_row, int *waves,
-                          int *stages, int64_t *workgroups);
+                          int *stages, int *tile_rows, int64_t *workgroups);
 
 #define Q8_LAUNCH_ROWS 0         /* one op, rows-and-group-slots kernel (its latency plan) */
 #define Q8_LAUNCH_SUPERROWS 1    /* one op of another width, super-row kernel */
@@ -259,6 +261,10 @@ typedef struct q8_0_launch_plan {
     int32_t lanes_per_row;  /* as q8_0_gemv_plan (0: super-row kernel) */
     int32_t waves;
     int32_t stages;
+    int32_t tile_rows;      /* rows per tile: as q8_0_gemv_plan for one-op launches, 64 / lanes_per_row
+                               for fused ones (mixed: 64 rows or one super-row tile); 0 for the
+                               super-row kernel */
+    int32_t pad_;
     int64_t first_op;       /* the launch computes ops[first_op .. first_op + n_ops) */
     int64_t n_ops;
     int64_t workgroups;
@@ -270,8 +276,8 @@ typedef struct q8_0_launch_plan {
  * q8_0_chain_plan: the launches q8_0_chain_create(ops, n_ops, flags) would
  * record, in order, and for fused launches the item of every workgroup:
  * tile_op[k] = the op (index into ops), tile_id[k] = the tile within it (of
- * 64 / lanes_per_row rows; in mixed launches bit 31 marks a tail tile, rows
- * past the op's super-rows).  The same validation as q8_0_chain_create (the
+ * tile_rows rows; in mixed launches bit 31 marks a tail tile, rows past the
+ * op's super-rows).  The same validation as q8_0_chain_create (the
  * pointers are compared, never dereferenced).  *n_launches and *n_tiles are
  * always set; the arrays are filled only when they are given and hold that
  * many entries.

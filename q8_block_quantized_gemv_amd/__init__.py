@@ -86,7 +86,8 @@ class Q8Op(ctypes.Structure):
 
 class Q8LaunchPlan(ctypes.Structure):
     _fields_ = [("kind", ctypes.c_int32), ("lanes_per_row", ctypes.c_int32), ("waves", ctypes.c_int32),
-                ("stages", ctypes.c_int32), ("first_op", ctypes.c_int64), ("n_ops", ctypes.c_int64),
+                ("stages", ctypes.c_int32), ("tile_rows", ctypes.c_int32), ("pad_", ctypes.c_int32),
+                ("first_op", ctypes.c_int64), ("n_ops", ctypes.c_int64),
                 ("workgroups", ctypes.c_int64), ("first_tile", ctypes.c_int64)]
 
 
@@ -139,7 +140,7 @@ def _load():
     lib.q8_0_gemm_smallm_workspace.argtypes = [i64, i64, i64, ctypes.c_int, ctypes.POINTER(sz)]
     lib.q8_0_gemm_smallm_noalloc.argtypes = [vp, vp, vp, i64, i64, i64, vp]
     ip = ctypes.POINTER(ctypes.c_int)
-    lib.q8_0_gemv_plan.argtypes = [i64, i64, i64, ip, ip, ip, ctypes.POINTER(i64)]
+    lib.q8_0_gemv_plan.argtypes = [i64, i64, i64, ip, ip, ip, ip, ctypes.POINTER(i64)]
     lib.q8_0_chain_plan.argtypes = [ctypes.POINTER(Q8Op), i64, ctypes.c_uint32, i64,
                                     ctypes.POINTER(Q8LaunchPlan), i64, ctypes.POINTER(i64),
                                     ctypes.POINTER(i64), ctypes.POINTER(ctypes.c_uint32), i64,
@@ -226,12 +227,12 @@ def argmax_workspace(n: int) -> int:
 
 
 def gemv_plan(n: int, p: int, cus: int = 256):
-    """(lanes_per_row, waves, stages, workgroups) of q8_0_gemv for (n, p) on a
-    GPU of `cus` compute units (host only)."""
-    c, w, st, g = ctypes.c_int(), ctypes.c_int(), ctypes.c_int(), ctypes.c_int64()
+    """(lanes_per_row, waves, stages, tile_rows, workgroups) of q8_0_gemv for
+    (n, p) on a GPU of `cus` compute units (host only)."""
+    c, w, st, tr, g = ctypes.c_int(), ctypes.c_int(), ctypes.c_int(), ctypes.c_int(), ctypes.c_int64()
     check(lib.q8_0_gemv_plan(int(n), int(p), int(cus), ctypes.byref(c), ctypes.byref(w), ctypes.byref(st),
-                             ctypes.byref(g)))
-    return c.value, w.value, st.value, g.value
+                             ctypes.byref(tr), ctypes.byref(g)))
+    return c.value, w.value, st.value, tr.value, g.value
 
 
 def chain_plan(ops, flags: int = 0, cus: int = 256):

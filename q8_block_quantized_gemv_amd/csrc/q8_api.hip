@@ -197,19 +197,42 @@ int64_t tiles_of(const OpDesc &d, int nw) {
 //    one-wave tiles of 32 rows, half the workgroups, are fastest.
 // One W stage per wave: twice the waves fit, which measured faster than a
 // second stage at every one of these shapes.
-RcShape plan_rc_latency(int64_t rows, int64_t G, int xmode, int ymode, int64_t cus) {
+//
+// One op (`single`): where the tiles are all resident but come two or more
+// to a CU, some CUs get one tile more than others and finish last; tiles of
+// fewer rows, ceil(rows / (k * cus)) for k tiles a CU, even the CUs out.
+// Measured on lone launches: the 7B gate|up pair 30.0 -> 28.3 us (32 -> 26
+// rows a tile), and the 7B gate alone 18.9 us in one-wave tiles of 16 rows
+// -> 18.1 us in two-wave tiles of 25 (of 32) rows.  Where one round of tiles
+// leaves CUs idle (k = 1) smaller tiles measured no faster (7B q, k, down:
+// latency, not rows, sets their time), and for many rounds (lm_heads) the
+// rule gives whole tiles anyway.  Not for the residual-add output, whose
+// tiles hold whole 16-row blocks.
+RcShape plan_rc_latency(int64_t rows, int64_t G, int xmode, int ymode, int64_t cus, bool single) {
     auto resident = [&](RcShape sh) {
         const int b = gemv_rc_lds_bytes(sh, xmode, ymode);
         return b > 0 ? cus * std::max(1, kLdsPerCu / b) : 0;
     };
+    auto balanced = [&](RcShape sh) {
+        const int R = kWave / sh.c;
+        const int64_t t = (rows + R - 1) / R, k = (t + cus - 1) / cus;
+        if (!single || ymode == kYResAdd || k < 2 || t > resident(sh)) return sh;
+        const int64_t tr = (rows + k * cus - 1) / (k * cus);
+        if (tr < R) sh.tr = (int)tr;
+        return sh;
+    };
     const int64_t J4 = (G + 3) / 4;
     const int n4 = J4 >= 3 ? 4 : (int)J4;
     const int64_t t4 = (rows + 15) / 16;
-    if (t4 <= resident({4, n4, 1})) return {4, n4, 1};
-    if ((G + 1) / 2 >= 4 && (rows + 31) / 32 <= resident({2, 4, 1})) return {2, 4, 1};
-    if (xmode == kXNormAdd || ymode == kYSwiGLU) return {2, 1, 1};
-    if (t4 <= resident({4, 1, 1})) return {4, 1, 1};
-    return {4, J4 >= 2 ? 2 : 1, 1};
+    if (t4 <= resident({4, n4, 1})) return balanced({4, n4, 1});
+    if ((G + 1) / 2 >= 4 && (rows + 31) / 32 <= resident({2, 4, 1})) return balanced({2, 4, 1});
+    if (xmode == kXNormAdd || ymode == kYSwiGLU) return balanced({2, 1, 1});
+    if (single && (G + 1) / 2 >= 2) {
+        const int64_t t2 = (rows + 31) / 32;
+        if (t2 > cus && t2 <= resident({2, 2, 1})) return balanced({2, 2, 1});
+    }
+    if (t4 <= resident({4, 1, 1})) return balanced({4, 1, 1});
+    return balanced({4, J4 >= 2 ? 2 : 1, 1});
 }
 
 // Launch shape of a fused launch of independent ops (a throughput launch):
@@ -237,8 +260,8 @@ int gemv_launch(const float *x, const void *w, float *y, int64_t n, int64_t p, h
     if (e != hipSuccess) return fail_hip(e, "hipGetDevice");
     OpDesc d = plan_op(x, w, y, 1, n, p, true, kWaves);
     if (d.rs == 1) {
-        if (sh.c == 0) sh = plan_rc_latency(p, d.gsr, xmode, kYPlain, cu_count(dev));
-        e = launch_gemv_rc(d, sh, rc_tiles_for(p, sh.c), s, xmode);
+        if (sh.c == 0) sh = plan_rc_latency(p, d.gsr, xmode, kYPlain, cu_count(dev), true);
+        e = launch_gemv_rc(d, sh, rc_tiles_for(p, sh), s, xmode);
     } else {
         e = launch_gemv_single(d, Variant{kWaves, 1}, tiles_of(d, kWaves), s, xmode);
     }
@@ -778,8 +801,8 @@ int plan_chain(const q8_0_op *ops, int64_t n_ops, uint32_t flags, const OpExtra 
             si.L.single = d;
             if (d.rs == 1) {
                 si.L.kind = q8_0_chain::Launch::kSingleRc;
-                si.L.shape = plan_rc_latency(d.p, d.gsr, xmode, ymode, cus);
-                si.L.grid = rc_tiles_for(d.p, si.L.shape.c);
+                si.L.shape = plan_rc_latency(d.p, d.gsr, xmode, ymode, cus, true);
+                si.L.grid = rc_tiles_for(d.p, si.L.shape);
             } else {
                 si.L.kind = q8_0_chain::Launch::kSingleSuperrow;
                 si.L.grid = tiles_of(d, kWaves);
@@ -805,7 +828,7 @@ int plan_chain(const q8_0_op *ops, int64_t n_ops, uint32_t flags, const OpExtra 
             // the steady-state one-wave tiles, largest tiles first so that
             // the smallest finish the launch
             const RcShape sh = latency && one_width
-                                   ? plan_rc_latency(rows, ops[sg.first].n / (kQuants * kGroupBlocks), xmode, ymode, cus)
+                                   ? plan_rc_latency(rows, ops[sg.first].n / (kQuants * kGroupBlocks), xmode, ymode, cus, false)
                                    : fuse_shape(wg / wsum);
             struct Item { Tile t; int64_t bytes; };
             std::vector<Item> items;
@@ -934,7 +957,9 @@ int q8_0_chain_plan(const q8_0_op *ops, int64_t n_ops, uint32_t flags, int64_t c
                 o.lanes_per_row = si.L.shape.c;
                 o.waves = si.L.shape.nwk;
                 o.stages = si.L.shape.nst;
+                o.tile_rows = rc_rows(si.L.shape);
             }
+            if (si.L.kind == q8_0_chain::Launch::kFusedMixed) o.tile_rows = kWave;
         }
     }
     if (tile_op && tile_id && max_tiles >= *n_tiles) {
@@ -951,8 +976,8 @@ int q8_0_chain_plan(const q8_0_op *ops, int64_t n_ops, uint32_t flags, int64_t c
 }
 
 int q8_0_gemv_plan(int64_t n, int64_t p, int64_t cus, int *lanes_per_row, int *waves, int *stages,
-                   int64_t *workgroups) {
-    if (!lanes_per_row || !waves || !stages || !workgroups)
+                   int *tile_rows, int64_t *workgroups) {
+    if (!lanes_per_row || !waves || !stages || !tile_rows || !workgroups)
         return fail(Q8_ERR_INVALID_ARG, "q8_0_gemv_plan: null output");
     if (n <= 0 || n % kQuants != 0 || n > Q8_MAX_N || p <= 0 || p > Q8_MAX_P)
         return fail(Q8_ERR_SHAPE, "q8_0_gemv_plan: shape out of range");
@@ -961,15 +986,17 @@ int q8_0_gemv_plan(int64_t n, int64_t p, int64_t cus, int *lanes_per_row, int *w
     static const float kDummy[4] = {0.f, 0.f, 0.f, 0.f};
     OpDesc d = plan_op(kDummy, kDummy, nullptr, 1, n, p, true, kWaves);
     if (d.rs == 1) {
-        const RcShape sh = plan_rc_latency(p, d.gsr, kXFloat, kYPlain, cus);
+        const RcShape sh = plan_rc_latency(p, d.gsr, kXFloat, kYPlain, cus, true);
         *lanes_per_row = sh.c;
         *waves = sh.nwk;
         *stages = sh.nst;
-        *workgroups = rc_tiles_for(p, sh.c);
+        *tile_rows = rc_rows(sh);
+        *workgroups = rc_tiles_for(p, sh);
     } else {
         *lanes_per_row = 0;
         *waves = kWaves;
         *stages = 0;
+        *tile_rows = 0;
         *workgroups = tiles_of(d, kWaves);
     }
     return Q8_OK;

@@ -93,9 +93,13 @@ constexpr int lds_of() { return fits<C, NWK, NST>() ? rc_lds_bytes<C, NWK, XM, N
 static int shape_key(RcShape sh) { return 100 * sh.c + 10 * sh.nwk + sh.nst; }
 
 hipError_t Q8_CAT(launch_gemv_rc_, Q8_RC_MODE)(const OpDesc &op, RcShape sh, int64_t grid, hipStream_t s) {
-    if (grid <= 0 || op.rs != 1) return hipErrorInvalidValue;
+    if (grid <= 0 || op.rs != 1 || sh.tr < 0 || sh.tr > kWave / sh.c) return hipErrorInvalidValue;
+    // the residual-add output sums squares over whole 16-row blocks of a tile
+    if (YM == kYResAdd && sh.tr % kPsumRows) return hipErrorInvalidValue;
+    OpDesc o = op;
+    o.tile_rows = sh.tr;
     switch (shape_key(sh)) {
-        Q8_RC_CASES(single_t, op, grid, s)
+        Q8_RC_CASES(single_t, o, grid, s)
         default: return hipErrorInvalidValue;
     }
 }

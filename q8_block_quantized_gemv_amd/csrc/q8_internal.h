@@ -53,7 +53,7 @@ struct OpDesc {
     int32_t fast_tiles;  // workgroup tiles of the fast path
     int32_t tail_row0;   // first tail row = nsr * rs
     int32_t m;           // activation rows (1 for a matvec)
-    int32_t pad0_;
+    int32_t tile_rows;   // rows-and-group-slots tiles: rows per tile, 1 .. 64 / C (0: 64 / C)
     const float *x_up;   // kXSiluUp: the input is silu(x) * x_up, elementwise
     // kXNormAdd: the input is rms_norm(x + x_res) * norm_w over the op's n
     // columns; the op-local tile 0's workgroup also writes x + x_res to x_out
@@ -121,7 +121,10 @@ struct RcShape {
     int c;
     int nwk;
     int nst;
+    int tr = 0;   // rows per tile, 1 .. 64 / c (0: 64 / c); one-op launches only
 };
+// rows of a tile of shape sh
+inline int rc_rows(RcShape sh) { return sh.tr > 0 ? sh.tr : kWave / sh.c; }
 
 // rs > 1: fast tiles cover (nw / ks) * 64 super-rows each.
 inline int64_t fast_tiles_for(int64_t nsr, int ks, int nw = kWaves) {
@@ -132,9 +135,13 @@ inline int64_t fast_tiles_for(int64_t nsr, int ks, int nw = kWaves) {
 inline int64_t tail_tiles_for(int64_t tail_rows, int nw = kWaves) {
     return (tail_rows + nw - 1) / nw;
 }
-// rs == 1: tiles of 64 / C rows.
+// rs == 1: tiles of 64 / C rows, or of the shape's rc_rows.
 inline int64_t rc_tiles_for(int64_t p, int c) {
     const int64_t rows = kWave / c;
+    return (p + rows - 1) / rows;
+}
+inline int64_t rc_tiles_for(int64_t p, RcShape sh) {
+    const int64_t rows = rc_rows(sh);
     return (p + rows - 1) / rows;
 }
 
@@ -150,7 +157,8 @@ hipError_t launch_gemv_fused(const OpDesc *d_ops, const Tile *d_tiles, const Var
 // rs == 1 ops (q8_gemv_rc.hip, built once per build mode M -- a pair of
 // input and output modes, kBuildModes -- with the entry points below with
 // the mode's number appended).  One op: grid =
-// rc_tiles_for(p, c) workgroups.  A table of tiles of independent rs == 1
+// rc_tiles_for(p, sh) workgroups, tiles of sh.tr rows when it is set (a
+// multiple of 16 for the residual-add output).  A table of tiles of independent rs == 1
 // ops read in one mode.  LDS bytes of a workgroup (0: no such shape, or one
 // whose LDS does not fit a workgroup).
 // build mode -> (XMode, YMode)

@@ -132,8 +132,11 @@ __device__ __forceinline__ void rc_tile(const OpDesc &op, int64_t tile, uint8_t 
     const int half = YM == kYSwiGLU ? wave / NWK : 0;
     const int wk = wave - half * NWK;    // the wave's place among the NWK sharing its rows
     const int r = lane / C, c = lane % C;
-    const int64_t row0 = tile * R;
-    const int last = (int)min((int64_t)op.p - 1 - row0, (int64_t)R - 1);   // rows past p re-read this one
+    // a tile covers TR <= R rows (lanes past them compute a copy of the
+    // last row and store nothing)
+    const int TR = op.tile_rows > 0 && op.tile_rows < R ? op.tile_rows : R;
+    const int64_t row0 = tile * TR;
+    const int last = (int)min((int64_t)op.p - 1 - row0, (int64_t)TR - 1);   // rows past p re-read this one
     const int G = op.gsr;                 // groups per row
     const int J = (G + C - 1) / C;        // group columns
     const int64_t RB = op.sr_bytes;       // bytes per row

@@ -41,14 +41,23 @@ def tiles(p, lanes):
 @pytest.mark.parametrize("n", [256, 512, 1024, 2048, 3072, 3584, 18944, 1 << 20, 96, 160, 896, 4864])
 def test_gemv_plan_is_a_legal_shape(q8, n, cus):
     for p in (1, 7, 63, 64, 300, 3584, 4608, 18944, 152064, (1 << 22) + 3):
-        c, w, st, g = q8.gemv_plan(n, p, cus)
+        c, w, st, tr, g = q8.gemv_plan(n, p, cus)
         if n % 256:
-            assert (c, st) == (0, 0) and w in (1, 4) and g >= 1
+            assert (c, st, tr) == (0, 0, 0) and w in (1, 4) and g >= 1
             continue
         assert c in (1, 2, 4) and w in (1, 2, 4) and st in (1, 2)
         assert (16 // c) % w == 0                   # every group slot has exactly one owner wave
-        assert w * (st * W_STAGE + 2 * c * X_SLICE) <= LDS_PER_CU
-        assert g == tiles(p, c)
+        lds = w * (st * W_STAGE + 2 * c * X_SLICE)
+        assert lds <= LDS_PER_CU
+        assert 1 <= tr <= 64 // c and g == -(-p // tr)
+        if tr < 64 // c:
+            # shorter tiles only to even out CUs that hold two or more whole
+            # tiles: still all resident, no more tiles a CU than whole tiles
+            # would give, and the fewest rows a tile that allows
+            whole = tiles(p, c)
+            k = -(-whole // cus)
+            assert k >= 2 and whole <= cus * (LDS_PER_CU // lds)
+            assert -(-g // cus) == k and tr == -(-p // (k * cus))
 
 
 def test_gemv_plan_row_poor_ops_use_small_tiles(q8):
@@ -57,9 +66,19 @@ def test_gemv_plan_row_poor_ops_use_small_tiles(q8):
     over as many waves as there are columns, up to 4: all rows in one round
     of workgroups."""
     for n, p in ((3584, 3584), (18944, 3584), (1024, 2048), (3072, 1024), (2048, 1024)):
-        c, w, _, g = q8.gemv_plan(n, p, 256)
-        assert c == 4 and g == -(-p // 16) and g <= 256
+        c, w, _, tr, g = q8.gemv_plan(n, p, 256)
+        assert c == 4 and tr == 16 and g == -(-p // 16) and g <= 256
         assert w == min(4, -(-groups(n) // 4)) or (w == 4 and groups(n) > 8)
+
+
+def test_gemv_plan_evens_out_resident_tiles(q8):
+    """The 7B gate (3584 -> 18944): 592 two-wave tiles of 32 rows would come
+    two or three to a CU of 256; 758 tiles of 25 rows come at most three to
+    a CU, all resident (three 42 KiB workgroups a CU)."""
+    assert q8.gemv_plan(3584, 18944, 256) == (2, 2, 1, 25, 758)
+    # an lm_head (many rounds of tiles) keeps whole tiles
+    c, _, _, tr, _ = q8.gemv_plan(3584, 152064, 256)
+    assert tr == 64 // c
 
 
 @pytest.mark.parametrize("args,code", [((0, 64, 256), -2), ((48, 64, 256), -2), ((256, 0, 256), -2),
@@ -125,10 +144,11 @@ def check_plan(q8, ops, flags, cus=256):
             assert any(depends(a, nxt) for a in members)
         if L["n_ops"] == 1:
             n, p = members[0][3], members[0][4]
-            c, w, st, g = q8.gemv_plan(n, p, cus)
+            c, w, st, tr, g = q8.gemv_plan(n, p, cus)
             if n % 256 == 0:
                 assert L["kind"] == q8.LAUNCH_ROWS
-                assert (L["lanes_per_row"], L["waves"], L["stages"], L["workgroups"]) == (c, w, st, g)
+                assert (L["lanes_per_row"], L["waves"], L["stages"], L["tile_rows"], L["workgroups"]) == \
+                    (c, w, st, tr, g)
             else:
                 assert L["kind"] == q8.LAUNCH_SUPERROWS and L["workgroups"] == g
             assert L["first_tile"] == -1
@@ -144,14 +164,17 @@ def check_plan(q8, ops, flags, cus=256):
         assert sorted(by_op) == list(range(L["first_op"], L["first_op"] + L["n_ops"]))
         whole = all(m[3] % 256 == 0 for m in members)
         if whole:
-            assert L["kind"] == q8.LAUNCH_FUSED
+            assert L["kind"] == q8.LAUNCH_FUSED and L["tile_rows"] == 64 // L["lanes_per_row"]
             for o, ts in by_op.items():
                 assert sorted(ts) == list(range(tiles(ops[o][4], L["lanes_per_row"])))
             same_width = len({m[3] for m in members}) == 1
             if flags & q8.Q8_CHAIN_SPLIT_K and same_width:
-                # the latency plan of all the launch's rows, tiles in op order
-                c, w, st, _ = q8.gemv_plan(members[0][3], sum(m[4] for m in members), cus)
-                assert (L["lanes_per_row"], L["waves"], L["stages"]) == (c, w, st)
+                # the latency plan of all the launch's rows (whole tiles:
+                # where one op's plan would even out shorter tiles, the
+                # launch keeps the whole-tile rules), tiles in op order
+                c, w, st, tr, _ = q8.gemv_plan(members[0][3], sum(m[4] for m in members), cus)
+                if tr == 64 // c:
+                    assert (L["lanes_per_row"], L["waves"], L["stages"]) == (c, w, st)
                 assert items == sorted(items)
             else:
                 # steady-state tiles: two lanes per row when rows are long,
