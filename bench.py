@@ -157,13 +157,19 @@ def bench_smallm(args, q8, synth, torch, np):
     VALU_LANE_OPS = 256 * 4 * 16 * 2.4e9    # CUs x SIMDs x lanes x clock (no packed FP32)
     stream = torch.cuda.current_stream()
     cases = []
+    only = {tuple(c.split(":")) for c in args.smallm_cases.split(",") if c}
+    want = lambda shape, m: not only or (shape.name, str(m)) in only
     for shape in synth.SMALLM_SHAPES:
+        if not any(want(shape, m) for m in synth.SMALLM_M):
+            continue
         w, _ = synth.generate_smallm(shape, 2)
         wbytes = w.size
         copies = max(1, -(-(1 << 30) // wbytes))
         say("smallm %s: %d copies of %.1f MB" % (shape.name, copies, wbytes / 1e6))
         wd = [torch.from_numpy(w.reshape(shape.p, -1)).to("cuda") for _ in range(copies)]
         for m in synth.SMALLM_M:
+            if not want(shape, m):
+                continue
             _, X = synth.generate_smallm(shape, m)
             Xd = torch.from_numpy(X).to("cuda")
             Y = torch.empty((m, shape.p), dtype=torch.float32, device="cuda")
@@ -322,6 +328,8 @@ def main():
     ap.add_argument("--smallm", action="store_true",
                     help="instead of the chain: time q8_0_gemm_smallm at the 7B shapes, "
                          "m in {2,4,8,16}, rotating weight copies past the 256 MB cache")
+    ap.add_argument("--smallm-cases", default="", metavar="SHAPE:M,...",
+                    help="with --smallm: only these cases (e.g. down:2,lm_head:16), in the bench's order")
     ap.add_argument("--xq", action="store_true",
                     help="the chain's ops quantize x to Q8_0 and multiply integers "
                          "(q8_0_gemv_q8q8 semantics) instead of multiplying float x")
