@@ -261,6 +261,7 @@ int gemv_launch(const float *x, const void *w, float *y, int64_t n, int64_t p, h
     OpDesc d = plan_op(x, w, y, 1, n, p, true, kWaves);
     if (d.rs == 1) {
         if (sh.c == 0) sh = plan_rc_latency(p, d.gsr, xmode, kYPlain, cu_count(dev), true);
+        d.w_once = 1;
         e = launch_gemv_rc(d, sh, rc_tiles_for(p, sh), s, xmode);
     } else {
         e = launch_gemv_single(d, Variant{kWaves, 1}, tiles_of(d, kWaves), s, xmode);
@@ -801,6 +802,7 @@ int plan_chain(const q8_0_op *ops, int64_t n_ops, uint32_t flags, const OpExtra 
             si.L.single = d;
             if (d.rs == 1) {
                 si.L.kind = q8_0_chain::Launch::kSingleRc;
+                si.L.single.w_once = 1;
                 si.L.shape = plan_rc_latency(d.p, d.gsr, xmode, ymode, cus, true);
                 si.L.grid = rc_tiles_for(d.p, si.L.shape);
             } else {
@@ -836,6 +838,7 @@ int plan_chain(const q8_0_op *ops, int64_t n_ops, uint32_t flags, const OpExtra 
                 const q8_0_op &o = ops[i];
                 OpDesc d = plan_op(o.x, o.w, o.y, 1, o.n, o.p, false, 1);
                 set_extra(d, ex(i));
+                d.w_once = latency && one_width ? 1 : 0;   // the latency plan's launch
                 const uint32_t oi = (uint32_t)(h_ops.size() - si.op0);
                 h_ops.push_back(d);
                 const int64_t tb = (int64_t)(kWave / sh.c) * d.sr_bytes;

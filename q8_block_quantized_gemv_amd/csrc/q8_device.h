@@ -71,6 +71,11 @@ __device__ __forceinline__ void dma16_s(const uint8_t *sbase, uint32_t voff, uin
     asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2"
                  :: "s"(lds), "v"(voff), "s"(uniform_ptr(sbase)) : "memory", "m0");
 }
+// the same with the non-temporal hint (streaming data read once)
+__device__ __forceinline__ void dma16_s_nt(const uint8_t *sbase, uint32_t voff, uint32_t lds) {
+    asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2 nt"
+                 :: "s"(lds), "v"(voff), "s"(uniform_ptr(sbase)) : "memory", "m0");
+}
 // 16 bytes per lane: global (per-lane address) -> LDS (m0 + 16 * lane)
 __device__ __forceinline__ void dma16_v(const void *addr, uint32_t lds) {
     asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off"

@@ -69,6 +69,11 @@ struct OpDesc {
     // 16-row block, and (x_out not null) x_out = y * norm_w, p floats.
     // kYSwiGLU: rows of w2 too; y = silu(W x) * (W2 x).
     int32_t psum_n;
+    // rows-and-group-slots tiles: W's lines are loaded with the non-temporal
+    // hint (a launch that waits on the one before and is waited on by the
+    // next: its weights, read once, then do not push out of L2 the
+    // activations, norm sums and KV cache the next launches read)
+    int32_t w_once;
     float *psum;
     const uint8_t *w2;
 };

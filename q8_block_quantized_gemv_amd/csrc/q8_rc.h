@@ -13,6 +13,7 @@
 //    columns" j = 0, 1, ...: column j is groups C*j .. C*j + C-1 of each of
 //    the R rows, and lane (r, c) computes group C*j + c of row r.
 //  * Each column moves HBM -> LDS as 17 direct 16-byte loads per lane
+//    (non-temporal in latency launches, op.w_once)
 //    (global_load_lds_dwordx4): load i of lane l carries chunk (64i + l) of
 //    the column's R runs of C*272 contiguous bytes, so every load
 //    instruction reads whole contiguous KiB, and lane l finds its own group
@@ -164,13 +165,22 @@ __device__ __forceinline__ void rc_tile(const OpDesc &op, int64_t tile, uint8_t 
     // this wave's group columns j = wk + NWK * t, t < nt
     const int nt = J > wk ? (J - wk + NWK - 1) / NWK : 0;
     float4 na[C], nr[C], nw[C];   // kXNormAdd: x, x_res and gain of the column, prefetched
+    const bool w_once = op.w_once != 0;
     auto issue = [&](int t) {
         const int j = wk + NWK * t;
         const uint32_t l0 = __builtin_amdgcn_readfirstlane(lds_addr(wst + (t % NST) * kStageW));
+        if (w_once) {
 #pragma unroll
-        for (int i = 0; i < kGroupChunks; ++i) {
-            const uint32_t kk = min((uint32_t)(C * j) + cs[i], (uint32_t)(G - 1));
-            dma16_s(wbase, base[i] + kk * kGroupBytes, l0 + kWave * 16 * i);
+            for (int i = 0; i < kGroupChunks; ++i) {
+                const uint32_t kk = min((uint32_t)(C * j) + cs[i], (uint32_t)(G - 1));
+                dma16_s_nt(wbase, base[i] + kk * kGroupBytes, l0 + kWave * 16 * i);
+            }
+        } else {
+#pragma unroll
+            for (int i = 0; i < kGroupChunks; ++i) {
+                const uint32_t kk = min((uint32_t)(C * j) + cs[i], (uint32_t)(G - 1));
+                dma16_s(wbase, base[i] + kk * kGroupBytes, l0 + kWave * 16 * i);
+            }
         }
         uint8_t *xs = xst + (t & 1) * L::kX;
 #pragma unroll
