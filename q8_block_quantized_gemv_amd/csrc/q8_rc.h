@@ -137,6 +137,7 @@ __device__ __forceinline__ void rc_tile(const OpDesc &op, int64_t tile, uint8_t 
     // last row and store nothing)
     const int TR = op.tile_rows > 0 && op.tile_rows < R ? op.tile_rows : R;
     const int64_t row0 = tile * TR;
+    if (row0 >= op.p) return;   // a grid past the op's tiles (every wave of the workgroup leaves)
     const int last = (int)min((int64_t)op.p - 1 - row0, (int64_t)TR - 1);   // rows past p re-read this one
     const int G = op.gsr;                 // groups per row
     const int J = (G + C - 1) / C;        // group columns

@@ -426,8 +426,10 @@ def test_split_k_chain(q8, per_op):
 
 # n multiple of 256: 4, 12, 14, 74 and 37 groups per row (columns that do and
 # do not fill 2 and 4 lanes), ragged row counts and rows that leave a last
-# tile of one row
-SHAPED = [(1024, 3072), (3072, 1024), (3584, 515), (18944, 70), (9472, 17), (256, 1), (1024, 65)]
+# tile of one row; (1024, 5000) and (3584, 9000) are planned with tiles
+# shorter than a wave's rows (10 of 16, 18 of 32) to even out the CUs
+SHAPED = [(1024, 3072), (3072, 1024), (3584, 515), (18944, 70), (9472, 17), (256, 1), (1024, 65),
+          (1024, 5000), (3584, 9000)]
 
 
 @pytest.mark.parametrize("n,p", SHAPED, ids=lambda v: str(v))
@@ -437,7 +439,7 @@ def test_every_launch_shape_same_bits(q8, n, p):
     gives q8_0_gemv's bits exactly, and those are within the bar against the
     oracle."""
     import torch
-    log("launch shapes n=%d p=%d" % (n, p))
+    log("launch shapes n=%d p=%d plan=%s" % (n, p, q8.gemv_plan(n, p)))
     rng = np.random.default_rng(31 * n + p)
     w = synth.q8_weights(n, p, rng)
     x = synth.activations(n, rng)
