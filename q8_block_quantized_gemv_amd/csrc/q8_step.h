@@ -9,6 +9,8 @@ namespace q8 {
 // Cached rows per attention workgroup; a head's rows [0, seq) are split into
 // ceil(seq / kAttnChunk) chunks whose partial softmaxes are merged in order.
 constexpr int kAttnChunk = 128;
+// contexts of at most kAttnShort rows are one chunk of a body sized for them
+constexpr int kAttnShort = 32;
 
 struct AttnDesc {
     const float *q;      // n_heads x head_dim

@@ -346,7 +346,7 @@ __global__ __launch_bounds__(256) void k_append_kv(const float *k, const float *
 
 // ---------------------------------------------------------------- attention_decode
 // Workgroup (chunk c, head h) of 256 threads: the scores of cached rows
-// [c*kAttnChunk, min(seq, (c+1)*kAttnChunk)) on KV head h / kv_group, their
+// [c*CHUNK, min(seq, (c+1)*CHUNK)) on KV head h / kv_group, their
 // local softmax (max m, sum s of e^(score - m)) and acc[j] = sum e * v[j].
 // A head of one chunk writes acc / s; otherwise the last chunk of a head to
 // arrive merges the parts in chunk order.
@@ -366,19 +366,19 @@ constexpr int kAttnThreads = 256;
 constexpr int kAttnWaves = kAttnThreads / kWave;
 constexpr int kMergeBatch = 8;
 
-template <int HD, bool FUSED>
-__global__ __launch_bounds__(kAttnThreads) void k_attention(AttnDesc d, AttnFuse f) {
+template <int HD, bool FUSED, int CHUNK>
+__device__ __forceinline__ void attention_part(const AttnDesc &d, const AttnFuse &f, const int seq) {
     constexpr int NV = HD / 4;                                   // float4 per row
     constexpr int HALF = HD / 2;
     constexpr int L = NV <= 16 ? 16 : NV <= 32 ? 32 : 64;        // lanes per row
     constexpr int RPW = kWave / L;                               // rows per wave per pass
     constexpr int RPP = kAttnWaves * RPW;                        // rows per pass
-    constexpr int PASSES = kAttnChunk / RPP;
+    constexpr int PASSES = CHUNK / RPP;
     constexpr int SB = PASSES < 16 ? PASSES : 16;                // score loads in flight
     constexpr int RG = kAttnThreads / NV;                        // value row groups
-    constexpr int RPT = (kAttnChunk + RG - 1) / RG;              // rows per thread
+    constexpr int RPT = (CHUNK + RG - 1) / RG;                   // rows per thread
     constexpr int VB = RPT < 16 ? RPT : 16;                      // value loads in flight
-    __shared__ float sc[kAttnChunk];
+    __shared__ float sc[CHUNK];
     __shared__ float pt[kAttnWaves * SB * 65];   // each wave's partial-dot tile
     __shared__ float red[2 * kAttnWaves];
     __shared__ float4 accp[kAttnThreads];
@@ -387,11 +387,10 @@ __global__ __launch_bounds__(kAttnThreads) void k_attention(AttnDesc d, AttnFuse
     __shared__ __attribute__((aligned(16))) float kn[FUSED ? kAttnWaves * HD : 4];
     const int head = blockIdx.x % d.n_heads;
     const int c = blockIdx.x / d.n_heads;
-    const int seq = d.pos_dev ? min(*d.pos_dev + 1, d.seq) : d.seq;
-    const int n_chunks = (seq + kAttnChunk - 1) / kAttnChunk;
+    const int n_chunks = (seq + CHUNK - 1) / CHUNK;
     if (c >= n_chunks) return;   // the whole workgroup: no part, no arrival
     const int tid = threadIdx.x, lane = tid & (kWave - 1), wv = tid / kWave;
-    const int t0 = c * kAttnChunk, rows = min(kAttnChunk, seq - t0);
+    const int t0 = c * CHUNK, rows = min(CHUNK, seq - t0);
     const int kvh = head / d.kv_group;
     const int64_t kv_off = (int64_t)kvh * HD;
     const int pos = seq - 1;
@@ -570,7 +569,7 @@ __global__ __launch_bounds__(kAttnThreads) void k_attention(AttnDesc d, AttnFuse
 #pragma unroll
                 for (int b = 0; b < VB; ++b) {
                     const int r = rg + (r0 + b) * RG;
-                    const float e = sc[min(r, kAttnChunk - 1)];
+                    const float e = sc[min(r, CHUNK - 1)];
                     ee[b] = r < rows ? e : 0.f;
                 }
 #pragma unroll
@@ -665,6 +664,18 @@ __global__ __launch_bounds__(kAttnThreads) void k_attention(AttnDesc d, AttnFuse
     }
     if (tid == 0)   // ready for the next launch
         __hip_atomic_store(d.cnt + head, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Contexts of at most kAttnShort rows take one chunk of that many rows: the
+// same arithmetic in a body whose loads and loops are sized for it (a chunk
+// of kAttnChunk rows issues and masks that many rows' loads however few
+// rows there are).  Measured per token at position 0 against one body of
+// 128-row chunks: 7B 2171 -> 2125 us, Qwen3-0.6B 809 -> 774 us.
+template <int HD, bool FUSED>
+__global__ __launch_bounds__(kAttnThreads) void k_attention(AttnDesc d, AttnFuse f) {
+    const int seq = d.pos_dev ? min(*d.pos_dev + 1, d.seq) : d.seq;
+    if (seq <= kAttnShort) attention_part<HD, FUSED, kAttnShort>(d, f, seq);
+    else attention_part<HD, FUSED, kAttnChunk>(d, f, seq);
 }
 
 // ---------------------------------------------------------------- add_inplace, silu_hadamard
