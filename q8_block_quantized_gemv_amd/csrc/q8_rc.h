@@ -204,6 +204,14 @@ __device__ __forceinline__ void rc_tile(const OpDesc &op, int64_t tile, uint8_t 
     // streams in (kXNormScale: by the waves that write the rows)
     float ninv = 0.f;
     if (nt > 0) issue(0);
+    // kYResAdd: the row's residual and gain, read while the first column
+    // streams in (not after the sums, a round trip later)
+    float xres = 0.f, ngain = 0.f;
+    if constexpr (YM == kYResAdd)
+        if (wk == 0 && c == 0 && r <= last) {
+            xres = op.x_res[row0 + r];
+            if (op.x_out) ngain = op.norm_w[row0 + r];
+        }
     if constexpr (XM == kXNormAdd) ninv = rc_norm_inv<NWK>(op, lane, wave, op.x_out && writer);
     if constexpr (XM == kXNormScale)
         if (wk == 0) ninv = psum_inv(op, lane);
@@ -304,9 +312,9 @@ __device__ __forceinline__ void rc_tile(const OpDesc &op, int64_t tile, uint8_t 
         // first row stores the sum
         float out = 0.f;
         if (c == 0 && r <= last) {
-            out = op.x_res[row0 + r] + row;
+            out = xres + row;
             op.y[row0 + r] = out;
-            if (op.x_out) op.x_out[row0 + r] = out * op.norm_w[row0 + r];
+            if (op.x_out) op.x_out[row0 + r] = out * ngain;
         }
         float sq = out * out;
 #pragma unroll
