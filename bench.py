@@ -412,7 +412,8 @@ def main():
     torch.cuda.synchronize()
     say("warm; timing %d steps" % args.steps)
 
-    # the timed region: K graph replays between a synchronize on each side
+    # the timed region: K graph-mode tokens (one launch, or one graph replay)
+    # between a synchronize on each side
     torch.cuda.synchronize()
     t_wall0 = time.perf_counter()
     sec = time_steps(run_graph, args.steps)
@@ -516,7 +517,9 @@ def main():
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": "i8xi8->f32" if args.xq else "f32", "data": "synthetic",
         "config": {"workload": args.workload, "ops_per_token": len(ops_shape),
-                   "bytes_per_token": nbytes, "mode": "hipGraph replay, fused launch",
+                   "bytes_per_token": nbytes,
+                   "mode": "q8_0_decode_chain in graph mode, %d launch(es) per token (%s)" % (
+                       chain.launches, "issued directly" if chain.launches == 1 else "one hipGraph replay"),
                    "activations_as": "Q8_0, integer dots" if args.xq else "float32",
                    "weights": "Q8_0, scale U[0.001,0.02] as f16, quants U{-127..127}",
                    "activations": "f32 N(0,1), independent per op",

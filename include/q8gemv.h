@@ -185,7 +185,8 @@ typedef struct q8_0_chain q8_0_chain; /* opaque */
 #define Q8_CHAIN_XQ 4u      /* every op as q8_0_gemv_q8q8: x quantized to Q8_0, integer dots */
 
 /* decode_chain modes */
-#define Q8_MODE_GRAPH 0     /* replay the recorded hipGraph: one host call per token */
+#define Q8_MODE_GRAPH 0     /* replay the recorded hipGraph: one host call per token (a chain
+                               of one launch issues that launch directly) */
 #define Q8_MODE_EAGER 1     /* re-issue the chain's launches on the stream */
 #define Q8_MODE_SYNC_EACH 2 /* one launch, then wait for it, per launch */
 
