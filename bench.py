@@ -157,6 +157,8 @@ def bench_smallm(args, q8, synth, torch, np):
     VALU_LANE_OPS = 256 * 4 * 16 * 2.4e9    # CUs x SIMDs x lanes x clock (no packed FP32)
     stream = torch.cuda.current_stream()
     cases = []
+    kernel_arg = getattr(q8, "SMALLM_" + args.smallm_kernel) if args.smallm_kernel else None
+    kernel_id = q8.SMALLM_AUTO if kernel_arg is None else kernel_arg
     only = {tuple(c.split(":")) for c in args.smallm_cases.split(",") if c}
     want = lambda shape, m: not only or (shape.name, str(m)) in only
     for shape in synth.SMALLM_SHAPES:
@@ -174,29 +176,33 @@ def bench_smallm(args, q8, synth, torch, np):
             Xd = torch.from_numpy(X).to("cuda")
             Y = torch.empty((m, shape.p), dtype=torch.float32, device="cuda")
             # the caller-owned workspace, allocated once per case
-            ws = torch.empty(max(1, q8.gemm_smallm_workspace(m, shape.n, shape.p)), dtype=torch.uint8,
+            ws = torch.empty(max(1, q8.gemm_smallm_workspace(m, shape.n, shape.p, kernel_id)), dtype=torch.uint8,
                              device="cuda")
             if not cases:   # the first case: settle the GPU before anything is timed
                 ring = iter(range(1 << 62))
-                settle(lambda: q8.gemm_smallm(Xd, wd[next(ring) % copies], Y, stream, workspace=ws),
+                settle(lambda: q8.gemm_smallm(Xd, wd[next(ring) % copies], Y, stream, workspace=ws, kernel=kernel_arg),
                        torch.cuda.synchronize)
             for i in range(copies):
-                q8.gemm_smallm(Xd, wd[i], Y, stream, workspace=ws)
+                q8.gemm_smallm(Xd, wd[i], Y, stream, workspace=ws, kernel=kernel_arg)
             k = max(copies * 4, 20)
             torch.cuda.synchronize()
             e0 = torch.cuda.Event(enable_timing=True)
             e1 = torch.cuda.Event(enable_timing=True)
             e0.record(stream)
             for i in range(k):
-                q8.gemm_smallm(Xd, wd[i % copies], Y, stream, workspace=ws)
+                q8.gemm_smallm(Xd, wd[i % copies], Y, stream, workspace=ws, kernel=kernel_arg)
             e1.record(stream)
             torch.cuda.synchronize()
             t = e0.elapsed_time(e1) / 1e3 / k
             nbytes = synth.workload_bytes([shape], m)
             t_hbm = nbytes / 8e12
-            if m <= 3 and shape.n % 256 == 0:
+            chosen = q8.gemm_smallm_choice(m, shape.n, shape.p) if kernel_arg is None else kernel_arg
+            if chosen == q8.SMALLM_VROW:
                 kernel, unit = "k_q8_gemm_vrow<%d,2>" % m, "alu"
                 t_cmp = (1 + m) * shape.n * shape.p / VALU_LANE_OPS
+            elif chosen == q8.SMALLM_KS:
+                kernel, unit = "k_split_x + k_q8_gemm_ks<8> (+ k_ks_reduce)", "mfma"
+                t_cmp = 2 * 3 * 16 * shape.n * shape.p / MFMA_BF16_FLOPS
             else:
                 kernel, unit = "k_split_x + k_q8_gemm_mfma<1>", "mfma"
                 t_cmp = 2 * 3 * 16 * shape.n * shape.p / MFMA_BF16_FLOPS
@@ -212,8 +218,8 @@ def bench_smallm(args, q8, synth, torch, np):
         torch.cuda.empty_cache()
     return {"metric": "q8_0_gemm_smallm at 7B shapes", "unit": "us", "n_gpus": 1,
             "dtype": "f32", "data": "synthetic",
-            "roof_note": "HBM 8 TB/s; m <= 3: FP32 vector lanes 39.3e12 instr/s (1 + m per weight); "
-                         "m >= 4: bf16 MFMA 2.5 PFLOP/s dense (3 exact x parts, 16 padded rows)",
+            "roof_note": "HBM 8 TB/s; vector units: FP32 lanes 39.3e12 instr/s (1 + m per weight); "
+                         "matrix cores: bf16 MFMA 2.5 PFLOP/s dense (3 exact x parts, 16 padded rows)",
             "cases": cases}
 
 
@@ -328,6 +334,8 @@ def main():
     ap.add_argument("--smallm", action="store_true",
                     help="instead of the chain: time q8_0_gemm_smallm at the 7B shapes, "
                          "m in {2,4,8,16}, rotating weight copies past the 256 MB cache")
+    ap.add_argument("--smallm-kernel", default="", metavar="NAME",
+                    help="with --smallm: run this kernel (VALU, MFMA, VROW, VROW1, KS) instead of the library's choice")
     ap.add_argument("--smallm-cases", default="", metavar="SHAPE:M,...",
                     help="with --smallm: only these cases (e.g. down:2,lm_head:16), in the bench's order")
     ap.add_argument("--xq", action="store_true",

@@ -150,6 +150,17 @@ Q8_API int q8_0_gemm_smallm_noalloc(const float *X, const void *w, float *Y, int
 #define Q8_SMALLM_VROW 3  /* vector units, lanes over a row and a block pair, two waves per
                              workgroup; n % 256 == 0 and m <= 3 */
 #define Q8_SMALLM_VROW1 4 /* the same with one wave per workgroup */
+#define Q8_SMALLM_KS 5    /* bf16 matrix cores on X split exactly in three parts, each column
+                             range's parts held in LDS by the workgroups that stream its rows;
+                             n % 256 == 0 */
+
+/*
+ * *kernel = the kernel (Q8_SMALLM_*, never AUTO) q8_0_gemm_smallm runs for
+ * (m, n, p), m = 2..16, on the current device.  Enqueues nothing.
+ * Q8_ERR_SHAPE for a shape out of range, Q8_ERR_INVALID_ARG for a null
+ * kernel, Q8_ERR_NO_DEVICE without a device.
+ */
+Q8_API int q8_0_gemm_smallm_choice(int64_t m, int64_t n, int64_t p, int *kernel);
 
 /*
  * q8_0_gemm_smallm on a named kernel (for measurements and for tests of each

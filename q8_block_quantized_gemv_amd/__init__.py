@@ -54,13 +54,14 @@ SMALLM_VALU = 1
 SMALLM_MFMA = 2
 SMALLM_VROW = 3
 SMALLM_VROW1 = 4
+SMALLM_KS = 5
 
 BLOCK_QUANTS = 32
 BLOCK_BYTES = 34
 
 EXPORTS = ("q8_0_gemv", "q8_0_gemv_shaped", "q8_0_gemm_smallm", "q8_0_gemm_smallm_kernel",
            "q8_0_gemm_smallm_workspace", "q8_0_attention_workspace", "q8_0_argmax_workspace",
-           "q8_0_gemm_smallm_noalloc", "q8_0_gemv_plan", "q8_0_chain_plan",
+           "q8_0_gemm_smallm_noalloc", "q8_0_gemm_smallm_choice", "q8_0_gemv_plan", "q8_0_chain_plan",
            "q8_0_chain_create", "q8_0_decode_chain",
            "q8_0_chain_launches", "q8_0_chain_destroy", "q8_0_stream_wait",
            "q8_0_status_string", "q8_0_last_error", "q8_0_gemv_q8q8", "q8_0_quantize",
@@ -139,6 +140,7 @@ def _load():
     lib.q8_0_gemm_smallm_kernel.argtypes = [vp, vp, vp, i64, i64, i64, ctypes.c_int, vp, sz, vp]
     lib.q8_0_gemm_smallm_workspace.argtypes = [i64, i64, i64, ctypes.c_int, ctypes.POINTER(sz)]
     lib.q8_0_gemm_smallm_noalloc.argtypes = [vp, vp, vp, i64, i64, i64, vp]
+    lib.q8_0_gemm_smallm_choice.argtypes = [i64, i64, i64, ctypes.POINTER(ctypes.c_int)]
     ip = ctypes.POINTER(ctypes.c_int)
     lib.q8_0_gemv_plan.argtypes = [i64, i64, i64, ip, ip, ip, ip, ctypes.POINTER(i64)]
     lib.q8_0_chain_plan.argtypes = [ctypes.POINTER(Q8Op), i64, ctypes.c_uint32, i64,
@@ -216,6 +218,13 @@ def _size_query(fn, *args) -> int:
 def gemm_smallm_workspace(m: int, n: int, p: int, kernel: int = SMALLM_AUTO) -> int:
     """Workspace bytes q8_0_gemm_smallm needs on the current device."""
     return _size_query(lib.q8_0_gemm_smallm_workspace, int(m), int(n), int(p), int(kernel))
+
+
+def gemm_smallm_choice(m: int, n: int, p: int) -> int:
+    """The kernel (SMALLM_*) q8_0_gemm_smallm runs for (m, n, p), m = 2..16."""
+    out = ctypes.c_int(0)
+    check(lib.q8_0_gemm_smallm_choice(int(m), int(n), int(p), ctypes.byref(out)))
+    return int(out.value)
 
 
 def attention_workspace(seq: int, head_dim: int, n_heads: int) -> int:

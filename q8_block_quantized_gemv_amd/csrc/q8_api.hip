@@ -304,6 +304,23 @@ size_t plan_streamk(GemmDesc &d, int64_t cus, int wpc, int min_items) {
     return (size_t)(2 * wgs) * d.m * kWave * d.rs * sizeof(float);
 }
 
+// The column ranges and row blocks of the matrix cores with X held in LDS
+// (k_q8_gemm_ks, eight waves, one workgroup per CU): as many groups per
+// range as the LDS left by the waves' stages holds parts of X for (1.5 KiB
+// per row of X and group), ranges evened out; then the shortest row blocks
+// (a multiple of 32 rows) whose workgroups all fit on the CUs at once
+// (measured: one round of workgroups, 25.2 us for gate at m = 16, against
+// 31-35 us for blocks that leave a second, partial round).
+void plan_ks(GemmDesc &d, int64_t cus) {
+    const int64_t gk_max = std::max<int64_t>(1, ks_a_bytes(8) / ((int64_t)kGroupBlocks * d.m * 192));
+    const int64_t nkr = (d.gsr + gk_max - 1) / gk_max;
+    d.ks_ranges = (int32_t)nkr;
+    d.ks_groups = (int32_t)((d.gsr + nkr - 1) / nkr);
+    const int64_t blocks = std::max<int64_t>(1, cus / nkr);
+    int64_t rows = (d.p + blocks - 1) / blocks;
+    d.ks_rows = (int32_t)std::max<int64_t>(32, (rows + 31) / 32 * 32);
+}
+
 // A small-batch product's workspace, every piece 256-byte aligned: the
 // per-row-tile arrival counters (8 bytes each, tagged with the call's epoch,
 // so they need no clearing), then (matrix cores) X split into bf16 parts,
@@ -319,6 +336,16 @@ SmallmWs smallm_plan(GemmDesc &d, int kernel, int64_t cus) {
     SmallmWs L;
     if (d.m == 1) return L;
     size_t part = 0, xs = 0;
+    if (kernel == Q8_SMALLM_KS) {
+        plan_ks(d, cus);
+        xs = (size_t)d.nb * d.m * 192;
+        part = d.ks_ranges > 1 ? (size_t)d.ks_ranges * d.m * d.p * sizeof(float) : 0;
+        L.cnt = 0;
+        L.xs = 0;
+        L.part = align256(xs);
+        L.bytes = L.part + align256(part);
+        return L;
+    }
     if (kernel == Q8_SMALLM_MFMA) {
         part = plan_streamk(d, cus, 4, 4);   // four double-buffered one-wave workgroups fill a CU's LDS
         xs = (size_t)d.nb * kXPartsBytesPerBlock;
@@ -333,30 +360,49 @@ SmallmWs smallm_plan(GemmDesc &d, int kernel, int64_t cus) {
     return L;
 }
 
-// The kernel a small-batch call runs (AUTO resolved), or an error status
-// (negative).
+// A small-batch call's kernel argument checked against (m, n): the kernel
+// (Q8_SMALLM_AUTO stays so; smallm_resolve picks once the device is known),
+// or an error status (negative).
 int smallm_kernel(int kernel, int64_t m, int64_t n, const char *what) {
-    if (kernel < Q8_SMALLM_AUTO || kernel > Q8_SMALLM_VROW1)
+    if (kernel < Q8_SMALLM_AUTO || kernel > Q8_SMALLM_KS)
         return fail(Q8_ERR_INVALID_ARG, std::string(what) + ": unknown kernel");
     const int64_t rs = kGroupBlocks / gcd64(n / kQuants, kGroupBlocks);
     const bool mfma_ok = rs <= 2, vrow_ok = rs == 1 && m >= 2 && m <= kVrowMaxM;
-    if ((kernel == Q8_SMALLM_MFMA && !(mfma_ok && m >= 2)) ||
+    if ((kernel == Q8_SMALLM_MFMA && !(mfma_ok && m >= 2)) || (kernel == Q8_SMALLM_KS && !(rs == 1 && m >= 2)) ||
         ((kernel == Q8_SMALLM_VROW || kernel == Q8_SMALLM_VROW1) && !vrow_ok) ||
         (kernel == Q8_SMALLM_VALU && m < 2))
         return fail(Q8_ERR_SHAPE, std::string(what) + ": this kernel does not take m=" + std::to_string(m) +
                                        ", n=" + std::to_string(n));
-    // m = 2..3 with rows of one super-row (n a multiple of 256) run on the
-    // vector units with lanes over (row, block pair): each lane holds the x
-    // values of its two blocks in registers, the quants are converted once
-    // for all rows of X, and no split of X is needed (measured 16-24 % faster
-    // than the matrix cores at m = 2 on the 7B shapes, 9-17 % at m = 3,
-    // slower from m = 4).  Where rows fill super-rows of 1 or 2 (n a multiple
-    // of 128) the matrix cores take the other m >= 2: on the vector units
-    // with a lane per row, the x values every lane needs come through LDS
-    // broadcast reads, m of them per quant and lane.  Other widths run on the
-    // vector units with a lane per row, kValuMaxM rows of X per pass over W.
-    if (kernel == Q8_SMALLM_AUTO) kernel = vrow_ok ? Q8_SMALLM_VROW : mfma_ok ? Q8_SMALLM_MFMA : Q8_SMALLM_VALU;
     return kernel;
+}
+
+// The kernel Q8_SMALLM_AUTO runs for a validated (m, n, p) on a device of
+// `cus` CUs; a named kernel is returned as it is.
+int smallm_resolve(int kernel, int64_t m, int64_t n, int64_t p, int64_t cus) {
+    if (kernel != Q8_SMALLM_AUTO) return kernel;
+    const int64_t rs = kGroupBlocks / gcd64(n / kQuants, kGroupBlocks);
+    const bool mfma_ok = rs <= 2, vrow_ok = rs == 1 && m >= 2 && m <= kVrowMaxM;
+    // Rows of whole groups (n a multiple of 256) run on the matrix cores with
+    // each column range's parts of X held in LDS (one copy of X per
+    // workgroup, not per wave): at the 7B shapes 26-32 us for down and gate
+    // at m = 4..16 against 30-44 us for the stream-K matrix-core kernel, and
+    // 109-161 us for the lm_head at m = 2..16 against 115-172 us -- except
+    // m = 2..3 at fewer than 65536 rows, where the vector units with lanes
+    // over (row, block pair) keep each lane's x values in registers and need
+    // no split of X (down 26.6 us, gate 22.6 us at m = 2, against 39.1 and
+    // 25.3), and shapes whose per-range sums would pass 16 MiB (the 7B
+    // lm_head at m = 16), which stay on the stream-K kernel.  Where rows fill
+    // super-rows of 1 or 2 (n a multiple of 128) the stream-K matrix cores
+    // take m >= 2.  Other widths run on the vector units with a lane per
+    // row, kValuMaxM rows of X per pass over W.
+    if (rs == 1 && m >= 2 && !(m <= kVrowMaxM && p < 65536)) {
+        static const float kShapeOnly[4] = {0.f, 0.f, 0.f, 0.f};   // the plan reads only shapes
+        GemmDesc d = plan_gemm(kShapeOnly, kShapeOnly, nullptr, m, n, p);
+        plan_ks(d, cus);
+        const int64_t part = d.ks_ranges > 1 ? (int64_t)d.ks_ranges * m * p * (int64_t)sizeof(float) : 0;
+        if (part <= ((int64_t)16 << 20)) return Q8_SMALLM_KS;
+    }
+    return vrow_ok ? Q8_SMALLM_VROW : mfma_ok ? Q8_SMALLM_MFMA : Q8_SMALLM_VALU;
 }
 
 // Workspace bytes of a call (the largest of its launches; they run in order
@@ -387,7 +433,13 @@ int smallm_launch(const float *X, const void *w, float *Y, int64_t mi, int64_t n
     d.ws = (float *)(ws + L.part);
     d.epoch = next_epoch();
     hipError_t e;
-    if (kernel == Q8_SMALLM_MFMA) {
+    if (kernel == Q8_SMALLM_KS) {
+        d.xs = (const bf16x8 *)(ws + L.xs);
+        d.yp = (float *)(ws + L.part);
+        e = launch_split_x(X, ws + L.xs, (int)mi, (int)n, s, (int)mi);
+        if (e != hipSuccess) return fail_hip(e, "q8_0_gemm_smallm split launch");
+        e = launch_gemm_ks(d, 8, s);
+    } else if (kernel == Q8_SMALLM_MFMA) {
         d.xs = (const bf16x8 *)(ws + L.xs);
         e = launch_split_x(X, ws + L.xs, (int)mi, (int)n, s);
         if (e != hipSuccess) return fail_hip(e, "q8_0_gemm_smallm split launch");
@@ -521,14 +573,27 @@ int q8_0_gemm_smallm_workspace(int64_t m, int64_t n, int64_t p, int kernel, size
     *bytes = 0;
     if (n <= 0 || n % kQuants != 0 || n > Q8_MAX_N || p <= 0 || p > Q8_MAX_P || m < 1 || m > Q8_MAX_M)
         return fail(Q8_ERR_SHAPE, "q8_0_gemm_smallm_workspace: shape out of range");
-    const int k = smallm_kernel(kernel, m, n, "q8_0_gemm_smallm_workspace");
+    int k = smallm_kernel(kernel, m, n, "q8_0_gemm_smallm_workspace");
     if (k < 0) return k;
     int dev = 0;
     int rc = check_device(&dev);
     if (rc) return rc;
+    k = smallm_resolve(k, m, n, p, cu_count(dev));
     // (the plan reads only shapes; these pointers are never dereferenced)
     static const float kDummyX[4] = {0.f, 0.f, 0.f, 0.f};
     *bytes = smallm_bytes(kDummyX, kDummyX, nullptr, m, n, p, k, cu_count(dev));
+    return Q8_OK;
+}
+
+int q8_0_gemm_smallm_choice(int64_t m, int64_t n, int64_t p, int *kernel) {
+    if (!kernel) return fail(Q8_ERR_INVALID_ARG, "q8_0_gemm_smallm_choice: kernel is null");
+    *kernel = Q8_SMALLM_AUTO;
+    if (n <= 0 || n % kQuants != 0 || n > Q8_MAX_N || p <= 0 || p > Q8_MAX_P || m < 2 || m > Q8_MAX_M)
+        return fail(Q8_ERR_SHAPE, "q8_0_gemm_smallm_choice: shape out of range (m = 2..16)");
+    int dev = 0;
+    const int rc = check_device(&dev);
+    if (rc) return rc;
+    *kernel = smallm_resolve(Q8_SMALLM_AUTO, m, n, p, cu_count(dev));
     return Q8_OK;
 }
 
@@ -536,11 +601,12 @@ int q8_0_gemm_smallm_kernel(const float *X, const void *w, float *Y, int64_t m, 
                             int kernel, void *workspace, size_t workspace_bytes, void *stream) {
     int rc = validate(X, w, Y, m, n, p, "q8_0_gemm_smallm");
     if (rc) return rc;
-    const int k = smallm_kernel(kernel, m, n, "q8_0_gemm_smallm_kernel");
+    int k = smallm_kernel(kernel, m, n, "q8_0_gemm_smallm_kernel");
     if (k < 0) return k;
     int dev = 0;
     if ((rc = check_device(&dev))) return rc;
     const int64_t cus = cu_count(dev);
+    k = smallm_resolve(k, m, n, p, cus);
     const size_t need = smallm_bytes(X, w, Y, m, n, p, k, cus);
     if (need > 0) {
         if (!workspace || ((uintptr_t)workspace & 255u))
@@ -566,11 +632,12 @@ int q8_0_gemm_smallm_noalloc(const float *X, const void *w, float *Y, int64_t m,
                              void *stream) {
     int rc = validate(X, w, Y, m, n, p, "q8_0_gemm_smallm_noalloc");
     if (rc) return rc;
-    const int k = smallm_kernel(Q8_SMALLM_AUTO, m, n, "q8_0_gemm_smallm_noalloc");
+    int k = smallm_kernel(Q8_SMALLM_AUTO, m, n, "q8_0_gemm_smallm_noalloc");
     if (k < 0) return k;
     int dev = 0;
     if ((rc = check_device(&dev))) return rc;
     const int64_t cus = cu_count(dev);
+    k = smallm_resolve(k, m, n, p, cus);
     const size_t need = smallm_bytes(X, w, Y, m, n, p, k, cus);
     if (need > kScratchBytes)
         return fail(Q8_ERR_SHAPE, "q8_0_gemm_smallm_noalloc: m=" + std::to_string(m) + ", n=" + std::to_string(n) +

@@ -34,9 +34,19 @@ struct GemmDesc {
     int32_t fast_wgs;    // stream-K workgroups; the tail rows follow, one per workgroup
     int32_t tail_row0;
     uint32_t epoch;      // this call's tag on the arrival counters (never 0)
+    int32_t ks_groups;   // k_q8_gemm_ks: groups per column range
+    int32_t ks_ranges;   // column ranges
+    int32_t ks_rows;     // rows per workgroup (a multiple of 32)
+    float *yp;           // per-range sums (ks_ranges > 1)
 };
 
 hipError_t launch_gemm_mfma(const GemmDesc &d, int64_t grid, hipStream_t s);
+// the matrix cores with X held in LDS (k_q8_gemm_ks): rs == 1, 2 <= m <= 16,
+// ks_ranges * ceil(p / ks_rows) workgroups of nw (4 or 8) waves, d.xs from
+// launch_split_x(rows = m), d.yp (ks_ranges * m * p floats) when
+// ks_ranges > 1 (then a second launch adds the ranges)
+hipError_t launch_gemm_ks(const GemmDesc &d, int nw, hipStream_t s);
+int ks_a_bytes(int nw);   // LDS a workgroup keeps for the parts of X (0: no such nw)
 // the vector-unit small batch for m = 2..4 (any rs); d.xs is not used
 hipError_t launch_gemm_valu(const GemmDesc &d, int64_t grid, hipStream_t s);
 int gemm_valu_stage_bytes(int m);   // LDS bytes per workgroup (0 if m is not 2..4)
@@ -47,7 +57,7 @@ constexpr int kVrowMaxM = 3;
 constexpr int kValuMaxM = 4;
 // X (m x n) -> the bf16 parts the matrix-core kernel reads: kXPartsBytesPerBlock
 // bytes per block of 32 columns, for up to 16 rows
-hipError_t launch_split_x(const float *X, void *xs, int m, int n, hipStream_t s);
+hipError_t launch_split_x(const float *X, void *xs, int m, int n, hipStream_t s, int rows = 16);
 // p[0 .. n) = 0 (a fill kernel: no memset node, so it may be captured)
 hipError_t launch_zero_u32(uint32_t *p, int64_t n, hipStream_t s);
 constexpr int64_t kXPartsBytesPerBlock = 3 * 16 * 4 * 16;   // parts x rows x column groups x bf16x8

@@ -52,12 +52,14 @@ __device__ __forceinline__ void split3(const float (&x)[8], bf16x8 &h, bf16x8 &m
 // contiguous 1 KiB, so that one load instruction of a wave (lane = i + 16 g
 // reads entry 4i + g) covers whole cache lines.  Rows i >= m are never
 // written or read.
-__device__ __forceinline__ int64_t xpart_index(int b, int part, int i, int g) {
-    return ((int64_t)b * 3 + part) * 64 + i * 4 + g;
+__device__ __forceinline__ int64_t xpart_index(int b, int part, int i, int g, int rows = 16) {
+    return ((int64_t)b * 3 + part) * (4 * rows) + i * 4 + g;
 }
 
+// rows: the layout's rows per (block, part) -- 16 (rows past m unwritten)
+// or m (k_q8_gemm_ks, which copies whole blocks of parts into LDS)
 __global__ __launch_bounds__(256) void k_split_x(const float *__restrict__ X,
-                                                 bf16x8 *__restrict__ xs, int m, int n) {
+                                                 bf16x8 *__restrict__ xs, int m, int n, int rows) {
     const int nb = n / kQuants;
     const int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x;   // (i, b, g)
     if (t >= (int64_t)m * nb * 4) return;
@@ -67,9 +69,9 @@ __global__ __launch_bounds__(256) void k_split_x(const float *__restrict__ X,
     const float x[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
     XParts o;
     split3(x, o.h, o.m, o.l);
-    xs[xpart_index(b, 0, i, g)] = o.h;
-    xs[xpart_index(b, 1, i, g)] = o.m;
-    xs[xpart_index(b, 2, i, g)] = o.l;
+    xs[xpart_index(b, 0, i, g, rows)] = o.h;
+    xs[xpart_index(b, 1, i, g, rows)] = o.m;
+    xs[xpart_index(b, 2, i, g, rows)] = o.l;
 }
 
 __global__ __launch_bounds__(256) void k_zero_u32(uint32_t *__restrict__ p, int64_t n) {
@@ -807,6 +809,226 @@ __device__ void vrow_streamk(const GemmDesc &d, int64_t b, uint8_t *stage) {
     }
 }
 
+// ---------------------------------------------------------------- m > 1, matrix cores, X held in LDS
+// Y = X W^T for 2 <= m <= 16 where every row is one super-row (n a multiple
+// of 256), on v_mfma_f32_16x16x32_bf16 with X split exactly into bf16 parts
+// (k_split_x, rows = m) as in k_q8_gemm_mfma.  The columns are cut into
+// d.ks_ranges ranges of d.ks_groups groups, and a workgroup owns one range
+// and a block of d.ks_rows rows:
+//  * at its start it copies the range's parts of X (m rows, 1.5 KiB per row
+//    and group) into LDS by direct loads, and keeps them there: every wave
+//    reads its A operands from them, so X crosses from L2 once per workgroup;
+//  * its NW waves take the block's 32-row sub-tiles in turn (wave w:
+//    sub-tiles w, w + NW, ...), each walking the range's groups.  A step
+//    (sub-tile, group) moves 32 rows of W HBM -> LDS by the matvec tile's
+//    direct loads into the wave's one stage (row r at LDS offset 272 r); once
+//    landed, each lane copies the words it feeds the matrix cores -- for
+//    MFMA tile t and block K the quants 8g .. 8g+7 of row 16t + j and the
+//    block's scale -- into registers, the next step's loads go into the
+//    stage at once, and the step is computed from registers.
+// A sub-tile's sums over the range go to Y (one range) or to the range's
+// slice of d.yp, which k_ks_reduce then adds over the ranges in range order.
+template <int NW>
+struct Ks {
+    static constexpr int kWaveRows = 32;
+    static constexpr int kChunks = kWaveRows * kGroupChunks;      // 16-byte chunks of a step's W
+    static constexpr int kLoads = (kChunks + kWave - 1) / kWave;   // direct loads per lane (the last one half)
+    static constexpr int kStage = kWaveRows * kGroupBytes;          // 8704
+    // the parts of X: whatever LDS the stages leave for this many
+    // workgroups per CU (1 with eight waves, 2 with four)
+    static constexpr int kWgsPerCu = NW >= 8 ? 1 : 2;
+    static constexpr int kA = ((160 * 1024 / kWgsPerCu - NW * kStage - 64) / 1536) * 1536;
+};
+
+// One lane's words of a step: quants of tile t, block K, and the scales
+// (binary16 bits) of blocks 2h and 2h + 1 in the low and high halves of
+// s[t][h].
+struct McHeld {
+    uint32_t q[2][kGroupBlocks][2];
+    uint32_t s[2][kGroupBlocks / 2];
+};
+
+// Block K of tile t (rows 16t .. 16t + 15 of the stage) for lane (j, g):
+// the eight quants 8g .. 8g+7 of row 16t + j.
+template <int K>
+__device__ __forceinline__ void mc_hold_quants(const uint8_t *grp, int g, uint32_t (&q)[2]) {
+    constexpr int q0 = K * kBlockBytes + 2;   // the block's first quant byte
+    if constexpr ((q0 & 3) == 0) {
+        const uint32_t *p = reinterpret_cast<const uint32_t *>(grp + q0 + 8 * g);
+        q[0] = p[0];
+        q[1] = p[1];
+    } else {   // the quants start two bytes into a dword
+        const uint32_t *p = reinterpret_cast<const uint32_t *>(grp + q0 - 2 + 8 * g);
+        const uint32_t a0 = p[0], a1 = p[1], a2 = p[2];
+        q[0] = __builtin_amdgcn_alignbyte(a1, a0, 2);
+        q[1] = __builtin_amdgcn_alignbyte(a2, a1, 2);
+    }
+}
+
+__device__ __forceinline__ void mc_hold(const uint8_t *stage, int j, int g, McHeld &H) {
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+        const uint8_t *grp = stage + kGroupBytes * (16 * t + j);
+        mc_hold_quants<0>(grp, g, H.q[t][0]);
+        mc_hold_quants<1>(grp, g, H.q[t][1]);
+        mc_hold_quants<2>(grp, g, H.q[t][2]);
+        mc_hold_quants<3>(grp, g, H.q[t][3]);
+        mc_hold_quants<4>(grp, g, H.q[t][4]);
+        mc_hold_quants<5>(grp, g, H.q[t][5]);
+        mc_hold_quants<6>(grp, g, H.q[t][6]);
+        mc_hold_quants<7>(grp, g, H.q[t][7]);
+#pragma unroll
+        for (int h = 0; h < kGroupBlocks / 2; ++h) {
+            const uint32_t lo = *reinterpret_cast<const uint16_t *>(grp + 2 * h * kBlockBytes);
+            const uint32_t hi = *reinterpret_cast<const uint16_t *>(grp + (2 * h + 1) * kBlockBytes);
+            H.s[t][h] = lo | (hi << 16);
+        }
+    }
+}
+
+// Eight int8 quants -> the B operand (bfloat16 holds every int8 exactly).
+__device__ __forceinline__ bf16x8 mc_bq(const uint32_t (&q)[2]) {
+    bf16x8 b;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        b[e] = (__bf16)(float)(int8_t)(q[0] >> (8 * e));
+        b[4 + e] = (__bf16)(float)(int8_t)(q[1] >> (8 * e));
+    }
+    return b;
+}
+
+// Block K of the held step; `ab` points at its first block's parts in LDS
+// (layout of k_split_x with rows = m): for each tile t, C_t = sum over the
+// parts (h, then m, then l) of A_part B_t, then acc_t += d_t C_t.
+template <int K>
+__device__ __forceinline__ void mc_block(const McHeld &H, const bf16x8 *ab, int ii, int g, int m, f32x4 (&acc)[2]) {
+    const bf16x8 ah = ab[((K * 3 + 0) * m + ii) * 4 + g];
+    const bf16x8 am = ab[((K * 3 + 1) * m + ii) * 4 + g];
+    const bf16x8 al = ab[((K * 3 + 2) * m + ii) * 4 + g];
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+        const bf16x8 b = mc_bq(H.q[t][K]);
+        f32x4 c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, b, f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
+        c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(am, b, c, 0, 0, 0);
+        c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(al, b, c, 0, 0, 0);
+        acc[t] += half_to_float(H.s[t][K / 2] >> (16 * (K & 1))) * c;
+    }
+}
+
+template <int NW>
+__global__ __launch_bounds__(NW * kWave, 1) void k_q8_gemm_ks(GemmDesc d) {
+    using P = Ks<NW>;
+    __shared__ __attribute__((aligned(16))) uint8_t lds[P::kA + NW * P::kStage];
+    const int lane = lane_id();
+    const int wk = NW > 1 ? wave_id() : 0;
+    const int j = lane & 15, g = lane >> 4;
+    const int m = d.m;
+    const int ii = min(j, m - 1);   // A: lane (i, g) with i = lane & 15; rows i >= m read row m - 1
+    const int nkr = d.ks_ranges;
+    const int kr = (int)(blockIdx.x % (uint32_t)nkr);
+    const int64_t row_lo = (int64_t)(blockIdx.x / (uint32_t)nkr) * d.ks_rows;
+    const int G = d.gsr;
+    const int k0 = kr * d.ks_groups, k1 = min(G, k0 + d.ks_groups);
+    const int64_t rows = min((int64_t)d.ks_rows, (int64_t)d.p - row_lo);
+    const int nst = (int)((rows + P::kWaveRows - 1) / P::kWaveRows);
+    uint8_t *wst = lds + P::kA + wk * P::kStage;
+    const bf16x8 *abase = reinterpret_cast<const bf16x8 *>(lds);
+    // the range's parts: blocks 8 k0 .. 8 k1 - 1, m * 192 bytes each, one
+    // contiguous run of the split layout, copied 1 KiB per wave load
+    {
+        const int chunks = (k1 - k0) * kGroupBlocks * m * 12;
+        const uint8_t *src = reinterpret_cast<const uint8_t *>(d.xs) + (int64_t)k0 * kGroupBlocks * m * 192;
+        const uint32_t la = __builtin_amdgcn_readfirstlane(lds_addr(lds));
+        for (int c = wk; c * kWave < chunks; c += NW)
+            if (c * kWave + lane < chunks) dma16_v(src + 16 * (c * kWave + lane), la + 1024 * c);
+    }
+    const uint8_t *wt = uniform_ptr(d.w + row_lo * d.sr_bytes);
+    const uint32_t lw = __builtin_amdgcn_readfirstlane(lds_addr(wst));
+    const int last = (int)(rows - 1);   // the block's last row
+    // load c of lane l carries chunk q = 64c + l of a step: row q / 17 of
+    // the sub-tile (clamped to the block's last row), chunk q % 17
+    uint32_t off[P::kLoads];
+    auto offsets = [&](int st) {
+#pragma unroll
+        for (int c = 0; c < P::kLoads; ++c) {
+            const int q = kWave * c + lane;
+            const int r = q / kGroupChunks;
+            off[c] = (uint32_t)((int64_t)min(P::kWaveRows * st + r, last) * d.sr_bytes + 16 * (q - kGroupChunks * r));
+        }
+    };
+    auto issue = [&](int kk) {
+#pragma unroll
+        for (int c = 0; c < P::kLoads; ++c) {
+            if (c + 1 < P::kLoads || P::kChunks % kWave == 0 || lane < P::kChunks % kWave)
+                dma16_s(wt, off[c] + (uint32_t)kk * kGroupBytes, lw + kWave * 16 * c);
+        }
+    };
+    int st = wk, kk = k0;
+    if (st < nst && k0 < k1) {
+        offsets(st);
+        issue(kk);
+    }
+    // the parts (every wave's share) and this wave's first step have landed
+    __builtin_amdgcn_s_waitcnt(0x0F70);
+    asm volatile("" ::: "memory");
+    __syncthreads();
+    if (k0 >= k1) return;
+    f32x4 acc[2];
+    acc[0] = f32x4{0.f, 0.f, 0.f, 0.f};
+    acc[1] = acc[0];
+    while (st < nst) {
+        __builtin_amdgcn_s_waitcnt(0x0F70);   // this step's W has landed
+        asm volatile("" ::: "memory");
+        McHeld H;
+        mc_hold(wst, j, g, H);
+        // the stage is refilled only after every read of it has returned
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+        int nst_next = st, nkk = kk + 1;
+        if (nkk == k1) {
+            nkk = k0;
+            nst_next = st + NW;
+        }
+        if (nst_next < nst) {
+            if (nst_next != st) offsets(nst_next);
+            issue(nkk);
+        }
+        const bf16x8 *ab = abase + (kk - k0) * kGroupBlocks * 3 * m * 4;
+        mc_block<0>(H, ab, ii, g, m, acc);
+        mc_block<1>(H, ab, ii, g, m, acc);
+        mc_block<2>(H, ab, ii, g, m, acc);
+        mc_block<3>(H, ab, ii, g, m, acc);
+        mc_block<4>(H, ab, ii, g, m, acc);
+        mc_block<5>(H, ab, ii, g, m, acc);
+        mc_block<6>(H, ab, ii, g, m, acc);
+        mc_block<7>(H, ab, ii, g, m, acc);
+        if (kk + 1 == k1) {
+            // lane (j, g) holds Y[4g + e][row_lo + 32 st + 16t + j] in acc[t][e]
+            float *out = nkr == 1 ? d.Y : d.yp + (int64_t)kr * m * d.p;
+#pragma unroll
+            for (int t = 0; t < 2; ++t)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int i = 4 * g + e, r = P::kWaveRows * st + 16 * t + j;
+                    if (i < m && r <= last) out[(int64_t)i * d.p + row_lo + r] = acc[t][e];
+                }
+            acc[0] = f32x4{0.f, 0.f, 0.f, 0.f};
+            acc[1] = acc[0];
+        }
+        st = nst_next;
+        kk = nkk;
+    }
+}
+
+// Y = the sum over the ranges of d.yp, in range order.
+__global__ __launch_bounds__(256) void k_ks_reduce(GemmDesc d) {
+    const int64_t total = (int64_t)d.m * d.p;
+    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (i >= total) return;
+    float v = d.yp[i];
+    for (int r = 1; r < d.ks_ranges; ++r) v += d.yp[(int64_t)r * total + i];
+    d.Y[i] = v;
+}
+
 template <int RS>
 __global__ __launch_bounds__(kWave, 1) void k_q8_gemm_mfma(GemmDesc d) {
     __shared__ __attribute__((aligned(16))) uint8_t stage[2 * kStageBytesM];
@@ -844,10 +1066,10 @@ __global__ __launch_bounds__(NW * kWave) void k_q8_gemm_vrow(GemmDesc d) {
 
 }  // namespace
 
-hipError_t launch_split_x(const float *X, void *xs, int m, int n, hipStream_t s) {
+hipError_t launch_split_x(const float *X, void *xs, int m, int n, hipStream_t s, int rows) {
     const int64_t items = (int64_t)m * (n / kQuants) * 4;
     hipLaunchKernelGGL(k_split_x, dim3((unsigned)((items + 255) / 256)), dim3(256), 0, s, X,
-                       (bf16x8 *)xs, m, n);
+                       (bf16x8 *)xs, m, n, rows);
     return hipGetLastError();
 }
 
@@ -864,6 +1086,27 @@ hipError_t launch_gemm_mfma(const GemmDesc &d, int64_t grid, hipStream_t s) {
         case 2: hipLaunchKernelGGL((k_q8_gemm_mfma<2>), gr, bl, 0, s, d); break;
         default: return hipErrorInvalidValue;
     }
+    return hipGetLastError();
+}
+
+int ks_a_bytes(int nw) { return nw == 8 ? Ks<8>::kA : nw == 4 ? Ks<4>::kA : 0; }
+
+hipError_t launch_gemm_ks(const GemmDesc &d, int nw, hipStream_t s) {
+    if (d.rs != 1 || d.m < 2 || d.m > 16 || d.ks_ranges < 1 || d.ks_groups < 1 || d.ks_rows < 32 ||
+        d.ks_rows % 32 || (int64_t)d.ks_ranges * d.ks_groups < d.gsr ||
+        (int64_t)d.ks_groups * kGroupBlocks * d.m * 192 > ks_a_bytes(nw))
+        return hipErrorInvalidValue;
+    const int64_t blocks = (int64_t)d.ks_ranges * ((d.p + d.ks_rows - 1) / d.ks_rows);
+    const dim3 gr((unsigned)blocks), bl((unsigned)(nw * kWave));
+    switch (nw) {
+        case 4: hipLaunchKernelGGL((k_q8_gemm_ks<4>), gr, bl, 0, s, d); break;
+        case 8: hipLaunchKernelGGL((k_q8_gemm_ks<8>), gr, bl, 0, s, d); break;
+        default: return hipErrorInvalidValue;
+    }
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess || d.ks_ranges == 1) return e;
+    const int64_t total = (int64_t)d.m * d.p;
+    hipLaunchKernelGGL(k_ks_reduce, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, s, d);
     return hipGetLastError();
 }
 

@@ -142,7 +142,8 @@ def test_gemv_shaped_validation(q8, c, waves, st, n, code):
 
 
 @pytest.mark.parametrize("m,n,kernel,code", [
-    (2, 256, 5, -1), (2, 256, -1, -1),          # unknown kernel
+    (2, 256, 6, -1), (2, 256, -1, -1),          # unknown kernel
+    (2, 896, 5, -2),                            # X held in LDS: rows of whole groups
     (4, 256, 3, -2), (4, 256, 4, -2),           # the row-and-block-pair kernel takes m <= 3
     (2, 896, 3, -2),                            # ... and rows of whole groups (n % 256 == 0)
     (2, 96, 2, -2),                             # the matrix cores take rows of 1 or 2 per super-row
@@ -164,6 +165,8 @@ def test_no_device_path(q8):
     assert q8.lib.q8_0_argmax(X, 8, Y, WS, 1 << 20, None) == -5
     assert q8.lib.q8_0_attention_decode(X, W, F, Y, 8, 128, 64, 2, 1, WS, 1 << 20, None) == -5
     assert q8.lib.q8_0_gemm_smallm(X, W, Y, 2, 64, 4, WS, 1 << 20, None) == -5
+    k = ctypes.c_int(-7)
+    assert q8.lib.q8_0_gemm_smallm_choice(2, 256, 4, ctypes.byref(k)) == -5
     layers = (q8.Q8LayerW * 1)(_layer(q8))
     h = ctypes.c_void_p()
     assert q8.lib.q8_0_step_create(ctypes.byref(_model(q8, layers)), ctypes.byref(h)) == -5
@@ -297,6 +300,11 @@ def test_workspace_queries_refuse(q8):
     assert _query(L.q8_0_gemm_smallm_workspace, 2, 48, 4, 0)[0] == -2
     assert _query(L.q8_0_gemm_smallm_workspace, 2, 256, 4, 9)[0] == -1     # unknown kernel
     assert _query(L.q8_0_gemm_smallm_workspace, 4, 256, 4, 3)[0] == -2     # kernel does not take m
+    k = ctypes.c_int(-7)
+    assert L.q8_0_gemm_smallm_choice(2, 256, 4, None) == -1
+    assert L.q8_0_gemm_smallm_choice(1, 256, 4, ctypes.byref(k)) == -2 and k.value == 0   # m = 1 is the matvec's
+    assert L.q8_0_gemm_smallm_choice(17, 256, 4, ctypes.byref(k)) == -2
+    assert L.q8_0_gemm_smallm_choice(2, 48, 4, ctypes.byref(k)) == -2
 
 
 @pytest.mark.parametrize("call,code", [

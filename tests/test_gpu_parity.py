@@ -176,7 +176,8 @@ GEMM_SHAPES = [(256, 130), (896, 70), (896, 71), (3584, 300), (160, 11), (192, 3
 # row-and-block-pair kernel with one wave per workgroup instead of two.
 GEMM_CASES = ([(m, None) for m in (1, 2, 3, 4, 5, 8, 13, 16)] +
               [(m, "VALU") for m in (2, 3, 4, 5, 8, 13, 16)] +
-              [(m, "MFMA") for m in (2, 3)] + [(m, "VROW1") for m in (2, 3)])
+              [(m, "MFMA") for m in (2, 3)] + [(m, "VROW1") for m in (2, 3)] +
+              [(m, "KS") for m in (2, 5, 8, 16)])
 
 
 def _kernel_takes(kernel, m, n):
@@ -186,6 +187,8 @@ def _kernel_takes(kernel, m, n):
         return rs <= 2 and m >= 2
     if kernel in ("VROW", "VROW1"):
         return rs == 1 and 2 <= m <= 3
+    if kernel == "KS":
+        return rs == 1 and m >= 2
     return m >= 2
 
 
@@ -291,6 +294,53 @@ def test_gemm_mfma_sweep(q8, n, p, m):
     assert np.array_equal(down(Y).view(np.uint32), Yh.view(np.uint32))
 
 
+@pytest.mark.parametrize("m,n,p,kernel", [
+    (2, 18944, 3584, "VROW"), (3, 3584, 18944, "VROW"), (2, 3584, 152064, "KS"), (4, 18944, 3584, "KS"),
+    (16, 3584, 18944, "KS"), (16, 3584, 152064, "MFMA"), (5, 896, 70, "MFMA"), (5, 192, 37, "VALU")])
+def test_gemm_choice(q8, m, n, p, kernel):
+    """The kernel q8_0_gemm_smallm runs, as q8_0_gemm_smallm_choice reports
+    it: the row-and-block-pair vector kernel at m <= 3 below 65536 rows, the
+    matrix cores with X held in LDS for other rows of whole groups (unless
+    their per-range sums pass 16 MiB: the 7B lm_head at m = 16), the
+    stream-K matrix cores for super-rows of 1 or 2, else the vector units."""
+    log("gemm choice m=%d n=%d p=%d" % (m, n, p))
+    assert q8.gemm_smallm_choice(m, n, p) == getattr(q8, "SMALLM_" + kernel)
+
+
+def _ks_sweep_cases():
+    rng = np.random.default_rng(5151)
+    cases = []
+    for k in range(20):
+        n = 256 * int(rng.integers(1, 80))               # rows of whole groups
+        p = int(rng.integers(1, 6000))
+        cases.append((n, p, int(rng.integers(2, 17))))
+    return cases
+
+
+@pytest.mark.parametrize("n,p,m", _ks_sweep_cases(), ids=lambda v: str(v))
+def test_gemm_ks_sweep(q8, n, p, m):
+    """Seeded random shapes on the matrix cores with X held in LDS (m =
+    2..16; one or several column ranges, so with and without the sum over
+    ranges; row blocks ending inside a 32-row sub-tile): every output
+    against the oracle, and bitwise repeatable."""
+    import torch
+    log("gemm ks sweep n=%d p=%d m=%d" % (n, p, m))
+    rng = np.random.default_rng(n * 7919 + p * 31 + m)
+    w = synth.q8_weights(n, p, rng)
+    X = synth.activations(n, rng, m).reshape(m, n)
+    wd = w_dev(w, n, p)
+    Xd = up(X)
+    Y = torch.full((m, p), float("nan"), dtype=torch.float32, device="cuda")
+    q8.gemm_smallm(Xd, wd, Y, kernel=q8.SMALLM_KS)
+    Yh = down(Y).copy()
+    _, Y64, MAG = oracle.gemm(w, X, m, n, p)
+    for i in range(m):
+        parity(Yh[i], Y64[i], MAG[i], "ks sweep row %d" % i)
+    Y.fill_(float("nan"))
+    q8.gemm_smallm(Xd, wd, Y, kernel=q8.SMALLM_KS)
+    assert np.array_equal(down(Y).view(np.uint32), Yh.view(np.uint32))
+
+
 @pytest.mark.parametrize("m", [2, 3, 16])
 def test_gemm_identical_rows(q8, m):
     """m equal rows of X give m bitwise-equal rows of Y (m = 2, 3 on the
@@ -308,7 +358,7 @@ def test_gemm_identical_rows(q8, m):
     del torch
 
 
-@pytest.mark.parametrize("m,path", [(2, None), (3, None), (5, "VALU"), (5, None), (16, None)],
+@pytest.mark.parametrize("m,path", [(2, None), (3, None), (5, "VALU"), (5, None), (16, None), (16, "KS")],
                          ids=lambda v: str(v))
 def test_gemm_sign_and_scale(q8, m, path):
     """Y(4X) = 4 Y(X) bit for bit on every path, and Y(-X) = -Y(X) bit for

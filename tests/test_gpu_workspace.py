@@ -114,7 +114,7 @@ def _replays_equal_eager(q8, label, run, outs, replays=3):
 
 
 @pytest.mark.parametrize("m,kernel", [(2, "VROW"), (3, "VROW1"), (4, "VALU"), (6, "VALU"), (5, "MFMA"),
-                                      (16, "MFMA"), (2, None), (16, None)])
+                                      (16, "MFMA"), (8, "KS"), (16, "KS"), (2, None), (16, None)])
 def test_smallm_under_capture(q8, m, kernel):
     import torch
     log("smallm under capture m=%d kernel=%s" % (m, kernel))
