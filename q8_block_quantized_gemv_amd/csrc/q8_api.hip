@@ -338,12 +338,9 @@ SmallmWs smallm_plan(GemmDesc &d, int kernel, int64_t cus) {
     size_t part = 0, xs = 0;
     if (kernel == Q8_SMALLM_KS) {
         plan_ks(d, cus);
-        xs = (size_t)d.nb * d.m * 192;
         part = d.ks_ranges > 1 ? (size_t)d.ks_ranges * d.m * d.p * sizeof(float) : 0;
-        L.cnt = 0;
-        L.xs = 0;
-        L.part = align256(xs);
-        L.bytes = L.part + align256(part);
+        L.part = 0;
+        L.bytes = align256(part);
         return L;
     }
     if (kernel == Q8_SMALLM_MFMA) {
@@ -434,10 +431,7 @@ int smallm_launch(const float *X, const void *w, float *Y, int64_t mi, int64_t n
     d.epoch = next_epoch();
     hipError_t e;
     if (kernel == Q8_SMALLM_KS) {
-        d.xs = (const bf16x8 *)(ws + L.xs);
         d.yp = (float *)(ws + L.part);
-        e = launch_split_x(X, ws + L.xs, (int)mi, (int)n, s, (int)mi);
-        if (e != hipSuccess) return fail_hip(e, "q8_0_gemm_smallm split launch");
         e = launch_gemm_ks(d, 8, s);
     } else if (kernel == Q8_SMALLM_MFMA) {
         d.xs = (const bf16x8 *)(ws + L.xs);

@@ -42,9 +42,9 @@ struct GemmDesc {
 
 hipError_t launch_gemm_mfma(const GemmDesc &d, int64_t grid, hipStream_t s);
 // the matrix cores with X held in LDS (k_q8_gemm_ks): rs == 1, 2 <= m <= 16,
-// ks_ranges * ceil(p / ks_rows) workgroups of nw (4 or 8) waves, d.xs from
-// launch_split_x(rows = m), d.yp (ks_ranges * m * p floats) when
-// ks_ranges > 1 (then a second launch adds the ranges)
+// ks_ranges * ceil(p / ks_rows) workgroups of nw (4 or 8) waves (each splits
+// its range of X itself; d.xs is not used), d.yp (ks_ranges * m * p floats,
+// 16-byte aligned) when ks_ranges > 1 (then a second launch adds the ranges)
 hipError_t launch_gemm_ks(const GemmDesc &d, int nw, hipStream_t s);
 int ks_a_bytes(int nw);   // LDS a workgroup keeps for the parts of X (0: no such nw)
 // the vector-unit small batch for m = 2..4 (any rs); d.xs is not used
@@ -57,7 +57,7 @@ constexpr int kVrowMaxM = 3;
 constexpr int kValuMaxM = 4;
 // X (m x n) -> the bf16 parts the matrix-core kernel reads: kXPartsBytesPerBlock
 // bytes per block of 32 columns, for up to 16 rows
-hipError_t launch_split_x(const float *X, void *xs, int m, int n, hipStream_t s, int rows = 16);
+hipError_t launch_split_x(const float *X, void *xs, int m, int n, hipStream_t s);
 // p[0 .. n) = 0 (a fill kernel: no memset node, so it may be captured)
 hipError_t launch_zero_u32(uint32_t *p, int64_t n, hipStream_t s);
 constexpr int64_t kXPartsBytesPerBlock = 3 * 16 * 4 * 16;   // parts x rows x column groups x bf16x8

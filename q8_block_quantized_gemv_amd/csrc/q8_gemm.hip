@@ -52,14 +52,12 @@ __device__ __forceinline__ void split3(const float (&x)[8], bf16x8 &h, bf16x8 &m
 // contiguous 1 KiB, so that one load instruction of a wave (lane = i + 16 g
 // reads entry 4i + g) covers whole cache lines.  Rows i >= m are never
 // written or read.
-__device__ __forceinline__ int64_t xpart_index(int b, int part, int i, int g, int rows = 16) {
-    return ((int64_t)b * 3 + part) * (4 * rows) + i * 4 + g;
+__device__ __forceinline__ int64_t xpart_index(int b, int part, int i, int g) {
+    return ((int64_t)b * 3 + part) * 64 + i * 4 + g;
 }
 
-// rows: the layout's rows per (block, part) -- 16 (rows past m unwritten)
-// or m (k_q8_gemm_ks, which copies whole blocks of parts into LDS)
 __global__ __launch_bounds__(256) void k_split_x(const float *__restrict__ X,
-                                                 bf16x8 *__restrict__ xs, int m, int n, int rows) {
+                                                 bf16x8 *__restrict__ xs, int m, int n) {
     const int nb = n / kQuants;
     const int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x;   // (i, b, g)
     if (t >= (int64_t)m * nb * 4) return;
@@ -69,9 +67,9 @@ __global__ __launch_bounds__(256) void k_split_x(const float *__restrict__ X,
     const float x[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
     XParts o;
     split3(x, o.h, o.m, o.l);
-    xs[xpart_index(b, 0, i, g, rows)] = o.h;
-    xs[xpart_index(b, 1, i, g, rows)] = o.m;
-    xs[xpart_index(b, 2, i, g, rows)] = o.l;
+    xs[xpart_index(b, 0, i, g)] = o.h;
+    xs[xpart_index(b, 1, i, g)] = o.m;
+    xs[xpart_index(b, 2, i, g)] = o.l;
 }
 
 __global__ __launch_bounds__(256) void k_zero_u32(uint32_t *__restrict__ p, int64_t n) {
@@ -812,12 +810,13 @@ __device__ void vrow_streamk(const GemmDesc &d, int64_t b, uint8_t *stage) {
 // ---------------------------------------------------------------- m > 1, matrix cores, X held in LDS
 // Y = X W^T for 2 <= m <= 16 where every row is one super-row (n a multiple
 // of 256), on v_mfma_f32_16x16x32_bf16 with X split exactly into bf16 parts
-// (k_split_x, rows = m) as in k_q8_gemm_mfma.  The columns are cut into
-// d.ks_ranges ranges of d.ks_groups groups, and a workgroup owns one range
-// and a block of d.ks_rows rows:
-//  * at its start it copies the range's parts of X (m rows, 1.5 KiB per row
-//    and group) into LDS by direct loads, and keeps them there: every wave
-//    reads its A operands from them, so X crosses from L2 once per workgroup;
+// as in k_q8_gemm_mfma.  The columns are cut into d.ks_ranges ranges of
+// d.ks_groups groups, and a workgroup owns one range and a block of
+// d.ks_rows rows:
+//  * at its start it reads the range's x values (m rows) and splits them
+//    into their parts in LDS (1.5 KiB per row of X and group), and keeps them
+//    there: every wave reads its A operands from them, so X crosses from L2
+//    once per workgroup and needs no launch of its own;
 //  * its NW waves take the block's 32-row sub-tiles in turn (wave w:
 //    sub-tiles w, w + NW, ...), each walking the range's groups.  A step
 //    (sub-tile, group) moves 32 rows of W HBM -> LDS by the matvec tile's
@@ -933,15 +932,6 @@ __global__ __launch_bounds__(NW * kWave, 1) void k_q8_gemm_ks(GemmDesc d) {
     const int nst = (int)((rows + P::kWaveRows - 1) / P::kWaveRows);
     uint8_t *wst = lds + P::kA + wk * P::kStage;
     const bf16x8 *abase = reinterpret_cast<const bf16x8 *>(lds);
-    // the range's parts: blocks 8 k0 .. 8 k1 - 1, m * 192 bytes each, one
-    // contiguous run of the split layout, copied 1 KiB per wave load
-    {
-        const int chunks = (k1 - k0) * kGroupBlocks * m * 12;
-        const uint8_t *src = reinterpret_cast<const uint8_t *>(d.xs) + (int64_t)k0 * kGroupBlocks * m * 192;
-        const uint32_t la = __builtin_amdgcn_readfirstlane(lds_addr(lds));
-        for (int c = wk; c * kWave < chunks; c += NW)
-            if (c * kWave + lane < chunks) dma16_v(src + 16 * (c * kWave + lane), la + 1024 * c);
-    }
     const uint8_t *wt = uniform_ptr(d.w + row_lo * d.sr_bytes);
     const uint32_t lw = __builtin_amdgcn_readfirstlane(lds_addr(wst));
     const int last = (int)(rows - 1);   // the block's last row
@@ -968,9 +958,27 @@ __global__ __launch_bounds__(NW * kWave, 1) void k_q8_gemm_ks(GemmDesc d) {
         offsets(st);
         issue(kk);
     }
-    // the parts (every wave's share) and this wave's first step have landed
-    __builtin_amdgcn_s_waitcnt(0x0F70);
-    asm volatile("" ::: "memory");
+    // The range's x values, split into their parts in LDS (layout of
+    // k_split_x with rows = m, blocks counted from the range's first): thread
+    // q takes pieces q, q + 64 NW, ... of (row i, block b, column group g),
+    // eight floats each.  (Their loads are waited for together with the
+    // first step's, which the step needs anyway.)
+    {
+        bf16x8 *ab = reinterpret_cast<bf16x8 *>(lds);
+        const int nbk = (k1 - k0) * kGroupBlocks;
+        for (int c = threadIdx.x; c < m * nbk * 4; c += NW * kWave) {
+            const int i = c / (nbk * 4), b = (c >> 2) % nbk, gg = c & 3;
+            const float4 *src = reinterpret_cast<const float4 *>(d.X + (int64_t)i * d.n +
+                                                                 (int64_t)(k0 * kGroupBlocks + b) * kQuants + 8 * gg);
+            const float4 v0 = src[0], v1 = src[1];
+            const float x[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
+            XParts o;
+            split3(x, o.h, o.m, o.l);
+            ab[((b * 3 + 0) * m + i) * 4 + gg] = o.h;
+            ab[((b * 3 + 1) * m + i) * 4 + gg] = o.m;
+            ab[((b * 3 + 2) * m + i) * 4 + gg] = o.l;
+        }
+    }
     __syncthreads();
     if (k0 >= k1) return;
     f32x4 acc[2];
@@ -1019,14 +1027,33 @@ __global__ __launch_bounds__(NW * kWave, 1) void k_q8_gemm_ks(GemmDesc d) {
     }
 }
 
-// Y = the sum over the ranges of d.yp, in range order.
+// Y = the sum over the ranges of d.yp, in range order, four outputs a thread
+// (read as float4 when m * p is a multiple of 4, so that every range's slice
+// of the 256-byte aligned workspace stays 16-byte aligned; else one by one).
 __global__ __launch_bounds__(256) void k_ks_reduce(GemmDesc d) {
     const int64_t total = (int64_t)d.m * d.p;
-    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    const int64_t i = 4 * ((int64_t)blockIdx.x * 256 + threadIdx.x);
     if (i >= total) return;
-    float v = d.yp[i];
-    for (int r = 1; r < d.ks_ranges; ++r) v += d.yp[(int64_t)r * total + i];
-    d.Y[i] = v;
+    if (i + 4 <= total && (total & 3) == 0) {
+        float4 v = *reinterpret_cast<const float4 *>(d.yp + i);
+        for (int r = 1; r < d.ks_ranges; ++r) {
+            const float4 u = *reinterpret_cast<const float4 *>(d.yp + (int64_t)r * total + i);
+            v.x += u.x;
+            v.y += u.y;
+            v.z += u.z;
+            v.w += u.w;
+        }
+        d.Y[i] = v.x;   // Y is only 4-byte aligned
+        d.Y[i + 1] = v.y;
+        d.Y[i + 2] = v.z;
+        d.Y[i + 3] = v.w;
+        return;
+    }
+    for (int64_t k = i; k < min(i + 4, total); ++k) {
+        float v = d.yp[k];
+        for (int r = 1; r < d.ks_ranges; ++r) v += d.yp[(int64_t)r * total + k];
+        d.Y[k] = v;
+    }
 }
 
 template <int RS>
@@ -1066,10 +1093,10 @@ __global__ __launch_bounds__(NW * kWave) void k_q8_gemm_vrow(GemmDesc d) {
 
 }  // namespace
 
-hipError_t launch_split_x(const float *X, void *xs, int m, int n, hipStream_t s, int rows) {
+hipError_t launch_split_x(const float *X, void *xs, int m, int n, hipStream_t s) {
     const int64_t items = (int64_t)m * (n / kQuants) * 4;
     hipLaunchKernelGGL(k_split_x, dim3((unsigned)((items + 255) / 256)), dim3(256), 0, s, X,
-                       (bf16x8 *)xs, m, n, rows);
+                       (bf16x8 *)xs, m, n);
     return hipGetLastError();
 }
 
@@ -1106,7 +1133,7 @@ hipError_t launch_gemm_ks(const GemmDesc &d, int nw, hipStream_t s) {
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || d.ks_ranges == 1) return e;
     const int64_t total = (int64_t)d.m * d.p;
-    hipLaunchKernelGGL(k_ks_reduce, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, s, d);
+    hipLaunchKernelGGL(k_ks_reduce, dim3((unsigned)((total + 1023) / 1024)), dim3(256), 0, s, d);
     return hipGetLastError();
 }
 

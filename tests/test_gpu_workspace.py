@@ -62,8 +62,10 @@ def test_smallm_repeated_calls_allocate_nothing(q8):
 
 
 def test_smallm_workspace_too_small_is_refused(q8):
+    """Workspace errors, on a call that needs one (n = 18944 at m = 4 cuts the
+    columns into several ranges, whose sums the workspace holds)."""
     import torch
-    n, p, m = 3584, 300, 4
+    n, p, m = 18944, 300, 4
     rng = np.random.default_rng(5)
     wd = w_dev(synth.q8_weights(n, p, rng), n, p)
     X = up(synth.activations(n, rng, m).reshape(m, n))

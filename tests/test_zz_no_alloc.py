@@ -74,10 +74,11 @@ def test_noalloc_allocates_nothing(q8):
 
 
 def test_noalloc_refuses_past_its_scratch(q8):
-    """m = 8 at n = 2^20 runs on the matrix cores, whose split of X alone
-    takes 48 MiB: refused before anything is enqueued."""
+    """m = 4 at n = 2^20 - 128 (rows of two per super-row) runs on the
+    stream-K matrix cores, whose split of X alone takes 96 MiB: refused
+    before anything is enqueued."""
     import torch
-    m, n, p = 8, 1 << 20, 64
+    m, n, p = 4, (1 << 20) - 128, 64
     need = q8.gemm_smallm_workspace(m, n, p)
     assert need > 32 << 20
     X = torch.zeros((m, n), dtype=torch.float32, device="cuda")
