@@ -319,6 +319,14 @@ void plan_ks(GemmDesc &d, int64_t cus) {
     const int64_t blocks = std::max<int64_t>(1, cus / nkr);
     int64_t rows = (d.p + blocks - 1) / blocks;
     d.ks_rows = (int32_t)std::max<int64_t>(32, (rows + 31) / 32 * 32);
+    // The ranges' sums: added by each row block's last workgroup (no second
+    // launch) where that is at most 32 loads a thread and the ranges hold at
+    // most 512K sums, else by k_ks_reduce.  The in-kernel sum has its sums
+    // stored device-coherent, one by one: measured 1.1 us faster for down at
+    // m = 4 and 8, but 4.2 us slower for gate at m = 16 (1.5M sums, 60
+    // loads a thread) and 10.9 us for the lm_head at m = 8 (2.4M sums).
+    d.ks_sum_here = nkr > 1 && nkr * d.m * (int64_t)d.ks_rows <= 32 * 8 * kWave &&
+                    nkr * d.m * (int64_t)d.p <= ((int64_t)1 << 19) ? 1 : 0;
 }
 
 // A small-batch product's workspace, every piece 256-byte aligned: the
@@ -339,8 +347,10 @@ SmallmWs smallm_plan(GemmDesc &d, int kernel, int64_t cus) {
     if (kernel == Q8_SMALLM_KS) {
         plan_ks(d, cus);
         part = d.ks_ranges > 1 ? (size_t)d.ks_ranges * d.m * d.p * sizeof(float) : 0;
-        L.part = 0;
-        L.bytes = align256(part);
+        const size_t cnt = d.ks_sum_here ? (size_t)((d.p + d.ks_rows - 1) / d.ks_rows) * 8 : 0;
+        L.cnt = 0;
+        L.part = align256(cnt);
+        L.bytes = L.part + align256(part);
         return L;
     }
     if (kernel == Q8_SMALLM_MFMA) {
@@ -432,7 +442,7 @@ int smallm_launch(const float *X, const void *w, float *Y, int64_t mi, int64_t n
     hipError_t e;
     if (kernel == Q8_SMALLM_KS) {
         d.yp = (float *)(ws + L.part);
-        e = launch_gemm_ks(d, 8, s);
+        e = launch_gemm_ks(d, 8, s);   // (d.cnt and d.epoch are set above)
     } else if (kernel == Q8_SMALLM_MFMA) {
         d.xs = (const bf16x8 *)(ws + L.xs);
         e = launch_split_x(X, ws + L.xs, (int)mi, (int)n, s);

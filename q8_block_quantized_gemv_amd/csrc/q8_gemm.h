@@ -38,13 +38,16 @@ struct GemmDesc {
     int32_t ks_ranges;   // column ranges
     int32_t ks_rows;     // rows per workgroup (a multiple of 32)
     float *yp;           // per-range sums (ks_ranges > 1)
+    int32_t ks_sum_here; // the last workgroup of a row block adds the ranges (counters in cnt)
 };
 
 hipError_t launch_gemm_mfma(const GemmDesc &d, int64_t grid, hipStream_t s);
 // the matrix cores with X held in LDS (k_q8_gemm_ks): rs == 1, 2 <= m <= 16,
 // ks_ranges * ceil(p / ks_rows) workgroups of nw (4 or 8) waves (each splits
 // its range of X itself; d.xs is not used), d.yp (ks_ranges * m * p floats,
-// 16-byte aligned) when ks_ranges > 1 (then a second launch adds the ranges)
+// 16-byte aligned) when ks_ranges > 1 (then the row blocks' last workgroups
+// add the ranges, with d.cnt one counter per row block, or a second launch
+// does, as d.ks_sum_here says)
 hipError_t launch_gemm_ks(const GemmDesc &d, int nw, hipStream_t s);
 int ks_a_bytes(int nw);   // LDS a workgroup keeps for the parts of X (0: no such nw)
 // the vector-unit small batch for m = 2..4 (any rs); d.xs is not used

@@ -826,7 +826,9 @@ __device__ void vrow_streamk(const GemmDesc &d, int64_t b, uint8_t *stage) {
 //    block's scale -- into registers, the next step's loads go into the
 //    stage at once, and the step is computed from registers.
 // A sub-tile's sums over the range go to Y (one range) or to the range's
-// slice of d.yp, which k_ks_reduce then adds over the ranges in range order.
+// slice of d.yp; the ranges' slices are then added in range order, by the
+// last of a row block's workgroups to arrive on its counter (d.ks_sum_here)
+// or by a second launch, k_ks_reduce.
 template <int NW>
 struct Ks {
     static constexpr int kWaveRows = 32;
@@ -980,11 +982,10 @@ __global__ __launch_bounds__(NW * kWave, 1) void k_q8_gemm_ks(GemmDesc d) {
         }
     }
     __syncthreads();
-    if (k0 >= k1) return;
     f32x4 acc[2];
     acc[0] = f32x4{0.f, 0.f, 0.f, 0.f};
     acc[1] = acc[0];
-    while (st < nst) {
+    while (st < nst) {   // (the launcher refuses empty ranges)
         __builtin_amdgcn_s_waitcnt(0x0F70);   // this step's W has landed
         asm volatile("" ::: "memory");
         McHeld H;
@@ -1011,19 +1012,60 @@ __global__ __launch_bounds__(NW * kWave, 1) void k_q8_gemm_ks(GemmDesc d) {
         mc_block<7>(H, ab, ii, g, m, acc);
         if (kk + 1 == k1) {
             // lane (j, g) holds Y[4g + e][row_lo + 32 st + 16t + j] in acc[t][e]
-            float *out = nkr == 1 ? d.Y : d.yp + (int64_t)kr * m * d.p;
 #pragma unroll
             for (int t = 0; t < 2; ++t)
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
                     const int i = 4 * g + e, r = P::kWaveRows * st + 16 * t + j;
-                    if (i < m && r <= last) out[(int64_t)i * d.p + row_lo + r] = acc[t][e];
+                    if (i < m && r <= last) {
+                        float *o = nkr == 1 ? d.Y + (int64_t)i * d.p + row_lo + r
+                                            : d.yp + ((int64_t)kr * m + i) * d.p + row_lo + r;
+                        if (d.ks_sum_here) store_partial(o, acc[t][e]);   // read by another workgroup
+                        else *o = acc[t][e];
+                    }
                 }
             acc[0] = f32x4{0.f, 0.f, 0.f, 0.f};
             acc[1] = acc[0];
         }
         st = nst_next;
         kk = nkk;
+    }
+    if (nkr == 1 || !d.ks_sum_here) return;
+    // The ranges' sums meet here: every wave's share is stored before wave 0
+    // counts the workgroup's arrival on the row block's counter, and the last
+    // of the block's ranges to arrive adds them, in range order, with all its
+    // threads.
+    __shared__ uint32_t last_flag;
+    __builtin_amdgcn_s_waitcnt(0);
+    asm volatile("" ::: "memory");
+    __syncthreads();
+    const int rb = (int)(blockIdx.x / (uint32_t)nkr);
+    if (wk == 0) {
+        uint32_t prev = 0;
+        if (lane == 0) prev = arrive(d, rb);
+        prev = __shfl(prev, 0, kWave);
+        if (lane == 0) last_flag = prev == (uint32_t)nkr - 1 ? 1u : 0u;
+    }
+    __syncthreads();
+    if (!last_flag) return;
+    asm volatile("" ::: "memory");
+    const int64_t slice = (int64_t)m * d.p;
+    for (int o = threadIdx.x; o < m * (int)rows; o += NW * kWave) {
+        const int i = o / (int)rows, r = o - i * (int)rows;
+        const float *src = d.yp + (int64_t)i * d.p + row_lo + r;
+        float v = 0.f;
+        for (int q0 = 0; q0 < nkr; q0 += 8) {
+            float t8[8];
+#pragma unroll
+            for (int u = 0; u < 8; ++u)
+                t8[u] = q0 + u < nkr ? __hip_atomic_load(src + (int64_t)(q0 + u) * slice, __ATOMIC_RELAXED,
+                                                         __HIP_MEMORY_SCOPE_AGENT)
+                                     : 0.f;
+#pragma unroll
+            for (int u = 0; u < 8; ++u)
+                if (q0 + u < nkr) v = (q0 + u == 0) ? t8[u] : v + t8[u];
+        }
+        d.Y[(int64_t)i * d.p + row_lo + r] = v;
     }
 }
 
@@ -1121,6 +1163,7 @@ int ks_a_bytes(int nw) { return nw == 8 ? Ks<8>::kA : nw == 4 ? Ks<4>::kA : 0; }
 hipError_t launch_gemm_ks(const GemmDesc &d, int nw, hipStream_t s) {
     if (d.rs != 1 || d.m < 2 || d.m > 16 || d.ks_ranges < 1 || d.ks_groups < 1 || d.ks_rows < 32 ||
         d.ks_rows % 32 || (int64_t)d.ks_ranges * d.ks_groups < d.gsr ||
+        (int64_t)(d.ks_ranges - 1) * d.ks_groups >= d.gsr ||   // no empty range
         (int64_t)d.ks_groups * kGroupBlocks * d.m * 192 > ks_a_bytes(nw))
         return hipErrorInvalidValue;
     const int64_t blocks = (int64_t)d.ks_ranges * ((d.p + d.ks_rows - 1) / d.ks_rows);
@@ -1131,7 +1174,7 @@ hipError_t launch_gemm_ks(const GemmDesc &d, int nw, hipStream_t s) {
         default: return hipErrorInvalidValue;
     }
     hipError_t e = hipGetLastError();
-    if (e != hipSuccess || d.ks_ranges == 1) return e;
+    if (e != hipSuccess || d.ks_ranges == 1 || d.ks_sum_here) return e;
     const int64_t total = (int64_t)d.m * d.p;
     hipLaunchKernelGGL(k_ks_reduce, dim3((unsigned)((total + 1023) / 1024)), dim3(256), 0, s, d);
     return hipGetLastError();
