@@ -201,7 +201,7 @@ def bench_smallm(args, q8, synth, torch, np):
                 kernel, unit = "k_q8_gemm_vrow<%d,2>" % m, "alu"
                 t_cmp = (1 + m) * shape.n * shape.p / VALU_LANE_OPS
             elif chosen == q8.SMALLM_KS:
-                kernel, unit = "k_split_x + k_q8_gemm_ks<8> (+ k_ks_reduce)", "mfma"
+                kernel, unit = "k_q8_gemm_ks<8> (+ k_ks_reduce)", "mfma"
                 t_cmp = 2 * 3 * 16 * shape.n * shape.p / MFMA_BF16_FLOPS
             else:
                 kernel, unit = "k_split_x + k_q8_gemm_mfma<1>", "mfma"
