@@ -438,21 +438,24 @@ def main():
     launches = chain.launches
     kernel_s = time_steps(lambda: chain.run(q8.MODE_EAGER, stream), args.steps) / args.steps / launches
     achieved = nbytes / launches / kernel_s / 1e9
-    # a chain of one op is that op's standalone launch (its latency plan);
-    # more independent ops share one fused launch of one-wave tiles with two
-    # weight stages: two lanes per row where the chain's byte-weighted mean
-    # row is 8 groups or more, else one (the library's rule); widths that
-    # are not whole groups take the mixed-width kernel.  Template arguments:
-    # lanes per row, waves per workgroup, weight stages in LDS, build mode
-    # (0 float activations, 1 activations quantized to Q8_0)
+    # The kernel, named from the library's own plan of this chain
+    # (q8_0_chain_plan): a chain of one op is that op's standalone launch
+    # (its latency plan); more independent ops share one fused launch, of
+    # the rows-and-group-slots tile where every width is whole groups, else
+    # of the mixed-width kernel.  Template arguments: lanes per row, waves
+    # per workgroup, weight stages in LDS, build mode (0 float activations,
+    # 1 activations quantized to Q8_0).
     mode = 1 if args.xq else 0
-    whole = all(o.n % 256 == 0 for o in ops_shape)
-    wb = [synth.workload_bytes([o]) for o in ops_shape]
-    mean_groups = sum(b * (o.n // 256) for b, o in zip(wb, ops_shape)) / sum(wb)
+    plan, _, _ = q8.chain_plan([(x.data_ptr(), w.data_ptr(), y.data_ptr(), o.n, o.p)
+                                for (x, w, y), o in zip(dev_ops, ops_shape)],
+                               q8.Q8_CHAIN_XQ if args.xq else 0,
+                               torch.cuda.get_device_properties(0).multi_processor_count)
+    lp = plan[0]
     if len(ops_shape) == 1:
-        kernel = "k_q8_gemv_rc<C,NWK,NST,%d> (the op's latency plan)" % mode
-    elif whole:
-        kernel = "k_q8_gemv_rc_fused<%d,1,2,%d>" % (2 if mean_groups >= 8.0 else 1, mode)
+        kernel = "k_q8_gemv_rc<%d,%d,%d,%d> (the op's latency plan)" % (
+            lp["lanes_per_row"], lp["waves"], lp["stages"], mode)
+    elif lp["kind"] == 2:
+        kernel = "k_q8_gemv_rc_fused<%d,%d,%d,%d>" % (lp["lanes_per_row"], lp["waves"], lp["stages"], mode)
     else:
         kernel = "k_q8_gemv_mixed<%d>" % mode
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,

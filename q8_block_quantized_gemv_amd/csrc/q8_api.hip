@@ -236,15 +236,17 @@ RcShape plan_rc_latency(int64_t rows, int64_t G, int xmode, int ymode, int64_t c
 }
 
 // Launch shape of a fused launch of independent ops (a throughput launch):
-// one-wave tiles with two W stages, the steady-state layout, and one lane
-// per row when rows are short, two when they are long, by the launch's
-// byte-weighted mean of groups per row G.  Measured on the decode chains
-// (kernel time per token): the 0.6B chain (G ~ 5.5) 108 us with one lane,
-// 115 with two; the 7B chain (G ~ 20) 1226 us with one lane, 1190 with two.
-// Two lanes give each row twice the contiguous bytes per load and the
-// workgroup half the rows, but halve the group columns a tile streams.
+// one-wave tiles, two lanes per row, by the launch's byte-weighted mean of
+// groups per row G: two W stages where rows are long, one where they are
+// short.  Measured on the decode chains (kernel time per token): the 7B
+// chain (G ~ 20) 1190 us with {2 lanes, 2 stages}, 1226 with one lane; the
+// 0.6B chain (G ~ 5.5) 107.3 us with {2 lanes, 1 stage}, 109.1 with {1
+// lane, 2 stages}, 109.2 with {1 lane, 2 waves, 1 stage}, 115 with {2
+// lanes, 2 stages}, 121-126 with {1, 1, 1}, {1, 2, 2}, {2, 2, 1}.  Two lanes
+// give each row twice the contiguous bytes per load and a tile half the
+// rows; one stage halves a wave's LDS, so twice the waves fit on a CU.
 RcShape fuse_shape(double mean_groups) {
-    return mean_groups >= 8.0 ? RcShape{2, 1, 2} : RcShape{1, 1, 2};
+    return mean_groups >= 8.0 ? RcShape{2, 1, 2} : RcShape{2, 1, 1};
 }
 
 bool shape_ok(int c, int nwk, int nst) {
