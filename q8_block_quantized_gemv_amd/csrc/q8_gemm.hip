@@ -1069,33 +1069,25 @@ __global__ __launch_bounds__(NW * kWave, 1) void k_q8_gemm_ks(GemmDesc d) {
     }
 }
 
-// Y = the sum over the ranges of d.yp, in range order, four outputs a thread
-// (read as float4 when m * p is a multiple of 4, so that every range's slice
-// of the 256-byte aligned workspace stays 16-byte aligned; else one by one).
+// Y = the sum over the ranges of d.yp, in range order: one output a thread,
+// its ranges' values loaded eight at a time before they are added, so that
+// a sum over many ranges costs a few round trips to memory, not one each.
 __global__ __launch_bounds__(256) void k_ks_reduce(GemmDesc d) {
     const int64_t total = (int64_t)d.m * d.p;
-    const int64_t i = 4 * ((int64_t)blockIdx.x * 256 + threadIdx.x);
+    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
     if (i >= total) return;
-    if (i + 4 <= total && (total & 3) == 0) {
-        float4 v = *reinterpret_cast<const float4 *>(d.yp + i);
-        for (int r = 1; r < d.ks_ranges; ++r) {
-            const float4 u = *reinterpret_cast<const float4 *>(d.yp + (int64_t)r * total + i);
-            v.x += u.x;
-            v.y += u.y;
-            v.z += u.z;
-            v.w += u.w;
-        }
-        d.Y[i] = v.x;   // Y is only 4-byte aligned
-        d.Y[i + 1] = v.y;
-        d.Y[i + 2] = v.z;
-        d.Y[i + 3] = v.w;
-        return;
+    const int nkr = d.ks_ranges;
+    const float *src = d.yp + i;
+    float v = 0.f;
+    for (int q0 = 0; q0 < nkr; q0 += 8) {
+        float t8[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) t8[u] = q0 + u < nkr ? src[(int64_t)(q0 + u) * total] : 0.f;
+#pragma unroll
+        for (int u = 0; u < 8; ++u)
+            if (q0 + u < nkr) v = (q0 + u == 0) ? t8[u] : v + t8[u];
     }
-    for (int64_t k = i; k < min(i + 4, total); ++k) {
-        float v = d.yp[k];
-        for (int r = 1; r < d.ks_ranges; ++r) v += d.yp[(int64_t)r * total + k];
-        d.Y[k] = v;
-    }
+    d.Y[i] = v;
 }
 
 template <int RS>
@@ -1176,7 +1168,7 @@ hipError_t launch_gemm_ks(const GemmDesc &d, int nw, hipStream_t s) {
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || d.ks_ranges == 1 || d.ks_sum_here) return e;
     const int64_t total = (int64_t)d.m * d.p;
-    hipLaunchKernelGGL(k_ks_reduce, dim3((unsigned)((total + 1023) / 1024)), dim3(256), 0, s, d);
+    hipLaunchKernelGGL(k_ks_reduce, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, s, d);
     return hipGetLastError();
 }
 
