@@ -938,8 +938,12 @@ int plan_chain(const q8_0_op *ops, int64_t n_ops, uint32_t flags, const OpExtra 
                 set_extra(d, ex(i));
                 const uint32_t oi = (uint32_t)(h_ops.size() - si.op0);
                 h_ops.push_back(d);
-                const int64_t fb = (int64_t)kWave * d.sr_bytes;
-                for (int64_t t = 0; t < d.fast_tiles; ++t) items.push_back({{oi, (uint32_t)t}, fb});
+                // rows of whole groups: the rows-and-group-slots tile of the
+                // mixed launch (kMixC lanes per row); others: 64 super-rows
+                const bool rc = d.rs == 1;
+                const int64_t nf = rc ? rc_tiles_for(d.p, kMixC) : d.fast_tiles;
+                const int64_t fb = (rc ? kWave / kMixC : kWave) * d.sr_bytes;
+                for (int64_t t = 0; t < nf; ++t) items.push_back({{oi, (uint32_t)t}, fb});
                 const int64_t tt = tail_tiles_for((int64_t)d.p - d.tail_row0, 1);
                 for (int64_t t = 0; t < tt; ++t)
                     items.push_back({{oi, (uint32_t)t | kTailBit}, (int64_t)d.nb * kBlockBytes});

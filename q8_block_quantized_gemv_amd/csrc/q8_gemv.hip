@@ -278,12 +278,12 @@ __global__ __launch_bounds__(NW * kWave) void k_q8_gemv(OpDesc op) {
 
 // A fused launch of one-wave workgroups over a table of tiles of
 // independent ops: rows of whole groups take the rows-and-group-slots tile
-// with one lane per row and two W stages (RcShape {1, 1, 2}), the others
-// the super-row tile.
+// with kMixC lanes per row and kMixNst W stages, the others the super-row
+// tile; the LDS is the larger of the two.
 template <int XM>
 constexpr int mixed_lds_bytes() {
-    return kBufs * stage_bytes<XM>() > rc_lds_bytes<1, 1, XM, 2>() ? kBufs * stage_bytes<XM>()
-                                                                    : rc_lds_bytes<1, 1, XM, 2>();
+    return kBufs * stage_bytes<XM>() > rc_lds_bytes<kMixC, 1, XM, kMixNst>() ? kBufs * stage_bytes<XM>()
+                                                                            : rc_lds_bytes<kMixC, 1, XM, kMixNst>();
 }
 
 template <int XM>
@@ -292,7 +292,7 @@ __global__ __launch_bounds__(kWave) void k_q8_gemv_mixed(const OpDesc *__restric
     __shared__ __attribute__((aligned(16))) uint8_t stage[mixed_lds_bytes<XM>()];
     const Tile tl = tiles[blockIdx.x];
     const OpDesc op = ops[tl.op];
-    if (op.rs == 1) rc_tile<1, 1, XM, 2>(op, tl.tile, stage, tl.tile == 0);
+    if (op.rs == 1) rc_tile<kMixC, 1, XM, kMixNst>(op, tl.tile, stage, tl.tile == 0);
     else run_superrow<1, XM>(op, tl.tile, stage);
 }
 

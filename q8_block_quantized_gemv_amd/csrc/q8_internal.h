@@ -141,6 +141,15 @@ inline int64_t tail_tiles_for(int64_t tail_rows, int nw = kWaves) {
     return (tail_rows + nw - 1) / nw;
 }
 // rs == 1: tiles of 64 / C rows, or of the shape's rc_rows.
+// The mixed-width fused launch (k_q8_gemv_mixed): rows of whole groups take
+// the rows-and-group-slots tile with kMixC lanes per row and kMixNst W
+// stages (as fuse_shape's short-row launch; measured on the Qwen2.5-0.5B
+// chain, whose whole-group rows are its 24 down projections: 98.6 us per
+// token against 99.5 with {1 lane, 2 stages}), the other widths the
+// super-row tile.  (The super-row tile with one W stage and two x stages
+// measured no faster there: 99.7-107.6 us.)
+constexpr int kMixC = 2, kMixNst = 1;
+
 inline int64_t rc_tiles_for(int64_t p, int c) {
     const int64_t rows = kWave / c;
     return (p + rows - 1) / rows;

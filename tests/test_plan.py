@@ -193,6 +193,9 @@ def check_plan(q8, ops, flags, cus=256):
                 tail = sorted(t & ~q8.TAIL_BIT for t in ts if t & q8.TAIL_BIT)
                 assert fast == list(range(len(fast))) and tail == list(range(len(tail)))
                 assert fast or tail
+                n, p = ops[o][3], ops[o][4]
+                if n % 256 == 0:   # rows of whole groups: 32-row tiles (two lanes per row)
+                    assert len(fast) == -(-p // 32) and not tail
     return launches
 
 
