@@ -189,11 +189,11 @@ int64_t tiles_of(const OpDesc &d, int nw) {
 //    such workgroups covers the rows (a row-poor op: every wave then streams
 //    its columns at once, e.g. 7B q/o/down, every 0.6B projection);
 //  * tiles of 32 rows with four waves when that still fits (7B q|k|v);
-//  * otherwise one-wave tiles of 16 rows if they are all resident at once
-//    (7B gate), else two-wave tiles (lm_heads: fewer columns per wave
-//    shortens the last wave of tiles) -- except where every workgroup first
-//    sums the squares of x + x_res over the whole row (kXNormAdd), and for
-//    the gate|up pair (kYSwiGLU, two waves per tile already): there
+//  * otherwise one-wave tiles of 16 rows (7B gate; the lm_heads, with the
+//    weights read non-temporal: 7B 98.2 us against 102.3 with two-wave
+//    tiles, 0.6B 34.6 us against 53.9) -- except where every workgroup
+//    first sums the squares of x + x_res over the whole row (kXNormAdd), and
+//    for the gate|up pair (kYSwiGLU, two waves per tile already): there
 //    one-wave tiles of 32 rows, half the workgroups, are fastest.
 // One W stage per wave: twice the waves fit, which measured faster than a
 // second stage at every one of these shapes.
@@ -231,8 +231,7 @@ RcShape plan_rc_latency(int64_t rows, int64_t G, int xmode, int ymode, int64_t c
         const int64_t t2 = (rows + 31) / 32;
         if (t2 > cus && t2 <= resident({2, 2, 1})) return balanced({2, 2, 1});
     }
-    if (t4 <= resident({4, 1, 1})) return balanced({4, 1, 1});
-    return balanced({4, J4 >= 2 ? 2 : 1, 1});
+    return balanced({4, 1, 1});
 }
 
 // Launch shape of a fused launch of independent ops (a throughput launch):
