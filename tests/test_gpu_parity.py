@@ -341,6 +341,30 @@ def test_gemm_ks_sweep(q8, n, p, m):
     assert np.array_equal(down(Y).view(np.uint32), Yh.view(np.uint32))
 
 
+@pytest.mark.parametrize("m,n,p", [(8, 18944, 300), (16, 18944, 3584), (4, 3584, 700)])
+def test_gemm_ks_y_offset(q8, m, n, p):
+    """Y only 4-byte aligned (one float past a 256-byte boundary), on the
+    matrix cores with X held in LDS: with the ranges' sums added by the last
+    workgroup of each row block (n = 18944 at m = 8), by a second launch
+    (m = 16), and with one range (n = 3584 at m = 4).  Every output against
+    the oracle; the floats around Y untouched."""
+    import torch
+    log("gemm ks y offset m=%d n=%d p=%d" % (m, n, p))
+    rng = np.random.default_rng(n + 7 * p + m)
+    w = synth.q8_weights(n, p, rng)
+    X = synth.activations(n, rng, m).reshape(m, n)
+    wd = w_dev(w, n, p)
+    buf = torch.full((m * p + 2,), 7.0, dtype=torch.float32, device="cuda")
+    Y = buf[1:1 + m * p].view(m, p)
+    q8.gemm_smallm(up(X), wd, Y, kernel=q8.SMALLM_KS)
+    b = down(buf)
+    assert b[0] == 7.0 and b[-1] == 7.0
+    Yh = b[1:1 + m * p].reshape(m, p)
+    _, Y64, MAG = oracle.gemm(w, X, m, n, p)
+    for i in range(m):
+        parity(Yh[i], Y64[i], MAG[i], "ks y offset row %d" % i)
+
+
 @pytest.mark.parametrize("m", [2, 3, 16])
 def test_gemm_identical_rows(q8, m):
     """m equal rows of X give m bitwise-equal rows of Y (m = 2, 3 on the
