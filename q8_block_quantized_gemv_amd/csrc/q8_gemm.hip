@@ -1069,23 +1069,51 @@ __global__ __launch_bounds__(NW * kWave, 1) void k_q8_gemm_ks(GemmDesc d) {
     }
 }
 
-// Y = the sum over the ranges of d.yp, in range order: one output a thread,
-// its ranges' values loaded eight at a time before they are added, so that
-// a sum over many ranges costs a few round trips to memory, not one each.
+// Y = the sum over the ranges of d.yp, in range order.  Where p is a
+// multiple of 4 a thread takes four consecutive outputs (16-byte loads of
+// the slices, up to 16 ranges' loads in flight before they are added),
+// else one output; either way every output is v_0 + v_1 + ... in range
+// order, the same bits as the last-arriver sum in k_q8_gemm_ks.  Y is
+// stored a float at a time (it need only be 4-byte aligned).
+constexpr int kReduceBatch = 16;
 __global__ __launch_bounds__(256) void k_ks_reduce(GemmDesc d) {
     const int64_t total = (int64_t)d.m * d.p;
+    const int nkr = d.ks_ranges;
+    if (d.p % 4 == 0) {
+        const int64_t i4 = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 4;
+        if (i4 >= total) return;
+        const float4 *src = reinterpret_cast<const float4 *>(d.yp + i4);
+        const int64_t slice4 = total / 4;
+        float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
+        for (int q0 = 0; q0 < nkr; q0 += kReduceBatch) {
+            float4 t[kReduceBatch];
+#pragma unroll
+            for (int u = 0; u < kReduceBatch; ++u)
+                t[u] = q0 + u < nkr ? src[(int64_t)(q0 + u) * slice4] : make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+            for (int u = 0; u < kReduceBatch; ++u)
+                if (q0 + u < nkr) {
+                    if (q0 + u == 0) v = t[u];
+                    else v = make_float4(v.x + t[u].x, v.y + t[u].y, v.z + t[u].z, v.w + t[u].w);
+                }
+        }
+        d.Y[i4] = v.x;
+        d.Y[i4 + 1] = v.y;
+        d.Y[i4 + 2] = v.z;
+        d.Y[i4 + 3] = v.w;
+        return;
+    }
     const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
     if (i >= total) return;
-    const int nkr = d.ks_ranges;
     const float *src = d.yp + i;
     float v = 0.f;
-    for (int q0 = 0; q0 < nkr; q0 += 8) {
-        float t8[8];
+    for (int q0 = 0; q0 < nkr; q0 += kReduceBatch) {
+        float t[kReduceBatch];
 #pragma unroll
-        for (int u = 0; u < 8; ++u) t8[u] = q0 + u < nkr ? src[(int64_t)(q0 + u) * total] : 0.f;
+        for (int u = 0; u < kReduceBatch; ++u) t[u] = q0 + u < nkr ? src[(int64_t)(q0 + u) * total] : 0.f;
 #pragma unroll
-        for (int u = 0; u < 8; ++u)
-            if (q0 + u < nkr) v = (q0 + u == 0) ? t8[u] : v + t8[u];
+        for (int u = 0; u < kReduceBatch; ++u)
+            if (q0 + u < nkr) v = (q0 + u == 0) ? t[u] : v + t[u];
     }
     d.Y[i] = v;
 }
@@ -1168,7 +1196,8 @@ hipError_t launch_gemm_ks(const GemmDesc &d, int nw, hipStream_t s) {
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || d.ks_ranges == 1 || d.ks_sum_here) return e;
     const int64_t total = (int64_t)d.m * d.p;
-    hipLaunchKernelGGL(k_ks_reduce, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, s, d);
+    const int64_t threads = d.p % 4 == 0 ? total / 4 : total;   // four outputs a thread where p allows
+    hipLaunchKernelGGL(k_ks_reduce, dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, s, d);
     return hipGetLastError();
 }
 

@@ -341,12 +341,13 @@ def test_gemm_ks_sweep(q8, n, p, m):
     assert np.array_equal(down(Y).view(np.uint32), Yh.view(np.uint32))
 
 
-@pytest.mark.parametrize("m,n,p", [(8, 18944, 300), (16, 18944, 3584), (4, 3584, 700)])
+@pytest.mark.parametrize("m,n,p", [(8, 18944, 300), (16, 18944, 3584), (16, 18944, 1030), (4, 3584, 700)])
 def test_gemm_ks_y_offset(q8, m, n, p):
     """Y only 4-byte aligned (one float past a 256-byte boundary), on the
     matrix cores with X held in LDS: with the ranges' sums added by the last
     workgroup of each row block (n = 18944 at m = 8), by a second launch
-    (m = 16), and with one range (n = 3584 at m = 4).  Every output against
+    (m = 16: four outputs a thread where p is a multiple of 4, one where it
+    is not), and with one range (n = 3584 at m = 4).  Every output against
     the oracle; the floats around Y untouched."""
     import torch
     log("gemm ks y offset m=%d n=%d p=%d" % (m, n, p))
