@@ -234,18 +234,31 @@ RcShape plan_rc_latency(int64_t rows, int64_t G, int xmode, int ymode, int64_t c
     return balanced({4, 1, 1});
 }
 
-// Launch shape of a fused launch of independent ops (a throughput launch):
-// one-wave tiles, two lanes per row, by the launch's byte-weighted mean of
-// groups per row G: two W stages where rows are long, one where they are
-// short.  Measured on the decode chains (kernel time per token): the 7B
-// chain (G ~ 20) 1190 us with {2 lanes, 2 stages}, 1226 with one lane; the
-// 0.6B chain (G ~ 5.5) 107.3 us with {2 lanes, 1 stage}, 109.1 with {1
-// lane, 2 stages}, 109.2 with {1 lane, 2 waves, 1 stage}, 115 with {2
-// lanes, 2 stages}, 121-126 with {1, 1, 1}, {1, 2, 2}, {2, 2, 1}.  Two lanes
-// give each row twice the contiguous bytes per load and a tile half the
-// rows; one stage halves a wave's LDS, so twice the waves fit on a CU.
-RcShape fuse_shape(double mean_groups) {
-    return mean_groups >= 8.0 ? RcShape{2, 1, 2} : RcShape{2, 1, 1};
+// Launch shape of a fused launch of independent ops (a throughput launch),
+// and whether its weights are loaded non-temporal (each is read once).
+//  * Float x: one-wave 16-row tiles, four lanes per row, one W stage,
+//    non-temporal.  A group column is then 16 runs of 1088 contiguous bytes
+//    (whole rows where n = 1024), so few 128-byte lines are split between
+//    two columns, and the hint pays.  Measured (kernel time per token): 7B
+//    chain 1180-1182 us against 1189-1193 with the shape below; 0.6B chain
+//    102.5-106.3 against 107.3-107.4 (box to box), 111.6 with four lanes and
+//    plain loads, 104.0 with the hint only where a column holds whole rows;
+//    with two lanes (runs of 544 bytes) the hint lost (7B chain 1360 us:
+//    every line two runs share came in twice).
+//  * x quantized per column (kXQuant): two lanes per row, plain loads, two
+//    W stages where the launch's byte-weighted mean row is 8 groups or more,
+//    else one: a tile quantizes each column's x slices, and 16-row tiles
+//    would do that twice as often per weight byte (7B chain 1261 us against
+//    1190).  The 7B chain (mean ~20 groups) 1190 us with {2, 1, 2}, 1226 with
+//    one lane; the 0.6B shape (mean ~5.6) 107.3 us with {2, 1, 1}, 109.1
+//    with {1, 1, 2}, 115 with {2, 1, 2}.
+struct FusePlan {
+    RcShape shape;
+    bool w_once;
+};
+FusePlan fuse_plan(int xmode, double mean_groups) {
+    if (xmode == kXQuant) return {mean_groups >= 8.0 ? RcShape{2, 1, 2} : RcShape{2, 1, 1}, false};
+    return {RcShape{4, 1, 1}, true};
 }
 
 bool shape_ok(int c, int nwk, int nst) {
@@ -901,23 +914,24 @@ int plan_chain(const q8_0_op *ops, int64_t n_ops, uint32_t flags, const OpExtra 
             // over all the launch's rows when they share a width; otherwise
             // the steady-state one-wave tiles, largest tiles first so that
             // the smallest finish the launch
-            const RcShape sh = latency && one_width
-                                   ? plan_rc_latency(rows, ops[sg.first].n / (kQuants * kGroupBlocks), xmode, ymode, cus, false)
-                                   : fuse_shape(wg / wsum);
+            const bool lat = latency && one_width;
+            const FusePlan fp = fuse_plan(xmode, wg / wsum);
+            const RcShape sh = lat ? plan_rc_latency(rows, ops[sg.first].n / (kQuants * kGroupBlocks), xmode, ymode, cus, false)
+                                   : fp.shape;
             struct Item { Tile t; int64_t bytes; };
             std::vector<Item> items;
             for (int64_t i = sg.first; i < sg.second; ++i) {
                 const q8_0_op &o = ops[i];
                 OpDesc d = plan_op(o.x, o.w, o.y, 1, o.n, o.p, false, 1);
                 set_extra(d, ex(i));
-                d.w_once = latency && one_width ? 1 : 0;   // the latency plan's launch
+                d.w_once = lat || fp.w_once ? 1 : 0;
                 const uint32_t oi = (uint32_t)(h_ops.size() - si.op0);
                 h_ops.push_back(d);
                 const int64_t tb = (int64_t)(kWave / sh.c) * d.sr_bytes;
                 const int64_t nt = rc_tiles_for(d.p, sh.c);
                 for (int64_t t = 0; t < nt; ++t) items.push_back({{oi, (uint32_t)t}, tb});
             }
-            if (!(latency && one_width))
+            if (!lat)
                 std::stable_sort(items.begin(), items.end(),
                                  [](const Item &a, const Item &b) { return a.bytes > b.bytes; });
             for (auto &it : items) h_tiles.push_back(it.t);

@@ -13,7 +13,7 @@
 //    columns" j = 0, 1, ...: column j is groups C*j .. C*j + C-1 of each of
 //    the R rows, and lane (r, c) computes group C*j + c of row r.
 //  * Each column moves HBM -> LDS as 17 direct 16-byte loads per lane
-//    (non-temporal in latency launches, op.w_once)
+//    (non-temporal where op.w_once: latency and fused launches)
 //    (global_load_lds_dwordx4): load i of lane l carries chunk (64i + l) of
 //    the column's R runs of C*272 contiguous bytes, so every load
 //    instruction reads whole contiguous KiB, and lane l finds its own group

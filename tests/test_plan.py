@@ -177,12 +177,16 @@ def check_plan(q8, ops, flags, cus=256):
                     assert (L["lanes_per_row"], L["waves"], L["stages"]) == (c, w, st)
                 assert items == sorted(items)
             else:
-                # steady-state tiles: one-wave tiles, two lanes per row, two
-                # weight stages when rows are long, one when they are short;
-                # largest tiles first
-                b = [wbytes(m[3], m[4]) for m in members]
-                mean = sum(bb * groups(m[3]) for bb, m in zip(b, members)) / sum(b)
-                assert (L["lanes_per_row"], L["waves"], L["stages"]) == (2, 1, (2 if mean >= 8 else 1))
+                # steady-state tiles, largest tiles first: float x, one-wave
+                # 16-row tiles, four lanes per row, one weight stage; x
+                # quantized per column, two lanes per row, two weight stages
+                # when rows are long, one when they are short
+                if flags & q8.Q8_CHAIN_XQ:
+                    b = [wbytes(m[3], m[4]) for m in members]
+                    mean = sum(bb * groups(m[3]) for bb, m in zip(b, members)) / sum(b)
+                    assert (L["lanes_per_row"], L["waves"], L["stages"]) == (2, 1, (2 if mean >= 8 else 1))
+                else:
+                    assert (L["lanes_per_row"], L["waves"], L["stages"]) == (4, 1, 1)
                 rows = 64 // L["lanes_per_row"]
                 sizes = [rows * (ops[o][3] // 32) * 34 for o, _ in items]
                 assert sizes == sorted(sizes, reverse=True)
