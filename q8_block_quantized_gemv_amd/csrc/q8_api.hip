@@ -949,11 +949,13 @@ int plan_chain(const q8_0_op *ops, int64_t n_ops, uint32_t flags, const OpExtra 
                 const q8_0_op &o = ops[i];
                 OpDesc d = plan_op(o.x, o.w, o.y, 1, o.n, o.p, false, 1);
                 set_extra(d, ex(i));
+                // rows of whole groups: the rows-and-group-slots tile of the
+                // mixed launch (kMixC lanes per row, W loaded non-temporal);
+                // others: 64 super-rows
+                const bool rc = d.rs == 1;
+                d.w_once = rc ? 1 : 0;
                 const uint32_t oi = (uint32_t)(h_ops.size() - si.op0);
                 h_ops.push_back(d);
-                // rows of whole groups: the rows-and-group-slots tile of the
-                // mixed launch (kMixC lanes per row); others: 64 super-rows
-                const bool rc = d.rs == 1;
                 const int64_t nf = rc ? rc_tiles_for(d.p, kMixC) : d.fast_tiles;
                 const int64_t fb = (rc ? kWave / kMixC : kWave) * d.sr_bytes;
                 for (int64_t t = 0; t < nf; ++t) items.push_back({{oi, (uint32_t)t}, fb});

@@ -143,11 +143,13 @@ inline int64_t tail_tiles_for(int64_t tail_rows, int nw = kWaves) {
 // rs == 1: tiles of 64 / C rows, or of the shape's rc_rows.
 // The mixed-width fused launch (k_q8_gemv_mixed): rows of whole groups take
 // the rows-and-group-slots tile with kMixC lanes per row and kMixNst W
-// stages (as fuse_shape's short-row launch; measured on the Qwen2.5-0.5B
-// chain, whose whole-group rows are its 24 down projections: 98.6 us per
-// token against 99.5 with {1 lane, 2 stages}), the other widths the
-// super-row tile.  (The super-row tile with one W stage and two x stages
-// measured no faster there: 99.7-107.6 us.)
+// stages, W loaded non-temporal (measured on the Qwen2.5-0.5B chain, whose
+// whole-group rows are its 24 down projections: 97.4-97.6 us per token
+// against 98.6-98.7 with plain loads, 97.9-98.1 with four lanes and the
+// hint, 101.2-101.5 with four lanes and plain loads, 99.5 with {1 lane,
+// 2 stages}), the other widths the super-row tile.  (The super-row tile
+// with one W stage and two x stages measured no faster there: 99.7-107.6
+// us.)
 constexpr int kMixC = 2, kMixNst = 1;
 
 inline int64_t rc_tiles_for(int64_t p, int c) {
