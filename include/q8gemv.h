@@ -134,7 +134,12 @@ Q8_API int q8_0_gemm_smallm_workspace(int64_t m, int64_t n, int64_t p, int kerne
  * their own (code under stream capture, tight serving loops, harnesses that
  * forbid allocation): the same kernels and the same results, with the
  * workspace taken from a scratch array inside the library, 32 MiB on each
- * GPU it runs on, held until the process ends.  Allocates nothing.
+ * GPU it runs on, held until the process ends.  Allocates nothing.  One
+ * exception to "the same kernels": where q8_0_gemm_smallm would run
+ * Q8_SMALLM_KS with more than 16 MiB of per-range sums (rows of whole
+ * groups, m and n large, e.g. m = 16, n = 3584, p = 152064), this call runs
+ * Q8_SMALLM_MFMA instead, which needs far less; its results then meet the
+ * same bar but round differently.
  * Q8_ERR_SHAPE (with the bytes needed in q8_0_last_error) when the call needs
  * more than that (q8_0_gemm_smallm_workspace tells).  Every call on one GPU
  * shares its array: calls that may overlap on one GPU (other streams,

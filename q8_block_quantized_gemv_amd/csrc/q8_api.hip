@@ -397,9 +397,15 @@ int smallm_kernel(int kernel, int64_t m, int64_t n, const char *what) {
     return kernel;
 }
 
+// Most bytes of per-range sums Q8_SMALLM_AUTO lets the held-X kernel take:
+// with a caller's workspace, and within the library's scratch (the
+// allocation-free entry point, whose choice must fit what it has).
+constexpr int64_t kKsPartCap = int64_t(64) << 20;
+constexpr int64_t kKsPartCapNoAlloc = int64_t(16) << 20;
+
 // The kernel Q8_SMALLM_AUTO runs for a validated (m, n, p) on a device of
 // `cus` CUs; a named kernel is returned as it is.
-int smallm_resolve(int kernel, int64_t m, int64_t n, int64_t p, int64_t cus) {
+int smallm_resolve(int kernel, int64_t m, int64_t n, int64_t p, int64_t cus, int64_t part_cap = kKsPartCap) {
     if (kernel != Q8_SMALLM_AUTO) return kernel;
     const int64_t rs = kGroupBlocks / gcd64(n / kQuants, kGroupBlocks);
     const bool mfma_ok = rs <= 2, vrow_ok = rs == 1 && m >= 2 && m <= kVrowMaxM;
@@ -411,8 +417,10 @@ int smallm_resolve(int kernel, int64_t m, int64_t n, int64_t p, int64_t cus) {
     // m = 2..3 at fewer than 65536 rows, where the vector units with lanes
     // over (row, block pair) keep each lane's x values in registers and need
     // no split of X (down 26.6 us, gate 22.6 us at m = 2, against 39.1 and
-    // 25.3), and shapes whose per-range sums would pass 16 MiB (the 7B
-    // lm_head at m = 16), which stay on the stream-K kernel.  Where rows fill
+    // 25.3), and shapes whose per-range sums would pass part_cap, which stay
+    // on the stream-K kernel (the 7B lm_head at m = 16, 48.7 MB of sums:
+    // 149.3-149.5 us held-X against 164.1-164.6 stream-K, so a caller's
+    // workspace may hold them; the library's scratch may not).  Where rows fill
     // super-rows of 1 or 2 (n a multiple of 128) the stream-K matrix cores
     // take m >= 2.  Other widths run on the vector units with a lane per
     // row, kValuMaxM rows of X per pass over W.
@@ -421,7 +429,7 @@ int smallm_resolve(int kernel, int64_t m, int64_t n, int64_t p, int64_t cus) {
         GemmDesc d = plan_gemm(kShapeOnly, kShapeOnly, nullptr, m, n, p);
         plan_ks(d, cus);
         const int64_t part = d.ks_ranges > 1 ? (int64_t)d.ks_ranges * m * p * (int64_t)sizeof(float) : 0;
-        if (part <= ((int64_t)16 << 20)) return Q8_SMALLM_KS;
+        if (part <= part_cap) return Q8_SMALLM_KS;
     }
     return vrow_ok ? Q8_SMALLM_VROW : mfma_ok ? Q8_SMALLM_MFMA : Q8_SMALLM_VALU;
 }
@@ -655,7 +663,7 @@ int q8_0_gemm_smallm_noalloc(const float *X, const void *w, float *Y, int64_t m,
     int dev = 0;
     if ((rc = check_device(&dev))) return rc;
     const int64_t cus = cu_count(dev);
-    k = smallm_resolve(k, m, n, p, cus);
+    k = smallm_resolve(k, m, n, p, cus, kKsPartCapNoAlloc);
     const size_t need = smallm_bytes(X, w, Y, m, n, p, k, cus);
     if (need > kScratchBytes)
         return fail(Q8_ERR_SHAPE, "q8_0_gemm_smallm_noalloc: m=" + std::to_string(m) + ", n=" + std::to_string(n) +

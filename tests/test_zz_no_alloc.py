@@ -56,6 +56,35 @@ def test_noalloc_equals_workspace_call(q8, first, second):
                 parity(got[i], Y64[i], MAG[i], "noalloc row %d" % i)
 
 
+def test_noalloc_keeps_to_its_scratch(q8):
+    """The 7B lm_head at m = 16: q8_0_gemm_smallm holds X in LDS and needs
+    48.7 MB for its per-range sums; the allocation-free call, whose scratch
+    is 32 MiB, runs the stream-K matrix cores instead -- bitwise what that
+    kernel gives through a workspace -- and both meet the bar on sampled
+    rows."""
+    import torch
+    m, n, p = 16, 3584, 152064
+    log("noalloc m=%d n=%d p=%d (held X needs more than the scratch)" % (m, n, p))
+    assert q8.gemm_smallm_choice(m, n, p) == q8.SMALLM_KS
+    w, X, wd, Xd, Y = _case(q8, m, n, p, 4242)
+    Y.fill_(float("nan"))
+    assert _noalloc(q8, Xd, wd, Y, m, n, p) == 0, q8.last_error()
+    got = down(Y).copy()
+    ref = torch.full_like(Y, float("nan"))
+    q8.gemm_smallm(Xd, wd, ref, kernel=q8.SMALLM_MFMA)
+    assert np.array_equal(got.view(np.uint32), down(ref).view(np.uint32))
+    ks = torch.full_like(Y, float("nan"))
+    q8.gemm_smallm(Xd, wd, ks)
+    ks = down(ks)
+    rows = np.random.default_rng(7).choice(p, 64, replace=False)
+    rb = n // 32 * 34
+    sub = np.ascontiguousarray(w.reshape(p, rb)[rows]).reshape(-1)
+    _, Y64, MAG = oracle.gemm(sub, X, m, n, len(rows))
+    for i in range(m):
+        parity(got[i, rows], Y64[i], MAG[i], "noalloc lm_head row %d" % i)
+        parity(ks[i, rows], Y64[i], MAG[i], "held-X lm_head row %d" % i)
+
+
 def test_noalloc_allocates_nothing(q8):
     import torch
     cases = [_case(q8, m, n, p, 50 + m) for m, n, p in ((16, 18944, 3584), (2, 3584, 18944), (5, 3584, 4608))]
