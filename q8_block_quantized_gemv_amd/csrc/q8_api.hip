@@ -416,8 +416,9 @@ int smallm_resolve(int kernel, int64_t m, int64_t n, int64_t p, int64_t cus, int
     // 109-161 us for the lm_head at m = 2..16 against 115-172 us -- except
     // m = 2..3 at fewer than 65536 rows, where the vector units with lanes
     // over (row, block pair) keep each lane's x values in registers and need
-    // no split of X (down 26.6 us, gate 22.6 us at m = 2, against 39.1 and
-    // 25.3), and shapes whose per-range sums would pass part_cap, which stay
+    // no split of X (down 26.5-26.9 us, gate 22.5 us at m = 2, against 39.1
+    // and 25.3 on the stream-K matrix cores and 36.0-36.2 and 23.4 with X
+    // held in LDS), and shapes whose per-range sums would pass part_cap, which stay
     // on the stream-K kernel (the 7B lm_head at m = 16, 48.7 MB of sums:
     // 149.3-149.5 us held-X against 164.1-164.6 stream-K, so a caller's
     // workspace may hold them; the library's scratch may not).  Where rows fill
